@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the centroid-indexed KV retrieval hot path on one MI355X.
+
+One step = one pass of the whole path over one Qwen3-8B-shaped layer
+(8 KV heads, 32 query heads, head dim 128, bf16, batch 1, 32768 prefill keys
+per head, C = 2048, 10 Lloyd rounds):
+  prefill : kv_cluster_build (K-means assign/update x10, CSR pack of K/V);
+  decode  : 256 steps of kv_boundary -> kv_select -> kv_gather_attend on the
+            seeded query walk, replayed from one captured HIP graph.
+Inputs are synthetic (seeded Gaussian-mixture keys, random values and query
+walks) and resident in HBM before timing starts.
+
+Printed JSON (one line): value = prefill keys clustered per second of whole
+steps (the decode loop included); the split into prefill time and decode
+microseconds per layer-step, the decode bytes moved per layer-step and the
+fraction of HBM peak are extra fields. ``roofline`` covers the dominant
+kernel, the MFMA K-means assignment, timed with HIP events on its stream;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, inp, q, lloyd_iters):
+    """Time the oracle on a bounded sample and scale to one whole step."""
+    import numpy as np
+
+    from oracle import kmeans as okm
+    from oracle.decode import run_decode
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    keys0, vals0, init0 = inp["keys"][0, 0], inp["values"][0, 0], inp["init_idx"][0, 0]
+    t0 = time.perf_counter()
+    o = okm.lloyd(keys0, init0, lloyd_iters, mode="parity", dtype=cfg.dtype)
+    t_lloyd = (time.perf_counter() - t0) * cfg.iters / lloyd_iters
+    pack = okm.pack(keys0, vals0, o["labels"], o["centroids"], cfg.dtype)
+    dec_steps = 16
+    t0 = time.perf_counter()
+    run_decode([pack], q[:dec_steps, 0, :cfg.group], cfg.tau, cfg.budget, cfg.scale, cfg.dtype)
+    t_dec = (time.perf_counter() - t0) / dec_steps  # one KV head, one step
+    heads = cfg.batch * cfg.n_kv_heads
+    t_step = heads * t_lloyd + cfg.steps * heads * t_dec
+    return {
+        "value": heads * cfg.n_keys / t_step,
+        "unit": "keys/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle: Lloyd on 1 of {heads} KV heads ({cfg.n_keys} keys, "
+                   f"C={cfg.n_clusters}, {lloyd_iters} of {cfg.iters} rounds timed) + {dec_steps} "
+                   f"decode steps of 1 KV head; scaled to {heads} heads, {cfg.iters} rounds, "
+                   f"{cfg.steps} decode steps"),
+        "step_s_extrapolated": t_step,
+        "decode_us_per_layer_step": t_dec * heads * 1e6,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-lloyd-iters", type=int, default=3)
+    ap.add_argument("--assign-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_kv_kmeans_amd as kvc
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kvc.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    cfg = wl.get_config(args.config)
+    if cfg.layers != 1 or cfg.buf_cap != 0:
+        raise SystemExit("bench.py times single-layer prefill+decode workloads (configs 0, 1, 4)")
+    t_gen = time.perf_counter()
+    inp = wl.layer_inputs(cfg, 0)
+    q_np, _ = wl.layer_queries(cfg, 0)
+    log(f"inputs generated in {time.perf_counter() - t_gen:.1f}s")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, H, N, d = inp["keys"].shape
+    C, T, Hq = cfg.n_clusters, cfg.steps, cfg.n_q_heads
+    keys = torch.from_numpy(inp["keys"]).to(tdt).cuda()
+    vals = torch.from_numpy(inp["values"]).to(tdt).cuda()
+    init = torch.from_numpy(inp["init_idx"]).cuda()
+    q = torch.from_numpy(q_np).to(tdt).cuda()  # [T, B, Hq, d]
+    pool = kvc.Pool(B, H, d, tdt, row_cap=N, unit_cap=C)
+    labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
+    ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
+    sel_cap = min(cfg.budget, C)
+    flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
+    sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
+    sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+    sel_rows = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+    out = torch.zeros(T, B, Hq, d, dtype=torch.float32, device="cuda")
+    ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
+    ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, cfg.budget))
+
+    def prefill():
+        kvc.kv_cluster_build(pool, keys, vals, C, cfg.iters, init, assign_out=labels, ws=ws_build)
+
+    def decode(record=None):
+        for t in range(T):
+            kvc.kv_boundary(q[t - 1] if t else None, q[t], cfg.tau, flags[t])
+            kvc.kv_select(pool, q[t], cfg.budget, flags[t], sel, sel_n, sel_rows, ws=ws_sel)
+            kvc.kv_gather_attend(pool, q[t], cfg.scale, sel, sel_n, cfg.budget, out[t], ws=ws_att)
+            if record is not None:
+                record.append(sel_rows.clone())
+
+    # eager pass: loads kernels and records the per-step work for the byte count
+    prefill()
+    rows_rec = []
+    decode(rows_rec)
+    torch.cuda.synchronize()
+    rows = torch.stack(rows_rec).cpu().numpy()  # [T, B, H]
+    fl = flags.cpu().numpy().astype(bool)       # [T, B]
+    e = 2 if cfg.dtype == "bf16" else 4
+    n_cand = C
+    bytes_steps = (2 * Hq * d * e * B
+                   + fl.sum(1) * H * n_cand * (d * e + 4)
+                   + rows.sum((1, 2)) * 2 * d * e
+                   + B * Hq * d * 4)
+    dec_bytes = float(bytes_steps.mean())
+    log(f"retrieval steps: {int(fl.sum())} of {T}; mean attended rows/head {rows.mean():.1f}")
+
+    # capture the decode loop once; replay per step
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        decode()  # warm on the capture stream
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        decode()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        with torch.cuda.stream(stream):
+            if i is not None:
+                ev[i][0].record(stream)
+            prefill()
+            if i is not None:
+                ev[i][1].record(stream)
+            graph.replay()
+            if i is not None:
+                ev[i][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    pre_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    dec_us = dec_ms * 1e3 / T
+
+    # dominant kernel: the MFMA assignment, timed live with HIP events on its stream
+    cents = pool.unit_mean[:, :, :C].reshape(B * H, C, d).contiguous()
+    k3 = keys.reshape(B * H, N, d)
+    lab2 = torch.zeros(B * H, N, dtype=torch.int32, device="cuda")
+    ws_asg = kvc.workspace(kvc.lib().kv_cluster_build_workspace(B, H, N, d, C, kvc.dtype_code(tdt)))
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.assign_reps)]
+    with torch.cuda.stream(stream):
+        kvc.kv_kmeans_assign(k3, cents, lab2, ws=ws_asg)
+        for a, b in aev:
+            a.record(stream)
+            kvc.kv_kmeans_assign(k3, cents, lab2, ws=ws_asg)
+            b.record(stream)
+    torch.cuda.synchronize()
+    asg_ms = float(np.mean([a.elapsed_time(b) for a, b in aev]))
+    flops = 2.0 * B * H * N * C * d
+    achieved = flops / (asg_ms * 1e-3) / 1e12
+
+    keys_per_step = B * H * N
+    res = {
+        "metric": "prefill keys clustered/s; decode select+gather+attend us/layer-step, %HBM peak",
+        "value": keys_per_step / (ms_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "n_kv_heads": H, "n_q_heads": Hq,
+                   "head_dim": d, "n_keys": N, "n_clusters": C, "iters": cfg.iters,
+                   "decode_steps": T, "budget": cfg.budget, "tau": cfg.tau},
+        "prefill_ms": pre_ms,
+        "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),
+        "decode_us_per_layer_step": dec_us,
+        "decode_bytes_per_layer_step": dec_bytes,
+        "decode_hbm_frac": dec_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+        "roofline": {"bound": "mfma", "kernel": "k_assign_mfma (via kv_kmeans_assign)",
+                     "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": asg_ms},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, args.cpu_lloyd_iters)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

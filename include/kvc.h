@@ -1,0 +1,229 @@
+/*
+ * kvc.h -- centroid-indexed KV-cache retrieval on MI355X (gfx950).
+ *
+ * The method is LouisKV's ("LouisKV: Efficient KV Cache Retrieval for Long
+ * Input-Output Sequences", papernotes.org note; edgentiq blog of the same
+ * method). At prefill each KV head's keys are clustered with K-means and
+ * every cluster is indexed by the mean of its keys; at decode, generated KV
+ * is cut into temporal segments at semantic boundaries, each indexed by its
+ * key mean; a retrieval happens only when the adjacent-query cosine r_t
+ * falls below tau, and then selects whole units under a token budget, one
+ * set per GQA group; attention runs over the selected rows.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless marked [host]. Every call validates
+ *   its arguments on the host, enqueues kernels on `stream` and returns; it
+ *   never synchronises, never allocates device memory and keeps no global
+ *   state. The caller owns every buffer, including workspaces.
+ * - Return value: KV_OK (0) or a negative kv_status. Argument errors are
+ *   reported before anything is enqueued. Conditions that depend on device
+ *   data (running out of pool rows or units while appending) are written to
+ *   the pool's device status word; the caller reads it after its own sync.
+ * - Element types: KV_BF16 (stored as raw bfloat16 bits) or KV_F32. Head
+ *   dimension 64 or 128. Index arithmetic is int32.
+ * - Layouts are dense, row-major, innermost dimension last, as written in
+ *   brackets. "BH" means batch * n_kv_heads (sequence-major).
+ * - GQA: query head h belongs to KV head h / (n_q_heads / n_kv_heads).
+ * - Workspaces must be 256-byte aligned. Workspaces of kv_select and
+ *   kv_gather_attend hold completion counters: zero-fill them once before
+ *   first use; every completed call leaves them zero again. Calls that share
+ *   a workspace must not run concurrently.
+ * - Determinism: every output is bitwise reproducible for identical inputs
+ *   (no floating-point atomics anywhere).
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent shapes */
+  KV_ERR_UNSUPPORTED = -2, /* head_dim or dtype not supported */
+  KV_ERR_WORKSPACE = -3,   /* workspace too small or misaligned */
+  KV_ERR_CAPACITY = -4,    /* pool rows/units or selection capacity exceeded */
+  KV_ERR_HIP = -5          /* a HIP launch failed */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+
+/*
+ * The unified KV pool of one layer ("Key designs" item 2 of the LouisKV note:
+ * prefill clusters and decode segments share one pool and one scoring
+ * mechanism). Here the pool lives in HBM. Rows of each (sequence, KV head)
+ * are stored cluster by cluster (CSR) after kv_cluster_build, then decode
+ * rows are appended in time order. Units are contiguous row ranges:
+ * clusters have ids 0..C-1, segments C, C+1, ... in closing order.
+ * Bookkeeping counters are per sequence (all KV heads of a sequence share
+ * cluster count and segment boundaries).
+ *
+ * The struct itself is [host] memory; every pointer in it is device memory
+ * owned by the caller.
+ */
+typedef struct kv_pool {
+  int32_t batch;      /* sequences */
+  int32_t n_kv_heads; /* KV heads per sequence */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t dtype;      /* kv_dtype of k, v and unit_index */
+  int32_t row_cap;    /* rows per (sequence, KV head) */
+  int32_t unit_cap;   /* units per (sequence, KV head) */
+  void *k;            /* [batch][n_kv_heads][row_cap][head_dim] */
+  void *v;            /* same */
+  int32_t *unit_start; /* [batch][n_kv_heads][unit_cap] first row of each unit */
+  int32_t *unit_size;  /* [batch][n_kv_heads][unit_cap] rows of each unit (0 = empty) */
+  float *unit_mean;    /* [batch][n_kv_heads][unit_cap][head_dim] fp32 key mean */
+  void *unit_index;    /* same shape, dtype: the scoring copy, RNE of unit_mean */
+  int32_t *n_rows;     /* [batch] rows in use */
+  int32_t *n_units;    /* [batch] units written (clusters + closed segments) */
+  int32_t *n_cand;     /* [batch] selectable units: clusters + evicted segments */
+  int32_t buf_cap;     /* local-buffer rows; 0 = no decode segments */
+  int32_t *buf_begin;  /* [batch] first row of the local buffer */
+  int32_t *seg_begin;  /* [batch] first row of the open segment */
+  float *seg_sum;      /* [batch][n_kv_heads][head_dim] fp32 key sum of the open
+                          segment; may be NULL when buf_cap == 0 */
+  int32_t *status;     /* [1] device status word (kv_status of async errors) */
+} kv_pool;
+
+/* Human-readable name of a status code (static string). */
+const char *kv_status_string(kv_status s);
+
+/* ------------------------------------------------------------------------
+ * Prefill: K-means over each (sequence, KV head)'s keys, then the CSR pack.
+ * LouisKV note, "Key designs" item 2: similar keys are grouped with K-means
+ * and each cluster's centroid, the mean of its keys, is its retrieval index.
+ *
+ * Lloyd's algorithm, exactly `iters` rounds of
+ *   assign: a(x) = argmin_k ||x - c_k||^2, ties to the lowest k, with c_k
+ *           rounded to the storage dtype (bf16 RNE of the fp32 master copy)
+ *           and fp32 accumulation;
+ *   update: c_k = mean of its members (fp32, members summed in key order);
+ *           an empty cluster keeps its previous centroid.
+ * Init: c_k = keys[init_idx[k]]. Then rows are packed cluster by cluster
+ * (stable in key order) into pool->k / pool->v and the unit tables, and the
+ * per-sequence counters are set (n_rows = n_keys, n_units = n_cand =
+ * n_clusters, buf_begin = seg_begin = n_keys, seg_sum = 0).
+ *
+ * keys, values: [batch][n_kv_heads][n_keys][head_dim] in pool->dtype.
+ * init_idx:     [batch][n_kv_heads][n_clusters] distinct indices in
+ *               [0, n_keys) (distinctness is a precondition, not checked).
+ * assign_in:    NULL, or [BH][n_keys] labels in [0, n_clusters): skip Lloyd
+ *               and pack this clustering (centroids = its member means;
+ *               empty clusters take keys[init_idx[k]]).
+ * assign_out:   NULL, or [BH][n_keys]: the final labels.
+ * iters >= 1 unless assign_in is given. n_clusters <= n_keys,
+ * n_keys <= pool->row_cap, n_clusters <= pool->unit_cap.
+ */
+size_t kv_cluster_build_workspace(int32_t batch, int32_t n_kv_heads, int32_t n_keys,
+                                  int32_t head_dim, int32_t n_clusters, kv_dtype dtype);
+kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *values,
+                           int32_t n_keys, int32_t n_clusters, int32_t iters,
+                           const int32_t *init_idx, const int32_t *assign_in,
+                           int32_t *assign_out, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* One Lloyd assignment step (the same kernel kv_cluster_build runs).
+ * keys [n_heads][n_keys][head_dim] (dtype); centroids [n_heads][n_clusters]
+ * [head_dim] fp32 master copies; labels out [n_heads][n_keys] int32.
+ * For KV_BF16 the distance uses bf16(centroid) on the matrix cores. */
+size_t kv_kmeans_assign_workspace(int32_t n_heads, int32_t n_clusters, int32_t head_dim,
+                                  kv_dtype dtype);
+kv_status kv_kmeans_assign(const void *keys, const float *centroids, int32_t n_heads,
+                           int32_t n_keys, int32_t head_dim, int32_t n_clusters,
+                           kv_dtype dtype, int32_t *labels, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* One Lloyd update step: centroids_out[k] = mean of keys labelled k, or
+ * centroids_in[k] when the cluster is empty. counts (nullable) receives the
+ * member counts [n_heads][n_clusters]. centroids_out may alias centroids_in. */
+size_t kv_kmeans_update_workspace(int32_t n_heads, int32_t n_keys, int32_t n_clusters);
+kv_status kv_kmeans_update(const void *keys, const int32_t *labels, const float *centroids_in,
+                           float *centroids_out, int32_t *counts, int32_t n_heads,
+                           int32_t n_keys, int32_t head_dim, int32_t n_clusters,
+                           kv_dtype dtype, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode step 1: the semantic-boundary test. LouisKV note, "Key designs"
+ * item 1 and the flowchart of "Overall framework":
+ *   r = (1/H) * sum_h cos(q_prev^h, q_cur^h) over all n_q_heads heads,
+ *   flag = (r < tau), strict. cos is 0 when either norm is 0.
+ * q_prev NULL means the first decode step: flag = 1 and r = NaN.
+ * q_prev, q_cur: [batch][n_q_heads][head_dim] (dtype). flag: [batch] uint8.
+ * r: NULL or [batch] fp32.
+ */
+kv_status kv_boundary(const void *q_prev, const void *q_cur, int32_t batch, int32_t n_q_heads,
+                      int32_t head_dim, kv_dtype dtype, float tau, uint8_t *flag, float *r,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode step 2 (long-output workloads, pool->buf_cap > 0): temporal
+ * segments and the fixed-size local buffer. LouisKV note, "Key designs"
+ * item 2 (decode half): generated KV is cut at the semantic boundaries into
+ * segments indexed by their key mean; the most recent segments stay in a
+ * fixed-size local buffer and the oldest moves to the pool when it is full.
+ * Per sequence b, in this order:
+ *   1. close the open segment when flag[b] and it is non-empty, or when it
+ *      already holds buf_cap rows: it becomes unit n_units[b] with
+ *      unit_mean = seg_sum / size and unit_index = dtype(unit_mean);
+ *   2. append k_t, v_t as row n_rows[b] and add k_t to seg_sum;
+ *   3. while the buffer [buf_begin, n_rows) holds more than buf_cap rows,
+ *      evict the oldest closed segment: n_cand[b]++ and buf_begin moves past
+ *      it (no data moves; the pool and the buffer share the row store).
+ * k_t, v_t: [batch][n_kv_heads][head_dim] (dtype). flag: [batch] uint8 from
+ * kv_boundary of the same step. Out of rows or units: *pool->status =
+ * KV_ERR_CAPACITY and that sequence's step is skipped.
+ */
+kv_status kv_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
+                            const uint8_t *flag, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode step 3: group-consistent scoring and budgeted selection. LouisKV
+ * note, flowchart (on a boundary, q_t is compared with every unit's centroid
+ * and the Top-B units are fetched) and "Key designs" item 3 (one unit set per
+ * GQA group; batched selection under a token budget over units of variable
+ * size). For every (b, g) with flag[b] != 0 (or flag == NULL):
+ *   s_u = sum over the group's query heads h of q[b][h] . unit_index[b][g][u]
+ *         (fp32) for u < n_cand[b];
+ *   rank non-empty units by (s_u descending, u ascending) and keep the
+ *   longest prefix whose total unit_size is <= budget.
+ * The selected ids are written ascending to sel_units[b][g][0..sel_n), with
+ * sel_n[b][g] and sel_rows[b][g] (total rows). When flag[b] == 0 nothing of
+ * sequence b is touched, so the previous selection is reused.
+ * q: [batch][n_q_heads][head_dim] (dtype). sel_units: [BH][sel_cap] with
+ * sel_cap >= min(budget, unit_cap). scores_out: NULL or [BH][unit_cap] fp32
+ * (entries u >= n_cand[b] untouched).
+ */
+size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads);
+kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
+                    const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
+                    int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode step 4: gather the selected rows and attend. LouisKV note,
+ * flowchart: the retrieved (or reused) critical KV feeds attention. For each
+ * query head h of KV head g:
+ *   out[b][h] = softmax(scale * K_S q[b][h]) V_S   (fp32; 0 if S is empty)
+ * where S = rows of the units sel_units[b][g][0..sel_n[b][g]) followed, when
+ * pool->buf_cap > 0, by the local-buffer rows [buf_begin[b], n_rows[b]).
+ * q: [batch][n_q_heads][head_dim] (dtype). out: [batch][n_q_heads][head_dim]
+ * fp32. max_rows: expected upper bound on selected pool rows per (b, g) (the
+ * budget); it sizes the launch and the workspace, results do not depend on
+ * it. sel_cap <= 4096.
+ */
+size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t max_rows);
+kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
+                           const int32_t *sel_units, int32_t sel_cap, const int32_t *sel_n,
+                           int32_t max_rows, float *out, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

@@ -1,0 +1,279 @@
+"""Centroid-indexed KV-cache retrieval (LouisKV's hot path) on MI355X.
+
+Thin Python binding over ``libkvc.so`` (HIP, gfx950). Every function here
+only marshals arguments -- device pointers of torch tensors, sizes and the
+current HIP stream -- into the C ABI declared in ``include/kvc.h``; all
+computation runs in the library's kernels. Torch supplies device memory and
+streams only. If the library is missing, importing works but every call
+raises ``KvcLibraryMissing``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvc.so")
+
+KV_OK = 0
+KV_ERR_INVALID_ARG = -1
+KV_ERR_UNSUPPORTED = -2
+KV_ERR_WORKSPACE = -3
+KV_ERR_CAPACITY = -4
+KV_ERR_HIP = -5
+
+KV_F32 = 0
+KV_BF16 = 1
+
+EXPORTED = [
+    "kv_status_string",
+    "kv_cluster_build_workspace", "kv_cluster_build",
+    "kv_kmeans_assign_workspace", "kv_kmeans_assign",
+    "kv_kmeans_update_workspace", "kv_kmeans_update",
+    "kv_boundary",
+    "kv_segment_append",
+    "kv_select_workspace", "kv_select",
+    "kv_gather_attend_workspace", "kv_gather_attend",
+]
+
+
+class KvcLibraryMissing(RuntimeError):
+    pass
+
+
+class KvError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)} ({code})")
+        self.code = code
+
+
+class KVPool(ctypes.Structure):
+    """Mirror of ``struct kv_pool`` in kvc.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("row_cap", ctypes.c_int32), ("unit_cap", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("unit_start", ctypes.c_void_p), ("unit_size", ctypes.c_void_p),
+        ("unit_mean", ctypes.c_void_p), ("unit_index", ctypes.c_void_p),
+        ("n_rows", ctypes.c_void_p), ("n_units", ctypes.c_void_p), ("n_cand", ctypes.c_void_p),
+        ("buf_cap", ctypes.c_int32),
+        ("buf_begin", ctypes.c_void_p), ("seg_begin", ctypes.c_void_p),
+        ("seg_sum", ctypes.c_void_p), ("status", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvc.so; raises KvcLibraryMissing if it was never built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KvcLibraryMissing(
+            f"{LIB_PATH} not found: build it with `python -m long_context_kv_kmeans_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    pool_p = ctypes.POINTER(KVPool)
+    sig = {
+        "kv_status_string": (ctypes.c_char_p, [c_int]),
+        "kv_cluster_build_workspace": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
+        "kv_cluster_build": (c_int, [pool_p, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]),
+        "kv_kmeans_assign_workspace": (c_size, [c_int, c_int, c_int, c_int]),
+        "kv_kmeans_assign": (c_int, [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp, c_size, vp]),
+        "kv_kmeans_update_workspace": (c_size, [c_int, c_int, c_int]),
+        "kv_kmeans_update": (c_int, [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp,
+                                     c_size, vp]),
+        "kv_boundary": (c_int, [vp, vp, c_int, c_int, c_int, c_int, ctypes.c_float, vp, vp, vp]),
+        "kv_segment_append": (c_int, [pool_p, vp, vp, vp, vp]),
+        "kv_select_workspace": (c_size, [pool_p, c_int]),
+        "kv_select": (c_int, [pool_p, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, c_size, vp]),
+        "kv_gather_attend_workspace": (c_size, [pool_p, c_int, c_int]),
+        "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, c_int, vp, c_int, vp,
+                                     vp, c_size, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    try:
+        return lib().kv_status_string(code).decode()
+    except KvcLibraryMissing:
+        return str(code)
+
+
+def _check(fn: str, code: int) -> None:
+    if code != KV_OK:
+        raise KvError(fn, code)
+
+
+# ---------------------------------------------------------------- marshalling
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KV_BF16
+    if t == torch.float32:
+        return KV_F32
+    raise ValueError(f"unsupported element type {t}")
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == KV_BF16 else torch.float32
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Zero-filled device workspace of at least ``nbytes`` (256-byte aligned)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Pool:
+    """Device tensors behind one ``kv_pool`` (see kvc.h for the layout)."""
+
+    batch: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: torch.dtype
+    row_cap: int
+    unit_cap: int
+    buf_cap: int = 0
+    device: str = "cuda"
+
+    def __post_init__(self):
+        B, H, D = self.batch, self.n_kv_heads, self.head_dim
+        dev, i32 = self.device, torch.int32
+        self.k = torch.zeros(B, H, self.row_cap, D, dtype=self.dtype, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.unit_start = torch.zeros(B, H, self.unit_cap, dtype=i32, device=dev)
+        self.unit_size = torch.zeros(B, H, self.unit_cap, dtype=i32, device=dev)
+        self.unit_mean = torch.zeros(B, H, self.unit_cap, D, dtype=torch.float32, device=dev)
+        self.unit_index = torch.zeros(B, H, self.unit_cap, D, dtype=self.dtype, device=dev)
+        self.n_rows = torch.zeros(B, dtype=i32, device=dev)
+        self.n_units = torch.zeros(B, dtype=i32, device=dev)
+        self.n_cand = torch.zeros(B, dtype=i32, device=dev)
+        self.buf_begin = torch.zeros(B, dtype=i32, device=dev)
+        self.seg_begin = torch.zeros(B, dtype=i32, device=dev)
+        self.seg_sum = (torch.zeros(B, H, D, dtype=torch.float32, device=dev)
+                        if self.buf_cap > 0 else None)
+        self.status = torch.zeros(1, dtype=i32, device=dev)
+        self._struct = None
+
+    def struct(self) -> KVPool:
+        if self._struct is None:
+            p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+            self._struct = KVPool(
+                self.batch, self.n_kv_heads, self.head_dim, dtype_code(self.dtype),
+                self.row_cap, self.unit_cap, p(self.k), p(self.v), p(self.unit_start),
+                p(self.unit_size), p(self.unit_mean), p(self.unit_index), p(self.n_rows),
+                p(self.n_units), p(self.n_cand), self.buf_cap, p(self.buf_begin),
+                p(self.seg_begin), p(self.seg_sum), p(self.status))
+        return self._struct
+
+    def ref(self):
+        return ctypes.byref(self.struct())
+
+
+# ---------------------------------------------------------------- K-means
+def kv_cluster_build_workspace(batch, n_kv_heads, n_keys, head_dim, n_clusters, dtype) -> int:
+    return lib().kv_cluster_build_workspace(batch, n_kv_heads, n_keys, head_dim, n_clusters,
+                                            dtype_code(dtype))
+
+
+def kv_cluster_build(pool: Pool, keys, values, n_clusters: int, iters: int, init_idx,
+                     assign_in=None, assign_out=None, ws=None, stream=None) -> None:
+    B, H, N, D = keys.shape
+    if ws is None:
+        ws = workspace(kv_cluster_build_workspace(B, H, N, D, n_clusters, keys.dtype))
+    _check("kv_cluster_build", lib().kv_cluster_build(
+        pool.ref(), _ptr(keys), _ptr(values), N, n_clusters, iters, _ptr(init_idx),
+        _ptr(assign_in), _ptr(assign_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kv_kmeans_assign(keys, centroids, labels, ws=None, stream=None) -> None:
+    """keys [BH, N, D]; centroids [BH, C, D] fp32; labels [BH, N] int32."""
+    BH, N, D = keys.shape
+    C = centroids.shape[1]
+    dt = dtype_code(keys.dtype)
+    if ws is None:
+        ws = workspace(lib().kv_kmeans_assign_workspace(BH, C, D, dt))
+    _check("kv_kmeans_assign", lib().kv_kmeans_assign(
+        _ptr(keys), _ptr(centroids), BH, N, D, C, dt, _ptr(labels), _ptr(ws), ws.numel(),
+        _stream(stream)))
+
+
+def kv_kmeans_update(keys, labels, centroids_in, centroids_out, counts=None, ws=None,
+                     stream=None) -> None:
+    BH, N, D = keys.shape
+    C = centroids_in.shape[1]
+    if ws is None:
+        ws = workspace(lib().kv_kmeans_update_workspace(BH, N, C))
+    _check("kv_kmeans_update", lib().kv_kmeans_update(
+        _ptr(keys), _ptr(labels), _ptr(centroids_in), _ptr(centroids_out), _ptr(counts), BH, N,
+        D, C, dtype_code(keys.dtype), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- decode
+def kv_boundary(q_prev, q_cur, tau: float, flag, r=None, stream=None) -> None:
+    B, Hq, D = q_cur.shape
+    _check("kv_boundary", lib().kv_boundary(
+        _ptr(q_prev), _ptr(q_cur), B, Hq, D, dtype_code(q_cur.dtype), float(tau), _ptr(flag),
+        _ptr(r), _stream(stream)))
+
+
+def kv_segment_append(pool: Pool, k_t, v_t, flag, stream=None) -> None:
+    _check("kv_segment_append", lib().kv_segment_append(
+        pool.ref(), _ptr(k_t), _ptr(v_t), _ptr(flag), _stream(stream)))
+
+
+def kv_select_workspace(pool: Pool, n_q_heads: int) -> int:
+    return lib().kv_select_workspace(pool.ref(), n_q_heads)
+
+
+def kv_select(pool: Pool, q, budget: int, flag, sel_units, sel_n, sel_rows, scores_out=None,
+              ws=None, stream=None) -> None:
+    Hq = q.shape[1]
+    if ws is None:
+        ws = workspace(kv_select_workspace(pool, Hq))
+    _check("kv_select", lib().kv_select(
+        pool.ref(), _ptr(q), Hq, int(budget), _ptr(flag), _ptr(sel_units), sel_units.shape[-1],
+        _ptr(sel_n), _ptr(sel_rows), _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kv_gather_attend_workspace(pool: Pool, n_q_heads: int, max_rows: int) -> int:
+    return lib().kv_gather_attend_workspace(pool.ref(), n_q_heads, max_rows)
+
+
+def kv_gather_attend(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: int, out,
+                     ws=None, stream=None) -> None:
+    Hq = q.shape[1]
+    if ws is None:
+        ws = workspace(kv_gather_attend_workspace(pool, Hq, max_rows))
+    _check("kv_gather_attend", lib().kv_gather_attend(
+        pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n),
+        int(max_rows), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -1,0 +1,238 @@
+// C ABI of libkvc: argument validation on the host, workspace carving and
+// kernel composition. Every entry point validates before touching HIP, so
+// argument errors are reported without a device.
+#include "kvc_internal.hpp"
+
+using namespace kvc;
+
+namespace {
+
+bool dims_ok(int d) { return d == 64 || d == 128; }
+bool dtype_ok(int dt) { return dt == KV_F32 || dt == KV_BF16; }
+bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+kv_status check_pool(const kv_pool *p) {
+  if (!p) return KV_ERR_INVALID_ARG;
+  if (p->batch <= 0 || p->n_kv_heads <= 0 || p->row_cap <= 0 || p->unit_cap <= 0)
+    return KV_ERR_INVALID_ARG;
+  if (!dtype_ok(p->dtype) || !dims_ok(p->head_dim)) return KV_ERR_UNSUPPORTED;
+  if (!p->k || !p->v || !p->unit_start || !p->unit_size || !p->unit_mean || !p->unit_index ||
+      !p->n_rows || !p->n_units || !p->n_cand || !p->buf_begin || !p->seg_begin || !p->status)
+    return KV_ERR_INVALID_ARG;
+  if (p->buf_cap < 0) return KV_ERR_INVALID_ARG;
+  if (p->buf_cap > 0 && !p->seg_sum) return KV_ERR_INVALID_ARG;
+  return KV_OK;
+}
+
+size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_cent,
+                         size_t *off_labels, size_t *off_assign, size_t *off_update) {
+  size_t o = 0;
+  *off_cent = o;
+  o += align_up((size_t)bh * c * d * sizeof(float), 256);
+  *off_labels = o;
+  o += align_up((size_t)bh * n * sizeof(int32_t), 256);
+  *off_assign = o;
+  o += assign_ws_bytes(bh, c, d, dt);
+  *off_update = o;
+  o += update_ws_bytes(bh, n, c);
+  return o;
+}
+
+constexpr int kMaxClusters = 32768;  // label histogram of one chunk lives in LDS
+
+}  // namespace
+
+extern "C" {
+
+const char *kv_status_string(kv_status s) {
+  switch (s) {
+    case KV_OK: return "KV_OK";
+    case KV_ERR_INVALID_ARG: return "KV_ERR_INVALID_ARG";
+    case KV_ERR_UNSUPPORTED: return "KV_ERR_UNSUPPORTED";
+    case KV_ERR_WORKSPACE: return "KV_ERR_WORKSPACE";
+    case KV_ERR_CAPACITY: return "KV_ERR_CAPACITY";
+    case KV_ERR_HIP: return "KV_ERR_HIP";
+  }
+  return "KV_ERR_UNKNOWN";
+}
+
+// ---------------------------------------------------------------- K-means steps
+size_t kv_kmeans_assign_workspace(int32_t n_heads, int32_t n_clusters, int32_t head_dim,
+                                  kv_dtype dtype) {
+  if (n_heads <= 0 || n_clusters <= 0 || !dims_ok(head_dim) || !dtype_ok(dtype)) return 0;
+  return assign_ws_bytes(n_heads, n_clusters, head_dim, dtype);
+}
+
+kv_status kv_kmeans_assign(const void *keys, const float *centroids, int32_t n_heads,
+                           int32_t n_keys, int32_t head_dim, int32_t n_clusters, kv_dtype dtype,
+                           int32_t *labels, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!keys || !centroids || !labels) return KV_ERR_INVALID_ARG;
+  if (n_heads <= 0 || n_keys <= 0 || n_clusters <= 0) return KV_ERR_INVALID_ARG;
+  if (!dims_ok(head_dim) || !dtype_ok(dtype)) return KV_ERR_UNSUPPORTED;
+  if (n_clusters > kMaxClusters) return KV_ERR_UNSUPPORTED;
+  if (!ws || !aligned256(ws) || ws_bytes < assign_ws_bytes(n_heads, n_clusters, head_dim, dtype))
+    return KV_ERR_WORKSPACE;
+  return launch_assign(keys, centroids, n_heads, n_keys, head_dim, n_clusters, dtype, labels, ws,
+                       stream);
+}
+
+size_t kv_kmeans_update_workspace(int32_t n_heads, int32_t n_keys, int32_t n_clusters) {
+  if (n_heads <= 0 || n_keys <= 0 || n_clusters <= 0) return 0;
+  return update_ws_bytes(n_heads, n_keys, n_clusters);
+}
+
+kv_status kv_kmeans_update(const void *keys, const int32_t *labels, const float *centroids_in,
+                           float *centroids_out, int32_t *counts, int32_t n_heads, int32_t n_keys,
+                           int32_t head_dim, int32_t n_clusters, kv_dtype dtype, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!keys || !labels || !centroids_in || !centroids_out) return KV_ERR_INVALID_ARG;
+  if (n_heads <= 0 || n_keys <= 0 || n_clusters <= 0) return KV_ERR_INVALID_ARG;
+  if (!dims_ok(head_dim) || !dtype_ok(dtype)) return KV_ERR_UNSUPPORTED;
+  if (n_clusters > kMaxClusters) return KV_ERR_UNSUPPORTED;
+  if (!ws || !aligned256(ws) || ws_bytes < update_ws_bytes(n_heads, n_keys, n_clusters))
+    return KV_ERR_WORKSPACE;
+  return launch_update(keys, labels, centroids_in, centroids_out, counts, n_heads, n_keys,
+                       head_dim, n_clusters, dtype, ws, stream, nullptr, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------- cluster build
+size_t kv_cluster_build_workspace(int32_t batch, int32_t n_kv_heads, int32_t n_keys,
+                                  int32_t head_dim, int32_t n_clusters, kv_dtype dtype) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_keys <= 0 || n_clusters <= 0 || !dims_ok(head_dim) ||
+      !dtype_ok(dtype))
+    return 0;
+  size_t a, b, c, d;
+  return cluster_ws_layout(batch * n_kv_heads, n_keys, head_dim, n_clusters, dtype, &a, &b, &c,
+                           &d);
+}
+
+kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *values,
+                           int32_t n_keys, int32_t n_clusters, int32_t iters,
+                           const int32_t *init_idx, const int32_t *assign_in, int32_t *assign_out,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  if (!keys || !values || !init_idx) return KV_ERR_INVALID_ARG;
+  if (n_keys <= 0 || n_clusters <= 0 || n_clusters > n_keys) return KV_ERR_INVALID_ARG;
+  if (!assign_in && iters < 1) return KV_ERR_INVALID_ARG;
+  if (n_clusters > kMaxClusters) return KV_ERR_UNSUPPORTED;
+  if (n_keys > pool->row_cap || n_clusters > pool->unit_cap) return KV_ERR_CAPACITY;
+  const int bh = pool->batch * pool->n_kv_heads, d = pool->head_dim;
+  const kv_dtype dt = (kv_dtype)pool->dtype;
+  size_t o_cent, o_lab, o_asg, o_upd;
+  const size_t need = cluster_ws_layout(bh, n_keys, d, n_clusters, dt, &o_cent, &o_lab, &o_asg,
+                                        &o_upd);
+  if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  float *cent = reinterpret_cast<float *>(w + o_cent);
+  int32_t *labels = assign_out ? assign_out : reinterpret_cast<int32_t *>(w + o_lab);
+  void *asg_ws = w + o_asg;
+  void *upd_ws = w + o_upd;
+
+  st = launch_init_centroids(keys, init_idx, cent, bh, n_keys, n_clusters, d, dt, stream);
+  if (st != KV_OK) return st;
+  const int32_t *perm = nullptr, *start = nullptr, *tot = nullptr;
+  if (assign_in) {
+    st = launch_update(keys, assign_in, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt, upd_ws,
+                       stream, &perm, &start, &tot);
+    if (st != KV_OK) return st;
+    if (assign_out && assign_out != assign_in)
+      if (hipMemcpyAsync(assign_out, assign_in, (size_t)bh * n_keys * 4, hipMemcpyDeviceToDevice,
+                         stream) != hipSuccess)
+        return KV_ERR_HIP;
+  } else {
+    for (int it = 0; it < iters; ++it) {
+      st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream);
+      if (st != KV_OK) return st;
+      st = launch_update(keys, labels, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt, upd_ws,
+                         stream, &perm, &start, &tot);
+      if (st != KV_OK) return st;
+    }
+  }
+  return launch_pack(pool, keys, values, cent, perm, start, tot, n_keys, n_clusters, stream);
+}
+
+// ---------------------------------------------------------------- decode
+kv_status kv_boundary(const void *q_prev, const void *q_cur, int32_t batch, int32_t n_q_heads,
+                      int32_t head_dim, kv_dtype dtype, float tau, uint8_t *flag, float *r,
+                      hipStream_t stream) {
+  if (!q_cur || !flag) return KV_ERR_INVALID_ARG;
+  if (batch <= 0 || n_q_heads <= 0) return KV_ERR_INVALID_ARG;
+  if (!dims_ok(head_dim) || !dtype_ok(dtype)) return KV_ERR_UNSUPPORTED;
+  if (tau != tau) return KV_ERR_INVALID_ARG;
+  return launch_boundary(q_prev, q_cur, batch, n_q_heads, head_dim, dtype, tau, flag, r, stream);
+}
+
+kv_status kv_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
+                            const uint8_t *flag, hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  if (!k_t || !v_t || !flag) return KV_ERR_INVALID_ARG;
+  if (pool->buf_cap <= 0) return KV_ERR_INVALID_ARG;
+  return launch_segment_append(pool, k_t, v_t, flag, stream);
+}
+
+size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads) {
+  if (check_pool(pool) != KV_OK || n_q_heads <= 0) return 0;
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  return align_up(bh * sizeof(int32_t), 256) + align_up(bh * pool->unit_cap * sizeof(float), 256);
+}
+
+kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
+                    const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
+                    int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  if (!q || !sel_units || !sel_n || !sel_rows) return KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || budget < 0 || sel_cap <= 0)
+    return KV_ERR_INVALID_ARG;
+  const int G = n_q_heads / pool->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  if (sel_cap < (budget < pool->unit_cap ? budget : pool->unit_cap)) return KV_ERR_CAPACITY;
+  const size_t need = kv_select_workspace(pool, n_q_heads);
+  if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  int32_t *counters = static_cast<int32_t *>(ws);
+  float *scores = scores_out ? scores_out
+                             : reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                                         align_up(bh * sizeof(int32_t), 256));
+  return launch_select(pool, q, n_q_heads, budget, flag, sel_units, sel_cap, sel_n, sel_rows,
+                       scores, counters, stream);
+}
+
+size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t max_rows) {
+  if (check_pool(pool) != KV_OK || n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 ||
+      max_rows < 0)
+    return 0;
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  const size_t G = (size_t)(n_q_heads / pool->n_kv_heads);
+  const size_t ns = (size_t)attend_num_splits(pool, max_rows);
+  return align_up(bh * sizeof(int32_t), 256) +
+         align_up(bh * ns * G * (pool->head_dim + 2) * sizeof(float), 256);
+}
+
+kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
+                           const int32_t *sel_units, int32_t sel_cap, const int32_t *sel_n,
+                           int32_t max_rows, float *out, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  if (!q || !sel_units || !sel_n || !out) return KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || sel_cap <= 0 || max_rows < 0)
+    return KV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return KV_ERR_INVALID_ARG;
+  const int G = n_q_heads / pool->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
+  const size_t need = kv_gather_attend_workspace(pool, n_q_heads, max_rows);
+  if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  int32_t *counters = static_cast<int32_t *>(ws);
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                              align_up(bh * sizeof(int32_t), 256));
+  return launch_gather_attend(pool, q, n_q_heads, scale, sel_units, sel_cap, sel_n,
+                              attend_num_splits(pool, max_rows), out, partials, counters, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Internal helpers shared by the HIP translation units of libkvc (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kMaxSel = 4096; // selected units staged in LDS by the attend kernel
+
+// bf16 is carried as raw uint16_t bits.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float to_f32(float x) { return x; }
+  __device__ __forceinline__ static float from_f32(float x) { return x; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+  __device__ __forceinline__ static uint16_t from_f32(float x) { return f32_to_bf16_rne(x); }
+};
+
+// Unpack one 16-byte vector of elements into fp32 values.
+template <typename T> __device__ __forceinline__ void unpack16(const uint4 &v, float *out);
+template <> __device__ __forceinline__ void unpack16<float>(const uint4 &v, float *out) {
+  out[0] = __uint_as_float(v.x);
+  out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z);
+  out[3] = __uint_as_float(v.w);
+}
+template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4 &v, float *out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Map a hardware workgroup id to a logical one so that each XCD (which
+// receives ids x, x+8, x+16, ...) processes one contiguous range of logical
+// work; neighbouring logical blocks then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int hw_id, int total) {
+  const int per = total / kNumXcd, rem = total % kNumXcd;
+  const int xcd = hw_id % kNumXcd, j = hw_id / kNumXcd;
+  return (xcd < rem) ? xcd * (per + 1) + j : rem * (per + 1) + (xcd - rem) * per + j;
+}
+
+// Orderable key of a float: larger float -> larger unsigned (-0 folded to +0).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace kvc
+
+// Host-side launchers (defined in the .hip files, used by api.hip).
+namespace kvc {
+
+// K-means
+kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
+                                int n, int c, int d, kv_dtype dt, hipStream_t s);
+size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt);
+kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
+                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s);
+size_t update_ws_bytes(int bh, int n, int c);
+kv_status launch_update(const void *keys, const int32_t *labels, const float *cent_in,
+                        float *cent_out, int32_t *counts, int bh, int n, int d, int c,
+                        kv_dtype dt, void *ws, hipStream_t s,
+                        const int32_t **perm_out, const int32_t **start_out,
+                        const int32_t **tot_out);
+kv_status launch_pack(const kv_pool *pool, const void *keys, const void *values,
+                      const float *cent, const int32_t *perm, const int32_t *start,
+                      const int32_t *tot, int n, int c, hipStream_t s);
+
+// Decode
+kv_status launch_boundary(const void *q_prev, const void *q_cur, int batch, int hq, int d,
+                          kv_dtype dt, float tau, uint8_t *flag, float *r, hipStream_t s);
+kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
+                                const uint8_t *flag, hipStream_t s);
+int select_num_blocks(const kv_pool *pool);
+kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
+                        const uint8_t *flag, int32_t *sel_units, int sel_cap, int32_t *sel_n,
+                        int32_t *sel_rows, float *scores, int32_t *counters, hipStream_t s);
+int attend_num_splits(const kv_pool *pool, int max_rows);
+kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
+                               const int32_t *sel_units, int sel_cap, const int32_t *sel_n,
+                               int nsplit, float *out, float *partials, int32_t *counters,
+                               hipStream_t s);
+
+}  // namespace kvc

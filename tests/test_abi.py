@@ -1,0 +1,151 @@
+"""The C-ABI library: it loads on a CPU-only host, exports every function that
+include/kvc.h declares, and rejects bad arguments synchronously before any
+HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_kv_kmeans_amd as kvc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvc.LIB_PATH),
+                                reason="libkvc.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kvc.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    L = kvc.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code, name in [(0, "KV_OK"), (-1, "KV_ERR_INVALID_ARG"), (-2, "KV_ERR_UNSUPPORTED"),
+                       (-3, "KV_ERR_WORKSPACE"), (-4, "KV_ERR_CAPACITY"), (-5, "KV_ERR_HIP")]:
+        assert kvc.status_string(code) == name
+
+
+def _fake_pool(**kw):
+    # Non-null dummy addresses: validation only inspects them, never dereferences.
+    a = 0x10000
+    p = kvc.KVPool(kw.get("batch", 1), kw.get("n_kv_heads", 8), kw.get("head_dim", 128),
+                   kw.get("dtype", kvc.KV_BF16), kw.get("row_cap", 4096), kw.get("unit_cap", 256),
+                   a, a, a, a, a, a, a, a, a, kw.get("buf_cap", 0), a, a,
+                   kw.get("seg_sum", None), a)
+    return p
+
+
+def test_boundary_validation():
+    L = kvc.lib()
+    f = ctypes.c_float(0.7)
+    a = ctypes.c_void_p(0x10000)
+    assert L.kv_boundary(None, None, 1, 4, 64, 0, f, a, None, None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_boundary(None, a, 0, 4, 64, 0, f, a, None, None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_boundary(None, a, 1, 4, 96, 0, f, a, None, None) == kvc.KV_ERR_UNSUPPORTED
+    assert L.kv_boundary(None, a, 1, 4, 64, 7, f, a, None, None) == kvc.KV_ERR_UNSUPPORTED
+    assert L.kv_boundary(None, a, 1, 4, 64, 0, ctypes.c_float(float("nan")), a, None,
+                         None) == kvc.KV_ERR_INVALID_ARG
+
+
+def test_pool_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x10000)  # 256-aligned dummy
+    p = _fake_pool(head_dim=96)
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_UNSUPPORTED
+    p = _fake_pool(batch=0)
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_INVALID_ARG
+    p = _fake_pool()
+    # query heads not a multiple of KV heads
+    assert L.kv_select(ctypes.byref(p), a, 30, 512, None, a, 512, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_INVALID_ARG
+    # negative budget
+    assert L.kv_select(ctypes.byref(p), a, 32, -1, None, a, 512, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_INVALID_ARG
+    # selection capacity below min(budget, unit_cap)
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 100, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_CAPACITY
+    # workspace too small / misaligned
+    assert L.kv_select(ctypes.byref(p), a, 32, 128, None, a, 256, a, a, None, ws, 16,
+                       None) == kvc.KV_ERR_WORKSPACE
+    assert L.kv_select(ctypes.byref(p), a, 32, 128, None, a, 256, a, a, None,
+                       ctypes.c_void_p(0x10004), 1 << 30, None) == kvc.KV_ERR_WORKSPACE
+    # group size 3 unsupported
+    p3 = _fake_pool(n_kv_heads=2)
+    assert L.kv_select(ctypes.byref(p3), a, 6, 128, None, a, 256, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_UNSUPPORTED
+    # segments need a local buffer and seg_sum
+    assert L.kv_segment_append(ctypes.byref(p), a, a, a, None) == kvc.KV_ERR_INVALID_ARG
+    pb = _fake_pool(buf_cap=16)  # seg_sum NULL
+    assert L.kv_segment_append(ctypes.byref(pb), a, a, a, None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_select(None, a, 32, 128, None, a, 256, a, a, None, ws, 1 << 30,
+                       None) == kvc.KV_ERR_INVALID_ARG
+
+
+def test_attend_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    p = _fake_pool()
+    need = L.kv_gather_attend_workspace(ctypes.byref(p), 32, 512)
+    assert need > 0
+    assert L.kv_gather_attend(ctypes.byref(p), a, 32, ctypes.c_float(0.1), a, 5000, a, 512, a, a,
+                              need, None) == kvc.KV_ERR_UNSUPPORTED  # sel_cap > 4096
+    assert L.kv_gather_attend(ctypes.byref(p), a, 32, ctypes.c_float(0.1), a, 512, a, 512, a, a,
+                              need - 1, None) == kvc.KV_ERR_WORKSPACE
+    assert L.kv_gather_attend(ctypes.byref(p), None, 32, ctypes.c_float(0.1), a, 512, a, 512, a,
+                              a, need, None) == kvc.KV_ERR_INVALID_ARG
+
+
+def test_cluster_build_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    p = _fake_pool(row_cap=1000, unit_cap=64)
+    ws_need = L.kv_cluster_build_workspace(1, 8, 1000, 128, 64, kvc.KV_BF16)
+    assert ws_need > 0
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 65, 10, a, None, None, a, ws_need,
+                              None) == kvc.KV_ERR_CAPACITY  # clusters > unit_cap
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1001, 64, 10, a, None, None, a, ws_need,
+                              None) == kvc.KV_ERR_CAPACITY  # keys > row_cap
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 50, 64, 10, a, None, None, a, ws_need,
+                              None) == kvc.KV_ERR_INVALID_ARG  # clusters > keys
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 0, a, None, None, a, ws_need,
+                              None) == kvc.KV_ERR_INVALID_ARG  # no iterations, no labels
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 10, None, None, None, a, ws_need,
+                              None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 10, a, None, None, a, ws_need - 1,
+                              None) == kvc.KV_ERR_WORKSPACE
+    assert L.kv_kmeans_assign(a, a, 8, 1000, 128, 40000, kvc.KV_BF16, a, a, 1 << 30,
+                              None) == kvc.KV_ERR_UNSUPPORTED  # too many clusters
+    assert L.kv_kmeans_update(a, a, a, a, None, 8, 1000, 128, 64, kvc.KV_BF16, a, 10,
+                              None) == kvc.KV_ERR_WORKSPACE
+
+
+def test_workspace_sizes_scale():
+    L = kvc.lib()
+    small = L.kv_cluster_build_workspace(1, 8, 32768, 128, 2048, kvc.KV_BF16)
+    big = L.kv_cluster_build_workspace(1, 8, 131072, 128, 8192, kvc.KV_BF16)
+    assert 0 < small < big < 256 << 20
+    assert L.kv_cluster_build_workspace(0, 8, 10, 128, 2, 1) == 0
+
+
+def test_product_path_has_no_oracle_dependency():
+    root = os.path.dirname(os.path.abspath(kvc.__file__))
+    for dirpath, _, files in os.walk(root):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

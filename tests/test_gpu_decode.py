@@ -1,0 +1,113 @@
+"""GPU parity: whole decode loops (boundary -> [segments] -> select -> attend).
+
+LouisKV note, overall-framework flowchart and key designs 1-3. The GPU pool
+is packed from the oracle's clustering with the oracle's index vectors, then
+both sides run the same seeded query walk:
+  * flags bit-exact at every step;
+  * segment bookkeeping (long-output config) bit-exact: row/unit counters,
+    buffer start, segment start/size;
+  * selected unit sets equal the oracle's (near-ties within the fp32 score
+    error are counted and must be 0 here);
+  * attention output within 2e-3 of exact attention over the GPU's selection
+    (which equals the oracle's when the sets agree).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import attend as oat
+from oracle.decode import run_decode, unit_rows
+from tests.gpu_util import gpu_decode, max_rel_err, oracle_clustering, oracle_packs, \
+    pool_from_labels, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _run(cfg, steps, seqs, compare_every=1):
+    inp = wl.layer_inputs(cfg, 0, seqs=seqs)
+    B, H, N, d = inp["keys"].shape
+    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    q, _ = wl.layer_queries(cfg, 0, steps=steps, seqs=seqs)
+    dk = dv = None
+    extra_rows, n_units = 0, cfg.n_clusters
+    if cfg.buf_cap > 0:
+        dk, dv = wl.layer_decode_kv(cfg, 0, steps=steps, seqs=seqs)
+        extra_rows, n_units = steps, cfg.n_clusters + steps
+    pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                                  n_units=n_units, buf_cap=cfg.buf_cap, extra_rows=extra_rows)
+    sel_cap = min(cfg.budget, n_units)
+    rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                     dec_k=None if dk is None else to_dev(dk, cfg.dtype),
+                     dec_v=None if dv is None else to_dev(dv, cfg.dtype))
+    flags = rec.flag.cpu().numpy().astype(bool)
+    out = rec.out.cpu().numpy()
+    sel_n = rec.sel_n.cpu().numpy()
+    sel = rec.sel.cpu().numpy()
+    counters = rec.counters.cpu().numpy()
+    G = cfg.group
+    stats = {"retrievals": 0, "set_mismatch": 0, "max_err": 0.0}
+    for bi in range(B):
+        packs = oracle_packs(inp["keys"], inp["values"], labels, cents, cfg.dtype, bi)
+        log, opool = run_decode(packs, q[:, bi], cfg.tau, cfg.budget, cfg.scale, cfg.dtype,
+                                buf_cap=cfg.buf_cap,
+                                dec_k=None if dk is None else dk[:, bi],
+                                dec_v=None if dv is None else dv[:, bi])
+        for t, e in enumerate(log):
+            assert flags[t, bi] == e["flag"], (t, bi)
+            if cfg.buf_cap > 0:
+                assert counters[t, :, bi].tolist() == [e["n_rows"], cfg.n_clusters + len(
+                    [s for s in opool.seg.seg_start if s < e["seg_begin"]]), e["n_cand"],
+                    e["buf_begin"], e["seg_begin"]], t
+            stats["retrievals"] += int(e["flag"])
+            if t % compare_every and not e["flag"]:
+                continue
+            for g in range(H):
+                got = sel[t, bi, g, :sel_n[t, bi, g]]
+                if not np.array_equal(got, e["sel"][g]):
+                    stats["set_mismatch"] += 1
+                start, size, _ = opool.unit_table(g)
+                rows = unit_rows(start, size, got)
+                if cfg.buf_cap > 0:
+                    rows = np.concatenate([rows, np.arange(e["buf_begin"], e["n_rows"])])
+                K, V = opool.rows(g, rows)
+                ref = oat.attend_exact(q[t, bi, g * G:(g + 1) * G], K, V, cfg.scale)
+                err = max_rel_err(out[t, bi, g * G:(g + 1) * G], ref)
+                stats["max_err"] = max(stats["max_err"], err)
+                assert err <= TOL, (t, bi, g, err)
+        if cfg.buf_cap > 0:
+            # segment tables: ids C.. in closing order, bit-exact rows
+            st = opool.seg
+            ns = len(st.seg_start)
+            us = pool.unit_start[bi, 0, cfg.n_clusters:cfg.n_clusters + ns].cpu().numpy()
+            uz = pool.unit_size[bi, 0, cfg.n_clusters:cfg.n_clusters + ns].cpu().numpy()
+            assert us.tolist() == st.seg_start and uz.tolist() == st.seg_size
+            um = pool.unit_mean[bi, :, cfg.n_clusters:cfg.n_clusters + ns].cpu().numpy()
+            om = np.stack(st.seg_mean, axis=1)  # [H, ns, d]
+            assert np.abs(um - om).max() <= 1e-5 * max(1.0, np.abs(om).max())
+    print(stats)
+    assert stats["set_mismatch"] == 0
+    return stats
+
+
+@pytest.mark.parametrize("cfg_idx,over,steps,seqs", [
+    (0, {}, 64, [0]),
+    (1, dict(n_keys=8192, n_clusters=512, n_components=128, iters=3), 96, [0]),
+    (4, dict(n_keys=4096, n_clusters=256, n_components=64, iters=3), 48, [0, 5]),
+])
+def test_decode_loop_parity(cfg_idx, over, steps, seqs):
+    cfg = wl.get_config(cfg_idx, **over)
+    st = _run(cfg, steps, seqs)
+    assert st["retrievals"] >= 1
+
+
+def test_decode_long_output_segments_small_buffer():
+    # long-output config with a small buffer so eviction and forced closes occur often
+    cfg = wl.get_config(2, buf_cap=64, steps=600, p_jump=0.05, budget=256, iters=3)
+    _run(cfg, cfg.steps, [0])
+
+
+def test_decode_long_output_segments():
+    cfg = wl.get_config(2, iters=3)
+    _run(cfg, 3000, [0], compare_every=7)
