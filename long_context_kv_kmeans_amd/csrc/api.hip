@@ -141,11 +141,19 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
                          stream) != hipSuccess)
         return KV_ERR_HIP;
   } else {
-    for (int it = 0; it < iters; ++it) {
-      st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream);
+    // bf16: the first round's fragments come from the init centroids; later
+    // rounds get theirs from the update kernel that produced the centroids.
+    const bool fused = dt == KV_BF16;
+    if (fused) {
+      st = launch_prep_frags(cent, bh, d, n_clusters, asg_ws, stream);
       if (st != KV_OK) return st;
+    }
+    for (int it = 0; it < iters; ++it) {
+      st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream, fused);
+      if (st != KV_OK) return st;
+      void *next_frags = (fused && it + 1 < iters) ? asg_ws : nullptr;
       st = launch_update(keys, labels, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt, upd_ws,
-                         stream, &perm, &start, &tot);
+                         stream, &perm, &start, &tot, next_frags);
       if (st != KV_OK) return st;
     }
   }

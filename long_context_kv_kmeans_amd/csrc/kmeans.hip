@@ -20,7 +20,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kAssignKeysPerWave = 64;                   // two 32-key MFMA column blocks
 constexpr int kAssignWaves = 4;
 constexpr int kAssignKeysPerBlock = kAssignKeysPerWave * kAssignWaves;
-constexpr int kTilesPerStage = 2;                        // 64 centroids per LDS stage
+constexpr int kTilesPerStage = 4;                        // 128 centroids per LDS stage
 constexpr int kRankChunk = 1024;                         // keys per counting-sort chunk
 
 // ---------------------------------------------------------------- init
@@ -53,69 +53,102 @@ kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float
 // Centroid fragments for v_mfma_f32_32x32x16_bf16 with centroids as the A
 // operand (32 rows x 16 k per instruction): for tile t, k-step s and lane l,
 // the lane holds row m = l % 32 and k = 16 s + 8 (l / 32) + j, j = 0..7.
-// The last k-step carries the bias: for lanes l < 32, k = D..D+2 hold
-// -(hi, mid, lo) with hi + mid + lo = |c^|^2 / 2 split into three bf16 parts
-// (about 24 significant bits), while the keys' matching entries are 1.0, so
-// the MFMA accumulates x . c^ - |c^|^2 / 2 directly. Padding rows (k >= C)
-// get a bias of -3.39e38 and never win.
+// One extra k-step carries the norms so the matrix cores accumulate
+//   x . c^ - |c^|^2 / 2 - |x|^2 / 2 = -|x - c^|^2 / 2:
+// for lanes l < 32 the centroid side holds (-hc, -mc, -lc, 1, 1, 1, 0, 0) and
+// the key side (1, 1, 1, -hx, -mx, -lx, 0, 0), where h + m + l splits a half
+// squared norm into three bf16 parts (about 24 significant bits). Padding rows
+// (k >= C) carry -3.39e38 instead of their norm and are also masked out.
+constexpr uint32_t kBf16One = 0x3f80u;
+constexpr uint32_t kBf16NegMax = 0xff7fu;  // -3.39e38
+
+__device__ __forceinline__ void split3_neg(float v, uint32_t *h, uint32_t *m, uint32_t *l) {
+  const uint16_t a = f32_to_bf16_rne(v);
+  const float r1 = v - bf16_bits_to_f32(a);
+  const uint16_t b = f32_to_bf16_rne(r1);
+  const float r2 = r1 - bf16_bits_to_f32(b);
+  const uint16_t c = f32_to_bf16_rne(r2);
+  *h = a ^ 0x8000u;
+  *m = b ^ 0x8000u;
+  *l = c ^ 0x8000u;
+}
+
+// Writes the norm k-step of centroid row `k` of tile t (lanes m and m + 32).
+__device__ __forceinline__ void write_centroid_aug(uint16_t *tile_base, int ks, int m, bool real,
+                                                   float halfsq) {
+  uint4 a0;
+  if (real) {
+    uint32_t h, md, lo;
+    split3_neg(halfsq, &h, &md, &lo);
+    a0.x = h | (md << 16);
+    a0.y = lo | (kBf16One << 16);
+  } else {
+    a0.x = kBf16NegMax;
+    a0.y = kBf16One << 16;
+  }
+  a0.z = kBf16One | (kBf16One << 16);
+  a0.w = 0u;
+  uint4 *aug = reinterpret_cast<uint4 *>(tile_base + (size_t)(ks - 1) * 64 * 8);
+  aug[m] = a0;
+  aug[m + 32] = uint4{0u, 0u, 0u, 0u};
+}
+
+// fp32 centroids -> fragments; D/4 threads per centroid row, 4 elements each.
 template <int D>
-__global__ void __launch_bounds__(64) k_prep_frags(const float *__restrict__ cent,
-                                                   uint16_t *__restrict__ frags, int c, int ntile) {
+__global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ cent,
+                                                    uint16_t *__restrict__ frags, int c, int ntile) {
   constexpr int KS = D / 16 + 1;
-  const int bh = blockIdx.y, t = blockIdx.x, l = threadIdx.x;
-  const int m = l & 31, half = l >> 5, k = t * 32 + m;
-  const bool real = k < c;
-  const float *row = cent + ((size_t)bh * c + (real ? k : 0)) * D;
-  uint16_t *out = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int bh = blockIdx.y;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int e0 = (threadIdx.x % TPR) * 4;
+  if (row >= ntile * 32) return;  // uniform per row group (TPR divides 64)
+  const bool real = row < c;
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  if (real) v = *reinterpret_cast<const float4 *>(cent + ((size_t)bh * c + row) * D + e0);
+  const uint16_t b0 = f32_to_bf16_rne(v.x), b1 = f32_to_bf16_rne(v.y);
+  const uint16_t b2 = f32_to_bf16_rne(v.z), b3 = f32_to_bf16_rne(v.w);
   float sq = 0.f;
+  sq = fmaf(bf16_bits_to_f32(b0), bf16_bits_to_f32(b0), sq);
+  sq = fmaf(bf16_bits_to_f32(b1), bf16_bits_to_f32(b1), sq);
+  sq = fmaf(bf16_bits_to_f32(b2), bf16_bits_to_f32(b2), sq);
+  sq = fmaf(bf16_bits_to_f32(b3), bf16_bits_to_f32(b3), sq);
 #pragma unroll
-  for (int s = 0; s < KS - 1; ++s) {
-    uint16_t v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = real ? row[16 * s + 8 * half + j] : 0.f;
-      v[j] = f32_to_bf16_rne(x);
-      const float xr = bf16_bits_to_f32(v[j]);
-      sq = fmaf(xr, xr, sq);
-    }
-    uint4 pk;
-    pk.x = v[0] | ((uint32_t)v[1] << 16);
-    pk.y = v[2] | ((uint32_t)v[3] << 16);
-    pk.z = v[4] | ((uint32_t)v[5] << 16);
-    pk.w = v[6] | ((uint32_t)v[7] << 16);
-    *reinterpret_cast<uint4 *>(out + ((size_t)s * 64 + l) * 8) = pk;
-  }
-  sq += __shfl_xor(sq, 32);
-  const float halfsq = 0.5f * sq;
-  const uint16_t hi = f32_to_bf16_rne(halfsq);
-  const float r1 = halfsq - bf16_bits_to_f32(hi);
-  const uint16_t mid = f32_to_bf16_rne(r1);
-  const float r2 = r1 - bf16_bits_to_f32(mid);
-  const uint16_t lo = f32_to_bf16_rne(r2);
-  uint4 pk = {0u, 0u, 0u, 0u};
-  if (half == 0) {
-    if (real) {
-      pk.x = (uint32_t)(hi ^ 0x8000u) | ((uint32_t)(mid ^ 0x8000u) << 16);
-      pk.y = (uint32_t)(lo ^ 0x8000u);
-    } else {
-      pk.x = 0xff7fu;  // bf16 -3.39e38
-    }
-  }
-  *reinterpret_cast<uint4 *>(out + ((size_t)(KS - 1) * 64 + l) * 8) = pk;
+  for (int o = TPR / 2; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+  const int t = row / 32, m = row % 32, s = e0 / 16, hf = (e0 % 16) / 8, j0 = e0 % 8;
+  uint16_t *tile_base = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
+  uint2 pk;
+  pk.x = b0 | ((uint32_t)b1 << 16);
+  pk.y = b2 | ((uint32_t)b3 << 16);
+  *reinterpret_cast<uint2 *>(tile_base + ((size_t)s * 64 + m + 32 * hf) * 8 + j0) = pk;
+  if (e0 == 0) write_centroid_aug(tile_base, KS, m, real, 0.5f * sq);
 }
 
 // One workgroup = 4 waves x 64 keys. Keys are the B operand (column n = key),
 // resident in VGPRs for the whole centroid sweep; centroid tiles stream
-// through double-buffered LDS. Each lane sees one key and 16 centroid rows
-// per tile, so the running argmax is two registers per column block and the
-// final merge is one exchange with lane ^ 32.
+// through double-buffered LDS, and the MFMAs of tile t+1 are issued before
+// the argmin of tile t so the matrix cores and the VALU overlap.
+//
+// Argmin: every lane sees one key and 16 centroid rows per tile. A score
+// -d^2/2 (<= 0, negative floats order inversely to their bit patterns) is
+// packed as (bits & ~15) | r, so among packed values the unsigned minimum is
+// the largest score (nearest centroid) and, on equal upper 28 bits, the
+// lowest row r: one v_and_or and half a v_min3 per score. A score that
+// rounding leaves slightly above 0 (a key sitting on a centroid) packs below
+// every negative one, i.e. it still ranks as nearest.
+// Across tiles a new minimum must be strictly smaller in the upper 28 bits,
+// so earlier (lower-index) tiles win ties. Comparing 28 of 32 bits moves a
+// decision only where two distances agree to about 2^-19 relative, below the
+// fp32 accumulation error of the 144-term dot product.
 template <int D>
 __global__ void __launch_bounds__(256, 2)
     k_assign_mfma(const uint16_t *__restrict__ keys, const uint16_t *__restrict__ frags,
                   int32_t *__restrict__ labels, int n, int c, int ntile, int blocks_per_head,
                   int total_blocks) {
   constexpr int KS = D / 16 + 1;
-  constexpr int STAGE_U4 = kTilesPerStage * KS * 64;  // 16-byte units per stage
+  constexpr int TILE_U4 = KS * 64;
+  constexpr int STAGE_U4 = kTilesPerStage * TILE_U4;  // 16-byte units per stage
   constexpr int PF = (STAGE_U4 + 255) / 256;          // prefetch registers per thread
   __shared__ uint4 lds[2][STAGE_U4];
 
@@ -131,93 +164,122 @@ __global__ void __launch_bounds__(256, 2)
   for (int cb = 0; cb < 2; ++cb) {
     const int key = key0 + cb * 32 + (lane & 31);
     const uint16_t *krow = keys + ((size_t)bh * n + (key < n ? key : 0)) * D;
+    float sq = 0.f;
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s) {
       uint4 v = {0u, 0u, 0u, 0u};
       if (key < n) v = *reinterpret_cast<const uint4 *>(krow + 16 * s + 8 * half);
       bfrag[cb][s] = __builtin_bit_cast(bf16x8_t, v);
+      float f[8];
+      unpack16<uint16_t>(v, f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sq = fmaf(f[j], f[j], sq);
     }
+    sq += __shfl_xor(sq, 32);
+    uint32_t h, md, lo;
+    split3_neg(0.5f * sq, &h, &md, &lo);
     uint4 aug = {0u, 0u, 0u, 0u};
     if (half == 0) {
-      aug.x = 0x3f803f80u;  // 1.0, 1.0
-      aug.y = 0x00003f80u;  // 1.0, 0
+      aug.x = kBf16One | (kBf16One << 16);
+      aug.y = kBf16One | (h << 16);
+      aug.z = md | (lo << 16);
     }
     bfrag[cb][KS - 1] = __builtin_bit_cast(bf16x8_t, aug);
   }
 
-  float best[2] = {-INFINITY, -INFINITY};
-  int bidx[2] = {0, 0};
+  uint32_t bestp[2] = {0xffffffffu, 0xffffffffu};
+  int btile[2] = {0, 0};
 
-  const uint4 *gfr = reinterpret_cast<const uint4 *>(frags) + (size_t)bh * ntile * KS * 64;
+  const uint4 *gfr = reinterpret_cast<const uint4 *>(frags) + (size_t)bh * ntile * TILE_U4;
   const int nstage = (ntile + kTilesPerStage - 1) / kTilesPerStage;
-  const int tile_u4 = KS * 64;
 
+  // Stage st of the centroid fragments: 16-byte units [st * STAGE_U4, +STAGE_U4)
+  // (units of tiles >= ntile are never read, so they are not fetched).
   uint4 pf[PF];
-  auto fetch = [&](int st) {
+#define KVC_FETCH(st)                                                           \
+  _Pragma("unroll") for (int i = 0; i < PF; ++i) {                              \
+    const int u = threadIdx.x + i * 256;                                        \
+    const bool ok = u < STAGE_U4 && (st) * kTilesPerStage + u / TILE_U4 < ntile; \
+    pf[i] = ok ? gfr[(size_t)(st) * STAGE_U4 + u] : uint4{0u, 0u, 0u, 0u};      \
+  }
+#define KVC_STASH(buf)                                                          \
+  _Pragma("unroll") for (int i = 0; i < PF; ++i) {                              \
+    const int u = threadIdx.x + i * 256;                                        \
+    if (u < STAGE_U4) lds[buf][u] = pf[i];                                      \
+  }
+  auto mfma_tile = [&](int t, f32x16_t &o0, f32x16_t &o1) {
+    const int buf = (t / kTilesPerStage) & 1, tt = t % kTilesPerStage;
+    o0 = f32x16_t{};
+    o1 = f32x16_t{};
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int u = threadIdx.x + i * 256;
-      const int t = st * kTilesPerStage + u / tile_u4;
-      if (u < STAGE_U4 && t < ntile) pf[i] = gfr[(size_t)st * STAGE_U4 + u];
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds[buf][(tt * KS + s) * 64 + lane]);
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[0][s], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[1][s], o1, 0, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
+  // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4.
+  auto argmin_tile = [&](const f32x16_t &acc, int cb, int t, bool last) {
+    uint32_t p[16];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int u = threadIdx.x + i * 256;
-      if (u < STAGE_U4) lds[buf][u] = pf[i];
+    for (int r = 0; r < 16; ++r)
+      p[r] = (__float_as_uint(acc[r]) & 0xfffffff0u) | (uint32_t)r;
+    if (last && t * 32 + 32 > c) {  // ragged last tile: padding rows never take part
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (t * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= c) p[r] = 0xffffffffu;
+    }
+    const uint32_t m0 = min(min(p[0], p[1]), p[2]);
+    const uint32_t m1 = min(min(p[3], p[4]), p[5]);
+    const uint32_t m2 = min(min(p[6], p[7]), p[8]);
+    const uint32_t m3 = min(min(p[9], p[10]), p[11]);
+    const uint32_t m4 = min(min(p[12], p[13]), p[14]);
+    const uint32_t q0 = min(min(m0, m1), m2);
+    const uint32_t q1 = min(min(m3, m4), p[15]);
+    const uint32_t m = min(q0, q1);
+    if ((m | 15u) < (bestp[cb] & 0xfffffff0u)) {
+      bestp[cb] = m;
+      btile[cb] = t;
     }
   };
 
-  fetch(0);
-  stash(0);
+  KVC_FETCH(0);
+  KVC_STASH(0);
   __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstage) fetch(st + 1);
-#pragma unroll
-    for (int tt = 0; tt < kTilesPerStage; ++tt) {
-      const int t = st * kTilesPerStage + tt;
-      if (t >= ntile) break;
-      f32x16_t acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds[buf][(tt * KS + s) * 64 + lane]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[0][s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[1][s], acc1, 0, 0, 0);
-      }
-      // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4.
-      if (t * 32 + 32 <= c) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int idx = t * 32 + 8 * (r >> 2) + (r & 3);
-          if (acc0[r] > best[0]) { best[0] = acc0[r]; bidx[0] = idx; }
-          if (acc1[r] > best[1]) { best[1] = acc1[r]; bidx[1] = idx; }
-        }
-      } else {  // ragged last tile: padding rows never take part
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int idx = t * 32 + 8 * (r >> 2) + (r & 3);
-          const bool real = idx + 4 * half < c;
-          if (real && acc0[r] > best[0]) { best[0] = acc0[r]; bidx[0] = idx; }
-          if (real && acc1[r] > best[1]) { best[1] = acc1[r]; bidx[1] = idx; }
-        }
-      }
+  if (nstage > 1) { KVC_FETCH(1); }
+  f32x16_t a0, a1;
+  mfma_tile(0, a0, a1);
+  for (int t = 0; t + 1 < ntile; ++t) {
+    const int nt = t + 1;
+    if (nt % kTilesPerStage == 0) {
+      const int st = nt / kTilesPerStage;
+      KVC_STASH(st & 1);
+      __syncthreads();
+      if (st + 1 < nstage) { KVC_FETCH(st + 1); }
     }
-    if (st + 1 < nstage) stash(buf ^ 1);
-    __syncthreads();
+    f32x16_t b0, b1;
+    mfma_tile(nt, b0, b1);
+    argmin_tile(a0, 0, t, false);
+    argmin_tile(a1, 1, t, false);
+    a0 = b0;
+    a1 = b1;
   }
+  argmin_tile(a0, 0, ntile - 1, true);
+  argmin_tile(a1, 1, ntile - 1, true);
 
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    int idx = bidx[cb] + 4 * half;
-    float v = best[cb];
-    const float ov = __shfl_xor(v, 32);
+    const uint32_t r = bestp[cb] & 15u;
+    const uint32_t key_t = bestp[cb] & 0xfffffff0u;
+    int idx = btile[cb] * 32 + 8 * (int)(r >> 2) + (int)(r & 3u) + 4 * half;
+    const uint32_t ok = __shfl_xor(key_t, 32);
     const int oi = __shfl_xor(idx, 32);
-    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+    if (ok < key_t || (ok == key_t && oi < idx)) idx = oi;
     const int key = key0 + cb * 32 + (lane & 31);
     if (half == 0 && key < n) labels[(size_t)bh * n + key] = idx;
   }
+#undef KVC_FETCH
+#undef KVC_STASH
 }
 
 // ---------------------------------------------------------------- fp32 assign
@@ -275,22 +337,33 @@ size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt) {
   return align_up((size_t)bh * c * sizeof(float), 256);
 }
 
+kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, hipStream_t s) {
+  const int ntile = (c + 31) / 32;
+  uint16_t *frags = static_cast<uint16_t *>(ws);
+  if (d == 128)
+    k_prep_frags<128><<<dim3((ntile * 32 + 7) / 8, bh), 256, 0, s>>>(cent, frags, c, ntile);
+  else
+    k_prep_frags<64><<<dim3((ntile * 32 + 15) / 16, bh), 256, 0, s>>>(cent, frags, c, ntile);
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
 kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
-                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s) {
+                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s, bool frags_ready) {
   if (dt == KV_BF16) {
     const int ntile = (c + 31) / 32;
     uint16_t *frags = static_cast<uint16_t *>(ws);
     const int bph = (n + kAssignKeysPerBlock - 1) / kAssignKeysPerBlock;
     const int total = bph * bh;
-    if (d == 128) {
-      k_prep_frags<128><<<dim3(ntile, bh), 64, 0, s>>>(cent, frags, c, ntile);
+    if (!frags_ready) {
+      const kv_status st = launch_prep_frags(cent, bh, d, c, ws, s);
+      if (st != KV_OK) return st;
+    }
+    if (d == 128)
       k_assign_mfma<128><<<total, 256, 0, s>>>((const uint16_t *)keys, frags, labels, n, c, ntile,
                                               bph, total);
-    } else {
-      k_prep_frags<64><<<dim3(ntile, bh), 64, 0, s>>>(cent, frags, c, ntile);
+    else
       k_assign_mfma<64><<<total, 256, 0, s>>>((const uint16_t *)keys, frags, labels, n, c, ntile,
                                              bph, total);
-    }
   } else {
     float *hn = static_cast<float *>(ws);
     const long tot = (long)bh * c;
@@ -320,27 +393,35 @@ __global__ void __launch_bounds__(64) k_rank_hist(const int32_t *__restrict__ la
                                                   int32_t *__restrict__ rank,
                                                   int32_t *__restrict__ hist, int n, int c,
                                                   int nbits, int nchunk) {
+  constexpr int SUB = kRankChunk / 64;
   extern __shared__ int32_t cnt[];
   const int bh = blockIdx.y, ch = blockIdx.x, lane = threadIdx.x;
-  for (int k = lane; k < c; k += 64) cnt[k] = 0;
-  __syncthreads();
   const int32_t *lab = labels + (size_t)bh * n;
   const int base = ch * kRankChunk;
+  int a[SUB];
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) {
+    const int i = base + sub * 64 + lane;
+    a[sub] = i < n ? lab[i] : -1;
+  }
+  for (int k = lane; k < c; k += 64) cnt[k] = 0;
+  __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int sub = 0; sub < kRankChunk; sub += 64) {
-    const int i = base + sub + lane;
-    const bool valid = i < n;
-    const int a = valid ? lab[i] : 0;
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) {
+    const int i = base + sub * 64 + lane;
+    const bool valid = a[sub] >= 0;
+    const int v = valid ? a[sub] : 0;
     uint64_t mask = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
-      const bool bit = (a >> b) & 1;
+      const bool bit = (v >> b) & 1;
       const uint64_t m = __ballot(bit);
       mask &= bit ? m : ~m;
     }
     if (valid) {
-      const int r = cnt[a] + __popcll(mask & below);
+      const int r = cnt[v] + __popcll(mask & below);
       rank[(size_t)bh * n + i] = r;
-      if ((mask >> lane) == 1ull) cnt[a] += __popcll(mask);
+      if ((mask >> lane) == 1ull) cnt[v] += __popcll(mask);
     }
     __syncthreads();
   }
@@ -354,7 +435,18 @@ __global__ void k_colscan(int32_t *__restrict__ hist, int32_t *__restrict__ tot,
   if (k >= c) return;
   int32_t run = 0;
   int32_t *col = hist + (size_t)bh * nchunk * c + k;
-  for (int ch = 0; ch < nchunk; ++ch) {
+  int ch = 0;
+  for (; ch + 8 <= nchunk; ch += 8) {
+    int32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = col[(size_t)(ch + i) * c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      col[(size_t)(ch + i) * c] = run;
+      run += h[i];
+    }
+  }
+  for (; ch < nchunk; ++ch) {
     const int32_t h = col[(size_t)ch * c];
     col[(size_t)ch * c] = run;
     run += h;
@@ -416,49 +508,93 @@ __global__ void k_scatter(const int32_t *__restrict__ labels, const int32_t *__r
   perm[(size_t)bh * n + dest] = i;
 }
 
-// One wave per cluster: members summed in key order (fp32), then divided.
+// One wave per cluster. Lanes split a key row into 16-byte pieces, so one
+// wave instruction reads RPI member rows; members are dealt round-robin to
+// the RPI row slots, each slot sums its members in key order, and the slots
+// are combined in a fixed order (fp32 throughout, so the result is
+// reproducible bit for bit). The mean replaces the centroid (an empty
+// cluster keeps its value). For bf16 keys the same pass writes the next
+// round's MFMA fragments and norm k-step, so no separate prep is needed.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
                                                 const int32_t *__restrict__ perm,
                                                 const int32_t *__restrict__ start,
                                                 const int32_t *__restrict__ tot,
-                                                const float *cent_in, float *cent_out, int n,
-                                                int c) {
-  constexpr int EPL = D / 64;
+                                                const float *cent_in, float *cent_out,
+                                                uint16_t *__restrict__ frags, int n, int c,
+                                                int ntile) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane
+  constexpr int LPR = D / EPL;               // lanes per row
+  constexpr int RPI = 64 / LPR;              // member rows per wave instruction
+  constexpr int UNR = 4;
+  constexpr int KS = D / 16 + 1;
   const int bh = blockIdx.y;
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int part = lane % LPR, slot = lane / LPR;
   if (k >= c) return;
   const int cnt = tot[(size_t)bh * c + k];
   const int st = start[(size_t)bh * c + k];
   const int32_t *p = perm + (size_t)bh * n + st;
-  const T *kb = keys + (size_t)bh * n * D + lane * EPL;
+  const T *kb = keys + (size_t)bh * n * D + part * EPL;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  int j = 0;
-  for (; j + 4 <= cnt; j += 4) {
-    T v[4][EPL];
+  for (int j0 = 0; j0 < cnt; j0 += RPI * UNR) {
+    uint4 v[UNR];
+    bool ok[UNR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const T *row = kb + (size_t)p[j + u] * D;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) v[u][e] = row[e];
+    for (int u = 0; u < UNR; ++u) {
+      const int j = j0 + u * RPI + slot;
+      ok[u] = j < cnt;
+      const int row = ok[u] ? p[j] : 0;
+      v[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)row * D);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < UNR; ++u) {
+      float f[EPL];
+      unpack16<T>(v[u], f);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += Elem<T>::to_f32(v[u][e]);
+      for (int e = 0; e < EPL; ++e) acc[e] += ok[u] ? f[e] : 0.f;
+    }
   }
-  for (; j < cnt; ++j) {
-    const T *row = kb + (size_t)p[j] * D;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += Elem<T>::to_f32(row[e]);
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o);
+  float mean[EPL];
+  const float *in = cent_in + ((size_t)bh * c + k) * D + part * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) mean[e] = cnt > 0 ? acc[e] / (float)cnt : in[e];
+  if (slot == 0) {
+    float *out = cent_out + ((size_t)bh * c + k) * D + part * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = mean[e];
   }
-  float *out = cent_out + ((size_t)bh * c + k) * D + lane * EPL;
-  const float *in = cent_in + ((size_t)bh * c + k) * D + lane * EPL;
+  if (frags != nullptr && EPL == 8) {
+    // element e0 = 8 part lives in k-step e0 / 16, lane half (e0 % 16) / 8
+    uint16_t b[8];
+    float sq = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) out[e] = cnt > 0 ? acc[e] / (float)cnt : in[e];
+    for (int e = 0; e < 8; ++e) {
+      b[e] = f32_to_bf16_rne(mean[e % EPL]);
+      const float r = bf16_bits_to_f32(b[e]);
+      sq = fmaf(r, r, sq);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+    const int t = k / 32, m = k % 32, e0 = part * 8;
+    uint16_t *tile_base = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
+    if (slot == 0) {
+      uint4 pk;
+      pk.x = b[0] | ((uint32_t)b[1] << 16);
+      pk.y = b[2] | ((uint32_t)b[3] << 16);
+      pk.z = b[4] | ((uint32_t)b[5] << 16);
+      pk.w = b[6] | ((uint32_t)b[7] << 16);
+      *reinterpret_cast<uint4 *>(tile_base + ((size_t)(e0 / 16) * 64 + m + 32 * ((e0 % 16) / 8)) * 8) = pk;
+    }
+    if (lane == 0) write_centroid_aug(tile_base, KS, m, true, 0.5f * sq);
+  }
 }
 
 static int ceil_log2(int c) {
@@ -481,7 +617,7 @@ size_t update_ws_bytes(int bh, int n, int c) {
 kv_status launch_update(const void *keys, const int32_t *labels, const float *cent_in,
                         float *cent_out, int32_t *counts, int bh, int n, int d, int c,
                         kv_dtype dt, void *ws, hipStream_t s, const int32_t **perm_out,
-                        const int32_t **start_out, const int32_t **tot_out) {
+                        const int32_t **start_out, const int32_t **tot_out, void *frags_out) {
   const int nchunk = (n + kRankChunk - 1) / kRankChunk;
   char *w = static_cast<char *>(ws);
   int32_t *rank = reinterpret_cast<int32_t *>(w);
@@ -501,20 +637,22 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, perm, n, c,
                                                       nchunk);
   const dim3 g((c + 3) / 4, bh);
+  uint16_t *fr = static_cast<uint16_t *>(frags_out);
+  const int ntile = (c + 31) / 32;
   if (dt == KV_BF16) {
     if (d == 128)
       k_segsum<uint16_t, 128><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, tot, cent_in,
-                                                cent_out, n, c);
+                                                cent_out, fr, n, c, ntile);
     else
       k_segsum<uint16_t, 64><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, tot, cent_in,
-                                               cent_out, n, c);
+                                               cent_out, fr, n, c, ntile);
   } else {
     if (d == 128)
       k_segsum<float, 128><<<g, 256, 0, s>>>((const float *)keys, perm, start, tot, cent_in,
-                                             cent_out, n, c);
+                                             cent_out, nullptr, n, c, ntile);
     else
       k_segsum<float, 64><<<g, 256, 0, s>>>((const float *)keys, perm, start, tot, cent_in,
-                                            cent_out, n, c);
+                                            cent_out, nullptr, n, c, ntile);
   }
   if (perm_out) *perm_out = perm;
   if (start_out) *start_out = start;

@@ -85,14 +85,16 @@ namespace kvc {
 kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
                                 int n, int c, int d, kv_dtype dt, hipStream_t s);
 size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt);
+kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, hipStream_t s);
 kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
-                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s);
+                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s,
+                        bool frags_ready = false);
 size_t update_ws_bytes(int bh, int n, int c);
 kv_status launch_update(const void *keys, const int32_t *labels, const float *cent_in,
                         float *cent_out, int32_t *counts, int bh, int n, int d, int c,
                         kv_dtype dt, void *ws, hipStream_t s,
                         const int32_t **perm_out, const int32_t **start_out,
-                        const int32_t **tot_out);
+                        const int32_t **tot_out, void *frags_out = nullptr);
 kv_status launch_pack(const kv_pool *pool, const void *keys, const void *values,
                       const float *cent, const int32_t *perm, const int32_t *start,
                       const int32_t *tot, int n, int c, hipStream_t s);
