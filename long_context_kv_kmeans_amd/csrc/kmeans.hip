@@ -17,10 +17,9 @@ namespace kvc {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kAssignKeysPerWave = 64;                   // two 32-key MFMA column blocks
-constexpr int kAssignWaves = 4;
-constexpr int kAssignKeysPerBlock = kAssignKeysPerWave * kAssignWaves;
-constexpr int kTilesPerStage = 4;                        // 128 centroids per LDS stage
+constexpr int kAssignColBlocks = 2;                      // 32-key MFMA column blocks per wave
+constexpr int kAssignMinWaves = 3;                       // waves per SIMD the register budget targets
+constexpr int kTilesPerStage = 2;                        // 64 centroids per LDS stage
 constexpr int kRankChunk = 1024;                         // keys per counting-sort chunk
 
 // ---------------------------------------------------------------- init
@@ -126,8 +125,12 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
 }
 
 // One workgroup = 4 waves x 64 keys. Keys are the B operand (column n = key),
-// resident in VGPRs for the whole centroid sweep; centroid tiles stream
-// through double-buffered LDS, and the MFMAs of tile t+1 are issued before
+// resident in VGPRs for the whole centroid sweep. Centroid tiles stream into
+// two LDS stage buffers with direct global->LDS loads (each wave instruction
+// moves one 1 KB fragment block), so staging costs neither VGPRs nor LDS
+// write instructions; the two buffers are separate objects and are selected
+// statically, which lets the compiler keep the next stage's loads in flight
+// while the current stage is read. The MFMAs of tile t+1 are issued before
 // the argmin of tile t so the matrix cores and the VALU overlap.
 //
 // Argmin: every lane sees one key and 16 centroid rows per tile. A score
@@ -141,27 +144,28 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
 // so earlier (lower-index) tiles win ties. Comparing 28 of 32 bits moves a
 // decision only where two distances agree to about 2^-19 relative, below the
 // fp32 accumulation error of the 144-term dot product.
-template <int D>
-__global__ void __launch_bounds__(256, 2)
+template <int D, int NCB, int MINW>
+__global__ void __launch_bounds__(256, MINW)
     k_assign_mfma(const uint16_t *__restrict__ keys, const uint16_t *__restrict__ frags,
                   int32_t *__restrict__ labels, int n, int c, int ntile, int blocks_per_head,
                   int total_blocks) {
   constexpr int KS = D / 16 + 1;
   constexpr int TILE_U4 = KS * 64;
   constexpr int STAGE_U4 = kTilesPerStage * TILE_U4;  // 16-byte units per stage
-  constexpr int PF = (STAGE_U4 + 255) / 256;          // prefetch registers per thread
-  __shared__ uint4 lds[2][STAGE_U4];
+  __shared__ uint4 lds0[STAGE_U4];
+  __shared__ uint4 lds1[STAGE_U4];
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int bh = bid / blocks_per_head;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int key0 = (bid % blocks_per_head) * kAssignKeysPerBlock + wave * kAssignKeysPerWave;
+  constexpr int KPW = 32 * NCB;  // keys per wave
+  const int key0 = (bid % blocks_per_head) * (4 * KPW) + wave * KPW;
   const int half = lane >> 5;
 
   // Key fragments (B operand): lane holds key n = lane % 32, k = 16 s + 8 half + j.
-  bf16x8_t bfrag[2][KS];
+  bf16x8_t bfrag[NCB][KS];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const int key = key0 + cb * 32 + (lane & 31);
     const uint16_t *krow = keys + ((size_t)bh * n + (key < n ? key : 0)) * D;
     float sq = 0.f;
@@ -187,35 +191,36 @@ __global__ void __launch_bounds__(256, 2)
     bfrag[cb][KS - 1] = __builtin_bit_cast(bf16x8_t, aug);
   }
 
-  uint32_t bestp[2] = {0xffffffffu, 0xffffffffu};
-  int btile[2] = {0, 0};
+  uint32_t bestp[NCB];
+  int btile[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    bestp[cb] = 0xffffffffu;
+    btile[cb] = 0;
+  }
 
   const uint4 *gfr = reinterpret_cast<const uint4 *>(frags) + (size_t)bh * ntile * TILE_U4;
   const int nstage = (ntile + kTilesPerStage - 1) / kTilesPerStage;
 
-  // Stage st of the centroid fragments: 16-byte units [st * STAGE_U4, +STAGE_U4)
-  // (units of tiles >= ntile are never read, so they are not fetched).
-  uint4 pf[PF];
-#define KVC_FETCH(st)                                                           \
-  _Pragma("unroll") for (int i = 0; i < PF; ++i) {                              \
-    const int u = threadIdx.x + i * 256;                                        \
-    const bool ok = u < STAGE_U4 && (st) * kTilesPerStage + u / TILE_U4 < ntile; \
-    pf[i] = ok ? gfr[(size_t)(st) * STAGE_U4 + u] : uint4{0u, 0u, 0u, 0u};      \
-  }
-#define KVC_STASH(buf)                                                          \
-  _Pragma("unroll") for (int i = 0; i < PF; ++i) {                              \
-    const int u = threadIdx.x + i * 256;                                        \
-    if (u < STAGE_U4) lds[buf][u] = pf[i];                                      \
-  }
-  auto mfma_tile = [&](int t, f32x16_t &o0, f32x16_t &o1) {
-    const int buf = (t / kTilesPerStage) & 1, tt = t % kTilesPerStage;
-    o0 = f32x16_t{};
-    o1 = f32x16_t{};
+  // Stage st -> LDS: wave w moves fragment blocks w, w + 4, ... (1 KB each);
+  // blocks of tiles >= ntile are never read and are skipped.
+  auto dma_stage = [&](int st, uint4 *dst) {
+#pragma unroll
+    for (int i = wave; i < kTilesPerStage * KS; i += 4) {
+      if (st * kTilesPerStage + i / KS < ntile)
+        __builtin_amdgcn_global_load_lds(gfr + (size_t)st * STAGE_U4 + i * 64 + lane, dst + i * 64,
+                                         16, 0, 0);
+    }
+  };
+  auto mfma_tile = [&](const uint4 *buf, int tt, f32x16_t *o) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds[buf][(tt * KS + s) * 64 + lane]);
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[0][s], o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[1][s], o1, 0, 0, 0);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, buf[(tt * KS + s) * 64 + lane]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[cb][s], o[cb], 0, 0, 0);
     }
   };
   // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4.
@@ -243,32 +248,49 @@ __global__ void __launch_bounds__(256, 2)
     }
   };
 
-  KVC_FETCH(0);
-  KVC_STASH(0);
-  __syncthreads();
-  if (nstage > 1) { KVC_FETCH(1); }
-  f32x16_t a0, a1;
-  mfma_tile(0, a0, a1);
-  for (int t = 0; t + 1 < ntile; ++t) {
-    const int nt = t + 1;
-    if (nt % kTilesPerStage == 0) {
-      const int st = nt / kTilesPerStage;
-      KVC_STASH(st & 1);
-      __syncthreads();
-      if (st + 1 < nstage) { KVC_FETCH(st + 1); }
+  f32x16_t acc[NCB], nxt_acc[NCB];
+  int t = 0;  // tile whose scores sit in acc
+  auto argmin_all = [&](bool last) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) argmin_tile(acc[cb], cb, t, last);
+  };
+  auto advance = [&](const uint4 *buf, int tt, int nt) {
+    mfma_tile(buf, tt, nxt_acc);  // tile nt's MFMAs go out before tile t's argmin
+    argmin_all(false);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = nxt_acc[cb];
+    t = nt;
+  };
+  // Tiles [st * TPS + 1, (st + 1) * TPS) of stage st (in `cur`), then the first
+  // tile of stage st + 1 (in `nxt`) once that stage has landed.
+  auto run_stage = [&](int st, const uint4 *cur, uint4 *cur_w, const uint4 *nxt) {
+#pragma unroll
+    for (int tt = 1; tt < kTilesPerStage; ++tt) {
+      const int nt = st * kTilesPerStage + tt;
+      if (nt >= ntile) return;
+      advance(cur, tt, nt);
     }
-    f32x16_t b0, b1;
-    mfma_tile(nt, b0, b1);
-    argmin_tile(a0, 0, t, false);
-    argmin_tile(a1, 1, t, false);
-    a0 = b0;
-    a1 = b1;
+    const int nt = (st + 1) * kTilesPerStage;
+    if (nt >= ntile) return;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): stage st + 1 has landed
+    __syncthreads();                     // ... for every wave; `cur` is free again
+    if (st + 2 < nstage) dma_stage(st + 2, cur_w);
+    advance(nxt, 0, nt);
+  };
+
+  dma_stage(0, lds0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  if (nstage > 1) dma_stage(1, lds1);
+  mfma_tile(lds0, 0, acc);
+  for (int st = 0; st < nstage; st += 2) {
+    run_stage(st, lds0, lds0, lds1);
+    if (st + 1 < nstage) run_stage(st + 1, lds1, lds1, lds0);
   }
-  argmin_tile(a0, 0, ntile - 1, true);
-  argmin_tile(a1, 1, ntile - 1, true);
+  argmin_all(true);
 
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const uint32_t r = bestp[cb] & 15u;
     const uint32_t key_t = bestp[cb] & 0xfffffff0u;
     int idx = btile[cb] * 32 + 8 * (int)(r >> 2) + (int)(r & 3u) + 4 * half;
@@ -278,8 +300,6 @@ __global__ void __launch_bounds__(256, 2)
     const int key = key0 + cb * 32 + (lane & 31);
     if (half == 0 && key < n) labels[(size_t)bh * n + key] = idx;
   }
-#undef KVC_FETCH
-#undef KVC_STASH
 }
 
 // ---------------------------------------------------------------- fp32 assign
@@ -352,18 +372,19 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
   if (dt == KV_BF16) {
     const int ntile = (c + 31) / 32;
     uint16_t *frags = static_cast<uint16_t *>(ws);
-    const int bph = (n + kAssignKeysPerBlock - 1) / kAssignKeysPerBlock;
+    constexpr int NCB = kAssignColBlocks;
+    const int bph = (n + 128 * NCB - 1) / (128 * NCB);
     const int total = bph * bh;
     if (!frags_ready) {
       const kv_status st = launch_prep_frags(cent, bh, d, c, ws, s);
       if (st != KV_OK) return st;
     }
     if (d == 128)
-      k_assign_mfma<128><<<total, 256, 0, s>>>((const uint16_t *)keys, frags, labels, n, c, ntile,
-                                              bph, total);
+      k_assign_mfma<128, NCB, kAssignMinWaves><<<total, 256, 0, s>>>(
+          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
     else
-      k_assign_mfma<64><<<total, 256, 0, s>>>((const uint16_t *)keys, frags, labels, n, c, ntile,
-                                             bph, total);
+      k_assign_mfma<64, NCB, kAssignMinWaves><<<total, 256, 0, s>>>(
+          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
   } else {
     float *hn = static_cast<float *>(ws);
     const long tot = (long)bh * c;
