@@ -19,12 +19,36 @@
 
 namespace kvc {
 
+// Completion protocol for the last-block steps. After the block barrier all
+// of the block's stores sit in this XCD's L2; one release fence by thread 0
+// makes them visible device-wide before the counter moves, and only the
+// block that completes the count pays for an acquire (L2/L1 invalidate)
+// before reading the other blocks' results. Returns true in that block.
+__device__ __forceinline__ bool last_block_arrives(int32_t *counter, int nblocks, int *s_last) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = (old == nblocks - 1);
+    if (*s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  return *s_last != 0;
+}
+
 // ---------------------------------------------------------------- boundary
+// One workgroup per sequence; each wave owns up to 8 query heads and issues
+// all of their loads before reducing, so the step costs one memory round trip.
+// Summation order is fixed (heads in order within a wave, then waves in
+// order), so r is reproducible bit for bit.
+constexpr int kBoundaryHeadsPerWave = 8;
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_boundary(const T *__restrict__ q_prev,
                                                   const T *__restrict__ q_cur, int hq, float tau,
                                                   uint8_t *__restrict__ flag, float *__restrict__ r) {
   constexpr int EPL = D / 64;
+  constexpr int HPW = kBoundaryHeadsPerWave;
   __shared__ float part[4];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (q_prev == nullptr) {
@@ -35,22 +59,34 @@ __global__ void __launch_bounds__(256) k_boundary(const T *__restrict__ q_prev,
     return;
   }
   float csum = 0.f;
-  for (int h = wave; h < hq; h += 4) {
-    const size_t o = ((size_t)b * hq + h) * D + lane * EPL;
-    float dot = 0.f, n1 = 0.f, n2 = 0.f;
+  for (int h0 = wave * HPW; h0 < hq; h0 += 4 * HPW) {
+    T a[HPW][EPL], c[HPW][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float a = Elem<T>::to_f32(q_prev[o + e]);
-      const float c = Elem<T>::to_f32(q_cur[o + e]);
-      dot = fmaf(a, c, dot);
-      n1 = fmaf(a, a, n1);
-      n2 = fmaf(c, c, n2);
+    for (int i = 0; i < HPW; ++i) {
+      const int h = h0 + i;
+      const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        a[i][e] = q_prev[o + e];
+        c[i][e] = q_cur[o + e];
+      }
     }
-    dot = wave_sum(dot);
-    n1 = wave_sum(n1);
-    n2 = wave_sum(n2);
-    const float cosv = (n1 > 0.f && n2 > 0.f) ? dot / (sqrtf(n1) * sqrtf(n2)) : 0.f;
-    csum += cosv;
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+      float dot = 0.f, n1 = 0.f, n2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float x = Elem<T>::to_f32(a[i][e]), y = Elem<T>::to_f32(c[i][e]);
+        dot = fmaf(x, y, dot);
+        n1 = fmaf(x, x, n1);
+        n2 = fmaf(y, y, n2);
+      }
+      dot = wave_sum(dot);
+      n1 = wave_sum(n1);
+      n2 = wave_sum(n2);
+      const float cosv = (n1 > 0.f && n2 > 0.f) ? dot / (sqrtf(n1) * sqrtf(n2)) : 0.f;
+      if (h0 + i < hq) csum += cosv;
+    }
   }
   if (lane == 0) part[wave] = csum;
   __syncthreads();
@@ -166,7 +202,17 @@ kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void
 }
 
 // ---------------------------------------------------------------- select
-constexpr int kScoreUnitsPerBlock = 256;
+// Scoring: 1024-thread workgroups each score up to 1024 units; a unit's index
+// vector is read as 16-byte pieces, so one wave instruction covers 64 / LPU
+// units. Selection: the last workgroup of (b, g) holds every candidate as a
+// 64-bit key (orderable score << 32 | ~id) in registers, KPT consecutive
+// units per thread, and finds the first unit that no longer fits the budget
+// with an MSB-first weighted radix select (per-wave LDS histograms, one
+// digit of 8 bits per pass, early exit once the crossing bucket holds a
+// single unit). Every unit ranked before it is selected.
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / 64;
+constexpr int kScoreUnitsPerBlock = kSelectThreads;
 
 // Wave 0 helper: given per-digit weights w[0..255] (LDS), the weight already
 // above the range and the budget, find the highest digit whose inclusion
@@ -182,7 +228,6 @@ __device__ int find_crossing_digit(const int *w, long above, long budget, long *
     dg[i] = w[255 - 4 * lane - i];
     local += dg[i];
   }
-  // inclusive prefix over lanes (lane 0 = highest digits)
   long incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -190,7 +235,6 @@ __device__ int find_crossing_digit(const int *w, long above, long budget, long *
     if (lane >= o) incl += y;
   }
   const long excl = incl - local;
-  // crossing inside this lane's digits?
   int found = -1;
   long found_above = 0;
   long run = above + excl;
@@ -211,30 +255,34 @@ __device__ int find_crossing_digit(const int *w, long above, long budget, long *
   return __shfl(found, src);
 }
 
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(256) k_select(kv_pool pool, const T *__restrict__ q, int hq,
-                                                int budget, const uint8_t *__restrict__ flag,
-                                                int32_t *__restrict__ sel_units, int sel_cap,
-                                                int32_t *__restrict__ sel_n,
-                                                int32_t *__restrict__ sel_rows,
-                                                float *__restrict__ scores, int32_t *counters) {
-  constexpr int EPL = 16 / Elem<T>::kBytes;       // elements per 16-byte lane load
-  constexpr int LPU = D / EPL;                     // lanes per index vector
-  constexpr int UPW = 64 / LPU;                    // units per wave instruction
+__device__ __forceinline__ unsigned long long unit_key(float score, int u) {
+  return ((unsigned long long)float_order_key(score) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
+}
+
+template <typename T, int D, int KPT>
+__global__ void __launch_bounds__(kSelectThreads)
+    k_select(kv_pool pool, const T *__restrict__ q, int hq, int group, int budget,
+             const uint8_t *__restrict__ flag, int32_t *__restrict__ sel_units, int sel_cap,
+             int32_t *__restrict__ sel_n, int32_t *__restrict__ sel_rows, float *__restrict__ scores,
+             int32_t *counters) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per 16-byte lane load
+  constexpr int LPU = D / EPL;               // lanes per index vector
+  constexpr int UPW = 64 / LPU;              // units per wave instruction
+  constexpr int UNR = 4;
   const int H = pool.n_kv_heads;
   const int bg = blockIdx.y, b = bg / H, g = bg % H;
   if (flag != nullptr && flag[b] == 0) return;
   const int U = min(max(pool.n_cand[b], 0), pool.unit_cap);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int part = lane % LPU, slot = lane / LPU;
 
   // ---- scoring: s_u = (sum_h q_h) . idx_u, fp32
   float qs[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qs[e] = 0.f;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * G + h) * D + part * EPL);
+  for (int h = 0; h < group; ++h) {
+    const uint4 v =
+        *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * group + h) * D + part * EPL);
     float f[EPL];
     unpack16<T>(v, f);
 #pragma unroll
@@ -242,73 +290,90 @@ __global__ void __launch_bounds__(256) k_select(kv_pool pool, const T *__restric
   }
   const T *idx = static_cast<const T *>(pool.unit_index) + (size_t)bg * pool.unit_cap * D;
   float *sc = scores + (size_t)bg * pool.unit_cap;
-  const int u_begin = blockIdx.x * kScoreUnitsPerBlock;
-  const int u_end = min(U, u_begin + kScoreUnitsPerBlock);
-  for (int u0 = u_begin + wave * UPW; u0 < u_end; u0 += 4 * UPW) {
-    const int u = u0 + slot;
-    float f[EPL];
-    if (u < u_end) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(idx + (size_t)u * D + part * EPL);
-      unpack16<T>(v, f);
-    } else {
+  const int wbase = blockIdx.x * kScoreUnitsPerBlock + wave * 64;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) f[e] = 0.f;
+  for (int j0 = 0; j0 < 64; j0 += UPW * UNR) {
+    uint4 v[UNR];
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) {
+      const int u = wbase + j0 + i * UPW + slot;
+      v[i] = u < U ? *reinterpret_cast<const uint4 *>(idx + (size_t)u * D + part * EPL)
+                   : uint4{0u, 0u, 0u, 0u};
     }
-    float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dot = fmaf(qs[e], f[e], dot);
+    for (int i = 0; i < UNR; ++i) {
+      float f[EPL];
+      unpack16<T>(v[i], f);
+      float dot = 0.f;
 #pragma unroll
-    for (int o = LPU / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-    if (part == 0 && u < u_end) sc[u] = dot;
+      for (int e = 0; e < EPL; ++e) dot = fmaf(qs[e], f[e], dot);
+#pragma unroll
+      for (int o = LPU / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+      const int u = wbase + j0 + i * UPW + slot;
+      if (part == 0 && u < U) sc[u] = dot;
+    }
   }
 
   // ---- completion: the last block of (b, g) selects
   __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(&counters[bg], 1);
-    s_last = (old == (int)gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (!last_block_arrives(&counters[bg], (int)gridDim.x, &s_last)) return;
 
-  // ---- weighted radix select over 64-bit keys (score order key, ~id)
-  __shared__ int hw[256];
-  __shared__ int hc[256];
+  const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
+  unsigned long long key[KPT];
+  int sz[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int u = tid * KPT + j;
+    const int s = u < U ? usz[u] : 0;
+    sz[j] = s > 0 ? s : 0;
+    key[j] = (u < U && s > 0) ? unit_key(sc[u], u) : 0ull;
+  }
+
+  __shared__ int hw[kSelectWaves][256];
+  __shared__ int hc[kSelectWaves][256];
+  __shared__ int tw[256];
+  __shared__ int tc[256];
   __shared__ int hu[256];
   __shared__ long s_above;
-  __shared__ int s_digit, s_done, s_none;
+  __shared__ int s_done, s_none;
   __shared__ unsigned long long s_prefix, s_kstar;
-  const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     s_above = 0;
     s_prefix = 0ull;
     s_done = 0;
     s_none = 0;
   }
-  __syncthreads();
   for (int sh = 56; sh >= 0; sh -= 8) {
-    hw[threadIdx.x] = 0;
-    hc[threadIdx.x] = 0;
+    for (int i = tid; i < kSelectWaves * 256; i += kSelectThreads) {
+      (&hw[0][0])[i] = 0;
+      (&hc[0][0])[i] = 0;
+    }
     __syncthreads();
     const unsigned long long prefix = s_prefix;
-    for (int u = threadIdx.x; u < U; u += 256) {
-      const int sz = usz[u];
-      if (sz <= 0) continue;
-      const unsigned long long key =
-          ((unsigned long long)float_order_key(sc[u]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
-      if (sh < 56 && (key >> (sh + 8)) != (prefix >> (sh + 8))) continue;
-      const int dgt = (int)((key >> sh) & 255ull);
-      atomicAdd(&hw[dgt], sz);
-      atomicAdd(&hc[dgt], 1);
-      hu[dgt] = u;  // any member; used only when the bucket holds one unit
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (sz[j] == 0) continue;
+      if (sh < 56 && (key[j] >> (sh + 8)) != (prefix >> (sh + 8))) continue;
+      const int dgt = (int)((key[j] >> sh) & 255ull);
+      atomicAdd(&hw[wave][dgt], sz[j]);
+      atomicAdd(&hc[wave][dgt], 1);
+      hu[dgt] = tid * KPT + j;  // any member; read only when the bucket holds one unit
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int w = 0, c = 0;
+#pragma unroll
+      for (int v = 0; v < kSelectWaves; ++v) {
+        w += hw[v][tid];
+        c += hc[v][tid];
+      }
+      tw[tid] = w;
+      tc[tid] = c;
     }
     __syncthreads();
     if (wave == 0) {
       long above_out = 0;
-      const int dgt = find_crossing_digit(hw, s_above, budget, &above_out);
+      const int dgt = find_crossing_digit(tw, s_above, budget, &above_out);
       if (lane == 0) {
         if (dgt < 0) {
           s_none = 1;  // everything in range fits (only possible at the top level)
@@ -316,10 +381,9 @@ __global__ void __launch_bounds__(256) k_select(kv_pool pool, const T *__restric
         } else {
           s_above = above_out;
           s_prefix = prefix | ((unsigned long long)dgt << sh);
-          if (hc[dgt] == 1) {
+          if (tc[dgt] == 1) {
             const int u = hu[dgt];
-            s_kstar = ((unsigned long long)float_order_key(sc[u]) << 32) |
-                      (uint32_t)(0xffffffffu - (uint32_t)u);
+            s_kstar = unit_key(sc[u], u);
             s_done = 1;
           } else if (sh == 0) {
             s_kstar = s_prefix;
@@ -334,51 +398,47 @@ __global__ void __launch_bounds__(256) k_select(kv_pool pool, const T *__restric
   const bool take_all = s_none != 0;
   const unsigned long long kstar = s_kstar;
 
-  // ---- compaction in ascending unit id
-  const int per = (U + 255) / 256;
-  const int lo = threadIdx.x * per;
-  const int hi = min(U, lo + per);
+  // ---- compaction in ascending unit id (thread t owns units t*KPT .. t*KPT+KPT-1)
   int cnt = 0, rows = 0;
-  for (int u = lo; u < hi; ++u) {
-    const int sz = usz[u];
-    if (sz <= 0) continue;
-    const unsigned long long key =
-        ((unsigned long long)float_order_key(sc[u]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
-    if (take_all || key > kstar) {
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (sz[j] > 0 && (take_all || key[j] > kstar)) {
       ++cnt;
-      rows += sz;
+      rows += sz[j];
     }
-  }
-  __shared__ int wsum[4], wrows[4];
+  __shared__ int wsum[kSelectWaves], wrows[kSelectWaves];
   int incl = cnt, rincl = rows;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o), z = __shfl_up(rincl, o);
-    if (lane >= o) { incl += y; rincl += z; }
+    if (lane >= o) {
+      incl += y;
+      rincl += z;
+    }
   }
-  if (lane == 63) { wsum[wave] = incl; wrows[wave] = rincl; }
+  if (lane == 63) {
+    wsum[wave] = incl;
+    wrows[wave] = rincl;
+  }
   __syncthreads();
   int off = 0, total = 0, total_rows = 0;
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kSelectWaves; ++w) {
     if (w < wave) off += wsum[w];
     total += wsum[w];
     total_rows += wrows[w];
   }
   int pos = off + incl - cnt;
   int32_t *out = sel_units + (size_t)bg * sel_cap;
-  for (int u = lo; u < hi; ++u) {
-    const int sz = usz[u];
-    if (sz <= 0) continue;
-    const unsigned long long key =
-        ((unsigned long long)float_order_key(sc[u]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
-    if (take_all || key > kstar) {
-      if (pos < sel_cap) out[pos] = u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (sz[j] > 0 && (take_all || key[j] > kstar)) {
+      if (pos < sel_cap) out[pos] = tid * KPT + j;
       ++pos;
     }
-  }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     if (total > sel_cap) {
-      __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
       total = sel_cap;
     }
     sel_n[bg] = total;
@@ -393,22 +453,21 @@ int select_num_blocks(const kv_pool *pool) {
 }
 
 template <typename T, int D>
-static kv_status select_dispatch_g(const kv_pool *pool, const void *q, int hq, int budget,
-                                   const uint8_t *flag, int32_t *sel_units, int sel_cap,
-                                   int32_t *sel_n, int32_t *sel_rows, float *scores,
-                                   int32_t *counters, hipStream_t s) {
+static kv_status select_dispatch(const kv_pool *pool, const void *q, int hq, int budget,
+                                 const uint8_t *flag, int32_t *sel_units, int sel_cap,
+                                 int32_t *sel_n, int32_t *sel_rows, float *scores,
+                                 int32_t *counters, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(select_num_blocks(pool), pool->batch * pool->n_kv_heads);
-#define KVC_SEL(GG)                                                                            \
-  k_select<T, D, GG><<<grid, 256, 0, s>>>(*pool, (const T *)q, hq, budget, flag, sel_units,     \
-                                          sel_cap, sel_n, sel_rows, scores, counters)
-  switch (G) {
-    case 1: KVC_SEL(1); break;
-    case 2: KVC_SEL(2); break;
-    case 4: KVC_SEL(4); break;
-    case 8: KVC_SEL(8); break;
-    default: return KV_ERR_UNSUPPORTED;
-  }
+  const int per = (pool->unit_cap + kSelectThreads - 1) / kSelectThreads;
+#define KVC_SEL(K)                                                                            \
+  k_select<T, D, K><<<grid, kSelectThreads, 0, s>>>(*pool, (const T *)q, hq, G, budget, flag,  \
+                                                     sel_units, sel_cap, sel_n, sel_rows,      \
+                                                     scores, counters)
+  if (per <= 2) KVC_SEL(2);
+  else if (per <= 8) KVC_SEL(8);
+  else if (per <= kSelectMaxKeysPerThread) KVC_SEL(kSelectMaxKeysPerThread);
+  else return KV_ERR_UNSUPPORTED;
 #undef KVC_SEL
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
@@ -418,55 +477,71 @@ kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         int32_t *sel_rows, float *scores, int32_t *counters, hipStream_t s) {
   if (pool->dtype == KV_BF16)
     return pool->head_dim == 128
-               ? select_dispatch_g<uint16_t, 128>(pool, q, hq, budget, flag, sel_units, sel_cap,
-                                                  sel_n, sel_rows, scores, counters, s)
-               : select_dispatch_g<uint16_t, 64>(pool, q, hq, budget, flag, sel_units, sel_cap,
-                                                 sel_n, sel_rows, scores, counters, s);
+               ? select_dispatch<uint16_t, 128>(pool, q, hq, budget, flag, sel_units, sel_cap,
+                                                sel_n, sel_rows, scores, counters, s)
+               : select_dispatch<uint16_t, 64>(pool, q, hq, budget, flag, sel_units, sel_cap,
+                                               sel_n, sel_rows, scores, counters, s);
   return pool->head_dim == 128
-             ? select_dispatch_g<float, 128>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n,
-                                             sel_rows, scores, counters, s)
-             : select_dispatch_g<float, 64>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n,
-                                            sel_rows, scores, counters, s);
+             ? select_dispatch<float, 128>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n,
+                                           sel_rows, scores, counters, s)
+             : select_dispatch<float, 64>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n,
+                                          sel_rows, scores, counters, s);
 }
 
 // ---------------------------------------------------------------- gather + attend
-constexpr int kAttendRowsPerSplit = 64;  // target rows per workgroup
-constexpr int kAttendPiece = 256;        // rows resolved per row-table pass
-constexpr int kAttendUnroll = 4;         // row loads in flight per lane group
-
-struct SoftmaxState {
-  float m, l;
-};
+// Rows of (b, g): the selected units' row ranges (CSR order of the selection
+// list) followed by the local-buffer rows. A workgroup of 8 waves takes one
+// contiguous share of those rows; each wave keeps 32 rows of K and V in
+// flight (16 bytes per lane per row piece) and folds them into a per-lane
+// online softmax for the group's G query heads; waves merge through LDS.
+// With one share per (b, g) the workgroup writes the output directly;
+// otherwise it publishes (m, l, acc) and the last workgroup merges the
+// shares in order.
+constexpr int kAttendThreads = 512;
+constexpr int kAttendWaves = kAttendThreads / 64;
+constexpr int kAttendRowsPerWave = 32;    // rows in flight per wave
+constexpr int kAttendMinRowsPerSplit = 128;
+constexpr int kAttendTargetBlocks = 256;  // one wave of workgroups across the CUs
 
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
   return m_old == -INFINITY ? 0.f : exp2f(m_old - m_new);
 }
 
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__restrict__ q,
-                                                       int hq, float scale_log2,
-                                                       const int32_t *__restrict__ sel_units,
-                                                       int sel_cap, const int32_t *__restrict__ sel_n,
-                                                       float *__restrict__ out,
-                                                       float *__restrict__ partials,
-                                                       int32_t *counters) {
+__global__ void __launch_bounds__(kAttendThreads)
+    k_gather_attend(kv_pool pool, const T *__restrict__ q, int hq, float scale_log2,
+                    const int32_t *__restrict__ sel_units, int sel_cap,
+                    const int32_t *__restrict__ sel_n, float *__restrict__ out,
+                    float *__restrict__ partials, int32_t *counters) {
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane (one 16-byte load)
   constexpr int LPR = D / EPL;               // lanes per row
   constexpr int RPI = 64 / LPR;              // rows per wave instruction
-  constexpr int ROWS_PER_WAVE_IT = RPI * kAttendUnroll;
-  __shared__ int s_psum[kMaxSel + 1];
+  constexpr int UNR = kAttendRowsPerWave / RPI;
+  constexpr int NW = kAttendWaves;
+  __shared__ int s_psum[kMaxSel];
   __shared__ int s_start[kMaxSel];
-  __shared__ int s_rowtab[kAttendPiece];
-  __shared__ int s_wsum[4];
-  __shared__ float s_m[4][G], s_l[4][G];
-  __shared__ float s_acc[4][G][D];
+  __shared__ int s_rowtab[kAttendThreads];
+  __shared__ int s_wsum[NW];
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ float s_acc[NW][G][D];
   __shared__ int s_last;
 
   const int H = pool.n_kv_heads;
   const int bg = blockIdx.y, b = bg / H, g = bg % H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int part = lane % LPR, slot = lane / LPR;
   const int nsplit = gridDim.x, split = blockIdx.x;
+
+  // ---- queries of the group, pre-scaled so that exp2 gives the softmax
+  float qf[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 v =
+        *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * G + h) * D + part * EPL);
+    unpack16<T>(v, qf[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[h][e] *= scale_log2;
+  }
 
   // ---- selected units -> LDS prefix table (block-wide scan of sizes)
   const int n = min(min(sel_n[bg], sel_cap), kMaxSel);
@@ -474,8 +549,8 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
   const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
   const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
   int carry = 0;
-  for (int base = 0; base < n; base += 256) {
-    const int i = base + threadIdx.x;
+  for (int base = 0; base < n; base += kAttendThreads) {
+    const int i = base + tid;
     int sz = 0;
     if (i < n) {
       const int u = su[i];
@@ -491,9 +566,9 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
     }
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
-    int off = carry;
-    int tot = 0;
-    for (int w = 0; w < 4; ++w) {
+    int off = carry, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
       if (w < wave) off += s_wsum[w];
       tot += s_wsum[w];
     }
@@ -511,15 +586,6 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
   const int chunk = (R + nsplit - 1) / nsplit;
   const int r_lo = min(R, split * chunk), r_hi = min(R, r_lo + chunk);
 
-  // ---- queries of the group, pre-scaled so that exp2 gives the softmax
-  float qf[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * G + h) * D + part * EPL);
-    unpack16<T>(v, qf[h]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[h][e] *= scale_log2;
-  }
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -528,15 +594,13 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-
   const T *kbase = static_cast<const T *>(pool.k) + (size_t)bg * pool.row_cap * D + part * EPL;
   const T *vbase = static_cast<const T *>(pool.v) + (size_t)bg * pool.row_cap * D + part * EPL;
 
-  for (int p0 = r_lo; p0 < r_hi; p0 += kAttendPiece) {
-    const int plen = min(kAttendPiece, r_hi - p0);
-    __syncthreads();
-    if (threadIdx.x < plen) {
-      const int j = p0 + threadIdx.x;
+  for (int p0 = r_lo; p0 < r_hi; p0 += kAttendThreads) {
+    const int plen = min(kAttendThreads, r_hi - p0);
+    if (tid < plen) {
+      const int j = p0 + tid;
       int row;
       if (j < r_sel) {
         int lo = 0, hi = n - 1;  // last i with s_psum[i] <= j
@@ -548,23 +612,23 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
       } else {
         row = buf_begin + (j - r_sel);
       }
-      s_rowtab[threadIdx.x] = min(max(row, 0), pool.row_cap - 1);
+      s_rowtab[tid] = min(max(row, 0), pool.row_cap - 1);
     }
     __syncthreads();
-    for (int it = wave * ROWS_PER_WAVE_IT; it < plen; it += 4 * ROWS_PER_WAVE_IT) {
-      uint4 kv[kAttendUnroll], vv[kAttendUnroll];
-      bool ok[kAttendUnroll];
+    for (int it = wave * kAttendRowsPerWave; it < plen; it += NW * kAttendRowsPerWave) {
+      uint4 kv[UNR], vv[UNR];
+      bool ok[UNR];
 #pragma unroll
-      for (int uu = 0; uu < kAttendUnroll; ++uu) {
+      for (int uu = 0; uu < UNR; ++uu) {
         const int li = it + uu * RPI + slot;
         ok[uu] = li < plen;
         const size_t row = ok[uu] ? (size_t)s_rowtab[li] : 0;
         kv[uu] = *reinterpret_cast<const uint4 *>(kbase + row * D);
         vv[uu] = *reinterpret_cast<const uint4 *>(vbase + row * D);
       }
-      float s[kAttendUnroll][G];
+      float s[UNR][G];
 #pragma unroll
-      for (int uu = 0; uu < kAttendUnroll; ++uu) {
+      for (int uu = 0; uu < UNR; ++uu) {
         float kf[EPL];
         unpack16<T>(kv[uu], kf);
 #pragma unroll
@@ -581,12 +645,12 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
       for (int h = 0; h < G; ++h) {
         float mx = m[h];
 #pragma unroll
-        for (int uu = 0; uu < kAttendUnroll; ++uu) mx = fmaxf(mx, s[uu][h]);
+        for (int uu = 0; uu < UNR; ++uu) mx = fmaxf(mx, s[uu][h]);
         const float alpha = safe_scale(m[h], mx);
-        float p[kAttendUnroll];
+        float p[UNR];
         float psum = 0.f;
 #pragma unroll
-        for (int uu = 0; uu < kAttendUnroll; ++uu) {
+        for (int uu = 0; uu < UNR; ++uu) {
           p[uu] = ok[uu] ? exp2f(s[uu][h] - mx) : 0.f;
           psum += p[uu];
         }
@@ -595,7 +659,7 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
 #pragma unroll
-        for (int uu = 0; uu < kAttendUnroll; ++uu) {
+        for (int uu = 0; uu < UNR; ++uu) {
           float vf[EPL];
           unpack16<T>(vv[uu], vf);
 #pragma unroll
@@ -603,6 +667,7 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
         }
       }
     }
+    __syncthreads();
   }
 
   // ---- merge the row groups of the wave (lanes with equal `part`)
@@ -635,34 +700,36 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
     }
   }
   __syncthreads();
-  // ---- merge the 4 waves and publish this split's partial state
+  // ---- merge the waves (in order); one share: write the output directly
   const size_t pstride = (size_t)G * (D + 2);
   float *mine = partials + ((size_t)bg * nsplit + split) * pstride;
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  for (int i = tid; i < G * D; i += kAttendThreads) {
     const int h = i / D, e = i % D;
     float mx = -INFINITY;
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, s_m[w][h]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w][h]);
     float a = 0.f, lsum = 0.f;
-    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
       const float sc = safe_scale(s_m[w][h], mx);
       a += s_acc[w][h][e] * sc;
       lsum += s_l[w][h] * sc;
     }
-    mine[h * (D + 2) + e] = a;
-    if (e == 0) {
-      mine[h * (D + 2) + D] = mx;
-      mine[h * (D + 2) + D + 1] = lsum;
+    if (nsplit == 1) {
+      out[((size_t)b * hq + g * G + h) * D + e] = lsum > 0.f ? a / lsum : 0.f;
+    } else {
+      mine[h * (D + 2) + e] = a;
+      if (e == 0) {
+        mine[h * (D + 2) + D] = mx;
+        mine[h * (D + 2) + D + 1] = lsum;
+      }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&counters[bg], 1) == nsplit - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // ---- final merge over splits, in split order
+  if (nsplit == 1) return;
+  if (!last_block_arrives(&counters[bg], nsplit, &s_last)) return;
+  // ---- final merge over shares, in share order
   const float *allp = partials + (size_t)bg * nsplit * pstride;
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  for (int i = tid; i < G * D; i += kAttendThreads) {
     const int h = i / D, e = i % D;
     float mx = -INFINITY;
     for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, allp[sp * pstride + h * (D + 2) + D]);
@@ -675,29 +742,31 @@ __global__ void __launch_bounds__(256) k_gather_attend(kv_pool pool, const T *__
     }
     out[((size_t)b * hq + g * G + h) * D + e] = lsum > 0.f ? a / lsum : 0.f;
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 int attend_num_splits(const kv_pool *pool, int max_rows) {
   const long rows = (long)(max_rows > 0 ? max_rows : 0) + (pool->buf_cap > 0 ? pool->buf_cap : 0);
-  long ns = (rows + kAttendRowsPerSplit - 1) / kAttendRowsPerSplit;
+  const long bh = (long)pool->batch * pool->n_kv_heads;
+  long by_rows = (rows + kAttendMinRowsPerSplit - 1) / kAttendMinRowsPerSplit;
+  long by_grid = (kAttendTargetBlocks + bh - 1) / bh;
+  long ns = by_rows < by_grid ? by_rows : by_grid;
   if (ns < 1) ns = 1;
-  if (ns > 256) ns = 256;
+  if (ns > 64) ns = 64;
   return (int)ns;
 }
 
 template <typename T, int D>
-static kv_status attend_dispatch_g(const kv_pool *pool, const void *q, int hq, float scale_log2,
-                                   const int32_t *sel_units, int sel_cap, const int32_t *sel_n,
-                                   int nsplit, float *out, float *partials, int32_t *counters,
-                                   hipStream_t s) {
+static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, float scale_log2,
+                                 const int32_t *sel_units, int sel_cap, const int32_t *sel_n,
+                                 int nsplit, float *out, float *partials, int32_t *counters,
+                                 hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
 #define KVC_ATT(GG)                                                                            \
-  k_gather_attend<T, D, GG><<<grid, 256, 0, s>>>(*pool, (const T *)q, hq, scale_log2,          \
-                                                 sel_units, sel_cap, sel_n, out, partials,     \
-                                                 counters)
+  k_gather_attend<T, D, GG><<<grid, kAttendThreads, 0, s>>>(*pool, (const T *)q, hq,           \
+                                                            scale_log2, sel_units, sel_cap,    \
+                                                            sel_n, out, partials, counters)
   switch (G) {
     case 1: KVC_ATT(1); break;
     case 2: KVC_ATT(2); break;
@@ -716,15 +785,15 @@ kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float
   const float sl2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = exp2(x log2 e)
   if (pool->dtype == KV_BF16)
     return pool->head_dim == 128
-               ? attend_dispatch_g<uint16_t, 128>(pool, q, hq, sl2, sel_units, sel_cap, sel_n,
-                                                  nsplit, out, partials, counters, s)
-               : attend_dispatch_g<uint16_t, 64>(pool, q, hq, sl2, sel_units, sel_cap, sel_n,
-                                                 nsplit, out, partials, counters, s);
+               ? attend_dispatch<uint16_t, 128>(pool, q, hq, sl2, sel_units, sel_cap, sel_n,
+                                                nsplit, out, partials, counters, s)
+               : attend_dispatch<uint16_t, 64>(pool, q, hq, sl2, sel_units, sel_cap, sel_n,
+                                               nsplit, out, partials, counters, s);
   return pool->head_dim == 128
-             ? attend_dispatch_g<float, 128>(pool, q, hq, sl2, sel_units, sel_cap, sel_n, nsplit,
-                                             out, partials, counters, s)
-             : attend_dispatch_g<float, 64>(pool, q, hq, sl2, sel_units, sel_cap, sel_n, nsplit,
-                                            out, partials, counters, s);
+             ? attend_dispatch<float, 128>(pool, q, hq, sl2, sel_units, sel_cap, sel_n, nsplit,
+                                           out, partials, counters, s)
+             : attend_dispatch<float, 64>(pool, q, hq, sl2, sel_units, sel_cap, sel_n, nsplit,
+                                          out, partials, counters, s);
 }
 
 }  // namespace kvc

@@ -12,6 +12,7 @@ namespace kvc {
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int kMaxSel = 4096; // selected units staged in LDS by the attend kernel
+constexpr int kSelectMaxKeysPerThread = 32;  // selection keys held per thread (x1024 threads)
 
 // bf16 is carried as raw uint16_t bits.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
