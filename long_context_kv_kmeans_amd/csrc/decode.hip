@@ -12,25 +12,34 @@
 //                       with an online softmax and a deterministic merge.
 //
 // Multi-block kernels finish with a "last block" step: each block publishes
-// its results, fences at agent scope and bumps a per-(sequence, head)
+// its results with device-coherent stores and bumps a per-(sequence, head)
 // counter; the block that brings the counter to the grid size does the final
 // reduction in a fixed order and resets the counter to zero.
 #include "kvc_internal.hpp"
 
 namespace kvc {
 
-// Completion protocol for the last-block steps. After the block barrier all
-// of the block's stores sit in this XCD's L2; one release fence by thread 0
-// makes them visible device-wide before the counter moves, and only the
-// block that completes the count pays for an acquire (L2/L1 invalidate)
-// before reading the other blocks' results. Returns true in that block.
+// Completion protocol for the last-block steps. Results that another
+// workgroup will read are written with device-coherent stores (relaxed
+// agent-scope atomic stores: `sc1` on gfx950, so they do not sit in this
+// XCD's non-coherent L2). Every wave waits for its stores to be acknowledged
+// (vmcnt(0)) before the workgroup barrier; only then does thread 0 bump the
+// counter, so a workgroup that sees the final count also sees every
+// published result when it reads them with device-coherent loads. This
+// avoids the L2-wide writeback / invalidate that agent-scope fences cost.
+// Returns true in the workgroup that completes the count.
+__device__ __forceinline__ void coherent_store(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ bool last_block_arrives(int32_t *counter, int nblocks, int *s_last) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's coherent stores are acknowledged
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_last = (old == nblocks - 1);
-    if (*s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   return *s_last != 0;
@@ -307,10 +316,9 @@ __global__ void __launch_bounds__(kSelectThreads)
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dot = fmaf(qs[e], f[e], dot);
-#pragma unroll
-      for (int o = LPU / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+      dot = group_sum<LPU>(dot);
       const int u = wbase + j0 + i * UPW + slot;
-      if (part == 0 && u < U) sc[u] = dot;
+      if (part == 0 && u < U) coherent_store(&sc[u], dot);
     }
   }
 
@@ -326,7 +334,7 @@ __global__ void __launch_bounds__(kSelectThreads)
     const int u = tid * KPT + j;
     const int s = u < U ? usz[u] : 0;
     sz[j] = s > 0 ? s : 0;
-    key[j] = (u < U && s > 0) ? unit_key(sc[u], u) : 0ull;
+    key[j] = (u < U && s > 0) ? unit_key(coherent_load(&sc[u]), u) : 0ull;
   }
 
   __shared__ int hw[kSelectWaves][256];
@@ -383,7 +391,7 @@ __global__ void __launch_bounds__(kSelectThreads)
           s_prefix = prefix | ((unsigned long long)dgt << sh);
           if (tc[dgt] == 1) {
             const int u = hu[dgt];
-            s_kstar = unit_key(sc[u], u);
+            s_kstar = unit_key(coherent_load(&sc[u]), u);
             s_done = 1;
           } else if (sh == 0) {
             s_kstar = s_prefix;
@@ -490,37 +498,451 @@ kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
 
 // ---------------------------------------------------------------- gather + attend
 // Rows of (b, g): the selected units' row ranges (CSR order of the selection
-// list) followed by the local-buffer rows. A workgroup of 8 waves takes one
-// contiguous share of those rows; each wave keeps 32 rows of K and V in
-// flight (16 bytes per lane per row piece) and folds them into a per-lane
-// online softmax for the group's G query heads; waves merge through LDS.
-// With one share per (b, g) the workgroup writes the output directly;
-// otherwise it publishes (m, l, acc) and the last workgroup merges the
-// shares in order.
-constexpr int kAttendThreads = 512;
-constexpr int kAttendWaves = kAttendThreads / 64;
-constexpr int kAttendRowsPerWave = 32;    // rows in flight per wave
+// list) followed by the local-buffer rows. A workgroup takes one contiguous
+// share of those rows and folds them into an online softmax for the group's
+// G query heads; waves merge through LDS. With one share per (b, g) the
+// workgroup writes the output directly; otherwise it publishes (m, l, acc)
+// and the last workgroup merges the shares in order.
+//
+// bf16 keys: q.k for 16 rows x 16 query columns (G used) is one
+// v_mfma_f32_16x16x32_bf16 chain over the head dimension; the probabilities
+// go through LDS to the lanes holding the V rows, which accumulate p.v on
+// the VALU. fp32 keys take an all-VALU variant.
 constexpr int kAttendMinRowsPerSplit = 128;
-constexpr int kAttendTargetBlocks = 256;  // one wave of workgroups across the CUs
+constexpr int kAttendTargetBlocks = 256;  // one 8-wave workgroup per CU
+constexpr int kAttendPiece = 256;         // rows resolved per row-table pass
 
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
   return m_old == -INFINITY ? 0.f : exp2f(m_old - m_new);
 }
 
-template <typename T, int D, int G>
+// Selected units of (b, g) -> LDS: s_start[i] first row, s_psum[i] rows before
+// unit i in the concatenated selection. Thread t owns the contiguous run of
+// list positions [t per, (t + 1) per), per = ceil(sel_cap / NT), and loads its
+// ids before the list length is known (positions past the length are simply
+// not used), so the ids, the length and the unit table cost two dependent
+// memory round trips whatever the length. Sets *n_out to the list length
+// (clamped to [0, sel_cap]) and returns the selection's row count.
+template <int NT>
+__device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t *su,
+                                     const int32_t *sel_n, int sel_cap, int *n_out, int *s_psum,
+                                     int *s_start, int *s_wsum) {
+  constexpr int NW = NT / 64;
+  constexpr int PER_MAX = kMaxSel / NT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (sel_cap + NT - 1) / NT;  // sel_cap <= kMaxSel
+  const int i0 = tid * per;
+  int uid[PER_MAX];
+#pragma unroll
+  for (int j = 0; j < PER_MAX; ++j) uid[j] = (j < per && i0 + j < sel_cap) ? su[i0 + j] : -1;
+  const int n = min(max(sel_n[bg], 0), sel_cap);
+  const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
+  const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
+  int sz[PER_MAX], st[PER_MAX];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < PER_MAX; ++j) {
+    const int u = uid[j];
+    // foreign ids count as empty units
+    const bool valid = j < per && i0 + j < n && u >= 0 && u < pool.unit_cap;
+    sz[j] = valid ? max(usz[u], 0) : 0;
+    st[j] = valid ? ust[u] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < PER_MAX; ++j) run += sz[j];
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int off = incl - run, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) off += s_wsum[w];
+    tot += s_wsum[w];
+  }
+#pragma unroll
+  for (int j = 0; j < PER_MAX; ++j) {
+    if (j < per && i0 + j < n) {
+      s_psum[i0 + j] = off;
+      s_start[i0 + j] = st[j];
+    }
+    off += sz[j];
+  }
+  __syncthreads();
+  *n_out = n;
+  return tot;
+}
+
+// Pool row of position j (< r_sel: inside the selection, else the buffer).
+__device__ __forceinline__ int attend_row_of(int j, int n, int r_sel, int buf_begin,
+                                             const int *s_psum, const int *s_start, int row_cap) {
+  int row;
+  if (j < r_sel) {
+    int lo = 0, hi = n - 1;  // last i with s_psum[i] <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_psum[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    row = s_start[lo] + (j - s_psum[lo]);
+  } else {
+    row = buf_begin + (j - r_sel);
+  }
+  return min(max(row, 0), row_cap - 1);
+}
+
+// Merge NW wave states (m, l, acc over D) per head, then either write the
+// output (one share) or publish the share and let the last workgroup merge.
+// The last workgroup reads every share with all loads in flight at once: one
+// wave per head reduces (m, l) across the shares (lane = share), then each
+// thread folds its output elements over the shares in batches of kMergeBatch.
+constexpr int kMaxSplits = 64;
+constexpr int kMergeBatch = 16;
+
+// Share values (output element tid + k NT, shares sp0 .. sp0 + kMergeBatch - 1).
+template <int NT, int G, int D, int EPT>
+__device__ __forceinline__ void merge_load_batch(float (&v)[EPT][kMergeBatch], const float *allp,
+                                                 size_t pstride, int sp0, int nsplit) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int i = tid + k * NT, h = i / D, e = i % D;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      v[k][j] = (i < G * D && sp0 + j < nsplit)
+                    ? coherent_load(&allp[(sp0 + j) * pstride + h * (D + 2) + e])
+                    : 0.f;
+  }
+}
+
+template <int NT, int G, int D>
+__device__ void attend_finish(int bg, int b, int g, int hq, int nsplit, int split,
+                              const float (*s_m)[G], const float (*s_l)[G],
+                              const float (*s_acc)[G][D], float *out, float *partials,
+                              int32_t *counters, int *s_last) {
+  constexpr int NW = NT / 64;
+  constexpr int EPT = (G * D + NT - 1) / NT;  // output elements per thread
+  __shared__ float s_scale[kMaxSplits][G];
+  __shared__ float s_lsum[G];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t pstride = (size_t)G * (D + 2);
+  float *mine = partials + ((size_t)bg * nsplit + split) * pstride;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, e = i % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float a = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = safe_scale(s_m[w][h], mx);
+      a += s_acc[w][h][e] * sc;
+      lsum += s_l[w][h] * sc;
+    }
+    if (nsplit == 1) {
+      out[((size_t)b * hq + g * G + h) * D + e] = lsum > 0.f ? a / lsum : 0.f;
+    } else {
+      coherent_store(&mine[h * (D + 2) + e], a);
+      if (e == 0) {
+        coherent_store(&mine[h * (D + 2) + D], mx);
+        coherent_store(&mine[h * (D + 2) + D + 1], lsum);
+      }
+    }
+  }
+  if (nsplit == 1) return;
+  if (!last_block_arrives(&counters[bg], nsplit, s_last)) return;
+  const float *allp = partials + (size_t)bg * nsplit * pstride;
+  // The first batch of share values is requested before (m, l) so that both
+  // arrive in one memory round trip.
+  float v[EPT][kMergeBatch];
+  merge_load_batch<NT, G, D, EPT>(v, allp, pstride, 0, nsplit);
+  for (int h = wave; h < G; h += NW) {
+    const bool on = lane < nsplit;
+    const float m = on ? coherent_load(&allp[lane * pstride + h * (D + 2) + D]) : -INFINITY;
+    const float l = on ? coherent_load(&allp[lane * pstride + h * (D + 2) + D + 1]) : 0.f;
+    float mx = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float sc = safe_scale(m, mx);
+    const float lsum = wave_sum(l * sc);
+    if (on) s_scale[lane][h] = sc;
+    if (lane == 0) s_lsum[h] = lsum;
+  }
+  __syncthreads();
+  float a[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) a[k] = 0.f;
+  for (int sp0 = 0;;) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int h = ((tid + k * NT) / D) % G;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (sp0 + j < nsplit) a[k] += v[k][j] * s_scale[sp0 + j][h];
+    }
+    sp0 += kMergeBatch;
+    if (sp0 >= nsplit) break;
+    merge_load_batch<NT, G, D, EPT>(v, allp, pstride, sp0, nsplit);
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D) {
+      const int h = i / D, e = i % D;
+      const float lsum = s_lsum[h];
+      out[((size_t)b * hq + g * G + h) * D + e] = lsum > 0.f ? a[k] / lsum : 0.f;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- bf16: MFMA q.k, VALU p.v -------------------------------------------------
+constexpr int kAttendThreads = 512;
+constexpr int kAttendWaves = kAttendThreads / 64;
+constexpr int kAttendChunk = 32;  // rows per wave step: two 16-row MFMA tiles
+constexpr int kAttendMfmaPiece = 1024;  // rows resolved per row-table pass
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8a_t __attribute__((ext_vector_type(8)));
+
+// One wave step's operands: K fragments of two 16-row tiles (A operand: lane
+// holds row l%16 of a tile and head-dimension entries 32 s + 8 (l/16) .. +7 of
+// k-step s) and the V rows this lane accumulates (8 elements each).
+template <int D> struct AttendChunk {
+  static constexpr int KS = D / 32;
+  static constexpr int LPR = D / 8;
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int VU = kAttendChunk / RPI;
+  bf16x8a_t kf[2][KS];
+  uint4 vv[VU];
+};
+
+template <int D>
+__device__ __forceinline__ void attend_chunk_load(AttendChunk<D> &c, const int *s_rowtab, int it,
+                                                  int plen, const uint16_t *kbase,
+                                                  const uint16_t *vbase, int col, int quad,
+                                                  int vslot, int vpart) {
+  using C = AttendChunk<D>;
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+    const int li = it + tk * 16 + col;
+    const size_t row = li < plen ? (size_t)s_rowtab[li] : 0;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      c.kf[tk][s] = __builtin_bit_cast(
+          bf16x8a_t, *reinterpret_cast<const uint4 *>(kbase + row * D + 32 * s + 8 * quad));
+  }
+#pragma unroll
+  for (int i = 0; i < C::VU; ++i) {
+    const int li = it + vslot + C::RPI * i;
+    const size_t row = li < plen ? (size_t)s_rowtab[li] : 0;
+    c.vv[i] = *reinterpret_cast<const uint4 *>(vbase + row * D + 8 * vpart);
+  }
+}
+
+// Fold one chunk into the wave's online-softmax state. Scores: lane holds rows
+// 4 (l/16) + r of each tile for query head l%16; probabilities and the rescale
+// factor reach the V lanes through this wave's LDS slice.
+template <int D, int G>
+__device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const bf16x8a_t *qf,
+                                                  int it, int plen, float scale_log2,
+                                                  float &m_run, float &l_run, float (*acc)[8],
+                                                  float (*s_p)[G], float *s_alpha, int lane,
+                                                  int col, int quad, int vslot) {
+  using C = AttendChunk<D>;
+  f32x4_t sc[2];
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+    sc[tk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      sc[tk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.kf[tk][s], qf[s], sc[tk], 0, 0, 0);
+  }
+  float sv[8];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int li = it + tk * 16 + 4 * quad + r;
+      const float v = li < plen ? sc[tk][r] * scale_log2 : -INFINITY;
+      sv[tk * 4 + r] = v;
+      mt = fmaxf(mt, v);
+    }
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float m_new = fmaxf(m_run, mt);
+  const float alpha = safe_scale(m_run, m_new);
+  float ps = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float p = sv[k] == -INFINITY ? 0.f : exp2f(sv[k] - m_new);
+    ps += p;
+    if (col < G) s_p[(k >> 2) * 16 + 4 * quad + (k & 3)][col] = p;
+  }
+  ps += __shfl_xor(ps, 16);
+  ps += __shfl_xor(ps, 32);
+  l_run = l_run * alpha + ps;
+  m_run = m_new;
+  if (lane < G) s_alpha[lane] = alpha;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  float al[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) al[h] = s_alpha[h];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+#pragma unroll
+  for (int i = 0; i < C::VU; ++i) {
+    float vf[8];
+    unpack16<uint16_t>(c.vv[i], vf);
+    const int rl = vslot + C::RPI * i;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = s_p[rl][h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // s_p / s_alpha are rewritten next step
+}
+
+template <int D, int G>
 __global__ void __launch_bounds__(kAttendThreads)
-    k_gather_attend(kv_pool pool, const T *__restrict__ q, int hq, float scale_log2,
-                    const int32_t *__restrict__ sel_units, int sel_cap,
-                    const int32_t *__restrict__ sel_n, float *__restrict__ out,
-                    float *__restrict__ partials, int32_t *counters) {
+    k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
+                         const int32_t *__restrict__ sel_units, int sel_cap,
+                         const int32_t *__restrict__ sel_n, float *__restrict__ out,
+                         float *__restrict__ partials, int32_t *counters) {
+  static_assert(G <= 16, "query columns of one MFMA tile");
+  constexpr int NT = kAttendThreads, NW = kAttendWaves;
+  constexpr int KS = D / 32;
+  constexpr int LPR = D / 8;
+  constexpr int STEP = NW * kAttendChunk;
+  __shared__ int s_psum[kMaxSel];
+  __shared__ int s_start[kMaxSel];
+  __shared__ int s_rowtab[kAttendMfmaPiece];
+  __shared__ int s_wsum[NW];
+  __shared__ float s_p[NW][kAttendChunk][G];
+  __shared__ float s_alpha[NW][G];
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ float s_acc[NW][G][D];
+  __shared__ int s_last;
+
+  const int H = pool.n_kv_heads;
+  const int bg = blockIdx.y, b = bg / H, g = bg % H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nsplit = gridDim.x, split = blockIdx.x;
+  const int col = lane & 15, quad = lane >> 4;     // MFMA: column (query head) and k group
+  const int vpart = lane % LPR, vslot = lane / LPR;  // V rows: element piece and row slot
+
+  // Query fragments (B operand, 32 k x 16 columns): lane holds column `col`
+  // (query head col < G, else zero) and the same head-dimension entries as
+  // the K fragments, so one K load instruction reads a contiguous 64-byte
+  // span of each of 16 rows.
+  bf16x8a_t qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (col < G)
+      v = *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * G + col) * D + 32 * s + 8 * quad);
+    qf[s] = __builtin_bit_cast(bf16x8a_t, v);
+  }
+
+  int n;
+  const int r_sel = attend_load_selection<NT>(pool, bg, sel_units + (size_t)bg * sel_cap, sel_n,
+                                              sel_cap, &n, s_psum, s_start, s_wsum);
+  int r_buf = 0, buf_begin = 0;
+  if (pool.buf_cap > 0) {
+    buf_begin = pool.buf_begin[b];
+    r_buf = max(pool.n_rows[b] - buf_begin, 0);
+  }
+  const int R = r_sel + r_buf;
+  const int chunk = (R + nsplit - 1) / nsplit;
+  const int r_lo = min(R, split * chunk), r_hi = min(R, r_lo + chunk);
+
+  // Online softmax state. m_run / l_run: per query head `col`, identical in
+  // the four lanes col, col+16, col+32, col+48. acc: p.v partial sums of this
+  // lane's V rows, elements 8 vpart .. 8 vpart + 7, relative to m_run.
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  const uint16_t *kbase = static_cast<const uint16_t *>(pool.k) + (size_t)bg * pool.row_cap * D;
+  const uint16_t *vbase = static_cast<const uint16_t *>(pool.v) + (size_t)bg * pool.row_cap * D;
+
+  for (int p0 = r_lo; p0 < r_hi; p0 += kAttendMfmaPiece) {
+    const int plen = min(kAttendMfmaPiece, r_hi - p0);
+    for (int i = tid; i < plen; i += NT)
+      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, pool.row_cap);
+    __syncthreads();
+    // Two register sets: the next step's loads are in flight while this
+    // step's scores and p.v run.
+    int it = wave * kAttendChunk;
+    AttendChunk<D> ca, cb;
+    if (it < plen) attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, col, quad, vslot, vpart);
+    while (it < plen) {
+      if (it + STEP < plen)
+        attend_chunk_load<D>(cb, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
+      attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
+                              s_alpha[wave], lane, col, quad, vslot);
+      it += STEP;
+      if (it >= plen) break;
+      if (it + STEP < plen)
+        attend_chunk_load<D>(ca, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
+      attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
+                              s_alpha[wave], lane, col, quad, vslot);
+      it += STEP;
+    }
+    __syncthreads();
+  }
+
+  // rows of one wave share m_run: lane groups combine by plain sums
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+  if (vslot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vpart + e] = acc[h][e];
+  }
+  if (lane < G) {
+    s_m[wave][lane] = m_run;
+    s_l[wave][lane] = l_run;
+  }
+  __syncthreads();
+  attend_finish<NT, G, D>(bg, b, g, hq, nsplit, split, s_m, s_l, s_acc, out, partials, counters,
+                          &s_last);
+}
+
+// ---- fp32: all-VALU variant ------------------------------------------------------
+constexpr int kAttendValuThreads = 512;
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kAttendValuThreads)
+    k_gather_attend_valu(kv_pool pool, const T *__restrict__ q, int hq, float scale_log2,
+                         const int32_t *__restrict__ sel_units, int sel_cap,
+                         const int32_t *__restrict__ sel_n, float *__restrict__ out,
+                         float *__restrict__ partials, int32_t *counters) {
+  constexpr int NT = kAttendValuThreads, NW = NT / 64;
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane (one 16-byte load)
   constexpr int LPR = D / EPL;               // lanes per row
   constexpr int RPI = 64 / LPR;              // rows per wave instruction
-  constexpr int UNR = kAttendRowsPerWave / RPI;
-  constexpr int NW = kAttendWaves;
+  constexpr int UNR = (G >= 4 ? 4 : 8);       // row pieces in flight per lane group
   __shared__ int s_psum[kMaxSel];
   __shared__ int s_start[kMaxSel];
-  __shared__ int s_rowtab[kAttendThreads];
+  __shared__ int s_rowtab[NT];
   __shared__ int s_wsum[NW];
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
@@ -532,7 +954,6 @@ __global__ void __launch_bounds__(kAttendThreads)
   const int part = lane % LPR, slot = lane / LPR;
   const int nsplit = gridDim.x, split = blockIdx.x;
 
-  // ---- queries of the group, pre-scaled so that exp2 gives the softmax
   float qf[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -542,41 +963,9 @@ __global__ void __launch_bounds__(kAttendThreads)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[h][e] *= scale_log2;
   }
-
-  // ---- selected units -> LDS prefix table (block-wide scan of sizes)
-  const int n = min(min(sel_n[bg], sel_cap), kMaxSel);
-  const int32_t *su = sel_units + (size_t)bg * sel_cap;
-  const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
-  const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
-  int carry = 0;
-  for (int base = 0; base < n; base += kAttendThreads) {
-    const int i = base + tid;
-    int sz = 0;
-    if (i < n) {
-      const int u = su[i];
-      const bool valid = u >= 0 && u < pool.unit_cap;  // foreign ids count as empty units
-      sz = valid ? max(usz[u], 0) : 0;
-      s_start[i] = valid ? ust[u] : 0;
-    }
-    int incl = sz;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
-    int off = carry, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) off += s_wsum[w];
-      tot += s_wsum[w];
-    }
-    if (i < n) s_psum[i] = off + incl - sz;
-    carry += tot;
-    __syncthreads();
-  }
-  const int r_sel = carry;
+  int n;
+  const int r_sel = attend_load_selection<NT>(pool, bg, sel_units + (size_t)bg * sel_cap, sel_n,
+                                              sel_cap, &n, s_psum, s_start, s_wsum);
   int r_buf = 0, buf_begin = 0;
   if (pool.buf_cap > 0) {
     buf_begin = pool.buf_begin[b];
@@ -597,25 +986,12 @@ __global__ void __launch_bounds__(kAttendThreads)
   const T *kbase = static_cast<const T *>(pool.k) + (size_t)bg * pool.row_cap * D + part * EPL;
   const T *vbase = static_cast<const T *>(pool.v) + (size_t)bg * pool.row_cap * D + part * EPL;
 
-  for (int p0 = r_lo; p0 < r_hi; p0 += kAttendThreads) {
-    const int plen = min(kAttendThreads, r_hi - p0);
-    if (tid < plen) {
-      const int j = p0 + tid;
-      int row;
-      if (j < r_sel) {
-        int lo = 0, hi = n - 1;  // last i with s_psum[i] <= j
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_psum[mid] <= j) lo = mid; else hi = mid - 1;
-        }
-        row = s_start[lo] + (j - s_psum[lo]);
-      } else {
-        row = buf_begin + (j - r_sel);
-      }
-      s_rowtab[tid] = min(max(row, 0), pool.row_cap - 1);
-    }
+  for (int p0 = r_lo; p0 < r_hi; p0 += NT) {
+    const int plen = min(NT, r_hi - p0);
+    if (tid < plen)
+      s_rowtab[tid] = attend_row_of(p0 + tid, n, r_sel, buf_begin, s_psum, s_start, pool.row_cap);
     __syncthreads();
-    for (int it = wave * kAttendRowsPerWave; it < plen; it += NW * kAttendRowsPerWave) {
+    for (int it = wave * UNR * RPI; it < plen; it += NW * UNR * RPI) {
       uint4 kv[UNR], vv[UNR];
       bool ok[UNR];
 #pragma unroll
@@ -636,8 +1012,7 @@ __global__ void __launch_bounds__(kAttendThreads)
           float d0 = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[h][e], kf[e], d0);
-#pragma unroll
-          for (int o = LPR / 2; o >= 1; o >>= 1) d0 += __shfl_xor(d0, o);
+          d0 = group_sum<LPR>(d0);
           s[uu][h] = ok[uu] ? d0 : -INFINITY;
         }
       }
@@ -669,8 +1044,6 @@ __global__ void __launch_bounds__(kAttendThreads)
     }
     __syncthreads();
   }
-
-  // ---- merge the row groups of the wave (lanes with equal `part`)
 #pragma unroll
   for (int o = LPR; o < 64; o <<= 1) {
 #pragma unroll
@@ -700,49 +1073,8 @@ __global__ void __launch_bounds__(kAttendThreads)
     }
   }
   __syncthreads();
-  // ---- merge the waves (in order); one share: write the output directly
-  const size_t pstride = (size_t)G * (D + 2);
-  float *mine = partials + ((size_t)bg * nsplit + split) * pstride;
-  for (int i = tid; i < G * D; i += kAttendThreads) {
-    const int h = i / D, e = i % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_m[w][h]);
-    float a = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sc = safe_scale(s_m[w][h], mx);
-      a += s_acc[w][h][e] * sc;
-      lsum += s_l[w][h] * sc;
-    }
-    if (nsplit == 1) {
-      out[((size_t)b * hq + g * G + h) * D + e] = lsum > 0.f ? a / lsum : 0.f;
-    } else {
-      mine[h * (D + 2) + e] = a;
-      if (e == 0) {
-        mine[h * (D + 2) + D] = mx;
-        mine[h * (D + 2) + D + 1] = lsum;
-      }
-    }
-  }
-  if (nsplit == 1) return;
-  if (!last_block_arrives(&counters[bg], nsplit, &s_last)) return;
-  // ---- final merge over shares, in share order
-  const float *allp = partials + (size_t)bg * nsplit * pstride;
-  for (int i = tid; i < G * D; i += kAttendThreads) {
-    const int h = i / D, e = i % D;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, allp[sp * pstride + h * (D + 2) + D]);
-    float a = 0.f, lsum = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float *pp = allp + sp * pstride + h * (D + 2);
-      const float sc = safe_scale(pp[D], mx);
-      a += pp[e] * sc;
-      lsum += pp[D + 1] * sc;
-    }
-    out[((size_t)b * hq + g * G + h) * D + e] = lsum > 0.f ? a / lsum : 0.f;
-  }
-  if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  attend_finish<NT, G, D>(bg, b, g, hq, nsplit, split, s_m, s_l, s_acc, out, partials, counters,
+                          &s_last);
 }
 
 int attend_num_splits(const kv_pool *pool, int max_rows) {
@@ -752,7 +1084,7 @@ int attend_num_splits(const kv_pool *pool, int max_rows) {
   long by_grid = (kAttendTargetBlocks + bh - 1) / bh;
   long ns = by_rows < by_grid ? by_rows : by_grid;
   if (ns < 1) ns = 1;
-  if (ns > 64) ns = 64;
+  if (ns > kMaxSplits) ns = kMaxSplits;
   return (int)ns;
 }
 
@@ -763,10 +1095,17 @@ static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, flo
                                  hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
-#define KVC_ATT(GG)                                                                            \
-  k_gather_attend<T, D, GG><<<grid, kAttendThreads, 0, s>>>(*pool, (const T *)q, hq,           \
-                                                            scale_log2, sel_units, sel_cap,    \
-                                                            sel_n, out, partials, counters)
+#define KVC_ATT(GG)                                                                             \
+  do {                                                                                          \
+    if constexpr (sizeof(T) == 2)                                                               \
+      k_gather_attend_mfma<D, GG><<<grid, kAttendThreads, 0, s>>>(                              \
+          *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_cap, sel_n, out, partials, \
+          counters);                                                                            \
+    else                                                                                        \
+      k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                       \
+          *pool, (const T *)q, hq, scale_log2, sel_units, sel_cap, sel_n, out, partials,        \
+          counters);                                                                            \
+  } while (0)
   switch (G) {
     case 1: KVC_ATT(1); break;
     case 2: KVC_ATT(2); break;

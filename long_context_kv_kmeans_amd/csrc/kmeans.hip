@@ -113,8 +113,7 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
   sq = fmaf(bf16_bits_to_f32(b1), bf16_bits_to_f32(b1), sq);
   sq = fmaf(bf16_bits_to_f32(b2), bf16_bits_to_f32(b2), sq);
   sq = fmaf(bf16_bits_to_f32(b3), bf16_bits_to_f32(b3), sq);
-#pragma unroll
-  for (int o = TPR / 2; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+  sq = group_sum<TPR>(sq);
   const int t = row / 32, m = row % 32, s = e0 / 16, hf = (e0 % 16) / 8, j0 = e0 % 8;
   uint16_t *tile_base = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
   uint2 pk;
@@ -602,8 +601,7 @@ __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
       const float r = bf16_bits_to_f32(b[e]);
       sq = fmaf(r, r, sq);
     }
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+    sq = group_sum<LPR>(sq);
     const int t = k / 32, m = k % 32, e0 = part * 8;
     uint16_t *tile_base = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
     if (slot == 0) {

@@ -53,11 +53,36 @@ template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4 &v, f
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+// DPP lane moves (gfx9 encodings): mirror a 16-lane row, mirror each 8-lane
+// half row, and permute within quads.
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
+
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32, 64); every lane of a
+// group receives the group total. Within a 16-lane row the pairing is
+// mirror -> half mirror -> quad swaps: after the row-mirror step lane i holds
+// x_i + x_15-i, after the half-mirror step it holds the four lanes
+// {j, 7-j, 8+j, 15-j} (j = i mod 8), and the two quad swaps combine the four
+// such sets of a row. Wider groups add an exchange across rows. All lanes must
+// be active.
+template <int N> __device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
+  if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+  if constexpr (N >= 4) v += dpp_mov<kDppQuadSwap2>(v);
+  v += dpp_mov<kDppQuadSwap1>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32);
   return v;
 }
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 // Map a hardware workgroup id to a logical one so that each XCD (which
 // receives ids x, x+8, x+16, ...) processes one contiguous range of logical
