@@ -5,8 +5,9 @@ One step = one pass of the whole path over one Qwen3-8B-shaped layer
 (8 KV heads, 32 query heads, head dim 128, bf16, batch 1, 32768 prefill keys
 per head, C = 2048, 10 Lloyd rounds):
   prefill : kv_cluster_build (K-means assign/update x10, CSR pack of K/V);
-  decode  : 256 steps of kv_boundary -> kv_select -> kv_gather_attend on the
-            seeded query walk, replayed from one captured HIP graph.
+  decode  : 256 steps of kv_boundary_select (boundary test + selection in one
+            launch) -> kv_gather_attend on the seeded query walk, replayed from
+            one captured HIP graph.
 Inputs are synthetic (seeded Gaussian-mixture keys, random values and query
 walks) and resident in HBM before timing starts.
 
@@ -14,8 +15,12 @@ Printed JSON (one line): value = prefill keys clustered per second of whole
 steps (the decode loop included); the split into prefill time and decode
 microseconds per layer-step, the decode bytes moved per layer-step and the
 fraction of HBM peak are extra fields. ``roofline`` covers the dominant
-kernel, the MFMA K-means assignment, timed with HIP events on its stream;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
+kernel by total time per step, the decode gather-attend (HBM bound);
+``roofline_assign`` covers the MFMA K-means assignment. Both kernels are
+timed with HIP events on the stream they run on around back-to-back
+launches queued behind a GPU sleep, so that host enqueue gaps do not enter
+the interval. ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same work.
 """
 from __future__ import annotations
 
@@ -83,6 +88,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-lloyd-iters", type=int, default=3)
     ap.add_argument("--assign-reps", type=int, default=20)
+    ap.add_argument("--attend-reps", type=int, default=100)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
@@ -129,8 +135,8 @@ def main():
 
     def decode(record=None):
         for t in range(T):
-            kvc.kv_boundary(q[t - 1] if t else None, q[t], cfg.tau, flags[t])
-            kvc.kv_select(pool, q[t], cfg.budget, flags[t], sel, sel_n, sel_rows, ws=ws_sel)
+            kvc.kv_boundary_select(pool, q[t - 1] if t else None, q[t], cfg.tau, cfg.budget,
+                                   flags[t], sel, sel_n, sel_rows, ws=ws_sel)
             kvc.kv_gather_attend(pool, q[t], cfg.scale, sel, sel_n, cfg.budget, out[t], ws=ws_att)
             if record is not None:
                 record.append(sel_rows.clone())
@@ -188,23 +194,46 @@ def main():
     dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
     dec_us = dec_ms * 1e3 / T
 
-    # dominant kernel: the MFMA assignment, timed live with HIP events on its stream
+    def launch_ms(fn, reps):
+        """Mean GPU time per launch of fn: `reps` back-to-back launches on
+        `stream` between two HIP events, all queued behind a GPU sleep so that
+        the host's enqueue rate does not stretch the interval."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda._sleep(20_000_000)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # gather-attend on the final step's selection (the state the graph left)
+    sel_units_n = int(sel_n.sum().item())
+    att_rows = int(sel_rows.sum().item())
+    att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, q[T - 1], cfg.scale, sel, sel_n,
+                                                    cfg.budget, out[T - 1], ws=ws_att),
+                       args.attend_reps)
+    att_bytes = (att_rows * 2 * d * e          # selected K and V rows
+                 + B * Hq * d * e              # queries
+                 + B * Hq * d * 4              # fp32 output
+                 + sel_units_n * 12)           # unit id, start, size per selected unit
+    att_gbs = att_bytes / (att_ms * 1e-3) / 1e9
+
+    # MFMA K-means assignment against prepared centroids (the kernel the
+    # prefill runs once per Lloyd round)
     cents = pool.unit_mean[:, :, :C].reshape(B * H, C, d).contiguous()
     k3 = keys.reshape(B * H, N, d)
     lab2 = torch.zeros(B * H, N, dtype=torch.int32, device="cuda")
-    ws_asg = kvc.workspace(kvc.lib().kv_cluster_build_workspace(B, H, N, d, C, kvc.dtype_code(tdt)))
-    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.assign_reps)]
+    ws_asg = kvc.workspace(kvc.lib().kv_kmeans_assign_workspace(B * H, C, d, kvc.dtype_code(tdt)))
     with torch.cuda.stream(stream):
-        kvc.kv_kmeans_assign(k3, cents, lab2, ws=ws_asg)
-        for a, b in aev:
-            a.record(stream)
-            kvc.kv_kmeans_assign(k3, cents, lab2, ws=ws_asg)
-            b.record(stream)
-    torch.cuda.synchronize()
-    asg_ms = float(np.mean([a.elapsed_time(b) for a, b in aev]))
+        kvc.kv_kmeans_prepare(cents, tdt, ws_asg)
+    asg_ms = launch_ms(lambda: kvc.kv_kmeans_assign_prepared(k3, cents, lab2, ws_asg),
+                       args.assign_reps)
     flops = 2.0 * B * H * N * C * d
     achieved = flops / (asg_ms * 1e-3) / 1e12
+    share = {"k_gather_attend": T * att_ms / ms_step, "k_assign_mfma": cfg.iters * asg_ms / ms_step}
 
     keys_per_step = B * H * N
     res = {
@@ -228,10 +257,15 @@ def main():
         "decode_us_per_layer_step": dec_us,
         "decode_bytes_per_layer_step": dec_bytes,
         "decode_hbm_frac": dec_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
-        "roofline": {"bound": "mfma", "kernel": "k_assign_mfma (via kv_kmeans_assign)",
-                     "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                     "flops_per_launch": flops, "avg_launch_ms": asg_ms},
+        "roofline": {"bound": "hbm", "kernel": "k_gather_attend_mfma (kv_gather_attend)",
+                     "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": att_bytes, "avg_launch_ms": att_ms},
+        "roofline_assign": {"bound": "mfma", "kernel": "k_assign_mfma (kv_kmeans_assign_prepared)",
+                            "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                            "flops_per_launch": flops, "avg_launch_ms": asg_ms},
+        "time_share_per_step": share,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

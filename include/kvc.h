@@ -139,6 +139,25 @@ kv_status kv_kmeans_assign(const void *keys, const float *centroids, int32_t n_h
                            kv_dtype dtype, int32_t *labels, void *ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* The assignment step split in two, for callers that assign several key
+ * sets against one set of centroids (the centroids are converted once).
+ * kv_kmeans_prepare writes the centroids' assignment form into ws (same size
+ * as kv_kmeans_assign_workspace: for KV_BF16 the bf16 split fragments and
+ * half norms, for KV_F32 the half norms). kv_kmeans_assign_prepared then
+ * labels keys exactly as kv_kmeans_assign would with those centroids; it
+ * reads ws without modifying it, so ws stays valid until the caller
+ * overwrites it. centroids must be the array given to kv_kmeans_prepare (the
+ * fp32 path reads it; the bf16 path reads only ws). Both calls validate like
+ * kv_kmeans_assign. kv_kmeans_assign = kv_kmeans_prepare followed by
+ * kv_kmeans_assign_prepared on the same stream. */
+kv_status kv_kmeans_prepare(const float *centroids, int32_t n_heads, int32_t head_dim,
+                            int32_t n_clusters, kv_dtype dtype, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+kv_status kv_kmeans_assign_prepared(const void *keys, const float *centroids, int32_t n_heads,
+                                    int32_t n_keys, int32_t head_dim, int32_t n_clusters,
+                                    kv_dtype dtype, int32_t *labels, const void *ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
 /* One Lloyd update step: centroids_out[k] = mean of keys labelled k, or
  * centroids_in[k] when the cluster is empty. counts (nullable) receives the
  * member counts [n_heads][n_clusters]. centroids_out may alias centroids_in. */
@@ -204,6 +223,22 @@ kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32
                     const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
                     int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
                     hipStream_t stream);
+
+/* Decode steps 1 and 3 in one launch: exactly kv_boundary(q_prev, q_cur,
+ * pool->batch, n_q_heads, pool->head_dim, pool->dtype, tau, flag, r)
+ * followed by kv_select(pool, q_cur, n_q_heads, budget, flag, ...), with the
+ * same results bit for bit (flag, r, selection, scores_out). Each select
+ * workgroup evaluates the boundary test of its own sequence, so a step
+ * without a boundary costs one memory round trip and no second launch.
+ * Pools with a local buffer (buf_cap > 0) get KV_ERR_UNSUPPORTED: there
+ * kv_segment_append of the step runs between the boundary test and the
+ * selection, so the three calls stay separate. Workspace:
+ * kv_select_workspace. flag: [batch] uint8 out; r: NULL or [batch] fp32 out. */
+kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void *q_cur,
+                             int32_t n_q_heads, float tau, int32_t budget, uint8_t *flag,
+                             float *r, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
+                             int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Decode step 4: gather the selected rows and attend. LouisKV note,

@@ -33,10 +33,11 @@ EXPORTED = [
     "kv_status_string",
     "kv_cluster_build_workspace", "kv_cluster_build",
     "kv_kmeans_assign_workspace", "kv_kmeans_assign",
+    "kv_kmeans_prepare", "kv_kmeans_assign_prepared",
     "kv_kmeans_update_workspace", "kv_kmeans_update",
     "kv_boundary",
     "kv_segment_append",
-    "kv_select_workspace", "kv_select",
+    "kv_select_workspace", "kv_select", "kv_boundary_select",
     "kv_gather_attend_workspace", "kv_gather_attend",
 ]
 
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
         "kv_cluster_build": (c_int, [pool_p, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]),
         "kv_kmeans_assign_workspace": (c_size, [c_int, c_int, c_int, c_int]),
         "kv_kmeans_assign": (c_int, [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp, c_size, vp]),
+        "kv_kmeans_prepare": (c_int, [vp, c_int, c_int, c_int, c_int, vp, c_size, vp]),
+        "kv_kmeans_assign_prepared": (c_int, [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp,
+                                              c_size, vp]),
         "kv_kmeans_update_workspace": (c_size, [c_int, c_int, c_int]),
         "kv_kmeans_update": (c_int, [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp,
                                      c_size, vp]),
@@ -95,6 +99,8 @@ def lib() -> ctypes.CDLL:
         "kv_segment_append": (c_int, [pool_p, vp, vp, vp, vp]),
         "kv_select_workspace": (c_size, [pool_p, c_int]),
         "kv_select": (c_int, [pool_p, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, c_size, vp]),
+        "kv_boundary_select": (c_int, [pool_p, vp, vp, c_int, ctypes.c_float, c_int, vp, vp, vp,
+                                       c_int, vp, vp, vp, vp, c_size, vp]),
         "kv_gather_attend_workspace": (c_size, [pool_p, c_int, c_int]),
         "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, c_int, vp, c_int, vp,
                                      vp, c_size, vp]),
@@ -227,6 +233,22 @@ def kv_kmeans_assign(keys, centroids, labels, ws=None, stream=None) -> None:
         _stream(stream)))
 
 
+def kv_kmeans_prepare(centroids, dtype, ws, stream=None) -> None:
+    """centroids [BH, C, D] fp32 -> their assignment form in ws (for keys of `dtype`)."""
+    BH, C, D = centroids.shape
+    _check("kv_kmeans_prepare", lib().kv_kmeans_prepare(
+        _ptr(centroids), BH, D, C, dtype_code(dtype), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kv_kmeans_assign_prepared(keys, centroids, labels, ws, stream=None) -> None:
+    """Labels of keys [BH, N, D] against centroids already prepared in ws."""
+    BH, N, D = keys.shape
+    C = centroids.shape[1]
+    _check("kv_kmeans_assign_prepared", lib().kv_kmeans_assign_prepared(
+        _ptr(keys), _ptr(centroids), BH, N, D, C, dtype_code(keys.dtype), _ptr(labels), _ptr(ws),
+        ws.numel(), _stream(stream)))
+
+
 def kv_kmeans_update(keys, labels, centroids_in, centroids_out, counts=None, ws=None,
                      stream=None) -> None:
     BH, N, D = keys.shape
@@ -263,6 +285,18 @@ def kv_select(pool: Pool, q, budget: int, flag, sel_units, sel_n, sel_rows, scor
     _check("kv_select", lib().kv_select(
         pool.ref(), _ptr(q), Hq, int(budget), _ptr(flag), _ptr(sel_units), sel_units.shape[-1],
         _ptr(sel_n), _ptr(sel_rows), _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kv_boundary_select(pool: Pool, q_prev, q_cur, tau: float, budget: int, flag, sel_units,
+                       sel_n, sel_rows, r=None, scores_out=None, ws=None, stream=None) -> None:
+    """kv_boundary then kv_select in one launch (q_prev None: first decode step)."""
+    Hq = q_cur.shape[1]
+    if ws is None:
+        ws = workspace(kv_select_workspace(pool, Hq))
+    _check("kv_boundary_select", lib().kv_boundary_select(
+        pool.ref(), _ptr(q_prev), _ptr(q_cur), Hq, float(tau), int(budget), _ptr(flag), _ptr(r),
+        _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n), _ptr(sel_rows), _ptr(scores_out),
+        _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def kv_gather_attend_workspace(pool: Pool, n_q_heads: int, max_rows: int) -> int:

@@ -76,6 +76,32 @@ kv_status kv_kmeans_assign(const void *keys, const float *centroids, int32_t n_h
                        stream);
 }
 
+kv_status kv_kmeans_prepare(const float *centroids, int32_t n_heads, int32_t head_dim,
+                            int32_t n_clusters, kv_dtype dtype, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!centroids) return KV_ERR_INVALID_ARG;
+  if (n_heads <= 0 || n_clusters <= 0) return KV_ERR_INVALID_ARG;
+  if (!dims_ok(head_dim) || !dtype_ok(dtype)) return KV_ERR_UNSUPPORTED;
+  if (n_clusters > kMaxClusters) return KV_ERR_UNSUPPORTED;
+  if (!ws || !aligned256(ws) || ws_bytes < assign_ws_bytes(n_heads, n_clusters, head_dim, dtype))
+    return KV_ERR_WORKSPACE;
+  return launch_assign_prepare(centroids, n_heads, head_dim, n_clusters, dtype, ws, stream);
+}
+
+kv_status kv_kmeans_assign_prepared(const void *keys, const float *centroids, int32_t n_heads,
+                                    int32_t n_keys, int32_t head_dim, int32_t n_clusters,
+                                    kv_dtype dtype, int32_t *labels, const void *ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (!keys || !centroids || !labels) return KV_ERR_INVALID_ARG;
+  if (n_heads <= 0 || n_keys <= 0 || n_clusters <= 0) return KV_ERR_INVALID_ARG;
+  if (!dims_ok(head_dim) || !dtype_ok(dtype)) return KV_ERR_UNSUPPORTED;
+  if (n_clusters > kMaxClusters) return KV_ERR_UNSUPPORTED;
+  if (!ws || !aligned256(ws) || ws_bytes < assign_ws_bytes(n_heads, n_clusters, head_dim, dtype))
+    return KV_ERR_WORKSPACE;
+  return launch_assign_prepared(keys, centroids, n_heads, n_keys, head_dim, n_clusters, dtype,
+                                labels, ws, stream);
+}
+
 size_t kv_kmeans_update_workspace(int32_t n_heads, int32_t n_keys, int32_t n_clusters) {
   if (n_heads <= 0 || n_keys <= 0 || n_clusters <= 0) return 0;
   return update_ws_bytes(n_heads, n_keys, n_clusters);
@@ -186,15 +212,18 @@ size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads) {
   return align_up(bh * sizeof(int32_t), 256) + align_up(bh * pool->unit_cap * sizeof(float), 256);
 }
 
-kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
-                    const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
-                    int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
-                    hipStream_t stream) {
+namespace {
+kv_status select_common(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
+                        const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
+                        int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
+                        bool fused, const void *q_prev, float tau, uint8_t *flag_out,
+                        float *r_out, hipStream_t stream) {
   kv_status st = check_pool(pool);
   if (st != KV_OK) return st;
   if (!q || !sel_units || !sel_n || !sel_rows) return KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || budget < 0 || sel_cap <= 0)
     return KV_ERR_INVALID_ARG;
+  if (fused && (!flag_out || tau != tau)) return KV_ERR_INVALID_ARG;
   const int G = n_q_heads / pool->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
   if (sel_cap < (budget < pool->unit_cap ? budget : pool->unit_cap)) return KV_ERR_CAPACITY;
@@ -207,7 +236,26 @@ kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32
                              : reinterpret_cast<float *>(static_cast<char *>(ws) +
                                                          align_up(bh * sizeof(int32_t), 256));
   return launch_select(pool, q, n_q_heads, budget, flag, sel_units, sel_cap, sel_n, sel_rows,
-                       scores, counters, stream);
+                       scores, counters, fused, q_prev, tau, flag_out, r_out, stream);
+}
+}  // namespace
+
+kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
+                    const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
+                    int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  return select_common(pool, q, n_q_heads, budget, flag, sel_units, sel_cap, sel_n, sel_rows,
+                       scores_out, ws, ws_bytes, false, nullptr, 0.f, nullptr, nullptr, stream);
+}
+
+kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void *q_cur,
+                             int32_t n_q_heads, float tau, int32_t budget, uint8_t *flag,
+                             float *r, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
+                             int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  if (pool && pool->buf_cap > 0) return KV_ERR_UNSUPPORTED;  // the segment append goes between
+  return select_common(pool, q_cur, n_q_heads, budget, nullptr, sel_units, sel_cap, sel_n,
+                       sel_rows, scores_out, ws, ws_bytes, true, q_prev, tau, flag, r, stream);
 }
 
 size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t max_rows) {

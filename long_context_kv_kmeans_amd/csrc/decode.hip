@@ -52,14 +52,58 @@ __device__ __forceinline__ bool last_block_arrives(int32_t *counter, int nblocks
 // order), so r is reproducible bit for bit.
 constexpr int kBoundaryHeadsPerWave = 8;
 
+// r of sequence b, computed by waves 0..3 of the calling workgroup (all of
+// its threads must call: the partial sums meet in LDS `part`[4]). Every
+// thread receives r. Callers of any workgroup size get the same bits.
+template <typename T, int D>
+__device__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
+                            int b, float *part) {
+  constexpr int EPL = D / 64;
+  constexpr int HPW = kBoundaryHeadsPerWave;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < 4) {
+    float csum = 0.f;
+    for (int h0 = wave * HPW; h0 < hq; h0 += 4 * HPW) {
+      T a[HPW][EPL], c[HPW][EPL];
+#pragma unroll
+      for (int i = 0; i < HPW; ++i) {
+        const int h = h0 + i;
+        const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          a[i][e] = q_prev[o + e];
+          c[i][e] = q_cur[o + e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < HPW; ++i) {
+        float dot = 0.f, n1 = 0.f, n2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float x = Elem<T>::to_f32(a[i][e]), y = Elem<T>::to_f32(c[i][e]);
+          dot = fmaf(x, y, dot);
+          n1 = fmaf(x, x, n1);
+          n2 = fmaf(y, y, n2);
+        }
+        dot = wave_sum(dot);
+        n1 = wave_sum(n1);
+        n2 = wave_sum(n2);
+        const float cosv = (n1 > 0.f && n2 > 0.f) ? dot / (sqrtf(n1) * sqrtf(n2)) : 0.f;
+        if (h0 + i < hq) csum += cosv;
+      }
+    }
+    if (lane == 0) part[wave] = csum;
+  }
+  __syncthreads();
+  return (((part[0] + part[1]) + part[2]) + part[3]) / (float)hq;
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_boundary(const T *__restrict__ q_prev,
                                                   const T *__restrict__ q_cur, int hq, float tau,
                                                   uint8_t *__restrict__ flag, float *__restrict__ r) {
-  constexpr int EPL = D / 64;
-  constexpr int HPW = kBoundaryHeadsPerWave;
   __shared__ float part[4];
-  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x;
   if (q_prev == nullptr) {
     if (threadIdx.x == 0) {
       flag[b] = 1;
@@ -67,40 +111,8 @@ __global__ void __launch_bounds__(256) k_boundary(const T *__restrict__ q_prev,
     }
     return;
   }
-  float csum = 0.f;
-  for (int h0 = wave * HPW; h0 < hq; h0 += 4 * HPW) {
-    T a[HPW][EPL], c[HPW][EPL];
-#pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-      const int h = h0 + i;
-      const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + lane * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        a[i][e] = q_prev[o + e];
-        c[i][e] = q_cur[o + e];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-      float dot = 0.f, n1 = 0.f, n2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float x = Elem<T>::to_f32(a[i][e]), y = Elem<T>::to_f32(c[i][e]);
-        dot = fmaf(x, y, dot);
-        n1 = fmaf(x, x, n1);
-        n2 = fmaf(y, y, n2);
-      }
-      dot = wave_sum(dot);
-      n1 = wave_sum(n1);
-      n2 = wave_sum(n2);
-      const float cosv = (n1 > 0.f && n2 > 0.f) ? dot / (sqrtf(n1) * sqrtf(n2)) : 0.f;
-      if (h0 + i < hq) csum += cosv;
-    }
-  }
-  if (lane == 0) part[wave] = csum;
-  __syncthreads();
+  const float rv = boundary_r<T, D>(q_prev, q_cur, hq, b, part);
   if (threadIdx.x == 0) {
-    const float rv = (((part[0] + part[1]) + part[2]) + part[3]) / (float)hq;
     flag[b] = rv < tau ? 1 : 0;
     if (r) r[b] = rv;
   }
@@ -268,34 +280,61 @@ __device__ __forceinline__ unsigned long long unit_key(float score, int u) {
   return ((unsigned long long)float_order_key(score) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
 }
 
-template <typename T, int D, int KPT>
+// FUSED: the workgroup first runs the boundary test of its sequence on
+// (q_prev, q) itself (flag_out / r_out written once per sequence) instead of
+// reading flag. The unit count and the group's queries are requested in the
+// same memory round trip as the decision's inputs.
+template <typename T, int D, int KPT, bool FUSED>
 __global__ void __launch_bounds__(kSelectThreads)
     k_select(kv_pool pool, const T *__restrict__ q, int hq, int group, int budget,
              const uint8_t *__restrict__ flag, int32_t *__restrict__ sel_units, int sel_cap,
              int32_t *__restrict__ sel_n, int32_t *__restrict__ sel_rows, float *__restrict__ scores,
-             int32_t *counters) {
+             int32_t *counters, const T *__restrict__ q_prev, float tau,
+             uint8_t *__restrict__ flag_out, float *__restrict__ r_out) {
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per 16-byte lane load
   constexpr int LPU = D / EPL;               // lanes per index vector
   constexpr int UPW = 64 / LPU;              // units per wave instruction
   constexpr int UNR = 4;
   const int H = pool.n_kv_heads;
   const int bg = blockIdx.y, b = bg / H, g = bg % H;
-  if (flag != nullptr && flag[b] == 0) return;
-  const int U = min(max(pool.n_cand[b], 0), pool.unit_cap);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int part = lane % LPU, slot = lane / LPU;
+  const int n_cand = pool.n_cand[b];
+  uint4 qv[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    if (h < group)
+      qv[h] = *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * group + h) * D + part * EPL);
+  if constexpr (FUSED) {
+    __shared__ float s_part[4];
+    int f = 1;
+    float rv = __builtin_nanf("");
+    if (q_prev != nullptr) {
+      rv = boundary_r<T, D>(q_prev, q, hq, b, s_part);
+      f = rv < tau ? 1 : 0;
+    }
+    if (blockIdx.x == 0 && g == 0 && tid == 0) {
+      flag_out[b] = (uint8_t)f;
+      if (r_out) r_out[b] = rv;
+    }
+    if (!f) return;
+  } else {
+    if (flag != nullptr && flag[b] == 0) return;
+  }
+  const int U = min(max(n_cand, 0), pool.unit_cap);
 
   // ---- scoring: s_u = (sum_h q_h) . idx_u, fp32
   float qs[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qs[e] = 0.f;
-  for (int h = 0; h < group; ++h) {
-    const uint4 v =
-        *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * group + h) * D + part * EPL);
-    float f[EPL];
-    unpack16<T>(v, f);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qs[e] += f[e];
+  for (int h = 0; h < 8; ++h) {
+    if (h < group) {
+      float f[EPL];
+      unpack16<T>(qv[h], f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qs[e] += f[e];
+    }
   }
   const T *idx = static_cast<const T *>(pool.unit_index) + (size_t)bg * pool.unit_cap * D;
   float *sc = scores + (size_t)bg * pool.unit_cap;
@@ -322,19 +361,24 @@ __global__ void __launch_bounds__(kSelectThreads)
     }
   }
 
-  // ---- completion: the last block of (b, g) selects
-  __shared__ int s_last;
-  if (!last_block_arrives(&counters[bg], (int)gridDim.x, &s_last)) return;
-
+  // ---- completion: the last block of (b, g) selects. Unit sizes are
+  // requested before the arrival so that they land with the store acks.
   const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
-  unsigned long long key[KPT];
   int sz[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int u = tid * KPT + j;
     const int s = u < U ? usz[u] : 0;
     sz[j] = s > 0 ? s : 0;
-    key[j] = (u < U && s > 0) ? unit_key(coherent_load(&sc[u]), u) : 0ull;
+  }
+  __shared__ int s_last;
+  if (!last_block_arrives(&counters[bg], (int)gridDim.x, &s_last)) return;
+
+  unsigned long long key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int u = tid * KPT + j;
+    key[j] = sz[j] > 0 ? unit_key(coherent_load(&sc[u]), u) : 0ull;
   }
 
   __shared__ int hw[kSelectWaves][256];
@@ -464,36 +508,46 @@ template <typename T, int D>
 static kv_status select_dispatch(const kv_pool *pool, const void *q, int hq, int budget,
                                  const uint8_t *flag, int32_t *sel_units, int sel_cap,
                                  int32_t *sel_n, int32_t *sel_rows, float *scores,
-                                 int32_t *counters, hipStream_t s) {
+                                 int32_t *counters, bool fused, const void *q_prev, float tau,
+                                 uint8_t *flag_out, float *r_out, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(select_num_blocks(pool), pool->batch * pool->n_kv_heads);
   const int per = (pool->unit_cap + kSelectThreads - 1) / kSelectThreads;
-#define KVC_SEL(K)                                                                            \
-  k_select<T, D, K><<<grid, kSelectThreads, 0, s>>>(*pool, (const T *)q, hq, G, budget, flag,  \
-                                                     sel_units, sel_cap, sel_n, sel_rows,      \
-                                                     scores, counters)
-  if (per <= 2) KVC_SEL(2);
-  else if (per <= 8) KVC_SEL(8);
-  else if (per <= kSelectMaxKeysPerThread) KVC_SEL(kSelectMaxKeysPerThread);
+#define KVC_SEL(K, F)                                                                          \
+  k_select<T, D, K, F><<<grid, kSelectThreads, 0, s>>>(                                        \
+      *pool, (const T *)q, hq, G, budget, flag, sel_units, sel_cap, sel_n, sel_rows, scores,   \
+      counters, (const T *)q_prev, tau, flag_out, r_out)
+#define KVC_SEL2(K)         \
+  do {                      \
+    if (fused)              \
+      KVC_SEL(K, true);     \
+    else                    \
+      KVC_SEL(K, false);    \
+  } while (0)
+  if (per <= 2) KVC_SEL2(2);
+  else if (per <= 8) KVC_SEL2(8);
+  else if (per <= kSelectMaxKeysPerThread) KVC_SEL2(kSelectMaxKeysPerThread);
   else return KV_ERR_UNSUPPORTED;
+#undef KVC_SEL2
 #undef KVC_SEL
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
 kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         const uint8_t *flag, int32_t *sel_units, int sel_cap, int32_t *sel_n,
-                        int32_t *sel_rows, float *scores, int32_t *counters, hipStream_t s) {
+                        int32_t *sel_rows, float *scores, int32_t *counters, bool fused,
+                        const void *q_prev, float tau, uint8_t *flag_out, float *r_out,
+                        hipStream_t s) {
+#define KVC_SD(T, D)                                                                          \
+  select_dispatch<T, D>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n, sel_rows, scores, \
+                        counters, fused, q_prev, tau, flag_out, r_out, s)
+  kv_status st;
   if (pool->dtype == KV_BF16)
-    return pool->head_dim == 128
-               ? select_dispatch<uint16_t, 128>(pool, q, hq, budget, flag, sel_units, sel_cap,
-                                                sel_n, sel_rows, scores, counters, s)
-               : select_dispatch<uint16_t, 64>(pool, q, hq, budget, flag, sel_units, sel_cap,
-                                               sel_n, sel_rows, scores, counters, s);
-  return pool->head_dim == 128
-             ? select_dispatch<float, 128>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n,
-                                           sel_rows, scores, counters, s)
-             : select_dispatch<float, 64>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n,
-                                          sel_rows, scores, counters, s);
+    st = pool->head_dim == 128 ? KVC_SD(uint16_t, 128) : KVC_SD(uint16_t, 64);
+  else
+    st = pool->head_dim == 128 ? KVC_SD(float, 128) : KVC_SD(float, 64);
+#undef KVC_SD
+  return st;
 }
 
 // ---------------------------------------------------------------- gather + attend

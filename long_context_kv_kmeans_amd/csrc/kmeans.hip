@@ -366,18 +366,26 @@ kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, h
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
-kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
-                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s, bool frags_ready) {
+kv_status launch_assign_prepare(const float *cent, int bh, int d, int c, kv_dtype dt, void *ws,
+                                hipStream_t s) {
+  if (dt == KV_BF16) return launch_prep_frags(cent, bh, d, c, ws, s);
+  float *hn = static_cast<float *>(ws);
+  const long tot = (long)bh * c;
+  if (d == 128)
+    k_halfnorm_f32<128><<<(unsigned)((tot + 255) / 256), 256, 0, s>>>(cent, hn, tot);
+  else
+    k_halfnorm_f32<64><<<(unsigned)((tot + 255) / 256), 256, 0, s>>>(cent, hn, tot);
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, int n, int d, int c,
+                                 kv_dtype dt, int32_t *labels, const void *ws, hipStream_t s) {
   if (dt == KV_BF16) {
     const int ntile = (c + 31) / 32;
-    uint16_t *frags = static_cast<uint16_t *>(ws);
+    const uint16_t *frags = static_cast<const uint16_t *>(ws);
     constexpr int NCB = kAssignColBlocks;
     const int bph = (n + 128 * NCB - 1) / (128 * NCB);
     const int total = bph * bh;
-    if (!frags_ready) {
-      const kv_status st = launch_prep_frags(cent, bh, d, c, ws, s);
-      if (st != KV_OK) return st;
-    }
     if (d == 128)
       k_assign_mfma<128, NCB, kAssignMinWaves><<<total, 256, 0, s>>>(
           (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
@@ -385,18 +393,23 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
       k_assign_mfma<64, NCB, kAssignMinWaves><<<total, 256, 0, s>>>(
           (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
   } else {
-    float *hn = static_cast<float *>(ws);
-    const long tot = (long)bh * c;
+    const float *hn = static_cast<const float *>(ws);
     const dim3 grid((n + 255) / 256, bh);
-    if (d == 128) {
-      k_halfnorm_f32<128><<<(unsigned)((tot + 255) / 256), 256, 0, s>>>(cent, hn, tot);
+    if (d == 128)
       k_assign_f32<128><<<grid, 256, 0, s>>>((const float *)keys, cent, hn, labels, n, c);
-    } else {
-      k_halfnorm_f32<64><<<(unsigned)((tot + 255) / 256), 256, 0, s>>>(cent, hn, tot);
+    else
       k_assign_f32<64><<<grid, 256, 0, s>>>((const float *)keys, cent, hn, labels, n, c);
-    }
   }
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
+                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s, bool frags_ready) {
+  if (!(frags_ready && dt == KV_BF16)) {
+    const kv_status st = launch_assign_prepare(cent, bh, d, c, dt, ws, s);
+    if (st != KV_OK) return st;
+  }
+  return launch_assign_prepared(keys, cent, bh, n, d, c, dt, labels, ws, s);
 }
 
 // ---------------------------------------------------------------- update

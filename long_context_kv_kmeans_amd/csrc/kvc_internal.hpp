@@ -112,6 +112,10 @@ kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float
                                 int n, int c, int d, kv_dtype dt, hipStream_t s);
 size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt);
 kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, hipStream_t s);
+kv_status launch_assign_prepare(const float *cent, int bh, int d, int c, kv_dtype dt, void *ws,
+                                hipStream_t s);
+kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, int n, int d, int c,
+                                 kv_dtype dt, int32_t *labels, const void *ws, hipStream_t s);
 kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
                         kv_dtype dt, int32_t *labels, void *ws, hipStream_t s,
                         bool frags_ready = false);
@@ -131,9 +135,13 @@ kv_status launch_boundary(const void *q_prev, const void *q_cur, int batch, int 
 kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
                                 const uint8_t *flag, hipStream_t s);
 int select_num_blocks(const kv_pool *pool);
+// fused: run the boundary test on (q_prev, q) inside the select kernel and
+// write flag_out / r_out instead of reading flag.
 kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         const uint8_t *flag, int32_t *sel_units, int sel_cap, int32_t *sel_n,
-                        int32_t *sel_rows, float *scores, int32_t *counters, hipStream_t s);
+                        int32_t *sel_rows, float *scores, int32_t *counters, bool fused,
+                        const void *q_prev, float tau, uint8_t *flag_out, float *r_out,
+                        hipStream_t s);
 int attend_num_splits(const kv_pool *pool, int max_rows);
 kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
                                const int32_t *sel_units, int sel_cap, const int32_t *sel_n,

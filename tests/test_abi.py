@@ -59,6 +59,27 @@ def test_boundary_validation():
                          None) == kvc.KV_ERR_INVALID_ARG
 
 
+def test_boundary_select_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    f = ctypes.c_float(0.7)
+    p = _fake_pool()
+    need = L.kv_select_workspace(ctypes.byref(p), 32)
+    assert need > 0
+    # the same checks as kv_select, plus flag out and a finite tau
+    assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, f, 64, None, None, a, 256, a, a,
+                                None, a, need, None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, ctypes.c_float(float("nan")), 64,
+                                a, None, a, 256, a, a, None, a, need, None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_boundary_select(ctypes.byref(p), None, a, 24, f, 64, a, None, a, 256, a, a,
+                                None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # G = 3
+    assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, f, 64, a, None, a, 256, a, a,
+                                None, a, need - 1, None) == kvc.KV_ERR_WORKSPACE
+    pb = _fake_pool(buf_cap=64, seg_sum=0x10000)
+    assert L.kv_boundary_select(ctypes.byref(pb), None, a, 32, f, 64, a, None, a, 256, a, a,
+                                None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # local buffer
+
+
 def test_pool_validation():
     L = kvc.lib()
     a = ctypes.c_void_p(0x10000)
@@ -130,6 +151,18 @@ def test_cluster_build_validation():
                               None) == kvc.KV_ERR_WORKSPACE
     assert L.kv_kmeans_assign(a, a, 8, 1000, 128, 40000, kvc.KV_BF16, a, a, 1 << 30,
                               None) == kvc.KV_ERR_UNSUPPORTED  # too many clusters
+    need = L.kv_kmeans_assign_workspace(8, 64, 128, kvc.KV_BF16)
+    assert L.kv_kmeans_prepare(a, 8, 128, 64, kvc.KV_BF16, a, need - 1,
+                               None) == kvc.KV_ERR_WORKSPACE
+    assert L.kv_kmeans_prepare(None, 8, 128, 64, kvc.KV_BF16, a, need,
+                               None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_kmeans_prepare(a, 8, 96, 64, kvc.KV_BF16, a, need,
+                               None) == kvc.KV_ERR_UNSUPPORTED  # head_dim
+    assert L.kv_kmeans_assign_prepared(a, a, 8, 0, 128, 64, kvc.KV_BF16, a, a, need,
+                                       None) == kvc.KV_ERR_INVALID_ARG  # no keys
+    assert L.kv_kmeans_assign_prepared(a, a, 8, 1000, 128, 64, kvc.KV_BF16, a,
+                                       ctypes.c_void_p(0x10010), need,
+                                       None) == kvc.KV_ERR_WORKSPACE  # misaligned
     assert L.kv_kmeans_update(a, a, a, a, None, 8, 1000, 128, 64, kvc.KV_BF16, a, 10,
                               None) == kvc.KV_ERR_WORKSPACE
 

@@ -111,3 +111,30 @@ def test_decode_long_output_segments_small_buffer():
 def test_decode_long_output_segments():
     cfg = wl.get_config(2, iters=3)
     _run(cfg, 3000, [0], compare_every=7)
+
+
+@pytest.mark.parametrize("cfg_idx,over,steps,seqs", [
+    (0, {}, 64, [0]),
+    (1, dict(n_keys=8192, n_clusters=512, n_components=128, iters=3), 96, [0]),
+    (4, dict(n_keys=4096, n_clusters=256, n_components=64, iters=3), 48, [0, 5]),
+])
+def test_fused_boundary_select_matches_separate_calls(cfg_idx, over, steps, seqs):
+    # kv_boundary_select == kv_boundary followed by kv_select, bit for bit
+    cfg = wl.get_config(cfg_idx, **over)
+    inp = wl.layer_inputs(cfg, 0, seqs=seqs)
+    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    q, _ = wl.layer_queries(cfg, 0, steps=steps, seqs=seqs)
+    pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                                  n_units=cfg.n_clusters)
+    sel_cap = min(cfg.budget, cfg.n_clusters)
+    qd = to_dev(q, cfg.dtype)
+    a = gpu_decode(pool, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap)
+    b = gpu_decode(pool, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap, fused=True)
+    assert int(a.flag.sum()) >= 2
+    for name in ("flag", "sel_n", "sel"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    ra, rb = a.r.cpu().numpy(), b.r.cpu().numpy()
+    assert np.isnan(ra[0]).all() and np.isnan(rb[0]).all()
+    np.testing.assert_array_equal(ra[1:].view(np.uint32), rb[1:].view(np.uint32))
+    np.testing.assert_array_equal(a.out.cpu().numpy().view(np.uint32),
+                                  b.out.cpu().numpy().view(np.uint32))

@@ -104,6 +104,36 @@ def test_assign_ties_and_padding():
     assert not np.isin(gl[0], [20, 44]).any()
 
 
+@pytest.mark.parametrize("cfg_idx,over", [(0, {}), (1, dict(n_keys=4133, n_clusters=250,
+                                                              n_components=64))])
+def test_prepared_assign_matches_assign(cfg_idx, over):
+    # one prepared workspace labels two key sets (the second shorter) exactly as
+    # kv_kmeans_assign does, and the workspace is not consumed by the calls
+    cfg = wl.get_config(cfg_idx, **over)
+    _, keys, init = _keys(cfg, [0, 1])
+    BH, N, d = keys.shape
+    c = np.stack([keys[h][init[h]].astype(np.float64) for h in range(BH)])
+    c = c + 0.01 * np.random.default_rng(3).standard_normal(c.shape)
+    cent = torch.from_numpy(c.astype(np.float32)).cuda()
+    dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    ws = kvc.workspace(kvc.lib().kv_kmeans_assign_workspace(BH, cfg.n_clusters, d,
+                                                            kvc.dtype_code(dt)))
+    kvc.kv_kmeans_prepare(cent, dt, ws)
+    for n in (N, N // 3 + 5):
+        kd = to_dev(np.ascontiguousarray(keys[:, :n]), cfg.dtype)
+        lab_p = torch.full((BH, n), -1, dtype=torch.int32, device="cuda")
+        kvc.kv_kmeans_assign_prepared(kd, cent, lab_p, ws)
+        lab_a = torch.full((BH, n), -1, dtype=torch.int32, device="cuda")
+        kvc.kv_kmeans_assign(kd, cent, lab_a)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(lab_p.cpu().numpy(), lab_a.cpu().numpy())
+        c_in = c.astype(np.float32).astype(np.float64)
+        ol = np.stack([okm.assign(keys[h, :n], okm.centroid_for_distance(c_in[h], "parity",
+                                                                          cfg.dtype))
+                       for h in range(BH)])
+        assert (lab_p.cpu().numpy() == ol).mean() >= AGREE
+
+
 def test_update_empty_cluster_keeps_centroid(tiny):
     case = tiny["kmeans_empty"]
     keys = np.zeros((1, 2, 64), np.float32)
