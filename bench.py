@@ -42,6 +42,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def profiled_traffic(workload):
+    """HBM bytes per dispatch from the committed rocprofv3 counter summary of
+    this workload, or None when there is none or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in ("decode.hip", "kmeans.hip", "kvc_internal.hpp"):
+        with open(os.path.join(ROOT, "long_context_kv_kmeans_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != data.get("source_sha256_16"):
+        return None
+    return data
+
+
 def cpu_baseline(cfg, inp, q, lloyd_iters):
     """Time the oracle on a bounded sample and scale to one whole step."""
     import numpy as np
@@ -89,6 +112,7 @@ def main():
     ap.add_argument("--cpu-lloyd-iters", type=int, default=3)
     ap.add_argument("--assign-reps", type=int, default=20)
     ap.add_argument("--attend-reps", type=int, default=100)
+    ap.add_argument("--copy-calibration-mib", type=int, default=64)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
@@ -235,6 +259,7 @@ def main():
     achieved = flops / (asg_ms * 1e-3) / 1e12
     share = {"k_gather_attend": T * att_ms / ms_step, "k_assign_mfma": cfg.iters * asg_ms / ms_step}
 
+    traffic = profiled_traffic(cfg.name)
     keys_per_step = B * H * N
     res = {
         "metric": "prefill keys clustered/s; decode select+gather+attend us/layer-step, %HBM peak",
@@ -259,14 +284,25 @@ def main():
         "decode_hbm_frac": dec_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
         "roofline": {"bound": "hbm", "kernel": "k_gather_attend_mfma (kv_gather_attend)",
                      "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": att_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic["k_gather_attend_mfma"]["bytes"] if traffic else None,
                      "bytes_per_launch": att_bytes, "avg_launch_ms": att_ms},
         "roofline_assign": {"bound": "mfma", "kernel": "k_assign_mfma (kv_kmeans_assign_prepared)",
                             "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                            "frac": achieved / BF16_PEAK_TFLOPS,
+                            "traffic": traffic["k_assign_mfma"]["bytes"] if traffic else None,
                             "flops_per_launch": flops, "avg_launch_ms": asg_ms},
         "time_share_per_step": share,
     }
+    # A plain copy of known size after the timed region: the reference that
+    # scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes.
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, args.cpu_lloyd_iters)
