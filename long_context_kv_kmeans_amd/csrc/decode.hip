@@ -866,6 +866,11 @@ __device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const
   __builtin_amdgcn_wave_barrier();  // s_p / s_alpha are rewritten next step
 }
 
+// The register budget at 8 waves per workgroup is 256 VGPRs: G = 8 (p.v
+// accumulators) and G = 1 do not fit a second chunk in flight without
+// spilling, so they fold one chunk at a time.
+template <int G> constexpr bool kAttendPipelined = G == 2 || G == 4;
+
 template <int D, int G>
 __global__ void __launch_bounds__(kAttendThreads)
     k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
@@ -937,23 +942,33 @@ __global__ void __launch_bounds__(kAttendThreads)
     for (int i = tid; i < plen; i += NT)
       s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, pool.row_cap);
     __syncthreads();
-    // Two register sets: the next step's loads are in flight while this
-    // step's scores and p.v run.
     int it = wave * kAttendChunk;
-    AttendChunk<D> ca, cb;
-    if (it < plen) attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, col, quad, vslot, vpart);
-    while (it < plen) {
-      if (it + STEP < plen)
-        attend_chunk_load<D>(cb, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
-      attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
-                              s_alpha[wave], lane, col, quad, vslot);
-      it += STEP;
-      if (it >= plen) break;
-      if (it + STEP < plen)
-        attend_chunk_load<D>(ca, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
-      attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
-                              s_alpha[wave], lane, col, quad, vslot);
-      it += STEP;
+    if constexpr (kAttendPipelined<G>) {
+      // Two register sets: the next step's loads are in flight while this
+      // step's scores and p.v run.
+      AttendChunk<D> ca, cb;
+      if (it < plen)
+        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, col, quad, vslot, vpart);
+      while (it < plen) {
+        if (it + STEP < plen)
+          attend_chunk_load<D>(cb, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
+        attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
+                                s_alpha[wave], lane, col, quad, vslot);
+        it += STEP;
+        if (it >= plen) break;
+        if (it + STEP < plen)
+          attend_chunk_load<D>(ca, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
+        attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
+                                s_alpha[wave], lane, col, quad, vslot);
+        it += STEP;
+      }
+    } else {
+      for (; it < plen; it += STEP) {
+        AttendChunk<D> ca;
+        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, col, quad, vslot, vpart);
+        attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
+                                s_alpha[wave], lane, col, quad, vslot);
+      }
     }
     __syncthreads();
   }

@@ -45,6 +45,16 @@ def _sel_tensors(sel_lists, B, H, cap):
     (1, dict(n_keys=4096, n_clusters=256, n_components=64, iters=2), "full"),
     (4, dict(n_keys=2048, n_clusters=128, n_components=32, iters=2, batch=3), "budget"),
     (1, dict(n_keys=3001, n_clusters=100, n_components=30, iters=2, head_dim=64), "random"),
+    # every GQA group size of the bf16 and fp32 kernels, single- and multi-share
+    (1, dict(n_keys=4096, n_clusters=256, n_components=64, iters=2, n_q_heads=8), "budget"),
+    (1, dict(n_keys=4096, n_clusters=256, n_components=64, iters=2, n_q_heads=8), "full"),
+    (1, dict(n_keys=4096, n_clusters=256, n_components=64, iters=2, n_q_heads=16), "full"),
+    (1, dict(n_keys=4096, n_clusters=256, n_components=64, iters=2, n_q_heads=64), "budget"),
+    (1, dict(n_keys=4096, n_clusters=256, n_components=64, iters=2, n_q_heads=64), "full"),
+    (1, dict(n_keys=3001, n_clusters=100, n_components=30, iters=2, head_dim=64,
+             n_q_heads=64), "full"),
+    (0, dict(n_q_heads=16), "full"),
+    (0, dict(n_q_heads=2), "budget"),
 ])
 def test_attend_parity(cfg_idx, over, mode):
     cfg = wl.get_config(cfg_idx, **over)
