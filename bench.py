@@ -6,8 +6,9 @@ One step = one pass of the whole path over one Qwen3-8B-shaped layer
 per head, C = 2048, 10 Lloyd rounds):
   prefill : kv_cluster_build (K-means assign/update x10, CSR pack of K/V);
   decode  : 256 steps of kv_boundary_select (boundary test + selection in one
-            launch) -> kv_gather_attend on the seeded query walk, replayed from
-            one captured HIP graph.
+            launch, writing the selected units' row spans) -> kv_gather_attend
+            (reading those spans) on the seeded query walk, replayed from one
+            captured HIP graph.
 Inputs are synthetic (seeded Gaussian-mixture keys, random values and query
 walks) and resident in HBM before timing starts.
 
@@ -150,6 +151,7 @@ def main():
     sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
     sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
     sel_rows = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+    sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device="cuda")
     out = torch.zeros(T, B, Hq, d, dtype=torch.float32, device="cuda")
     ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
     ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, cfg.budget))
@@ -160,8 +162,9 @@ def main():
     def decode(record=None):
         for t in range(T):
             kvc.kv_boundary_select(pool, q[t - 1] if t else None, q[t], cfg.tau, cfg.budget,
-                                   flags[t], sel, sel_n, sel_rows, ws=ws_sel)
-            kvc.kv_gather_attend(pool, q[t], cfg.scale, sel, sel_n, cfg.budget, out[t], ws=ws_att)
+                                   flags[t], sel, sel_n, sel_rows, ws=ws_sel, sel_spans=sel_spans)
+            kvc.kv_gather_attend(pool, q[t], cfg.scale, None, sel_n, cfg.budget, out[t], ws=ws_att,
+                                 sel_spans=sel_spans)
             if record is not None:
                 record.append(sel_rows.clone())
 
@@ -236,13 +239,14 @@ def main():
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
     att_rows = int(sel_rows.sum().item())
-    att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, q[T - 1], cfg.scale, sel, sel_n,
-                                                    cfg.budget, out[T - 1], ws=ws_att),
+    att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, q[T - 1], cfg.scale, None, sel_n,
+                                                    cfg.budget, out[T - 1], ws=ws_att,
+                                                    sel_spans=sel_spans),
                        args.attend_reps)
     att_bytes = (att_rows * 2 * d * e          # selected K and V rows
                  + B * Hq * d * e              # queries
                  + B * Hq * d * 4              # fp32 output
-                 + sel_units_n * 12)           # unit id, start, size per selected unit
+                 + sel_units_n * 8)            # row span (start, size) per selected unit
     att_gbs = att_bytes / (att_ms * 1e-3) / 1e9
 
     # MFMA K-means assignment against prepared centroids (the kernel the

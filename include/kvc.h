@@ -212,8 +212,11 @@ kv_status kv_segment_append(const kv_pool *pool, const void *k_t, const void *v_
  *   rank non-empty units by (s_u descending, u ascending) and keep the
  *   longest prefix whose total unit_size is <= budget.
  * The selected ids are written ascending to sel_units[b][g][0..sel_n), with
- * sel_n[b][g] and sel_rows[b][g] (total rows). When flag[b] == 0 nothing of
- * sequence b is touched, so the previous selection is reused.
+ * sel_n[b][g] and sel_rows[b][g] (total rows). sel_spans (nullable):
+ * [BH][sel_cap][2] int32 receives (unit_start[u], unit_size[u]) of each
+ * selected unit at the same positions, the row ranges kv_gather_attend
+ * needs. When flag[b] == 0 nothing of sequence b is touched, so the
+ * previous selection is reused.
  * q: [batch][n_q_heads][head_dim] (dtype). sel_units: [BH][sel_cap] with
  * sel_cap >= min(budget, unit_cap). scores_out: NULL or [BH][unit_cap] fp32
  * (entries u >= n_cand[b] untouched).
@@ -221,8 +224,8 @@ kv_status kv_segment_append(const kv_pool *pool, const void *k_t, const void *v_
 size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads);
 kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
                     const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
-                    int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
-                    hipStream_t stream);
+                    int32_t *sel_rows, int32_t *sel_spans, float *scores_out, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
 
 /* Decode steps 1 and 3 in one launch: exactly kv_boundary(q_prev, q_cur,
  * pool->batch, n_q_heads, pool->head_dim, pool->dtype, tau, flag, r)
@@ -237,8 +240,8 @@ kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32
 kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void *q_cur,
                              int32_t n_q_heads, float tau, int32_t budget, uint8_t *flag,
                              float *r, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
-                             int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             int32_t *sel_rows, int32_t *sel_spans, float *scores_out, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Decode step 4: gather the selected rows and attend. LouisKV note,
@@ -247,6 +250,10 @@ kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void
  *   out[b][h] = softmax(scale * K_S q[b][h]) V_S   (fp32; 0 if S is empty)
  * where S = rows of the units sel_units[b][g][0..sel_n[b][g]) followed, when
  * pool->buf_cap > 0, by the local-buffer rows [buf_begin[b], n_rows[b]).
+ * When sel_spans ([BH][sel_cap][2] int32, as written by kv_select) is given,
+ * the units' row ranges are read from it instead of looking the ids up in
+ * the unit table (one dependent memory round trip less; sel_units may then
+ * be NULL). Row indices are clamped into [0, row_cap).
  * q: [batch][n_q_heads][head_dim] (dtype). out: [batch][n_q_heads][head_dim]
  * fp32. max_rows: expected upper bound on selected pool rows per (b, g) (the
  * budget); it sizes the launch and the workspace, results do not depend on
@@ -254,9 +261,9 @@ kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void
  */
 size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t max_rows);
 kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
-                           const int32_t *sel_units, int32_t sel_cap, const int32_t *sel_n,
-                           int32_t max_rows, float *out, void *ws, size_t ws_bytes,
-                           hipStream_t stream);
+                           const int32_t *sel_units, const int32_t *sel_spans, int32_t sel_cap,
+                           const int32_t *sel_n, int32_t max_rows, float *out, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

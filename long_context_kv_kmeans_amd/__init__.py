@@ -98,12 +98,13 @@ def lib() -> ctypes.CDLL:
         "kv_boundary": (c_int, [vp, vp, c_int, c_int, c_int, c_int, ctypes.c_float, vp, vp, vp]),
         "kv_segment_append": (c_int, [pool_p, vp, vp, vp, vp]),
         "kv_select_workspace": (c_size, [pool_p, c_int]),
-        "kv_select": (c_int, [pool_p, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, c_size, vp]),
+        "kv_select": (c_int, [pool_p, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, vp, c_size,
+                              vp]),
         "kv_boundary_select": (c_int, [pool_p, vp, vp, c_int, ctypes.c_float, c_int, vp, vp, vp,
-                                       c_int, vp, vp, vp, vp, c_size, vp]),
+                                       c_int, vp, vp, vp, vp, vp, c_size, vp]),
         "kv_gather_attend_workspace": (c_size, [pool_p, c_int, c_int]),
-        "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, c_int, vp, c_int, vp,
-                                     vp, c_size, vp]),
+        "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, c_int, vp, c_int,
+                                     vp, vp, c_size, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -278,25 +279,28 @@ def kv_select_workspace(pool: Pool, n_q_heads: int) -> int:
 
 
 def kv_select(pool: Pool, q, budget: int, flag, sel_units, sel_n, sel_rows, scores_out=None,
-              ws=None, stream=None) -> None:
+              ws=None, stream=None, sel_spans=None) -> None:
+    """sel_spans (optional) [B, H, sel_cap, 2] int32 receives the selected units' row spans."""
     Hq = q.shape[1]
     if ws is None:
         ws = workspace(kv_select_workspace(pool, Hq))
     _check("kv_select", lib().kv_select(
         pool.ref(), _ptr(q), Hq, int(budget), _ptr(flag), _ptr(sel_units), sel_units.shape[-1],
-        _ptr(sel_n), _ptr(sel_rows), _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans), _ptr(scores_out), _ptr(ws), ws.numel(),
+        _stream(stream)))
 
 
 def kv_boundary_select(pool: Pool, q_prev, q_cur, tau: float, budget: int, flag, sel_units,
-                       sel_n, sel_rows, r=None, scores_out=None, ws=None, stream=None) -> None:
+                       sel_n, sel_rows, r=None, scores_out=None, ws=None, stream=None,
+                       sel_spans=None) -> None:
     """kv_boundary then kv_select in one launch (q_prev None: first decode step)."""
     Hq = q_cur.shape[1]
     if ws is None:
         ws = workspace(kv_select_workspace(pool, Hq))
     _check("kv_boundary_select", lib().kv_boundary_select(
         pool.ref(), _ptr(q_prev), _ptr(q_cur), Hq, float(tau), int(budget), _ptr(flag), _ptr(r),
-        _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n), _ptr(sel_rows), _ptr(scores_out),
-        _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans),
+        _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def kv_gather_attend_workspace(pool: Pool, n_q_heads: int, max_rows: int) -> int:
@@ -304,10 +308,12 @@ def kv_gather_attend_workspace(pool: Pool, n_q_heads: int, max_rows: int) -> int
 
 
 def kv_gather_attend(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: int, out,
-                     ws=None, stream=None) -> None:
+                     ws=None, stream=None, sel_spans=None) -> None:
+    """sel_spans (optional, from kv_select) replaces the unit-table lookup of sel_units."""
     Hq = q.shape[1]
     if ws is None:
         ws = workspace(kv_gather_attend_workspace(pool, Hq, max_rows))
+    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
     _check("kv_gather_attend", lib().kv_gather_attend(
-        pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n),
-        int(max_rows), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+        pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), _ptr(sel_spans), cap,
+        _ptr(sel_n), int(max_rows), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -215,8 +215,8 @@ size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads) {
 namespace {
 kv_status select_common(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
                         const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
-                        int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
-                        bool fused, const void *q_prev, float tau, uint8_t *flag_out,
+                        int32_t *sel_rows, int32_t *sel_spans, float *scores_out, void *ws,
+                        size_t ws_bytes, bool fused, const void *q_prev, float tau, uint8_t *flag_out,
                         float *r_out, hipStream_t stream) {
   kv_status st = check_pool(pool);
   if (st != KV_OK) return st;
@@ -236,26 +236,28 @@ kv_status select_common(const kv_pool *pool, const void *q, int32_t n_q_heads, i
                              : reinterpret_cast<float *>(static_cast<char *>(ws) +
                                                          align_up(bh * sizeof(int32_t), 256));
   return launch_select(pool, q, n_q_heads, budget, flag, sel_units, sel_cap, sel_n, sel_rows,
-                       scores, counters, fused, q_prev, tau, flag_out, r_out, stream);
+                       sel_spans, scores, counters, fused, q_prev, tau, flag_out, r_out, stream);
 }
 }  // namespace
 
 kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,
                     const uint8_t *flag, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
-                    int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    int32_t *sel_rows, int32_t *sel_spans, float *scores_out, void *ws,
+                    size_t ws_bytes, hipStream_t stream) {
   return select_common(pool, q, n_q_heads, budget, flag, sel_units, sel_cap, sel_n, sel_rows,
-                       scores_out, ws, ws_bytes, false, nullptr, 0.f, nullptr, nullptr, stream);
+                       sel_spans, scores_out, ws, ws_bytes, false, nullptr, 0.f, nullptr, nullptr,
+                       stream);
 }
 
 kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void *q_cur,
                              int32_t n_q_heads, float tau, int32_t budget, uint8_t *flag,
                              float *r, int32_t *sel_units, int32_t sel_cap, int32_t *sel_n,
-                             int32_t *sel_rows, float *scores_out, void *ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             int32_t *sel_rows, int32_t *sel_spans, float *scores_out, void *ws,
+                             size_t ws_bytes, hipStream_t stream) {
   if (pool && pool->buf_cap > 0) return KV_ERR_UNSUPPORTED;  // the segment append goes between
   return select_common(pool, q_cur, n_q_heads, budget, nullptr, sel_units, sel_cap, sel_n,
-                       sel_rows, scores_out, ws, ws_bytes, true, q_prev, tau, flag, r, stream);
+                       sel_rows, sel_spans, scores_out, ws, ws_bytes, true, q_prev, tau, flag, r,
+                       stream);
 }
 
 size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t max_rows) {
@@ -270,12 +272,12 @@ size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_
 }
 
 kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
-                           const int32_t *sel_units, int32_t sel_cap, const int32_t *sel_n,
-                           int32_t max_rows, float *out, void *ws, size_t ws_bytes,
-                           hipStream_t stream) {
+                           const int32_t *sel_units, const int32_t *sel_spans, int32_t sel_cap,
+                           const int32_t *sel_n, int32_t max_rows, float *out, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
   kv_status st = check_pool(pool);
   if (st != KV_OK) return st;
-  if (!q || !sel_units || !sel_n || !out) return KV_ERR_INVALID_ARG;
+  if (!q || (!sel_units && !sel_spans) || !sel_n || !out) return KV_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || sel_cap <= 0 || max_rows < 0)
     return KV_ERR_INVALID_ARG;
   if (!(scale == scale)) return KV_ERR_INVALID_ARG;
@@ -288,7 +290,7 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
   int32_t *counters = static_cast<int32_t *>(ws);
   float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               align_up(bh * sizeof(int32_t), 256));
-  return launch_gather_attend(pool, q, n_q_heads, scale, sel_units, sel_cap, sel_n,
+  return launch_gather_attend(pool, q, n_q_heads, scale, sel_units, sel_spans, sel_cap, sel_n,
                               attend_num_splits(pool, max_rows), out, partials, counters, stream);
 }
 

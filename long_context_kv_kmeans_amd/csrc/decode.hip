@@ -288,7 +288,8 @@ template <typename T, int D, int KPT, bool FUSED>
 __global__ void __launch_bounds__(kSelectThreads)
     k_select(kv_pool pool, const T *__restrict__ q, int hq, int group, int budget,
              const uint8_t *__restrict__ flag, int32_t *__restrict__ sel_units, int sel_cap,
-             int32_t *__restrict__ sel_n, int32_t *__restrict__ sel_rows, float *__restrict__ scores,
+             int32_t *__restrict__ sel_n, int32_t *__restrict__ sel_rows,
+             int32_t *__restrict__ sel_spans, float *__restrict__ scores,
              int32_t *counters, const T *__restrict__ q_prev, float tau,
              uint8_t *__restrict__ flag_out, float *__restrict__ r_out) {
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per 16-byte lane load
@@ -481,10 +482,16 @@ __global__ void __launch_bounds__(kSelectThreads)
   }
   int pos = off + incl - cnt;
   int32_t *out = sel_units + (size_t)bg * sel_cap;
+  int32_t *spans = sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr;
+  const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (sz[j] > 0 && (take_all || key[j] > kstar)) {
-      if (pos < sel_cap) out[pos] = tid * KPT + j;
+      if (pos < sel_cap) {
+        const int u = tid * KPT + j;
+        out[pos] = u;
+        if (spans) *reinterpret_cast<int2 *>(spans + 2 * pos) = int2{ust[u], sz[j]};
+      }
       ++pos;
     }
   if (tid == 0) {
@@ -507,16 +514,16 @@ int select_num_blocks(const kv_pool *pool) {
 template <typename T, int D>
 static kv_status select_dispatch(const kv_pool *pool, const void *q, int hq, int budget,
                                  const uint8_t *flag, int32_t *sel_units, int sel_cap,
-                                 int32_t *sel_n, int32_t *sel_rows, float *scores,
-                                 int32_t *counters, bool fused, const void *q_prev, float tau,
-                                 uint8_t *flag_out, float *r_out, hipStream_t s) {
+                                 int32_t *sel_n, int32_t *sel_rows, int32_t *sel_spans,
+                                 float *scores, int32_t *counters, bool fused, const void *q_prev,
+                                 float tau, uint8_t *flag_out, float *r_out, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(select_num_blocks(pool), pool->batch * pool->n_kv_heads);
   const int per = (pool->unit_cap + kSelectThreads - 1) / kSelectThreads;
 #define KVC_SEL(K, F)                                                                          \
   k_select<T, D, K, F><<<grid, kSelectThreads, 0, s>>>(                                        \
-      *pool, (const T *)q, hq, G, budget, flag, sel_units, sel_cap, sel_n, sel_rows, scores,   \
-      counters, (const T *)q_prev, tau, flag_out, r_out)
+      *pool, (const T *)q, hq, G, budget, flag, sel_units, sel_cap, sel_n, sel_rows,           \
+      sel_spans, scores, counters, (const T *)q_prev, tau, flag_out, r_out)
 #define KVC_SEL2(K)         \
   do {                      \
     if (fused)              \
@@ -535,12 +542,13 @@ static kv_status select_dispatch(const kv_pool *pool, const void *q, int hq, int
 
 kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         const uint8_t *flag, int32_t *sel_units, int sel_cap, int32_t *sel_n,
-                        int32_t *sel_rows, float *scores, int32_t *counters, bool fused,
+                        int32_t *sel_rows, int32_t *sel_spans, float *scores, int32_t *counters,
+                        bool fused,
                         const void *q_prev, float tau, uint8_t *flag_out, float *r_out,
                         hipStream_t s) {
 #define KVC_SD(T, D)                                                                          \
-  select_dispatch<T, D>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n, sel_rows, scores, \
-                        counters, fused, q_prev, tau, flag_out, r_out, s)
+  select_dispatch<T, D>(pool, q, hq, budget, flag, sel_units, sel_cap, sel_n, sel_rows,         \
+                        sel_spans, scores, counters, fused, q_prev, tau, flag_out, r_out, s)
   kv_status st;
   if (pool->dtype == KV_BF16)
     st = pool->head_dim == 128 ? KVC_SD(uint16_t, 128) : KVC_SD(uint16_t, 64);
@@ -579,29 +587,48 @@ __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
 // (clamped to [0, sel_cap]) and returns the selection's row count.
 template <int NT>
 __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t *su,
-                                     const int32_t *sel_n, int sel_cap, int *n_out, int *s_psum,
-                                     int *s_start, int *s_wsum) {
+                                     const int32_t *spans, const int32_t *sel_n, int sel_cap,
+                                     int *n_out, int *s_psum, int *s_start, int *s_wsum) {
   constexpr int NW = NT / 64;
   constexpr int PER_MAX = kMaxSel / NT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int per = (sel_cap + NT - 1) / NT;  // sel_cap <= kMaxSel
   const int i0 = tid * per;
-  int uid[PER_MAX];
-#pragma unroll
-  for (int j = 0; j < PER_MAX; ++j) uid[j] = (j < per && i0 + j < sel_cap) ? su[i0 + j] : -1;
-  const int n = min(max(sel_n[bg], 0), sel_cap);
-  const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
-  const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
   int sz[PER_MAX], st[PER_MAX];
-  int run = 0;
+  int n;
+  if (spans != nullptr) {
+    // row spans given: ids are not needed, one round trip
 #pragma unroll
-  for (int j = 0; j < PER_MAX; ++j) {
-    const int u = uid[j];
-    // foreign ids count as empty units
-    const bool valid = j < per && i0 + j < n && u >= 0 && u < pool.unit_cap;
-    sz[j] = valid ? max(usz[u], 0) : 0;
-    st[j] = valid ? ust[u] : 0;
+    for (int j = 0; j < PER_MAX; ++j) {
+      int2 v = {0, 0};
+      if (j < per && i0 + j < sel_cap) v = *reinterpret_cast<const int2 *>(spans + 2 * (i0 + j));
+      st[j] = v.x;
+      sz[j] = v.y;
+    }
+    n = min(max(sel_n[bg], 0), sel_cap);
+#pragma unroll
+    for (int j = 0; j < PER_MAX; ++j) {
+      const bool valid = j < per && i0 + j < n;
+      sz[j] = valid ? max(sz[j], 0) : 0;
+      st[j] = valid ? st[j] : 0;
+    }
+  } else {
+    int uid[PER_MAX];
+#pragma unroll
+    for (int j = 0; j < PER_MAX; ++j) uid[j] = (j < per && i0 + j < sel_cap) ? su[i0 + j] : -1;
+    n = min(max(sel_n[bg], 0), sel_cap);
+    const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
+    const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
+#pragma unroll
+    for (int j = 0; j < PER_MAX; ++j) {
+      const int u = uid[j];
+      // foreign ids count as empty units
+      const bool valid = j < per && i0 + j < n && u >= 0 && u < pool.unit_cap;
+      sz[j] = valid ? max(usz[u], 0) : 0;
+      st[j] = valid ? ust[u] : 0;
+    }
   }
+  int run = 0;
 #pragma unroll
   for (int j = 0; j < PER_MAX; ++j) run += sz[j];
   int incl = run;
@@ -874,7 +901,8 @@ template <int G> constexpr bool kAttendPipelined = G == 2 || G == 4;
 template <int D, int G>
 __global__ void __launch_bounds__(kAttendThreads)
     k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
-                         const int32_t *__restrict__ sel_units, int sel_cap,
+                         const int32_t *__restrict__ sel_units,
+                         const int32_t *__restrict__ sel_spans, int sel_cap,
                          const int32_t *__restrict__ sel_n, float *__restrict__ out,
                          float *__restrict__ partials, int32_t *counters) {
   static_assert(G <= 16, "query columns of one MFMA tile");
@@ -913,8 +941,10 @@ __global__ void __launch_bounds__(kAttendThreads)
   }
 
   int n;
-  const int r_sel = attend_load_selection<NT>(pool, bg, sel_units + (size_t)bg * sel_cap, sel_n,
-                                              sel_cap, &n, s_psum, s_start, s_wsum);
+  const int r_sel = attend_load_selection<NT>(
+      pool, bg, sel_units ? sel_units + (size_t)bg * sel_cap : nullptr,
+      sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr, sel_n, sel_cap, &n, s_psum,
+      s_start, s_wsum);
   int r_buf = 0, buf_begin = 0;
   if (pool.buf_cap > 0) {
     buf_begin = pool.buf_begin[b];
@@ -1001,7 +1031,8 @@ constexpr int kAttendValuThreads = 512;
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kAttendValuThreads)
     k_gather_attend_valu(kv_pool pool, const T *__restrict__ q, int hq, float scale_log2,
-                         const int32_t *__restrict__ sel_units, int sel_cap,
+                         const int32_t *__restrict__ sel_units,
+                         const int32_t *__restrict__ sel_spans, int sel_cap,
                          const int32_t *__restrict__ sel_n, float *__restrict__ out,
                          float *__restrict__ partials, int32_t *counters) {
   constexpr int NT = kAttendValuThreads, NW = NT / 64;
@@ -1033,8 +1064,10 @@ __global__ void __launch_bounds__(kAttendValuThreads)
     for (int e = 0; e < EPL; ++e) qf[h][e] *= scale_log2;
   }
   int n;
-  const int r_sel = attend_load_selection<NT>(pool, bg, sel_units + (size_t)bg * sel_cap, sel_n,
-                                              sel_cap, &n, s_psum, s_start, s_wsum);
+  const int r_sel = attend_load_selection<NT>(
+      pool, bg, sel_units ? sel_units + (size_t)bg * sel_cap : nullptr,
+      sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr, sel_n, sel_cap, &n, s_psum,
+      s_start, s_wsum);
   int r_buf = 0, buf_begin = 0;
   if (pool.buf_cap > 0) {
     buf_begin = pool.buf_begin[b];
@@ -1159,20 +1192,22 @@ int attend_num_splits(const kv_pool *pool, int max_rows) {
 
 template <typename T, int D>
 static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, float scale_log2,
-                                 const int32_t *sel_units, int sel_cap, const int32_t *sel_n,
-                                 int nsplit, float *out, float *partials, int32_t *counters,
-                                 hipStream_t s) {
+                                 const int32_t *sel_units, const int32_t *sel_spans,
+                                 int sel_cap, const int32_t *sel_n, int nsplit, float *out,
+                                 float *partials, int32_t *counters, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
 #define KVC_ATT(GG)                                                                             \
   do {                                                                                          \
     if constexpr (sizeof(T) == 2)                                                               \
       k_gather_attend_mfma<D, GG><<<grid, kAttendThreads, 0, s>>>(                              \
-          *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_cap, sel_n, out, partials, \
+          *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,     \
+          out, partials,                                                                        \
           counters);                                                                            \
     else                                                                                        \
       k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                       \
-          *pool, (const T *)q, hq, scale_log2, sel_units, sel_cap, sel_n, out, partials,        \
+          *pool, (const T *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, out,       \
+          partials,                                                                             \
           counters);                                                                            \
   } while (0)
   switch (G) {
@@ -1187,21 +1222,20 @@ static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, flo
 }
 
 kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
-                               const int32_t *sel_units, int sel_cap, const int32_t *sel_n,
-                               int nsplit, float *out, float *partials, int32_t *counters,
-                               hipStream_t s) {
+                               const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
+                               const int32_t *sel_n, int nsplit, float *out, float *partials,
+                               int32_t *counters, hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = exp2(x log2 e)
+#define KVC_AD(T, D)                                                                          \
+  attend_dispatch<T, D>(pool, q, hq, sl2, sel_units, sel_spans, sel_cap, sel_n, nsplit, out, \
+                        partials, counters, s)
+  kv_status st;
   if (pool->dtype == KV_BF16)
-    return pool->head_dim == 128
-               ? attend_dispatch<uint16_t, 128>(pool, q, hq, sl2, sel_units, sel_cap, sel_n,
-                                                nsplit, out, partials, counters, s)
-               : attend_dispatch<uint16_t, 64>(pool, q, hq, sl2, sel_units, sel_cap, sel_n,
-                                               nsplit, out, partials, counters, s);
-  return pool->head_dim == 128
-             ? attend_dispatch<float, 128>(pool, q, hq, sl2, sel_units, sel_cap, sel_n, nsplit,
-                                           out, partials, counters, s)
-             : attend_dispatch<float, 64>(pool, q, hq, sl2, sel_units, sel_cap, sel_n, nsplit,
-                                          out, partials, counters, s);
+    st = pool->head_dim == 128 ? KVC_AD(uint16_t, 128) : KVC_AD(uint16_t, 64);
+  else
+    st = pool->head_dim == 128 ? KVC_AD(float, 128) : KVC_AD(float, 64);
+#undef KVC_AD
+  return st;
 }
 
 }  // namespace kvc

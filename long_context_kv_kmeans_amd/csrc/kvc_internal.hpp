@@ -139,13 +139,14 @@ int select_num_blocks(const kv_pool *pool);
 // write flag_out / r_out instead of reading flag.
 kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         const uint8_t *flag, int32_t *sel_units, int sel_cap, int32_t *sel_n,
-                        int32_t *sel_rows, float *scores, int32_t *counters, bool fused,
+                        int32_t *sel_rows, int32_t *sel_spans, float *scores, int32_t *counters,
+                        bool fused,
                         const void *q_prev, float tau, uint8_t *flag_out, float *r_out,
                         hipStream_t s);
 int attend_num_splits(const kv_pool *pool, int max_rows);
 kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
-                               const int32_t *sel_units, int sel_cap, const int32_t *sel_n,
-                               int nsplit, float *out, float *partials, int32_t *counters,
-                               hipStream_t s);
+                               const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
+                               const int32_t *sel_n, int nsplit, float *out, float *partials,
+                               int32_t *counters, hipStream_t s);
 
 }  // namespace kvc

@@ -74,9 +74,10 @@ class DecodeRecord:
 
 
 def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, steps=None,
-               record_sel=True, fused=False):
+               record_sel=True, fused=False, spans=False):
     """Run the decode loop through the C ABI. q: device [T, B, Hq, d].
-    fused: boundary test and selection through kv_boundary_select (no segments)."""
+    fused: boundary test and selection through kv_boundary_select (no segments).
+    spans: selection also writes row spans and attention reads them."""
     T = q.shape[0] if steps is None else steps
     B, Hq, d = q.shape[1:]
     H = pool.n_kv_heads
@@ -93,17 +94,21 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     sel_rows = torch.zeros(B, H, dtype=torch.int32, device=dev)
     ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
     ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, budget))
+    sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device=dev) if spans else None
     for t in range(T):
         if fused:
             assert dec_k is None
             kvc.kv_boundary_select(pool, q[t - 1] if t else None, q[t], tau, budget, rec.flag[t],
-                                   sel_units, sel_n, sel_rows, r=rec.r[t], ws=ws_sel)
+                                   sel_units, sel_n, sel_rows, r=rec.r[t], ws=ws_sel,
+                                   sel_spans=sel_spans)
         else:
             kvc.kv_boundary(q[t - 1] if t else None, q[t], tau, rec.flag[t], rec.r[t])
             if dec_k is not None:
                 kvc.kv_segment_append(pool, dec_k[t], dec_v[t], rec.flag[t])
-            kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel)
-        kvc.kv_gather_attend(pool, q[t], scale, sel_units, sel_n, budget, rec.out[t], ws=ws_att)
+            kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel,
+                          sel_spans=sel_spans)
+        kvc.kv_gather_attend(pool, q[t], scale, None if spans else sel_units, sel_n, budget,
+                             rec.out[t], ws=ws_att, sel_spans=sel_spans)
         rec.sel_n[t].copy_(sel_n)
         if record_sel:
             rec.sel[t].copy_(sel_units)

@@ -68,16 +68,17 @@ def test_boundary_select_validation():
     assert need > 0
     # the same checks as kv_select, plus flag out and a finite tau
     assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, f, 64, None, None, a, 256, a, a,
-                                None, a, need, None) == kvc.KV_ERR_INVALID_ARG
+                                None, None, a, need, None) == kvc.KV_ERR_INVALID_ARG
     assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, ctypes.c_float(float("nan")), 64,
-                                a, None, a, 256, a, a, None, a, need, None) == kvc.KV_ERR_INVALID_ARG
+                                a, None, a, 256, a, a, None, None, a, need,
+                                None) == kvc.KV_ERR_INVALID_ARG
     assert L.kv_boundary_select(ctypes.byref(p), None, a, 24, f, 64, a, None, a, 256, a, a,
-                                None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # G = 3
+                                None, None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # G = 3
     assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, f, 64, a, None, a, 256, a, a,
-                                None, a, need - 1, None) == kvc.KV_ERR_WORKSPACE
+                                None, None, a, need - 1, None) == kvc.KV_ERR_WORKSPACE
     pb = _fake_pool(buf_cap=64, seg_sum=0x10000)
     assert L.kv_boundary_select(ctypes.byref(pb), None, a, 32, f, 64, a, None, a, 256, a, a,
-                                None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # local buffer
+                                None, None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # local buffer
 
 
 def test_pool_validation():
@@ -85,35 +86,35 @@ def test_pool_validation():
     a = ctypes.c_void_p(0x10000)
     ws = ctypes.c_void_p(0x10000)  # 256-aligned dummy
     p = _fake_pool(head_dim=96)
-    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, ws, 1 << 30,
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_UNSUPPORTED
     p = _fake_pool(batch=0)
-    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, ws, 1 << 30,
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_INVALID_ARG
     p = _fake_pool()
     # query heads not a multiple of KV heads
-    assert L.kv_select(ctypes.byref(p), a, 30, 512, None, a, 512, a, a, None, ws, 1 << 30,
+    assert L.kv_select(ctypes.byref(p), a, 30, 512, None, a, 512, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_INVALID_ARG
     # negative budget
-    assert L.kv_select(ctypes.byref(p), a, 32, -1, None, a, 512, a, a, None, ws, 1 << 30,
+    assert L.kv_select(ctypes.byref(p), a, 32, -1, None, a, 512, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_INVALID_ARG
     # selection capacity below min(budget, unit_cap)
-    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 100, a, a, None, ws, 1 << 30,
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 100, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_CAPACITY
     # workspace too small / misaligned
-    assert L.kv_select(ctypes.byref(p), a, 32, 128, None, a, 256, a, a, None, ws, 16,
+    assert L.kv_select(ctypes.byref(p), a, 32, 128, None, a, 256, a, a, None, None, ws, 16,
                        None) == kvc.KV_ERR_WORKSPACE
-    assert L.kv_select(ctypes.byref(p), a, 32, 128, None, a, 256, a, a, None,
+    assert L.kv_select(ctypes.byref(p), a, 32, 128, None, a, 256, a, a, None, None,
                        ctypes.c_void_p(0x10004), 1 << 30, None) == kvc.KV_ERR_WORKSPACE
     # group size 3 unsupported
     p3 = _fake_pool(n_kv_heads=2)
-    assert L.kv_select(ctypes.byref(p3), a, 6, 128, None, a, 256, a, a, None, ws, 1 << 30,
+    assert L.kv_select(ctypes.byref(p3), a, 6, 128, None, a, 256, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_UNSUPPORTED
     # segments need a local buffer and seg_sum
     assert L.kv_segment_append(ctypes.byref(p), a, a, a, None) == kvc.KV_ERR_INVALID_ARG
     pb = _fake_pool(buf_cap=16)  # seg_sum NULL
     assert L.kv_segment_append(ctypes.byref(pb), a, a, a, None) == kvc.KV_ERR_INVALID_ARG
-    assert L.kv_select(None, a, 32, 128, None, a, 256, a, a, None, ws, 1 << 30,
+    assert L.kv_select(None, a, 32, 128, None, a, 256, a, a, None, None, ws, 1 << 30,
                        None) == kvc.KV_ERR_INVALID_ARG
 
 
@@ -123,12 +124,16 @@ def test_attend_validation():
     p = _fake_pool()
     need = L.kv_gather_attend_workspace(ctypes.byref(p), 32, 512)
     assert need > 0
-    assert L.kv_gather_attend(ctypes.byref(p), a, 32, ctypes.c_float(0.1), a, 5000, a, 512, a, a,
-                              need, None) == kvc.KV_ERR_UNSUPPORTED  # sel_cap > 4096
-    assert L.kv_gather_attend(ctypes.byref(p), a, 32, ctypes.c_float(0.1), a, 512, a, 512, a, a,
-                              need - 1, None) == kvc.KV_ERR_WORKSPACE
-    assert L.kv_gather_attend(ctypes.byref(p), None, 32, ctypes.c_float(0.1), a, 512, a, 512, a,
-                              a, need, None) == kvc.KV_ERR_INVALID_ARG
+    c01 = ctypes.c_float(0.1)
+    assert L.kv_gather_attend(ctypes.byref(p), a, 32, c01, a, None, 5000, a, 512, a, a, need,
+                              None) == kvc.KV_ERR_UNSUPPORTED  # sel_cap > 4096
+    assert L.kv_gather_attend(ctypes.byref(p), a, 32, c01, a, None, 512, a, 512, a, a, need - 1,
+                              None) == kvc.KV_ERR_WORKSPACE
+    assert L.kv_gather_attend(ctypes.byref(p), None, 32, c01, a, None, 512, a, 512, a, a, need,
+                              None) == kvc.KV_ERR_INVALID_ARG
+    # neither ids nor spans
+    assert L.kv_gather_attend(ctypes.byref(p), a, 32, c01, None, None, 512, a, 512, a, a, need,
+                              None) == kvc.KV_ERR_INVALID_ARG
 
 
 def test_cluster_build_validation():

@@ -129,12 +129,36 @@ def test_fused_boundary_select_matches_separate_calls(cfg_idx, over, steps, seqs
     sel_cap = min(cfg.budget, cfg.n_clusters)
     qd = to_dev(q, cfg.dtype)
     a = gpu_decode(pool, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap)
-    b = gpu_decode(pool, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap, fused=True)
     assert int(a.flag.sum()) >= 2
-    for name in ("flag", "sel_n", "sel"):
-        assert torch.equal(getattr(a, name), getattr(b, name)), name
-    ra, rb = a.r.cpu().numpy(), b.r.cpu().numpy()
-    assert np.isnan(ra[0]).all() and np.isnan(rb[0]).all()
-    np.testing.assert_array_equal(ra[1:].view(np.uint32), rb[1:].view(np.uint32))
-    np.testing.assert_array_equal(a.out.cpu().numpy().view(np.uint32),
-                                  b.out.cpu().numpy().view(np.uint32))
+    # fused boundary+select, with and without row spans handed to the attention
+    for kw in (dict(fused=True), dict(fused=True, spans=True)):
+        b = gpu_decode(pool, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap, **kw)
+        for name in ("flag", "sel_n", "sel"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (kw, name)
+        ra, rb = a.r.cpu().numpy(), b.r.cpu().numpy()
+        assert np.isnan(ra[0]).all() and np.isnan(rb[0]).all()
+        np.testing.assert_array_equal(ra[1:].view(np.uint32), rb[1:].view(np.uint32))
+        np.testing.assert_array_equal(a.out.cpu().numpy().view(np.uint32),
+                                      b.out.cpu().numpy().view(np.uint32))
+
+
+def test_decode_segments_with_spans_matches_unit_lookup():
+    # long-output config: spans written by kv_select (segments included) give the
+    # same attention as the unit-table lookup, bit for bit
+    cfg = wl.get_config(2, buf_cap=64, steps=300, p_jump=0.05, budget=256, iters=3)
+    inp = wl.layer_inputs(cfg, 0)
+    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    q, _ = wl.layer_queries(cfg, 0, steps=cfg.steps)
+    dk, dv = wl.layer_decode_kv(cfg, 0, steps=cfg.steps)
+    n_units = cfg.n_clusters + cfg.steps
+    sel_cap = min(cfg.budget, n_units)
+    outs = []
+    for spans in (False, True):
+        pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                                      n_units=n_units, buf_cap=cfg.buf_cap, extra_rows=cfg.steps)
+        rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                         dec_k=to_dev(dk, cfg.dtype), dec_v=to_dev(dv, cfg.dtype), spans=spans)
+        outs.append(rec)
+    assert torch.equal(outs[0].sel, outs[1].sel)
+    np.testing.assert_array_equal(outs[0].out.cpu().numpy().view(np.uint32),
+                                  outs[1].out.cpu().numpy().view(np.uint32))

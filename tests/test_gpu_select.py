@@ -28,8 +28,22 @@ def _run_select(pool, q_d, budget, sel_cap, flag=None, sel=None):
                torch.full((B, H), -7, dtype=torch.int32, device="cuda"),
                torch.full((B, H), -7, dtype=torch.int32, device="cuda"))
     scores = torch.zeros(B, H, pool.unit_cap, dtype=torch.float32, device="cuda")
-    kvc.kv_select(pool, q_d, budget, flag, sel[0], sel[1], sel[2], scores_out=scores)
+    spans = torch.full((B, H, sel_cap, 2), -9, dtype=torch.int32, device="cuda")
+    kvc.kv_select(pool, q_d, budget, flag, sel[0], sel[1], sel[2], scores_out=scores,
+                  sel_spans=spans)
     torch.cuda.synchronize()
+    # row spans: (unit_start, unit_size) of each selected id, at the same positions
+    su, sn, sp = sel[0].cpu().numpy(), sel[1].cpu().numpy(), spans.cpu().numpy()
+    ust, usz = pool.unit_start.cpu().numpy(), pool.unit_size.cpu().numpy()
+    fl = None if flag is None else flag.cpu().numpy()
+    for b in range(B):
+        for g in range(H):
+            if fl is not None and fl[b] == 0:
+                assert (sp[b, g] == -9).all()
+                continue
+            ids = su[b, g, :sn[b, g]]
+            np.testing.assert_array_equal(sp[b, g, :sn[b, g], 0], ust[b, g, ids])
+            np.testing.assert_array_equal(sp[b, g, :sn[b, g], 1], usz[b, g, ids])
     return sel, scores
 
 
