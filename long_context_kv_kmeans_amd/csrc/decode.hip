@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(kSelectThreads)
   __shared__ int hc[kSelectWaves][256];
   __shared__ int tw[256];
   __shared__ int tc[256];
-  __shared__ int hu[256];
+  __shared__ unsigned long long hk[256];
   __shared__ long s_above;
   __shared__ int s_done, s_none;
   __shared__ unsigned long long s_prefix, s_kstar;
@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(kSelectThreads)
       const int dgt = (int)((key[j] >> sh) & 255ull);
       atomicAdd(&hw[wave][dgt], sz[j]);
       atomicAdd(&hc[wave][dgt], 1);
-      hu[dgt] = tid * KPT + j;  // any member; read only when the bucket holds one unit
+      hk[dgt] = key[j];  // any member; read only when the bucket holds one unit
     }
     __syncthreads();
     if (tid < 256) {
@@ -435,8 +435,7 @@ __global__ void __launch_bounds__(kSelectThreads)
           s_above = above_out;
           s_prefix = prefix | ((unsigned long long)dgt << sh);
           if (tc[dgt] == 1) {
-            const int u = hu[dgt];
-            s_kstar = unit_key(coherent_load(&sc[u]), u);
+            s_kstar = hk[dgt];
             s_done = 1;
           } else if (sh == 0) {
             s_kstar = s_prefix;
