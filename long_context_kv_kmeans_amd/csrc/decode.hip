@@ -743,9 +743,7 @@ __device__ void attend_finish(int bg, int b, int g, int hq, int nsplit, int spli
     const bool on = lane < nsplit;
     const float m = on ? coherent_load(&allp[lane * pstride + h * (D + 2) + D]) : -INFINITY;
     const float l = on ? coherent_load(&allp[lane * pstride + h * (D + 2) + D + 1]) : 0.f;
-    float mx = m;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float mx = wave_max(m);
     const float sc = safe_scale(m, mx);
     const float lsum = wave_sum(l * sc);
     if (on) s_scale[lane][h] = sc;
@@ -852,8 +850,7 @@ __device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const
       sv[tk * 4 + r] = v;
       mt = fmaxf(mt, v);
     }
-  mt = fmaxf(mt, __shfl_xor(mt, 16));
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  mt = max_xor32(max_xor16(mt));  // over the four lanes of query head `col`
   const float m_new = fmaxf(m_run, mt);
   const float alpha = safe_scale(m_run, m_new);
   float ps = 0.f;
@@ -863,8 +860,7 @@ __device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const
     ps += p;
     if (col < G) s_p[(k >> 2) * 16 + 4 * quad + (k & 3)][col] = p;
   }
-  ps += __shfl_xor(ps, 16);
-  ps += __shfl_xor(ps, 32);
+  ps = sum_xor32(sum_xor16(ps));
   l_run = l_run * alpha + ps;
   m_run = m_new;
   if (lane < G) s_alpha[lane] = alpha;
@@ -1004,11 +1000,9 @@ __global__ void __launch_bounds__(kAttendThreads)
 
   // rows of one wave share m_run: lane groups combine by plain sums
 #pragma unroll
-  for (int o = LPR; o < 64; o <<= 1)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+    for (int e = 0; e < 8; ++e) acc[h][e] = sum_stride<LPR>(acc[h][e]);
   if (vslot == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)

@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256, MINW)
 #pragma unroll
       for (int j = 0; j < 8; ++j) sq = fmaf(f[j], f[j], sq);
     }
-    sq += __shfl_xor(sq, 32);
+    sq = sum_xor32(sq);
     uint32_t h, md, lo;
     split3_neg(0.5f * sq, &h, &md, &lo);
     uint4 aug = {0u, 0u, 0u, 0u};
@@ -592,9 +592,7 @@ __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
     }
   }
 #pragma unroll
-  for (int o = LPR; o < 64; o <<= 1)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o);
+  for (int e = 0; e < EPL; ++e) acc[e] = sum_stride<LPR>(acc[e]);
   float mean[EPL];
   const float *in = cent_in + ((size_t)bh * c + k) * D + part * EPL;
 #pragma unroll

@@ -54,9 +54,11 @@ template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4 &v, f
 }
 
 // DPP lane moves (gfx9 encodings): mirror a 16-lane row, mirror each 8-lane
-// half row, and permute within quads.
+// half row, rotate a row by 8 lanes (= lane ^ 8 within the row), and permute
+// within quads.
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowRor8 = 0x128;
 constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
 constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
 
@@ -64,21 +66,79 @@ template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// Exchanges across 16- and 32-lane distance with gfx950's lane-swap
+// instructions (VALU, no LDS permute). Swapping v with itself leaves, in
+// every lane l, the pair {v[l], v[l ^ 16]} (resp. v[l ^ 32]) in some order;
+// + and max are commutative, so the results equal v op shfl_xor(v, 16 / 32)
+// bit for bit.
+__device__ __forceinline__ void swap_pair16(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap_pair32(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  float a, b;
+  swap_pair16(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  float a, b;
+  swap_pair32(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  float a, b;
+  swap_pair16(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  float a, b;
+  swap_pair32(v, a, b);
+  return fmaxf(a, b);
+}
+
 // Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32, 64); every lane of a
 // group receives the group total. Within a 16-lane row the pairing is
 // mirror -> half mirror -> quad swaps: after the row-mirror step lane i holds
 // x_i + x_15-i, after the half-mirror step it holds the four lanes
 // {j, 7-j, 8+j, 15-j} (j = i mod 8), and the two quad swaps combine the four
-// such sets of a row. Wider groups add an exchange across rows. All lanes must
-// be active.
+// such sets of a row. Wider groups add the 16- and 32-lane exchanges. All
+// lanes must be active.
 template <int N> __device__ __forceinline__ float group_sum(float v) {
   static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
   if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
   if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
   if constexpr (N >= 4) v += dpp_mov<kDppQuadSwap2>(v);
   v += dpp_mov<kDppQuadSwap1>(v);
-  if constexpr (N >= 32) v += __shfl_xor(v, 16);
-  if constexpr (N >= 64) v += __shfl_xor(v, 32);
+  if constexpr (N >= 32) v = sum_xor16(v);
+  if constexpr (N >= 64) v = sum_xor32(v);
+  return v;
+}
+
+// Maximum over the whole wave, in every lane (same pairing as group_sum).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadSwap1>(v));
+  v = max_xor16(v);
+  return max_xor32(v);
+}
+
+// Sum over the lanes l' with l' % L == l % L (L = 8, 16, 32): lane groups that
+// hold the same elements of different rows.
+template <int L> __device__ __forceinline__ float sum_stride(float v) {
+  static_assert(L == 8 || L == 16 || L == 32 || L == 64, "stride");
+  if constexpr (L <= 8) v += dpp_mov<kDppRowRor8>(v);
+  if constexpr (L <= 16) v = sum_xor16(v);
+  if constexpr (L <= 32) v = sum_xor32(v);
   return v;
 }
 
