@@ -15,6 +15,8 @@
 // its results with device-coherent stores and bumps a per-(sequence, head)
 // counter; the block that brings the counter to the grid size does the final
 // reduction in a fixed order and resets the counter to zero.
+#include <utility>
+
 #include "kvc_internal.hpp"
 
 namespace kvc {
@@ -786,14 +788,34 @@ constexpr int kAttendMfmaPiece = 1024;  // rows resolved per row-table pass
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8a_t __attribute__((ext_vector_type(8)));
 
-// One wave step's operands: K fragments of two 16-row tiles (A operand: lane
-// holds row l%16 of a tile and head-dimension entries 32 s + 8 (l/16) .. +7 of
-// k-step s) and the V rows this lane accumulates (8 elements each).
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Lane H of each 16-lane row, broadcast to the row.
+template <int H> __device__ __forceinline__ float row_bcast(float v) {
+  static_assert(H >= 0 && H < 16, "lane");
+  return dpp_mov<kDppRowBcast0 + H>(v);
+}
+
+// One wave step's operands for 32 rows (two 16-row MFMA tiles). K fragments
+// (A operand): lane holds row l%16 of a tile and head-dimension entries
+// 32 s + 8 (l/16) .. +7 of k-step s. The score of row 16 t + 4 q + r (tile t)
+// for query head c then sits in lane 16 q + c; V rows are dealt so that the
+// 16-lane row q holds exactly rows {16 t + 4 q + r}: lane l loads, for
+// i < VU, row 16 t + 4 q + r with k = 4 t + r = i RPL + sub (q = l/16,
+// sub = (l%16) / LPR), elements 8 (l % LPR) .. +7. A probability then
+// reaches its V lanes by a broadcast within the 16-lane row.
 template <int D> struct AttendChunk {
   static constexpr int KS = D / 32;
-  static constexpr int LPR = D / 8;
-  static constexpr int RPI = 64 / LPR;
-  static constexpr int VU = kAttendChunk / RPI;
+  static constexpr int LPR = D / 8;     // lanes per V row
+  static constexpr int RPL = 16 / LPR;  // V rows per 16-lane row and instruction
+  static constexpr int VU = 8 / RPL;    // V loads per lane
   bf16x8a_t kf[2][KS];
   uint4 vv[VU];
 };
@@ -801,9 +823,10 @@ template <int D> struct AttendChunk {
 template <int D>
 __device__ __forceinline__ void attend_chunk_load(AttendChunk<D> &c, const int *s_rowtab, int it,
                                                   int plen, const uint16_t *kbase,
-                                                  const uint16_t *vbase, int col, int quad,
-                                                  int vslot, int vpart) {
+                                                  const uint16_t *vbase, int lane) {
   using C = AttendChunk<D>;
+  const int col = lane & 15, quad = lane >> 4;
+  const int vpart = lane % C::LPR, sub = (lane & 15) / C::LPR;
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk) {
     const int li = it + tk * 16 + col;
@@ -815,22 +838,24 @@ __device__ __forceinline__ void attend_chunk_load(AttendChunk<D> &c, const int *
   }
 #pragma unroll
   for (int i = 0; i < C::VU; ++i) {
-    const int li = it + vslot + C::RPI * i;
+    const int k = i * C::RPL + sub;
+    const int li = it + 16 * (k >> 2) + 4 * quad + (k & 3);
     const size_t row = li < plen ? (size_t)s_rowtab[li] : 0;
     c.vv[i] = *reinterpret_cast<const uint4 *>(vbase + row * D + 8 * vpart);
   }
 }
 
-// Fold one chunk into the wave's online-softmax state. Scores: lane holds rows
-// 4 (l/16) + r of each tile for query head l%16; probabilities and the rescale
-// factor reach the V lanes through this wave's LDS slice.
+// Fold one chunk into the wave's online-softmax state (m_run, l_run per
+// query head `col`, identical in the four lanes col + 16 q; acc per head for
+// this lane's V elements, relative to m_run). Probabilities and the rescale
+// factor move to the V lanes by row broadcasts: no LDS round trip.
 template <int D, int G>
 __device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const bf16x8a_t *qf,
                                                   int it, int plen, float scale_log2,
                                                   float &m_run, float &l_run, float (*acc)[8],
-                                                  float (*s_p)[G], float *s_alpha, int lane,
-                                                  int col, int quad, int vslot) {
+                                                  int lane) {
   using C = AttendChunk<D>;
+  const int quad = lane >> 4, sub = (lane & 15) / C::LPR;
   f32x4_t sc[2];
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk) {
@@ -853,39 +878,39 @@ __device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const
   mt = max_xor32(max_xor16(mt));  // over the four lanes of query head `col`
   const float m_new = fmaxf(m_run, mt);
   const float alpha = safe_scale(m_run, m_new);
+  float p[8];
   float ps = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float p = sv[k] == -INFINITY ? 0.f : exp2f(sv[k] - m_new);
-    ps += p;
-    if (col < G) s_p[(k >> 2) * 16 + 4 * quad + (k & 3)][col] = p;
+    p[k] = sv[k] == -INFINITY ? 0.f : exp2f(sv[k] - m_new);
+    ps += p[k];
   }
   ps = sum_xor32(sum_xor16(ps));
   l_run = l_run * alpha + ps;
   m_run = m_new;
-  if (lane < G) s_alpha[lane] = alpha;
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  float al[G];
+  static_for<G>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const float al = row_bcast<h>(alpha);
 #pragma unroll
-  for (int h = 0; h < G; ++h) al[h] = s_alpha[h];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+    for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+  });
 #pragma unroll
   for (int i = 0; i < C::VU; ++i) {
     float vf[8];
     unpack16<uint16_t>(c.vv[i], vf);
-    const int rl = vslot + C::RPI * i;
+    static_for<G>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      float pu;
+      if constexpr (C::RPL == 1) {
+        pu = row_bcast<h>(p[i]);
+      } else {
+        const float b0 = row_bcast<h>(p[i * C::RPL]), b1 = row_bcast<h>(p[i * C::RPL + 1]);
+        pu = sub ? b1 : b0;
+      }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = s_p[rl][h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-    }
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pu, vf[e], acc[h][e]);
+    });
   }
-  __builtin_amdgcn_wave_barrier();  // s_p / s_alpha are rewritten next step
 }
 
 // The register budget at 8 waves per workgroup is 256 VGPRs: G = 8 (p.v
@@ -909,8 +934,6 @@ __global__ void __launch_bounds__(kAttendThreads)
   __shared__ int s_start[kMaxSel];
   __shared__ int s_rowtab[kAttendMfmaPiece];
   __shared__ int s_wsum[NW];
-  __shared__ float s_p[NW][kAttendChunk][G];
-  __shared__ float s_alpha[NW][G];
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
   __shared__ int s_last;
@@ -919,8 +942,8 @@ __global__ void __launch_bounds__(kAttendThreads)
   const int bg = blockIdx.y, b = bg / H, g = bg % H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nsplit = gridDim.x, split = blockIdx.x;
-  const int col = lane & 15, quad = lane >> 4;     // MFMA: column (query head) and k group
-  const int vpart = lane % LPR, vslot = lane / LPR;  // V rows: element piece and row slot
+  const int col = lane & 15, quad = lane >> 4;  // MFMA: column (query head) and k group
+  const int vpart = lane % LPR;                   // V elements 8 vpart .. 8 vpart + 7
 
   // Query fragments (B operand, 32 k x 16 columns): lane holds column `col`
   // (query head col < G, else zero) and the same head-dimension entries as
@@ -973,26 +996,23 @@ __global__ void __launch_bounds__(kAttendThreads)
       // step's scores and p.v run.
       AttendChunk<D> ca, cb;
       if (it < plen)
-        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, col, quad, vslot, vpart);
+        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, lane);
       while (it < plen) {
         if (it + STEP < plen)
-          attend_chunk_load<D>(cb, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
-        attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
-                                s_alpha[wave], lane, col, quad, vslot);
+          attend_chunk_load<D>(cb, s_rowtab, it + STEP, plen, kbase, vbase, lane);
+        attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
         if (it >= plen) break;
         if (it + STEP < plen)
-          attend_chunk_load<D>(ca, s_rowtab, it + STEP, plen, kbase, vbase, col, quad, vslot, vpart);
-        attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
-                                s_alpha[wave], lane, col, quad, vslot);
+          attend_chunk_load<D>(ca, s_rowtab, it + STEP, plen, kbase, vbase, lane);
+        attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
       }
     } else {
       for (; it < plen; it += STEP) {
         AttendChunk<D> ca;
-        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, col, quad, vslot, vpart);
-        attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, s_p[wave],
-                                s_alpha[wave], lane, col, quad, vslot);
+        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, lane);
+        attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
       }
     }
     __syncthreads();
@@ -1003,7 +1023,7 @@ __global__ void __launch_bounds__(kAttendThreads)
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = sum_stride<LPR>(acc[h][e]);
-  if (vslot == 0) {
+  if (lane < LPR) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll

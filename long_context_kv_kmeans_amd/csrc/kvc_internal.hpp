@@ -54,11 +54,12 @@ template <> __device__ __forceinline__ void unpack16<uint16_t>(const uint4 &v, f
 }
 
 // DPP lane moves (gfx9 encodings): mirror a 16-lane row, mirror each 8-lane
-// half row, rotate a row by 8 lanes (= lane ^ 8 within the row), and permute
-// within quads.
+// half row, rotate a row by 8 lanes (= lane ^ 8 within the row), broadcast
+// one lane of each row to the row, and permute within quads.
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowBcast0 = 0x150;  // + n: lane n of each row to the whole row (gfx90a+)
 constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
 constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
 
