@@ -17,6 +17,7 @@ import torch
 
 import workloads as wl
 from oracle import attend as oat
+from oracle import kmeans as okm
 from oracle.decode import run_decode, unit_rows
 from tests.gpu_util import gpu_decode, max_rel_err, oracle_clustering, oracle_packs, \
     pool_from_labels, to_dev
@@ -25,10 +26,27 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _run(cfg, steps, seqs, compare_every=1):
+def _fixed_clustering(keys, C):
+    """Labels k mod C with the oracle's member means: a cheap, valid clustering for
+    sequences that only fill the batch and are not checked."""
+    B, H, N, d = keys.shape
+    labels = np.tile(np.arange(N) % C, (B, H, 1))
+    cents = np.empty((B, H, C, d))
+    for b in range(B):
+        for g in range(H):
+            cents[b, g], _ = okm.update(keys[b, g], labels[b, g], np.zeros((C, d)))
+    return labels, cents
+
+
+def _run(cfg, steps, seqs, compare_every=1, check=None, **decode_kw):
+    """check: positions in `seqs` compared with the oracle (default all); the other
+    sequences get _fixed_clustering and only fill the launch."""
     inp = wl.layer_inputs(cfg, 0, seqs=seqs)
     B, H, N, d = inp["keys"].shape
-    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    check = list(range(B)) if check is None else list(check)
+    labels, cents = _fixed_clustering(inp["keys"], cfg.n_clusters)
+    lc, cc = oracle_clustering(inp["keys"][check], inp["init_idx"][check], cfg.iters, cfg.dtype)
+    labels[check], cents[check] = lc, cc
     q, _ = wl.layer_queries(cfg, 0, steps=steps, seqs=seqs)
     dk = dv = None
     extra_rows, n_units = 0, cfg.n_clusters
@@ -40,7 +58,7 @@ def _run(cfg, steps, seqs, compare_every=1):
     sel_cap = min(cfg.budget, n_units)
     rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, cfg.budget, cfg.scale, sel_cap,
                      dec_k=None if dk is None else to_dev(dk, cfg.dtype),
-                     dec_v=None if dv is None else to_dev(dv, cfg.dtype))
+                     dec_v=None if dv is None else to_dev(dv, cfg.dtype), **decode_kw)
     flags = rec.flag.cpu().numpy().astype(bool)
     out = rec.out.cpu().numpy()
     sel_n = rec.sel_n.cpu().numpy()
@@ -48,7 +66,7 @@ def _run(cfg, steps, seqs, compare_every=1):
     counters = rec.counters.cpu().numpy()
     G = cfg.group
     stats = {"retrievals": 0, "set_mismatch": 0, "max_err": 0.0}
-    for bi in range(B):
+    for bi in check:
         packs = oracle_packs(inp["keys"], inp["values"], labels, cents, cfg.dtype, bi)
         log, opool = run_decode(packs, q[:, bi], cfg.tau, cfg.budget, cfg.scale, cfg.dtype,
                                 buf_cap=cfg.buf_cap,
@@ -100,6 +118,25 @@ def test_decode_loop_parity(cfg_idx, over, steps, seqs):
     cfg = wl.get_config(cfg_idx, **over)
     st = _run(cfg, steps, seqs)
     assert st["retrievals"] >= 1
+
+
+def test_decode_full_size_cfg1_benchmark_path():
+    # the Qwen3-8B-shaped layer at full size (8 KV heads x 32768 keys, C = 2048, 256 steps)
+    # through the calls the benchmark times: kv_boundary_select with row spans, then
+    # kv_gather_attend on the spans. Two Lloyd rounds suffice: the clustering only sets up
+    # the pool, and full-size K-means has its own sampled test.
+    cfg = wl.get_config(1, iters=2)
+    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True)
+    assert st["retrievals"] >= 2
+
+
+def test_decode_full_size_cfg4_batch16_benchmark_path():
+    # batched decode at full size: 16 sequences x 8 KV heads x 32768 keys in one launch,
+    # budget 1024; sequences 0 and 9 carry the oracle's clustering and are checked
+    cfg = wl.get_config(4, iters=2)
+    st = _run(cfg, 128, list(range(16)), compare_every=8, check=[0, 9], fused=True,
+              spans=True)
+    assert st["retrievals"] >= 2
 
 
 def test_decode_long_output_segments_small_buffer():
