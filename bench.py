@@ -12,6 +12,16 @@ per head, C = 2048, 10 Lloyd rounds):
 Inputs are synthetic (seeded Gaussian-mixture keys, random values and query
 walks) and resident in HBM before timing starts.
 
+``--config`` selects another workload of the same family: 0 (tiny, fp32),
+2 (long output: 2048 prefill keys, 16384 decode steps with temporal segments
+and a 1024-token local buffer; the decode step is kv_boundary ->
+kv_segment_append -> kv_select -> kv_gather_attend), 3 (36 layers of 131072
+keys, C = 8192, 1024 decode steps per layer; every layer clusters into a pool
+of its own and has its own query walk, so each layer-step reads its KV from
+HBM as in a real model; the layers share one layer's synthetic prefill
+keys/values), 4 (16 sequences of 32768 keys). Long decode loops are captured
+as several graphs.
+
 Printed JSON (one line): value = prefill keys clustered per second of whole
 steps (the decode loop included); the split into prefill time and decode
 microseconds per layer-step, the decode bytes moved per layer-step and the
@@ -66,7 +76,7 @@ def profiled_traffic(workload):
     return data
 
 
-def cpu_baseline(cfg, inp, q, lloyd_iters):
+def cpu_baseline(cfg, inp, q, lloyd_iters, dk=None, dv=None):
     """Time the oracle on a bounded sample and scale to one whole step."""
     import numpy as np
 
@@ -85,19 +95,23 @@ def cpu_baseline(cfg, inp, q, lloyd_iters):
     pack = okm.pack(keys0, vals0, o["labels"], o["centroids"], cfg.dtype)
     dec_steps = 16
     t0 = time.perf_counter()
-    run_decode([pack], q[:dec_steps, 0, :cfg.group], cfg.tau, cfg.budget, cfg.scale, cfg.dtype)
+    seg = {} if dk is None else dict(buf_cap=cfg.buf_cap, dec_k=dk[:dec_steps, 0, :1],
+                                     dec_v=dv[:dec_steps, 0, :1])
+    run_decode([pack], q[:dec_steps, 0, :cfg.group], cfg.tau, cfg.budget, cfg.scale, cfg.dtype,
+               **seg)
     t_dec = (time.perf_counter() - t0) / dec_steps  # one KV head, one step
     heads = cfg.batch * cfg.n_kv_heads
-    t_step = heads * t_lloyd + cfg.steps * heads * t_dec
+    t_step = cfg.layers * (heads * t_lloyd + cfg.steps * heads * t_dec)
     return {
-        "value": heads * cfg.n_keys / t_step,
+        "value": cfg.layers * heads * cfg.n_keys / t_step,
         "unit": "keys/s",
         "cores": int(cores),
         "kind": "oracle",
         "sample": (f"numpy fp64 oracle: Lloyd on 1 of {heads} KV heads ({cfg.n_keys} keys, "
                    f"C={cfg.n_clusters}, {lloyd_iters} of {cfg.iters} rounds timed) + {dec_steps} "
                    f"decode steps of 1 KV head; scaled to {heads} heads, {cfg.iters} rounds, "
-                   f"{cfg.steps} decode steps"),
+                   f"{cfg.steps} decode steps" + (f", {cfg.layers} layers" if cfg.layers > 1
+                                                 else "")),
         "step_s_extrapolated": t_step,
         "decode_us_per_layer_step": t_dec * heads * 1e6,
     }
@@ -130,69 +144,126 @@ def main():
     kvc.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     cfg = wl.get_config(args.config)
-    if cfg.layers != 1 or cfg.buf_cap != 0:
-        raise SystemExit("bench.py times single-layer prefill+decode workloads (configs 0, 1, 4)")
-    t_gen = time.perf_counter()
-    inp = wl.layer_inputs(cfg, 0)
-    q_np, _ = wl.layer_queries(cfg, 0)
-    log(f"inputs generated in {time.perf_counter() - t_gen:.1f}s")
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    B, H, N, d = inp["keys"].shape
-    C, T, Hq = cfg.n_clusters, cfg.steps, cfg.n_q_heads
-    keys = torch.from_numpy(inp["keys"]).to(tdt).cuda()
-    vals = torch.from_numpy(inp["values"]).to(tdt).cuda()
-    init = torch.from_numpy(inp["init_idx"]).cuda()
-    q = torch.from_numpy(q_np).to(tdt).cuda()  # [T, B, Hq, d]
-    pool = kvc.Pool(B, H, d, tdt, row_cap=N, unit_cap=C)
-    labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
-    ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
-    sel_cap = min(cfg.budget, C)
-    flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
-    sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
-    sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
-    sel_rows = torch.zeros(B, H, dtype=torch.int32, device="cuda")
-    sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device="cuda")
-    out = torch.zeros(T, B, Hq, d, dtype=torch.float32, device="cuda")
-    ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
-    ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, cfg.budget))
+    e = 2 if cfg.dtype == "bf16" else 4
+    B, H, N, d = cfg.batch, cfg.n_kv_heads, cfg.n_keys, cfg.head_dim
+    C, T, Hq, L = cfg.n_clusters, cfg.steps, cfg.n_q_heads, cfg.layers
+    seg = cfg.buf_cap > 0
+    # units: clusters, plus (long-output) the segments closed during decode
+    unit_cap = C + min(T, 8192 - C) if seg else C
+    row_cap = N + (T if seg else 0)
+    sel_cap = min(cfg.budget, unit_cap)
+
+    class Layer:
+        pass
+
+    layers = []
+    t_gen = time.perf_counter()
+    for li in range(L):
+        # Multi-layer workloads share layer 0's prefill keys/values (drawing them
+        # takes seconds per layer on the host); every layer still clusters them
+        # into a pool of its own and has its own query walk.
+        inp_l = wl.layer_inputs(cfg, li) if li == 0 else None
+        q_l, _ = wl.layer_queries(cfg, li)
+        y = Layer()
+        if li == 0:
+            y.keys = torch.from_numpy(inp_l["keys"]).to(tdt).cuda()
+            y.vals = torch.from_numpy(inp_l["values"]).to(tdt).cuda()
+            y.init = torch.from_numpy(inp_l["init_idx"]).cuda()
+        else:
+            y.keys, y.vals, y.init = layers[0].keys, layers[0].vals, layers[0].init
+        y.q = torch.from_numpy(q_l).to(tdt).cuda()  # [T, B, Hq, d]
+        if seg:
+            dk, dv = wl.layer_decode_kv(cfg, li)
+            y.dk = torch.from_numpy(dk).to(tdt).cuda()  # [T, B, H, d]
+            y.dv = torch.from_numpy(dv).to(tdt).cuda()
+        y.pool = kvc.Pool(B, H, d, tdt, row_cap=row_cap, unit_cap=unit_cap, buf_cap=cfg.buf_cap)
+        y.labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
+        y.ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
+        y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
+        y.sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
+        y.sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+        y.sel_rows = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+        y.sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device="cuda")
+        y.out = torch.zeros(B, Hq, d, dtype=torch.float32, device="cuda")
+        y.ws_sel = kvc.workspace(kvc.kv_select_workspace(y.pool, Hq))
+        y.ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(y.pool, Hq, cfg.budget))
+        layers.append(y)
+        if li == 0:
+            inp, q_np = inp_l, q_l  # layer 0 feeds the CPU baseline
+            dk0, dv0 = (dk, dv) if seg else (None, None)
+        del inp_l, q_l
+        if L > 1 and (li + 1) % 6 == 0:
+            log(f"inputs of {li + 1}/{L} layers generated ({time.perf_counter() - t_gen:.0f}s)")
+    log(f"inputs generated in {time.perf_counter() - t_gen:.1f}s")
+    y0 = layers[0]
+    keys, pool, sel, sel_n, sel_rows, sel_spans = (y0.keys, y0.pool, y0.sel, y0.sel_n,
+                                                   y0.sel_rows, y0.sel_spans)
 
     def prefill():
-        kvc.kv_cluster_build(pool, keys, vals, C, cfg.iters, init, assign_out=labels, ws=ws_build)
+        for y in layers:
+            kvc.kv_cluster_build(y.pool, y.keys, y.vals, C, cfg.iters, y.init,
+                                 assign_out=y.labels, ws=y.ws_build)
 
-    def decode(record=None):
-        for t in range(T):
-            kvc.kv_boundary_select(pool, q[t - 1] if t else None, q[t], cfg.tau, cfg.budget,
-                                   flags[t], sel, sel_n, sel_rows, ws=ws_sel, sel_spans=sel_spans)
-            kvc.kv_gather_attend(pool, q[t], cfg.scale, None, sel_n, cfg.budget, out[t], ws=ws_att,
-                                 sel_spans=sel_spans)
+    def decode_step(y, t):
+        q_prev = y.q[t - 1] if t else None
+        if seg:  # boundary -> segment append -> selection -> attention
+            kvc.kv_boundary(q_prev, y.q[t], cfg.tau, y.flags[t])
+            kvc.kv_segment_append(y.pool, y.dk[t], y.dv[t], y.flags[t])
+            kvc.kv_select(y.pool, y.q[t], cfg.budget, y.flags[t], y.sel, y.sel_n, y.sel_rows,
+                          ws=y.ws_sel, sel_spans=y.sel_spans)
+        else:
+            kvc.kv_boundary_select(y.pool, q_prev, y.q[t], cfg.tau, cfg.budget, y.flags[t],
+                                   y.sel, y.sel_n, y.sel_rows, ws=y.ws_sel,
+                                   sel_spans=y.sel_spans)
+        kvc.kv_gather_attend(y.pool, y.q[t], cfg.scale, None, y.sel_n, cfg.budget, y.out,
+                             ws=y.ws_att, sel_spans=y.sel_spans)
+
+    def decode(t0, t1, record=None):
+        for t in range(t0, t1):
+            for y in layers:
+                decode_step(y, t)
             if record is not None:
-                record.append(sel_rows.clone())
+                record[0][t].copy_(y0.sel_rows)
+                if seg:
+                    record[1][t].copy_(y0.pool.n_rows - y0.pool.buf_begin)
 
     # eager pass: loads kernels and records the per-step work for the byte count
     prefill()
-    rows_rec = []
-    decode(rows_rec)
+    rec = (torch.zeros(T, B, H, dtype=torch.int32, device="cuda"),
+           torch.zeros(T, B, dtype=torch.int32, device="cuda"))
+    decode(0, T, rec)
     torch.cuda.synchronize()
-    rows = torch.stack(rows_rec).cpu().numpy()  # [T, B, H]
-    fl = flags.cpu().numpy().astype(bool)       # [T, B]
-    e = 2 if cfg.dtype == "bf16" else 4
-    n_cand = C
+    rows = rec[0].cpu().numpy().astype(np.int64)   # [T, B, H] selected pool rows (layer 0)
+    buf_rows = rec[1].cpu().numpy().astype(np.int64) if seg else np.zeros((T, B), np.int64)
+    fl = y0.flags.cpu().numpy().astype(bool)       # [T, B]
+    n_cand = C  # candidates scored on a retrieval step (clusters; segments add a few)
     bytes_steps = (2 * Hq * d * e * B
                    + fl.sum(1) * H * n_cand * (d * e + 4)
-                   + rows.sum((1, 2)) * 2 * d * e
+                   + (rows.sum((1, 2)) + H * buf_rows.sum(1)) * 2 * d * e
                    + B * Hq * d * 4)
     dec_bytes = float(bytes_steps.mean())
-    log(f"retrieval steps: {int(fl.sum())} of {T}; mean attended rows/head {rows.mean():.1f}")
+    log(f"retrieval steps: {int(fl.sum())} of {T} (layer 0); mean selected rows/head "
+        f"{rows.mean():.1f}" + (f", mean buffer rows {buf_rows.mean():.1f}" if seg else ""))
 
-    # capture the decode loop once; replay per step
+    # capture the decode loop in graphs of at most ~4096 launches; replay per step
     stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
+    calls = (4 if seg else 2) * L
+    chunk = max(1, min(T, 4096 // calls))
     with torch.cuda.stream(stream):
-        decode()  # warm on the capture stream
+        prefill()
+        decode(0, T)  # warm on the capture stream
     torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=stream):
-        decode()
+    graphs = []
+    prefill()  # decode state as after a prefill
     torch.cuda.synchronize()
+    for t0 in range(0, T, chunk):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            decode(t0, min(T, t0 + chunk))
+        graphs.append(g)
+    torch.cuda.synchronize()
+    log(f"decode captured in {len(graphs)} graph(s) of up to {chunk} steps x {calls} launches")
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -204,7 +275,8 @@ def main():
             prefill()
             if i is not None:
                 ev[i][1].record(stream)
-            graph.replay()
+            for g in graphs:
+                g.replay()
             if i is not None:
                 ev[i][2].record(stream)
 
@@ -219,7 +291,11 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     pre_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-    dec_us = dec_ms * 1e3 / T
+    dec_us = dec_ms * 1e3 / (T * L)
+    for y in layers:
+        st = int(y.pool.status.item())
+        if st != 0:
+            raise SystemExit(f"pool status {st} ({kvc.lib().kv_status_string(st).decode()})")
 
     def launch_ms(fn, reps):
         """Mean GPU time per launch of fn: `reps` back-to-back launches on
@@ -239,11 +315,12 @@ def main():
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
     att_rows = int(sel_rows.sum().item())
-    att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, q[T - 1], cfg.scale, None, sel_n,
-                                                    cfg.budget, out[T - 1], ws=ws_att,
+    att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, y0.q[T - 1], cfg.scale, None, sel_n,
+                                                    cfg.budget, y0.out, ws=y0.ws_att,
                                                     sel_spans=sel_spans),
                        args.attend_reps)
-    att_bytes = (att_rows * 2 * d * e          # selected K and V rows
+    att_buf = int((pool.n_rows - pool.buf_begin).sum().item()) * H if seg else 0
+    att_bytes = ((att_rows + att_buf) * 2 * d * e  # selected (and local-buffer) K and V rows
                  + B * Hq * d * e              # queries
                  + B * Hq * d * 4              # fp32 output
                  + sel_units_n * 8)            # row span (start, size) per selected unit
@@ -261,10 +338,11 @@ def main():
                        args.assign_reps)
     flops = 2.0 * B * H * N * C * d
     achieved = flops / (asg_ms * 1e-3) / 1e12
-    share = {"k_gather_attend": T * att_ms / ms_step, "k_assign_mfma": cfg.iters * asg_ms / ms_step}
+    share = {"k_gather_attend": T * L * att_ms / ms_step,
+             "k_assign_mfma": cfg.iters * L * asg_ms / ms_step}
 
     traffic = profiled_traffic(cfg.name)
-    keys_per_step = B * H * N
+    keys_per_step = L * B * H * N
     res = {
         "metric": "prefill keys clustered/s; decode select+gather+attend us/layer-step, %HBM peak",
         "value": keys_per_step / (ms_step * 1e-3),
@@ -278,9 +356,10 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": B, "n_kv_heads": H, "n_q_heads": Hq,
-                   "head_dim": d, "n_keys": N, "n_clusters": C, "iters": cfg.iters,
-                   "decode_steps": T, "budget": cfg.budget, "tau": cfg.tau},
+        "config": {"workload": cfg.name, "layers": L, "batch": B, "n_kv_heads": H,
+                   "n_q_heads": Hq, "head_dim": d, "n_keys": N, "n_clusters": C,
+                   "iters": cfg.iters, "decode_steps": T, "budget": cfg.budget,
+                   "local_buffer": cfg.buf_cap, "tau": cfg.tau},
         "prefill_ms": pre_ms,
         "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),
         "decode_us_per_layer_step": dec_us,
@@ -309,7 +388,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, args.cpu_lloyd_iters)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, args.cpu_lloyd_iters, dk0, dv0)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
