@@ -14,8 +14,8 @@ walks) and resident in HBM before timing starts.
 
 ``--config`` selects another workload of the same family: 0 (tiny, fp32),
 2 (long output: 2048 prefill keys, 16384 decode steps with temporal segments
-and a 1024-token local buffer; the decode step is kv_boundary ->
-kv_segment_append -> kv_select -> kv_gather_attend), 3 (36 layers of 131072
+and a 1024-token local buffer; the decode step is kv_boundary_segment_append
+(boundary test + append in one launch) -> kv_select -> kv_gather_attend), 3 (36 layers of 131072
 keys, C = 8192, 1024 decode steps per layer; every layer clusters into a pool
 of its own and has its own query walk, so each layer-step reads its KV from
 HBM as in a real model; the layers share one layer's synthetic prefill
@@ -207,9 +207,9 @@ def main():
 
     def decode_step(y, t):
         q_prev = y.q[t - 1] if t else None
-        if seg:  # boundary -> segment append -> selection -> attention
-            kvc.kv_boundary(q_prev, y.q[t], cfg.tau, y.flags[t])
-            kvc.kv_segment_append(y.pool, y.dk[t], y.dv[t], y.flags[t])
+        if seg:  # boundary + segment append -> selection -> attention
+            kvc.kv_boundary_segment_append(y.pool, q_prev, y.q[t], cfg.tau, y.dk[t], y.dv[t],
+                                           y.flags[t])
             kvc.kv_select(y.pool, y.q[t], cfg.budget, y.flags[t], y.sel, y.sel_n, y.sel_rows,
                           ws=y.ws_sel, sel_spans=y.sel_spans)
         else:
@@ -248,7 +248,7 @@ def main():
 
     # capture the decode loop in graphs of at most ~4096 launches; replay per step
     stream = torch.cuda.Stream()
-    calls = (4 if seg else 2) * L
+    calls = (3 if seg else 2) * L
     chunk = max(1, min(T, 4096 // calls))
     with torch.cuda.stream(stream):
         prefill()

@@ -201,6 +201,18 @@ kv_status kv_boundary(const void *q_prev, const void *q_cur, int32_t batch, int3
 kv_status kv_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
                             const uint8_t *flag, hipStream_t stream);
 
+/* Decode steps 1 and 2 in one launch: exactly kv_boundary(q_prev, q_cur,
+ * pool->batch, n_q_heads, pool->head_dim, pool->dtype, tau, flag, r)
+ * followed by kv_segment_append(pool, k_t, v_t, flag), with the same results
+ * bit for bit. The append workgroup of each sequence evaluates that
+ * sequence's boundary test itself. flag: [batch] uint8 out (the selection of
+ * the same step reads it); r: NULL or [batch] fp32 out. Validation as the
+ * two calls (pool->buf_cap > 0 required). */
+kv_status kv_boundary_segment_append(const kv_pool *pool, const void *q_prev, const void *q_cur,
+                                     int32_t n_q_heads, float tau, const void *k_t,
+                                     const void *v_t, uint8_t *flag, float *r,
+                                     hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Decode step 3: group-consistent scoring and budgeted selection. LouisKV
  * note, flowchart (on a boundary, q_t is compared with every unit's centroid

@@ -36,7 +36,7 @@ EXPORTED = [
     "kv_kmeans_prepare", "kv_kmeans_assign_prepared",
     "kv_kmeans_update_workspace", "kv_kmeans_update",
     "kv_boundary",
-    "kv_segment_append",
+    "kv_segment_append", "kv_boundary_segment_append",
     "kv_select_workspace", "kv_select", "kv_boundary_select",
     "kv_gather_attend_workspace", "kv_gather_attend",
 ]
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
                                      c_size, vp]),
         "kv_boundary": (c_int, [vp, vp, c_int, c_int, c_int, c_int, ctypes.c_float, vp, vp, vp]),
         "kv_segment_append": (c_int, [pool_p, vp, vp, vp, vp]),
+        "kv_boundary_segment_append": (c_int, [pool_p, vp, vp, c_int, ctypes.c_float, vp, vp, vp,
+                                               vp, vp]),
         "kv_select_workspace": (c_size, [pool_p, c_int]),
         "kv_select": (c_int, [pool_p, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, vp, c_size,
                               vp]),
@@ -272,6 +274,14 @@ def kv_boundary(q_prev, q_cur, tau: float, flag, r=None, stream=None) -> None:
 def kv_segment_append(pool: Pool, k_t, v_t, flag, stream=None) -> None:
     _check("kv_segment_append", lib().kv_segment_append(
         pool.ref(), _ptr(k_t), _ptr(v_t), _ptr(flag), _stream(stream)))
+
+
+def kv_boundary_segment_append(pool: Pool, q_prev, q_cur, tau: float, k_t, v_t, flag, r=None,
+                               stream=None) -> None:
+    """kv_boundary then kv_segment_append in one launch (q_prev None: first step)."""
+    _check("kv_boundary_segment_append", lib().kv_boundary_segment_append(
+        pool.ref(), _ptr(q_prev), _ptr(q_cur), q_cur.shape[1], float(tau), _ptr(k_t), _ptr(v_t),
+        _ptr(flag), _ptr(r), _stream(stream)))
 
 
 def kv_select_workspace(pool: Pool, n_q_heads: int) -> int:

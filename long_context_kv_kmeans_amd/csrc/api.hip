@@ -203,7 +203,21 @@ kv_status kv_segment_append(const kv_pool *pool, const void *k_t, const void *v_
   if (st != KV_OK) return st;
   if (!k_t || !v_t || !flag) return KV_ERR_INVALID_ARG;
   if (pool->buf_cap <= 0) return KV_ERR_INVALID_ARG;
-  return launch_segment_append(pool, k_t, v_t, flag, stream);
+  return launch_segment_append(pool, k_t, v_t, flag, false, nullptr, nullptr, 0, 0.f, nullptr,
+                               nullptr, stream);
+}
+
+kv_status kv_boundary_segment_append(const kv_pool *pool, const void *q_prev, const void *q_cur,
+                                     int32_t n_q_heads, float tau, const void *k_t,
+                                     const void *v_t, uint8_t *flag, float *r,
+                                     hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  if (!q_cur || !k_t || !v_t || !flag) return KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || tau != tau) return KV_ERR_INVALID_ARG;
+  if (pool->buf_cap <= 0) return KV_ERR_INVALID_ARG;
+  return launch_segment_append(pool, k_t, v_t, nullptr, true, q_prev, q_cur, n_q_heads, tau,
+                               flag, r, stream);
 }
 
 size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads) {

@@ -144,35 +144,80 @@ kv_status launch_boundary(const void *q_prev, const void *q_cur, int batch, int 
 // One workgroup per sequence. Thread 0 does the scalar bookkeeping; all
 // threads move the (head, element) data. Segment boundaries are shared by
 // the sequence's KV heads, so head 0's unit table is read for evictions.
-template <typename T>
+// BD > 0: the workgroup first runs the boundary test of its sequence
+// (head_dim BD) on (q_prev, q_cur) itself and writes flag / r, instead of
+// reading flag.
+constexpr int kAppendPrefetch = 8;  // (head, element) pairs per thread loaded up front
+
+template <typename T, int BD>
 __global__ void __launch_bounds__(256) k_segment_append(kv_pool pool, const T *__restrict__ k_t,
                                                         const T *__restrict__ v_t,
-                                                        const uint8_t *__restrict__ flag) {
+                                                        const uint8_t *__restrict__ flag,
+                                                        const T *__restrict__ q_prev,
+                                                        const T *__restrict__ q_cur, int hq,
+                                                        float tau, uint8_t *__restrict__ flag_out,
+                                                        float *__restrict__ r_out) {
+  constexpr int PER = kAppendPrefetch;
   __shared__ int s_close, s_ok, s_open_len, s_seg_begin, s_n_rows, s_n_units;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int H = pool.n_kv_heads, D = pool.head_dim;
-  if (threadIdx.x == 0) {
-    const int n_rows = pool.n_rows[b], seg_begin = pool.seg_begin[b], n_units = pool.n_units[b];
-    const int open_len = n_rows - seg_begin;
-    const int close = ((flag[b] != 0) && open_len > 0) || open_len >= pool.buf_cap;
-    int ok = n_rows < pool.row_cap && (!close || n_units < pool.unit_cap);
+  const int HD = H * D;
+  // Everything that does not depend on the boundary decision is requested
+  // first, so it shares one memory round trip with the boundary test's loads.
+  int c_rows = 0, c_seg = 0, c_units = 0, c_buf = 0, c_cand = 0;
+  if (tid == 0) {
+    c_rows = pool.n_rows[b];
+    c_seg = pool.seg_begin[b];
+    c_units = pool.n_units[b];
+    c_buf = pool.buf_begin[b];
+    c_cand = pool.n_cand[b];
+  }
+  float sums[PER];
+  T kvs[PER], vvs[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * 256;
+    if (i < HD) {
+      sums[j] = pool.seg_sum[(size_t)b * HD + i];
+      kvs[j] = k_t[(size_t)b * HD + i];
+      vvs[j] = v_t[(size_t)b * HD + i];
+    }
+  }
+  int f;
+  if constexpr (BD > 0) {
+    __shared__ float s_part[4];
+    float rv = __builtin_nanf("");
+    f = 1;
+    if (q_prev != nullptr) {
+      rv = boundary_r<T, BD>(q_prev, q_cur, hq, b, s_part);
+      f = rv < tau ? 1 : 0;
+    }
+    if (tid == 0) {
+      flag_out[b] = (uint8_t)f;
+      if (r_out) r_out[b] = rv;
+    }
+  } else {
+    f = tid == 0 ? flag[b] != 0 : 0;
+  }
+  if (tid == 0) {
+    const int open_len = c_rows - c_seg;
+    const int close = (f && open_len > 0) || open_len >= pool.buf_cap;
+    int ok = c_rows < pool.row_cap && (!close || c_units < pool.unit_cap);
     if (!ok) __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
     s_close = close;
     s_ok = ok;
     s_open_len = open_len;
-    s_seg_begin = seg_begin;
-    s_n_rows = n_rows;
-    s_n_units = n_units;
+    s_seg_begin = c_seg;
+    s_n_rows = c_rows;
+    s_n_units = c_units;
   }
   __syncthreads();
   if (!s_ok) return;
   const int close = s_close, open_len = s_open_len, n_rows = s_n_rows, n_units = s_n_units;
-  const size_t HD = (size_t)H * D;
-  for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
+  auto move = [&](int i, float sum, T kv, T vv) {
     const int g = i / D, e = i % D;
     const size_t bg = (size_t)b * H + g;
-    float sum = pool.seg_sum[b * HD + i];
     if (close) {
       const float mean = sum / (float)open_len;
       const size_t uo = (bg * pool.unit_cap + n_units) * D + e;
@@ -184,18 +229,24 @@ __global__ void __launch_bounds__(256) k_segment_append(kv_pool pool, const T *_
       }
       sum = 0.f;
     }
-    const T kv = k_t[b * HD + i];
     const size_t ro = (bg * pool.row_cap + n_rows) * D + e;
     static_cast<T *>(pool.k)[ro] = kv;
-    static_cast<T *>(pool.v)[ro] = v_t[b * HD + i];
-    pool.seg_sum[b * HD + i] = sum + Elem<T>::to_f32(kv);
+    static_cast<T *>(pool.v)[ro] = vv;
+    pool.seg_sum[(size_t)b * HD + i] = sum + Elem<T>::to_f32(kv);
+  };
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * 256;
+    if (i < HD) move(i, sums[j], kvs[j], vvs[j]);
   }
-  if (threadIdx.x == 0) {
+  for (int i = tid + PER * 256; i < HD; i += 256)  // more than PER elements per thread
+    move(i, pool.seg_sum[(size_t)b * HD + i], k_t[(size_t)b * HD + i], v_t[(size_t)b * HD + i]);
+  if (tid == 0) {
     const int new_rows = n_rows + 1;
     const int new_units = n_units + close;
     int seg_begin = close ? n_rows : s_seg_begin;
-    int buf_begin = pool.buf_begin[b];
-    int n_cand = pool.n_cand[b];
+    int buf_begin = c_buf;
+    int n_cand = c_cand;
     const int32_t *us = pool.unit_start + (size_t)b * H * pool.unit_cap;
     const int32_t *uz = pool.unit_size + (size_t)b * H * pool.unit_cap;
     while (new_rows - buf_begin > pool.buf_cap && n_cand < new_units) {
@@ -214,13 +265,24 @@ __global__ void __launch_bounds__(256) k_segment_append(kv_pool pool, const T *_
 }
 
 kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
-                                const uint8_t *flag, hipStream_t s) {
-  if (pool->dtype == KV_BF16)
-    k_segment_append<uint16_t><<<pool->batch, 256, 0, s>>>(*pool, (const uint16_t *)k_t,
-                                                           (const uint16_t *)v_t, flag);
-  else
-    k_segment_append<float><<<pool->batch, 256, 0, s>>>(*pool, (const float *)k_t,
-                                                        (const float *)v_t, flag);
+                                const uint8_t *flag, bool fused, const void *q_prev,
+                                const void *q_cur, int hq, float tau, uint8_t *flag_out,
+                                float *r_out, hipStream_t s) {
+#define KVC_SA(T, BD)                                                                         \
+  k_segment_append<T, BD><<<pool->batch, 256, 0, s>>>(                                        \
+      *pool, (const T *)k_t, (const T *)v_t, flag, (const T *)q_prev, (const T *)q_cur, hq, \
+      tau, flag_out, r_out)
+  const bool d128 = pool->head_dim == 128;
+  if (pool->dtype == KV_BF16) {
+    if (!fused) KVC_SA(uint16_t, 0);
+    else if (d128) KVC_SA(uint16_t, 128);
+    else KVC_SA(uint16_t, 64);
+  } else {
+    if (!fused) KVC_SA(float, 0);
+    else if (d128) KVC_SA(float, 128);
+    else KVC_SA(float, 64);
+  }
+#undef KVC_SA
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

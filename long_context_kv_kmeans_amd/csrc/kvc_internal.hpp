@@ -193,8 +193,12 @@ kv_status launch_pack(const kv_pool *pool, const void *keys, const void *values,
 // Decode
 kv_status launch_boundary(const void *q_prev, const void *q_cur, int batch, int hq, int d,
                           kv_dtype dt, float tau, uint8_t *flag, float *r, hipStream_t s);
+// fused: run the boundary test on (q_prev, q_cur) inside the append kernel and
+// write flag_out / r_out instead of reading flag.
 kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void *v_t,
-                                const uint8_t *flag, hipStream_t s);
+                                const uint8_t *flag, bool fused, const void *q_prev,
+                                const void *q_cur, int hq, float tau, uint8_t *flag_out,
+                                float *r_out, hipStream_t s);
 int select_num_blocks(const kv_pool *pool);
 // fused: run the boundary test on (q_prev, q) inside the select kernel and
 // write flag_out / r_out instead of reading flag.

@@ -74,10 +74,11 @@ class DecodeRecord:
 
 
 def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, steps=None,
-               record_sel=True, fused=False, spans=False):
+               record_sel=True, fused=False, spans=False, fused_append=False):
     """Run the decode loop through the C ABI. q: device [T, B, Hq, d].
     fused: boundary test and selection through kv_boundary_select (no segments).
-    spans: selection also writes row spans and attention reads them."""
+    spans: selection also writes row spans and attention reads them.
+    fused_append: boundary test and segment append through kv_boundary_segment_append."""
     T = q.shape[0] if steps is None else steps
     B, Hq, d = q.shape[1:]
     H = pool.n_kv_heads
@@ -102,9 +103,13 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
                                    sel_units, sel_n, sel_rows, r=rec.r[t], ws=ws_sel,
                                    sel_spans=sel_spans)
         else:
-            kvc.kv_boundary(q[t - 1] if t else None, q[t], tau, rec.flag[t], rec.r[t])
-            if dec_k is not None:
-                kvc.kv_segment_append(pool, dec_k[t], dec_v[t], rec.flag[t])
+            if fused_append:
+                kvc.kv_boundary_segment_append(pool, q[t - 1] if t else None, q[t], tau,
+                                               dec_k[t], dec_v[t], rec.flag[t], r=rec.r[t])
+            else:
+                kvc.kv_boundary(q[t - 1] if t else None, q[t], tau, rec.flag[t], rec.r[t])
+                if dec_k is not None:
+                    kvc.kv_segment_append(pool, dec_k[t], dec_v[t], rec.flag[t])
             kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel,
                           sel_spans=sel_spans)
         kvc.kv_gather_attend(pool, q[t], scale, None if spans else sel_units, sel_n, budget,

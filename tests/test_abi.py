@@ -81,6 +81,23 @@ def test_boundary_select_validation():
                                 None, None, a, need, None) == kvc.KV_ERR_UNSUPPORTED  # local buffer
 
 
+def test_boundary_segment_append_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    f = ctypes.c_float(0.7)
+    pb = _fake_pool(buf_cap=64, seg_sum=0x10000)
+    assert L.kv_boundary_segment_append(ctypes.byref(pb), None, None, 32, f, a, a, a,
+                                        None, None) == kvc.KV_ERR_INVALID_ARG  # q_cur
+    assert L.kv_boundary_segment_append(ctypes.byref(pb), None, a, 32, f, a, a, None,
+                                        None, None) == kvc.KV_ERR_INVALID_ARG  # flag out
+    assert L.kv_boundary_segment_append(ctypes.byref(pb), None, a, 32,
+                                        ctypes.c_float(float("nan")), a, a, a, None,
+                                        None) == kvc.KV_ERR_INVALID_ARG
+    p = _fake_pool()  # no local buffer
+    assert L.kv_boundary_segment_append(ctypes.byref(p), None, a, 32, f, a, a, a, None,
+                                        None) == kvc.KV_ERR_INVALID_ARG
+
+
 def test_pool_validation():
     L = kvc.lib()
     a = ctypes.c_void_p(0x10000)

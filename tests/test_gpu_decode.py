@@ -179,9 +179,11 @@ def test_fused_boundary_select_matches_separate_calls(cfg_idx, over, steps, seqs
                                       b.out.cpu().numpy().view(np.uint32))
 
 
-def test_decode_segments_with_spans_matches_unit_lookup():
+def test_decode_segments_spans_and_fused_append_match_separate_calls():
     # long-output config: spans written by kv_select (segments included) give the
-    # same attention as the unit-table lookup, bit for bit
+    # same attention as the unit-table lookup, and kv_boundary_segment_append the
+    # same flags, r, segment bookkeeping and outputs as kv_boundary +
+    # kv_segment_append, bit for bit
     cfg = wl.get_config(2, buf_cap=64, steps=300, p_jump=0.05, budget=256, iters=3)
     inp = wl.layer_inputs(cfg, 0)
     labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
@@ -190,12 +192,18 @@ def test_decode_segments_with_spans_matches_unit_lookup():
     n_units = cfg.n_clusters + cfg.steps
     sel_cap = min(cfg.budget, n_units)
     outs = []
-    for spans in (False, True):
+    # unit lookup; spans; spans + boundary test fused into the segment append
+    for kw in (dict(), dict(spans=True), dict(spans=True, fused_append=True)):
         pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
                                       n_units=n_units, buf_cap=cfg.buf_cap, extra_rows=cfg.steps)
         rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, cfg.budget, cfg.scale, sel_cap,
-                         dec_k=to_dev(dk, cfg.dtype), dec_v=to_dev(dv, cfg.dtype), spans=spans)
+                         dec_k=to_dev(dk, cfg.dtype), dec_v=to_dev(dv, cfg.dtype), **kw)
         outs.append(rec)
-    assert torch.equal(outs[0].sel, outs[1].sel)
-    np.testing.assert_array_equal(outs[0].out.cpu().numpy().view(np.uint32),
-                                  outs[1].out.cpu().numpy().view(np.uint32))
+    for o in outs[1:]:
+        for name in ("flag", "sel_n", "sel", "counters"):
+            assert torch.equal(outs[0].__dict__[name], o.__dict__[name]), name
+        ra, rb = outs[0].r.cpu().numpy(), o.r.cpu().numpy()
+        np.testing.assert_array_equal(ra[1:].view(np.uint32), rb[1:].view(np.uint32))
+        assert np.isnan(rb[0]).all()
+        np.testing.assert_array_equal(outs[0].out.cpu().numpy().view(np.uint32),
+                                      o.out.cpu().numpy().view(np.uint32))
