@@ -152,6 +152,17 @@ def test_attend_many_splits_and_buffer_rows():
     su, sn = _sel_tensors(sel, B, H, 64)
     q = wl.to_dtype(rng.standard_normal((B, H * G, d)), "bf16")
     out = _attend(pool, to_dev(q, "bf16"), su, sn, 1024, d ** -0.5)
+    # the same selection handed over as row spans (no unit ids) gives the same bits
+    spans = torch.zeros(B, H, 64, 2, dtype=torch.int32)
+    for b in range(B):
+        for g in range(H):
+            for i, u in enumerate(sel[b][g]):
+                spans[b, g, i, 0], spans[b, g, i, 1] = int(starts[u]), int(sizes[u])
+    out_s = torch.full((B, H * G, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.kv_gather_attend(pool, to_dev(q, "bf16"), d ** -0.5, None, sn, 1024, out_s,
+                         sel_spans=spans.cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out_s.cpu().numpy().view(np.uint32), out.view(np.uint32))
     nr, bb = [4700, 4321], [4001, 4000]
     for b in range(B):
         for g in range(H):
@@ -159,3 +170,24 @@ def test_attend_many_splits_and_buffer_rows():
             rows = np.concatenate([rows, np.arange(bb[b], nr[b])])
             ref = oat.attend_exact(q[b, g * G:(g + 1) * G], kk[b, g][rows], vv[b, g][rows], d ** -0.5)
             assert max_rel_err(out[b, g * G:(g + 1) * G], ref) <= TOL
+
+
+def test_attend_sel_n_out_of_range_is_clamped():
+    # sel_n above sel_cap reads only sel_cap entries; a negative sel_n is an empty selection
+    rng = np.random.default_rng(11)
+    d, G = 64, 2
+    pool = make_pool(1, 2, d, "fp32", 64, 8)
+    kk = rng.standard_normal((1, 2, 64, d)).astype(np.float32)
+    vv = rng.standard_normal((1, 2, 64, d)).astype(np.float32)
+    pool.k.copy_(torch.from_numpy(kk).cuda())
+    pool.v.copy_(torch.from_numpy(vv).cuda())
+    pool.unit_start[0, :, :8] = torch.arange(0, 64, 8, dtype=torch.int32).cuda()
+    pool.unit_size[0, :, :8] = 8
+    su, _ = _sel_tensors([[[0, 3, 5], [1, 2, 6]]], 1, 2, 3)
+    sn = torch.tensor([[7, -4]], dtype=torch.int32).cuda()
+    q = rng.standard_normal((1, 2 * G, d)).astype(np.float32)
+    out = _attend(pool, to_dev(q, "fp32"), su, sn, 24, 0.125)
+    rows = unit_rows(np.arange(0, 64, 8), np.full(8, 8), [0, 3, 5])
+    ref = oat.attend_exact(q[0, :G], kk[0, 0][rows], vv[0, 0][rows], 0.125)
+    assert max_rel_err(out[0, :G], ref) <= TOL
+    assert (out[0, G:] == 0).all()

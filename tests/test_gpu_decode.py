@@ -207,3 +207,36 @@ def test_decode_segments_spans_and_fused_append_match_separate_calls():
         assert np.isnan(rb[0]).all()
         np.testing.assert_array_equal(outs[0].out.cpu().numpy().view(np.uint32),
                                       o.out.cpu().numpy().view(np.uint32))
+
+
+def test_segment_append_capacity_errors_are_reported():
+    # out of rows: the status word says so, the sequence's step is skipped and
+    # nothing is written past row_cap; out of units likewise when a close is due
+    import long_context_kv_kmeans_amd as kvc
+    from tests.gpu_util import make_pool
+    d, H = 64, 2
+    pool = make_pool(1, H, d, "fp32", 10, 4, buf_cap=4, extra_rows=2)  # row_cap 12
+    pool.n_rows.fill_(10)
+    pool.n_units.fill_(2)
+    pool.n_cand.fill_(2)
+    pool.buf_begin.fill_(10)
+    pool.seg_begin.fill_(10)
+    kt = torch.ones(1, H, d, device="cuda")
+    flag = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        kvc.kv_segment_append(pool, kt, kt, flag)
+    torch.cuda.synchronize()
+    assert int(pool.status.item()) == kvc.KV_ERR_CAPACITY
+    assert int(pool.n_rows.item()) == 12
+    # units: a boundary with a full unit table
+    pool2 = make_pool(1, H, d, "fp32", 10, 2, buf_cap=4, extra_rows=8)
+    pool2.n_rows.fill_(12)
+    pool2.n_units.fill_(2)
+    pool2.n_cand.fill_(2)
+    pool2.buf_begin.fill_(10)
+    pool2.seg_begin.fill_(10)
+    flag.fill_(1)
+    kvc.kv_segment_append(pool2, kt, kt, flag)
+    torch.cuda.synchronize()
+    assert int(pool2.status.item()) == kvc.KV_ERR_CAPACITY
+    assert int(pool2.n_rows.item()) == 12 and int(pool2.n_units.item()) == 2

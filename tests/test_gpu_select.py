@@ -188,3 +188,10 @@ def test_select_full_size_cfg3_head():
     q = wl.to_dtype(rng.standard_normal((3, 1, cfg.group, d)), "bf16")
     sub = cfg.replace(n_kv_heads=1, n_q_heads=cfg.group, n_keys=N)
     assert _check_case(sub, keys, vals, labels, cents, q, cfg.budget) == 0
+
+
+def test_select_budget_zero_selects_nothing():
+    # no unit of positive size fits a zero budget
+    pool, q = _hand_pool([1.0, 2.0, 3.0], [1, 2, 3])
+    sel, _ = _run_select(pool, q, 0, 3)
+    assert int(sel[1][0, 0]) == 0 and int(sel[2][0, 0]) == 0
