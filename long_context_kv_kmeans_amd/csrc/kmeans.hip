@@ -18,8 +18,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kAssignColBlocks = 2;                      // 32-key MFMA column blocks per wave
-constexpr int kAssignMinWaves = 3;                       // waves per SIMD the register budget targets
+constexpr int kAssignMinWaves = 4;                       // waves per SIMD the register budget targets
 constexpr int kTilesPerStage = 2;                        // 64 centroids per LDS stage
+constexpr int kAssignWaves = 8;                          // waves per workgroup
 constexpr int kRankChunk = 1024;                         // keys per counting-sort chunk
 
 // ---------------------------------------------------------------- init
@@ -123,14 +124,16 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
   if (e0 == 0) write_centroid_aug(tile_base, KS, m, real, 0.5f * sq);
 }
 
-// One workgroup = 4 waves x 64 keys. Keys are the B operand (column n = key),
+// One workgroup = 8 waves x 64 keys. Keys are the B operand (column n = key),
 // resident in VGPRs for the whole centroid sweep. Centroid tiles stream into
 // two LDS stage buffers with direct global->LDS loads (each wave instruction
 // moves one 1 KB fragment block), so staging costs neither VGPRs nor LDS
 // write instructions; the two buffers are separate objects and are selected
 // statically, which lets the compiler keep the next stage's loads in flight
-// while the current stage is read. The MFMAs of tile t+1 are issued before
-// the argmin of tile t so the matrix cores and the VALU overlap.
+// while the current stage is read. A wave folds tile t into its argmin before
+// issuing tile t+1's MFMAs into the same accumulators (no copies); the matrix
+// cores and the VALU overlap across the 4 waves each SIMD holds (128 VGPRs),
+// and a stage's barrier is shared by 8 waves per 36 KB of staging.
 //
 // Argmin: every lane sees one key and 16 centroid rows per tile. A score
 // -d^2/2 (<= 0, negative floats order inversely to their bit patterns) is
@@ -144,7 +147,7 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
 // decision only where two distances agree to about 2^-19 relative, below the
 // fp32 accumulation error of the 144-term dot product.
 template <int D, int NCB, int MINW>
-__global__ void __launch_bounds__(256, MINW)
+__global__ void __launch_bounds__(64 * kAssignWaves, MINW)
     k_assign_mfma(const uint16_t *__restrict__ keys, const uint16_t *__restrict__ frags,
                   int32_t *__restrict__ labels, int n, int c, int ntile, int blocks_per_head,
                   int total_blocks) {
@@ -158,7 +161,7 @@ __global__ void __launch_bounds__(256, MINW)
   const int bh = bid / blocks_per_head;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int KPW = 32 * NCB;  // keys per wave
-  const int key0 = (bid % blocks_per_head) * (4 * KPW) + wave * KPW;
+  const int key0 = (bid % blocks_per_head) * (kAssignWaves * KPW) + wave * KPW;
   const int half = lane >> 5;
 
   // Key fragments (B operand): lane holds key n = lane % 32, k = 16 s + 8 half + j.
@@ -205,7 +208,7 @@ __global__ void __launch_bounds__(256, MINW)
   // blocks of tiles >= ntile are never read and are skipped.
   auto dma_stage = [&](int st, uint4 *dst) {
 #pragma unroll
-    for (int i = wave; i < kTilesPerStage * KS; i += 4) {
+    for (int i = wave; i < kTilesPerStage * KS; i += kAssignWaves) {
       if (st * kTilesPerStage + i / KS < ntile)
         __builtin_amdgcn_global_load_lds(gfr + (size_t)st * STAGE_U4 + i * 64 + lane, dst + i * 64,
                                          16, 0, 0);
@@ -247,17 +250,15 @@ __global__ void __launch_bounds__(256, MINW)
     }
   };
 
-  f32x16_t acc[NCB], nxt_acc[NCB];
+  f32x16_t acc[NCB];
   int t = 0;  // tile whose scores sit in acc
   auto argmin_all = [&](bool last) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) argmin_tile(acc[cb], cb, t, last);
   };
   auto advance = [&](const uint4 *buf, int tt, int nt) {
-    mfma_tile(buf, tt, nxt_acc);  // tile nt's MFMAs go out before tile t's argmin
     argmin_all(false);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = nxt_acc[cb];
+    mfma_tile(buf, tt, acc);
     t = nt;
   };
   // Tiles [st * TPS + 1, (st + 1) * TPS) of stage st (in `cur`), then the first
@@ -384,13 +385,14 @@ kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, in
     const int ntile = (c + 31) / 32;
     const uint16_t *frags = static_cast<const uint16_t *>(ws);
     constexpr int NCB = kAssignColBlocks;
-    const int bph = (n + 128 * NCB - 1) / (128 * NCB);
+    constexpr int KPB = kAssignWaves * 32 * NCB;  // keys per workgroup
+    const int bph = (n + KPB - 1) / KPB;
     const int total = bph * bh;
     if (d == 128)
-      k_assign_mfma<128, NCB, kAssignMinWaves><<<total, 256, 0, s>>>(
+      k_assign_mfma<128, NCB, kAssignMinWaves><<<total, 64 * kAssignWaves, 0, s>>>(
           (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
     else
-      k_assign_mfma<64, NCB, kAssignMinWaves><<<total, 256, 0, s>>>(
+      k_assign_mfma<64, NCB, kAssignMinWaves><<<total, 64 * kAssignWaves, 0, s>>>(
           (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
   } else {
     const float *hn = static_cast<const float *>(ws);
