@@ -32,6 +32,15 @@ timed with HIP events on the stream they run on around back-to-back
 launches queued behind a GPU sleep, so that host enqueue gaps do not enter
 the interval. ``cpu_baseline`` times the CPU oracle on a bounded sample of the
 same work.
+
+Variants (single-layer workloads without segments; the printed line names
+them in ``config``): ``--pool host`` keeps the pool's K/V rows in pinned
+host memory, as the LouisKV note deploys it, and each retrieval step fetches
+the selected rows into an HBM working set (kv_fetch_selected) that attention
+reads -- the line then carries ``fetch`` (the gather's GB/s against the host
+link); ``--pool host-direct`` lets attention read host memory every step;
+``--policy per-token|stride:S`` replaces the boundary test's decision of when
+to retrieve; ``--units page:P`` uses pages of P consecutive keys as units.
 """
 from __future__ import annotations
 
@@ -47,6 +56,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HOST_LINK_GBS = 64.0        # MI355X host interface: PCIe 5.0 x16, one direction
 
 
 def log(*a):
@@ -128,6 +138,15 @@ def main():
     ap.add_argument("--assign-reps", type=int, default=20)
     ap.add_argument("--attend-reps", type=int, default=100)
     ap.add_argument("--copy-calibration-mib", type=int, default=64)
+    ap.add_argument("--pool", choices=("hbm", "host", "host-direct"), default="hbm",
+                    help="where the pool's K/V rows live: hbm; host (pinned host memory, "
+                         "retrieval steps fetch the selected rows into an HBM working set "
+                         "that attention reads); host-direct (attention reads host memory "
+                         "every step)")
+    ap.add_argument("--policy", default="boundary",
+                    help="when to retrieve: boundary (the cosine test), per-token, stride:S")
+    ap.add_argument("--units", default="cluster",
+                    help="retrieval units: cluster (K-means) or page:P (P consecutive keys)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
@@ -149,6 +168,18 @@ def main():
     B, H, N, d = cfg.batch, cfg.n_kv_heads, cfg.n_keys, cfg.head_dim
     C, T, Hq, L = cfg.n_clusters, cfg.steps, cfg.n_q_heads, cfg.layers
     seg = cfg.buf_cap > 0
+    host = args.pool != "hbm"
+    fetch = args.pool == "host"
+    sched = wl.retrieval_schedule(args.policy, T)
+    page = int(args.units.split(":", 1)[1]) if args.units.startswith("page:") else None
+    if args.units != "cluster" and page is None:
+        raise SystemExit(f"unknown --units {args.units!r}")
+    variant = host or sched is not None or page is not None
+    if variant and (seg or L > 1):
+        raise SystemExit("--pool/--policy/--units variants run on single-layer workloads "
+                         "without decode segments (--config 0, 1 or 4)")
+    if page is not None:
+        C = -(-N // page)  # one unit per page
     # units: clusters, plus (long-output) the segments closed during decode
     unit_cap = C + min(T, 8192 - C) if seg else C
     row_cap = N + (T if seg else 0)
@@ -166,6 +197,7 @@ def main():
         inp_l = wl.layer_inputs(cfg, li) if li == 0 else None
         q_l, _ = wl.layer_queries(cfg, li)
         y = Layer()
+        y.assign_in = None
         if li == 0:
             y.keys = torch.from_numpy(inp_l["keys"]).to(tdt).cuda()
             y.vals = torch.from_numpy(inp_l["values"]).to(tdt).cuda()
@@ -177,7 +209,18 @@ def main():
             dk, dv = wl.layer_decode_kv(cfg, li)
             y.dk = torch.from_numpy(dk).to(tdt).cuda()  # [T, B, H, d]
             y.dv = torch.from_numpy(dv).to(tdt).cuda()
-        y.pool = kvc.Pool(B, H, d, tdt, row_cap=row_cap, unit_cap=unit_cap, buf_cap=cfg.buf_cap)
+        y.pool = kvc.Pool(B, H, d, tdt, row_cap=row_cap, unit_cap=unit_cap, buf_cap=cfg.buf_cap,
+                          host_kv=host)
+        if fetch:  # HBM working set: the rows of the current selection, one span per head
+            y.wset = kvc.Pool(B, H, d, tdt, row_cap=cfg.budget, unit_cap=1)
+            y.wspans = torch.zeros(B, H, 1, 2, dtype=torch.int32, device="cuda")
+            y.wn = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+        if sched is not None:
+            y.sched = torch.from_numpy(np.repeat(sched[:, None], B, axis=1).astype(np.uint8)).cuda()
+        if page is not None:
+            y.assign_in = torch.from_numpy(wl.page_labels(B, H, N, page)).cuda()
+            y.init = torch.from_numpy(np.broadcast_to(
+                (np.arange(C) * page).astype(np.int32), (B, H, C)).copy()).cuda()
         y.labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
         y.ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
         y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
@@ -203,21 +246,34 @@ def main():
     def prefill():
         for y in layers:
             kvc.kv_cluster_build(y.pool, y.keys, y.vals, C, cfg.iters, y.init,
-                                 assign_out=y.labels, ws=y.ws_build)
+                                 assign_in=y.assign_in,
+                                 assign_out=None if y.assign_in is not None else y.labels,
+                                 ws=y.ws_build)
 
     def decode_step(y, t):
         q_prev = y.q[t - 1] if t else None
+        flag = y.flags[t]
         if seg:  # boundary + segment append -> selection -> attention
             kvc.kv_boundary_segment_append(y.pool, q_prev, y.q[t], cfg.tau, y.dk[t], y.dv[t],
                                            y.flags[t])
             kvc.kv_select(y.pool, y.q[t], cfg.budget, y.flags[t], y.sel, y.sel_n, y.sel_rows,
                           ws=y.ws_sel, sel_spans=y.sel_spans)
+        elif sched is not None:  # the schedule decides; no boundary test
+            flag = y.sched[t]
+            kvc.kv_select(y.pool, y.q[t], cfg.budget, flag, y.sel, y.sel_n, y.sel_rows,
+                          ws=y.ws_sel, sel_spans=y.sel_spans)
         else:
             kvc.kv_boundary_select(y.pool, q_prev, y.q[t], cfg.tau, cfg.budget, y.flags[t],
                                    y.sel, y.sel_n, y.sel_rows, ws=y.ws_sel,
                                    sel_spans=y.sel_spans)
-        kvc.kv_gather_attend(y.pool, y.q[t], cfg.scale, None, y.sel_n, cfg.budget, y.out,
-                             ws=y.ws_att, sel_spans=y.sel_spans)
+        if fetch:
+            kvc.kv_fetch_selected(y.pool, flag, None, y.sel_n, y.wset, y.wspans, y.wn,
+                                  sel_spans=y.sel_spans)
+            kvc.kv_gather_attend(y.wset, y.q[t], cfg.scale, None, y.wn, cfg.budget, y.out,
+                                 ws=y.ws_att, sel_spans=y.wspans)
+        else:
+            kvc.kv_gather_attend(y.pool, y.q[t], cfg.scale, None, y.sel_n, cfg.budget, y.out,
+                                 ws=y.ws_att, sel_spans=y.sel_spans)
 
     def decode(t0, t1, record=None):
         for t in range(t0, t1):
@@ -236,7 +292,7 @@ def main():
     torch.cuda.synchronize()
     rows = rec[0].cpu().numpy().astype(np.int64)   # [T, B, H] selected pool rows (layer 0)
     buf_rows = rec[1].cpu().numpy().astype(np.int64) if seg else np.zeros((T, B), np.int64)
-    fl = y0.flags.cpu().numpy().astype(bool)       # [T, B]
+    fl = (y0.flags if sched is None else y0.sched).cpu().numpy().astype(bool)  # [T, B]
     n_cand = C  # candidates scored on a retrieval step (clusters; segments add a few)
     bytes_steps = (2 * Hq * d * e * B
                    + fl.sum(1) * H * n_cand * (d * e + 4)
@@ -248,7 +304,7 @@ def main():
 
     # capture the decode loop in graphs of at most ~4096 launches; replay per step
     stream = torch.cuda.Stream()
-    calls = (3 if seg else 2) * L
+    calls = (3 if seg or fetch else 2) * L
     chunk = max(1, min(T, 4096 // calls))
     with torch.cuda.stream(stream):
         prefill()
@@ -315,16 +371,44 @@ def main():
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
     att_rows = int(sel_rows.sum().item())
-    att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, y0.q[T - 1], cfg.scale, None, sel_n,
-                                                    cfg.budget, y0.out, ws=y0.ws_att,
-                                                    sel_spans=sel_spans),
-                       args.attend_reps)
+    if fetch:  # attention reads the working set: one span per head
+        att_ms = launch_ms(lambda: kvc.kv_gather_attend(y0.wset, y0.q[T - 1], cfg.scale, None,
+                                                        y0.wn, cfg.budget, y0.out, ws=y0.ws_att,
+                                                        sel_spans=y0.wspans),
+                           args.attend_reps)
+        att_spans = int(y0.wn.sum().item())
+    else:
+        att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, y0.q[T - 1], cfg.scale, None,
+                                                        sel_n, cfg.budget, y0.out, ws=y0.ws_att,
+                                                        sel_spans=sel_spans),
+                           args.attend_reps)
+        att_spans = sel_units_n
     att_buf = int((pool.n_rows - pool.buf_begin).sum().item()) * H if seg else 0
     att_bytes = ((att_rows + att_buf) * 2 * d * e  # selected (and local-buffer) K and V rows
                  + B * Hq * d * e              # queries
                  + B * Hq * d * 4              # fp32 output
-                 + sel_units_n * 8)            # row span (start, size) per selected unit
+                 + att_spans * 8)              # row span (start, size) per selected unit
     att_gbs = att_bytes / (att_ms * 1e-3) / 1e9
+    att_peak = HOST_LINK_GBS if args.pool == "host-direct" else HBM_PEAK_GBS
+
+    fetch_res = None
+    if fetch:
+        # the working-set fetch of the final selection, every sequence retrieving
+        ones = torch.ones(B, dtype=torch.uint8, device="cuda")
+        f_ms = launch_ms(lambda: kvc.kv_fetch_selected(pool, ones, None, sel_n, y0.wset,
+                                                       y0.wspans, y0.wn, sel_spans=sel_spans),
+                         args.attend_reps)
+        f_bytes = att_rows * 2 * d * e  # K and V rows read over the host link
+        # a plain pinned-host -> HBM copy of 64 MiB: the link's practical rate here
+        hsrc = torch.ones(16 << 20, dtype=torch.float32, pin_memory=True)
+        hdst = torch.empty(16 << 20, dtype=torch.float32, device="cuda")
+        h2d_ms = launch_ms(lambda: hdst.copy_(hsrc, non_blocking=True), 5)
+        del hsrc, hdst
+        fetch_res = {"bound": "host-link", "kernel": "k_fetch_rows (kv_fetch_selected)",
+                     "achieved": f_bytes / (f_ms * 1e-3) / 1e9, "peak": HOST_LINK_GBS,
+                     "unit": "GB/s", "frac": f_bytes / (f_ms * 1e-3) / 1e9 / HOST_LINK_GBS,
+                     "bytes_per_launch": f_bytes, "avg_launch_ms": f_ms,
+                     "h2d_copy_gbs": (64 << 20) / (h2d_ms * 1e-3) / 1e9}
 
     # MFMA K-means assignment against prepared centroids (the kernel the
     # prefill runs once per Lloyd round)
@@ -341,7 +425,7 @@ def main():
     share = {"k_gather_attend": T * L * att_ms / ms_step,
              "k_assign_mfma": cfg.iters * L * asg_ms / ms_step}
 
-    traffic = profiled_traffic(cfg.name)
+    traffic = profiled_traffic(cfg.name) if not variant else None
     keys_per_step = L * B * H * N
     res = {
         "metric": "prefill keys clustered/s; decode select+gather+attend us/layer-step, %HBM peak",
@@ -359,15 +443,18 @@ def main():
         "config": {"workload": cfg.name, "layers": L, "batch": B, "n_kv_heads": H,
                    "n_q_heads": Hq, "head_dim": d, "n_keys": N, "n_clusters": C,
                    "iters": cfg.iters, "decode_steps": T, "budget": cfg.budget,
-                   "local_buffer": cfg.buf_cap, "tau": cfg.tau},
+                   "local_buffer": cfg.buf_cap, "tau": cfg.tau, "pool": args.pool,
+                   "policy": args.policy, "units": args.units},
+        "retrieval_steps": int(fl.sum()),
         "prefill_ms": pre_ms,
         "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),
         "decode_us_per_layer_step": dec_us,
         "decode_bytes_per_layer_step": dec_bytes,
         "decode_hbm_frac": dec_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
-        "roofline": {"bound": "hbm", "kernel": "k_gather_attend_mfma (kv_gather_attend)",
-                     "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": att_gbs / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm" if args.pool != "host-direct" else "host-link",
+                     "kernel": "k_gather_attend_mfma (kv_gather_attend)",
+                     "achieved": att_gbs, "peak": att_peak, "unit": "GB/s",
+                     "frac": att_gbs / att_peak,
                      "traffic": traffic["k_gather_attend_mfma"]["bytes"] if traffic else None,
                      "bytes_per_launch": att_bytes, "avg_launch_ms": att_ms},
         "roofline_assign": {"bound": "mfma", "kernel": "k_assign_mfma (kv_kmeans_assign_prepared)",
@@ -377,6 +464,8 @@ def main():
                             "flops_per_launch": flops, "avg_launch_ms": asg_ms},
         "time_share_per_step": share,
     }
+    if fetch_res is not None:
+        res["fetch"] = fetch_res
     # A plain copy of known size after the timed region: the reference that
     # scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes.
     if args.copy_calibration_mib > 0:
@@ -386,7 +475,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline:
+    if variant:
+        res["cpu_baseline"] = None  # the oracle's sample covers the standard path only
+    elif not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, args.cpu_lloyd_iters, dk0, dv0)
     else:

@@ -57,7 +57,10 @@ typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
 /*
  * The unified KV pool of one layer ("Key designs" item 2 of the LouisKV note:
  * prefill clusters and decode segments share one pool and one scoring
- * mechanism). Here the pool lives in HBM. Rows of each (sequence, KV head)
+ * mechanism). The pool's tables live in HBM; its K and V rows live in HBM
+ * or, as in the note's deployment (the full KV cache kept in CPU memory,
+ * "Background"), in pinned host memory mapped into the device's address
+ * space (see kv_host_device_pointer). Rows of each (sequence, KV head)
  * are stored cluster by cluster (CSR) after kv_cluster_build, then decode
  * rows are appended in time order. Units are contiguous row ranges:
  * clusters have ids 0..C-1, segments C, C+1, ... in closing order.
@@ -65,7 +68,9 @@ typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
  * cluster count and segment boundaries).
  *
  * The struct itself is [host] memory; every pointer in it is device memory
- * owned by the caller.
+ * owned by the caller (k and v: device memory, or the device address of
+ * mapped host memory). Every kernel reads and writes k and v in place
+ * wherever they live; with host memory each access crosses the host link.
  */
 typedef struct kv_pool {
   int32_t batch;      /* sequences */
@@ -268,14 +273,51 @@ kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void
  * be NULL). Row indices are clamped into [0, row_cap).
  * q: [batch][n_q_heads][head_dim] (dtype). out: [batch][n_q_heads][head_dim]
  * fp32. max_rows: expected upper bound on selected pool rows per (b, g) (the
- * budget); it sizes the launch and the workspace, results do not depend on
- * it. sel_cap <= 4096.
+ * budget); it sizes the launch and the workspace and, through the split of
+ * the rows over workgroups, the order of the fp32 sums (for equal max_rows,
+ * equal rows in equal order give bitwise equal outputs). sel_cap <= 4096.
  */
 size_t kv_gather_attend_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t max_rows);
 kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
                            const int32_t *sel_units, const int32_t *sel_spans, int32_t sel_cap,
                            const int32_t *sel_n, int32_t max_rows, float *out, void *ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The GPU-side working set of a pool kept in host memory. LouisKV note,
+ * flowchart: on a boundary the top units are fetched from the CPU pool to
+ * the GPU, and the steps inside the segment reuse them; "Key designs" item 3:
+ * the chosen rows of the CPU tensor are copied straight to the GPU, without
+ * first gathering them on the CPU. Here the copy is a gather kernel that
+ * reads the selected rows where the pool keeps them (mapped host memory, or
+ * HBM) and writes them into `dst`, a second pool in HBM that holds one span
+ * per (b, g).
+ *
+ * For every sequence b with flag[b] != 0 and every KV head g: the rows of
+ * the selection (sel_units / sel_spans / sel_n exactly as kv_gather_attend
+ * reads them) are written in selection order to dst->k / dst->v rows
+ * [0, R) of (b, g), R = min(selected rows, dst->row_cap), and
+ * dst_spans[b][g] = {0, R}, dst_n[b][g] = (R > 0). Sequences with flag 0 are
+ * left untouched, so their previous working set is reused.
+ * kv_gather_attend(dst, q, ..., sel_spans = dst_spans, sel_cap = 1,
+ * sel_n = dst_n, max_rows) then attends over the same rows in the same order
+ * as kv_gather_attend(pool, q, ..., the selection, max_rows), with bitwise
+ * equal output. More selected rows than dst->row_cap sets *pool->status to
+ * KV_ERR_CAPACITY and keeps the first dst->row_cap rows.
+ * dst: same batch, n_kv_heads, head_dim and dtype as pool, buf_cap 0, its
+ * own k and v (only k, v and row_cap are used). dst_spans: [BH][2] int32;
+ * dst_n: [BH] int32. Pools with a local buffer (buf_cap > 0) get
+ * KV_ERR_UNSUPPORTED: the buffer rows are not part of a selection.
+ * sel_cap <= 4096. No workspace. */
+kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int32_t *sel_units,
+                            const int32_t *sel_spans, int32_t sel_cap, const int32_t *sel_n,
+                            const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
+                            hipStream_t stream);
+
+/* Device address of pinned host memory (hipHostMalloc, mapped), to place a
+ * pool's k and v in host memory. *dev receives the address the kernels use.
+ * KV_ERR_INVALID_ARG if `host` is not such memory. host, dev: [host]. */
+kv_status kv_host_device_pointer(void *host, void **dev);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,7 @@ EXPORTED = [
     "kv_segment_append", "kv_boundary_segment_append",
     "kv_select_workspace", "kv_select", "kv_boundary_select",
     "kv_gather_attend_workspace", "kv_gather_attend",
+    "kv_fetch_selected", "kv_host_device_pointer",
 ]
 
 
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
         "kv_gather_attend_workspace": (c_size, [pool_p, c_int, c_int]),
         "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, c_int, vp, c_int,
                                      vp, vp, c_size, vp]),
+        "kv_fetch_selected": (c_int, [pool_p, vp, vp, vp, c_int, vp, pool_p, vp, vp, vp]),
+        "kv_host_device_pointer": (c_int, [vp, ctypes.POINTER(vp)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -161,9 +164,19 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def host_device_pointer(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor (hipHostMalloc memory)."""
+    dev = ctypes.c_void_p()
+    _check("kv_host_device_pointer",
+           lib().kv_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(dev)))
+    return int(dev.value)
+
+
 @dataclass
 class Pool:
-    """Device tensors behind one ``kv_pool`` (see kvc.h for the layout)."""
+    """Tensors behind one ``kv_pool`` (see kvc.h for the layout). With
+    ``host_kv`` the K and V rows live in pinned host memory, which the kernels
+    reach through its device address; every table stays on the GPU."""
 
     batch: int
     n_kv_heads: int
@@ -173,12 +186,17 @@ class Pool:
     unit_cap: int
     buf_cap: int = 0
     device: str = "cuda"
+    host_kv: bool = False
 
     def __post_init__(self):
         B, H, D = self.batch, self.n_kv_heads, self.head_dim
         dev, i32 = self.device, torch.int32
-        self.k = torch.zeros(B, H, self.row_cap, D, dtype=self.dtype, device=dev)
-        self.v = torch.zeros_like(self.k)
+        if self.host_kv:
+            self.k = torch.zeros(B, H, self.row_cap, D, dtype=self.dtype, pin_memory=True)
+            self.v = torch.zeros(B, H, self.row_cap, D, dtype=self.dtype, pin_memory=True)
+        else:
+            self.k = torch.zeros(B, H, self.row_cap, D, dtype=self.dtype, device=dev)
+            self.v = torch.zeros_like(self.k)
         self.unit_start = torch.zeros(B, H, self.unit_cap, dtype=i32, device=dev)
         self.unit_size = torch.zeros(B, H, self.unit_cap, dtype=i32, device=dev)
         self.unit_mean = torch.zeros(B, H, self.unit_cap, D, dtype=torch.float32, device=dev)
@@ -196,9 +214,10 @@ class Pool:
     def struct(self) -> KVPool:
         if self._struct is None:
             p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+            kv = p if not self.host_kv else host_device_pointer
             self._struct = KVPool(
                 self.batch, self.n_kv_heads, self.head_dim, dtype_code(self.dtype),
-                self.row_cap, self.unit_cap, p(self.k), p(self.v), p(self.unit_start),
+                self.row_cap, self.unit_cap, kv(self.k), kv(self.v), p(self.unit_start),
                 p(self.unit_size), p(self.unit_mean), p(self.unit_index), p(self.n_rows),
                 p(self.n_units), p(self.n_cand), self.buf_cap, p(self.buf_begin),
                 p(self.seg_begin), p(self.seg_sum), p(self.status))
@@ -327,3 +346,15 @@ def kv_gather_attend(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: in
     _check("kv_gather_attend", lib().kv_gather_attend(
         pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), _ptr(sel_spans), cap,
         _ptr(sel_n), int(max_rows), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- working set
+def kv_fetch_selected(pool: Pool, flag, sel_units, sel_n, dst: Pool, dst_spans, dst_n,
+                      sel_spans=None, stream=None) -> None:
+    """Selected rows of `pool` -> the HBM working set `dst` (sequences with flag 1).
+    dst_spans [B, H, 1, 2] int32 and dst_n [B, H] int32 then describe it to
+    kv_gather_attend(dst, ..., sel_spans=dst_spans, sel_n=dst_n)."""
+    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
+    _check("kv_fetch_selected", lib().kv_fetch_selected(
+        pool.ref(), _ptr(flag), _ptr(sel_units), _ptr(sel_spans), cap, _ptr(sel_n), dst.ref(),
+        _ptr(dst_spans), _ptr(dst_n), _stream(stream)))

@@ -308,4 +308,39 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
                               attend_num_splits(pool, max_rows), out, partials, counters, stream);
 }
 
+
+// ---------------------------------------------------------------- working set
+kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int32_t *sel_units,
+                            const int32_t *sel_spans, int32_t sel_cap, const int32_t *sel_n,
+                            const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
+                            hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  st = check_pool(dst);
+  if (st != KV_OK) return st;
+  if (!flag || (!sel_units && !sel_spans) || !sel_n || !dst_spans || !dst_n)
+    return KV_ERR_INVALID_ARG;
+  if (sel_cap <= 0) return KV_ERR_INVALID_ARG;
+  if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
+  if (dst->batch != pool->batch || dst->n_kv_heads != pool->n_kv_heads ||
+      dst->head_dim != pool->head_dim || dst->dtype != pool->dtype)
+    return KV_ERR_INVALID_ARG;
+  if (dst->k == pool->k || dst->v == pool->v) return KV_ERR_INVALID_ARG;
+  // the local buffer of a segment pool is not part of the selection
+  if (pool->buf_cap > 0 || dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;
+  return launch_fetch_rows(pool, flag, sel_units, sel_spans, sel_cap, sel_n, dst, dst_spans,
+                           dst_n, stream);
+}
+
+kv_status kv_host_device_pointer(void *host, void **dev) {
+  if (!host || !dev) return KV_ERR_INVALID_ARG;
+  void *d = nullptr;
+  if (hipHostGetDevicePointer(&d, host, 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return KV_ERR_INVALID_ARG;
+  }
+  *dev = d;
+  return KV_OK;
+}
+
 }  // extern "C"

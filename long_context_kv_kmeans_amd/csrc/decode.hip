@@ -1313,4 +1313,108 @@ kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float
   return st;
 }
 
+
+// ---------------------------------------------------------------- working-set fetch
+// Rows of the selected units -> a device-resident working set, stored one
+// after another in selection order, so that attention over the working set
+// sees the same rows in the same order as attention over the pool. One (b, g)
+// per blockIdx.y; blockIdx.x takes a range of RPB rows of the concatenated
+// selection, so that a workgroup moves exactly kFetchBlockBytes (its K and V
+// pieces) with every thread holding kFetchUnroll 16-byte reads in flight
+// before it stores. Sequences whose flag is 0 return at once and keep the
+// previous working set. The source pool may live in host memory mapped into
+// the device's address space: then every piece is a read over the host link,
+// and keeping many in flight is what sets the rate.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kFetchThreads = 256;
+constexpr int kFetchUnroll = 8;
+constexpr int kFetchBlockBytes = kFetchThreads * kFetchUnroll * 16;
+
+template <int RB>
+__global__ void __launch_bounds__(kFetchThreads)
+k_fetch_rows(kv_pool src, const uint8_t *__restrict__ flag, const int32_t *sel_units,
+             const int32_t *sel_spans, int sel_cap, const int32_t *__restrict__ sel_n,
+             kv_pool dst, int32_t *__restrict__ dst_spans, int32_t *__restrict__ dst_n) {
+  constexpr int NT = kFetchThreads;
+  constexpr int LPR = RB / 16;                        // 16-byte pieces per row
+  constexpr int RPB = kFetchBlockBytes / (2 * RB);    // rows per workgroup
+  static_assert(RPB * LPR * 2 == NT * kFetchUnroll, "one pass per workgroup");
+  __shared__ int s_psum[kMaxSel];
+  __shared__ int s_start[kMaxSel];
+  __shared__ int s_wsum[NT / 64];
+  __shared__ int s_row[RPB];
+  const int tid = threadIdx.x;
+  const int bg = blockIdx.y, b = bg / src.n_kv_heads;
+  if (flag[b] == 0) return;  // uniform over the workgroup
+  int n;
+  const int r_all = attend_load_selection<NT>(
+      src, bg, sel_units ? sel_units + (size_t)bg * sel_cap : nullptr,
+      sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr, sel_n, sel_cap, &n, s_psum,
+      s_start, s_wsum);
+  const int R = min(r_all, dst.row_cap);
+  if (blockIdx.x == 0 && tid == 0) {
+    dst_spans[2 * bg] = 0;
+    dst_spans[2 * bg + 1] = R;
+    dst_n[bg] = R > 0 ? 1 : 0;
+    if (r_all > dst.row_cap)
+      __hip_atomic_store(src.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int r_lo = blockIdx.x * RPB;
+  if (r_lo >= R) return;  // uniform
+  const int rows = min(RPB, R - r_lo);
+  for (int i = tid; i < rows; i += NT)
+    s_row[i] = attend_row_of(r_lo + i, n, r_all, 0, s_psum, s_start, src.row_cap);
+  __syncthreads();
+  const size_t src_head = (size_t)bg * src.row_cap * LPR;
+  const size_t dst_head = ((size_t)bg * dst.row_cap + r_lo) * LPR;
+  const u32x4_t *ks = static_cast<const u32x4_t *>(src.k) + src_head;
+  const u32x4_t *vs = static_cast<const u32x4_t *>(src.v) + src_head;
+  u32x4_t *kd = static_cast<u32x4_t *>(dst.k) + dst_head;
+  u32x4_t *vd = static_cast<u32x4_t *>(dst.v) + dst_head;
+  const int pieces = rows * LPR;  // of K, and as many of V
+  // piece p < pieces: K piece p; else V piece p - pieces. Pieces past the
+  // end re-read the block's first piece (in bounds) and are not stored.
+  u32x4_t buf[kFetchUnroll];
+#pragma unroll
+  for (int u = 0; u < kFetchUnroll; ++u) {
+    int p = tid + u * NT;
+    p = p < 2 * pieces ? p : 0;
+    const bool is_v = p >= pieces;
+    const int q = is_v ? p - pieces : p;
+    buf[u] = (is_v ? vs : ks)[(size_t)s_row[q / LPR] * LPR + q % LPR];
+  }
+#pragma unroll
+  for (int u = 0; u < kFetchUnroll; ++u) {
+    const int p = tid + u * NT;
+    u32x4_t *d = p < pieces ? kd + p : vd + (p - pieces);
+    if (p < 2 * pieces) *d = buf[u];
+  }
+}
+
+int fetch_num_blocks(const kv_pool *dst) {
+  const int rb = dst->head_dim * (dst->dtype == KV_BF16 ? 2 : 4);
+  const int rpb = kFetchBlockBytes / (2 * rb);
+  return (dst->row_cap + rpb - 1) / rpb;
+}
+
+kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32_t *sel_units,
+                            const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
+                            const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
+                            hipStream_t s) {
+  const dim3 grid(fetch_num_blocks(dst), src->batch * src->n_kv_heads);
+  const int rb = src->head_dim * (src->dtype == KV_BF16 ? 2 : 4);
+#define KVC_FETCH(RB)                                                                          \
+  k_fetch_rows<RB><<<grid, kFetchThreads, 0, s>>>(*src, flag, sel_units, sel_spans, sel_cap,  \
+                                                  sel_n, *dst, dst_spans, dst_n)
+  switch (rb) {
+    case 128: KVC_FETCH(128); break;
+    case 256: KVC_FETCH(256); break;
+    case 512: KVC_FETCH(512); break;
+    default: return KV_ERR_UNSUPPORTED;
+  }
+#undef KVC_FETCH
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
 }  // namespace kvc

@@ -213,5 +213,10 @@ kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float
                                const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
                                const int32_t *sel_n, int nsplit, float *out, float *partials,
                                int32_t *counters, hipStream_t s);
+int fetch_num_blocks(const kv_pool *dst);
+kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32_t *sel_units,
+                            const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
+                            const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
+                            hipStream_t s);
 
 }  // namespace kvc

@@ -70,15 +70,23 @@ def unit_rows(start, size, units) -> np.ndarray:
 
 def run_decode(packs, queries, tau: float, budget: int, scale: float, dtype: str,
                buf_cap: int = 0, dec_k=None, dec_v=None, steps: int | None = None,
-               keep_scores: bool = False):
+               keep_scores: bool = False, retrieve=None):
     """Decode loop for one (layer, sequence).
 
     packs: per KV head, ``oracle.kmeans.pack`` dicts (same cluster count).
     queries: [steps, Hq, d]; dec_k/dec_v: [steps, H, d] when buf_cap > 0.
+    retrieve: optional [steps] bools that replace the boundary test's decision
+    of when to retrieve (r is still computed and logged): all true is the
+    per-token retrieval of the methods the note's "Motivation" section
+    criticises, every S-th step the fixed-stride policy of its ablation
+    table. Only without decode segments (buf_cap == 0), where the decision
+    does nothing else.
     Returns a list of per-step dicts: flag, r, sel (per head, ascending unit
     ids; the reused set on non-boundary steps), out [Hq, d], n_rows,
     buf_begin, n_cand and, if ``keep_scores``, the scores of boundary steps.
     """
+    if retrieve is not None and buf_cap > 0:
+        raise ValueError("a retrieval schedule replaces the boundary test only without segments")
     H = len(packs)
     steps = queries.shape[0] if steps is None else steps
     Hq, d = queries.shape[1], queries.shape[2]
@@ -93,7 +101,7 @@ def run_decode(packs, queries, tau: float, budget: int, scale: float, dtype: str
     for t in range(steps):
         q_prev = None if t == 0 else queries[t - 1][None]
         flag, r = boundary(q_prev, queries[t][None], tau)
-        flag = bool(flag[0])
+        flag = bool(flag[0]) if retrieve is None else bool(retrieve[t])
         if seg is not None:
             seg.step(flag, dec_k[t], dec_v[t])
         scores = {}

@@ -25,9 +25,10 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def make_pool(batch, n_kv_heads, head_dim, dtype, n_keys, n_units, buf_cap=0, extra_rows=0):
+def make_pool(batch, n_kv_heads, head_dim, dtype, n_keys, n_units, buf_cap=0, extra_rows=0,
+              host_kv=False):
     return kvc.Pool(batch, n_kv_heads, head_dim, tdtype(dtype), row_cap=n_keys + extra_rows,
-                    unit_cap=n_units, buf_cap=buf_cap)
+                    unit_cap=n_units, buf_cap=buf_cap, host_kv=host_kv)
 
 
 def oracle_clustering(keys, init_idx, iters, dtype):
@@ -49,11 +50,12 @@ def oracle_packs(keys, values, labels, cents, dtype, b=0):
 
 
 def pool_from_labels(keys_np, values_np, labels, cents, dtype, n_units=None, buf_cap=0,
-                     extra_rows=0, init_idx=None):
-    """GPU pool packed from the oracle's clustering, with the oracle's index vectors."""
+                     extra_rows=0, init_idx=None, host_kv=False):
+    """GPU pool packed from the oracle's clustering, with the oracle's index vectors
+    (host_kv: K/V rows in pinned host memory, packed there by the GPU)."""
     B, H, N, d = keys_np.shape
     C = cents.shape[2]
-    pool = make_pool(B, H, d, dtype, N, n_units or C, buf_cap, extra_rows)
+    pool = make_pool(B, H, d, dtype, N, n_units or C, buf_cap, extra_rows, host_kv=host_kv)
     keys = to_dev(keys_np, dtype)
     vals = to_dev(values_np, dtype)
     if init_idx is None:
@@ -73,12 +75,26 @@ class DecodeRecord:
     pass
 
 
+def working_set(pool, max_rows):
+    """An HBM pool holding one span per (b, g): the target of kv_fetch_selected."""
+    B, H = pool.batch, pool.n_kv_heads
+    ws = kvc.Pool(B, H, pool.head_dim, pool.dtype, row_cap=max_rows, unit_cap=1)
+    ws.spans = torch.zeros(B, H, 1, 2, dtype=torch.int32, device="cuda")
+    ws.count = torch.zeros(B, H, dtype=torch.int32, device="cuda")
+    return ws
+
+
 def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, steps=None,
-               record_sel=True, fused=False, spans=False, fused_append=False):
+               record_sel=True, fused=False, spans=False, fused_append=False, fetch=False,
+               flags=None):
     """Run the decode loop through the C ABI. q: device [T, B, Hq, d].
     fused: boundary test and selection through kv_boundary_select (no segments).
     spans: selection also writes row spans and attention reads them.
-    fused_append: boundary test and segment append through kv_boundary_segment_append."""
+    fused_append: boundary test and segment append through kv_boundary_segment_append.
+    fetch: on retrieval steps kv_fetch_selected copies the selected rows into an
+    HBM working set, and attention reads the working set.
+    flags: device [T, B] uint8 retrieval decisions to use instead of the boundary
+    test's (kv_boundary still writes r; the selection follows the given flags)."""
     T = q.shape[0] if steps is None else steps
     B, Hq, d = q.shape[1:]
     H = pool.n_kv_heads
@@ -96,8 +112,15 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
     ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, budget))
     sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device=dev) if spans else None
+    wset = working_set(pool, budget) if fetch else None
     for t in range(T):
-        if fused:
+        if flags is not None:
+            assert not fused and dec_k is None
+            kvc.kv_boundary(q[t - 1] if t else None, q[t], tau, rec.flag[t], rec.r[t])
+            rec.flag[t].copy_(flags[t])
+            kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel,
+                          sel_spans=sel_spans)
+        elif fused:
             assert dec_k is None
             kvc.kv_boundary_select(pool, q[t - 1] if t else None, q[t], tau, budget, rec.flag[t],
                                    sel_units, sel_n, sel_rows, r=rec.r[t], ws=ws_sel,
@@ -112,8 +135,14 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
                     kvc.kv_segment_append(pool, dec_k[t], dec_v[t], rec.flag[t])
             kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel,
                           sel_spans=sel_spans)
-        kvc.kv_gather_attend(pool, q[t], scale, None if spans else sel_units, sel_n, budget,
-                             rec.out[t], ws=ws_att, sel_spans=sel_spans)
+        if fetch:
+            kvc.kv_fetch_selected(pool, rec.flag[t], None if spans else sel_units, sel_n, wset,
+                                  wset.spans, wset.count, sel_spans=sel_spans)
+            kvc.kv_gather_attend(wset, q[t], scale, None, wset.count, budget, rec.out[t],
+                                 ws=ws_att, sel_spans=wset.spans)
+        else:
+            kvc.kv_gather_attend(pool, q[t], scale, None if spans else sel_units, sel_n, budget,
+                                 rec.out[t], ws=ws_att, sel_spans=sel_spans)
         rec.sel_n[t].copy_(sel_n)
         if record_sel:
             rec.sel[t].copy_(sel_units)

@@ -189,6 +189,44 @@ def test_cluster_build_validation():
                               None) == kvc.KV_ERR_WORKSPACE
 
 
+def test_fetch_selected_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    src = _fake_pool()
+    dst = _fake_pool(row_cap=512, unit_cap=1)
+    dst.k, dst.v = 0x20000, 0x30000
+    S, D = ctypes.byref(src), ctypes.byref(dst)
+
+    def call(src_=S, dst_=D, flag=a, su=a, sp=None, cap=64, sn=a, ds=a, dn=a):
+        return L.kv_fetch_selected(src_, flag, su, sp, cap, sn, dst_, ds, dn, None)
+
+    for kw in ({"src_": None}, {"dst_": None}, {"flag": None}, {"su": None}, {"sn": None},
+               {"ds": None}, {"dn": None}, {"cap": 0}):
+        assert call(**kw) == kvc.KV_ERR_INVALID_ARG, kw
+    assert call(cap=4097) == kvc.KV_ERR_UNSUPPORTED
+    for field, val in (("batch", 2), ("n_kv_heads", 4), ("head_dim", 64), ("dtype", kvc.KV_F32)):
+        bad = _fake_pool(row_cap=512, unit_cap=1)
+        bad.k, bad.v = 0x20000, 0x30000
+        setattr(bad, field, val)
+        assert call(dst_=ctypes.byref(bad)) == kvc.KV_ERR_INVALID_ARG, field
+    same = _fake_pool(row_cap=512, unit_cap=1)  # k, v alias the source's
+    assert call(dst_=ctypes.byref(same)) == kvc.KV_ERR_INVALID_ARG
+    seg = _fake_pool(buf_cap=64, seg_sum=0x10000)
+    assert call(src_=ctypes.byref(seg)) == kvc.KV_ERR_UNSUPPORTED
+
+
+def test_host_device_pointer_rejects_unpinned_memory():
+    L = kvc.lib()
+    out = ctypes.c_void_p()
+    assert L.kv_host_device_pointer(None, ctypes.byref(out)) == kvc.KV_ERR_INVALID_ARG
+    buf = ctypes.create_string_buffer(4096)
+    assert L.kv_host_device_pointer(ctypes.cast(buf, ctypes.c_void_p), None) == \
+        kvc.KV_ERR_INVALID_ARG
+    # pageable memory (and, on a host without a GPU, any memory) has no device address
+    assert L.kv_host_device_pointer(ctypes.cast(buf, ctypes.c_void_p),
+                                    ctypes.byref(out)) == kvc.KV_ERR_INVALID_ARG
+
+
 def test_workspace_sizes_scale():
     L = kvc.lib()
     small = L.kv_cluster_build_workspace(1, 8, 32768, 128, 2048, kvc.KV_BF16)

@@ -38,23 +38,49 @@ def _fixed_clustering(keys, C):
     return labels, cents
 
 
-def _run(cfg, steps, seqs, compare_every=1, check=None, **decode_kw):
+def _page_units(keys, page):
+    """Page-granularity units: key i in unit i // page, indexed by the page's key mean."""
+    B, H, N, d = keys.shape
+    labels = wl.page_labels(B, H, N, page).astype(np.int64)
+    C = -(-N // page)
+    cents = np.empty((B, H, C, d))
+    for b in range(B):
+        for g in range(H):
+            cents[b, g], _ = okm.update(keys[b, g], labels[b, g], np.zeros((C, d)))
+    return labels, cents
+
+
+def _run(cfg, steps, seqs, compare_every=1, check=None, policy="boundary", page=None,
+         pool_kw=None, **decode_kw):
     """check: positions in `seqs` compared with the oracle (default all); the other
-    sequences get _fixed_clustering and only fill the launch."""
+    sequences get _fixed_clustering and only fill the launch. policy: when to
+    retrieve ("boundary", "per-token", "stride:S"); page: page-granularity units of
+    that many keys instead of K-means clusters; pool_kw: extra pool_from_labels
+    arguments (host_kv)."""
     inp = wl.layer_inputs(cfg, 0, seqs=seqs)
     B, H, N, d = inp["keys"].shape
     check = list(range(B)) if check is None else list(check)
-    labels, cents = _fixed_clustering(inp["keys"], cfg.n_clusters)
-    lc, cc = oracle_clustering(inp["keys"][check], inp["init_idx"][check], cfg.iters, cfg.dtype)
-    labels[check], cents[check] = lc, cc
+    if page is not None:
+        labels, cents = _page_units(inp["keys"], page)
+        cfg = cfg.replace(n_clusters=cents.shape[2])
+    else:
+        labels, cents = _fixed_clustering(inp["keys"], cfg.n_clusters)
+        lc, cc = oracle_clustering(inp["keys"][check], inp["init_idx"][check], cfg.iters,
+                                   cfg.dtype)
+        labels[check], cents[check] = lc, cc
     q, _ = wl.layer_queries(cfg, 0, steps=steps, seqs=seqs)
+    sched = wl.retrieval_schedule(policy, steps)
+    if sched is not None:
+        decode_kw["flags"] = torch.from_numpy(
+            np.repeat(sched[:, None], B, axis=1).astype(np.uint8)).cuda()
     dk = dv = None
     extra_rows, n_units = 0, cfg.n_clusters
     if cfg.buf_cap > 0:
         dk, dv = wl.layer_decode_kv(cfg, 0, steps=steps, seqs=seqs)
         extra_rows, n_units = steps, cfg.n_clusters + steps
     pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
-                                  n_units=n_units, buf_cap=cfg.buf_cap, extra_rows=extra_rows)
+                                  n_units=n_units, buf_cap=cfg.buf_cap, extra_rows=extra_rows,
+                                  **(pool_kw or {}))
     sel_cap = min(cfg.budget, n_units)
     rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, cfg.budget, cfg.scale, sel_cap,
                      dec_k=None if dk is None else to_dev(dk, cfg.dtype),
@@ -71,7 +97,7 @@ def _run(cfg, steps, seqs, compare_every=1, check=None, **decode_kw):
         log, opool = run_decode(packs, q[:, bi], cfg.tau, cfg.budget, cfg.scale, cfg.dtype,
                                 buf_cap=cfg.buf_cap,
                                 dec_k=None if dk is None else dk[:, bi],
-                                dec_v=None if dv is None else dv[:, bi])
+                                dec_v=None if dv is None else dv[:, bi], retrieve=sched)
         for t, e in enumerate(log):
             assert flags[t, bi] == e["flag"], (t, bi)
             if cfg.buf_cap > 0:

@@ -1,0 +1,188 @@
+"""GPU: the pool's K/V rows in pinned host memory, the HBM working set that
+kv_fetch_selected fills, and the comparison retrieval policies and units.
+
+LouisKV note: "Background" (the full KV cache is kept in CPU memory), the
+flowchart (at a boundary the top units are fetched from the CPU pool to the
+GPU and reused inside the segment), "Key designs" item 3 (the chosen rows of
+the CPU tensor go straight to the GPU), the ablation table (fixed-stride
+retrieval, page-granularity units) and "Motivation" (per-token retrieval).
+  * the fetch copies exactly the selected rows, in selection order, bit for
+    bit, from HBM or host memory; sequences without a retrieval keep their
+    working set; overflow of the working set is reported;
+  * a host pool is packed bit-identically to an HBM pool, and decode loops
+    over it (attention straight from host memory, or from the working set)
+    give the HBM pool's flags, selections and outputs bit for bit;
+  * the per-token, fixed-stride and page-unit variants match the oracle's
+    decode loop with the same schedule and units.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_kv_kmeans_amd as kvc
+import workloads as wl
+from tests.gpu_util import gpu_decode, make_pool, oracle_clustering, pool_from_labels, to_dev, \
+    working_set
+from tests.test_gpu_decode import _run
+
+pytestmark = pytest.mark.gpu
+
+
+def test_pinned_host_tensor_has_a_device_address():
+    t = torch.zeros(4096, dtype=torch.bfloat16, pin_memory=True)
+    addr = kvc.host_device_pointer(t)
+    print(f"host {t.data_ptr():#x} device {addr:#x}")
+    assert addr != 0
+
+
+def _ragged_pool(B, H, d, dtype, row_cap, unit_cap, host_kv, seed):
+    """A pool with random K/V and a random ragged CSR unit table (sizes 0..40)."""
+    g = np.random.default_rng(seed)
+    pool = make_pool(B, H, d, dtype, row_cap, unit_cap, host_kv=host_kv)
+    tdt = pool.dtype
+    pool.k.copy_(torch.from_numpy(g.standard_normal(pool.k.shape, np.float32)).to(tdt))
+    pool.v.copy_(torch.from_numpy(g.standard_normal(pool.v.shape, np.float32)).to(tdt))
+    start = np.zeros((B, H, unit_cap), np.int32)
+    size = np.zeros((B, H, unit_cap), np.int32)
+    for b in range(B):
+        for h in range(H):
+            sz = g.integers(0, 41, unit_cap)
+            sz[g.random(unit_cap) < 0.1] = 0
+            st = np.concatenate([[0], np.cumsum(sz)[:-1]])
+            keep = st + sz <= row_cap
+            sz[~keep], st[~keep] = 0, 0
+            start[b, h], size[b, h] = st, sz
+    pool.unit_start.copy_(torch.from_numpy(start))
+    pool.unit_size.copy_(torch.from_numpy(size))
+    return pool, start, size
+
+
+@pytest.mark.parametrize("dtype,d,host_kv", [("bf16", 128, False), ("bf16", 128, True),
+                                             ("bf16", 64, False), ("fp32", 128, False),
+                                             ("fp32", 64, True)])
+def test_fetch_selected_copies_the_selection(dtype, d, host_kv):
+    B, H, row_cap, unit_cap, sel_cap = 3, 2, 3000, 150, 96
+    pool, start, size = _ragged_pool(B, H, d, dtype, row_cap, unit_cap, host_kv, seed=7 + d)
+    g = np.random.default_rng(11)
+    sel = np.full((B, H, sel_cap), -1, np.int32)
+    sel_n = np.zeros((B, H), np.int32)
+    for b in range(B):
+        for h in range(H):
+            n = int(g.integers(0, sel_cap + 1))
+            sel[b, h, :n] = g.permutation(unit_cap)[:n]
+            if n > 3:
+                sel[b, h, 1] = unit_cap + 5  # a foreign id counts as an empty unit
+            sel_n[b, h] = n
+    sel[2, 1] = g.permutation(unit_cap)[:sel_cap]  # enough rows to overflow below
+    sel_n[2, 1] = sel_cap
+    sel_n[0, 0] = sel_cap + 10  # clamped to sel_cap
+    spans = np.zeros((B, H, sel_cap, 2), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for j, u in enumerate(sel[b, h]):
+                if 0 <= u < unit_cap:
+                    spans[b, h, j] = (start[b, h, u], size[b, h, u])
+    flag = torch.tensor([1, 0, 1], dtype=torch.uint8, device="cuda")
+    su = torch.from_numpy(sel).cuda()
+    sn = torch.from_numpy(sel_n).cuda()
+    sp = torch.from_numpy(spans).cuda()
+    k_np = pool.k.float().cpu().numpy()
+    v_np = pool.v.float().cpu().numpy()
+    for by_spans in (False, True):
+        ws = working_set(pool, 4096)
+        ws.k.fill_(7.0)
+        ws.v.fill_(7.0)
+        ws.spans.fill_(-5)
+        ws.count.fill_(-5)
+        kvc.kv_fetch_selected(pool, flag, None if by_spans else su, sn, ws, ws.spans, ws.count,
+                              sel_spans=sp if by_spans else None)
+        torch.cuda.synchronize()
+        assert int(pool.status.item()) == 0
+        wk, wv = ws.k.float().cpu().numpy(), ws.v.float().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                if not flag[b]:
+                    assert (wk[b, h] == 7.0).all() and (wv[b, h] == 7.0).all()
+                    assert ws.spans[b, h].tolist() == [[-5, -5]] and ws.count[b, h] == -5
+                    continue
+                n = min(int(sel_n[b, h]), sel_cap)
+                rows = [np.arange(start[b, h, u], start[b, h, u] + size[b, h, u])
+                        for u in sel[b, h, :n] if 0 <= u < unit_cap]
+                rows = np.concatenate(rows) if rows else np.zeros(0, np.int64)
+                R = rows.size
+                assert ws.spans[b, h].tolist() == [[0, R]], (by_spans, b, h)
+                assert int(ws.count[b, h]) == (1 if R else 0)
+                np.testing.assert_array_equal(wk[b, h, :R], k_np[b, h, rows])
+                np.testing.assert_array_equal(wv[b, h, :R], v_np[b, h, rows])
+                assert (wk[b, h, R:] == 7.0).all()
+    # working set too small: status word, first row_cap rows kept
+    small = working_set(pool, 64)
+    flag.fill_(1)
+    kvc.kv_fetch_selected(pool, flag, su, sn, small, small.spans, small.count)
+    torch.cuda.synchronize()
+    assert int(pool.status.item()) == kvc.KV_ERR_CAPACITY
+    rows0 = np.concatenate([np.arange(start[2, 1, u], start[2, 1, u] + size[2, 1, u])
+                            for u in sel[2, 1, :sel_n[2, 1]] if 0 <= u < unit_cap])
+    assert rows0.size > 64
+    assert small.spans[2, 1].tolist() == [[0, 64]]
+    np.testing.assert_array_equal(small.k.float().cpu().numpy()[2, 1], k_np[2, 1, rows0[:64]])
+
+
+@pytest.mark.parametrize("cfg_idx,over,steps,seqs", [
+    (1, dict(n_keys=8192, n_clusters=512, n_components=128, iters=3), 96, [0]),
+    (4, dict(n_keys=4096, n_clusters=256, n_components=64, iters=3), 48, [0, 5, 7]),
+    (0, {}, 64, [0]),
+])
+def test_host_pool_decode_matches_hbm_pool(cfg_idx, over, steps, seqs):
+    cfg = wl.get_config(cfg_idx, **over)
+    inp = wl.layer_inputs(cfg, 0, seqs=seqs)
+    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    q, _ = wl.layer_queries(cfg, 0, steps=steps, seqs=seqs)
+    qd = to_dev(q, cfg.dtype)
+    pools = [pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                              n_units=cfg.n_clusters, host_kv=h)[0] for h in (False, True)]
+    hbm, host = pools
+    assert not host.k.is_cuda
+    # kv_cluster_build packed the rows into host memory exactly as into HBM
+    assert torch.equal(hbm.k.cpu(), host.k) and torch.equal(hbm.v.cpu(), host.v)
+    for name in ("unit_start", "unit_size", "n_rows", "n_units"):
+        assert torch.equal(getattr(hbm, name), getattr(host, name)), name
+    sel_cap = min(cfg.budget, cfg.n_clusters)
+    base = gpu_decode(hbm, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap, fused=True, spans=True)
+    assert int(base.flag.sum()) >= 2
+    runs = {
+        "host, direct": gpu_decode(host, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                                   fused=True, spans=True),
+        "host, working set": gpu_decode(host, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                                        fused=True, spans=True, fetch=True),
+        "host, working set by ids": gpu_decode(host, qd, cfg.tau, cfg.budget, cfg.scale,
+                                               sel_cap, fetch=True),
+        "hbm, working set": gpu_decode(hbm, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                                       fused=True, spans=True, fetch=True),
+    }
+    for label, rec in runs.items():
+        for name in ("flag", "sel_n", "sel"):
+            assert torch.equal(getattr(base, name), getattr(rec, name)), (label, name)
+        np.testing.assert_array_equal(base.out.cpu().numpy().view(np.uint32),
+                                      rec.out.cpu().numpy().view(np.uint32), err_msg=label)
+    assert int(host.status.item()) == 0 and int(hbm.status.item()) == 0
+
+
+def test_host_pool_working_set_decode_parity_cfg1_full_size():
+    # the Qwen3-8B-shaped layer at full size with its K/V in host memory: fetch on
+    # retrieval steps, attention over the working set, checked against the oracle
+    cfg = wl.get_config(1, iters=2)
+    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True, fetch=True,
+              pool_kw=dict(host_kv=True))
+    assert st["retrievals"] >= 2
+
+
+@pytest.mark.parametrize("policy,page", [("per-token", None), ("stride:8", None),
+                                         ("per-token", 16), ("boundary", 16)])
+def test_retrieval_policies_and_page_units_match_oracle(policy, page):
+    cfg = wl.get_config(1, n_keys=8192, n_clusters=512, n_components=128, iters=3)
+    st = _run(cfg, 64, [0], policy=policy, page=page, fetch=True, spans=True,
+              pool_kw=dict(host_kv=True))
+    sched = wl.retrieval_schedule(policy, 64)
+    if sched is not None:
+        assert st["retrievals"] == int(sched.sum())

@@ -113,3 +113,81 @@ def test_decode_reuses_selection_between_boundaries():
     for e in log:
         for g in range(2):
             assert packs[g]["unit_size"][e["sel"][g]].sum() <= 20
+
+
+def _walk(seed, T=30):
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((4, 8))
+    q = []
+    for t in range(T):
+        if t and rng.random() < 0.15:
+            base = rng.standard_normal((4, 8))
+        base = base + 0.05 * rng.standard_normal((4, 8))
+        q.append(base.copy())
+    return np.stack(q)
+
+
+def test_retrieval_schedule_replaces_only_the_decision():
+    packs = _tiny_pool(16)
+    q = _walk(17)
+    ref, _ = run_decode(packs, q, 0.7, budget=20, scale=0.3, dtype="fp32")
+    flags = np.array([e["flag"] for e in ref])
+    assert flags.sum() >= 2 and not flags.all()
+    # the boundary test's own decisions as a schedule: the same loop
+    same, _ = run_decode(packs, q, 0.7, budget=20, scale=0.3, dtype="fp32", retrieve=flags)
+    for a, b in zip(ref, same):
+        assert a["flag"] == b["flag"]
+        np.testing.assert_array_equal(a["r"], b["r"])  # NaN at the first step on both
+        assert all(np.array_equal(x, y) for x, y in zip(a["sel"], b["sel"]))
+        np.testing.assert_array_equal(a["out"], b["out"])
+    with pytest.raises(ValueError):
+        run_decode(packs, q, 0.7, budget=20, scale=0.3, dtype="fp32", buf_cap=4,
+                   dec_k=np.zeros((30, 2, 8)), dec_v=np.zeros((30, 2, 8)), retrieve=flags)
+
+
+def test_per_token_and_fixed_stride_retrieval():
+    # per-token: every step selects from its own query alone (a one-step loop,
+    # whose first step always retrieves, gives the same set); fixed stride S:
+    # steps between multiples of S reuse the set of the last multiple
+    packs = _tiny_pool(18)
+    q = _walk(19)
+    T = q.shape[0]
+    fresh = [run_decode(packs, q[t:t + 1], 0.7, budget=20, scale=0.3, dtype="fp32")[0][0]
+             for t in range(T)]
+    per_tok, _ = run_decode(packs, q, 0.7, budget=20, scale=0.3, dtype="fp32",
+                            retrieve=np.ones(T, bool))
+    boundary, _ = run_decode(packs, q, 0.7, budget=20, scale=0.3, dtype="fp32")
+    differs = False
+    for t in range(T):
+        assert per_tok[t]["flag"]
+        for g in range(2):
+            assert per_tok[t]["sel"][g].tolist() == fresh[t]["sel"][g].tolist()
+            differs |= per_tok[t]["sel"][g].tolist() != boundary[t]["sel"][g].tolist()
+        np.testing.assert_array_equal(per_tok[t]["out"], fresh[t]["out"])
+    assert differs  # reusing sets between boundaries is not per-token retrieval here
+    S = 4
+    stride, _ = run_decode(packs, q, 0.7, budget=20, scale=0.3, dtype="fp32",
+                           retrieve=np.arange(T) % S == 0)
+    for t in range(T):
+        assert stride[t]["flag"] == (t % S == 0)
+        src = fresh[t - t % S]
+        for g in range(2):
+            assert stride[t]["sel"][g].tolist() == src["sel"][g].tolist()
+
+
+def test_page_units_keep_time_order():
+    # pages of P consecutive keys: the CSR pack is the identity permutation,
+    # unit u spans rows [u P, min((u + 1) P, N)), indexed by the page's key mean
+    rng = np.random.default_rng(20)
+    N, d, P = 50, 8, 8
+    x = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    labels = np.arange(N) // P
+    C = -(-N // P)
+    cents, counts = kmeans.update(x, labels, np.zeros((C, d)))
+    pk = kmeans.pack(x, v, labels, cents, "fp32")
+    np.testing.assert_array_equal(pk["k"], x)
+    np.testing.assert_array_equal(pk["v"], v)
+    assert pk["unit_start"].tolist() == list(range(0, N, P))
+    assert pk["unit_size"].tolist() == [P] * (C - 1) + [N - P * (C - 1)]
+    np.testing.assert_allclose(cents[-1], x[P * (C - 1):].mean(0), rtol=1e-15, atol=0)

@@ -1,5 +1,6 @@
 """The seeded input generators: shapes, determinism and dtype exactness."""
 import numpy as np
+import pytest
 
 import workloads as wl
 
@@ -37,3 +38,16 @@ def test_decode_kv_shapes():
     cfg = wl.get_config(2, steps=20)
     k, v = wl.layer_decode_kv(cfg)
     assert k.shape == (20, 1, 8, 128) and v.shape == (20, 1, 8, 128)
+
+
+def test_retrieval_schedules_and_page_labels():
+    assert wl.retrieval_schedule("boundary", 5) is None
+    assert wl.retrieval_schedule("per-token", 3).tolist() == [True] * 3
+    assert wl.retrieval_schedule("stride:3", 7).tolist() == [True, False, False, True, False,
+                                                             False, True]
+    for bad in ("stride:0", "every-step"):
+        with pytest.raises(ValueError):
+            wl.retrieval_schedule(bad, 4)
+    lab = wl.page_labels(2, 3, 10, 4)
+    assert lab.shape == (2, 3, 10) and lab.dtype == np.int32
+    assert lab[1, 2].tolist() == [0, 0, 0, 0, 1, 1, 1, 1, 2, 2]

@@ -241,3 +241,30 @@ def layer_decode_kv(cfg: Config, layer: int = 0, steps: Optional[int] = None, se
         ks.append(np.stack(kh, axis=1))
         vs.append(np.stack(vh, axis=1))
     return np.stack(ks, axis=1), np.stack(vs, axis=1)
+
+
+def retrieval_schedule(policy: str, steps: int) -> Optional[np.ndarray]:
+    """When to retrieve, for the comparison policies: None for "boundary" (the
+    boundary test decides), all steps for "per-token" (retrieval at every
+    decoded token, as the methods the LouisKV note's "Motivation" section
+    discusses do), every S-th step from step 0 for "stride:S" (the
+    fixed-stride policy of the note's ablation table). Returns [steps] bool."""
+    if policy == "boundary":
+        return None
+    if policy == "per-token":
+        return np.ones(steps, dtype=bool)
+    if policy.startswith("stride:"):
+        s = int(policy.split(":", 1)[1])
+        if s < 1:
+            raise ValueError(f"stride must be >= 1 (got {s})")
+        return np.arange(steps) % s == 0
+    raise ValueError(f"unknown retrieval policy {policy!r}")
+
+
+def page_labels(batch: int, n_kv_heads: int, n_keys: int, page: int) -> np.ndarray:
+    """Page-granularity units (the note's ablation of fine-grained units against
+    pages): key i of every head belongs to unit i // page. [B, H, N] int32."""
+    if page < 1:
+        raise ValueError(f"page size must be >= 1 (got {page})")
+    return np.broadcast_to((np.arange(n_keys) // page).astype(np.int32),
+                           (batch, n_kv_heads, n_keys)).copy()
