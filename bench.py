@@ -35,12 +35,15 @@ same work.
 
 Variants (single-layer workloads without segments; the printed line names
 them in ``config``): ``--pool host`` keeps the pool's K/V rows in pinned
-host memory, as the LouisKV note deploys it, and each retrieval step fetches
-the selected rows into an HBM working set (kv_fetch_selected) that attention
-reads -- the line then carries ``fetch`` (the gather's GB/s against the host
-link); ``--pool host-direct`` lets attention read host memory every step;
+host memory, as the LouisKV note deploys it, and each retrieval step copies
+the selected rows into an HBM working set that attention reads
+(kv_fetch_attend: the copy fused into the attention launch) -- the line then
+carries ``fetch`` (the stand-alone gather kernel's and the fused retrieval
+step's GB/s against the host link); ``--pool host-direct`` lets attention read host memory every step;
 ``--policy per-token|stride:S`` replaces the boundary test's decision of when
-to retrieve; ``--units page:P`` uses pages of P consecutive keys as units.
+to retrieve; ``--units page:P`` uses pages of P consecutive keys as units. ``--overlap``
+adds ``prefill_overlap``: layer 0's K-means on a second stream beside a
+stand-in prefill forward of the same tokens, and the overhead it adds.
 """
 from __future__ import annotations
 
@@ -127,6 +130,73 @@ def cpu_baseline(cfg, inp, q, lloyd_iters, dk=None, dv=None):
     }
 
 
+def prefill_overlap(kvc, y, n_clusters, iters, n_tokens, reps=5):
+    """K-means of one layer's keys (kv_cluster_build on a second stream) while a
+    stand-in prefill forward runs on the first: the dense GEMMs of one
+    Qwen3-8B layer (QKV and output projections, gated MLP) over the same
+    tokens, with random weights, through torch's GEMMs. The stand-in leaves
+    out the attention itself and the norms. Returns the median times of the
+    stand-in alone, the clustering alone, both launched together, and the
+    overhead of the pair over the stand-in alone."""
+    import numpy as np
+    import torch
+
+    hid, inter, qkv = 4096, 12288, (32 + 2 * 8) * 128
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def w(*shape):
+        return (torch.randn(*shape, generator=g, device="cuda") / shape[0] ** 0.5).bfloat16()
+
+    x = torch.randn(n_tokens, hid, generator=g, device="cuda").bfloat16()
+    w_qkv, w_o, w_gu, w_d = w(hid, qkv), w(hid, hid), w(hid, 2 * inter), w(inter, hid)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def standin():
+        with torch.cuda.stream(sa):
+            h = x @ w_qkv
+            o = h[:, :hid] @ w_o
+            gu = o @ w_gu
+            act = torch.nn.functional.silu(gu[:, :inter]) * gu[:, inter:]
+            return act @ w_d
+
+    def kmeans():
+        kvc.kv_cluster_build(y.pool, y.keys, y.vals, n_clusters, iters, y.init,
+                             assign_in=y.assign_in,
+                             assign_out=None if y.assign_in is not None else y.labels,
+                             ws=y.ws_build, stream=sb)
+
+    def timed(parts):
+        """Both streams start together behind a GPU sleep (so that the host has
+        enqueued everything first); the interval ends when both are done."""
+        cur = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        a.record(cur)
+        sa.wait_event(a)
+        sb.wait_event(a)
+        for f in parts:
+            f()
+        for s_ in (sa, sb):
+            e_ = torch.cuda.Event()
+            e_.record(s_)
+            cur.wait_event(e_)
+        b.record(cur)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    for f in (standin, kmeans):
+        timed([f])  # warm
+    t_a = float(np.median([timed([standin]) for _ in range(reps)]))
+    t_b = float(np.median([timed([kmeans]) for _ in range(reps)]))
+    t_ab = float(np.median([timed([standin, kmeans]) for _ in range(reps)]))
+    flops = 2.0 * n_tokens * hid * (qkv + hid + 2 * inter) + 2.0 * n_tokens * inter * hid
+    return {"standin": "Qwen3-8B layer GEMMs (QKV, O, gate/up, down) over "
+                       f"{n_tokens} tokens, bf16, torch matmul; no attention or norms",
+            "standin_ms": t_a, "standin_tflops": flops / (t_a * 1e-3) / 1e12,
+            "kmeans_ms": t_b, "both_ms": t_ab, "overhead_frac": t_ab / t_a - 1.0,
+            "serial_overhead_frac": t_b / t_a}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,10 +213,17 @@ def main():
                          "retrieval steps fetch the selected rows into an HBM working set "
                          "that attention reads); host-direct (attention reads host memory "
                          "every step)")
+    ap.add_argument("--fetch", choices=("fused", "separate"), default="fused",
+                    help="--pool host: the working-set copy inside the attention launch "
+                         "(kv_fetch_attend) or as a launch of its own (kv_fetch_selected, "
+                         "then kv_gather_attend)")
     ap.add_argument("--policy", default="boundary",
                     help="when to retrieve: boundary (the cosine test), per-token, stride:S")
     ap.add_argument("--units", default="cluster",
                     help="retrieval units: cluster (K-means) or page:P (P consecutive keys)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time layer 0's K-means on a second stream beside a stand-in "
+                         "prefill forward (GEMMs of one layer) and report the overhead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
@@ -266,7 +343,11 @@ def main():
             kvc.kv_boundary_select(y.pool, q_prev, y.q[t], cfg.tau, cfg.budget, y.flags[t],
                                    y.sel, y.sel_n, y.sel_rows, ws=y.ws_sel,
                                    sel_spans=y.sel_spans)
-        if fetch:
+        if fetch and args.fetch == "fused":  # working-set copy inside the attention
+            kvc.kv_fetch_attend(y.pool, y.q[t], cfg.scale, flag, None, y.sel_n, cfg.budget,
+                                y.wset, y.wspans, y.wn, y.out, ws=y.ws_att,
+                                sel_spans=y.sel_spans)
+        elif fetch:
             kvc.kv_fetch_selected(y.pool, flag, None, y.sel_n, y.wset, y.wspans, y.wn,
                                   sel_spans=y.sel_spans)
             kvc.kv_gather_attend(y.wset, y.q[t], cfg.scale, None, y.wn, cfg.budget, y.out,
@@ -304,7 +385,7 @@ def main():
 
     # capture the decode loop in graphs of at most ~4096 launches; replay per step
     stream = torch.cuda.Stream()
-    calls = (3 if seg or fetch else 2) * L
+    calls = (3 if seg or (fetch and args.fetch == "separate") else 2) * L
     chunk = max(1, min(T, 4096 // calls))
     with torch.cuda.stream(stream):
         prefill()
@@ -399,6 +480,12 @@ def main():
                                                        y0.wspans, y0.wn, sel_spans=sel_spans),
                          args.attend_reps)
         f_bytes = att_rows * 2 * d * e  # K and V rows read over the host link
+        # a retrieval step of the fused call: copy into the working set + attention
+        fa_ms = launch_ms(lambda: kvc.kv_fetch_attend(pool, y0.q[T - 1], cfg.scale, ones, None,
+                                                      sel_n, cfg.budget, y0.wset, y0.wspans,
+                                                      y0.wn, y0.out, ws=y0.ws_att,
+                                                      sel_spans=sel_spans),
+                          args.attend_reps)
         # a plain pinned-host -> HBM copy of 64 MiB: the link's practical rate here
         hsrc = torch.ones(16 << 20, dtype=torch.float32, pin_memory=True)
         hdst = torch.empty(16 << 20, dtype=torch.float32, device="cuda")
@@ -408,7 +495,9 @@ def main():
                      "achieved": f_bytes / (f_ms * 1e-3) / 1e9, "peak": HOST_LINK_GBS,
                      "unit": "GB/s", "frac": f_bytes / (f_ms * 1e-3) / 1e9 / HOST_LINK_GBS,
                      "bytes_per_launch": f_bytes, "avg_launch_ms": f_ms,
-                     "h2d_copy_gbs": (64 << 20) / (h2d_ms * 1e-3) / 1e9}
+                     "h2d_copy_gbs": (64 << 20) / (h2d_ms * 1e-3) / 1e9,
+                     "fetch_attend_retrieval_ms": fa_ms,
+                     "fetch_attend_gbs": f_bytes / (fa_ms * 1e-3) / 1e9}
 
     # MFMA K-means assignment against prepared centroids (the kernel the
     # prefill runs once per Lloyd round)
@@ -444,6 +533,7 @@ def main():
                    "n_q_heads": Hq, "head_dim": d, "n_keys": N, "n_clusters": C,
                    "iters": cfg.iters, "decode_steps": T, "budget": cfg.budget,
                    "local_buffer": cfg.buf_cap, "tau": cfg.tau, "pool": args.pool,
+                   "fetch": args.fetch if fetch else None,
                    "policy": args.policy, "units": args.units},
         "retrieval_steps": int(fl.sum()),
         "prefill_ms": pre_ms,
@@ -466,6 +556,9 @@ def main():
     }
     if fetch_res is not None:
         res["fetch"] = fetch_res
+    if args.overlap:
+        log("timing K-means beside a stand-in prefill forward ...")
+        res["prefill_overlap"] = prefill_overlap(kvc, y0, C, cfg.iters, B * N)
     # A plain copy of known size after the timed region: the reference that
     # scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes.
     if args.copy_calibration_mib > 0:

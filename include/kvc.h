@@ -314,6 +314,25 @@ kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int3
                             const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
                             hipStream_t stream);
 
+/* kv_fetch_selected followed by kv_gather_attend over the working set, in
+ * one launch for bf16 pools: exactly
+ *   kv_fetch_selected(pool, flag, sel_units, sel_spans, sel_cap, sel_n,
+ *                     dst, dst_spans, dst_n);
+ *   kv_gather_attend(dst, q, n_q_heads, scale, NULL, dst_spans, 1, dst_n,
+ *                    max_rows, out, ws, ws_bytes);
+ * with the same working set, spans, status and output bit for bit. On a
+ * retrieval step (flag[b] != 0) each attention workgroup copies the rows it
+ * is about to attend from the pool into the working set and attends over
+ * them there; on other steps it reads the working set only, so a step
+ * without retrieval costs one launch. fp32 pools run the two launches.
+ * Arguments as for those two calls; workspace:
+ * kv_gather_attend_workspace(dst, n_q_heads, max_rows). */
+kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
+                          const uint8_t *flag, const int32_t *sel_units, const int32_t *sel_spans,
+                          int32_t sel_cap, const int32_t *sel_n, int32_t max_rows,
+                          const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n, float *out,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Device address of pinned host memory (hipHostMalloc, mapped), to place a
  * pool's k and v in host memory. *dev receives the address the kernels use.
  * KV_ERR_INVALID_ARG if `host` is not such memory. host, dev: [host]. */

@@ -39,7 +39,7 @@ EXPORTED = [
     "kv_segment_append", "kv_boundary_segment_append",
     "kv_select_workspace", "kv_select", "kv_boundary_select",
     "kv_gather_attend_workspace", "kv_gather_attend",
-    "kv_fetch_selected", "kv_host_device_pointer",
+    "kv_fetch_selected", "kv_fetch_attend", "kv_host_device_pointer",
 ]
 
 
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
         "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, c_int, vp, c_int,
                                      vp, vp, c_size, vp]),
         "kv_fetch_selected": (c_int, [pool_p, vp, vp, vp, c_int, vp, pool_p, vp, vp, vp]),
+        "kv_fetch_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, vp, c_int, vp,
+                                    c_int, pool_p, vp, vp, vp, vp, c_size, vp]),
         "kv_host_device_pointer": (c_int, [vp, ctypes.POINTER(vp)]),
     }
     for name, (res, args) in sig.items():
@@ -162,6 +164,16 @@ def torch_dtype(code: int) -> torch.dtype:
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """Zero-filled device workspace of at least ``nbytes`` (256-byte aligned)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _call_workspace(nbytes: int, stream=None) -> torch.Tensor:
+    """A workspace for one call enqueued on ``stream``: allocated and zero-filled
+    on that stream, so that the fill is ordered before the call's kernels and
+    the caching allocator reuses the memory only after them."""
+    if stream is None:
+        return workspace(nbytes)
+    with torch.cuda.stream(stream):
+        return workspace(nbytes)
 
 
 def host_device_pointer(t: torch.Tensor) -> int:
@@ -237,7 +249,7 @@ def kv_cluster_build(pool: Pool, keys, values, n_clusters: int, iters: int, init
                      assign_in=None, assign_out=None, ws=None, stream=None) -> None:
     B, H, N, D = keys.shape
     if ws is None:
-        ws = workspace(kv_cluster_build_workspace(B, H, N, D, n_clusters, keys.dtype))
+        ws = _call_workspace(kv_cluster_build_workspace(B, H, N, D, n_clusters, keys.dtype), stream)
     _check("kv_cluster_build", lib().kv_cluster_build(
         pool.ref(), _ptr(keys), _ptr(values), N, n_clusters, iters, _ptr(init_idx),
         _ptr(assign_in), _ptr(assign_out), _ptr(ws), ws.numel(), _stream(stream)))
@@ -249,7 +261,7 @@ def kv_kmeans_assign(keys, centroids, labels, ws=None, stream=None) -> None:
     C = centroids.shape[1]
     dt = dtype_code(keys.dtype)
     if ws is None:
-        ws = workspace(lib().kv_kmeans_assign_workspace(BH, C, D, dt))
+        ws = _call_workspace(lib().kv_kmeans_assign_workspace(BH, C, D, dt), stream)
     _check("kv_kmeans_assign", lib().kv_kmeans_assign(
         _ptr(keys), _ptr(centroids), BH, N, D, C, dt, _ptr(labels), _ptr(ws), ws.numel(),
         _stream(stream)))
@@ -276,7 +288,7 @@ def kv_kmeans_update(keys, labels, centroids_in, centroids_out, counts=None, ws=
     BH, N, D = keys.shape
     C = centroids_in.shape[1]
     if ws is None:
-        ws = workspace(lib().kv_kmeans_update_workspace(BH, N, C))
+        ws = _call_workspace(lib().kv_kmeans_update_workspace(BH, N, C), stream)
     _check("kv_kmeans_update", lib().kv_kmeans_update(
         _ptr(keys), _ptr(labels), _ptr(centroids_in), _ptr(centroids_out), _ptr(counts), BH, N,
         D, C, dtype_code(keys.dtype), _ptr(ws), ws.numel(), _stream(stream)))
@@ -312,7 +324,7 @@ def kv_select(pool: Pool, q, budget: int, flag, sel_units, sel_n, sel_rows, scor
     """sel_spans (optional) [B, H, sel_cap, 2] int32 receives the selected units' row spans."""
     Hq = q.shape[1]
     if ws is None:
-        ws = workspace(kv_select_workspace(pool, Hq))
+        ws = _call_workspace(kv_select_workspace(pool, Hq), stream)
     _check("kv_select", lib().kv_select(
         pool.ref(), _ptr(q), Hq, int(budget), _ptr(flag), _ptr(sel_units), sel_units.shape[-1],
         _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans), _ptr(scores_out), _ptr(ws), ws.numel(),
@@ -325,7 +337,7 @@ def kv_boundary_select(pool: Pool, q_prev, q_cur, tau: float, budget: int, flag,
     """kv_boundary then kv_select in one launch (q_prev None: first decode step)."""
     Hq = q_cur.shape[1]
     if ws is None:
-        ws = workspace(kv_select_workspace(pool, Hq))
+        ws = _call_workspace(kv_select_workspace(pool, Hq), stream)
     _check("kv_boundary_select", lib().kv_boundary_select(
         pool.ref(), _ptr(q_prev), _ptr(q_cur), Hq, float(tau), int(budget), _ptr(flag), _ptr(r),
         _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans),
@@ -341,7 +353,7 @@ def kv_gather_attend(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: in
     """sel_spans (optional, from kv_select) replaces the unit-table lookup of sel_units."""
     Hq = q.shape[1]
     if ws is None:
-        ws = workspace(kv_gather_attend_workspace(pool, Hq, max_rows))
+        ws = _call_workspace(kv_gather_attend_workspace(pool, Hq, max_rows), stream)
     cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
     _check("kv_gather_attend", lib().kv_gather_attend(
         pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), _ptr(sel_spans), cap,
@@ -358,3 +370,17 @@ def kv_fetch_selected(pool: Pool, flag, sel_units, sel_n, dst: Pool, dst_spans, 
     _check("kv_fetch_selected", lib().kv_fetch_selected(
         pool.ref(), _ptr(flag), _ptr(sel_units), _ptr(sel_spans), cap, _ptr(sel_n), dst.ref(),
         _ptr(dst_spans), _ptr(dst_n), _stream(stream)))
+
+
+def kv_fetch_attend(pool: Pool, q, scale: float, flag, sel_units, sel_n, max_rows: int,
+                    dst: Pool, dst_spans, dst_n, out, ws=None, stream=None,
+                    sel_spans=None) -> None:
+    """kv_fetch_selected + kv_gather_attend over the working set, in one launch."""
+    Hq = q.shape[1]
+    if ws is None:
+        ws = _call_workspace(kv_gather_attend_workspace(dst, Hq, max_rows), stream)
+    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
+    _check("kv_fetch_attend", lib().kv_fetch_attend(
+        pool.ref(), _ptr(q), Hq, float(scale), _ptr(flag), _ptr(sel_units), _ptr(sel_spans), cap,
+        _ptr(sel_n), int(max_rows), dst.ref(), _ptr(dst_spans), _ptr(dst_n), _ptr(out), _ptr(ws),
+        ws.numel(), _stream(stream)))

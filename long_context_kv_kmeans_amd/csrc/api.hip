@@ -332,6 +332,39 @@ kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int3
                            dst_n, stream);
 }
 
+kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
+                          const uint8_t *flag, const int32_t *sel_units, const int32_t *sel_spans,
+                          int32_t sel_cap, const int32_t *sel_n, int32_t max_rows,
+                          const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n, float *out,
+                          void *ws, size_t ws_bytes, hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  st = check_pool(dst);
+  if (st != KV_OK) return st;
+  if (!q || !flag || (!sel_units && !sel_spans) || !sel_n || !dst_spans || !dst_n || !out)
+    return KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || sel_cap <= 0 || max_rows < 0)
+    return KV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return KV_ERR_INVALID_ARG;
+  if (dst->batch != pool->batch || dst->n_kv_heads != pool->n_kv_heads ||
+      dst->head_dim != pool->head_dim || dst->dtype != pool->dtype)
+    return KV_ERR_INVALID_ARG;
+  if (dst->k == pool->k || dst->v == pool->v) return KV_ERR_INVALID_ARG;
+  if (pool->buf_cap > 0 || dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;
+  const int G = n_q_heads / pool->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
+  const size_t need = kv_gather_attend_workspace(dst, n_q_heads, max_rows);
+  if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  int32_t *counters = static_cast<int32_t *>(ws);
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                              align_up(bh * sizeof(int32_t), 256));
+  return launch_fetch_attend(pool, q, n_q_heads, scale, flag, sel_units, sel_spans, sel_cap,
+                             sel_n, attend_num_splits(dst, max_rows), dst, dst_spans, dst_n, out,
+                             partials, counters, stream);
+}
+
 kv_status kv_host_device_pointer(void *host, void **dev) {
   if (!host || !dev) return KV_ERR_INVALID_ARG;
   void *d = nullptr;

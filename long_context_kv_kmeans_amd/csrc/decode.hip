@@ -848,6 +848,7 @@ constexpr int kAttendChunk = 32;  // rows per wave step: two 16-row MFMA tiles
 constexpr int kAttendMfmaPiece = 1024;  // rows resolved per row-table pass
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8a_t __attribute__((ext_vector_type(8)));
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
@@ -905,6 +906,61 @@ __device__ __forceinline__ void attend_chunk_load(AttendChunk<D> &c, const int *
     const size_t row = li < plen ? (size_t)s_rowtab[li] : 0;
     c.vv[i] = *reinterpret_cast<const uint4 *>(vbase + row * D + 8 * vpart);
   }
+}
+
+// Working-set mode of the attention (fetch fused in): flag null = off.
+struct AttendFetch {
+  const uint8_t *flag;  // [batch]: 1 = retrieval step (fetch), 0 = read the working set
+  void *k, *v;          // working set [BH][cap][D]
+  int cap;
+  int32_t *spans;       // [BH][2]
+  int32_t *count;       // [BH]
+};
+
+// Rows [r_lo, r_hi) of the concatenated selection (n units, r_sel rows, in
+// s_psum / s_start) from the pool to the same positions of the working set,
+// kCopyUnroll 16-byte pieces in flight per thread, in passes of
+// kAttendMfmaPiece rows through the row table. Ends with a barrier.
+constexpr int kCopyUnroll = 8;
+
+template <int NT, int D>
+__device__ void attend_copy_rows(const kv_pool &pool, int bg, const AttendFetch &fx, int r_lo,
+                                 int r_hi, int n, int r_sel, const int *s_psum,
+                                 const int *s_start, int *s_rowtab) {
+  constexpr int LPR = D / 8;  // 16-byte pieces per bf16 row
+  const int tid = threadIdx.x;
+  const uint4 *ks = static_cast<const uint4 *>(pool.k) + (size_t)bg * pool.row_cap * LPR;
+  const uint4 *vs = static_cast<const uint4 *>(pool.v) + (size_t)bg * pool.row_cap * LPR;
+  uint4 *kd = static_cast<uint4 *>(fx.k) + (size_t)bg * fx.cap * LPR;
+  uint4 *vd = static_cast<uint4 *>(fx.v) + (size_t)bg * fx.cap * LPR;
+  for (int p0 = r_lo; p0 < r_hi; p0 += kAttendMfmaPiece) {
+    const int plen = min(kAttendMfmaPiece, r_hi - p0);
+    __syncthreads();  // the previous pass is done with the row table
+    for (int i = tid; i < plen; i += NT)
+      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, 0, s_psum, s_start, pool.row_cap);
+    __syncthreads();
+    const int pieces = plen * LPR;  // of K, and as many of V
+    for (int base = 0; base < 2 * pieces; base += NT * kCopyUnroll) {
+      u32x4_t buf[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        int p = base + tid + u * NT;
+        p = p < 2 * pieces ? p : 0;
+        const bool is_v = p >= pieces;
+        const int q = is_v ? p - pieces : p;
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(is_v ? vs : ks);
+        buf[u] = src[(size_t)s_rowtab[q / LPR] * LPR + q % LPR];
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int p = base + tid + u * NT;
+        u32x4_t *d = reinterpret_cast<u32x4_t *>(p < pieces ? kd + (size_t)p0 * LPR + p
+                                                            : vd + (size_t)p0 * LPR + (p - pieces));
+        if (p < 2 * pieces) *d = buf[u];
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // Fold one chunk into the wave's online-softmax state (m_run, l_run per
@@ -986,7 +1042,7 @@ __global__ void __launch_bounds__(kAttendThreads)
                          const int32_t *__restrict__ sel_units,
                          const int32_t *__restrict__ sel_spans, int sel_cap,
                          const int32_t *__restrict__ sel_n, float *__restrict__ out,
-                         float *__restrict__ partials, int32_t *counters) {
+                         float *__restrict__ partials, int32_t *counters, AttendFetch fx) {
   static_assert(G <= 16, "query columns of one MFMA tile");
   constexpr int NT = kAttendThreads, NW = kAttendWaves;
   constexpr int KS = D / 32;
@@ -1020,11 +1076,22 @@ __global__ void __launch_bounds__(kAttendThreads)
     qf[s] = __builtin_bit_cast(bf16x8a_t, v);
   }
 
+  // Rows come from the pool's selection, or (working-set mode on a step
+  // without retrieval) from the working set's one span; on a retrieval step
+  // of working-set mode they come from the pool and are stored to the
+  // working set as they are loaded.
+  const bool ws_mode = fx.flag != nullptr;
+  const bool fetching = ws_mode && fx.flag[b] != 0;  // uniform
+  const bool from_ws = ws_mode && !fetching;
+  const int scap = from_ws ? 1 : sel_cap;
+  const int32_t *su = from_ws ? nullptr : sel_units;
+  const int32_t *sp = from_ws ? fx.spans : sel_spans;
   int n;
-  const int r_sel = attend_load_selection<NT>(
-      pool, bg, sel_units ? sel_units + (size_t)bg * sel_cap : nullptr,
-      sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr, sel_n, sel_cap, &n, s_psum,
-      s_start, s_wsum);
+  int r_sel = attend_load_selection<NT>(
+      pool, bg, su ? su + (size_t)bg * scap : nullptr, sp ? sp + (size_t)bg * scap * 2 : nullptr,
+      from_ws ? fx.count : sel_n, scap, &n, s_psum, s_start, s_wsum);
+  const int r_all = r_sel;
+  if (fetching) r_sel = min(r_sel, fx.cap);
   int r_buf = 0, buf_begin = 0;
   if (pool.buf_cap > 0) {
     buf_begin = pool.buf_begin[b];
@@ -1033,6 +1100,30 @@ __global__ void __launch_bounds__(kAttendThreads)
   const int R = r_sel + r_buf;
   const int chunk = (R + nsplit - 1) / nsplit;
   const int r_lo = min(R, split * chunk), r_hi = min(R, r_lo + chunk);
+
+  if (fetching) {
+    // Retrieval step of working-set mode: this workgroup copies the rows it
+    // is about to attend, [r_lo, r_hi) of the selection, from the pool into
+    // the working set, then attends over them there like any later step.
+    if (split == 0 && tid == 0) {
+      fx.spans[2 * bg] = 0;
+      fx.spans[2 * bg + 1] = r_sel;
+      fx.count[bg] = r_sel > 0 ? 1 : 0;
+      if (r_all > fx.cap)
+        __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    attend_copy_rows<NT, D>(pool, bg, fx, r_lo, r_hi, n, r_sel, s_psum, s_start, s_rowtab);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the copies are written
+    __syncthreads();
+    if (tid == 0) {  // the selection is now the working set's one span
+      s_start[0] = 0;
+      s_psum[0] = 0;
+    }
+    n = 1;
+    __syncthreads();
+  }
+  const int row_cap = ws_mode ? fx.cap : pool.row_cap;
 
   // Online softmax state. m_run / l_run: per query head `col`, identical in
   // the four lanes col, col+16, col+32, col+48. acc: p.v partial sums of this
@@ -1044,13 +1135,15 @@ __global__ void __launch_bounds__(kAttendThreads)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-  const uint16_t *kbase = static_cast<const uint16_t *>(pool.k) + (size_t)bg * pool.row_cap * D;
-  const uint16_t *vbase = static_cast<const uint16_t *>(pool.v) + (size_t)bg * pool.row_cap * D;
+  const uint16_t *kbase =
+      static_cast<const uint16_t *>(ws_mode ? fx.k : pool.k) + (size_t)bg * row_cap * D;
+  const uint16_t *vbase =
+      static_cast<const uint16_t *>(ws_mode ? fx.v : pool.v) + (size_t)bg * row_cap * D;
 
   for (int p0 = r_lo; p0 < r_hi; p0 += kAttendMfmaPiece) {
     const int plen = min(kAttendMfmaPiece, r_hi - p0);
     for (int i = tid; i < plen; i += NT)
-      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, pool.row_cap);
+      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, row_cap);
     __syncthreads();
     int it = wave * kAttendChunk;
     if constexpr (kAttendPipelined<G>) {
@@ -1269,16 +1362,17 @@ template <typename T, int D>
 static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, float scale_log2,
                                  const int32_t *sel_units, const int32_t *sel_spans,
                                  int sel_cap, const int32_t *sel_n, int nsplit, float *out,
-                                 float *partials, int32_t *counters, hipStream_t s) {
+                                 float *partials, int32_t *counters, const AttendFetch &fx,
+                                 hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
+  if (sizeof(T) != 2 && fx.flag != nullptr) return KV_ERR_UNSUPPORTED;
 #define KVC_ATT(GG)                                                                             \
   do {                                                                                          \
     if constexpr (sizeof(T) == 2)                                                               \
       k_gather_attend_mfma<D, GG><<<grid, kAttendThreads, 0, s>>>(                              \
           *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,     \
-          out, partials,                                                                        \
-          counters);                                                                            \
+          out, partials, counters, fx);                                                         \
     else                                                                                        \
       k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                       \
           *pool, (const T *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, out,       \
@@ -1296,14 +1390,14 @@ static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, flo
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
-kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
+static kv_status attend_launch(const kv_pool *pool, const void *q, int hq, float scale,
                                const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
                                const int32_t *sel_n, int nsplit, float *out, float *partials,
-                               int32_t *counters, hipStream_t s) {
+                               int32_t *counters, const AttendFetch &fx, hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = exp2(x log2 e)
 #define KVC_AD(T, D)                                                                          \
   attend_dispatch<T, D>(pool, q, hq, sl2, sel_units, sel_spans, sel_cap, sel_n, nsplit, out, \
-                        partials, counters, s)
+                        partials, counters, fx, s)
   kv_status st;
   if (pool->dtype == KV_BF16)
     st = pool->head_dim == 128 ? KVC_AD(uint16_t, 128) : KVC_AD(uint16_t, 64);
@@ -1311,6 +1405,15 @@ kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float
     st = pool->head_dim == 128 ? KVC_AD(float, 128) : KVC_AD(float, 64);
 #undef KVC_AD
   return st;
+}
+
+kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
+                               const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
+                               const int32_t *sel_n, int nsplit, float *out, float *partials,
+                               int32_t *counters, hipStream_t s) {
+  const AttendFetch off{};
+  return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, out,
+                       partials, counters, off, s);
 }
 
 
@@ -1325,7 +1428,6 @@ kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float
 // previous working set. The source pool may live in host memory mapped into
 // the device's address space: then every piece is a read over the host link,
 // and keeping many in flight is what sets the rate.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kFetchThreads = 256;
 constexpr int kFetchUnroll = 8;
 constexpr int kFetchBlockBytes = kFetchThreads * kFetchUnroll * 16;
@@ -1415,6 +1517,27 @@ kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32
   }
 #undef KVC_FETCH
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+// Working-set fetch and attention in one launch (bf16): on a retrieval step
+// every attention workgroup stores the rows it loads from the pool into the
+// working set; otherwise it reads them from there. fp32 pools run the two
+// launches kv_fetch_selected and kv_gather_attend compose.
+kv_status launch_fetch_attend(const kv_pool *pool, const void *q, int hq, float scale,
+                              const uint8_t *flag, const int32_t *sel_units,
+                              const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
+                              int nsplit, const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
+                              float *out, float *partials, int32_t *counters, hipStream_t s) {
+  if (pool->dtype != KV_BF16) {
+    kv_status st = launch_fetch_rows(pool, flag, sel_units, sel_spans, sel_cap, sel_n, dst,
+                                     dst_spans, dst_n, s);
+    if (st != KV_OK) return st;
+    return launch_gather_attend(dst, q, hq, scale, nullptr, dst_spans, 1, dst_n, nsplit, out,
+                                partials, counters, s);
+  }
+  AttendFetch fx{flag, dst->k, dst->v, dst->row_cap, dst_spans, dst_n};
+  return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, out,
+                       partials, counters, fx, s);
 }
 
 }  // namespace kvc

@@ -218,5 +218,10 @@ kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32
                             const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
                             const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
                             hipStream_t s);
+kv_status launch_fetch_attend(const kv_pool *pool, const void *q, int hq, float scale,
+                              const uint8_t *flag, const int32_t *sel_units,
+                              const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
+                              int nsplit, const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
+                              float *out, float *partials, int32_t *counters, hipStream_t s);
 
 }  // namespace kvc

@@ -92,7 +92,8 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     spans: selection also writes row spans and attention reads them.
     fused_append: boundary test and segment append through kv_boundary_segment_append.
     fetch: on retrieval steps kv_fetch_selected copies the selected rows into an
-    HBM working set, and attention reads the working set.
+    HBM working set, and attention reads the working set; fetch="fused" does
+    both through kv_fetch_attend.
     flags: device [T, B] uint8 retrieval decisions to use instead of the boundary
     test's (kv_boundary still writes r; the selection follows the given flags)."""
     T = q.shape[0] if steps is None else steps
@@ -135,7 +136,11 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
                     kvc.kv_segment_append(pool, dec_k[t], dec_v[t], rec.flag[t])
             kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel,
                           sel_spans=sel_spans)
-        if fetch:
+        if fetch == "fused":
+            kvc.kv_fetch_attend(pool, q[t], scale, rec.flag[t], None if spans else sel_units,
+                                sel_n, budget, wset, wset.spans, wset.count, rec.out[t],
+                                ws=ws_att, sel_spans=sel_spans)
+        elif fetch:
             kvc.kv_fetch_selected(pool, rec.flag[t], None if spans else sel_units, sel_n, wset,
                                   wset.spans, wset.count, sel_spans=sel_spans)
             kvc.kv_gather_attend(wset, q[t], scale, None, wset.count, budget, rec.out[t],

@@ -215,6 +215,36 @@ def test_fetch_selected_validation():
     assert call(src_=ctypes.byref(seg)) == kvc.KV_ERR_UNSUPPORTED
 
 
+def test_fetch_attend_validation():
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    src = _fake_pool()
+    dst = _fake_pool(row_cap=512, unit_cap=1)
+    dst.k, dst.v = 0x20000, 0x30000
+    S, D = ctypes.byref(src), ctypes.byref(dst)
+    need = L.kv_gather_attend_workspace(D, 32, 512)
+    assert need > 0
+    f = ctypes.c_float(0.1)
+
+    def call(src_=S, dst_=D, q=a, hq=32, scale=f, flag=a, su=a, cap=64, sn=a, rows=512, ds=a,
+             dn=a, out=a, ws=a, nbytes=need):
+        return L.kv_fetch_attend(src_, q, hq, scale, flag, su, None, cap, sn, rows, dst_, ds, dn,
+                                 out, ws, nbytes, None)
+
+    for kw in ({"src_": None}, {"dst_": None}, {"q": None}, {"flag": None}, {"su": None},
+               {"sn": None}, {"ds": None}, {"dn": None}, {"out": None}, {"cap": 0},
+               {"hq": 12}, {"rows": -1}, {"scale": ctypes.c_float(float("nan"))}):
+        assert call(**kw) == kvc.KV_ERR_INVALID_ARG, kw
+    assert call(hq=24) == kvc.KV_ERR_UNSUPPORTED  # G = 3
+    assert call(cap=4097) == kvc.KV_ERR_UNSUPPORTED
+    assert call(nbytes=need - 1) == kvc.KV_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == kvc.KV_ERR_WORKSPACE  # misaligned
+    same = _fake_pool(row_cap=512, unit_cap=1)
+    assert call(dst_=ctypes.byref(same)) == kvc.KV_ERR_INVALID_ARG
+    seg = _fake_pool(buf_cap=64, seg_sum=0x10000)
+    assert call(src_=ctypes.byref(seg)) == kvc.KV_ERR_UNSUPPORTED
+
+
 def test_host_device_pointer_rejects_unpinned_memory():
     L = kvc.lib()
     out = ctypes.c_void_p()

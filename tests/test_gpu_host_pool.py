@@ -159,6 +159,11 @@ def test_host_pool_decode_matches_hbm_pool(cfg_idx, over, steps, seqs):
                                                sel_cap, fetch=True),
         "hbm, working set": gpu_decode(hbm, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap,
                                        fused=True, spans=True, fetch=True),
+        "host, fetch fused into attention": gpu_decode(host, qd, cfg.tau, cfg.budget, cfg.scale,
+                                                       sel_cap, fused=True, spans=True,
+                                                       fetch="fused"),
+        "host, fused, by ids": gpu_decode(host, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                                          fetch="fused"),
     }
     for label, rec in runs.items():
         for name in ("flag", "sel_n", "sel"):
@@ -168,11 +173,60 @@ def test_host_pool_decode_matches_hbm_pool(cfg_idx, over, steps, seqs):
     assert int(host.status.item()) == 0 and int(hbm.status.item()) == 0
 
 
+@pytest.mark.parametrize("dtype,d,hq,cap", [("bf16", 128, 8, 4096), ("bf16", 64, 4, 4096),
+                                             ("bf16", 128, 16, 300), ("fp32", 128, 4, 4096)])
+def test_fetch_attend_equals_fetch_then_attend(dtype, d, hq, cap):
+    # kv_fetch_attend == kv_fetch_selected + kv_gather_attend(working set): working
+    # set, spans, counts, status and output bit for bit, over a retrieval step and
+    # a reuse step (flags 1,0,1 then 0,0,0), with a working set too small for
+    # some selections when cap = 300
+    B, H, row_cap, unit_cap, sel_cap = 3, 2, 3000, 150, 96
+    pool, start, size = _ragged_pool(B, H, d, dtype, row_cap, unit_cap, True, seed=3)
+    g = np.random.default_rng(5)
+    sel = np.stack([[g.permutation(unit_cap)[:sel_cap] for _ in range(H)] for _ in range(B)])
+    sel_n = g.integers(0, sel_cap + 1, (B, H)).astype(np.int32)
+    su = torch.from_numpy(sel.astype(np.int32)).cuda()
+    sn = torch.from_numpy(sel_n).cuda()
+    q = torch.from_numpy(g.standard_normal((B, hq, d), np.float32)).to(pool.dtype).cuda()
+    max_rows = 4096
+    res = []
+    for fused in (False, True):
+        pool.status.zero_()
+        ws = working_set(pool, cap)
+        w = kvc.workspace(kvc.kv_gather_attend_workspace(ws, hq, max_rows))
+        outs = []
+        for flags in ([1, 0, 1], [0, 0, 0]):
+            flag = torch.tensor(flags, dtype=torch.uint8, device="cuda")
+            out = torch.zeros(B, hq, d, device="cuda")
+            if fused:
+                kvc.kv_fetch_attend(pool, q, 0.1, flag, su, sn, max_rows, ws, ws.spans, ws.count,
+                                    out, ws=w)
+            else:
+                kvc.kv_fetch_selected(pool, flag, su, sn, ws, ws.spans, ws.count)
+                kvc.kv_gather_attend(ws, q, 0.1, None, ws.count, max_rows, out, ws=w,
+                                     sel_spans=ws.spans)
+            outs.append(out)
+        torch.cuda.synchronize()
+        res.append((outs, ws, int(pool.status.item())))
+    (o0, w0, s0), (o1, w1, s1) = res
+    assert s0 == s1
+    if cap < 4096:
+        assert s0 == kvc.KV_ERR_CAPACITY
+    for a, b in zip(o0, o1):
+        np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+    assert torch.equal(w0.spans, w1.spans) and torch.equal(w0.count, w1.count)
+    for bi in (0, 2):  # sequences that retrieved: working sets equal where written
+        for h in range(H):
+            r = int(w0.spans[bi, h, 0, 1])
+            assert torch.equal(w0.k[bi, h, :r], w1.k[bi, h, :r])
+            assert torch.equal(w0.v[bi, h, :r], w1.v[bi, h, :r])
+
+
 def test_host_pool_working_set_decode_parity_cfg1_full_size():
     # the Qwen3-8B-shaped layer at full size with its K/V in host memory: fetch on
     # retrieval steps, attention over the working set, checked against the oracle
     cfg = wl.get_config(1, iters=2)
-    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True, fetch=True,
+    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True, fetch="fused",
               pool_kw=dict(host_kv=True))
     assert st["retrievals"] >= 2
 
@@ -181,7 +235,7 @@ def test_host_pool_working_set_decode_parity_cfg1_full_size():
                                          ("per-token", 16), ("boundary", 16)])
 def test_retrieval_policies_and_page_units_match_oracle(policy, page):
     cfg = wl.get_config(1, n_keys=8192, n_clusters=512, n_components=128, iters=3)
-    st = _run(cfg, 64, [0], policy=policy, page=page, fetch=True, spans=True,
+    st = _run(cfg, 64, [0], policy=policy, page=page, fetch="fused", spans=True,
               pool_kw=dict(host_kv=True))
     sched = wl.retrieval_schedule(policy, 64)
     if sched is not None:

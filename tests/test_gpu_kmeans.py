@@ -220,6 +220,34 @@ def test_cluster_build_deterministic():
     assert torch.equal(p1.k, p2.k)
 
 
+def test_cluster_build_beside_gemms_on_another_stream():
+    # K-means overlapped with a prefill forward (the note's asynchronous
+    # pipeline): kv_cluster_build on its own stream while large GEMMs run on
+    # another gives the same clustering and pool, bit for bit, as alone
+    cfg = wl.get_config(1, n_keys=8192, n_clusters=512, n_components=128)
+    inp, ref_pool, ref_lab = _cluster_build(cfg, [0, 1, 2, 3], 4)
+    B, H, N, d = inp["keys"].shape
+    keys = to_dev(inp["keys"], cfg.dtype)
+    vals = to_dev(inp["values"], cfg.dtype)
+    init = torch.from_numpy(inp["init_idx"]).cuda()
+    x = torch.randn(8192, 4096, device="cuda").bfloat16()
+    w = torch.randn(4096, 8192, device="cuda").bfloat16()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        pool = make_pool(B, H, d, cfg.dtype, N, cfg.n_clusters)
+        lab = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            y = [x @ w for _ in range(4)]
+        kvc.kv_cluster_build(pool, keys, vals, cfg.n_clusters, 4, init, assign_out=lab, stream=sb)
+        torch.cuda.synchronize()
+        del y
+        np.testing.assert_array_equal(lab.cpu().numpy(), ref_lab)
+        for name in ("k", "v", "unit_start", "unit_size", "unit_mean", "unit_index"):
+            assert torch.equal(getattr(pool, name), getattr(ref_pool, name)), name
+
+
 @pytest.mark.parametrize("cfg_idx,heads,sample", [(1, [0, 7], 4000), (3, [0], 3000), (4, [0], 3000)])
 def test_full_size_sampled(cfg_idx, heads, sample):
     """Full-size heads: GPU round on its own centroids, checked on sampled keys/clusters."""
