@@ -252,9 +252,12 @@ def main():
     if args.units != "cluster" and page is None:
         raise SystemExit(f"unknown --units {args.units!r}")
     variant = host or sched is not None or page is not None
-    if variant and (seg or L > 1):
+    if variant and L > 1:
         raise SystemExit("--pool/--policy/--units variants run on single-layer workloads "
-                         "without decode segments (--config 0, 1 or 4)")
+                         "(--config 0, 1, 2 or 4)")
+    if seg and (sched is not None or page is not None or (fetch and args.fetch == "separate")):
+        raise SystemExit("with decode segments (--config 2) only --pool host|host-direct "
+                         "(fused fetch) applies")
     if page is not None:
         C = -(-N // page)  # one unit per page
     # units: clusters, plus (long-output) the segments closed during decode
@@ -452,10 +455,12 @@ def main():
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
     att_rows = int(sel_rows.sum().item())
-    if fetch:  # attention reads the working set: one span per head
-        att_ms = launch_ms(lambda: kvc.kv_gather_attend(y0.wset, y0.q[T - 1], cfg.scale, None,
-                                                        y0.wn, cfg.budget, y0.out, ws=y0.ws_att,
-                                                        sel_spans=y0.wspans),
+    if fetch:  # a step without retrieval: the working set (+ the local buffer's HBM copy)
+        zeros = torch.zeros(B, dtype=torch.uint8, device="cuda")
+        att_ms = launch_ms(lambda: kvc.kv_fetch_attend(pool, y0.q[T - 1], cfg.scale, zeros, None,
+                                                       sel_n, cfg.budget, y0.wset, y0.wspans,
+                                                       y0.wn, y0.out, ws=y0.ws_att,
+                                                       sel_spans=sel_spans),
                            args.attend_reps)
         att_spans = int(y0.wn.sum().item())
     else:

@@ -94,6 +94,13 @@ typedef struct kv_pool {
   float *seg_sum;      /* [batch][n_kv_heads][head_dim] fp32 key sum of the open
                           segment; may be NULL when buf_cap == 0 */
   int32_t *status;     /* [1] device status word (kv_status of async errors) */
+  /* Optional HBM copy of the local buffer, for a pool whose k and v live in
+   * host memory (the note's "Key designs" item 2 keeps only a fixed-size local
+   * buffer on the GPU): pool row r of the buffer is also stored at slot
+   * r % buf_ring. Both NULL: the buffer rows are read from k and v. */
+  void *buf_k;        /* [batch][n_kv_heads][buf_ring][head_dim] or NULL */
+  void *buf_v;        /* same */
+  int32_t buf_ring;   /* slots per (sequence, KV head); >= buf_cap when set */
 } kv_pool;
 
 /* Human-readable name of a status code (static string). */
@@ -306,9 +313,9 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
  * KV_ERR_CAPACITY and keeps the first dst->row_cap rows.
  * dst: same batch, n_kv_heads, head_dim and dtype as pool, buf_cap 0, its
  * own k and v (only k, v and row_cap are used). dst_spans: [BH][2] int32;
- * dst_n: [BH] int32. Pools with a local buffer (buf_cap > 0) get
- * KV_ERR_UNSUPPORTED: the buffer rows are not part of a selection.
- * sel_cap <= 4096. No workspace. */
+ * dst_n: [BH] int32. The local buffer of a pool with decode segments is not
+ * part of a selection and is not copied (kv_fetch_attend reads it from the
+ * pool's HBM copy of it). sel_cap <= 4096. No workspace. */
 kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int32_t *sel_units,
                             const int32_t *sel_spans, int32_t sel_cap, const int32_t *sel_n,
                             const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
@@ -325,8 +332,13 @@ kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int3
  * is about to attend from the pool into the working set and attends over
  * them there; on other steps it reads the working set only, so a step
  * without retrieval costs one launch. fp32 pools run the two launches.
- * Arguments as for those two calls; workspace:
- * kv_gather_attend_workspace(dst, n_q_heads, max_rows). */
+ * A pool with decode segments (buf_cap > 0; bf16, with buf_k / buf_v set)
+ * is supported too: the attended rows are then the working set followed by
+ * the local buffer, read from the pool's HBM copy, i.e. exactly the rows
+ * and order of kv_gather_attend(pool, q, ..., the selection, max_rows),
+ * with bitwise equal output; other pools with buf_cap > 0 get
+ * KV_ERR_UNSUPPORTED. Arguments as for those two calls; workspace:
+ * kv_gather_attend_workspace(pool, n_q_heads, max_rows). */
 kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads, float scale,
                           const uint8_t *flag, const int32_t *sel_units, const int32_t *sel_spans,
                           int32_t sel_cap, const int32_t *sel_n, int32_t max_rows,

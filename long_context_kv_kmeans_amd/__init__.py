@@ -67,6 +67,7 @@ class KVPool(ctypes.Structure):
         ("buf_cap", ctypes.c_int32),
         ("buf_begin", ctypes.c_void_p), ("seg_begin", ctypes.c_void_p),
         ("seg_sum", ctypes.c_void_p), ("status", ctypes.c_void_p),
+        ("buf_k", ctypes.c_void_p), ("buf_v", ctypes.c_void_p), ("buf_ring", ctypes.c_int32),
     ]
 
 
@@ -188,7 +189,9 @@ def host_device_pointer(t: torch.Tensor) -> int:
 class Pool:
     """Tensors behind one ``kv_pool`` (see kvc.h for the layout). With
     ``host_kv`` the K and V rows live in pinned host memory, which the kernels
-    reach through its device address; every table stays on the GPU."""
+    reach through its device address; every table stays on the GPU, and a
+    pool with a local buffer also keeps an HBM copy of the buffer
+    (``buf_k``, ``buf_v``, ``buf_cap`` slots per head)."""
 
     batch: int
     n_kv_heads: int
@@ -221,6 +224,10 @@ class Pool:
         self.seg_sum = (torch.zeros(B, H, D, dtype=torch.float32, device=dev)
                         if self.buf_cap > 0 else None)
         self.status = torch.zeros(1, dtype=i32, device=dev)
+        self.buf_k = self.buf_v = None
+        if self.host_kv and self.buf_cap > 0:
+            self.buf_k = torch.zeros(B, H, self.buf_cap, D, dtype=self.dtype, device=dev)
+            self.buf_v = torch.zeros_like(self.buf_k)
         self._struct = None
 
     def struct(self) -> KVPool:
@@ -232,7 +239,8 @@ class Pool:
                 self.row_cap, self.unit_cap, kv(self.k), kv(self.v), p(self.unit_start),
                 p(self.unit_size), p(self.unit_mean), p(self.unit_index), p(self.n_rows),
                 p(self.n_units), p(self.n_cand), self.buf_cap, p(self.buf_begin),
-                p(self.seg_begin), p(self.seg_sum), p(self.status))
+                p(self.seg_begin), p(self.seg_sum), p(self.status), p(self.buf_k), p(self.buf_v),
+                self.buf_cap if self.buf_k is not None else 0)
         return self._struct
 
     def ref(self):
@@ -375,10 +383,11 @@ def kv_fetch_selected(pool: Pool, flag, sel_units, sel_n, dst: Pool, dst_spans, 
 def kv_fetch_attend(pool: Pool, q, scale: float, flag, sel_units, sel_n, max_rows: int,
                     dst: Pool, dst_spans, dst_n, out, ws=None, stream=None,
                     sel_spans=None) -> None:
-    """kv_fetch_selected + kv_gather_attend over the working set, in one launch."""
+    """kv_fetch_selected + kv_gather_attend over the working set (and the
+    pool's local buffer), in one launch."""
     Hq = q.shape[1]
     if ws is None:
-        ws = _call_workspace(kv_gather_attend_workspace(dst, Hq, max_rows), stream)
+        ws = _call_workspace(kv_gather_attend_workspace(pool, Hq, max_rows), stream)
     cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
     _check("kv_fetch_attend", lib().kv_fetch_attend(
         pool.ref(), _ptr(q), Hq, float(scale), _ptr(flag), _ptr(sel_units), _ptr(sel_spans), cap,

@@ -21,6 +21,8 @@ kv_status check_pool(const kv_pool *p) {
     return KV_ERR_INVALID_ARG;
   if (p->buf_cap < 0) return KV_ERR_INVALID_ARG;
   if (p->buf_cap > 0 && !p->seg_sum) return KV_ERR_INVALID_ARG;
+  if ((p->buf_k == nullptr) != (p->buf_v == nullptr)) return KV_ERR_INVALID_ARG;
+  if (p->buf_k && (p->buf_cap <= 0 || p->buf_ring < p->buf_cap)) return KV_ERR_INVALID_ARG;
   return KV_OK;
 }
 
@@ -326,8 +328,7 @@ kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int3
       dst->head_dim != pool->head_dim || dst->dtype != pool->dtype)
     return KV_ERR_INVALID_ARG;
   if (dst->k == pool->k || dst->v == pool->v) return KV_ERR_INVALID_ARG;
-  // the local buffer of a segment pool is not part of the selection
-  if (pool->buf_cap > 0 || dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;
+  if (dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;  // a working set has no local buffer
   return launch_fetch_rows(pool, flag, sel_units, sel_spans, sel_cap, sel_n, dst, dst_spans,
                            dst_n, stream);
 }
@@ -350,18 +351,20 @@ kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads,
       dst->head_dim != pool->head_dim || dst->dtype != pool->dtype)
     return KV_ERR_INVALID_ARG;
   if (dst->k == pool->k || dst->v == pool->v) return KV_ERR_INVALID_ARG;
-  if (pool->buf_cap > 0 || dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;
+  if (dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;  // a working set has no local buffer
+  // a local buffer is attended from the pool's HBM copy of it (bf16 kernel only)
+  if (pool->buf_cap > 0 && (!pool->buf_k || pool->dtype != KV_BF16)) return KV_ERR_UNSUPPORTED;
   const int G = n_q_heads / pool->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
   if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
-  const size_t need = kv_gather_attend_workspace(dst, n_q_heads, max_rows);
+  const size_t need = kv_gather_attend_workspace(pool, n_q_heads, max_rows);
   if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
   const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
   int32_t *counters = static_cast<int32_t *>(ws);
   float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               align_up(bh * sizeof(int32_t), 256));
   return launch_fetch_attend(pool, q, n_q_heads, scale, flag, sel_units, sel_spans, sel_cap,
-                             sel_n, attend_num_splits(dst, max_rows), dst, dst_spans, dst_n, out,
+                             sel_n, attend_num_splits(pool, max_rows), dst, dst_spans, dst_n, out,
                              partials, counters, stream);
 }
 

@@ -232,6 +232,11 @@ __global__ void __launch_bounds__(256) k_segment_append(kv_pool pool, const T *_
     const size_t ro = (bg * pool.row_cap + n_rows) * D + e;
     static_cast<T *>(pool.k)[ro] = kv;
     static_cast<T *>(pool.v)[ro] = vv;
+    if (pool.buf_k != nullptr) {  // the local buffer's HBM copy: slot n_rows % buf_ring
+      const size_t bo = (bg * pool.buf_ring + n_rows % pool.buf_ring) * D + e;
+      static_cast<T *>(pool.buf_k)[bo] = kv;
+      static_cast<T *>(pool.buf_v)[bo] = vv;
+    }
     pool.seg_sum[(size_t)b * HD + i] = sum + Elem<T>::to_f32(kv);
   };
 #pragma unroll
@@ -722,8 +727,12 @@ __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t 
 }
 
 // Pool row of position j (< r_sel: inside the selection, else the buffer).
+// ring > 0 (the pool keeps an HBM copy of its local buffer): a buffer row r
+// is returned as ~(r % ring), its slot in the copy, so that negative entries
+// of a row table name buffer slots.
 __device__ __forceinline__ int attend_row_of(int j, int n, int r_sel, int buf_begin,
-                                             const int *s_psum, const int *s_start, int row_cap) {
+                                             const int *s_psum, const int *s_start, int row_cap,
+                                             int ring = 0) {
   int row;
   if (j < r_sel) {
     int lo = 0, hi = n - 1;  // last i with s_psum[i] <= j
@@ -734,6 +743,7 @@ __device__ __forceinline__ int attend_row_of(int j, int n, int r_sel, int buf_be
     row = s_start[lo] + (j - s_psum[lo]);
   } else {
     row = buf_begin + (j - r_sel);
+    if (ring > 0) return ~(max(row, 0) % ring);
   }
   return min(max(row, 0), row_cap - 1);
 }
@@ -883,28 +893,38 @@ template <int D> struct AttendChunk {
   uint4 vv[VU];
 };
 
-template <int D>
+// A row-table entry r >= 0 is row r of kbase / vbase; with BUF (the pool keeps
+// an HBM copy of its local buffer) r < 0 is slot ~r of that copy (kbuf / vbuf).
+template <int D, bool BUF>
+__device__ __forceinline__ const uint16_t *attend_row_ptr(const uint16_t *base,
+                                                          const uint16_t *buf, int r) {
+  if constexpr (BUF) return r >= 0 ? base + (size_t)r * D : buf + (size_t)(~r) * D;
+  return base + (size_t)r * D;
+}
+
+template <int D, bool BUF>
 __device__ __forceinline__ void attend_chunk_load(AttendChunk<D> &c, const int *s_rowtab, int it,
                                                   int plen, const uint16_t *kbase,
-                                                  const uint16_t *vbase, int lane) {
+                                                  const uint16_t *vbase, const uint16_t *kbuf,
+                                                  const uint16_t *vbuf, int lane) {
   using C = AttendChunk<D>;
   const int col = lane & 15, quad = lane >> 4;
   const int vpart = lane % C::LPR, sub = (lane & 15) / C::LPR;
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk) {
     const int li = it + tk * 16 + col;
-    const size_t row = li < plen ? (size_t)s_rowtab[li] : 0;
+    const uint16_t *kr = attend_row_ptr<D, BUF>(kbase, kbuf, li < plen ? s_rowtab[li] : 0);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
       c.kf[tk][s] = __builtin_bit_cast(
-          bf16x8a_t, *reinterpret_cast<const uint4 *>(kbase + row * D + 32 * s + 8 * quad));
+          bf16x8a_t, *reinterpret_cast<const uint4 *>(kr + 32 * s + 8 * quad));
   }
 #pragma unroll
   for (int i = 0; i < C::VU; ++i) {
     const int k = i * C::RPL + sub;
     const int li = it + 16 * (k >> 2) + 4 * quad + (k & 3);
-    const size_t row = li < plen ? (size_t)s_rowtab[li] : 0;
-    c.vv[i] = *reinterpret_cast<const uint4 *>(vbase + row * D + 8 * vpart);
+    const uint16_t *vr = attend_row_ptr<D, BUF>(vbase, vbuf, li < plen ? s_rowtab[li] : 0);
+    c.vv[i] = *reinterpret_cast<const uint4 *>(vr + 8 * vpart);
   }
 }
 
@@ -1036,7 +1056,7 @@ __device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const
 // spilling, so they fold one chunk at a time.
 template <int G> constexpr bool kAttendPipelined = G == 2 || G == 4;
 
-template <int D, int G>
+template <int D, int G, bool BUF>
 __global__ void __launch_bounds__(kAttendThreads)
     k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
                          const int32_t *__restrict__ sel_units,
@@ -1113,7 +1133,8 @@ __global__ void __launch_bounds__(kAttendThreads)
         __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    attend_copy_rows<NT, D>(pool, bg, fx, r_lo, r_hi, n, r_sel, s_psum, s_start, s_rowtab);
+    attend_copy_rows<NT, D>(pool, bg, fx, min(r_lo, r_sel), min(r_hi, r_sel), n, r_sel, s_psum,
+                            s_start, s_rowtab);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the copies are written
     __syncthreads();
     if (tid == 0) {  // the selection is now the working set's one span
@@ -1139,11 +1160,17 @@ __global__ void __launch_bounds__(kAttendThreads)
       static_cast<const uint16_t *>(ws_mode ? fx.k : pool.k) + (size_t)bg * row_cap * D;
   const uint16_t *vbase =
       static_cast<const uint16_t *>(ws_mode ? fx.v : pool.v) + (size_t)bg * row_cap * D;
+  const int ring = BUF ? pool.buf_ring : 0;
+  const uint16_t *kbuf = nullptr, *vbuf = nullptr;
+  if (BUF) {
+    kbuf = static_cast<const uint16_t *>(pool.buf_k) + (size_t)bg * ring * D;
+    vbuf = static_cast<const uint16_t *>(pool.buf_v) + (size_t)bg * ring * D;
+  }
 
   for (int p0 = r_lo; p0 < r_hi; p0 += kAttendMfmaPiece) {
     const int plen = min(kAttendMfmaPiece, r_hi - p0);
     for (int i = tid; i < plen; i += NT)
-      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, row_cap);
+      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, row_cap, ring);
     __syncthreads();
     int it = wave * kAttendChunk;
     if constexpr (kAttendPipelined<G>) {
@@ -1151,22 +1178,22 @@ __global__ void __launch_bounds__(kAttendThreads)
       // step's scores and p.v run.
       AttendChunk<D> ca, cb;
       if (it < plen)
-        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, lane);
+        attend_chunk_load<D, BUF>(ca, s_rowtab, it, plen, kbase, vbase, kbuf, vbuf, lane);
       while (it < plen) {
         if (it + STEP < plen)
-          attend_chunk_load<D>(cb, s_rowtab, it + STEP, plen, kbase, vbase, lane);
+          attend_chunk_load<D, BUF>(cb, s_rowtab, it + STEP, plen, kbase, vbase, kbuf, vbuf, lane);
         attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
         if (it >= plen) break;
         if (it + STEP < plen)
-          attend_chunk_load<D>(ca, s_rowtab, it + STEP, plen, kbase, vbase, lane);
+          attend_chunk_load<D, BUF>(ca, s_rowtab, it + STEP, plen, kbase, vbase, kbuf, vbuf, lane);
         attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
       }
     } else {
       for (; it < plen; it += STEP) {
         AttendChunk<D> ca;
-        attend_chunk_load<D>(ca, s_rowtab, it, plen, kbase, vbase, lane);
+        attend_chunk_load<D, BUF>(ca, s_rowtab, it, plen, kbase, vbase, kbuf, vbuf, lane);
         attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
       }
     }
@@ -1255,11 +1282,18 @@ __global__ void __launch_bounds__(kAttendValuThreads)
   }
   const T *kbase = static_cast<const T *>(pool.k) + (size_t)bg * pool.row_cap * D + part * EPL;
   const T *vbase = static_cast<const T *>(pool.v) + (size_t)bg * pool.row_cap * D + part * EPL;
+  const int ring = pool.buf_k != nullptr ? pool.buf_ring : 0;
+  const T *kbuf = kbase, *vbuf = vbase;  // local buffer's HBM copy (slots ~r of negative rows)
+  if (ring > 0) {
+    kbuf = static_cast<const T *>(pool.buf_k) + (size_t)bg * ring * D + part * EPL;
+    vbuf = static_cast<const T *>(pool.buf_v) + (size_t)bg * ring * D + part * EPL;
+  }
 
   for (int p0 = r_lo; p0 < r_hi; p0 += NT) {
     const int plen = min(NT, r_hi - p0);
     if (tid < plen)
-      s_rowtab[tid] = attend_row_of(p0 + tid, n, r_sel, buf_begin, s_psum, s_start, pool.row_cap);
+      s_rowtab[tid] =
+          attend_row_of(p0 + tid, n, r_sel, buf_begin, s_psum, s_start, pool.row_cap, ring);
     __syncthreads();
     for (int it = wave * UNR * RPI; it < plen; it += NW * UNR * RPI) {
       uint4 kv[UNR], vv[UNR];
@@ -1268,9 +1302,11 @@ __global__ void __launch_bounds__(kAttendValuThreads)
       for (int uu = 0; uu < UNR; ++uu) {
         const int li = it + uu * RPI + slot;
         ok[uu] = li < plen;
-        const size_t row = ok[uu] ? (size_t)s_rowtab[li] : 0;
-        kv[uu] = *reinterpret_cast<const uint4 *>(kbase + row * D);
-        vv[uu] = *reinterpret_cast<const uint4 *>(vbase + row * D);
+        const int r = ok[uu] ? s_rowtab[li] : 0;
+        kv[uu] = *reinterpret_cast<const uint4 *>(r >= 0 ? kbase + (size_t)r * D
+                                                         : kbuf + (size_t)(~r) * D);
+        vv[uu] = *reinterpret_cast<const uint4 *>(r >= 0 ? vbase + (size_t)r * D
+                                                         : vbuf + (size_t)(~r) * D);
       }
       float s[UNR][G];
 #pragma unroll
@@ -1370,9 +1406,14 @@ static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, flo
 #define KVC_ATT(GG)                                                                             \
   do {                                                                                          \
     if constexpr (sizeof(T) == 2)                                                               \
-      k_gather_attend_mfma<D, GG><<<grid, kAttendThreads, 0, s>>>(                              \
-          *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,     \
-          out, partials, counters, fx);                                                         \
+      if (pool->buf_k != nullptr)                                                               \
+        k_gather_attend_mfma<D, GG, true><<<grid, kAttendThreads, 0, s>>>(                      \
+            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,   \
+            out, partials, counters, fx);                                                       \
+      else                                                                                      \
+        k_gather_attend_mfma<D, GG, false><<<grid, kAttendThreads, 0, s>>>(                     \
+            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,   \
+            out, partials, counters, fx);                                                       \
     else                                                                                        \
       k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                       \
           *pool, (const T *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, out,       \

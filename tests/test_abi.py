@@ -211,8 +211,9 @@ def test_fetch_selected_validation():
         assert call(dst_=ctypes.byref(bad)) == kvc.KV_ERR_INVALID_ARG, field
     same = _fake_pool(row_cap=512, unit_cap=1)  # k, v alias the source's
     assert call(dst_=ctypes.byref(same)) == kvc.KV_ERR_INVALID_ARG
-    seg = _fake_pool(buf_cap=64, seg_sum=0x10000)
-    assert call(src_=ctypes.byref(seg)) == kvc.KV_ERR_UNSUPPORTED
+    dseg = _fake_pool(row_cap=512, unit_cap=1, buf_cap=8, seg_sum=0x10000)
+    dseg.k, dseg.v = 0x20000, 0x30000
+    assert call(dst_=ctypes.byref(dseg)) == kvc.KV_ERR_UNSUPPORTED  # a working set has no buffer
 
 
 def test_fetch_attend_validation():
@@ -241,8 +242,29 @@ def test_fetch_attend_validation():
     assert call(ws=ctypes.c_void_p(0x10010)) == kvc.KV_ERR_WORKSPACE  # misaligned
     same = _fake_pool(row_cap=512, unit_cap=1)
     assert call(dst_=ctypes.byref(same)) == kvc.KV_ERR_INVALID_ARG
-    seg = _fake_pool(buf_cap=64, seg_sum=0x10000)
+    seg = _fake_pool(buf_cap=64, seg_sum=0x10000)  # local buffer without an HBM copy
     assert call(src_=ctypes.byref(seg)) == kvc.KV_ERR_UNSUPPORTED
+    segf = _fake_pool(buf_cap=64, seg_sum=0x10000, dtype=kvc.KV_F32)  # fp32 with a copy
+    segf.buf_k, segf.buf_v, segf.buf_ring = 0x40000, 0x50000, 64
+    dstf = _fake_pool(row_cap=512, unit_cap=1, dtype=kvc.KV_F32)
+    dstf.k, dstf.v = 0x20000, 0x30000
+    assert call(src_=ctypes.byref(segf), dst_=ctypes.byref(dstf)) == kvc.KV_ERR_UNSUPPORTED
+
+
+def test_local_buffer_copy_validation():
+    # buf_k / buf_v: both or neither, only with a local buffer, ring >= buf_cap
+    L = kvc.lib()
+    ok = _fake_pool(buf_cap=64, seg_sum=0x10000)
+    ok.buf_k, ok.buf_v, ok.buf_ring = 0x40000, 0x50000, 64
+    assert L.kv_gather_attend_workspace(ctypes.byref(ok), 32, 512) > 0
+    for field, val in (("buf_v", None), ("buf_ring", 63)):
+        bad = _fake_pool(buf_cap=64, seg_sum=0x10000)
+        bad.buf_k, bad.buf_v, bad.buf_ring = 0x40000, 0x50000, 64
+        setattr(bad, field, val)
+        assert L.kv_gather_attend_workspace(ctypes.byref(bad), 32, 512) == 0, field
+    nobuf = _fake_pool()
+    nobuf.buf_k, nobuf.buf_v, nobuf.buf_ring = 0x40000, 0x50000, 64
+    assert L.kv_gather_attend_workspace(ctypes.byref(nobuf), 32, 512) == 0
 
 
 def test_host_device_pointer_rejects_unpinned_memory():

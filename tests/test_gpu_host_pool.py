@@ -240,3 +240,51 @@ def test_retrieval_policies_and_page_units_match_oracle(policy, page):
     sched = wl.retrieval_schedule(policy, 64)
     if sched is not None:
         assert st["retrievals"] == int(sched.sum())
+
+
+def test_host_pool_with_segments_matches_hbm_pool():
+    # long-output config, small local buffer (frequent evictions and forced
+    # closes): K/V rows in host memory, the local buffer also in its HBM copy.
+    # Attention straight from the host pool (buffer rows from the copy) and
+    # through the working set give the HBM pool's flags, counters, selections
+    # and outputs bit for bit; the copy holds every buffered row.
+    cfg = wl.get_config(2, buf_cap=64, steps=300, p_jump=0.05, budget=256, iters=3)
+    inp = wl.layer_inputs(cfg, 0)
+    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    q, _ = wl.layer_queries(cfg, 0, steps=cfg.steps)
+    dk, dv = wl.layer_decode_kv(cfg, 0, steps=cfg.steps)
+    n_units = cfg.n_clusters + cfg.steps
+    sel_cap = min(cfg.budget, n_units)
+    runs = {}
+    for label, host, kw in (("hbm", False, {}), ("host, direct", True, {}),
+                            ("host, working set", True, {"fetch": "fused"})):
+        pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                                      n_units=n_units, buf_cap=cfg.buf_cap,
+                                      extra_rows=cfg.steps, host_kv=host)
+        assert (pool.buf_k is not None) == host
+        rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, cfg.budget, cfg.scale, sel_cap,
+                         dec_k=to_dev(dk, cfg.dtype), dec_v=to_dev(dv, cfg.dtype), spans=True,
+                         fused_append=True, **kw)
+        assert int(pool.status.item()) == 0
+        runs[label] = (rec, pool)
+    base, hbm = runs["hbm"]
+    assert int(base.flag.sum()) >= 5
+    for label in ("host, direct", "host, working set"):
+        rec, pool = runs[label]
+        for name in ("flag", "sel_n", "sel", "counters"):
+            assert torch.equal(getattr(base, name), getattr(rec, name)), (label, name)
+        np.testing.assert_array_equal(base.out.cpu().numpy().view(np.uint32),
+                                      rec.out.cpu().numpy().view(np.uint32), err_msg=label)
+        assert torch.equal(hbm.k.cpu(), pool.k) and torch.equal(hbm.v.cpu(), pool.v)
+        n_rows, buf_begin = int(pool.n_rows[0]), int(pool.buf_begin[0])
+        rows = torch.arange(buf_begin, n_rows)
+        slots = rows % cfg.buf_cap
+        assert torch.equal(pool.buf_k[0][:, slots].cpu(), pool.k[0][:, rows])
+        assert torch.equal(pool.buf_v[0][:, slots].cpu(), pool.v[0][:, rows])
+
+
+def test_host_pool_with_segments_parity():
+    # the same path against the oracle's decode loop (segment tables included)
+    cfg = wl.get_config(2, buf_cap=128, steps=600, p_jump=0.05, budget=512, iters=3)
+    _run(cfg, cfg.steps, [0], compare_every=3, spans=True, fused_append=True, fetch="fused",
+         pool_kw=dict(host_kv=True))
