@@ -252,9 +252,6 @@ def main():
     if args.units != "cluster" and page is None:
         raise SystemExit(f"unknown --units {args.units!r}")
     variant = host or sched is not None or page is not None
-    if variant and L > 1:
-        raise SystemExit("--pool/--policy/--units variants run on single-layer workloads "
-                         "(--config 0, 1, 2 or 4)")
     if seg and (sched is not None or page is not None or (fetch and args.fetch == "separate")):
         raise SystemExit("with decode segments (--config 2) only --pool host|host-direct "
                          "(fused fetch) applies")
