@@ -202,10 +202,14 @@ kv_status kv_boundary(const void *q_prev, const void *q_cur, int32_t batch, int3
  *   1. close the open segment when flag[b] and it is non-empty, or when it
  *      already holds buf_cap rows: it becomes unit n_units[b] with
  *      unit_mean = seg_sum / size and unit_index = dtype(unit_mean);
- *   2. append k_t, v_t as row n_rows[b] and add k_t to seg_sum;
+ *   2. append k_t, v_t as row n_rows[b] and add k_t to seg_sum (and, when
+ *      the pool keeps an HBM copy of its buffer, also to slot
+ *      n_rows[b] % buf_ring of buf_k / buf_v);
  *   3. while the buffer [buf_begin, n_rows) holds more than buf_cap rows,
  *      evict the oldest closed segment: n_cand[b]++ and buf_begin moves past
  *      it (no data moves; the pool and the buffer share the row store).
+ * The buffer therefore never holds more than buf_cap rows after a step, so
+ * buf_ring = buf_cap slots keep every buffered row.
  * k_t, v_t: [batch][n_kv_heads][head_dim] (dtype). flag: [batch] uint8 from
  * kv_boundary of the same step. Out of rows or units: *pool->status =
  * KV_ERR_CAPACITY and that sequence's step is skipped.
@@ -273,7 +277,8 @@ kv_status kv_boundary_select(const kv_pool *pool, const void *q_prev, const void
  * query head h of KV head g:
  *   out[b][h] = softmax(scale * K_S q[b][h]) V_S   (fp32; 0 if S is empty)
  * where S = rows of the units sel_units[b][g][0..sel_n[b][g]) followed, when
- * pool->buf_cap > 0, by the local-buffer rows [buf_begin[b], n_rows[b]).
+ * pool->buf_cap > 0, by the local-buffer rows [buf_begin[b], n_rows[b])
+ * (read from the pool's HBM copy of the buffer when buf_k is set).
  * When sel_spans ([BH][sel_cap][2] int32, as written by kv_select) is given,
  * the units' row ranges are read from it instead of looking the ids up in
  * the unit table (one dependent memory round trip less; sel_units may then
