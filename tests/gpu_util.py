@@ -113,7 +113,7 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
     ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, budget))
     sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device=dev) if spans else None
-    wset = working_set(pool, budget) if fetch else None
+    wset = working_set(pool, max(budget, 1)) if fetch else None
     for t in range(T):
         if flags is not None:
             assert not fused and dec_k is None

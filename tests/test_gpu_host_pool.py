@@ -242,13 +242,14 @@ def test_retrieval_policies_and_page_units_match_oracle(policy, page):
         assert st["retrievals"] == int(sched.sum())
 
 
-def test_host_pool_with_segments_matches_hbm_pool():
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_host_pool_with_segments_matches_hbm_pool(dtype):
     # long-output config, small local buffer (frequent evictions and forced
     # closes): K/V rows in host memory, the local buffer also in its HBM copy.
     # Attention straight from the host pool (buffer rows from the copy) and
-    # through the working set give the HBM pool's flags, counters, selections
-    # and outputs bit for bit; the copy holds every buffered row.
-    cfg = wl.get_config(2, buf_cap=64, steps=300, p_jump=0.05, budget=256, iters=3)
+    # (bf16) through the working set give the HBM pool's flags, counters,
+    # selections and outputs bit for bit; the copy holds every buffered row.
+    cfg = wl.get_config(2, buf_cap=64, steps=300, p_jump=0.05, budget=256, iters=3, dtype=dtype)
     inp = wl.layer_inputs(cfg, 0)
     labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
     q, _ = wl.layer_queries(cfg, 0, steps=cfg.steps)
@@ -256,8 +257,10 @@ def test_host_pool_with_segments_matches_hbm_pool():
     n_units = cfg.n_clusters + cfg.steps
     sel_cap = min(cfg.budget, n_units)
     runs = {}
-    for label, host, kw in (("hbm", False, {}), ("host, direct", True, {}),
-                            ("host, working set", True, {"fetch": "fused"})):
+    variants = [("hbm", False, {}), ("host, direct", True, {})]
+    if dtype == "bf16":
+        variants.append(("host, working set", True, {"fetch": "fused"}))
+    for label, host, kw in variants:
         pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
                                       n_units=n_units, buf_cap=cfg.buf_cap,
                                       extra_rows=cfg.steps, host_kv=host)
@@ -269,7 +272,7 @@ def test_host_pool_with_segments_matches_hbm_pool():
         runs[label] = (rec, pool)
     base, hbm = runs["hbm"]
     assert int(base.flag.sum()) >= 5
-    for label in ("host, direct", "host, working set"):
+    for label in [v[0] for v in variants[1:]]:
         rec, pool = runs[label]
         for name in ("flag", "sel_n", "sel", "counters"):
             assert torch.equal(getattr(base, name), getattr(rec, name)), (label, name)
@@ -288,3 +291,26 @@ def test_host_pool_with_segments_parity():
     cfg = wl.get_config(2, buf_cap=128, steps=600, p_jump=0.05, budget=512, iters=3)
     _run(cfg, cfg.steps, [0], compare_every=3, spans=True, fused_append=True, fetch="fused",
          pool_kw=dict(host_kv=True))
+
+
+def test_host_pool_segments_zero_budget_attends_the_buffer_only():
+    # budget 0: nothing is ever selected or fetched; the attention covers the
+    # local buffer alone, read from its HBM copy, equal to the HBM pool's
+    cfg = wl.get_config(2, buf_cap=32, steps=80, p_jump=0.1, budget=0, iters=2)
+    inp = wl.layer_inputs(cfg, 0)
+    labels, cents = oracle_clustering(inp["keys"], inp["init_idx"], cfg.iters, cfg.dtype)
+    q, _ = wl.layer_queries(cfg, 0, steps=cfg.steps)
+    dk, dv = wl.layer_decode_kv(cfg, 0, steps=cfg.steps)
+    n_units = cfg.n_clusters + cfg.steps
+    outs = []
+    for host, kw in ((False, {}), (True, {"fetch": "fused"})):
+        pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                                      n_units=n_units, buf_cap=cfg.buf_cap,
+                                      extra_rows=cfg.steps, host_kv=host)
+        rec = gpu_decode(pool, to_dev(q, cfg.dtype), cfg.tau, 0, cfg.scale, 8,
+                         dec_k=to_dev(dk, cfg.dtype), dec_v=to_dev(dv, cfg.dtype), spans=True,
+                         fused_append=True, **kw)
+        assert int(rec.sel_n.sum()) == 0 and int(pool.status.item()) == 0
+        outs.append(rec.out.cpu().numpy())
+    assert np.abs(outs[0]).max() > 0
+    np.testing.assert_array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
