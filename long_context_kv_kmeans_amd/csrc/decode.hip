@@ -57,41 +57,48 @@ constexpr int kBoundaryHeadsPerWave = 8;
 // r of sequence b, computed by waves 0..3 of the calling workgroup (all of
 // its threads must call: the partial sums meet in LDS `part`[4]). Every
 // thread receives r. Callers of any workgroup size get the same bits.
+// A head is read by LPH lanes with one 16-byte load each, so one wave
+// instruction covers HPI heads and the per-head sums reduce over LPH lanes
+// for all HPI heads at once; the HPI cosines then sum across lane groups.
 template <typename T, int D>
 __device__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
                             int b, float *part) {
-  constexpr int EPL = D / 64;
+  constexpr int EPL = 16 / (int)sizeof(T);  // elements per 16-byte load
+  constexpr int LPH = D / EPL;              // lanes per head
+  constexpr int HPI = 64 / LPH;             // heads per wave instruction
   constexpr int HPW = kBoundaryHeadsPerWave;
+  constexpr int NI = HPW / HPI;             // load instructions per tensor and wave step
+  static_assert(HPW % HPI == 0 && (LPH == 8 || LPH == 16 || LPH == 32), "head layout");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / LPH, piece = lane % LPH;
   if (wave < 4) {
     float csum = 0.f;
     for (int h0 = wave * HPW; h0 < hq; h0 += 4 * HPW) {
-      T a[HPW][EPL], c[HPW][EPL];
+      uint4 a[NI], c[NI];
 #pragma unroll
-      for (int i = 0; i < HPW; ++i) {
-        const int h = h0 + i;
-        const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + lane * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          a[i][e] = q_prev[o + e];
-          c[i][e] = q_cur[o + e];
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int h = h0 + i * HPI + sub;
+        const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + piece * EPL;
+        a[i] = *reinterpret_cast<const uint4 *>(q_prev + o);
+        c[i] = *reinterpret_cast<const uint4 *>(q_cur + o);
       }
 #pragma unroll
-      for (int i = 0; i < HPW; ++i) {
+      for (int i = 0; i < NI; ++i) {
+        float x[EPL], y[EPL];
+        unpack16<T>(a[i], x);
+        unpack16<T>(c[i], y);
         float dot = 0.f, n1 = 0.f, n2 = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          const float x = Elem<T>::to_f32(a[i][e]), y = Elem<T>::to_f32(c[i][e]);
-          dot = fmaf(x, y, dot);
-          n1 = fmaf(x, x, n1);
-          n2 = fmaf(y, y, n2);
+          dot = fmaf(x[e], y[e], dot);
+          n1 = fmaf(x[e], x[e], n1);
+          n2 = fmaf(y[e], y[e], n2);
         }
-        dot = wave_sum(dot);
-        n1 = wave_sum(n1);
-        n2 = wave_sum(n2);
+        dot = group_sum<LPH>(dot);
+        n1 = group_sum<LPH>(n1);
+        n2 = group_sum<LPH>(n2);
         const float cosv = (n1 > 0.f && n2 > 0.f) ? dot / (sqrtf(n1) * sqrtf(n2)) : 0.f;
-        if (h0 + i < hq) csum += cosv;
+        csum += sum_stride<LPH>(h0 + i * HPI + sub < hq ? cosv : 0.f);
       }
     }
     if (lane == 0) part[wave] = csum;
