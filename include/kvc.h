@@ -154,7 +154,7 @@ kv_status kv_kmeans_assign(const void *keys, const float *centroids, int32_t n_h
 /* The assignment step split in two, for callers that assign several key
  * sets against one set of centroids (the centroids are converted once).
  * kv_kmeans_prepare writes the centroids' assignment form into ws (same size
- * as kv_kmeans_assign_workspace: for KV_BF16 the bf16 split fragments and
+ * as kv_kmeans_assign_workspace: for KV_BF16 the bf16 MFMA fragments and fp32
  * half norms, for KV_F32 the half norms). kv_kmeans_assign_prepared then
  * labels keys exactly as kv_kmeans_assign would with those centroids; it
  * reads ws without modifying it, so ws stays valid until the caller

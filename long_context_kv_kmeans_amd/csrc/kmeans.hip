@@ -50,54 +50,32 @@ kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float
 }
 
 // ---------------------------------------------------------------- bf16 assign
-// Centroid fragments for v_mfma_f32_32x32x16_bf16 with centroids as the A
-// operand (32 rows x 16 k per instruction): for tile t, k-step s and lane l,
-// the lane holds row m = l % 32 and k = 16 s + 8 (l / 32) + j, j = 0..7.
-// One extra k-step carries the norms so the matrix cores accumulate
-//   x . c^ - |c^|^2 / 2 - |x|^2 / 2 = -|x - c^|^2 / 2:
-// for lanes l < 32 the centroid side holds (-hc, -mc, -lc, 1, 1, 1, 0, 0) and
-// the key side (1, 1, 1, -hx, -mx, -lx, 0, 0), where h + m + l splits a half
-// squared norm into three bf16 parts (about 24 significant bits). Padding rows
-// (k >= C) carry -3.39e38 instead of their norm and are also masked out.
-constexpr uint32_t kBf16One = 0x3f80u;
-constexpr uint32_t kBf16NegMax = 0xff7fu;  // -3.39e38
+// Centroid tiles for v_mfma_f32_32x32x16_bf16 with centroids as the A operand
+// (32 rows x 16 k per instruction). A tile of 32 centroids is KS = D / 16
+// fragment blocks followed by one norm block:
+//   fragment block s, lane l (16 bytes): row m = l % 32 and
+//     k = 16 s + 8 (l / 32) + j, j = 0..7;
+//   norm block (32 fp32): entry m = -|c^_m|^2 / 2 of the bf16-rounded row;
+//     padding rows (m >= C) hold kPadNorm and never win.
+// The norm block is the accumulator's initial value, so the matrix cores
+// produce x . c^ - |c^|^2 / 2 with no extra k-step.
+constexpr int kNormU4 = 8;  // 16-byte units of a tile's norm block
+constexpr float kPadNorm = -3.0e38f;
 
-__device__ __forceinline__ void split3_neg(float v, uint32_t *h, uint32_t *m, uint32_t *l) {
-  const uint16_t a = f32_to_bf16_rne(v);
-  const float r1 = v - bf16_bits_to_f32(a);
-  const uint16_t b = f32_to_bf16_rne(r1);
-  const float r2 = r1 - bf16_bits_to_f32(b);
-  const uint16_t c = f32_to_bf16_rne(r2);
-  *h = a ^ 0x8000u;
-  *m = b ^ 0x8000u;
-  *l = c ^ 0x8000u;
+template <int D> struct AssignTile {
+  static constexpr int KS = D / 16;             // k-steps per tile
+  static constexpr int U4 = KS * 64 + kNormU4;  // 16-byte units per tile
+};
+
+__device__ __forceinline__ void write_centroid_norm(uint4 *tile, int ks, int m, float neg_halfsq) {
+  reinterpret_cast<float *>(tile + ks * 64)[m] = neg_halfsq;
 }
 
-// Writes the norm k-step of centroid row `k` of tile t (lanes m and m + 32).
-__device__ __forceinline__ void write_centroid_aug(uint16_t *tile_base, int ks, int m, bool real,
-                                                   float halfsq) {
-  uint4 a0;
-  if (real) {
-    uint32_t h, md, lo;
-    split3_neg(halfsq, &h, &md, &lo);
-    a0.x = h | (md << 16);
-    a0.y = lo | (kBf16One << 16);
-  } else {
-    a0.x = kBf16NegMax;
-    a0.y = kBf16One << 16;
-  }
-  a0.z = kBf16One | (kBf16One << 16);
-  a0.w = 0u;
-  uint4 *aug = reinterpret_cast<uint4 *>(tile_base + (size_t)(ks - 1) * 64 * 8);
-  aug[m] = a0;
-  aug[m + 32] = uint4{0u, 0u, 0u, 0u};
-}
-
-// fp32 centroids -> fragments; D/4 threads per centroid row, 4 elements each.
+// fp32 centroids -> tiles; D/4 threads per centroid row, 4 elements each.
 template <int D>
 __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ cent,
                                                     uint16_t *__restrict__ frags, int c, int ntile) {
-  constexpr int KS = D / 16 + 1;
+  using TL = AssignTile<D>;
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
   const int bh = blockIdx.y;
@@ -116,46 +94,53 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
   sq = fmaf(bf16_bits_to_f32(b3), bf16_bits_to_f32(b3), sq);
   sq = group_sum<TPR>(sq);
   const int t = row / 32, m = row % 32, s = e0 / 16, hf = (e0 % 16) / 8, j0 = e0 % 8;
-  uint16_t *tile_base = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
+  uint4 *tile = reinterpret_cast<uint4 *>(frags) + ((size_t)bh * ntile + t) * TL::U4;
   uint2 pk;
   pk.x = b0 | ((uint32_t)b1 << 16);
   pk.y = b2 | ((uint32_t)b3 << 16);
-  *reinterpret_cast<uint2 *>(tile_base + ((size_t)s * 64 + m + 32 * hf) * 8 + j0) = pk;
-  if (e0 == 0) write_centroid_aug(tile_base, KS, m, real, 0.5f * sq);
+  *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(tile + s * 64 + m + 32 * hf) + j0) = pk;
+  if (e0 == 0) write_centroid_norm(tile, TL::KS, m, real ? -0.5f * sq : kPadNorm);
 }
 
 // One workgroup = 8 waves x 64 keys. Keys are the B operand (column n = key),
 // resident in VGPRs for the whole centroid sweep. Centroid tiles stream into
 // two LDS stage buffers with direct global->LDS loads (each wave instruction
-// moves one 1 KB fragment block), so staging costs neither VGPRs nor LDS
-// write instructions; the two buffers are separate objects and are selected
-// statically, which lets the compiler keep the next stage's loads in flight
-// while the current stage is read. A wave folds tile t into its argmin before
-// issuing tile t+1's MFMAs into the same accumulators (no copies); the matrix
-// cores and the VALU overlap across the 4 waves each SIMD holds (128 VGPRs),
-// and a stage's barrier is shared by 8 waves per 36 KB of staging.
+// moves one 1 KB block of the stage's flat copy), so staging costs neither
+// VGPRs nor LDS write instructions; the two buffers are separate objects and
+// are selected statically, which lets the compiler keep the next stage's
+// loads in flight while the current stage is read. A wave folds tile t into
+// its argmin before issuing tile t+1's MFMAs into the same accumulators (no
+// copies); the matrix cores and the VALU overlap across the 4 waves each SIMD
+// holds (128 VGPRs), and a stage's barrier is shared by 8 waves.
+//
+// Scores: the accumulators start from the tile's norm block minus K_w, the
+// largest |x|^2 / 2 among the wave's keys (plus 0.1%), so every score
+// x . c^ - |c^|^2 / 2 - K_w = -|x - c^|^2 / 2 - (K_w - |x|^2 / 2) is <= 0 and
+// orders a key's centroids exactly as the distance does.
 //
 // Argmin: every lane sees one key and 16 centroid rows per tile. A score
-// -d^2/2 (<= 0, negative floats order inversely to their bit patterns) is
-// packed as (bits & ~15) | r, so among packed values the unsigned minimum is
-// the largest score (nearest centroid) and, on equal upper 28 bits, the
-// lowest row r: one v_and_or and half a v_min3 per score. A score that
-// rounding leaves slightly above 0 (a key sitting on a centroid) packs below
-// every negative one, i.e. it still ranks as nearest.
+// (<= 0; negative floats order inversely to their bit patterns) is packed as
+// (bits & ~15) | r, so among packed values the unsigned minimum is the
+// largest score (nearest centroid) and, on equal upper 28 bits, the lowest
+// row r: one v_and_or and half a v_min3 per score. A score that rounding
+// leaves slightly above 0 packs below every negative one, i.e. it still
+// ranks as nearest.
 // Across tiles a new minimum must be strictly smaller in the upper 28 bits,
 // so earlier (lower-index) tiles win ties. Comparing 28 of 32 bits moves a
-// decision only where two distances agree to about 2^-19 relative, below the
-// fp32 accumulation error of the 144-term dot product.
+// decision only where two scores agree to about 2^-19 relative, the size of
+// the fp32 accumulation error of the 128-term dot product.
 template <int D, int NCB, int MINW>
 __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
     k_assign_mfma(const uint16_t *__restrict__ keys, const uint16_t *__restrict__ frags,
                   int32_t *__restrict__ labels, int n, int c, int ntile, int blocks_per_head,
                   int total_blocks) {
-  constexpr int KS = D / 16 + 1;
-  constexpr int TILE_U4 = KS * 64;
-  constexpr int STAGE_U4 = kTilesPerStage * TILE_U4;  // 16-byte units per stage
-  __shared__ uint4 lds0[STAGE_U4];
-  __shared__ uint4 lds1[STAGE_U4];
+  using TL = AssignTile<D>;
+  constexpr int KS = TL::KS;
+  constexpr int TILE_U4 = TL::U4;
+  constexpr int STAGE_U4 = kTilesPerStage * TILE_U4;   // 16-byte units per stage
+  constexpr int STAGE_BLOCKS = (STAGE_U4 + 63) / 64;  // 1 KB DMA blocks (the last partial)
+  __shared__ uint4 lds0[STAGE_BLOCKS * 64];
+  __shared__ uint4 lds1[STAGE_BLOCKS * 64];
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int bh = bid / blocks_per_head;
@@ -166,13 +151,14 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
 
   // Key fragments (B operand): lane holds key n = lane % 32, k = 16 s + 8 half + j.
   bf16x8_t bfrag[NCB][KS];
+  float kmax = 0.f;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int key = key0 + cb * 32 + (lane & 31);
     const uint16_t *krow = keys + ((size_t)bh * n + (key < n ? key : 0)) * D;
     float sq = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS - 1; ++s) {
+    for (int s = 0; s < KS; ++s) {
       uint4 v = {0u, 0u, 0u, 0u};
       if (key < n) v = *reinterpret_cast<const uint4 *>(krow + 16 * s + 8 * half);
       bfrag[cb][s] = __builtin_bit_cast(bf16x8_t, v);
@@ -181,17 +167,15 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
 #pragma unroll
       for (int j = 0; j < 8; ++j) sq = fmaf(f[j], f[j], sq);
     }
-    sq = sum_xor32(sq);
-    uint32_t h, md, lo;
-    split3_neg(0.5f * sq, &h, &md, &lo);
-    uint4 aug = {0u, 0u, 0u, 0u};
-    if (half == 0) {
-      aug.x = kBf16One | (kBf16One << 16);
-      aug.y = kBf16One | (h << 16);
-      aug.z = md | (lo << 16);
-    }
-    bfrag[cb][KS - 1] = __builtin_bit_cast(bf16x8_t, aug);
+    kmax = fmaxf(kmax, sum_xor32(sq));
   }
+  // The empty asm makes the product opaque, so the compiler cannot fuse it
+  // into the per-tile subtractions below in some tiles and not in others:
+  // every tile's accumulator start must be the same function of its norms
+  // bit for bit (identical centroids must score identically in every tile
+  // for the lowest-index tie rule).
+  float koff = 0.5f * wave_max(kmax) * 1.001f;
+  asm volatile("" : "+v"(koff));
 
   uint32_t bestp[NCB];
   int btile[NCB];
@@ -204,28 +188,39 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
   const uint4 *gfr = reinterpret_cast<const uint4 *>(frags) + (size_t)bh * ntile * TILE_U4;
   const int nstage = (ntile + kTilesPerStage - 1) / kTilesPerStage;
 
-  // Stage st -> LDS: wave w moves fragment blocks w, w + 4, ... (1 KB each);
-  // blocks of tiles >= ntile are never read and are skipped.
+  // Stage st -> LDS as one flat copy of its tiles: wave w moves 1 KB blocks
+  // w, w + 8, ...; units past the head's last tile are not loaded (and never read).
   auto dma_stage = [&](int st, uint4 *dst) {
+    const int lim = min(ntile - st * kTilesPerStage, kTilesPerStage) * TILE_U4;
 #pragma unroll
-    for (int i = wave; i < kTilesPerStage * KS; i += kAssignWaves) {
-      if (st * kTilesPerStage + i / KS < ntile)
+    for (int i = wave; i < STAGE_BLOCKS; i += kAssignWaves) {
+      if (i * 64 + lane < lim)
         __builtin_amdgcn_global_load_lds(gfr + (size_t)st * STAGE_U4 + i * 64 + lane, dst + i * 64,
                                          16, 0, 0);
     }
   };
+  // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4,
+  // whose norms are entries 8 j + 4 half .. + 3 (unit 2 j + half) of the norm block.
   auto mfma_tile = [&](const uint4 *buf, int tt, f32x16_t *o) {
+    const uint4 *tb = buf + tt * TILE_U4;
+    f32x16_t ci;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16_t{};
+    for (int j = 0; j < 4; ++j) {
+      const uint4 u = tb[KS * 64 + 2 * j + half];
+      ci[4 * j + 0] = __uint_as_float(u.x) - koff;
+      ci[4 * j + 1] = __uint_as_float(u.y) - koff;
+      ci[4 * j + 2] = __uint_as_float(u.z) - koff;
+      ci[4 * j + 3] = __uint_as_float(u.w) - koff;
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, buf[(tt * KS + s) * 64 + lane]);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, tb[s * 64 + lane]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[cb][s], o[cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[cb][s], s == 0 ? ci : o[cb], 0,
+                                                        0, 0);
     }
   };
-  // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4.
   auto argmin_tile = [&](const f32x16_t &acc, int cb, int t, bool last) {
     uint32_t p[16];
 #pragma unroll
@@ -352,7 +347,7 @@ __global__ void __launch_bounds__(256) k_assign_f32(const float *__restrict__ ke
 size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt) {
   if (dt == KV_BF16) {
     const size_t ntile = (size_t)(c + 31) / 32;
-    return align_up((size_t)bh * ntile * (d / 16 + 1) * 64 * 8 * sizeof(uint16_t), 256);
+    return align_up((size_t)bh * ntile * ((size_t)(d / 16) * 64 + kNormU4) * 16, 256);
   }
   return align_up((size_t)bh * c * sizeof(float), 256);
 }
@@ -549,7 +544,7 @@ __global__ void k_scatter(const int32_t *__restrict__ labels, const int32_t *__r
 // are combined in a fixed order (fp32 throughout, so the result is
 // reproducible bit for bit). The mean replaces the centroid (an empty
 // cluster keeps its value). For bf16 keys the same pass writes the next
-// round's MFMA fragments and norm k-step, so no separate prep is needed.
+// round's MFMA tiles (fragments and norm block), so no separate prep is needed.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
                                                 const int32_t *__restrict__ perm,
@@ -562,7 +557,6 @@ __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
   constexpr int LPR = D / EPL;               // lanes per row
   constexpr int RPI = 64 / LPR;              // member rows per wave instruction
   constexpr int UNR = 4;
-  constexpr int KS = D / 16 + 1;
   const int bh = blockIdx.y;
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -616,16 +610,16 @@ __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
     }
     sq = group_sum<LPR>(sq);
     const int t = k / 32, m = k % 32, e0 = part * 8;
-    uint16_t *tile_base = frags + ((size_t)bh * ntile + t) * KS * 64 * 8;
+    uint4 *tile = reinterpret_cast<uint4 *>(frags) + ((size_t)bh * ntile + t) * AssignTile<D>::U4;
     if (slot == 0) {
       uint4 pk;
       pk.x = b[0] | ((uint32_t)b[1] << 16);
       pk.y = b[2] | ((uint32_t)b[3] << 16);
       pk.z = b[4] | ((uint32_t)b[5] << 16);
       pk.w = b[6] | ((uint32_t)b[7] << 16);
-      *reinterpret_cast<uint4 *>(tile_base + ((size_t)(e0 / 16) * 64 + m + 32 * ((e0 % 16) / 8)) * 8) = pk;
+      tile[(e0 / 16) * 64 + m + 32 * ((e0 % 16) / 8)] = pk;
     }
-    if (lane == 0) write_centroid_aug(tile_base, KS, m, true, 0.5f * sq);
+    if (lane == 0) write_centroid_norm(tile, AssignTile<D>::KS, m, -0.5f * sq);
   }
 }
 
