@@ -201,8 +201,11 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
   };
   // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4,
   // whose norms are entries 8 j + 4 half .. + 3 (unit 2 j + half) of the norm block.
+  // The next k-step's A fragment is requested before this k-step's MFMAs issue.
   auto mfma_tile = [&](const uint4 *buf, int tt, f32x16_t *o) {
     const uint4 *tb = buf + tt * TILE_U4;
+    bf16x8_t a[2];
+    a[0] = __builtin_bit_cast(bf16x8_t, tb[lane]);
     f32x16_t ci;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -214,11 +217,11 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, tb[s * 64 + lane]);
+      if (s + 1 < KS) a[(s + 1) & 1] = __builtin_bit_cast(bf16x8_t, tb[(s + 1) * 64 + lane]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag[cb][s], s == 0 ? ci : o[cb], 0,
-                                                        0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1], bfrag[cb][s],
+                                                        s == 0 ? ci : o[cb], 0, 0, 0);
     }
   };
   auto argmin_tile = [&](const f32x16_t &acc, int cb, int t, bool last) {
