@@ -6,9 +6,13 @@ One step = one pass of the whole path over one Qwen3-8B-shaped layer
 per head, C = 2048, 10 Lloyd rounds):
   prefill : kv_cluster_build (K-means assign/update x10, CSR pack of K/V);
   decode  : 256 steps of kv_boundary_select (boundary test + selection in one
-            launch, writing the selected units' row spans) -> kv_gather_attend
-            (reading those spans) on the seeded query walk, replayed from one
-            captured HIP graph.
+            launch, writing the selected units' row spans) -> kv_fetch_attend
+            over an HBM working set (on a retrieval step the attention launch
+            first copies the selected rows there; on the other steps it reads
+            the working set's contiguous rows, whose addresses are known at
+            launch) on the seeded query walk, replayed from one captured HIP
+            graph. ``--attend pool`` attends the pool's rows directly
+            (kv_gather_attend reading the selection's row spans).
 Inputs are synthetic (seeded Gaussian-mixture keys, random values and query
 walks) and resident in HBM before timing starts.
 
@@ -213,6 +217,10 @@ def main():
                          "retrieval steps fetch the selected rows into an HBM working set "
                          "that attention reads); host-direct (attention reads host memory "
                          "every step)")
+    ap.add_argument("--attend", choices=("wset", "pool"), default="wset",
+                    help="HBM pool without a local buffer: attend an HBM working set holding "
+                         "the current selection's rows (kv_fetch_attend), or the pool's rows "
+                         "through the selection's spans (kv_gather_attend)")
     ap.add_argument("--fetch", choices=("fused", "separate"), default="fused",
                     help="--pool host: the working-set copy inside the attention launch "
                          "(kv_fetch_attend) or as a launch of its own (kv_fetch_selected, "
@@ -246,7 +254,10 @@ def main():
     C, T, Hq, L = cfg.n_clusters, cfg.steps, cfg.n_q_heads, cfg.layers
     seg = cfg.buf_cap > 0
     host = args.pool != "hbm"
-    fetch = args.pool == "host"
+    # working set: always for a host pool ("host"); for an HBM pool without a
+    # local buffer unless --attend pool
+    fetch = args.pool == "host" or (args.pool == "hbm" and cfg.buf_cap == 0
+                                    and args.attend == "wset")
     sched = wl.retrieval_schedule(args.policy, T)
     page = int(args.units.split(":", 1)[1]) if args.units.startswith("page:") else None
     if args.units != "cluster" and page is None:
@@ -475,7 +486,7 @@ def main():
     att_peak = HOST_LINK_GBS if args.pool == "host-direct" else HBM_PEAK_GBS
 
     fetch_res = None
-    if fetch:
+    if args.pool == "host":
         # the working-set fetch of the final selection, every sequence retrieving
         ones = torch.ones(B, dtype=torch.uint8, device="cuda")
         f_ms = launch_ms(lambda: kvc.kv_fetch_selected(pool, ones, None, sel_n, y0.wset,
@@ -516,7 +527,8 @@ def main():
     share = {"k_gather_attend": T * L * att_ms / ms_step,
              "k_assign_mfma": cfg.iters * L * asg_ms / ms_step}
 
-    traffic = profiled_traffic(cfg.name) if not variant else None
+    # the committed counter profile covers the default path only
+    traffic = profiled_traffic(cfg.name) if not variant and args.attend == "wset" else None
     keys_per_step = L * B * H * N
     res = {
         "metric": "prefill keys clustered/s; decode select+gather+attend us/layer-step, %HBM peak",
@@ -536,6 +548,7 @@ def main():
                    "iters": cfg.iters, "decode_steps": T, "budget": cfg.budget,
                    "local_buffer": cfg.buf_cap, "tau": cfg.tau, "pool": args.pool,
                    "fetch": args.fetch if fetch else None,
+                   "attend": "wset" if fetch else "pool",
                    "policy": args.policy, "units": args.units},
         "retrieval_steps": int(fl.sum()),
         "prefill_ms": pre_ms,
@@ -544,7 +557,9 @@ def main():
         "decode_bytes_per_layer_step": dec_bytes,
         "decode_hbm_frac": dec_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
         "roofline": {"bound": "hbm" if args.pool != "host-direct" else "host-link",
-                     "kernel": "k_gather_attend_mfma (kv_gather_attend)",
+                     "kernel": ("k_gather_attend_mfma (kv_fetch_attend, working set, step "
+                                "without retrieval)" if fetch else
+                                "k_gather_attend_mfma (kv_gather_attend)"),
                      "achieved": att_gbs, "peak": att_peak, "unit": "GB/s",
                      "frac": att_gbs / att_peak,
                      "traffic": traffic["k_gather_attend_mfma"]["bytes"] if traffic else None,

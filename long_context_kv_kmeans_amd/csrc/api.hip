@@ -307,7 +307,8 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
   float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               align_up(bh * sizeof(int32_t), 256));
   return launch_gather_attend(pool, q, n_q_heads, scale, sel_units, sel_spans, sel_cap, sel_n,
-                              attend_num_splits(pool, max_rows), out, partials, counters, stream);
+                              attend_num_splits(pool, max_rows), attend_row_bound(pool, max_rows),
+                              out, partials, counters, stream);
 }
 
 
@@ -364,7 +365,8 @@ kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads,
   float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                               align_up(bh * sizeof(int32_t), 256));
   return launch_fetch_attend(pool, q, n_q_heads, scale, flag, sel_units, sel_spans, sel_cap,
-                             sel_n, attend_num_splits(pool, max_rows), dst, dst_spans, dst_n, out,
+                             sel_n, attend_num_splits(pool, max_rows),
+                             attend_row_bound(pool, max_rows), dst, dst_spans, dst_n, out,
                              partials, counters, stream);
 }
 

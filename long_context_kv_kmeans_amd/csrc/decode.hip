@@ -935,6 +935,32 @@ __device__ __forceinline__ void attend_chunk_load(AttendChunk<D> &c, const int *
   }
 }
 
+// Rows rbase + position of a contiguous row range (clamped to rmax), in the
+// lane layout of attend_chunk_load: needs no row table, so it can be issued
+// before the range's length is known.
+template <int D>
+__device__ __forceinline__ void attend_chunk_load_direct(AttendChunk<D> &c, int rbase, int rmax,
+                                                         const uint16_t *kbase,
+                                                         const uint16_t *vbase, int lane) {
+  using C = AttendChunk<D>;
+  const int col = lane & 15, quad = lane >> 4;
+  const int vpart = lane % C::LPR, sub = (lane & 15) / C::LPR;
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+    const uint16_t *kr = kbase + (size_t)min(rbase + tk * 16 + col, rmax) * D;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      c.kf[tk][s] = __builtin_bit_cast(
+          bf16x8a_t, *reinterpret_cast<const uint4 *>(kr + 32 * s + 8 * quad));
+  }
+#pragma unroll
+  for (int i = 0; i < C::VU; ++i) {
+    const int k = i * C::RPL + sub;
+    const uint16_t *vr = vbase + (size_t)min(rbase + 16 * (k >> 2) + 4 * quad + (k & 3), rmax) * D;
+    c.vv[i] = *reinterpret_cast<const uint4 *>(vr + 8 * vpart);
+  }
+}
+
 // Working-set mode of the attention (fetch fused in): flag null = off.
 struct AttendFetch {
   const uint8_t *flag;  // [batch]: 1 = retrieval step (fetch), 0 = read the working set
@@ -995,12 +1021,21 @@ __device__ void attend_copy_rows(const kv_pool &pool, int bg, const AttendFetch 
 // this lane's V elements, relative to m_run). Probabilities and the rescale
 // factor move to the V lanes by row broadcasts: no LDS round trip.
 template <int D, int G>
-__device__ __forceinline__ void attend_chunk_fold(const AttendChunk<D> &c, const bf16x8a_t *qf,
+__device__ __forceinline__ void attend_chunk_fold(AttendChunk<D> &c, const bf16x8a_t *qf,
                                                   int it, int plen, float scale_log2,
                                                   float &m_run, float &l_run, float (*acc)[8],
                                                   int lane) {
   using C = AttendChunk<D>;
   const int quad = lane >> 4, sub = (lane & 15) / C::LPR;
+  if (it + kAttendChunk > plen) {
+    // rows past the piece: whatever was loaded for them, their p = 0 must
+    // meet v = 0 so that they add exactly nothing
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      const int k = i * C::RPL + sub;
+      if (it + 16 * (k >> 2) + 4 * quad + (k & 3) >= plen) c.vv[i] = uint4{0u, 0u, 0u, 0u};
+    }
+  }
   f32x4_t sc[2];
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk) {
@@ -1068,7 +1103,7 @@ __global__ void __launch_bounds__(kAttendThreads)
     k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
                          const int32_t *__restrict__ sel_units,
                          const int32_t *__restrict__ sel_spans, int sel_cap,
-                         const int32_t *__restrict__ sel_n, float *__restrict__ out,
+                         const int32_t *__restrict__ sel_n, int rcap, float *__restrict__ out,
                          float *__restrict__ partials, int32_t *counters, AttendFetch fx) {
   static_assert(G <= 16, "query columns of one MFMA tile");
   constexpr int NT = kAttendThreads, NW = kAttendWaves;
@@ -1108,15 +1143,57 @@ __global__ void __launch_bounds__(kAttendThreads)
   // of working-set mode they come from the pool and are stored to the
   // working set as they are loaded.
   const bool ws_mode = fx.flag != nullptr;
-  const bool fetching = ws_mode && fx.flag[b] != 0;  // uniform
+  // Working-set mode without a local buffer: the working set's rows are
+  // contiguous from row 0 and this workgroup's chunk starts at
+  // split * ceil(rcap / nsplit) whenever the span holds at most rcap rows, so
+  // each wave requests its first 32 rows now, in the same memory round trip
+  // as the flag and the span. A retrieval step (or any other span) discards
+  // them and takes the general path.
+  AttendChunk<D> ca;
+  const int spec_chunk = (max(rcap, 1) + nsplit - 1) / nsplit;
+  const int spec_lo = split * spec_chunk;
+  if (!BUF && ws_mode && wave * kAttendChunk < spec_chunk)  // waves with rows in the chunk
+    attend_chunk_load_direct<D>(
+        ca, spec_lo + wave * kAttendChunk, fx.cap - 1,
+        static_cast<const uint16_t *>(fx.k) + (size_t)bg * fx.cap * D,
+        static_cast<const uint16_t *>(fx.v) + (size_t)bg * fx.cap * D, lane);
+  // The flag and the working set's one span (read as attend_load_selection
+  // reads a one-entry list) are requested right behind the rows; every value
+  // feeds the test below, so none of the loads is deferred into a branch and
+  // all of them are in flight at once.
+  int ws_flag = 0, ws_cnt = 0;
+  int2 ws_sp = {0, 0};
+  if (ws_mode) {
+    ws_flag = fx.flag[b];
+    if (!BUF) {
+      ws_cnt = fx.count[bg];
+      ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * bg);
+    }
+  }
+  const int ws_n = min(max(ws_cnt, 0), 1);
+  const int ws_size = max(ws_sp.y, 0) * ws_n, ws_start = ws_sp.x * ws_n;
+  // uniform: a step without retrieval whose rows start at 0 and fit the bound,
+  // i.e. `ca` holds this wave's first chunk
+  const bool spec = !BUF && ws_mode && ws_flag == 0 && ws_start == 0 && ws_size <= rcap;
+  const bool fetching = ws_mode && ws_flag != 0;  // uniform
   const bool from_ws = ws_mode && !fetching;
-  const int scap = from_ws ? 1 : sel_cap;
-  const int32_t *su = from_ws ? nullptr : sel_units;
-  const int32_t *sp = from_ws ? fx.spans : sel_spans;
-  int n;
-  int r_sel = attend_load_selection<NT>(
-      pool, bg, su ? su + (size_t)bg * scap : nullptr, sp ? sp + (size_t)bg * scap * 2 : nullptr,
-      from_ws ? fx.count : sel_n, scap, &n, s_psum, s_start, s_wsum);
+  int n, r_sel;
+  if (!BUF && from_ws) {
+    n = ws_n;
+    r_sel = ws_size;
+    if (tid == 0) {
+      s_psum[0] = 0;
+      s_start[0] = ws_start;
+    }
+    __syncthreads();
+  } else {
+    const int scap = from_ws ? 1 : sel_cap;
+    const int32_t *su = from_ws ? nullptr : sel_units;
+    const int32_t *sp = from_ws ? fx.spans : sel_spans;
+    r_sel = attend_load_selection<NT>(
+        pool, bg, su ? su + (size_t)bg * scap : nullptr, sp ? sp + (size_t)bg * scap * 2 : nullptr,
+        from_ws ? fx.count : sel_n, scap, &n, s_psum, s_start, s_wsum);
+  }
   const int r_all = r_sel;
   if (fetching) r_sel = min(r_sel, fx.cap);
   int r_buf = 0, buf_begin = 0;
@@ -1125,7 +1202,7 @@ __global__ void __launch_bounds__(kAttendThreads)
     r_buf = max(pool.n_rows[b] - buf_begin, 0);
   }
   const int R = r_sel + r_buf;
-  const int chunk = (R + nsplit - 1) / nsplit;
+  const int chunk = (max(R, rcap) + nsplit - 1) / nsplit;
   const int r_lo = min(R, split * chunk), r_hi = min(R, r_lo + chunk);
 
   if (fetching) {
@@ -1174,36 +1251,45 @@ __global__ void __launch_bounds__(kAttendThreads)
     vbuf = static_cast<const uint16_t *>(pool.buf_v) + (size_t)bg * ring * D;
   }
 
+  // In the speculative case the rows are p0 + position (what the row table
+  // would hold), read straight from the working set.
+  bool preloaded = spec;
   for (int p0 = r_lo; p0 < r_hi; p0 += kAttendMfmaPiece) {
     const int plen = min(kAttendMfmaPiece, r_hi - p0);
-    for (int i = tid; i < plen; i += NT)
-      s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, row_cap, ring);
-    __syncthreads();
+    if (!spec) {
+      for (int i = tid; i < plen; i += NT)
+        s_rowtab[i] = attend_row_of(p0 + i, n, r_sel, buf_begin, s_psum, s_start, row_cap, ring);
+      __syncthreads();
+    }
+    auto load = [&](AttendChunk<D> &c, int pos) {
+      if (spec)
+        attend_chunk_load_direct<D>(c, p0 + pos, row_cap - 1, kbase, vbase, lane);
+      else
+        attend_chunk_load<D, BUF>(c, s_rowtab, pos, plen, kbase, vbase, kbuf, vbuf, lane);
+    };
     int it = wave * kAttendChunk;
     if constexpr (kAttendPipelined<G>) {
       // Two register sets: the next step's loads are in flight while this
       // step's scores and p.v run.
-      AttendChunk<D> ca, cb;
-      if (it < plen)
-        attend_chunk_load<D, BUF>(ca, s_rowtab, it, plen, kbase, vbase, kbuf, vbuf, lane);
+      AttendChunk<D> cb;
+      if (it < plen && !preloaded) load(ca, it);
       while (it < plen) {
-        if (it + STEP < plen)
-          attend_chunk_load<D, BUF>(cb, s_rowtab, it + STEP, plen, kbase, vbase, kbuf, vbuf, lane);
+        if (it + STEP < plen) load(cb, it + STEP);
         attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
         if (it >= plen) break;
-        if (it + STEP < plen)
-          attend_chunk_load<D, BUF>(ca, s_rowtab, it + STEP, plen, kbase, vbase, kbuf, vbuf, lane);
+        if (it + STEP < plen) load(ca, it + STEP);
         attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
       }
     } else {
       for (; it < plen; it += STEP) {
-        AttendChunk<D> ca;
-        attend_chunk_load<D, BUF>(ca, s_rowtab, it, plen, kbase, vbase, kbuf, vbuf, lane);
+        if (!preloaded) load(ca, it);
+        preloaded = false;
         attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
       }
     }
+    preloaded = false;
     __syncthreads();
   }
 
@@ -1235,7 +1321,7 @@ __global__ void __launch_bounds__(kAttendValuThreads)
     k_gather_attend_valu(kv_pool pool, const T *__restrict__ q, int hq, float scale_log2,
                          const int32_t *__restrict__ sel_units,
                          const int32_t *__restrict__ sel_spans, int sel_cap,
-                         const int32_t *__restrict__ sel_n, float *__restrict__ out,
+                         const int32_t *__restrict__ sel_n, int rcap, float *__restrict__ out,
                          float *__restrict__ partials, int32_t *counters) {
   constexpr int NT = kAttendValuThreads, NW = NT / 64;
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane (one 16-byte load)
@@ -1276,7 +1362,7 @@ __global__ void __launch_bounds__(kAttendValuThreads)
     r_buf = max(pool.n_rows[b] - buf_begin, 0);
   }
   const int R = r_sel + r_buf;
-  const int chunk = (R + nsplit - 1) / nsplit;
+  const int chunk = (max(R, rcap) + nsplit - 1) / nsplit;
   const int r_lo = min(R, split * chunk), r_hi = min(R, r_lo + chunk);
 
   float m[G], l[G], acc[G][EPL];
@@ -1390,8 +1476,16 @@ __global__ void __launch_bounds__(kAttendValuThreads)
                           &s_last);
 }
 
+// Attended rows a call expects per (b, g) at most: max_rows selected rows
+// plus a full local buffer. Rows are dealt to workgroups in chunks of
+// ceil(max(R, bound) / nsplit), so calls with equal max_rows split equal rows
+// identically, and a chunk's first row is known before R is.
+int attend_row_bound(const kv_pool *pool, int max_rows) {
+  return (max_rows > 0 ? max_rows : 0) + (pool->buf_cap > 0 ? pool->buf_cap : 0);
+}
+
 int attend_num_splits(const kv_pool *pool, int max_rows) {
-  const long rows = (long)(max_rows > 0 ? max_rows : 0) + (pool->buf_cap > 0 ? pool->buf_cap : 0);
+  const long rows = attend_row_bound(pool, max_rows);
   const long bh = (long)pool->batch * pool->n_kv_heads;
   long by_rows = (rows + kAttendMinRowsPerSplit - 1) / kAttendMinRowsPerSplit;
   long by_grid = (kAttendTargetBlocks + bh - 1) / bh;
@@ -1404,28 +1498,27 @@ int attend_num_splits(const kv_pool *pool, int max_rows) {
 template <typename T, int D>
 static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, float scale_log2,
                                  const int32_t *sel_units, const int32_t *sel_spans,
-                                 int sel_cap, const int32_t *sel_n, int nsplit, float *out,
-                                 float *partials, int32_t *counters, const AttendFetch &fx,
-                                 hipStream_t s) {
+                                 int sel_cap, const int32_t *sel_n, int nsplit, int rcap,
+                                 float *out, float *partials, int32_t *counters,
+                                 const AttendFetch &fx, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
   if (sizeof(T) != 2 && fx.flag != nullptr) return KV_ERR_UNSUPPORTED;
-#define KVC_ATT(GG)                                                                             \
-  do {                                                                                          \
-    if constexpr (sizeof(T) == 2)                                                               \
-      if (pool->buf_k != nullptr)                                                               \
-        k_gather_attend_mfma<D, GG, true><<<grid, kAttendThreads, 0, s>>>(                      \
-            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,   \
-            out, partials, counters, fx);                                                       \
-      else                                                                                      \
-        k_gather_attend_mfma<D, GG, false><<<grid, kAttendThreads, 0, s>>>(                     \
-            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n,   \
-            out, partials, counters, fx);                                                       \
-    else                                                                                        \
-      k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                       \
-          *pool, (const T *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, out,       \
-          partials,                                                                             \
-          counters);                                                                            \
+#define KVC_ATT(GG)                                                                           \
+  do {                                                                                        \
+    if constexpr (sizeof(T) == 2)                                                             \
+      if (pool->buf_k != nullptr)                                                             \
+        k_gather_attend_mfma<D, GG, true><<<grid, kAttendThreads, 0, s>>>(                    \
+            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, \
+            rcap, out, partials, counters, fx);                                               \
+      else                                                                                    \
+        k_gather_attend_mfma<D, GG, false><<<grid, kAttendThreads, 0, s>>>(                   \
+            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, \
+            rcap, out, partials, counters, fx);                                               \
+    else                                                                                      \
+      k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                     \
+          *pool, (const T *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, rcap,    \
+          out, partials, counters);                                                           \
   } while (0)
   switch (G) {
     case 1: KVC_ATT(1); break;
@@ -1440,12 +1533,13 @@ static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, flo
 
 static kv_status attend_launch(const kv_pool *pool, const void *q, int hq, float scale,
                                const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
-                               const int32_t *sel_n, int nsplit, float *out, float *partials,
-                               int32_t *counters, const AttendFetch &fx, hipStream_t s) {
+                               const int32_t *sel_n, int nsplit, int rcap, float *out,
+                               float *partials, int32_t *counters, const AttendFetch &fx,
+                               hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = exp2(x log2 e)
 #define KVC_AD(T, D)                                                                          \
-  attend_dispatch<T, D>(pool, q, hq, sl2, sel_units, sel_spans, sel_cap, sel_n, nsplit, out, \
-                        partials, counters, fx, s)
+  attend_dispatch<T, D>(pool, q, hq, sl2, sel_units, sel_spans, sel_cap, sel_n, nsplit, rcap, \
+                        out, partials, counters, fx, s)
   kv_status st;
   if (pool->dtype == KV_BF16)
     st = pool->head_dim == 128 ? KVC_AD(uint16_t, 128) : KVC_AD(uint16_t, 64);
@@ -1457,10 +1551,10 @@ static kv_status attend_launch(const kv_pool *pool, const void *q, int hq, float
 
 kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
                                const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
-                               const int32_t *sel_n, int nsplit, float *out, float *partials,
-                               int32_t *counters, hipStream_t s) {
+                               const int32_t *sel_n, int nsplit, int rcap, float *out,
+                               float *partials, int32_t *counters, hipStream_t s) {
   const AttendFetch off{};
-  return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, out,
+  return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, rcap, out,
                        partials, counters, off, s);
 }
 
@@ -1574,17 +1668,18 @@ kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32
 kv_status launch_fetch_attend(const kv_pool *pool, const void *q, int hq, float scale,
                               const uint8_t *flag, const int32_t *sel_units,
                               const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
-                              int nsplit, const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
-                              float *out, float *partials, int32_t *counters, hipStream_t s) {
+                              int nsplit, int rcap, const kv_pool *dst, int32_t *dst_spans,
+                              int32_t *dst_n, float *out, float *partials, int32_t *counters,
+                              hipStream_t s) {
   if (pool->dtype != KV_BF16) {
     kv_status st = launch_fetch_rows(pool, flag, sel_units, sel_spans, sel_cap, sel_n, dst,
                                      dst_spans, dst_n, s);
     if (st != KV_OK) return st;
-    return launch_gather_attend(dst, q, hq, scale, nullptr, dst_spans, 1, dst_n, nsplit, out,
-                                partials, counters, s);
+    return launch_gather_attend(dst, q, hq, scale, nullptr, dst_spans, 1, dst_n, nsplit, rcap,
+                                out, partials, counters, s);
   }
   AttendFetch fx{flag, dst->k, dst->v, dst->row_cap, dst_spans, dst_n};
-  return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, out,
+  return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, rcap, out,
                        partials, counters, fx, s);
 }
 

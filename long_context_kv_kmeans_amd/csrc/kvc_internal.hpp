@@ -209,10 +209,11 @@ kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         const void *q_prev, float tau, uint8_t *flag_out, float *r_out,
                         hipStream_t s);
 int attend_num_splits(const kv_pool *pool, int max_rows);
+int attend_row_bound(const kv_pool *pool, int max_rows);
 kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
                                const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,
-                               const int32_t *sel_n, int nsplit, float *out, float *partials,
-                               int32_t *counters, hipStream_t s);
+                               const int32_t *sel_n, int nsplit, int rcap, float *out,
+                               float *partials, int32_t *counters, hipStream_t s);
 int fetch_num_blocks(const kv_pool *dst);
 kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32_t *sel_units,
                             const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
@@ -221,7 +222,8 @@ kv_status launch_fetch_rows(const kv_pool *src, const uint8_t *flag, const int32
 kv_status launch_fetch_attend(const kv_pool *pool, const void *q, int hq, float scale,
                               const uint8_t *flag, const int32_t *sel_units,
                               const int32_t *sel_spans, int sel_cap, const int32_t *sel_n,
-                              int nsplit, const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n,
-                              float *out, float *partials, int32_t *counters, hipStream_t s);
+                              int nsplit, int rcap, const kv_pool *dst, int32_t *dst_spans,
+                              int32_t *dst_n, float *out, float *partials, int32_t *counters,
+                              hipStream_t s);
 
 }  // namespace kvc

@@ -159,6 +159,9 @@ def test_host_pool_decode_matches_hbm_pool(cfg_idx, over, steps, seqs):
                                                sel_cap, fetch=True),
         "hbm, working set": gpu_decode(hbm, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap,
                                        fused=True, spans=True, fetch=True),
+        "hbm, fetch fused into attention": gpu_decode(hbm, qd, cfg.tau, cfg.budget, cfg.scale,
+                                                      sel_cap, fused=True, spans=True,
+                                                      fetch="fused"),
         "host, fetch fused into attention": gpu_decode(host, qd, cfg.tau, cfg.budget, cfg.scale,
                                                        sel_cap, fused=True, spans=True,
                                                        fetch="fused"),
@@ -173,13 +176,17 @@ def test_host_pool_decode_matches_hbm_pool(cfg_idx, over, steps, seqs):
     assert int(host.status.item()) == 0 and int(hbm.status.item()) == 0
 
 
-@pytest.mark.parametrize("dtype,d,hq,cap", [("bf16", 128, 8, 4096), ("bf16", 64, 4, 4096),
-                                             ("bf16", 128, 16, 300), ("fp32", 128, 4, 4096)])
-def test_fetch_attend_equals_fetch_then_attend(dtype, d, hq, cap):
+@pytest.mark.parametrize("dtype,d,hq,cap,max_rows", [
+    ("bf16", 128, 8, 4096, 4096), ("bf16", 64, 4, 4096, 4096), ("bf16", 128, 16, 300, 4096),
+    ("fp32", 128, 4, 4096, 4096), ("bf16", 128, 8, 4096, 200), ("bf16", 128, 4, 4096, 1000)])
+def test_fetch_attend_equals_fetch_then_attend(dtype, d, hq, cap, max_rows):
     # kv_fetch_attend == kv_fetch_selected + kv_gather_attend(working set): working
     # set, spans, counts, status and output bit for bit, over a retrieval step and
     # a reuse step (flags 1,0,1 then 0,0,0), with a working set too small for
-    # some selections when cap = 300
+    # some selections when cap = 300. On the reuse step the attention requests
+    # its first working-set rows before it knows how many there are; max_rows =
+    # 200 makes most spans longer than that bound (the general path), 1000 puts
+    # chunk ends inside the spans and empty chunks past them.
     B, H, row_cap, unit_cap, sel_cap = 3, 2, 3000, 150, 96
     pool, start, size = _ragged_pool(B, H, d, dtype, row_cap, unit_cap, True, seed=3)
     g = np.random.default_rng(5)
@@ -188,7 +195,6 @@ def test_fetch_attend_equals_fetch_then_attend(dtype, d, hq, cap):
     su = torch.from_numpy(sel.astype(np.int32)).cuda()
     sn = torch.from_numpy(sel_n).cuda()
     q = torch.from_numpy(g.standard_normal((B, hq, d), np.float32)).to(pool.dtype).cuda()
-    max_rows = 4096
     res = []
     for fused in (False, True):
         pool.status.zero_()
