@@ -968,6 +968,9 @@ struct AttendFetch {
   int cap;
   int32_t *spans;       // [BH][2]
   int32_t *count;       // [BH]
+  int reread;           // retrieval step: 1 = attend the working set once the copy has
+                        // landed (pool rows behind the host link), 0 = attend the pool
+                        // rows the copy has just read (pool in device memory)
 };
 
 // Rows [r_lo, r_hi) of the concatenated selection (n units, r_sel rows, in
@@ -1208,7 +1211,10 @@ __global__ void __launch_bounds__(kAttendThreads)
   if (fetching) {
     // Retrieval step of working-set mode: this workgroup copies the rows it
     // is about to attend, [r_lo, r_hi) of the selection, from the pool into
-    // the working set, then attends over them there like any later step.
+    // the working set, then attends over them: for a pool in device memory
+    // over the same pool rows, which the copy has just brought into L2 (the
+    // stores need not land first); for a pool in host memory over the
+    // working set, so that no row crosses the host link twice.
     if (split == 0 && tid == 0) {
       fx.spans[2 * bg] = 0;
       fx.spans[2 * bg + 1] = r_sel;
@@ -1219,16 +1225,19 @@ __global__ void __launch_bounds__(kAttendThreads)
     }
     attend_copy_rows<NT, D>(pool, bg, fx, min(r_lo, r_sel), min(r_hi, r_sel), n, r_sel, s_psum,
                             s_start, s_rowtab);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the copies are written
-    __syncthreads();
-    if (tid == 0) {  // the selection is now the working set's one span
-      s_start[0] = 0;
-      s_psum[0] = 0;
+    if (fx.reread) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the copies are written
+      __syncthreads();
+      if (tid == 0) {  // the selection is now the working set's one span
+        s_start[0] = 0;
+        s_psum[0] = 0;
+      }
+      n = 1;
+      __syncthreads();
     }
-    n = 1;
-    __syncthreads();
   }
-  const int row_cap = ws_mode ? fx.cap : pool.row_cap;
+  const bool read_ws = ws_mode && (!fetching || fx.reread);
+  const int row_cap = read_ws ? fx.cap : pool.row_cap;
 
   // Online softmax state. m_run / l_run: per query head `col`, identical in
   // the four lanes col, col+16, col+32, col+48. acc: p.v partial sums of this
@@ -1241,9 +1250,9 @@ __global__ void __launch_bounds__(kAttendThreads)
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
   const uint16_t *kbase =
-      static_cast<const uint16_t *>(ws_mode ? fx.k : pool.k) + (size_t)bg * row_cap * D;
+      static_cast<const uint16_t *>(read_ws ? fx.k : pool.k) + (size_t)bg * row_cap * D;
   const uint16_t *vbase =
-      static_cast<const uint16_t *>(ws_mode ? fx.v : pool.v) + (size_t)bg * row_cap * D;
+      static_cast<const uint16_t *>(read_ws ? fx.v : pool.v) + (size_t)bg * row_cap * D;
   const int ring = BUF ? pool.buf_ring : 0;
   const uint16_t *kbuf = nullptr, *vbuf = nullptr;
   if (BUF) {
@@ -1678,7 +1687,14 @@ kv_status launch_fetch_attend(const kv_pool *pool, const void *q, int hq, float 
     return launch_gather_attend(dst, q, hq, scale, nullptr, dst_spans, 1, dst_n, nsplit, rcap,
                                 out, partials, counters, s);
   }
-  AttendFetch fx{flag, dst->k, dst->v, dst->row_cap, dst_spans, dst_n};
+  // Where the pool's rows live decides how a retrieval step reads them back.
+  hipPointerAttribute_t attr;
+  int reread = 1;
+  if (hipPointerGetAttributes(&attr, pool->k) == hipSuccess)
+    reread = attr.type == hipMemoryTypeDevice ? 0 : 1;
+  else
+    (void)hipGetLastError();
+  AttendFetch fx{flag, dst->k, dst->v, dst->row_cap, dst_spans, dst_n, reread};
   return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, rcap, out,
                        partials, counters, fx, s);
 }
