@@ -146,22 +146,27 @@ def test_decode_loop_parity(cfg_idx, over, steps, seqs):
     assert st["retrievals"] >= 1
 
 
-def test_decode_full_size_cfg1_benchmark_path():
+@pytest.mark.parametrize("attend", ["wset", "pool"])
+def test_decode_full_size_cfg1_benchmark_path(attend):
     # the Qwen3-8B-shaped layer at full size (8 KV heads x 32768 keys, C = 2048, 256 steps)
     # through the calls the benchmark times: kv_boundary_select with row spans, then
-    # kv_gather_attend on the spans. Two Lloyd rounds suffice: the clustering only sets up
-    # the pool, and full-size K-means has its own sampled test.
+    # kv_fetch_attend over an HBM working set (the default) or kv_gather_attend on the
+    # spans (bench.py --attend pool). Two Lloyd rounds suffice: the clustering only sets
+    # up the pool, and full-size K-means has its own sampled test.
     cfg = wl.get_config(1, iters=2)
-    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True)
+    kw = dict(fetch="fused") if attend == "wset" else {}
+    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True, **kw)
     assert st["retrievals"] >= 2
 
 
-def test_decode_full_size_cfg4_batch16_benchmark_path():
+@pytest.mark.parametrize("attend", ["wset", "pool"])
+def test_decode_full_size_cfg4_batch16_benchmark_path(attend):
     # batched decode at full size: 16 sequences x 8 KV heads x 32768 keys in one launch,
     # budget 1024; sequences 0 and 9 carry the oracle's clustering and are checked
     cfg = wl.get_config(4, iters=2)
+    kw = dict(fetch="fused") if attend == "wset" else {}
     st = _run(cfg, 128, list(range(16)), compare_every=8, check=[0, 9], fused=True,
-              spans=True)
+              spans=True, **kw)
     assert st["retrievals"] >= 2
 
 
