@@ -335,8 +335,12 @@ kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int3
  * with the same working set, spans, status and output bit for bit. On a
  * retrieval step (flag[b] != 0) each attention workgroup copies the rows it
  * is about to attend from the pool into the working set and attends over
- * them there; on other steps it reads the working set only, so a step
- * without retrieval costs one launch. fp32 pools run the two launches.
+ * them (over the pool rows it has just read when the pool is in device
+ * memory, over the working set when it is in host memory, so that no row
+ * crosses the host link twice); on other steps it reads the working set
+ * only, requesting its first rows together with the flag and the span, so
+ * a step without retrieval costs one launch and one memory round trip
+ * before the rows arrive. fp32 pools run the two launches.
  * A pool with decode segments (buf_cap > 0; bf16, with buf_k / buf_v set)
  * is supported too: the attended rows are then the working set followed by
  * the local buffer, read from the pool's HBM copy, i.e. exactly the rows
