@@ -199,6 +199,17 @@ def test_decode_long_output_segments():
     _run(cfg, 3000, [0], compare_every=7)
 
 
+def test_decode_long_output_benchmark_path():
+    # the long-output workload through the benchmark's calls (kv_boundary_segment_append,
+    # kv_select with row spans, kv_gather_attend on the spans) for 6000 of its 16384
+    # steps: ~120 boundaries, the 1024-token buffer full and evicting segments from step
+    # ~1024 on. (All 16384 steps take over two minutes, most of it the oracle's per-step
+    # exact attention.)
+    cfg = wl.get_config(2, iters=3)
+    st = _run(cfg, 6000, [0], compare_every=64, fused_append=True, spans=True)
+    assert st["retrievals"] >= 60
+
+
 @pytest.mark.parametrize("cfg_idx,over,steps,seqs", [
     (0, {}, 64, [0]),
     (1, dict(n_keys=8192, n_clusters=512, n_components=128, iters=3), 96, [0]),
