@@ -414,35 +414,42 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
 
 // ---------------------------------------------------------------- update
 // Stable counting sort of keys by label, in three passes:
-//  k_rank_hist -- one wave per chunk of 1024 keys: the rank of each key
-//                 among earlier keys of the chunk with the same label (label
-//                 equality found with one ballot per label bit) and the
-//                 chunk's label histogram;
+//  k_rank_hist -- one workgroup per chunk of 1024 keys, its NW waves taking
+//                 consecutive parts: the rank of each key among earlier keys
+//                 of the chunk with the same label (within a part, label
+//                 equality found with one ballot per label bit; then the
+//                 label's counts in the earlier parts, added in part order)
+//                 and the chunk's label histogram;
 //  k_colscan   -- per label, exclusive prefix of the histograms over chunks
 //                 and the label's total;
 //  k_startscan -- exclusive scan of totals over labels (cluster starts);
 //  k_scatter   -- perm[start[a] + chunk_prefix[a] + rank] = key.
-__global__ void __launch_bounds__(64) k_rank_hist(const int32_t *__restrict__ labels,
-                                                  int32_t *__restrict__ rank,
-                                                  int32_t *__restrict__ hist, int n, int c,
-                                                  int nbits, int nchunk) {
-  constexpr int SUB = kRankChunk / 64;
-  extern __shared__ int32_t cnt[];
-  const int bh = blockIdx.y, ch = blockIdx.x, lane = threadIdx.x;
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict__ labels,
+                                                       int32_t *__restrict__ rank,
+                                                       int32_t *__restrict__ hist, int n, int c,
+                                                       int nbits, int nchunk) {
+  constexpr int KPW = kRankChunk / NW;  // keys per wave: wave w takes the w-th part of the chunk
+  constexpr int SUB = KPW / 64;
+  extern __shared__ int32_t cnt[];      // [NW][c]: label counts of each wave's part
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t *lab = labels + (size_t)bh * n;
-  const int base = ch * kRankChunk;
+  const int base = ch * kRankChunk + wave * KPW;
   int a[SUB];
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub) {
     const int i = base + sub * 64 + lane;
     a[sub] = i < n ? lab[i] : -1;
   }
-  for (int k = lane; k < c; k += 64) cnt[k] = 0;
+  for (int k = threadIdx.x; k < NW * c; k += 64 * NW) cnt[k] = 0;
   __syncthreads();
+  // rank within the wave's part: earlier keys of the part with the same label
+  int32_t *mine = cnt + wave * c;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int lr[SUB];
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub) {
-    const int i = base + sub * 64 + lane;
     const bool valid = a[sub] >= 0;
     const int v = valid ? a[sub] : 0;
     uint64_t mask = __ballot(valid);
@@ -451,15 +458,31 @@ __global__ void __launch_bounds__(64) k_rank_hist(const int32_t *__restrict__ la
       const uint64_t m = __ballot(bit);
       mask &= bit ? m : ~m;
     }
+    lr[sub] = 0;
     if (valid) {
-      const int r = cnt[v] + __popcll(mask & below);
-      rank[(size_t)bh * n + i] = r;
-      if ((mask >> lane) == 1ull) cnt[v] += __popcll(mask);
+      lr[sub] = mine[v] + __popcll(mask & below);
+      if ((mask >> lane) == 1ull) mine[v] += __popcll(mask);
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // + the same label's keys in the chunk's earlier parts; the chunk histogram
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) {
+    const int i = base + sub * 64 + lane;
+    if (a[sub] >= 0) {
+      int r = lr[sub];
+      for (int w = 0; w < wave; ++w) r += cnt[w * c + a[sub]];
+      rank[(size_t)bh * n + i] = r;
+    }
   }
   int32_t *hrow = hist + ((size_t)bh * nchunk + ch) * c;
-  for (int k = lane; k < c; k += 64) hrow[k] = cnt[k];
+  for (int k = threadIdx.x; k < c; k += 64 * NW) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += cnt[w * c + k];
+    hrow[k] = t;
+  }
 }
 
 __global__ void k_colscan(int32_t *__restrict__ hist, int32_t *__restrict__ tot, int c,
@@ -659,8 +682,17 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   w += align_up((size_t)bh * c * 4, 256);
   int32_t *perm = reinterpret_cast<int32_t *>(w);
 
-  k_rank_hist<<<dim3(nchunk, bh), 64, (size_t)c * 4, s>>>(labels, rank, hist, n, c,
-                                                          ceil_log2(c), nchunk);
+  // a chunk's label counts stay within 64 KB of LDS: 4 waves per chunk up to 4096
+  // labels, 2 up to 8192, else 1
+  if (c <= 4096)
+    k_rank_hist<4><<<dim3(nchunk, bh), 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
+                                                                    ceil_log2(c), nchunk);
+  else if (c <= 8192)
+    k_rank_hist<2><<<dim3(nchunk, bh), 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
+                                                                    ceil_log2(c), nchunk);
+  else
+    k_rank_hist<1><<<dim3(nchunk, bh), 64, (size_t)c * 4, s>>>(labels, rank, hist, n, c,
+                                                               ceil_log2(c), nchunk);
   k_colscan<<<dim3((c + 255) / 256, bh), 256, 0, s>>>(hist, tot, c, nchunk);
   k_startscan<<<bh, 1024, 0, s>>>(tot, start, counts, c);
   k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, perm, n, c,
