@@ -635,19 +635,20 @@ kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
 
 // ---------------------------------------------------------------- gather + attend
 // Rows of (b, g): the selected units' row ranges (CSR order of the selection
-// list) followed by the local-buffer rows. A workgroup takes one contiguous
-// share of those rows and folds them into an online softmax for the group's
-// G query heads; waves merge through LDS. With one share per (b, g) the
-// workgroup writes the output directly; otherwise it publishes (m, l, acc)
-// and the last workgroup merges the shares in order.
+// list) followed by the local-buffer rows, or the working set's contiguous
+// rows. A workgroup takes one contiguous share of those rows (shares of
+// ceil(max(R, bound) / splits) rows, bound = max_rows + the buffer's
+// capacity) and folds them into an online softmax for the group's G query
+// heads; waves merge through LDS. With one share per (b, g) the workgroup
+// writes the output directly; otherwise it publishes (m, l, acc) and the
+// last workgroup merges the shares in order.
 //
 // bf16 keys: q.k for 16 rows x 16 query columns (G used) is one
 // v_mfma_f32_16x16x32_bf16 chain over the head dimension; the probabilities
-// go through LDS to the lanes holding the V rows, which accumulate p.v on
-// the VALU. fp32 keys take an all-VALU variant.
+// reach the lanes holding the V rows by row broadcasts, and those lanes
+// accumulate p.v on the VALU. fp32 keys take an all-VALU variant.
 constexpr int kAttendMinRowsPerSplit = 128;
 constexpr int kAttendTargetBlocks = 256;  // one 8-wave workgroup per CU
-constexpr int kAttendPiece = 256;         // rows resolved per row-table pass
 
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
   return m_old == -INFINITY ? 0.f : exp2f(m_old - m_new);
