@@ -93,23 +93,44 @@ def profiled_traffic(workload):
     return data
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, q, lloyd_iters, dk=None, dv=None):
-    """Time the oracle on a bounded sample and scale to one whole step."""
+    """Time the oracle on a bounded sample and scale to one whole step.
+
+    The sample is Lloyd on one KV head of layer 0 (all of its keys, all C
+    clusters, ``lloyd_iters`` of the rounds), its pack, and 16 decode steps of
+    that head; the figure is extrapolated to every head, round, decode step
+    and layer of the workload. numpy's BLAS runs with the threads it was
+    given (OMP_NUM_THREADS); ``cores`` reports those."""
     import numpy as np
 
     from oracle import kmeans as okm
     from oracle.decode import run_decode
 
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        cores = affinity
     keys0, vals0, init0 = inp["keys"][0, 0], inp["values"][0, 0], inp["init_idx"][0, 0]
     t0 = time.perf_counter()
     o = okm.lloyd(keys0, init0, lloyd_iters, mode="parity", dtype=cfg.dtype)
     t_lloyd = (time.perf_counter() - t0) * cfg.iters / lloyd_iters
+    t0 = time.perf_counter()
     pack = okm.pack(keys0, vals0, o["labels"], o["centroids"], cfg.dtype)
+    t_pack = time.perf_counter() - t0
     dec_steps = 16
     t0 = time.perf_counter()
     seg = {} if dk is None else dict(buf_cap=cfg.buf_cap, dec_k=dk[:dec_steps, 0, :1],
@@ -118,19 +139,22 @@ def cpu_baseline(cfg, inp, q, lloyd_iters, dk=None, dv=None):
                **seg)
     t_dec = (time.perf_counter() - t0) / dec_steps  # one KV head, one step
     heads = cfg.batch * cfg.n_kv_heads
-    t_step = cfg.layers * (heads * t_lloyd + cfg.steps * heads * t_dec)
+    t_step = cfg.layers * (heads * (t_lloyd + t_pack) + cfg.steps * heads * t_dec)
     return {
         "value": cfg.layers * heads * cfg.n_keys / t_step,
         "unit": "keys/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"numpy fp64 oracle: Lloyd on 1 of {heads} KV heads ({cfg.n_keys} keys, "
-                   f"C={cfg.n_clusters}, {lloyd_iters} of {cfg.iters} rounds timed) + {dec_steps} "
-                   f"decode steps of 1 KV head; scaled to {heads} heads, {cfg.iters} rounds, "
-                   f"{cfg.steps} decode steps" + (f", {cfg.layers} layers" if cfg.layers > 1
-                                                 else "")),
+        "sample": (f"numpy fp64 oracle on layer 0, KV head 0 of {heads}: Lloyd over its "
+                   f"{cfg.n_keys} keys with C={cfg.n_clusters} ({lloyd_iters} of {cfg.iters} "
+                   f"rounds timed), the pack, and {dec_steps} of {cfg.steps} decode steps; "
+                   f"scaled to {heads} heads, {cfg.iters} rounds, {cfg.steps} decode steps"
+                   + (f" and {cfg.layers} layers" if cfg.layers > 1 else "")),
+        "sample_s": t_lloyd * lloyd_iters / cfg.iters + t_pack + t_dec * dec_steps,
         "step_s_extrapolated": t_step,
         "decode_us_per_layer_step": t_dec * heads * 1e6,
+        "affinity_cores": affinity,
+        "cpu_model": cpu_model(),
     }
 
 
@@ -206,12 +230,23 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload (default 3: 36 layers x 131072 keys per KV head, the largest "
+                         "that fits one GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-lloyd-iters", type=int, default=3)
+    ap.add_argument("--cpu-lloyd-iters", type=int, default=None,
+                    help="Lloyd rounds the CPU oracle is timed on (default: 1 when a round "
+                         "takes more than ~2^28 key-cluster pairs, else 3)")
+    ap.add_argument("--gen-threads", type=int, default=None,
+                    help="host threads drawing the synthetic inputs (default: min(16, cores))")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="run fewer decode steps than the workload's (counter-profiling runs "
+                         "only; the printed line then names the override)")
     ap.add_argument("--assign-reps", type=int, default=20)
     ap.add_argument("--attend-reps", type=int, default=100)
     ap.add_argument("--copy-calibration-mib", type=int, default=64)
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="size of the write that evicts the caches before each cold launch")
     ap.add_argument("--pool", choices=("hbm", "host", "host-direct"), default="hbm",
                     help="where the pool's K/V rows live: hbm; host (pinned host memory, "
                          "retrieval steps fetch the selected rows into an HBM working set "
@@ -248,6 +283,8 @@ def main():
     kvc.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     cfg = wl.get_config(args.config)
+    if args.decode_steps is not None:
+        cfg = cfg.replace(steps=args.decode_steps)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     e = 2 if cfg.dtype == "bf16" else 4
     B, H, N, d = cfg.batch, cfg.n_kv_heads, cfg.n_keys, cfg.head_dim
@@ -276,22 +313,31 @@ def main():
     class Layer:
         pass
 
+    # Every layer draws its own prefill keys/values and query walk; the
+    # (sequence, head) streams of a layer are drawn on several host threads and
+    # the next layers' are drawn while the current one is uploaded.
+    import concurrent.futures as cf
+
+    gen_threads = args.gen_threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    per_layer = max(1, gen_threads // 2) if L > 1 else gen_threads
+
+    def gen_layer(li):
+        return wl.layer_inputs(cfg, li, threads=per_layer), wl.layer_queries(cfg, li)[0]
+
     layers = []
     t_gen = time.perf_counter()
+    gen_ex = cf.ThreadPoolExecutor(max_workers=2 if L > 1 else 1)
+    pending = [gen_ex.submit(gen_layer, li) for li in range(min(L, 2))]
     for li in range(L):
-        # Multi-layer workloads share layer 0's prefill keys/values (drawing them
-        # takes seconds per layer on the host); every layer still clusters them
-        # into a pool of its own and has its own query walk.
-        inp_l = wl.layer_inputs(cfg, li) if li == 0 else None
-        q_l, _ = wl.layer_queries(cfg, li)
+        inp_l, q_l = pending[li].result()
+        pending[li] = None
+        if li + 2 < L:
+            pending.append(gen_ex.submit(gen_layer, li + 2))
         y = Layer()
         y.assign_in = None
-        if li == 0:
-            y.keys = torch.from_numpy(inp_l["keys"]).to(tdt).cuda()
-            y.vals = torch.from_numpy(inp_l["values"]).to(tdt).cuda()
-            y.init = torch.from_numpy(inp_l["init_idx"]).cuda()
-        else:
-            y.keys, y.vals, y.init = layers[0].keys, layers[0].vals, layers[0].init
+        y.keys = torch.from_numpy(inp_l["keys"]).cuda().to(tdt)
+        y.vals = torch.from_numpy(inp_l["values"]).cuda().to(tdt)
+        y.init = torch.from_numpy(inp_l["init_idx"]).cuda()
         y.q = torch.from_numpy(q_l).to(tdt).cuda()  # [T, B, Hq, d]
         if seg:
             dk, dv = wl.layer_decode_kv(cfg, li)
@@ -310,22 +356,28 @@ def main():
             y.init = torch.from_numpy(np.broadcast_to(
                 (np.arange(C) * page).astype(np.int32), (B, H, C)).copy()).cuda()
         y.labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
-        y.ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
         y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
         y.sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
         y.sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
         y.sel_rows = torch.zeros(B, H, dtype=torch.int32, device="cuda")
         y.sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device="cuda")
         y.out = torch.zeros(B, Hq, d, dtype=torch.float32, device="cuda")
-        y.ws_sel = kvc.workspace(kvc.kv_select_workspace(y.pool, Hq))
-        y.ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(y.pool, Hq, cfg.budget))
+        if li == 0:  # the layers run one after another on one stream: one set of workspaces
+            ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
+            ws_sel = kvc.workspace(kvc.kv_select_workspace(y.pool, Hq))
+            ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(y.pool, Hq, cfg.budget))
+        y.ws_build, y.ws_sel, y.ws_att = ws_build, ws_sel, ws_att
         layers.append(y)
-        if li == 0:
-            inp, q_np = inp_l, q_l  # layer 0 feeds the CPU baseline
+        if li == 0:  # layer 0, sequence 0, KV head 0 feeds the CPU baseline
+            inp = {k: np.ascontiguousarray(inp_l[k][:1, :1]) for k in ("keys", "values",
+                                                                       "init_idx")}
+            q_np = q_l
             dk0, dv0 = (dk, dv) if seg else (None, None)
         del inp_l, q_l
         if L > 1 and (li + 1) % 6 == 0:
-            log(f"inputs of {li + 1}/{L} layers generated ({time.perf_counter() - t_gen:.0f}s)")
+            log(f"inputs of {li + 1}/{L} layers generated and uploaded "
+                f"({time.perf_counter() - t_gen:.0f}s)")
+    gen_ex.shutdown()
     log(f"inputs generated in {time.perf_counter() - t_gen:.1f}s")
     y0 = layers[0]
     keys, pool, sel, sel_n, sel_rows, sel_spans = (y0.keys, y0.pool, y0.sel, y0.sel_n,
@@ -460,23 +512,45 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    flush_buf = torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+
+    def single_launch_ms(fn, reps, cold):
+        """Mean GPU time of fn measured launch by launch (HIP events right
+        around each launch). With `cold`, a write of `--flush-mib` MiB runs
+        before every launch, outside its interval, so that the launch finds
+        its data in neither the L2s nor the Infinity Cache."""
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            fn()
+            for i, (a, b) in enumerate(pairs):
+                if cold:
+                    flush_buf.fill_(float(i))
+                a.record(stream)
+                fn()
+                b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
     att_rows = int(sel_rows.sum().item())
     if fetch:  # a step without retrieval: the working set (+ the local buffer's HBM copy)
         zeros = torch.zeros(B, dtype=torch.uint8, device="cuda")
-        att_ms = launch_ms(lambda: kvc.kv_fetch_attend(pool, y0.q[T - 1], cfg.scale, zeros, None,
-                                                       sel_n, cfg.budget, y0.wset, y0.wspans,
-                                                       y0.wn, y0.out, ws=y0.ws_att,
-                                                       sel_spans=sel_spans),
-                           args.attend_reps)
+
+        def att_fn():
+            kvc.kv_fetch_attend(pool, y0.q[T - 1], cfg.scale, zeros, None, sel_n, cfg.budget,
+                                y0.wset, y0.wspans, y0.wn, y0.out, ws=y0.ws_att,
+                                sel_spans=sel_spans)
         att_spans = int(y0.wn.sum().item())
     else:
-        att_ms = launch_ms(lambda: kvc.kv_gather_attend(pool, y0.q[T - 1], cfg.scale, None,
-                                                        sel_n, cfg.budget, y0.out, ws=y0.ws_att,
-                                                        sel_spans=sel_spans),
-                           args.attend_reps)
+        def att_fn():
+            kvc.kv_gather_attend(pool, y0.q[T - 1], cfg.scale, None, sel_n, cfg.budget, y0.out,
+                                 ws=y0.ws_att, sel_spans=sel_spans)
         att_spans = sel_units_n
+    att_ms = launch_ms(att_fn, args.attend_reps)
+    att_warm1_ms = single_launch_ms(att_fn, args.attend_reps, cold=False)
+    att_cold_ms = single_launch_ms(att_fn, args.attend_reps, cold=True)
     att_buf = int((pool.n_rows - pool.buf_begin).sum().item()) * H if seg else 0
     att_bytes = ((att_rows + att_buf) * 2 * d * e  # selected (and local-buffer) K and V rows
                  + B * Hq * d * e              # queries
@@ -520,15 +594,55 @@ def main():
     ws_asg = kvc.workspace(kvc.lib().kv_kmeans_assign_workspace(B * H, C, d, kvc.dtype_code(tdt)))
     with torch.cuda.stream(stream):
         kvc.kv_kmeans_prepare(cents, tdt, ws_asg)
-    asg_ms = launch_ms(lambda: kvc.kv_kmeans_assign_prepared(k3, cents, lab2, ws_asg),
-                       args.assign_reps)
+    asg_fn = lambda: kvc.kv_kmeans_assign_prepared(k3, cents, lab2, ws_asg)  # noqa: E731
+    asg_ms = launch_ms(asg_fn, args.assign_reps)
     flops = 2.0 * B * H * N * C * d
     achieved = flops / (asg_ms * 1e-3) / 1e12
     share = {"k_gather_attend": T * L * att_ms / ms_step,
-             "k_assign_mfma": cfg.iters * L * asg_ms / ms_step}
+             "k_assign_mfma": (0 if page is not None else cfg.iters) * L * asg_ms / ms_step}
+
+    # What this machine reaches on plain work: a 1 GiB device copy (bytes read +
+    # written) and a large bf16 GEMM through torch (hipBLASLt).
+    big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    big2 = torch.empty_like(big)
+    copy_ms = launch_ms(lambda: big2.copy_(big), 10)
+    del big, big2
+    ga = torch.randn(8192, 8192, device="cuda").bfloat16()
+    gb = torch.randn(8192, 8192, device="cuda").bfloat16()
+    gemm_ms = launch_ms(lambda: torch.matmul(ga, gb), 10)
+    del ga, gb
+    achievable = {"copy_gbs": 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
+                  "gemm_bf16_tflops": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
+                  "how": "1 GiB device-to-device copy (read + write bytes); "
+                         "8192^3 bf16 torch.matmul"}
 
     # the committed counter profile covers the default path only
-    traffic = profiled_traffic(cfg.name) if not variant and args.attend == "wset" else None
+    traffic = profiled_traffic(cfg.name) if (not variant and args.attend == "wset"
+                                             and args.decode_steps is None) else None
+    roof_attend = {"bound": "hbm" if args.pool != "host-direct" else "host-link",
+                   "kernel": ("k_gather_attend_mfma (kv_fetch_attend, working set, step "
+                              "without retrieval)" if fetch else
+                              "k_gather_attend_mfma (kv_gather_attend)"),
+                   "achieved": att_gbs, "peak": att_peak, "unit": "GB/s",
+                   "frac": att_gbs / att_peak,
+                   "traffic": traffic["k_gather_attend_mfma"]["bytes"] if traffic else None,
+                   "bytes_per_launch": att_bytes, "avg_launch_ms": att_ms,
+                   "warm_single_launch_ms": att_warm1_ms,
+                   "cold": {"avg_launch_ms": att_cold_ms,
+                            "achieved": att_bytes / (att_cold_ms * 1e-3) / 1e9,
+                            "frac": att_bytes / (att_cold_ms * 1e-3) / 1e9 / att_peak,
+                            "how": f"launch by launch, a {args.flush_mib} MiB write before "
+                                   "each, outside its event interval"},
+                   "frac_of_achievable": (att_gbs / achievable["copy_gbs"]
+                                          if args.pool != "host-direct" else None)}
+    roof_assign = {"bound": "mfma", "kernel": "k_assign_mfma (kv_kmeans_assign_prepared)",
+                   "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": achieved / BF16_PEAK_TFLOPS,
+                   "traffic": traffic["k_assign_mfma"]["bytes"] if traffic else None,
+                   "flops_per_launch": flops, "avg_launch_ms": asg_ms,
+                   "frac_of_achievable": achieved / achievable["gemm_bf16_tflops"]}
+    # `roofline` is the kernel with the larger share of step time
+    dominant = "assign" if share["k_assign_mfma"] >= share["k_gather_attend"] else "attend"
     keys_per_step = L * B * H * N
     res = {
         "metric": "prefill keys clustered/s; decode select+gather+attend us/layer-step, %HBM peak",
@@ -549,26 +663,19 @@ def main():
                    "local_buffer": cfg.buf_cap, "tau": cfg.tau, "pool": args.pool,
                    "fetch": args.fetch if fetch else None,
                    "attend": "wset" if fetch else "pool",
-                   "policy": args.policy, "units": args.units},
+                   "policy": args.policy, "units": args.units,
+                   "prefill_keys_shared_across_layers": False,
+                   "decode_steps_overridden": args.decode_steps is not None},
         "retrieval_steps": int(fl.sum()),
         "prefill_ms": pre_ms,
         "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),
         "decode_us_per_layer_step": dec_us,
         "decode_bytes_per_layer_step": dec_bytes,
         "decode_hbm_frac": dec_bytes / (dec_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
-        "roofline": {"bound": "hbm" if args.pool != "host-direct" else "host-link",
-                     "kernel": ("k_gather_attend_mfma (kv_fetch_attend, working set, step "
-                                "without retrieval)" if fetch else
-                                "k_gather_attend_mfma (kv_gather_attend)"),
-                     "achieved": att_gbs, "peak": att_peak, "unit": "GB/s",
-                     "frac": att_gbs / att_peak,
-                     "traffic": traffic["k_gather_attend_mfma"]["bytes"] if traffic else None,
-                     "bytes_per_launch": att_bytes, "avg_launch_ms": att_ms},
-        "roofline_assign": {"bound": "mfma", "kernel": "k_assign_mfma (kv_kmeans_assign_prepared)",
-                            "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": achieved / BF16_PEAK_TFLOPS,
-                            "traffic": traffic["k_assign_mfma"]["bytes"] if traffic else None,
-                            "flops_per_launch": flops, "avg_launch_ms": asg_ms},
+        "roofline": dict(roof_assign if dominant == "assign" else roof_attend),
+        "roofline_assign": roof_assign,
+        "roofline_attend": roof_attend,
+        "achievable": achievable,
         "time_share_per_step": share,
     }
     if fetch_res is not None:
@@ -589,7 +696,8 @@ def main():
         res["cpu_baseline"] = None  # the oracle's sample covers the standard path only
     elif not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, args.cpu_lloyd_iters, dk0, dv0)
+        iters = args.cpu_lloyd_iters or (1 if N * C > (1 << 28) else 3)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, iters, dk0, dv0)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

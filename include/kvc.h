@@ -112,11 +112,18 @@ const char *kv_status_string(kv_status s);
  * and each cluster's centroid, the mean of its keys, is its retrieval index.
  *
  * Lloyd's algorithm, exactly `iters` rounds of
- *   assign: a(x) = argmin_k ||x - c_k||^2, ties to the lowest k, with c_k
- *           rounded to the storage dtype (bf16 RNE of the fp32 master copy)
- *           and fp32 accumulation;
- *   update: c_k = mean of its members (fp32, members summed in key order);
+ *   assign: a(x) = argmin_k ||x - c_k||^2, with c_k rounded to the storage
+ *           dtype (bf16 RNE of the fp32 master copy) and fp32 accumulation.
+ *           For KV_BF16 the minimum is taken over the upper 28 bits of each
+ *           fp32 score, so centroids whose scores agree in those bits (exact
+ *           ties, and near-ties within about 2^-19 relative) go to the lowest
+ *           k; for KV_F32 exact ties go to the lowest k;
+ *   update: c_k = mean of its members in fp32; members are read in key order
+ *           and dealt round-robin to a fixed number of partial sums, which are
+ *           then combined in a fixed order, so the sum is the same bit for bit
+ *           on every run (not the left-to-right sum in key order);
  *           an empty cluster keeps its previous centroid.
+ * n_clusters <= 8192 (KV_ERR_UNSUPPORTED above).
  * Init: c_k = keys[init_idx[k]]. Then rows are packed cluster by cluster
  * (stable in key order) into pool->k / pool->v and the unit tables, and the
  * per-sequence counters are set (n_rows = n_keys, n_units = n_cand =
@@ -124,10 +131,14 @@ const char *kv_status_string(kv_status s);
  *
  * keys, values: [batch][n_kv_heads][n_keys][head_dim] in pool->dtype.
  * init_idx:     [batch][n_kv_heads][n_clusters] distinct indices in
- *               [0, n_keys) (distinctness is a precondition, not checked).
+ *               [0, n_keys) (distinctness is a precondition, not checked; an
+ *               index outside [0, n_keys) is clamped into it and
+ *               *pool->status is set to KV_ERR_INVALID_ARG).
  * assign_in:    NULL, or [BH][n_keys] labels in [0, n_clusters): skip Lloyd
  *               and pack this clustering (centroids = its member means;
- *               empty clusters take keys[init_idx[k]]).
+ *               empty clusters take keys[init_idx[k]]). A key whose label is
+ *               outside [0, n_clusters) is left out of every unit (its row is
+ *               not packed) and *pool->status is set to KV_ERR_INVALID_ARG.
  * assign_out:   NULL, or [BH][n_keys]: the final labels.
  * iters >= 1 unless assign_in is given. n_clusters <= n_keys,
  * n_keys <= pool->row_cap, n_clusters <= pool->unit_cap.
@@ -171,8 +182,10 @@ kv_status kv_kmeans_assign_prepared(const void *keys, const float *centroids, in
                                     size_t ws_bytes, hipStream_t stream);
 
 /* One Lloyd update step: centroids_out[k] = mean of keys labelled k, or
- * centroids_in[k] when the cluster is empty. counts (nullable) receives the
- * member counts [n_heads][n_clusters]. centroids_out may alias centroids_in. */
+ * centroids_in[k] when the cluster is empty (summation order as in
+ * kv_cluster_build). counts (nullable) receives the member counts
+ * [n_heads][n_clusters]. centroids_out may alias centroids_in. A key whose
+ * label is outside [0, n_clusters) takes part in no cluster. */
 size_t kv_kmeans_update_workspace(int32_t n_heads, int32_t n_keys, int32_t n_clusters);
 kv_status kv_kmeans_update(const void *keys, const int32_t *labels, const float *centroids_in,
                            float *centroids_out, int32_t *counts, int32_t n_heads,
@@ -247,7 +260,9 @@ kv_status kv_boundary_segment_append(const kv_pool *pool, const void *q_prev, co
  * previous selection is reused.
  * q: [batch][n_q_heads][head_dim] (dtype). sel_units: [BH][sel_cap] with
  * sel_cap >= min(budget, unit_cap). scores_out: NULL or [BH][unit_cap] fp32
- * (entries u >= n_cand[b] untouched).
+ * (entries u >= n_cand[b] untouched). pool->unit_cap <= 8192
+ * (KV_ERR_UNSUPPORTED above: each of the 1024 threads of a (b, g)'s last
+ * workgroup holds at most 8 candidates' sort keys in registers).
  */
 size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads);
 kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,

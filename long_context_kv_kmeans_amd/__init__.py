@@ -145,6 +145,30 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape=None, dtype=None,
+            optional: bool = False) -> None:
+    """Raise ValueError unless ``t`` has ``dtype`` and ``shape`` (None entries
+    in ``shape`` match any extent). The C ABI takes bare device pointers, so a
+    tensor of the wrong element type or extent would be read or written out of
+    its bounds: every wrapper checks here first."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: element type {t.dtype}, expected {dtype}")
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(e is None or int(a) == int(e)
+                                            for a, e in zip(t.shape, shape))
+        if not ok:
+            want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+            raise ValueError(f"{name}: shape {list(t.shape)}, expected {want}")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -255,62 +279,112 @@ def kv_cluster_build_workspace(batch, n_kv_heads, n_keys, head_dim, n_clusters, 
 
 def kv_cluster_build(pool: Pool, keys, values, n_clusters: int, iters: int, init_idx,
                      assign_in=None, assign_out=None, ws=None, stream=None) -> None:
-    B, H, N, D = keys.shape
+    B, H, D = pool.batch, pool.n_kv_heads, pool.head_dim
+    _expect("keys", keys, (B, H, None, D), pool.dtype)
+    N = keys.shape[2]
+    _expect("values", values, (B, H, N, D), pool.dtype)
+    _expect("init_idx", init_idx, (B, H, n_clusters), torch.int32)
+    _expect("assign_in", assign_in, (B, H, N), torch.int32, optional=True)
+    _expect("assign_out", assign_out, (B, H, N), torch.int32, optional=True)
     if ws is None:
         ws = _call_workspace(kv_cluster_build_workspace(B, H, N, D, n_clusters, keys.dtype), stream)
     _check("kv_cluster_build", lib().kv_cluster_build(
         pool.ref(), _ptr(keys), _ptr(values), N, n_clusters, iters, _ptr(init_idx),
-        _ptr(assign_in), _ptr(assign_out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(assign_in), _ptr(assign_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def kv_kmeans_assign(keys, centroids, labels, ws=None, stream=None) -> None:
     """keys [BH, N, D]; centroids [BH, C, D] fp32; labels [BH, N] int32."""
-    BH, N, D = keys.shape
-    C = centroids.shape[1]
+    BH, N, D, C = _kmeans_shapes(keys, centroids, labels)
     dt = dtype_code(keys.dtype)
     if ws is None:
         ws = _call_workspace(lib().kv_kmeans_assign_workspace(BH, C, D, dt), stream)
     _check("kv_kmeans_assign", lib().kv_kmeans_assign(
-        _ptr(keys), _ptr(centroids), BH, N, D, C, dt, _ptr(labels), _ptr(ws), ws.numel(),
+        _ptr(keys), _ptr(centroids), BH, N, D, C, dt, _ptr(labels), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def _kmeans_shapes(keys, centroids, labels):
+    if keys.dim() != 3:
+        raise ValueError(f"keys: shape {list(keys.shape)}, expected [BH, N, D]")
+    dtype_code(keys.dtype)
+    BH, N, D = keys.shape
+    _expect("centroids", centroids, (BH, None, D), torch.float32)
+    _expect("labels", labels, (BH, N), torch.int32)
+    return BH, N, D, centroids.shape[1]
 
 
 def kv_kmeans_prepare(centroids, dtype, ws, stream=None) -> None:
     """centroids [BH, C, D] fp32 -> their assignment form in ws (for keys of `dtype`)."""
+    _expect("centroids", centroids, (None, None, None), torch.float32)
     BH, C, D = centroids.shape
     _check("kv_kmeans_prepare", lib().kv_kmeans_prepare(
-        _ptr(centroids), BH, D, C, dtype_code(dtype), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(centroids), BH, D, C, dtype_code(dtype), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def kv_kmeans_assign_prepared(keys, centroids, labels, ws, stream=None) -> None:
     """Labels of keys [BH, N, D] against centroids already prepared in ws."""
-    BH, N, D = keys.shape
-    C = centroids.shape[1]
+    BH, N, D, C = _kmeans_shapes(keys, centroids, labels)
     _check("kv_kmeans_assign_prepared", lib().kv_kmeans_assign_prepared(
         _ptr(keys), _ptr(centroids), BH, N, D, C, dtype_code(keys.dtype), _ptr(labels), _ptr(ws),
-        ws.numel(), _stream(stream)))
+        _nbytes(ws), _stream(stream)))
 
 
 def kv_kmeans_update(keys, labels, centroids_in, centroids_out, counts=None, ws=None,
                      stream=None) -> None:
-    BH, N, D = keys.shape
-    C = centroids_in.shape[1]
+    BH, N, D, C = _kmeans_shapes(keys, centroids_in, labels)
+    _expect("centroids_out", centroids_out, (BH, C, D), torch.float32)
+    _expect("counts", counts, (BH, C), torch.int32, optional=True)
     if ws is None:
         ws = _call_workspace(lib().kv_kmeans_update_workspace(BH, N, C), stream)
     _check("kv_kmeans_update", lib().kv_kmeans_update(
         _ptr(keys), _ptr(labels), _ptr(centroids_in), _ptr(centroids_out), _ptr(counts), BH, N,
-        D, C, dtype_code(keys.dtype), _ptr(ws), ws.numel(), _stream(stream)))
+        D, C, dtype_code(keys.dtype), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # ---------------------------------------------------------------- decode
 def kv_boundary(q_prev, q_cur, tau: float, flag, r=None, stream=None) -> None:
+    if q_cur.dim() != 3:
+        raise ValueError(f"q_cur: shape {list(q_cur.shape)}, expected [B, Hq, D]")
     B, Hq, D = q_cur.shape
+    _expect("q_prev", q_prev, (B, Hq, D), q_cur.dtype, optional=True)
+    _expect("flag", flag, (B,), torch.uint8)
+    _expect("r", r, (B,), torch.float32, optional=True)
     _check("kv_boundary", lib().kv_boundary(
         _ptr(q_prev), _ptr(q_cur), B, Hq, D, dtype_code(q_cur.dtype), float(tau), _ptr(flag),
         _ptr(r), _stream(stream)))
 
 
+def _kv_step(pool: Pool, k_t, v_t, flag):
+    shape = (pool.batch, pool.n_kv_heads, pool.head_dim)
+    _expect("k_t", k_t, shape, pool.dtype)
+    _expect("v_t", v_t, shape, pool.dtype)
+    _expect("flag", flag, (pool.batch,), torch.uint8)
+
+
+def _queries(pool: Pool, q, name="q"):
+    """q [B, Hq, D] in the pool's element type; returns Hq."""
+    if q.dim() != 3:
+        raise ValueError(f"{name}: shape {list(q.shape)}, expected [B, Hq, D]")
+    _expect(name, q, (pool.batch, None, pool.head_dim), pool.dtype)
+    return q.shape[1]
+
+
+def _selection(pool: Pool, sel_units, sel_spans, sel_n, cap_from=None):
+    """Selection lists: sel_units [B, H, cap] and/or sel_spans [B, H, cap, 2]
+    (int32, same cap), sel_n [B, H]; returns cap."""
+    B, H = pool.batch, pool.n_kv_heads
+    if sel_units is None and sel_spans is None:
+        raise ValueError("sel_units or sel_spans is required")
+    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
+    _expect("sel_units", sel_units, (B, H, cap), torch.int32, optional=True)
+    _expect("sel_spans", sel_spans, (B, H, cap, 2), torch.int32, optional=True)
+    _expect("sel_n", sel_n, (B, H), torch.int32)
+    return cap
+
+
 def kv_segment_append(pool: Pool, k_t, v_t, flag, stream=None) -> None:
+    _kv_step(pool, k_t, v_t, flag)
     _check("kv_segment_append", lib().kv_segment_append(
         pool.ref(), _ptr(k_t), _ptr(v_t), _ptr(flag), _stream(stream)))
 
@@ -318,6 +392,10 @@ def kv_segment_append(pool: Pool, k_t, v_t, flag, stream=None) -> None:
 def kv_boundary_segment_append(pool: Pool, q_prev, q_cur, tau: float, k_t, v_t, flag, r=None,
                                stream=None) -> None:
     """kv_boundary then kv_segment_append in one launch (q_prev None: first step)."""
+    Hq = _queries(pool, q_cur, "q_cur")
+    _expect("q_prev", q_prev, tuple(q_cur.shape), pool.dtype, optional=True)
+    _kv_step(pool, k_t, v_t, flag)
+    _expect("r", r, (pool.batch,), torch.float32, optional=True)
     _check("kv_boundary_segment_append", lib().kv_boundary_segment_append(
         pool.ref(), _ptr(q_prev), _ptr(q_cur), q_cur.shape[1], float(tau), _ptr(k_t), _ptr(v_t),
         _ptr(flag), _ptr(r), _stream(stream)))
@@ -330,26 +408,40 @@ def kv_select_workspace(pool: Pool, n_q_heads: int) -> int:
 def kv_select(pool: Pool, q, budget: int, flag, sel_units, sel_n, sel_rows, scores_out=None,
               ws=None, stream=None, sel_spans=None) -> None:
     """sel_spans (optional) [B, H, sel_cap, 2] int32 receives the selected units' row spans."""
-    Hq = q.shape[1]
+    Hq = _queries(pool, q)
+    _expect("flag", flag, (pool.batch,), torch.uint8)
+    _select_outputs(pool, sel_units, sel_n, sel_rows, sel_spans, scores_out)
     if ws is None:
         ws = _call_workspace(kv_select_workspace(pool, Hq), stream)
     _check("kv_select", lib().kv_select(
         pool.ref(), _ptr(q), Hq, int(budget), _ptr(flag), _ptr(sel_units), sel_units.shape[-1],
-        _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans), _ptr(scores_out), _ptr(ws), ws.numel(),
+        _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans), _ptr(scores_out), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def _select_outputs(pool: Pool, sel_units, sel_n, sel_rows, sel_spans, scores_out):
+    B, H = pool.batch, pool.n_kv_heads
+    _expect("sel_units", sel_units, (B, H, None), torch.int32)
+    _selection(pool, sel_units, sel_spans, sel_n)
+    _expect("sel_rows", sel_rows, (B, H), torch.int32)
+    _expect("scores_out", scores_out, (B, H, pool.unit_cap), torch.float32, optional=True)
 
 
 def kv_boundary_select(pool: Pool, q_prev, q_cur, tau: float, budget: int, flag, sel_units,
                        sel_n, sel_rows, r=None, scores_out=None, ws=None, stream=None,
                        sel_spans=None) -> None:
     """kv_boundary then kv_select in one launch (q_prev None: first decode step)."""
-    Hq = q_cur.shape[1]
+    Hq = _queries(pool, q_cur, "q_cur")
+    _expect("q_prev", q_prev, tuple(q_cur.shape), pool.dtype, optional=True)
+    _expect("flag", flag, (pool.batch,), torch.uint8)
+    _expect("r", r, (pool.batch,), torch.float32, optional=True)
+    _select_outputs(pool, sel_units, sel_n, sel_rows, sel_spans, scores_out)
     if ws is None:
         ws = _call_workspace(kv_select_workspace(pool, Hq), stream)
     _check("kv_boundary_select", lib().kv_boundary_select(
         pool.ref(), _ptr(q_prev), _ptr(q_cur), Hq, float(tau), int(budget), _ptr(flag), _ptr(r),
         _ptr(sel_units), sel_units.shape[-1], _ptr(sel_n), _ptr(sel_rows), _ptr(sel_spans),
-        _ptr(scores_out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(scores_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def kv_gather_attend_workspace(pool: Pool, n_q_heads: int, max_rows: int) -> int:
@@ -359,13 +451,14 @@ def kv_gather_attend_workspace(pool: Pool, n_q_heads: int, max_rows: int) -> int
 def kv_gather_attend(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: int, out,
                      ws=None, stream=None, sel_spans=None) -> None:
     """sel_spans (optional, from kv_select) replaces the unit-table lookup of sel_units."""
-    Hq = q.shape[1]
+    Hq = _queries(pool, q)
+    cap = _selection(pool, sel_units, sel_spans, sel_n)
+    _expect("out", out, (pool.batch, Hq, pool.head_dim), torch.float32)
     if ws is None:
         ws = _call_workspace(kv_gather_attend_workspace(pool, Hq, max_rows), stream)
-    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
     _check("kv_gather_attend", lib().kv_gather_attend(
         pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), _ptr(sel_spans), cap,
-        _ptr(sel_n), int(max_rows), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(sel_n), int(max_rows), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # ---------------------------------------------------------------- working set
@@ -374,7 +467,8 @@ def kv_fetch_selected(pool: Pool, flag, sel_units, sel_n, dst: Pool, dst_spans, 
     """Selected rows of `pool` -> the HBM working set `dst` (sequences with flag 1).
     dst_spans [B, H, 1, 2] int32 and dst_n [B, H] int32 then describe it to
     kv_gather_attend(dst, ..., sel_spans=dst_spans, sel_n=dst_n)."""
-    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
+    cap = _selection(pool, sel_units, sel_spans, sel_n)
+    _working_set(pool, flag, dst, dst_spans, dst_n)
     _check("kv_fetch_selected", lib().kv_fetch_selected(
         pool.ref(), _ptr(flag), _ptr(sel_units), _ptr(sel_spans), cap, _ptr(sel_n), dst.ref(),
         _ptr(dst_spans), _ptr(dst_n), _stream(stream)))
@@ -385,11 +479,23 @@ def kv_fetch_attend(pool: Pool, q, scale: float, flag, sel_units, sel_n, max_row
                     sel_spans=None) -> None:
     """kv_fetch_selected + kv_gather_attend over the working set (and the
     pool's local buffer), in one launch."""
-    Hq = q.shape[1]
+    Hq = _queries(pool, q)
+    cap = _selection(pool, sel_units, sel_spans, sel_n)
+    _working_set(pool, flag, dst, dst_spans, dst_n)
+    _expect("out", out, (pool.batch, Hq, pool.head_dim), torch.float32)
     if ws is None:
         ws = _call_workspace(kv_gather_attend_workspace(pool, Hq, max_rows), stream)
-    cap = sel_units.shape[-1] if sel_units is not None else sel_spans.shape[-2]
     _check("kv_fetch_attend", lib().kv_fetch_attend(
         pool.ref(), _ptr(q), Hq, float(scale), _ptr(flag), _ptr(sel_units), _ptr(sel_spans), cap,
         _ptr(sel_n), int(max_rows), dst.ref(), _ptr(dst_spans), _ptr(dst_n), _ptr(out), _ptr(ws),
-        ws.numel(), _stream(stream)))
+        _nbytes(ws), _stream(stream)))
+
+
+def _working_set(pool: Pool, flag, dst: Pool, dst_spans, dst_n):
+    B, H = pool.batch, pool.n_kv_heads
+    _expect("flag", flag, (B,), torch.uint8)
+    _expect("dst_spans", dst_spans, None, torch.int32)
+    if dst_spans.numel() != B * H * 2:  # one (start, rows) span per (sequence, KV head)
+        raise ValueError(f"dst_spans: shape {list(dst_spans.shape)}, expected {B * H * 2} "
+                         "int32 values (e.g. [B, H, 1, 2])")
+    _expect("dst_n", dst_n, (B, H), torch.int32)

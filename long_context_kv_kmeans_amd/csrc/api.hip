@@ -40,7 +40,6 @@ size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_c
   return o;
 }
 
-constexpr int kMaxClusters = 32768;  // label histogram of one chunk lives in LDS
 
 }  // namespace
 
@@ -157,12 +156,13 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
   void *asg_ws = w + o_asg;
   void *upd_ws = w + o_upd;
 
-  st = launch_init_centroids(keys, init_idx, cent, bh, n_keys, n_clusters, d, dt, stream);
+  st = launch_init_centroids(keys, init_idx, cent, bh, n_keys, n_clusters, d, dt, pool->status,
+                             stream);
   if (st != KV_OK) return st;
   const int32_t *perm = nullptr, *start = nullptr, *tot = nullptr;
   if (assign_in) {
     st = launch_update(keys, assign_in, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt, upd_ws,
-                       stream, &perm, &start, &tot);
+                       stream, &perm, &start, &tot, nullptr, pool->status);
     if (st != KV_OK) return st;
     if (assign_out && assign_out != assign_in)
       if (hipMemcpyAsync(assign_out, assign_in, (size_t)bh * n_keys * 4, hipMemcpyDeviceToDevice,

@@ -606,9 +606,9 @@ static kv_status select_dispatch(const kv_pool *pool, const void *q, int hq, int
     else                    \
       KVC_SEL(K, false);    \
   } while (0)
+  static_assert(kSelectMaxKeysPerThread == 8, "one instantiation per key count");
   if (per <= 2) KVC_SEL2(2);
   else if (per <= 8) KVC_SEL2(8);
-  else if (per <= kSelectMaxKeysPerThread) KVC_SEL2(kSelectMaxKeysPerThread);
   else return KV_ERR_UNSUPPORTED;
 #undef KVC_SEL2
 #undef KVC_SEL

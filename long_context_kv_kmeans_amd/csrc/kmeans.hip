@@ -24,28 +24,37 @@ constexpr int kAssignWaves = 8;                          // waves per workgroup
 constexpr int kRankChunk = 1024;                         // keys per counting-sort chunk
 
 // ---------------------------------------------------------------- init
+// An index outside [0, n) is clamped into it (so no read leaves the head's
+// keys) and reported as KV_ERR_INVALID_ARG through *status when given.
 template <typename T>
 __global__ void k_init_centroids(const T *__restrict__ keys, const int32_t *__restrict__ init_idx,
-                                 float *__restrict__ cent, int n, int c, int d, long total) {
+                                 float *__restrict__ cent, int n, int c, int d, long total,
+                                 int32_t *status) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
        i += (long)gridDim.x * blockDim.x) {
     const long bh = i / ((long)c * d);
     const int k = (int)((i / d) % c), e = (int)(i % d);
-    const int src = init_idx[bh * c + k];
+    int src = init_idx[bh * c + k];
+    if (src < 0 || src >= n) {
+      if (status && e == 0)
+        __hip_atomic_store(status, (int)KV_ERR_INVALID_ARG, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      src = src < 0 ? 0 : n - 1;
+    }
     cent[i] = Elem<T>::to_f32(keys[(bh * n + src) * d + e]);
   }
 }
 
 kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
-                                int n, int c, int d, kv_dtype dt, hipStream_t s) {
+                                int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s) {
   const long total = (long)bh * c * d;
   const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   if (dt == KV_BF16)
     k_init_centroids<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t *)keys, init_idx, cent, n,
-                                                      c, d, total);
+                                                      c, d, total, status);
   else
     k_init_centroids<float><<<blocks, 256, 0, s>>>((const float *)keys, init_idx, cent, n, c, d,
-                                                   total);
+                                                   total, status);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -424,11 +433,13 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
 //                 and the label's total;
 //  k_startscan -- exclusive scan of totals over labels (cluster starts);
 //  k_scatter   -- perm[start[a] + chunk_prefix[a] + rank] = key.
+// A label outside [0, c) takes no part: its key gets no rank, no histogram
+// count and no place in the permutation (reported through *status when given).
 template <int NW>
 __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict__ labels,
                                                        int32_t *__restrict__ rank,
                                                        int32_t *__restrict__ hist, int n, int c,
-                                                       int nbits, int nchunk) {
+                                                       int nbits, int nchunk, int32_t *status) {
   constexpr int KPW = kRankChunk / NW;  // keys per wave: wave w takes the w-th part of the chunk
   constexpr int SUB = KPW / 64;
   extern __shared__ int32_t cnt[];      // [NW][c]: label counts of each wave's part
@@ -440,7 +451,11 @@ __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub) {
     const int i = base + sub * 64 + lane;
-    a[sub] = i < n ? lab[i] : -1;
+    const int v = i < n ? lab[i] : -1;
+    a[sub] = (v >= 0 && v < c) ? v : -1;
+    if (status && i < n && a[sub] < 0)
+      __hip_atomic_store(status, (int)KV_ERR_INVALID_ARG, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
   for (int k = threadIdx.x; k < NW * c; k += 64 * NW) cnt[k] = 0;
   __syncthreads();
@@ -558,6 +573,7 @@ __global__ void k_scatter(const int32_t *__restrict__ labels, const int32_t *__r
   const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const int a = labels[(size_t)bh * n + i];
+  if (a < 0 || a >= c) return;  // left out by k_rank_hist too
   const int ch = i / kRankChunk;
   const int dest = start[(size_t)bh * c + a] + hist[((size_t)bh * nchunk + ch) * c + a] +
                    rank[(size_t)bh * n + i];
@@ -669,7 +685,8 @@ size_t update_ws_bytes(int bh, int n, int c) {
 kv_status launch_update(const void *keys, const int32_t *labels, const float *cent_in,
                         float *cent_out, int32_t *counts, int bh, int n, int d, int c,
                         kv_dtype dt, void *ws, hipStream_t s, const int32_t **perm_out,
-                        const int32_t **start_out, const int32_t **tot_out, void *frags_out) {
+                        const int32_t **start_out, const int32_t **tot_out, void *frags_out,
+                        int32_t *status) {
   const int nchunk = (n + kRankChunk - 1) / kRankChunk;
   char *w = static_cast<char *>(ws);
   int32_t *rank = reinterpret_cast<int32_t *>(w);
@@ -682,17 +699,15 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   w += align_up((size_t)bh * c * 4, 256);
   int32_t *perm = reinterpret_cast<int32_t *>(w);
 
-  // a chunk's label counts stay within 64 KB of LDS: 4 waves per chunk up to 4096
-  // labels, 2 up to 8192, else 1
+  // a chunk's label counts ([waves][c] int32) stay within 64 KB of LDS: 4 waves
+  // per chunk up to 4096 labels, 2 up to kMaxClusters = 8192
+  if (c > kMaxClusters) return KV_ERR_UNSUPPORTED;
   if (c <= 4096)
     k_rank_hist<4><<<dim3(nchunk, bh), 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                                    ceil_log2(c), nchunk);
-  else if (c <= 8192)
-    k_rank_hist<2><<<dim3(nchunk, bh), 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                                    ceil_log2(c), nchunk);
+                                                                    ceil_log2(c), nchunk, status);
   else
-    k_rank_hist<1><<<dim3(nchunk, bh), 64, (size_t)c * 4, s>>>(labels, rank, hist, n, c,
-                                                               ceil_log2(c), nchunk);
+    k_rank_hist<2><<<dim3(nchunk, bh), 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
+                                                                    ceil_log2(c), nchunk, status);
   k_colscan<<<dim3((c + 255) / 256, bh), 256, 0, s>>>(hist, tot, c, nchunk);
   k_startscan<<<bh, 1024, 0, s>>>(tot, start, counts, c);
   k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, perm, n, c,
@@ -735,7 +750,11 @@ __global__ void __launch_bounds__(256) k_pack_rows(const char *__restrict__ ksrc
   const int j = blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
   if (j >= n) return;
-  const size_t src = ((size_t)bh * n + perm[(size_t)bh * n + j]) * ROW_BYTES + part * 16;
+  // rows past the clustered keys (keys whose label was out of range) have no
+  // permutation entry; an entry outside [0, n) is never followed
+  const int from = perm[(size_t)bh * n + j];
+  if (from < 0 || from >= n) return;
+  const size_t src = ((size_t)bh * n + from) * ROW_BYTES + part * 16;
   const size_t dst = ((size_t)bh * row_cap + j) * ROW_BYTES + part * 16;
   *reinterpret_cast<uint4 *>(kdst + dst) = *reinterpret_cast<const uint4 *>(ksrc + src);
   *reinterpret_cast<uint4 *>(vdst + dst) = *reinterpret_cast<const uint4 *>(vsrc + src);

@@ -12,7 +12,8 @@ namespace kvc {
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int kMaxSel = 4096; // selected units staged in LDS by the attend kernel
-constexpr int kSelectMaxKeysPerThread = 32;  // selection keys held per thread (x1024 threads)
+constexpr int kSelectMaxKeysPerThread = 8;  // selection keys held per thread (x1024 threads)
+constexpr int kMaxClusters = 8192;  // one counting-sort chunk's label counts fit 64 KB of LDS
 
 // bf16 is carried as raw uint16_t bits.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -170,7 +171,7 @@ namespace kvc {
 
 // K-means
 kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
-                                int n, int c, int d, kv_dtype dt, hipStream_t s);
+                                int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s);
 size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt);
 kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, hipStream_t s);
 kv_status launch_assign_prepare(const float *cent, int bh, int d, int c, kv_dtype dt, void *ws,
@@ -185,7 +186,8 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
                         float *cent_out, int32_t *counts, int bh, int n, int d, int c,
                         kv_dtype dt, void *ws, hipStream_t s,
                         const int32_t **perm_out, const int32_t **start_out,
-                        const int32_t **tot_out, void *frags_out = nullptr);
+                        const int32_t **tot_out, void *frags_out = nullptr,
+                        int32_t *status = nullptr);
 kv_status launch_pack(const kv_pool *pool, const void *keys, const void *values,
                       const float *cent, const int32_t *perm, const int32_t *start,
                       const int32_t *tot, int n, int c, hipStream_t s);

@@ -294,3 +294,115 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_ranges_beyond_the_kernels_limits_are_refused():
+    """Clusters above 8192 (one counting-sort chunk's label counts must fit
+    64 KB of LDS) and pools of more than 8192 units (8 selection keys per
+    thread of a 1024-thread workgroup) are refused before any launch."""
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    big = 1 << 30
+    assert L.kv_kmeans_assign(a, a, 8, 20000, 128, 8193, kvc.KV_BF16, a, a, big,
+                              None) == kvc.KV_ERR_UNSUPPORTED
+    assert L.kv_kmeans_prepare(a, 8, 128, 8193, kvc.KV_BF16, a, big, None) == kvc.KV_ERR_UNSUPPORTED
+    assert L.kv_kmeans_assign_prepared(a, a, 8, 20000, 128, 8193, kvc.KV_BF16, a, a, big,
+                                       None) == kvc.KV_ERR_UNSUPPORTED
+    assert L.kv_kmeans_update(a, a, a, a, None, 8, 20000, 128, 8193, kvc.KV_BF16, a, big,
+                              None) == kvc.KV_ERR_UNSUPPORTED
+    p = _fake_pool(row_cap=20000, unit_cap=9000)
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 20000, 8193, 10, a, None, None, a, big,
+                              None) == kvc.KV_ERR_UNSUPPORTED
+    # 8192 clusters and 8192 units are inside the limits (only the workspace is short here)
+    p = _fake_pool(row_cap=20000, unit_cap=8192)
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 20000, 8192, 10, a, None, None, a, 256,
+                              None) == kvc.KV_ERR_WORKSPACE
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, None, a, 16,
+                       None) == kvc.KV_ERR_WORKSPACE
+    p = _fake_pool(row_cap=20000, unit_cap=8193)
+    assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, None, a, big,
+                       None) == kvc.KV_ERR_UNSUPPORTED
+    assert L.kv_boundary_select(ctypes.byref(p), None, a, 32, ctypes.c_float(0.7), 512, a, None,
+                                a, 512, a, a, None, None, a, big,
+                                None) == kvc.KV_ERR_UNSUPPORTED
+
+
+def _cpu_pool(dtype=None, B=1, H=2, D=64, row_cap=64, unit_cap=8):
+    import torch
+    return kvc.Pool(B, H, D, dtype or torch.bfloat16, row_cap=row_cap, unit_cap=unit_cap,
+                    device="cpu")
+
+
+def test_binding_rejects_wrong_element_types_and_shapes():
+    """The binding checks every tensor's element type and extent against the
+    pool (and against each other) before a pointer reaches the library: the C
+    ABI has no way to tell a bf16 query from an fp32 one or a short buffer
+    from a long one. CPU tensors are used, so a call that passes the checks
+    stops at the 'must live on the GPU' error instead."""
+    import torch
+    B, H, Hq, D = 1, 2, 8, 64
+    pool = _cpu_pool()
+    bf, f32, i32, u8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+
+    def z(*shape, dt=i32):
+        return torch.zeros(*shape, dtype=dt)
+
+    q = z(B, Hq, D, dt=bf)
+    sel, sel_n, sel_rows = z(B, H, 16), z(B, H), z(B, H)
+    flag = z(B, dt=u8)
+    out = z(B, Hq, D, dt=f32)
+
+    def raises(match, fn, *a, **k):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **k)
+
+    # a call that passes every check reaches the device-pointer check
+    ws = z(256, dt=u8)
+    raises("must live on the GPU", kvc.kv_select, pool, q, 16, flag, sel, sel_n, sel_rows, ws=ws)
+    raises("q: element type", kvc.kv_select, pool, q.float(), 16, flag, sel, sel_n, sel_rows)
+    raises("q: shape", kvc.kv_select, pool, z(B, Hq, 128, dt=bf), 16, flag, sel, sel_n, sel_rows)
+    raises("flag: element type", kvc.kv_select, pool, q, 16, flag.int(), sel, sel_n, sel_rows)
+    raises("sel_n: shape", kvc.kv_select, pool, q, 16, flag, sel, z(B, H + 1), sel_rows)
+    raises("sel_spans: shape", kvc.kv_select, pool, q, 16, flag, sel, sel_n, sel_rows,
+           sel_spans=z(B, H, 15, 2))
+    raises("scores_out: shape", kvc.kv_select, pool, q, 16, flag, sel, sel_n, sel_rows,
+           scores_out=z(B, H, 7, dt=f32))
+    raises("q_prev: element type", kvc.kv_boundary_select, pool, q.float(), q, 0.7, 16, flag,
+           sel, sel_n, sel_rows)
+    # attention: output type and extent, span/id capacity agreement
+    raises("must live on the GPU", kvc.kv_gather_attend, pool, q, 0.1, sel, sel_n, 16, out, ws=ws)
+    raises("out: element type", kvc.kv_gather_attend, pool, q, 0.1, sel, sel_n, 16, out.bfloat16())
+    raises("out: shape", kvc.kv_gather_attend, pool, q, 0.1, sel, sel_n, 16, z(B, Hq, 32, dt=f32))
+    raises("sel_spans: shape", kvc.kv_gather_attend, pool, q, 0.1, sel, sel_n, 16, out,
+           sel_spans=z(B, H, 8, 2))
+    raises("required", kvc.kv_gather_attend, pool, q, 0.1, None, sel_n, 16, out)
+    wset = _cpu_pool(row_cap=16, unit_cap=1)
+    raises("dst_spans", kvc.kv_fetch_attend, pool, q, 0.1, flag, sel, sel_n, 16, wset,
+           z(B, H, 2, 2), z(B, H), out)
+    raises("dst_n: shape", kvc.kv_fetch_selected, pool, flag, sel, sel_n, wset, z(B, H, 1, 2),
+           z(B))
+    # prefill: keys/values against the pool, init and labels against the keys
+    keys, vals = z(B, H, 32, D, dt=bf), z(B, H, 32, D, dt=bf)
+    init = z(B, H, 4)
+    raises("must live on the GPU", kvc.kv_cluster_build, pool, keys, vals, 4, 1, init, ws=ws)
+    raises("keys: element type", kvc.kv_cluster_build, pool, keys.float(), vals, 4, 1, init)
+    raises("keys: shape", kvc.kv_cluster_build, pool, z(B, H + 1, 32, D, dt=bf), vals, 4, 1, init)
+    raises("values: shape", kvc.kv_cluster_build, pool, keys, z(B, H, 31, D, dt=bf), 4, 1, init)
+    raises("init_idx: shape", kvc.kv_cluster_build, pool, keys, vals, 5, 1, init)
+    raises("init_idx: element type", kvc.kv_cluster_build, pool, keys, vals, 4, 1, init.long())
+    raises("assign_in: shape", kvc.kv_cluster_build, pool, keys, vals, 4, 1, init,
+           assign_in=z(B, H, 31))
+    raises("assign_out: element type", kvc.kv_cluster_build, pool, keys, vals, 4, 1, init,
+           assign_out=z(B, H, 32, dt=torch.int64))
+    # K-means steps: centroids fp32 [BH, C, D], labels int32 [BH, N]
+    k3, c3, lab = z(2, 32, D, dt=bf), z(2, 4, D, dt=f32), z(2, 32)
+    raises("centroids: element type", kvc.kv_kmeans_assign, k3, c3.bfloat16(), lab)
+    raises("labels: shape", kvc.kv_kmeans_assign, k3, c3, z(2, 31))
+    raises("centroids_out: shape", kvc.kv_kmeans_update, k3, lab, c3, z(2, 5, D, dt=f32))
+    raises("counts: element type", kvc.kv_kmeans_update, k3, lab, c3, c3.clone(),
+           counts=z(2, 4, dt=f32))
+    # decode-step tensors of the segment append
+    kt = z(B, H, D, dt=bf)
+    raises("k_t: shape", kvc.kv_segment_append, pool, z(B, H, 32, dt=bf), kt, flag)
+    raises("v_t: element type", kvc.kv_segment_append, pool, kt, kt.float(), flag)
+    raises("r: element type", kvc.kv_boundary, q, q, 0.7, flag, r=z(B))

@@ -272,3 +272,60 @@ def test_full_size_sampled(cfg_idx, heads, sample):
                 assert np.linalg.norm(gc[h][k] - ref) <= 1e-5 * max(np.linalg.norm(ref), 1e-30)
             assert cnt[h].sum() == N
         c = gc
+
+
+def test_out_of_range_labels_and_init_indices_are_ignored_and_reported():
+    """Labels outside [0, C) given to the update (or to kv_cluster_build as
+    assign_in) leave their keys out of every cluster; init indices outside
+    [0, N) are clamped into the head's keys. kv_cluster_build reports either
+    case as KV_ERR_INVALID_ARG in the pool's status word. The clusters the
+    valid labels define must equal the oracle's update over those keys alone."""
+    cfg = wl.get_config(1, n_keys=2100, n_clusters=64, n_components=16)
+    inp, keys, init = _keys(cfg, [0, 1])
+    BH, N, d = keys.shape
+    C = cfg.n_clusters
+    keys_d = to_dev(keys, cfg.dtype)
+    g = np.random.default_rng(5)
+    lab = g.integers(0, C, (BH, N)).astype(np.int64)
+    bad = g.random((BH, N)) < 0.05
+    lab_bad = lab.copy()
+    lab_bad[bad] = np.where(g.random(bad.sum()) < 0.5, -3, C + np.arange(bad.sum()) % 7)
+    c0 = np.stack([keys[h][init[h]].astype(np.float64) for h in range(BH)])
+    cg, cnt = _gpu_update(keys_d, lab_bad, c0)
+    for h in range(BH):
+        ok = ~bad[h]
+        ref, rc = okm.update(keys[h][ok], lab[h][ok], c0[h])
+        assert (cnt[h] == rc).all()
+        assert _rel_err(cg[h], ref) <= 1e-5
+
+    # through kv_cluster_build: status word, unit sizes, valid rows packed
+    B, H = 1, BH
+    pool = make_pool(B, H, d, cfg.dtype, N, C)
+    vals_d = to_dev(inp["values"], cfg.dtype)
+    kvc.kv_cluster_build(pool, keys_d.reshape(B, H, N, d), vals_d, C, 1,
+                         torch.from_numpy(init.reshape(B, H, C)).cuda(),
+                         assign_in=torch.from_numpy(lab_bad.astype(np.int32).reshape(B, H, N)).cuda())
+    torch.cuda.synchronize()
+    assert int(pool.status.item()) == kvc.KV_ERR_INVALID_ARG
+    sizes = pool.unit_size[0].cpu().numpy()
+    starts = pool.unit_start[0].cpu().numpy()
+    pk = to_np(pool.k[0])
+    for h in range(H):
+        ok = ~bad[h]
+        assert (sizes[h] == np.bincount(lab[h][ok], minlength=C)).all()
+        order = np.argsort(lab[h][ok], kind="stable")
+        np.testing.assert_array_equal(pk[h][:ok.sum()], keys[h][ok][order])
+        assert starts[h][0] == 0
+
+    # init indices out of range: clamped, reported, the rest of the build unchanged
+    pool2 = make_pool(B, H, d, cfg.dtype, N, C)
+    init_bad = init.copy().reshape(B, H, C)
+    init_bad[0, 0, 3], init_bad[0, 1, 5] = -1, N + 10
+    lab_out = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
+    kvc.kv_cluster_build(pool2, keys_d.reshape(B, H, N, d), vals_d, C, 2,
+                         torch.from_numpy(init_bad).cuda(), assign_out=lab_out)
+    torch.cuda.synchronize()
+    assert int(pool2.status.item()) == kvc.KV_ERR_INVALID_ARG
+    lo = lab_out.cpu().numpy()
+    assert lo.min() >= 0 and lo.max() < C
+    assert int(pool2.unit_size.sum().item()) == H * N

@@ -25,6 +25,14 @@ def test_layer_inputs_deterministic_and_exact():
         assert len(set(idx.tolist())) == 32 and idx.min() >= 0 and idx.max() < 512
 
 
+def test_layer_inputs_threads_give_the_same_arrays():
+    cfg = wl.get_config(4, n_keys=256, n_clusters=16, n_components=8, batch=2)
+    a = wl.layer_inputs(cfg, 1)
+    b = wl.layer_inputs(cfg, 1, threads=5)
+    for k in ("keys", "values", "init_idx", "components"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
 def test_query_walk_structure():
     cfg = wl.get_config(0)
     q, jumps = wl.query_walk(cfg, 0, 0)

@@ -194,12 +194,14 @@ def decode_kv(cfg: Config, layer: int, seq: int, head: int, steps: Optional[int]
     return to_dtype(k, cfg.dtype), to_dtype(v, cfg.dtype)
 
 
-def layer_inputs(cfg: Config, layer: int = 0, heads=None, seqs=None):
+def layer_inputs(cfg: Config, layer: int = 0, heads=None, seqs=None, threads: int = 1):
     """All prefill inputs of one layer.
 
     Returns dict with keys [B, H, N, d], values [B, H, N, d], init_idx
     [B, H, C] (int32), components [B, H, N] (int64) -- float32 arrays hold
-    values exact in ``cfg.dtype``.
+    values exact in ``cfg.dtype``. ``threads`` > 1 draws the (sequence, head)
+    streams on that many threads; every stream has its own generator, so the
+    arrays are the same whatever the thread count.
     """
     seqs = range(cfg.batch) if seqs is None else seqs
     heads = range(cfg.n_kv_heads) if heads is None else heads
@@ -209,11 +211,23 @@ def layer_inputs(cfg: Config, layer: int = 0, heads=None, seqs=None):
     vals = np.empty((B, H, N, d), np.float32)
     init = np.empty((B, H, C), np.int32)
     comp = np.empty((B, H, N), np.int64)
-    for bi, b in enumerate(seqs):
-        for hi, h in enumerate(heads):
-            keys[bi, hi], comp[bi, hi] = head_keys(cfg, layer, b, h)
-            vals[bi, hi] = head_values(cfg, layer, b, h)
-            init[bi, hi] = init_indices(cfg, layer, b, h)
+
+    def one(job):
+        bi, hi = job
+        b, h = seqs[bi], heads[hi]
+        keys[bi, hi], comp[bi, hi] = head_keys(cfg, layer, b, h)
+        vals[bi, hi] = head_values(cfg, layer, b, h)
+        init[bi, hi] = init_indices(cfg, layer, b, h)
+
+    jobs = [(bi, hi) for bi in range(B) for hi in range(H)]
+    if threads > 1 and len(jobs) > 1:
+        import concurrent.futures as cf
+
+        with cf.ThreadPoolExecutor(max_workers=min(threads, len(jobs))) as ex:
+            list(ex.map(one, jobs))
+    else:
+        for job in jobs:
+            one(job)
     return {"keys": keys, "values": vals, "init_idx": init, "components": comp}
 
 
