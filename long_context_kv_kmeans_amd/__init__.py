@@ -409,7 +409,7 @@ def kv_select(pool: Pool, q, budget: int, flag, sel_units, sel_n, sel_rows, scor
               ws=None, stream=None, sel_spans=None) -> None:
     """sel_spans (optional) [B, H, sel_cap, 2] int32 receives the selected units' row spans."""
     Hq = _queries(pool, q)
-    _expect("flag", flag, (pool.batch,), torch.uint8)
+    _expect("flag", flag, (pool.batch,), torch.uint8, optional=True)  # None: every sequence
     _select_outputs(pool, sel_units, sel_n, sel_rows, sel_spans, scores_out)
     if ws is None:
         ws = _call_workspace(kv_select_workspace(pool, Hq), stream)

@@ -311,7 +311,6 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
                               out, partials, counters, stream);
 }
 
-
 // ---------------------------------------------------------------- working set
 kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int32_t *sel_units,
                             const int32_t *sel_spans, int32_t sel_cap, const int32_t *sel_n,

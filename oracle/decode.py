@@ -70,7 +70,7 @@ def unit_rows(start, size, units) -> np.ndarray:
 
 def run_decode(packs, queries, tau: float, budget: int, scale: float, dtype: str,
                buf_cap: int = 0, dec_k=None, dec_v=None, steps: int | None = None,
-               keep_scores: bool = False, retrieve=None):
+               keep_scores: bool = False, retrieve=None, attend_steps=None):
     """Decode loop for one (layer, sequence).
 
     packs: per KV head, ``oracle.kmeans.pack`` dicts (same cluster count).
@@ -81,6 +81,9 @@ def run_decode(packs, queries, tau: float, budget: int, scale: float, dtype: str
     criticises, every S-th step the fixed-stride policy of its ablation
     table. Only without decode segments (buf_cap == 0), where the decision
     does nothing else.
+    attend_steps: optional [steps] bools; attention is computed only on those
+    steps (``out`` is None on the others). It changes nothing else: the
+    attention output feeds no later step.
     Returns a list of per-step dicts: flag, r, sel (per head, ascending unit
     ids; the reused set on non-boundary steps), out [Hq, d], n_rows,
     buf_begin, n_cand and, if ``keep_scores``, the scores of boundary steps.
@@ -112,14 +115,17 @@ def run_decode(packs, queries, tau: float, budget: int, scale: float, dtype: str
                 sel[g] = select_prefix(s, size, budget)
                 if keep_scores:
                     scores[g] = s
-        out = np.zeros((Hq, d))
-        for g in range(H):
-            start, size, _ = pool.unit_table(g)
-            rows = unit_rows(start, size, sel[g])
-            if seg is not None:
-                rows = np.concatenate([rows, seg.buffer_rows()])
-            K, V = pool.rows(g, rows)
-            out[g * G:(g + 1) * G] = attend_exact(queries[t][g * G:(g + 1) * G], K, V, scale)
+        out = None
+        if attend_steps is None or attend_steps[t]:
+            out = np.zeros((Hq, d))
+            for g in range(H):
+                start, size, _ = pool.unit_table(g)
+                rows = unit_rows(start, size, sel[g])
+                if seg is not None:
+                    rows = np.concatenate([rows, seg.buffer_rows()])
+                K, V = pool.rows(g, rows)
+                out[g * G:(g + 1) * G] = attend_exact(queries[t][g * G:(g + 1) * G], K, V,
+                                                      scale)
         entry = {"flag": flag, "r": float(r[0]), "sel": [s.copy() for s in sel], "out": out,
                  "n_cand": pool.n_candidates()}
         if seg is not None:

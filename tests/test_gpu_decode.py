@@ -80,7 +80,9 @@ def _run(cfg, steps, seqs, compare_every=1, check=None, policy="boundary", page=
     extra_rows, n_units = 0, cfg.n_clusters
     if cfg.buf_cap > 0:
         dk, dv = wl.layer_decode_kv(cfg, 0, steps=steps, seqs=seqs)
-        extra_rows, n_units = steps, cfg.n_clusters + steps
+        # unit table: the clusters, then one unit per segment closed (at most one per
+        # step), within the selection's limit of 8192 units
+        extra_rows, n_units = steps, cfg.n_clusters + min(steps, 8192 - cfg.n_clusters)
     pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
                                   n_units=n_units, buf_cap=cfg.buf_cap, extra_rows=extra_rows,
                                   **(pool_kw or {}))
@@ -97,10 +99,14 @@ def _run(cfg, steps, seqs, compare_every=1, check=None, policy="boundary", page=
     stats = {"retrievals": 0, "set_mismatch": 0, "max_err": 0.0}
     for bi in check:
         packs = oracle_packs(inp["keys"], inp["values"], labels, cents, cfg.dtype, bi)
+        # the reference attention below is exact attention over the GPU's selection
+        # (equal to the oracle's, which is checked), so the loop's own outputs are
+        # not needed
         log, opool = run_decode(packs, q[:, bi], cfg.tau, cfg.budget, cfg.scale, cfg.dtype,
                                 buf_cap=cfg.buf_cap,
                                 dec_k=None if dk is None else dk[:, bi],
-                                dec_v=None if dv is None else dv[:, bi], retrieve=sched)
+                                dec_v=None if dv is None else dv[:, bi], retrieve=sched,
+                                attend_steps=np.zeros(steps, dtype=bool))
         for t, e in enumerate(log):
             assert flags[t, bi] == e["flag"], (t, bi)
             if cfg.buf_cap > 0:
@@ -201,13 +207,13 @@ def test_decode_long_output_segments():
 
 def test_decode_long_output_benchmark_path():
     # the long-output workload through the benchmark's calls (kv_boundary_segment_append,
-    # kv_select with row spans, kv_gather_attend on the spans) for 6000 of its 16384
-    # steps: ~120 boundaries, the 1024-token buffer full and evicting segments from step
-    # ~1024 on. (All 16384 steps take over two minutes, most of it the oracle's per-step
-    # exact attention.)
+    # kv_select with row spans, kv_gather_attend on the spans) for all of its 16384
+    # steps: ~330 boundaries, the 1024-token buffer full and evicting segments from step
+    # ~1024 on. Flags and segment counters are compared at every step, the selection
+    # and the attention output at every retrieval step and every 64th step.
     cfg = wl.get_config(2, iters=3)
-    st = _run(cfg, 6000, [0], compare_every=64, fused_append=True, spans=True)
-    assert st["retrievals"] >= 60
+    st = _run(cfg, cfg.steps, [0], compare_every=64, fused_append=True, spans=True)
+    assert st["retrievals"] >= 250
 
 
 @pytest.mark.parametrize("cfg_idx,over,steps,seqs", [
@@ -300,3 +306,97 @@ def test_segment_append_capacity_errors_are_reported():
     torch.cuda.synchronize()
     assert int(pool2.status.item()) == kvc.KV_ERR_CAPACITY
     assert int(pool2.n_rows.item()) == 12 and int(pool2.n_units.item()) == 2
+
+
+def test_decode_cfg3_two_layers_through_captured_graphs():
+    """Two layers of the 36-layer long-input long-output workload (131072 keys per KV
+    head, 8192 units, budget 2048), each with its own keys, pool, working set and
+    query walk, through the benchmark's launch configuration: every decode step
+    runs kv_boundary_select -> kv_fetch_attend for layer 0 then layer 1, captured
+    into HIP graphs and replayed. Each layer is compared with its own oracle loop:
+    flags and selected sets at every step, attention at every retrieval step and
+    every 16th step. Both sides use the fixed clustering of the one-layer test."""
+    import long_context_kv_kmeans_amd as kvc
+    from tests.gpu_util import working_set
+    cfg = wl.get_config(3)
+    L, T, C = 2, cfg.steps, cfg.n_clusters
+    sel_cap = min(cfg.budget, C)
+    stream = torch.cuda.Stream()
+
+    class Layer:
+        pass
+
+    layers = []
+    for li in range(L):
+        y = Layer()
+        inp = wl.layer_inputs(cfg, li, threads=8)
+        y.keys, y.vals = inp["keys"], inp["values"]
+        y.labels, y.cents = _fixed_clustering(inp["keys"], C)
+        y.q, _ = wl.layer_queries(cfg, li)
+        y.pool, _, _ = pool_from_labels(y.keys, y.vals, y.labels, y.cents, cfg.dtype, n_units=C)
+        y.qd = to_dev(y.q, cfg.dtype)
+        B, H, Hq, d = 1, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+        z = lambda *s: torch.zeros(*s, dtype=torch.int32, device="cuda")  # noqa: E731
+        y.sel, y.sel_n, y.sel_rows, y.spans = z(B, H, sel_cap), z(B, H), z(B, H), z(B, H, sel_cap, 2)
+        y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
+        y.out = torch.zeros(B, Hq, d, dtype=torch.float32, device="cuda")
+        y.wset = working_set(y.pool, cfg.budget)
+        y.ws_sel = kvc.workspace(kvc.kv_select_workspace(y.pool, Hq))
+        y.ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(y.pool, Hq, cfg.budget))
+        y.rec_out = torch.zeros(T, B, Hq, d, dtype=torch.float32, device="cuda")
+        y.rec_sel = z(T, B, H, sel_cap)
+        y.rec_n = z(T, B, H)
+        layers.append(y)
+
+    def step(t):
+        for y in layers:
+            kvc.kv_boundary_select(y.pool, y.qd[t - 1] if t else None, y.qd[t], cfg.tau,
+                                   cfg.budget, y.flags[t], y.sel, y.sel_n, y.sel_rows,
+                                   ws=y.ws_sel, sel_spans=y.spans)
+            kvc.kv_fetch_attend(y.pool, y.qd[t], cfg.scale, y.flags[t], None, y.sel_n,
+                                cfg.budget, y.wset, y.wset.spans, y.wset.count, y.out,
+                                ws=y.ws_att, sel_spans=y.spans)
+            y.rec_out[t].copy_(y.out)
+            y.rec_sel[t].copy_(y.sel)
+            y.rec_n[t].copy_(y.sel_n)
+
+    with torch.cuda.stream(stream):
+        step(0)  # loads the kernels; the replay starts again from step 0
+    torch.cuda.synchronize()
+    graphs = []
+    for t0 in range(0, T, 128):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(t0, min(T, t0 + 128)):
+                step(t)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+
+    G = cfg.group
+    for li, y in enumerate(layers):
+        assert int(y.pool.status.item()) == 0
+        flags = y.flags.cpu().numpy().astype(bool)[:, 0]
+        sel, sel_n = y.rec_sel.cpu().numpy()[:, 0], y.rec_n.cpu().numpy()[:, 0]
+        out = y.rec_out.cpu().numpy()[:, 0]
+        packs = oracle_packs(y.keys, y.vals, y.labels, y.cents, cfg.dtype, 0)
+        log, opool = run_decode(packs, y.q[:, 0], cfg.tau, cfg.budget, cfg.scale, cfg.dtype,
+                                attend_steps=np.zeros(T, dtype=bool))
+        assert flags.sum() >= 2, li
+        for t, e in enumerate(log):
+            assert flags[t] == e["flag"], (li, t)
+            for g in range(H):
+                got = sel[t, g, :sel_n[t, g]]
+                assert np.array_equal(got, e["sel"][g]), (li, t, g)
+            if t % 16 and not e["flag"]:
+                continue
+            for g in range(H):
+                start, size, _ = opool.unit_table(g)
+                K, V = opool.rows(g, unit_rows(start, size, e["sel"][g]))
+                ref = oat.attend_exact(y.q[t, 0, g * G:(g + 1) * G], K, V, cfg.scale)
+                err = max_rel_err(out[t, g * G:(g + 1) * G], ref)
+                assert err <= TOL, (li, t, g, err)
+        # the two layers are different workloads: their walks retrieve at different steps
+        if li == 1:
+            assert not np.array_equal(flags, layers[0].flags.cpu().numpy().astype(bool)[:, 0])

@@ -191,3 +191,27 @@ def test_page_units_keep_time_order():
     assert pk["unit_start"].tolist() == list(range(0, N, P))
     assert pk["unit_size"].tolist() == [P] * (C - 1) + [N - P * (C - 1)]
     np.testing.assert_allclose(cents[-1], x[P * (C - 1):].mean(0), rtol=1e-15, atol=0)
+
+
+def test_attention_on_chosen_steps_only_changes_nothing_else():
+    # skipping the attention output on some steps leaves every other logged
+    # quantity (flags, selections, segment counters) and the computed outputs
+    # exactly as in the full loop
+    packs = _tiny_pool(20)
+    rng = np.random.default_rng(21)
+    T = 30
+    q = _walk(22, T)
+    dk = rng.standard_normal((T, 2, 8))
+    dv = rng.standard_normal((T, 2, 8))
+    kw = dict(budget=20, scale=0.3, dtype="fp32", buf_cap=5, dec_k=dk, dec_v=dv)
+    full, _ = run_decode(packs, q, 0.7, **kw)
+    at = np.arange(T) % 4 == 1
+    part, _ = run_decode(packs, q, 0.7, attend_steps=at, **kw)
+    for t, (a, b) in enumerate(zip(full, part)):
+        for k in ("flag", "n_cand", "n_rows", "buf_begin", "seg_begin"):
+            assert a[k] == b[k], (t, k)
+        assert all(np.array_equal(x, y) for x, y in zip(a["sel"], b["sel"]))
+        if at[t]:
+            np.testing.assert_array_equal(a["out"], b["out"])
+        else:
+            assert b["out"] is None
