@@ -310,6 +310,25 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
                            const int32_t *sel_n, int32_t max_rows, float *out, void *ws,
                            size_t ws_bytes, hipStream_t stream);
 
+/* kv_gather_attend for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, bit for bit, as
+ * kv_gather_attend with the same arguments, but the completion counters and
+ * split partials live in a static device array of the library (4 MiB, one
+ * per device, held until the process ends) instead of a caller workspace.
+ * It calls no allocating routine. The first call on a device looks the array up and
+ * clears it with a kernel on `stream`; every completed call leaves its
+ * counters zero again. All calls on one device share the array, so calls
+ * that overlap in time on one device (different streams, or concurrent
+ * graph replays) race and must not be issued. Arguments and validation as
+ * kv_gather_attend; a call whose kv_gather_attend_workspace(pool, n_q_heads,
+ * max_rows) exceeds 4 MiB (4194304 bytes) returns KV_ERR_WORKSPACE. */
+kv_status kv_gather_attend_noalloc(const kv_pool *pool, const void *q, int32_t n_q_heads,
+                                   float scale, const int32_t *sel_units,
+                                   const int32_t *sel_spans, int32_t sel_cap,
+                                   const int32_t *sel_n, int32_t max_rows, float *out,
+                                   hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * The GPU-side working set of a pool kept in host memory. LouisKV note,
  * flowchart: on a boundary the top units are fetched from the CPU pool to

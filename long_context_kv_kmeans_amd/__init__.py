@@ -38,7 +38,7 @@ EXPORTED = [
     "kv_boundary",
     "kv_segment_append", "kv_boundary_segment_append",
     "kv_select_workspace", "kv_select", "kv_boundary_select",
-    "kv_gather_attend_workspace", "kv_gather_attend",
+    "kv_gather_attend_workspace", "kv_gather_attend", "kv_gather_attend_noalloc",
     "kv_fetch_selected", "kv_fetch_attend", "kv_host_device_pointer",
 ]
 
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
         "kv_gather_attend_workspace": (c_size, [pool_p, c_int, c_int]),
         "kv_gather_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, c_int, vp, c_int,
                                      vp, vp, c_size, vp]),
+        "kv_gather_attend_noalloc": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, c_int, vp,
+                                             c_int, vp, vp]),
         "kv_fetch_selected": (c_int, [pool_p, vp, vp, vp, c_int, vp, pool_p, vp, vp, vp]),
         "kv_fetch_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, vp, c_int, vp,
                                     c_int, pool_p, vp, vp, vp, vp, c_size, vp]),
@@ -459,6 +461,18 @@ def kv_gather_attend(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: in
     _check("kv_gather_attend", lib().kv_gather_attend(
         pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), _ptr(sel_spans), cap,
         _ptr(sel_n), int(max_rows), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def kv_gather_attend_noalloc(pool: Pool, q, scale: float, sel_units, sel_n, max_rows: int, out,
+                             stream=None, sel_spans=None) -> None:
+    """kv_gather_attend with the library's static device scratch in place of a
+    workspace: allocates nothing (calls that overlap on one device race)."""
+    Hq = _queries(pool, q)
+    cap = _selection(pool, sel_units, sel_spans, sel_n)
+    _expect("out", out, (pool.batch, Hq, pool.head_dim), torch.float32)
+    _check("kv_gather_attend_noalloc", lib().kv_gather_attend_noalloc(
+        pool.ref(), _ptr(q), Hq, float(scale), _ptr(sel_units), _ptr(sel_spans), cap,
+        _ptr(sel_n), int(max_rows), _ptr(out), _stream(stream)))
 
 
 # ---------------------------------------------------------------- working set

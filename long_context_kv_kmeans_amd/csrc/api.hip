@@ -1,6 +1,8 @@
 // C ABI of libkvc: argument validation on the host, workspace carving and
 // kernel composition. Every entry point validates before touching HIP, so
 // argument errors are reported without a device.
+#include <mutex>
+
 #include "kvc_internal.hpp"
 
 using namespace kvc;
@@ -41,6 +43,53 @@ size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_c
 }
 
 
+}  // namespace
+
+// ---------------------------------------------------------------- static scratch
+// Device memory of kv_gather_attend_noalloc: the attention's completion
+// counters and split partials live in this file-scope array instead of a
+// caller workspace. Each device the library runs on holds its own copy until
+// the process ends. Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the device symbol): the device address
+// comes from hipGetSymbolAddress, once per device, and is kept in
+// g_scratch_dev.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+__global__ void k_zero_words(uint32_t *p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The current device's scratch address; on the first call on a device, looks
+// it up and clears the whole array on `stream` (with a kernel, so that the
+// clear can also be recorded into a graph).
+kv_status scratch_for_current_device(void **out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return KV_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return KV_ERR_HIP;
+    }
+    k_zero_words<<<256, 256, 0, stream>>>(static_cast<uint32_t *>(ptr), kScratchBytes / 4);
+    if (hipGetLastError() != hipSuccess) return KV_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return KV_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -302,6 +351,34 @@ kv_status kv_gather_attend(const kv_pool *pool, const void *q, int32_t n_q_heads
   if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
   const size_t need = kv_gather_attend_workspace(pool, n_q_heads, max_rows);
   if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  int32_t *counters = static_cast<int32_t *>(ws);
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                              align_up(bh * sizeof(int32_t), 256));
+  return launch_gather_attend(pool, q, n_q_heads, scale, sel_units, sel_spans, sel_cap, sel_n,
+                              attend_num_splits(pool, max_rows), attend_row_bound(pool, max_rows),
+                              out, partials, counters, stream);
+}
+
+kv_status kv_gather_attend_noalloc(const kv_pool *pool, const void *q, int32_t n_q_heads,
+                                   float scale, const int32_t *sel_units,
+                                   const int32_t *sel_spans, int32_t sel_cap,
+                                   const int32_t *sel_n, int32_t max_rows, float *out,
+                                   hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  if (!q || (!sel_units && !sel_spans) || !sel_n || !out) return KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || sel_cap <= 0 || max_rows < 0)
+    return KV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return KV_ERR_INVALID_ARG;
+  const int G = n_q_heads / pool->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
+  const size_t need = kv_gather_attend_workspace(pool, n_q_heads, max_rows);
+  if (need == 0 || need > kScratchBytes) return KV_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = scratch_for_current_device(&ws, stream);
+  if (st != KV_OK) return st;
   const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
   int32_t *counters = static_cast<int32_t *>(ws);
   float *partials = reinterpret_cast<float *>(static_cast<char *>(ws) +

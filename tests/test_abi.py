@@ -406,3 +406,25 @@ def test_binding_rejects_wrong_element_types_and_shapes():
     raises("k_t: shape", kvc.kv_segment_append, pool, z(B, H, 32, dt=bf), kt, flag)
     raises("v_t: element type", kvc.kv_segment_append, pool, kt, kt.float(), flag)
     raises("r: element type", kvc.kv_boundary, q, q, 0.7, flag, r=z(B))
+
+
+def test_noalloc_attention_validation():
+    """kv_gather_attend_noalloc validates like kv_gather_attend and refuses a
+    launch whose partials would not fit its 4 MiB static scratch, all before
+    it touches the device."""
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    c01 = ctypes.c_float(0.1)
+    p = _fake_pool()
+    assert L.kv_gather_attend_noalloc(ctypes.byref(p), None, 32, c01, a, None, 512, a, 512, a,
+                                      None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_gather_attend_noalloc(ctypes.byref(p), a, 32, c01, None, None, 512, a, 512, a,
+                                      None) == kvc.KV_ERR_INVALID_ARG
+    assert L.kv_gather_attend_noalloc(ctypes.byref(p), a, 24, c01, a, None, 512, a, 512, a,
+                                      None) == kvc.KV_ERR_UNSUPPORTED  # G = 3
+    assert L.kv_gather_attend_noalloc(ctypes.byref(p), a, 32, c01, a, None, 5000, a, 512, a,
+                                      None) == kvc.KV_ERR_UNSUPPORTED  # sel_cap > 4096
+    big = _fake_pool(batch=256)
+    assert L.kv_gather_attend_workspace(ctypes.byref(big), 64, 4096) > 4 << 20
+    assert L.kv_gather_attend_noalloc(ctypes.byref(big), a, 64, c01, a, None, 4096, a, 4096, a,
+                                      None) == kvc.KV_ERR_WORKSPACE
