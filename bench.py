@@ -261,6 +261,11 @@ def main():
                     help="--pool host: the working-set copy inside the attention launch "
                          "(kv_fetch_attend) or as a launch of its own (kv_fetch_selected, "
                          "then kv_gather_attend)")
+    ap.add_argument("--launches", choices=("one", "two"), default="one",
+                    help="pools without a local buffer, fused working-set fetch, boundary "
+                         "policy: one launch per layer-step (kv_decode_step: boundary test, "
+                         "selection on retrieval steps, fetch and attention) or two "
+                         "(kv_boundary_select, then kv_fetch_attend)")
     ap.add_argument("--policy", default="boundary",
                     help="when to retrieve: boundary (the cosine test), per-token, stride:S")
     ap.add_argument("--units", default="cluster",
@@ -301,6 +306,10 @@ def main():
     if args.units != "cluster" and page is None:
         raise SystemExit(f"unknown --units {args.units!r}")
     variant = host or sched is not None or page is not None
+    # the whole layer-step in one launch where the path is boundary test -> select ->
+    # fused fetch + attention
+    one = (fetch and args.fetch == "fused" and not seg and sched is None
+           and args.launches == "one" and args.pool != "host-direct")
     if seg and (sched is not None or page is not None or (fetch and args.fetch == "separate")):
         raise SystemExit("with decode segments (--config 2) only --pool host|host-direct "
                          "(fused fetch) applies")
@@ -367,7 +376,9 @@ def main():
             ws_build = kvc.workspace(kvc.kv_cluster_build_workspace(B, H, N, d, C, tdt))
             ws_sel = kvc.workspace(kvc.kv_select_workspace(y.pool, Hq))
             ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(y.pool, Hq, cfg.budget))
-        y.ws_build, y.ws_sel, y.ws_att = ws_build, ws_sel, ws_att
+            ws_step = (kvc.workspace(kvc.kv_decode_step_workspace(y.pool, Hq, cfg.budget))
+                       if one else None)
+        y.ws_build, y.ws_sel, y.ws_att, y.ws_step = ws_build, ws_sel, ws_att, ws_step
         layers.append(y)
         if li == 0:  # layer 0, sequence 0, KV head 0 feeds the CPU baseline
             inp = {k: np.ascontiguousarray(inp_l[k][:1, :1]) for k in ("keys", "values",
@@ -394,6 +405,11 @@ def main():
     def decode_step(y, t):
         q_prev = y.q[t - 1] if t else None
         flag = y.flags[t]
+        if one:
+            kvc.kv_decode_step(y.pool, q_prev, y.q[t], cfg.tau, cfg.scale, cfg.budget, flag,
+                               y.sel, y.sel_spans, y.sel_n, y.sel_rows, y.wset, y.wspans, y.wn,
+                               y.out, ws=y.ws_step)
+            return
         if seg:  # boundary + segment append -> selection -> attention
             kvc.kv_boundary_segment_append(y.pool, q_prev, y.q[t], cfg.tau, y.dk[t], y.dv[t],
                                            y.flags[t])
@@ -449,7 +465,7 @@ def main():
 
     # capture the decode loop in graphs of at most ~4096 launches; replay per step
     stream = torch.cuda.Stream()
-    calls = (3 if seg or (fetch and args.fetch == "separate") else 2) * L
+    calls = (1 if one else 3 if seg or (fetch and args.fetch == "separate") else 2) * L
     chunk = max(1, min(T, 4096 // calls))
     with torch.cuda.stream(stream):
         prefill()
@@ -516,12 +532,25 @@ def main():
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
     att_rows = int(sel_rows.sum().item())
-    if fetch:  # a step without retrieval: the working set (+ the local buffer's HBM copy)
+    q_extra = 0
+    if one:
+        # the whole layer-step on a step without retrieval for every sequence (the
+        # boundary test, then the working set): two adjacent queries of a drift step
+        t_nr = int(np.nonzero(~fl.any(1))[0][-1])
+        flag_tmp = torch.zeros(B, dtype=torch.uint8, device="cuda")
+
+        def att_fn(wset=None):
+            kvc.kv_decode_step(pool, y0.q[t_nr - 1], y0.q[t_nr], cfg.tau, cfg.scale, cfg.budget,
+                               flag_tmp, sel, sel_spans, sel_n, sel_rows, wset or y0.wset,
+                               y0.wspans, y0.wn, y0.out, ws=y0.ws_step)
+        att_spans = int(y0.wn.sum().item())
+        q_extra = B * Hq * d * e  # the previous query, read by the boundary test
+    elif fetch:  # a step without retrieval: the working set (+ the local buffer's HBM copy)
         zeros = torch.zeros(B, dtype=torch.uint8, device="cuda")
 
-        def att_fn():
+        def att_fn(wset=None):
             kvc.kv_fetch_attend(pool, y0.q[T - 1], cfg.scale, zeros, None, sel_n, cfg.budget,
-                                y0.wset, y0.wspans, y0.wn, y0.out, ws=y0.ws_att,
+                                wset or y0.wset, y0.wspans, y0.wn, y0.out, ws=y0.ws_att,
                                 sel_spans=sel_spans)
         att_spans = int(y0.wn.sum().item())
     else:
@@ -548,13 +577,12 @@ def main():
         def cold_fn():
             c = copies[it[0] % n_copies]
             it[0] += 1
-            kvc.kv_fetch_attend(pool, y0.q[T - 1], cfg.scale, zeros, None, sel_n, cfg.budget,
-                                c, y0.wspans, y0.wn, y0.out, ws=y0.ws_att, sel_spans=sel_spans)
+            att_fn(c)
         att_cold_ms = launch_ms(cold_fn, max(args.attend_reps, 2 * n_copies))
         del copies
     att_buf = int((pool.n_rows - pool.buf_begin).sum().item()) * H if seg else 0
     att_bytes = ((att_rows + att_buf) * 2 * d * e  # selected (and local-buffer) K and V rows
-                 + B * Hq * d * e              # queries
+                 + B * Hq * d * e + q_extra    # queries
                  + B * Hq * d * 4              # fp32 output
                  + att_spans * 8)              # row span (start, size) per selected unit
     att_gbs = att_bytes / (att_ms * 1e-3) / 1e9
@@ -621,7 +649,9 @@ def main():
     traffic = profiled_traffic(cfg.name) if (not variant and args.attend == "wset"
                                              and args.decode_steps is None) else None
     roof_attend = {"bound": "hbm" if args.pool != "host-direct" else "host-link",
-                   "kernel": ("k_gather_attend_mfma (kv_fetch_attend, working set, step "
+                   "kernel": ("k_gather_attend_mfma (kv_decode_step: boundary test + "
+                              "working set, step without retrieval)" if one else
+                              "k_gather_attend_mfma (kv_fetch_attend, working set, step "
                               "without retrieval)" if fetch else
                               "k_gather_attend_mfma (kv_gather_attend)"),
                    "achieved": att_gbs, "peak": att_peak, "unit": "GB/s",
@@ -664,6 +694,7 @@ def main():
                    "iters": cfg.iters, "decode_steps": T, "budget": cfg.budget,
                    "local_buffer": cfg.buf_cap, "tau": cfg.tau, "pool": args.pool,
                    "fetch": args.fetch if fetch else None,
+                   "launches_per_layer_step": calls // L,
                    "attend": "wset" if fetch else "pool",
                    "policy": args.policy, "units": args.units,
                    "prefill_keys_shared_across_layers": False,

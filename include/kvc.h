@@ -388,6 +388,42 @@ kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads,
                           const kv_pool *dst, int32_t *dst_spans, int32_t *dst_n, float *out,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * A whole decode step of one layer in one launch. LouisKV note, flowchart
+ * of "Overall framework": at every step the semantic-boundary test decides,
+ * and only on a boundary are the units scored and the Top-B fetched; between
+ * boundaries the KV fetched last time is reused for attention. Exactly
+ *   kv_boundary_select(pool, q_prev, q_cur, n_q_heads, tau, budget, flag, r,
+ *                      sel_units, sel_cap, sel_n, sel_rows, sel_spans, NULL);
+ *   kv_fetch_attend(pool, q_cur, n_q_heads, scale, flag, NULL, sel_spans,
+ *                   sel_cap, sel_n, max_rows = budget, dst, dst_spans, dst_n,
+ *                   out);
+ * with the same flag, r, selection, working set, status and output bit for
+ * bit, but one launch: every attention workgroup evaluates the boundary test
+ * of its sequence itself; on a step without retrieval it goes straight to
+ * the working set; on a retrieval step the workgroups of (b, g) first score
+ * the units (each its share), the last to finish selects and publishes the
+ * selection (release), the others wait for it (acquire; the selecting
+ * workgroup is already running and waits for nothing, so the wait ends),
+ * and all of them then copy and attend as kv_fetch_attend does. A wait that
+ * does not end after about 2^22 sleeps would set *pool->status to
+ * KV_ERR_HIP. bf16 pools without a local buffer (buf_cap 0), in device or
+ * host memory; unit_cap <= 8192; sel_cap >= min(budget, unit_cap), <= 4096.
+ * sel_units and sel_spans are outputs ([BH][sel_cap] and [BH][sel_cap][2]
+ * int32), written on retrieval steps only, like sel_n and sel_rows ([BH]).
+ * flag: [batch] uint8 out; r: NULL or [batch] fp32 out. dst, dst_spans,
+ * dst_n: the working set, as for kv_fetch_attend. ws:
+ * kv_decode_step_workspace(pool, n_q_heads, budget) bytes, zero-filled once
+ * before first use (its counters return to zero after every call); calls
+ * sharing a workspace must not overlap. */
+size_t kv_decode_step_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t budget);
+kv_status kv_decode_step(const kv_pool *pool, const void *q_prev, const void *q_cur,
+                         int32_t n_q_heads, float tau, float scale, int32_t budget, uint8_t *flag,
+                         float *r, int32_t *sel_units, int32_t *sel_spans, int32_t sel_cap,
+                         int32_t *sel_n, int32_t *sel_rows, const kv_pool *dst,
+                         int32_t *dst_spans, int32_t *dst_n, float *out, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
 /* Device address of pinned host memory (hipHostMalloc, mapped), to place a
  * pool's k and v in host memory. *dev receives the address the kernels use.
  * KV_ERR_INVALID_ARG if `host` is not such memory. host, dev: [host]. */

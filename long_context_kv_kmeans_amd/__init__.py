@@ -40,6 +40,7 @@ EXPORTED = [
     "kv_select_workspace", "kv_select", "kv_boundary_select",
     "kv_gather_attend_workspace", "kv_gather_attend", "kv_gather_attend_noalloc",
     "kv_fetch_selected", "kv_fetch_attend", "kv_host_device_pointer",
+    "kv_decode_step_workspace", "kv_decode_step",
 ]
 
 
@@ -115,6 +116,10 @@ def lib() -> ctypes.CDLL:
         "kv_fetch_attend": (c_int, [pool_p, vp, c_int, ctypes.c_float, vp, vp, vp, c_int, vp,
                                     c_int, pool_p, vp, vp, vp, vp, c_size, vp]),
         "kv_host_device_pointer": (c_int, [vp, ctypes.POINTER(vp)]),
+        "kv_decode_step_workspace": (c_size, [pool_p, c_int, c_int]),
+        "kv_decode_step": (c_int, [pool_p, vp, vp, c_int, ctypes.c_float, ctypes.c_float, c_int,
+                                   vp, vp, vp, vp, c_int, vp, vp, pool_p, vp, vp, vp, vp, c_size,
+                                   vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -513,3 +518,30 @@ def _working_set(pool: Pool, flag, dst: Pool, dst_spans, dst_n):
         raise ValueError(f"dst_spans: shape {list(dst_spans.shape)}, expected {B * H * 2} "
                          "int32 values (e.g. [B, H, 1, 2])")
     _expect("dst_n", dst_n, (B, H), torch.int32)
+
+
+# ---------------------------------------------------------------- one launch per step
+def kv_decode_step_workspace(pool: Pool, n_q_heads: int, budget: int) -> int:
+    return lib().kv_decode_step_workspace(pool.ref(), n_q_heads, int(budget))
+
+
+def kv_decode_step(pool: Pool, q_prev, q_cur, tau: float, scale: float, budget: int, flag,
+                   sel_units, sel_spans, sel_n, sel_rows, dst: Pool, dst_spans, dst_n, out,
+                   r=None, ws=None, stream=None) -> None:
+    """kv_boundary_select + kv_fetch_attend (max_rows = budget) in one launch
+    (q_prev None: first decode step)."""
+    Hq = _queries(pool, q_cur, "q_cur")
+    _expect("q_prev", q_prev, tuple(q_cur.shape), pool.dtype, optional=True)
+    _expect("r", r, (pool.batch,), torch.float32, optional=True)
+    _select_outputs(pool, sel_units, sel_n, sel_rows, sel_spans, None)
+    _expect("sel_spans", sel_spans, (pool.batch, pool.n_kv_heads, sel_units.shape[-1], 2),
+            torch.int32)
+    _working_set(pool, flag, dst, dst_spans, dst_n)
+    _expect("out", out, (pool.batch, Hq, pool.head_dim), torch.float32)
+    if ws is None:
+        ws = _call_workspace(kv_decode_step_workspace(pool, Hq, budget), stream)
+    _check("kv_decode_step", lib().kv_decode_step(
+        pool.ref(), _ptr(q_prev), _ptr(q_cur), Hq, float(tau), float(scale), int(budget),
+        _ptr(flag), _ptr(r), _ptr(sel_units), _ptr(sel_spans), sel_units.shape[-1], _ptr(sel_n),
+        _ptr(sel_rows), dst.ref(), _ptr(dst_spans), _ptr(dst_n), _ptr(out), _ptr(ws),
+        _nbytes(ws), _stream(stream)))

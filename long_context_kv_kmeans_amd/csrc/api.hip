@@ -446,6 +446,78 @@ kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads,
                              partials, counters, stream);
 }
 
+// ---------------------------------------------------------------- one launch per step
+namespace {
+struct StepWs {
+  size_t counters, partials, sel_counters, gen, scores, total;
+};
+StepWs step_ws_layout(const kv_pool *pool, int32_t n_q_heads, int32_t budget) {
+  const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
+  const size_t G = (size_t)(n_q_heads / pool->n_kv_heads);
+  const size_t ns = (size_t)attend_num_splits(pool, budget);
+  StepWs w;
+  size_t o = 0;
+  w.counters = o;
+  o += align_up(bh * sizeof(int32_t), 256);
+  w.partials = o;
+  o += align_up(bh * ns * G * (pool->head_dim + 2) * sizeof(float), 256);
+  w.sel_counters = o;
+  o += align_up(bh * sizeof(int32_t), 256);
+  w.gen = o;
+  o += align_up(bh * sizeof(int32_t), 256);
+  w.scores = o;
+  o += align_up(bh * pool->unit_cap * sizeof(float), 256);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t kv_decode_step_workspace(const kv_pool *pool, int32_t n_q_heads, int32_t budget) {
+  if (check_pool(pool) != KV_OK || n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 ||
+      budget < 0)
+    return 0;
+  return step_ws_layout(pool, n_q_heads, budget).total;
+}
+
+kv_status kv_decode_step(const kv_pool *pool, const void *q_prev, const void *q_cur,
+                         int32_t n_q_heads, float tau, float scale, int32_t budget, uint8_t *flag,
+                         float *r, int32_t *sel_units, int32_t *sel_spans, int32_t sel_cap,
+                         int32_t *sel_n, int32_t *sel_rows, const kv_pool *dst,
+                         int32_t *dst_spans, int32_t *dst_n, float *out, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  kv_status st = check_pool(pool);
+  if (st != KV_OK) return st;
+  st = check_pool(dst);
+  if (st != KV_OK) return st;
+  if (!q_cur || !flag || !sel_units || !sel_spans || !sel_n || !sel_rows || !dst_spans ||
+      !dst_n || !out)
+    return KV_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % pool->n_kv_heads != 0 || budget < 0 || sel_cap <= 0)
+    return KV_ERR_INVALID_ARG;
+  if (tau != tau || !(scale == scale)) return KV_ERR_INVALID_ARG;
+  if (pool->dtype != KV_BF16 || pool->buf_cap > 0) return KV_ERR_UNSUPPORTED;
+  const int G = n_q_heads / pool->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  if (pool->unit_cap > 1024 * kSelectMaxKeysPerThread) return KV_ERR_UNSUPPORTED;
+  if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
+  if (sel_cap < (budget < pool->unit_cap ? budget : pool->unit_cap)) return KV_ERR_CAPACITY;
+  if (dst->batch != pool->batch || dst->n_kv_heads != pool->n_kv_heads ||
+      dst->head_dim != pool->head_dim || dst->dtype != pool->dtype)
+    return KV_ERR_INVALID_ARG;
+  if (dst->k == pool->k || dst->v == pool->v) return KV_ERR_INVALID_ARG;
+  if (dst->buf_cap > 0) return KV_ERR_UNSUPPORTED;  // a working set has no local buffer
+  const StepWs w = step_ws_layout(pool, n_q_heads, budget);
+  if (!ws || !aligned256(ws) || ws_bytes < w.total) return KV_ERR_WORKSPACE;
+  char *c = static_cast<char *>(ws);
+  return launch_decode_step(
+      pool, q_prev, q_cur, n_q_heads, tau, scale, budget, flag, r, sel_units, sel_spans, sel_cap,
+      sel_n, sel_rows, attend_num_splits(pool, budget), attend_row_bound(pool, budget), dst,
+      dst_spans, dst_n, out, reinterpret_cast<float *>(c + w.partials),
+      reinterpret_cast<int32_t *>(c + w.counters), reinterpret_cast<float *>(c + w.scores),
+      reinterpret_cast<int32_t *>(c + w.sel_counters), reinterpret_cast<int32_t *>(c + w.gen),
+      stream);
+}
+
 kv_status kv_host_device_pointer(void *host, void **dev) {
   if (!host || !dev) return KV_ERR_INVALID_ARG;
   void *d = nullptr;

@@ -356,52 +356,27 @@ __device__ __forceinline__ unsigned long long unit_key(float score, int u) {
   return ((unsigned long long)float_order_key(score) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
 }
 
-// FUSED: the workgroup first runs the boundary test of its sequence on
-// (q_prev, q) itself (flag_out / r_out written once per sequence) instead of
-// reading flag. The unit count and the group's queries are requested in the
-// same memory round trip as the decision's inputs.
-template <typename T, int D, int KPT, bool FUSED>
-__global__ void __launch_bounds__(kSelectThreads)
-    k_select(kv_pool pool, const T *__restrict__ q, int hq, int group, int budget,
-             const uint8_t *__restrict__ flag, int32_t *__restrict__ sel_units, int sel_cap,
-             int32_t *__restrict__ sel_n, int32_t *__restrict__ sel_rows,
-             int32_t *__restrict__ sel_spans, float *__restrict__ scores,
-             int32_t *counters, const T *__restrict__ q_prev, float tau,
-             uint8_t *__restrict__ flag_out, float *__restrict__ r_out) {
-  constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per 16-byte lane load
-  constexpr int LPU = D / EPL;               // lanes per index vector
-  constexpr int UPW = 64 / LPU;              // units per wave instruction
-  constexpr int UNR = 4;
-  const int H = pool.n_kv_heads;
-  const int bg = blockIdx.y, b = bg / H, g = bg % H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int part = lane % LPU, slot = lane / LPU;
-  const int n_cand = pool.n_cand[b];
-  uint4 qv[8];
+// ---- pieces of the selection shared by k_select and k_decode_step
+
+// The group's query pieces for scoring: lane part p of head h holds elements
+// EPL p .. EPL p + EPL - 1 (requested early, summed later).
+template <typename T, int D>
+__device__ __forceinline__ void score_query_load(const T *__restrict__ q, int hq, int b, int g,
+                                                 int group, int lane, uint4 (&qv)[8]) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;
+  constexpr int LPU = D / EPL;
+  const int part = lane % LPU;
 #pragma unroll
   for (int h = 0; h < 8; ++h)
     if (h < group)
       qv[h] = *reinterpret_cast<const uint4 *>(q + ((size_t)b * hq + g * group + h) * D + part * EPL);
-  if constexpr (FUSED) {
-    __shared__ float s_part[4];
-    int f = 1;
-    float rv = __builtin_nanf("");
-    if (q_prev != nullptr) {
-      rv = boundary_r<T, D>(q_prev, q, hq, b, s_part);
-      f = rv < tau ? 1 : 0;
-    }
-    if (blockIdx.x == 0 && g == 0 && tid == 0) {
-      flag_out[b] = (uint8_t)f;
-      if (r_out) r_out[b] = rv;
-    }
-    if (!f) return;
-  } else {
-    if (flag != nullptr && flag[b] == 0) return;
-  }
-  const int U = min(max(n_cand, 0), pool.unit_cap);
+}
 
-  // ---- scoring: s_u = (sum_h q_h) . idx_u, fp32
-  float qs[EPL];
+// Summed group query (heads in order), this lane's EPL elements.
+template <typename T, int D>
+__device__ __forceinline__ void score_query_sum(const uint4 (&qv)[8], int group,
+                                                float (&qs)[16 / Elem<T>::kBytes]) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qs[e] = 0.f;
 #pragma unroll
@@ -413,15 +388,26 @@ __global__ void __launch_bounds__(kSelectThreads)
       for (int e = 0; e < EPL; ++e) qs[e] += f[e];
     }
   }
-  const T *idx = static_cast<const T *>(pool.unit_index) + (size_t)bg * pool.unit_cap * D;
-  float *sc = scores + (size_t)bg * pool.unit_cap;
-  const int wbase = blockIdx.x * kScoreUnitsPerBlock + wave * 64;
+}
+
+// One wave scores units [u0, u0 + 64) (those below U): s_u = qs . idx_u in
+// fp32, a fixed summation order per unit whichever wave computes it; scores
+// go out with device-coherent stores.
+template <typename T, int D>
+__device__ __forceinline__ void score_units64(const T *__restrict__ idx, float *sc,
+                                              const float (&qs)[16 / Elem<T>::kBytes], int u0,
+                                              int U, int lane) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per 16-byte lane load
+  constexpr int LPU = D / EPL;               // lanes per index vector
+  constexpr int UPW = 64 / LPU;              // units per wave instruction
+  constexpr int UNR = 4;
+  const int part = lane % LPU, slot = lane / LPU;
 #pragma unroll
   for (int j0 = 0; j0 < 64; j0 += UPW * UNR) {
     uint4 v[UNR];
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
-      const int u = wbase + j0 + i * UPW + slot;
+      const int u = u0 + j0 + i * UPW + slot;
       v[i] = u < U ? *reinterpret_cast<const uint4 *>(idx + (size_t)u * D + part * EPL)
                    : uint4{0u, 0u, 0u, 0u};
     }
@@ -433,24 +419,41 @@ __global__ void __launch_bounds__(kSelectThreads)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dot = fmaf(qs[e], f[e], dot);
       dot = group_sum<LPU>(dot);
-      const int u = wbase + j0 + i * UPW + slot;
+      const int u = u0 + j0 + i * UPW + slot;
       if (part == 0 && u < U) coherent_store(&sc[u], dot);
     }
   }
+}
 
-  // ---- completion: the last block of (b, g) selects. Unit sizes are
-  // requested before the arrival so that they land with the store acks.
+// Unit sizes of this thread's KPT consecutive units (tid KPT ..), 0 past U.
+template <int KPT>
+__device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U, int (&sz)[KPT]) {
   const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
-  int sz[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int u = tid * KPT + j;
+    const int u = threadIdx.x * KPT + j;
     const int s = u < U ? usz[u] : 0;
     sz[j] = s > 0 ? s : 0;
   }
-  __shared__ int s_last;
-  if (!last_block_arrives(&counters[bg], (int)gridDim.x, &s_last)) return;
+}
 
+// The selection proper, run by the one workgroup of NT threads that holds all
+// of (b, g)'s scores: every candidate becomes a 64-bit key (orderable score
+// << 32 | ~id), KPT consecutive units per thread; an MSB-first weighted radix
+// select (per-wave LDS histograms hw / hc [NT / 64][256], one 8-bit digit
+// per pass, early exit once the crossing bucket holds a single unit) finds
+// the first unit that no longer fits the budget; every unit ranked before it
+// is written, in ascending id, to sel_units (and its row span to sel_spans),
+// with sel_n and sel_rows. Ends with a barrier.
+template <int NT, int KPT>
+__device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, const float *sc,
+                                    const int (&sz)[KPT], int32_t *__restrict__ sel_units,
+                                    int sel_cap, int32_t *__restrict__ sel_n,
+                                    int32_t *__restrict__ sel_rows,
+                                    int32_t *__restrict__ sel_spans, int (*hw)[256],
+                                    int (*hc)[256]) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned long long key[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -458,8 +461,6 @@ __global__ void __launch_bounds__(kSelectThreads)
     key[j] = sz[j] > 0 ? unit_key(coherent_load(&sc[u]), u) : 0ull;
   }
 
-  __shared__ int hw[kSelectWaves][256];
-  __shared__ int hc[kSelectWaves][256];
   __shared__ int tw[256];
   __shared__ int tc[256];
   __shared__ unsigned long long hk[256];
@@ -473,7 +474,7 @@ __global__ void __launch_bounds__(kSelectThreads)
     s_none = 0;
   }
   for (int sh = 56; sh >= 0; sh -= 8) {
-    for (int i = tid; i < kSelectWaves * 256; i += kSelectThreads) {
+    for (int i = tid; i < NW * 256; i += NT) {
       (&hw[0][0])[i] = 0;
       (&hc[0][0])[i] = 0;
     }
@@ -492,7 +493,7 @@ __global__ void __launch_bounds__(kSelectThreads)
     if (tid < 256) {
       int w = 0, c = 0;
 #pragma unroll
-      for (int v = 0; v < kSelectWaves; ++v) {
+      for (int v = 0; v < NW; ++v) {
         w += hw[v][tid];
         c += hc[v][tid];
       }
@@ -534,7 +535,7 @@ __global__ void __launch_bounds__(kSelectThreads)
       ++cnt;
       rows += sz[j];
     }
-  __shared__ int wsum[kSelectWaves], wrows[kSelectWaves];
+  __shared__ int wsum[NW], wrows[NW];
   int incl = cnt, rincl = rows;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -550,7 +551,7 @@ __global__ void __launch_bounds__(kSelectThreads)
   }
   __syncthreads();
   int off = 0, total = 0, total_rows = 0;
-  for (int w = 0; w < kSelectWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) off += wsum[w];
     total += wsum[w];
     total_rows += wrows[w];
@@ -577,8 +578,65 @@ __global__ void __launch_bounds__(kSelectThreads)
     }
     sel_n[bg] = total;
     sel_rows[bg] = total_rows;
-    __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __syncthreads();
+}
+
+// FUSED: the workgroup first runs the boundary test of its sequence on
+// (q_prev, q) itself (flag_out / r_out written once per sequence) instead of
+// reading flag. The unit count and the group's queries are requested in the
+// same memory round trip as the decision's inputs.
+template <typename T, int D, int KPT, bool FUSED>
+__global__ void __launch_bounds__(kSelectThreads)
+    k_select(kv_pool pool, const T *__restrict__ q, int hq, int group, int budget,
+             const uint8_t *__restrict__ flag, int32_t *__restrict__ sel_units, int sel_cap,
+             int32_t *__restrict__ sel_n, int32_t *__restrict__ sel_rows,
+             int32_t *__restrict__ sel_spans, float *__restrict__ scores,
+             int32_t *counters, const T *__restrict__ q_prev, float tau,
+             uint8_t *__restrict__ flag_out, float *__restrict__ r_out) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;
+  const int H = pool.n_kv_heads;
+  const int bg = blockIdx.y, b = bg / H, g = bg % H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n_cand = pool.n_cand[b];
+  uint4 qv[8];
+  score_query_load<T, D>(q, hq, b, g, group, lane, qv);
+  if constexpr (FUSED) {
+    __shared__ float s_part[4];
+    int f = 1;
+    float rv = __builtin_nanf("");
+    if (q_prev != nullptr) {
+      rv = boundary_r<T, D>(q_prev, q, hq, b, s_part);
+      f = rv < tau ? 1 : 0;
+    }
+    if (blockIdx.x == 0 && g == 0 && tid == 0) {
+      flag_out[b] = (uint8_t)f;
+      if (r_out) r_out[b] = rv;
+    }
+    if (!f) return;
+  } else {
+    if (flag != nullptr && flag[b] == 0) return;
+  }
+  const int U = min(max(n_cand, 0), pool.unit_cap);
+
+  // ---- scoring: s_u = (sum_h q_h) . idx_u, fp32
+  float qs[EPL];
+  score_query_sum<T, D>(qv, group, qs);
+  const T *idx = static_cast<const T *>(pool.unit_index) + (size_t)bg * pool.unit_cap * D;
+  float *sc = scores + (size_t)bg * pool.unit_cap;
+  score_units64<T, D>(idx, sc, qs, blockIdx.x * kScoreUnitsPerBlock + wave * 64, U, lane);
+
+  // ---- completion: the last block of (b, g) selects. Unit sizes are
+  // requested before the arrival so that they land with the store acks.
+  int sz[KPT];
+  select_sizes<KPT>(pool, bg, U, sz);
+  __shared__ int s_last;
+  if (!last_block_arrives(&counters[bg], (int)gridDim.x, &s_last)) return;
+  __shared__ int hw[kSelectWaves][256];
+  __shared__ int hc[kSelectWaves][256];
+  select_prefix_block<kSelectThreads, KPT>(pool, bg, budget, sc, sz, sel_units, sel_cap, sel_n,
+                                           sel_rows, sel_spans, hw, hc);
+  if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 int select_num_blocks(const kv_pool *pool) {
@@ -974,6 +1032,82 @@ struct AttendFetch {
                         // rows the copy has just read (pool in device memory)
 };
 
+// One whole decode step in the attention launch (kv_decode_step): the
+// boundary test and, on a retrieval step, the scoring and the selection run
+// inside it; otherwise as working-set mode. Null q_prev: first step.
+struct DecodeStep {
+  const uint16_t *q_prev;
+  float tau;
+  int budget;
+  int group;
+  uint8_t *flag;           // [batch] out
+  float *r;                // [batch] out, or null
+  int32_t *sel_units;      // [BH][sel_cap] out on retrieval steps
+  int32_t *sel_n;          // [BH]
+  int32_t *sel_rows;       // [BH]
+  int32_t *sel_spans;      // [BH][sel_cap][2]
+  int sel_cap;
+  float *scores;           // [BH][unit_cap] scratch
+  int32_t *sel_counters;   // [BH] scoring arrivals; zero between calls
+  int32_t *gen;            // [BH] selection generation; any start value
+  int32_t *status;         // pool status word
+};
+
+// Bounded wait of a workgroup for the selection of its (b, g) (a spin that
+// has not seen it after this many sleeps reports KV_ERR_HIP and goes on).
+constexpr int kStepSpinLimit = 1 << 22;
+
+// Retrieval step of kv_decode_step, run by all nsplit workgroups of (b, g):
+// each scores its share of the units, the last one to finish selects (the
+// same functions and arithmetic as k_select, so the same scores and the same
+// set bit for bit), publishes the selection with an agent-scope release and
+// bumps gen[bg]; the others wait for gen[bg] to move past the value they read
+// at launch (gen0, thread 0 only) and acquire. The selecting workgroup is
+// already running when the others wait, and it waits for nobody, so the wait
+// always ends. hw / hc: LDS for the radix histograms.
+template <int NT, int D, int KPT>
+__device__ void step_select(const kv_pool &pool, const DecodeStep &st,
+                            const uint16_t *__restrict__ q, int hq, int b, int g, int bg,
+                            int split, int nsplit, int gen0, int (*hw)[256], int (*hc)[256],
+                            int *s_last) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int U = min(max(pool.n_cand[b], 0), pool.unit_cap);
+  uint4 qv[8];
+  score_query_load<uint16_t, D>(q, hq, b, g, st.group, lane, qv);
+  float qs[8];
+  score_query_sum<uint16_t, D>(qv, st.group, qs);
+  const uint16_t *idx = static_cast<const uint16_t *>(pool.unit_index) + (size_t)bg * pool.unit_cap * D;
+  float *sc = st.scores + (size_t)bg * pool.unit_cap;
+  const int ups = ((pool.unit_cap + nsplit - 1) / nsplit + 63) / 64 * 64;  // units per workgroup
+  const int u_hi = min(U, (split + 1) * ups);
+  for (int u0 = split * ups + wave * 64; u0 < u_hi; u0 += NW * 64)
+    score_units64<uint16_t, D>(idx, sc, qs, u0, u_hi, lane);
+  int sz[KPT];
+  select_sizes<KPT>(pool, bg, U, sz);
+  if (last_block_arrives(&st.sel_counters[bg], nsplit, s_last)) {
+    select_prefix_block<NT, KPT>(pool, bg, st.budget, sc, sz, st.sel_units, st.sel_cap,
+                                 st.sel_n, st.sel_rows, st.sel_spans, hw, hc);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // every wave's selection stores
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_store(&st.sel_counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&st.gen[bg], gen0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (tid == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&st.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen0) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins >= kStepSpinLimit) {
+        __hip_atomic_store(st.status, (int)KV_ERR_HIP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the selection as published
+}
+
 // Rows [r_lo, r_hi) of the concatenated selection (n units, r_sel rows, in
 // s_psum / s_start) from the pool to the same positions of the working set,
 // kCopyUnroll 16-byte pieces in flight per thread, in passes of
@@ -1102,14 +1236,19 @@ __device__ __forceinline__ void attend_chunk_fold(AttendChunk<D> &c, const bf16x
 // spilling, so they fold one chunk at a time.
 template <int G> constexpr bool kAttendPipelined = G == 2 || G == 4;
 
-template <int D, int G, bool BUF>
+// STEP_KPT > 0 (working-set mode, no local buffer): the whole decode step, see
+// DecodeStep; the selection lists and flag of fx / sel_* are then outputs.
+template <int D, int G, bool BUF, int STEP_KPT = 0>
 __global__ void __launch_bounds__(kAttendThreads)
     k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
                          const int32_t *__restrict__ sel_units,
                          const int32_t *__restrict__ sel_spans, int sel_cap,
                          const int32_t *__restrict__ sel_n, int rcap, float *__restrict__ out,
-                         float *__restrict__ partials, int32_t *counters, AttendFetch fx) {
+                         float *__restrict__ partials, int32_t *counters, AttendFetch fx,
+                         DecodeStep st = DecodeStep{}) {
   static_assert(G <= 16, "query columns of one MFMA tile");
+  constexpr bool DSTEP = STEP_KPT > 0;
+  static_assert(!(DSTEP && BUF), "a decode step in one launch has no local buffer");
   constexpr int NT = kAttendThreads, NW = kAttendWaves;
   constexpr int KS = D / 32;
   constexpr int LPR = D / 8;
@@ -1167,11 +1306,28 @@ __global__ void __launch_bounds__(kAttendThreads)
   // all of them are in flight at once.
   int ws_flag = 0, ws_cnt = 0;
   int2 ws_sp = {0, 0};
+  int gen0 = 0;
   if (ws_mode) {
-    ws_flag = fx.flag[b];
+    if (!DSTEP) ws_flag = fx.flag[b];
     if (!BUF) {
       ws_cnt = fx.count[bg];
       ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * bg);
+    }
+  }
+  if constexpr (DSTEP) {
+    // the step's retrieval decision, taken here by every workgroup of the
+    // sequence with the same function as k_boundary (so the same bits)
+    if (tid == 0) gen0 = __hip_atomic_load(&st.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __shared__ float s_part[4];
+    float rv = __builtin_nanf("");
+    ws_flag = 1;
+    if (st.q_prev != nullptr) {
+      rv = boundary_r<uint16_t, D>(st.q_prev, q, hq, b, s_part);
+      ws_flag = rv < st.tau ? 1 : 0;
+    }
+    if (split == 0 && g == 0 && tid == 0) {
+      st.flag[b] = (uint8_t)ws_flag;
+      if (st.r) st.r[b] = rv;
     }
   }
   const int ws_n = min(max(ws_cnt, 0), 1);
@@ -1191,12 +1347,21 @@ __global__ void __launch_bounds__(kAttendThreads)
     }
     __syncthreads();
   } else {
-    const int scap = from_ws ? 1 : sel_cap;
-    const int32_t *su = from_ws ? nullptr : sel_units;
-    const int32_t *sp = from_ws ? fx.spans : sel_spans;
+    if constexpr (DSTEP) {
+      // retrieval step: select now (the radix histograms borrow s_psum, free until
+      // the selection is loaded into it below)
+      int(*hw)[256] = reinterpret_cast<int(*)[256]>(s_psum);
+      int(*hc)[256] = reinterpret_cast<int(*)[256]>(s_psum + NW * 256);
+      static_assert(2 * NW * 256 <= kMaxSel, "histograms fit s_psum");
+      step_select<NT, D, STEP_KPT>(pool, st, q, hq, b, g, bg, split, nsplit, gen0, hw, hc,
+                                   &s_last);
+    }
+    const int scap = from_ws ? 1 : (DSTEP ? st.sel_cap : sel_cap);
+    const int32_t *su = (from_ws || DSTEP) ? nullptr : sel_units;
+    const int32_t *sp = from_ws ? fx.spans : (DSTEP ? st.sel_spans : sel_spans);
     r_sel = attend_load_selection<NT>(
         pool, bg, su ? su + (size_t)bg * scap : nullptr, sp ? sp + (size_t)bg * scap * 2 : nullptr,
-        from_ws ? fx.count : sel_n, scap, &n, s_psum, s_start, s_wsum);
+        from_ws ? fx.count : (DSTEP ? st.sel_n : sel_n), scap, &n, s_psum, s_start, s_wsum);
   }
   const int r_all = r_sel;
   if (fetching) r_sel = min(r_sel, fx.cap);
@@ -1698,6 +1863,68 @@ kv_status launch_fetch_attend(const kv_pool *pool, const void *q, int hq, float 
   AttendFetch fx{flag, dst->k, dst->v, dst->row_cap, dst_spans, dst_n, reread};
   return attend_launch(pool, q, hq, scale, sel_units, sel_spans, sel_cap, sel_n, nsplit, rcap, out,
                        partials, counters, fx, s);
+}
+
+// The whole decode step in one launch (bf16 pool without a local buffer):
+// boundary test, on retrieval steps scoring + selection, working-set fetch
+// and attention. The split over workgroups is kv_fetch_attend's for
+// max_rows = budget, so the outputs equal kv_boundary_select followed by
+// kv_fetch_attend bit for bit.
+template <int D>
+static kv_status decode_step_dispatch(const kv_pool *pool, const void *q, int hq,
+                                      float scale_log2, int nsplit, int rcap, float *out,
+                                      float *partials, int32_t *counters, const AttendFetch &fx,
+                                      const DecodeStep &st, hipStream_t s) {
+  const int G = hq / pool->n_kv_heads;
+  const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
+  const bool small = pool->unit_cap <= kAttendThreads * 4;
+#define KVC_STEP(GG, KPT)                                                                     \
+  k_gather_attend_mfma<D, GG, false, KPT><<<grid, kAttendThreads, 0, s>>>(                   \
+      *pool, (const uint16_t *)q, hq, scale_log2, nullptr, nullptr, 1, nullptr, rcap, out,    \
+      partials, counters, fx, st)
+#define KVC_STEP2(GG)       \
+  do {                      \
+    if (small)              \
+      KVC_STEP(GG, 4);      \
+    else                    \
+      KVC_STEP(GG, 16);     \
+  } while (0)
+  switch (G) {
+    case 1: KVC_STEP2(1); break;
+    case 2: KVC_STEP2(2); break;
+    case 4: KVC_STEP2(4); break;
+    case 8: KVC_STEP2(8); break;
+    default: return KV_ERR_UNSUPPORTED;
+  }
+#undef KVC_STEP2
+#undef KVC_STEP
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+kv_status launch_decode_step(const kv_pool *pool, const void *q_prev, const void *q, int hq,
+                             float tau, float scale, int budget, uint8_t *flag, float *r,
+                             int32_t *sel_units, int32_t *sel_spans, int sel_cap, int32_t *sel_n,
+                             int32_t *sel_rows, int nsplit, int rcap, const kv_pool *dst,
+                             int32_t *dst_spans, int32_t *dst_n, float *out, float *partials,
+                             int32_t *counters, float *scores, int32_t *sel_counters,
+                             int32_t *gen, hipStream_t s) {
+  static_assert(kAttendThreads * 16 >= 8192, "16 selection keys per thread cover 8192 units");
+  if (pool->dtype != KV_BF16 || pool->buf_cap > 0) return KV_ERR_UNSUPPORTED;
+  hipPointerAttribute_t attr;
+  int reread = 1;
+  if (hipPointerGetAttributes(&attr, pool->k) == hipSuccess)
+    reread = attr.type == hipMemoryTypeDevice ? 0 : 1;
+  else
+    (void)hipGetLastError();
+  AttendFetch fx{flag, dst->k, dst->v, dst->row_cap, dst_spans, dst_n, reread};
+  DecodeStep st{(const uint16_t *)q_prev, tau, budget, hq / pool->n_kv_heads, flag, r, sel_units,
+                sel_n, sel_rows, sel_spans, sel_cap, scores, sel_counters, gen, pool->status};
+  const float sl2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = exp2(x log2 e)
+  return pool->head_dim == 128
+             ? decode_step_dispatch<128>(pool, q, hq, sl2, nsplit, rcap, out, partials,
+                                         counters, fx, st, s)
+             : decode_step_dispatch<64>(pool, q, hq, sl2, nsplit, rcap, out, partials, counters,
+                                        fx, st, s);
 }
 
 }  // namespace kvc

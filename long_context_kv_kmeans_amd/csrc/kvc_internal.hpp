@@ -211,6 +211,13 @@ kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
                         const void *q_prev, float tau, uint8_t *flag_out, float *r_out,
                         hipStream_t s);
 int attend_num_splits(const kv_pool *pool, int max_rows);
+kv_status launch_decode_step(const kv_pool *pool, const void *q_prev, const void *q, int hq,
+                             float tau, float scale, int budget, uint8_t *flag, float *r,
+                             int32_t *sel_units, int32_t *sel_spans, int sel_cap, int32_t *sel_n,
+                             int32_t *sel_rows, int nsplit, int rcap, const kv_pool *dst,
+                             int32_t *dst_spans, int32_t *dst_n, float *out, float *partials,
+                             int32_t *counters, float *scores, int32_t *sel_counters,
+                             int32_t *gen, hipStream_t s);
 int attend_row_bound(const kv_pool *pool, int max_rows);
 kv_status launch_gather_attend(const kv_pool *pool, const void *q, int hq, float scale,
                                const int32_t *sel_units, const int32_t *sel_spans, int sel_cap,

@@ -93,7 +93,8 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     fused_append: boundary test and segment append through kv_boundary_segment_append.
     fetch: on retrieval steps kv_fetch_selected copies the selected rows into an
     HBM working set, and attention reads the working set; fetch="fused" does
-    both through kv_fetch_attend.
+    both through kv_fetch_attend; fetch="step" runs the whole step (boundary
+    test, selection, fetch, attention) through kv_decode_step.
     flags: device [T, B] uint8 retrieval decisions to use instead of the boundary
     test's (kv_boundary still writes r; the selection follows the given flags)."""
     T = q.shape[0] if steps is None else steps
@@ -101,6 +102,7 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     H = pool.n_kv_heads
     dev = q.device
     rec = DecodeRecord()
+    rec.wset = None
     rec.flag = torch.zeros(T, B, dtype=torch.uint8, device=dev)
     rec.r = torch.zeros(T, B, dtype=torch.float32, device=dev)
     rec.out = torch.zeros(T, B, Hq, d, dtype=torch.float32, device=dev)
@@ -112,10 +114,18 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
     sel_rows = torch.zeros(B, H, dtype=torch.int32, device=dev)
     ws_sel = kvc.workspace(kvc.kv_select_workspace(pool, Hq))
     ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(pool, Hq, budget))
-    sel_spans = torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device=dev) if spans else None
+    step = fetch == "step"
+    sel_spans = (torch.zeros(B, H, sel_cap, 2, dtype=torch.int32, device=dev)
+                 if spans or step else None)
     wset = working_set(pool, max(budget, 1)) if fetch else None
+    ws_step = kvc.workspace(kvc.kv_decode_step_workspace(pool, Hq, budget)) if step else None
     for t in range(T):
-        if flags is not None:
+        if step:
+            assert flags is None and dec_k is None
+            kvc.kv_decode_step(pool, q[t - 1] if t else None, q[t], tau, scale, budget,
+                               rec.flag[t], sel_units, sel_spans, sel_n, sel_rows, wset,
+                               wset.spans, wset.count, rec.out[t], r=rec.r[t], ws=ws_step)
+        elif flags is not None:
             assert not fused and dec_k is None
             kvc.kv_boundary(q[t - 1] if t else None, q[t], tau, rec.flag[t], rec.r[t])
             rec.flag[t].copy_(flags[t])
@@ -136,7 +146,9 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
                     kvc.kv_segment_append(pool, dec_k[t], dec_v[t], rec.flag[t])
             kvc.kv_select(pool, q[t], budget, rec.flag[t], sel_units, sel_n, sel_rows, ws=ws_sel,
                           sel_spans=sel_spans)
-        if fetch == "fused":
+        if step:
+            pass
+        elif fetch == "fused":
             kvc.kv_fetch_attend(pool, q[t], scale, rec.flag[t], None if spans else sel_units,
                                 sel_n, budget, wset, wset.spans, wset.count, rec.out[t],
                                 ws=ws_att, sel_spans=sel_spans)
@@ -156,6 +168,7 @@ def gpu_decode(pool, q, tau, budget, scale, sel_cap, dec_k=None, dec_v=None, ste
                                    pool.seg_begin)):
                 rec.counters[t, i].copy_(c)
     torch.cuda.synchronize()
+    rec.wset = wset
     return rec
 
 

@@ -428,3 +428,40 @@ def test_noalloc_attention_validation():
     assert L.kv_gather_attend_workspace(ctypes.byref(big), 64, 4096) > 4 << 20
     assert L.kv_gather_attend_noalloc(ctypes.byref(big), a, 64, c01, a, None, 4096, a, 4096, a,
                                       None) == kvc.KV_ERR_WORKSPACE
+
+
+def test_decode_step_validation():
+    """kv_decode_step: bf16 pools without a local buffer, a distinct working set of the
+    same shape, every output pointer, a big enough selection list and workspace."""
+    L = kvc.lib()
+    a = ctypes.c_void_p(0x10000)
+    f07, c01 = ctypes.c_float(0.7), ctypes.c_float(0.1)
+    src = _fake_pool()
+    dst = _fake_pool(row_cap=512, unit_cap=1)
+    dst.k, dst.v = 0x20000, 0x30000
+    need = L.kv_decode_step_workspace(ctypes.byref(src), 32, 512)
+    assert need > L.kv_gather_attend_workspace(ctypes.byref(src), 32, 512)
+
+    def call(src_=None, dst_=None, hq=32, budget=512, su=a, sp=a, cap=512, out=a, ws_bytes=need,
+             q=a, tau=f07):
+        return L.kv_decode_step(ctypes.byref(src_ or src), None, q, hq, tau, c01, budget, a,
+                                None, su, sp, cap, a, a, ctypes.byref(dst_ or dst), a, a, out, a,
+                                ws_bytes, None)
+    # everything valid except the (dummy) workspace size: KV_ERR_WORKSPACE comes last
+    assert call(ws_bytes=need - 1) == kvc.KV_ERR_WORKSPACE
+    assert call(q=None) == kvc.KV_ERR_INVALID_ARG
+    assert call(su=None) == kvc.KV_ERR_INVALID_ARG
+    assert call(sp=None) == kvc.KV_ERR_INVALID_ARG
+    assert call(out=None) == kvc.KV_ERR_INVALID_ARG
+    assert call(tau=ctypes.c_float(float("nan"))) == kvc.KV_ERR_INVALID_ARG
+    assert call(hq=24) == kvc.KV_ERR_UNSUPPORTED  # G = 3
+    assert call(cap=100) == kvc.KV_ERR_CAPACITY    # below min(budget, unit_cap)
+    assert call(budget=5000, cap=4097) == kvc.KV_ERR_UNSUPPORTED
+    assert call(src_=_fake_pool(dtype=kvc.KV_F32)) == kvc.KV_ERR_UNSUPPORTED
+    assert call(src_=_fake_pool(buf_cap=64, seg_sum=0x10000)) == kvc.KV_ERR_UNSUPPORTED
+    assert call(src_=_fake_pool(unit_cap=8193)) == kvc.KV_ERR_UNSUPPORTED
+    same = _fake_pool(row_cap=512, unit_cap=1)  # k, v alias the source's
+    assert call(dst_=same) == kvc.KV_ERR_INVALID_ARG
+    other = _fake_pool(row_cap=512, unit_cap=1, n_kv_heads=4)
+    other.k, other.v = 0x20000, 0x30000
+    assert call(dst_=other) == kvc.KV_ERR_INVALID_ARG

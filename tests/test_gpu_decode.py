@@ -155,7 +155,7 @@ def test_decode_loop_parity(cfg_idx, over, steps, seqs):
     assert st["retrievals"] >= 1
 
 
-@pytest.mark.parametrize("attend", ["wset", "pool"])
+@pytest.mark.parametrize("attend", ["step", "wset", "pool"])
 def test_decode_full_size_cfg1_benchmark_path(attend):
     # the Qwen3-8B-shaped layer at full size (8 KV heads x 32768 keys, C = 2048, 256 steps)
     # through the calls the benchmark times: kv_boundary_select with row spans, then
@@ -163,23 +163,24 @@ def test_decode_full_size_cfg1_benchmark_path(attend):
     # spans (bench.py --attend pool). Two Lloyd rounds suffice: the clustering only sets
     # up the pool, and full-size K-means has its own sampled test.
     cfg = wl.get_config(1, iters=2)
-    kw = dict(fetch="fused") if attend == "wset" else {}
-    st = _run(cfg, cfg.steps, [0], compare_every=8, fused=True, spans=True, **kw)
+    kw = (dict(fetch="fused", fused=True) if attend == "wset" else
+          dict(fetch="step") if attend == "step" else dict(fused=True))
+    st = _run(cfg, cfg.steps, [0], compare_every=8, spans=True, **kw)
     assert st["retrievals"] >= 2
 
 
-@pytest.mark.parametrize("attend", ["wset", "pool"])
+@pytest.mark.parametrize("attend", ["step", "wset", "pool"])
 def test_decode_full_size_cfg4_batch16_benchmark_path(attend):
     # batched decode at full size: 16 sequences x 8 KV heads x 32768 keys in one launch,
     # budget 1024; sequences 0 and 9 carry the oracle's clustering and are checked
     cfg = wl.get_config(4, iters=2)
-    kw = dict(fetch="fused") if attend == "wset" else {}
-    st = _run(cfg, 128, list(range(16)), compare_every=8, check=[0, 9], fused=True,
-              spans=True, **kw)
+    kw = (dict(fetch="fused", fused=True) if attend == "wset" else
+          dict(fetch="step") if attend == "step" else dict(fused=True))
+    st = _run(cfg, 128, list(range(16)), compare_every=8, check=[0, 9], spans=True, **kw)
     assert st["retrievals"] >= 2
 
 
-@pytest.mark.parametrize("attend", ["wset", "pool"])
+@pytest.mark.parametrize("attend", ["step", "wset", "pool"])
 def test_decode_full_size_cfg3_layer_shape(attend):
     # one layer of the long-input long-output workload at full size: 8 KV heads x 131072
     # keys, 8192 units, budget 2048, 1024 steps, through the benchmark's calls.
@@ -188,9 +189,9 @@ def test_decode_full_size_cfg3_layer_shape(attend):
     # clustered, and Lloyd at this size in the fp64 oracle would take hours (full-size
     # K-means has its own sampled test).
     cfg = wl.get_config(3)
-    kw = dict(fetch="fused") if attend == "wset" else {}
-    st = _run(cfg, cfg.steps, [0], compare_every=16, clustering="fixed", fused=True,
-              spans=True, **kw)
+    kw = (dict(fetch="fused", fused=True) if attend == "wset" else
+          dict(fetch="step") if attend == "step" else dict(fused=True))
+    st = _run(cfg, cfg.steps, [0], compare_every=16, clustering="fixed", spans=True, **kw)
     assert st["retrievals"] >= 2
 
 
@@ -312,8 +313,8 @@ def test_decode_cfg3_two_layers_through_captured_graphs():
     """Two layers of the 36-layer long-input long-output workload (131072 keys per KV
     head, 8192 units, budget 2048), each with its own keys, pool, working set and
     query walk, through the benchmark's launch configuration: every decode step
-    runs kv_boundary_select -> kv_fetch_attend for layer 0 then layer 1, captured
-    into HIP graphs and replayed. Each layer is compared with its own oracle loop:
+    runs kv_decode_step (boundary test, selection, working-set fetch and attention
+    in one launch) for layer 0 then layer 1, captured into HIP graphs and replayed. Each layer is compared with its own oracle loop:
     flags and selected sets at every step, attention at every retrieval step and
     every 16th step. Both sides use the fixed clustering of the one-layer test."""
     import long_context_kv_kmeans_amd as kvc
@@ -341,8 +342,7 @@ def test_decode_cfg3_two_layers_through_captured_graphs():
         y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
         y.out = torch.zeros(B, Hq, d, dtype=torch.float32, device="cuda")
         y.wset = working_set(y.pool, cfg.budget)
-        y.ws_sel = kvc.workspace(kvc.kv_select_workspace(y.pool, Hq))
-        y.ws_att = kvc.workspace(kvc.kv_gather_attend_workspace(y.pool, Hq, cfg.budget))
+        y.ws_step = kvc.workspace(kvc.kv_decode_step_workspace(y.pool, Hq, cfg.budget))
         y.rec_out = torch.zeros(T, B, Hq, d, dtype=torch.float32, device="cuda")
         y.rec_sel = z(T, B, H, sel_cap)
         y.rec_n = z(T, B, H)
@@ -350,12 +350,10 @@ def test_decode_cfg3_two_layers_through_captured_graphs():
 
     def step(t):
         for y in layers:
-            kvc.kv_boundary_select(y.pool, y.qd[t - 1] if t else None, y.qd[t], cfg.tau,
-                                   cfg.budget, y.flags[t], y.sel, y.sel_n, y.sel_rows,
-                                   ws=y.ws_sel, sel_spans=y.spans)
-            kvc.kv_fetch_attend(y.pool, y.qd[t], cfg.scale, y.flags[t], None, y.sel_n,
-                                cfg.budget, y.wset, y.wset.spans, y.wset.count, y.out,
-                                ws=y.ws_att, sel_spans=y.spans)
+            kvc.kv_decode_step(y.pool, y.qd[t - 1] if t else None, y.qd[t], cfg.tau,
+                               cfg.scale, cfg.budget, y.flags[t], y.sel, y.spans, y.sel_n,
+                               y.sel_rows, y.wset, y.wset.spans, y.wset.count, y.out,
+                               ws=y.ws_step)
             y.rec_out[t].copy_(y.out)
             y.rec_sel[t].copy_(y.sel)
             y.rec_n[t].copy_(y.sel_n)
@@ -400,3 +398,45 @@ def test_decode_cfg3_two_layers_through_captured_graphs():
         # the two layers are different workloads: their walks retrieve at different steps
         if li == 1:
             assert not np.array_equal(flags, layers[0].flags.cpu().numpy().astype(bool)[:, 0])
+
+
+@pytest.mark.parametrize("cfg_idx,over,steps,seqs,host", [
+    (1, dict(n_keys=8192, n_clusters=512, n_components=128, iters=3), 96, [0], False),
+    (1, dict(n_keys=8192, n_clusters=512, n_components=128, iters=3, p_jump=0.3), 40, [0], True),
+    (1, dict(n_keys=3000, n_clusters=100, n_components=20, head_dim=64, n_q_heads=16,
+             iters=3, p_jump=0.2), 48, [0], False),
+    (1, dict(n_keys=2500, n_clusters=300, n_components=40, n_q_heads=64, iters=3,
+             p_jump=0.2), 48, [0], False),
+    (4, dict(n_keys=4096, n_clusters=256, n_components=64, iters=3, p_jump=0.2), 48, [0, 5, 9],
+     False),
+    (3, dict(n_keys=20000, n_clusters=8192, n_components=1024, iters=1, p_jump=0.2), 48, [0],
+     False),
+])
+def test_decode_step_one_launch_equals_two_launches(cfg_idx, over, steps, seqs, host):
+    """kv_decode_step == kv_boundary_select followed by kv_fetch_attend (max_rows =
+    budget), bit for bit: flags, r, selections, spans, working sets and outputs, for
+    group sizes 2, 4, 8, head dims 64 and 128, batches, a pool in host memory, many
+    retrievals, and 8192 units (the largest selection, 16 keys per thread)."""
+    cfg = wl.get_config(cfg_idx, **over)
+    inp = wl.layer_inputs(cfg, 0, seqs=seqs)
+    labels, cents = _fixed_clustering(inp["keys"], cfg.n_clusters)
+    q, _ = wl.layer_queries(cfg, 0, steps=steps, seqs=seqs)
+    qd = to_dev(q, cfg.dtype)
+    sel_cap = min(cfg.budget, cfg.n_clusters)
+    recs = []
+    for kw in (dict(fused=True, spans=True, fetch="fused"), dict(fetch="step")):
+        pool, _, _ = pool_from_labels(inp["keys"], inp["values"], labels, cents, cfg.dtype,
+                                      n_units=cfg.n_clusters, host_kv=host)
+        recs.append(gpu_decode(pool, qd, cfg.tau, cfg.budget, cfg.scale, sel_cap, **kw))
+        assert int(pool.status.item()) == 0
+    a, b = recs
+    assert int(a.flag.sum()) >= 3  # the first step and at least two jumps
+    for name in ("flag", "sel_n", "sel"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    ra, rb = a.r.cpu().numpy(), b.r.cpu().numpy()
+    np.testing.assert_array_equal(ra[1:].view(np.uint32), rb[1:].view(np.uint32))
+    assert np.isnan(rb[0]).all()
+    np.testing.assert_array_equal(a.out.cpu().numpy().view(np.uint32),
+                                  b.out.cpu().numpy().view(np.uint32))
+    assert torch.equal(a.wset.k, b.wset.k) and torch.equal(a.wset.spans, b.wset.spans)
+    assert torch.equal(a.wset.count, b.wset.count)
