@@ -15,6 +15,7 @@
 // its results with device-coherent stores and bumps a per-(sequence, head)
 // counter; the block that brings the counter to the grid size does the final
 // reduction in a fixed order and resets the counter to zero.
+#include <algorithm>
 #include <utility>
 
 #include "kvc_internal.hpp"
@@ -60,33 +61,69 @@ constexpr int kBoundaryHeadsPerWave = 8;
 // A head is read by LPH lanes with one 16-byte load each, so one wave
 // instruction covers HPI heads and the per-head sums reduce over LPH lanes
 // for all HPI heads at once; the HPI cosines then sum across lane groups.
-template <typename T, int D>
-__device__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
-                            int b, float *part) {
-  constexpr int EPL = 16 / (int)sizeof(T);  // elements per 16-byte load
-  constexpr int LPH = D / EPL;              // lanes per head
-  constexpr int HPI = 64 / LPH;             // heads per wave instruction
-  constexpr int HPW = kBoundaryHeadsPerWave;
-  constexpr int NI = HPW / HPI;             // load instructions per tensor and wave step
+// The loads of each wave's first HPW heads can be requested ahead
+// (boundary_prefetch), so that a caller with other loads in flight does not
+// wait for them before the test; boundary_r_pre then finishes the test with
+// the same arithmetic as boundary_r.
+template <typename T, int D> struct BoundaryFirst {
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per 16-byte load
+  static constexpr int LPH = D / EPL;              // lanes per head
+  static constexpr int HPI = 64 / LPH;             // heads per wave instruction
+  static constexpr int HPW = kBoundaryHeadsPerWave;
+  static constexpr int NI = HPW / HPI;             // load instructions per tensor and wave step
   static_assert(HPW % HPI == 0 && (LPH == 8 || LPH == 16 || LPH == 32), "head layout");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int sub = lane / LPH, piece = lane % LPH;
-  if (wave < 4) {
+  uint4 a[NI], c[NI];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void boundary_load_step(const T *__restrict__ q_prev,
+                                                   const T *__restrict__ q_cur, int hq, int b,
+                                                   int h0, BoundaryFirst<T, D> &f) {
+  using F = BoundaryFirst<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / F::LPH, piece = lane % F::LPH;
+#pragma unroll
+  for (int i = 0; i < F::NI; ++i) {
+    const int h = h0 + i * F::HPI + sub;
+    const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + piece * F::EPL;
+    f.a[i] = *reinterpret_cast<const uint4 *>(q_prev + o);
+    f.c[i] = *reinterpret_cast<const uint4 *>(q_cur + o);
+  }
+}
+
+// W0: the first of the four waves that run the test (its role 0); the roles,
+// not the wave numbers, decide the arithmetic.
+template <typename T, int D, int W0 = 0>
+__device__ __forceinline__ void boundary_prefetch(const T *__restrict__ q_prev,
+                                                  const T *__restrict__ q_cur, int hq, int b,
+                                                  BoundaryFirst<T, D> &f) {
+  const int wave = (int)(threadIdx.x >> 6) - W0;
+  if (wave >= 0 && wave < 4 && wave * kBoundaryHeadsPerWave < hq)
+    boundary_load_step<T, D>(q_prev, q_cur, hq, b, wave * kBoundaryHeadsPerWave, f);
+}
+
+// The four test waves' share: each writes its cosine sum to part[role].
+template <typename T, int D, int W0 = 0>
+__device__ __forceinline__ void boundary_partial(const T *__restrict__ q_prev,
+                                                 const T *__restrict__ q_cur, int hq, int b,
+                                                 float *part, const BoundaryFirst<T, D> &first) {
+  using F = BoundaryFirst<T, D>;
+  constexpr int EPL = F::EPL, LPH = F::LPH, HPI = F::HPI, HPW = F::HPW, NI = F::NI;
+  const int wave = (int)(threadIdx.x >> 6) - W0, lane = threadIdx.x & 63;
+  const int sub = lane / LPH;
+  if (wave >= 0 && wave < 4) {
     float csum = 0.f;
     for (int h0 = wave * HPW; h0 < hq; h0 += 4 * HPW) {
-      uint4 a[NI], c[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int h = h0 + i * HPI + sub;
-        const size_t o = ((size_t)b * hq + (h < hq ? h : 0)) * D + piece * EPL;
-        a[i] = *reinterpret_cast<const uint4 *>(q_prev + o);
-        c[i] = *reinterpret_cast<const uint4 *>(q_cur + o);
-      }
+      F f;
+      if (h0 == wave * HPW)
+        f = first;
+      else
+        boundary_load_step<T, D>(q_prev, q_cur, hq, b, h0, f);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float x[EPL], y[EPL];
-        unpack16<T>(a[i], x);
-        unpack16<T>(c[i], y);
+        unpack16<T>(f.a[i], x);
+        unpack16<T>(f.c[i], y);
         float dot = 0.f, n1 = 0.f, n2 = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -103,8 +140,27 @@ __device__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ 
     }
     if (lane == 0) part[wave] = csum;
   }
+}
+
+// r from the four shares (every thread of the workgroup must call).
+__device__ __forceinline__ float boundary_combine(const float *part, int hq) {
   __syncthreads();
   return (((part[0] + part[1]) + part[2]) + part[3]) / (float)hq;
+}
+
+template <typename T, int D, int W0 = 0>
+__device__ float boundary_r_pre(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
+                                int b, float *part, const BoundaryFirst<T, D> &first) {
+  boundary_partial<T, D, W0>(q_prev, q_cur, hq, b, part, first);
+  return boundary_combine(part, hq);
+}
+
+template <typename T, int D>
+__device__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
+                            int b, float *part) {
+  BoundaryFirst<T, D> f;
+  boundary_prefetch<T, D>(q_prev, q_cur, hq, b, f);
+  return boundary_r_pre<T, D>(q_prev, q_cur, hq, b, part, f);
 }
 
 template <typename T, int D>
@@ -1238,7 +1294,7 @@ template <int G> constexpr bool kAttendPipelined = G == 2 || G == 4;
 
 // STEP_KPT > 0 (working-set mode, no local buffer): the whole decode step, see
 // DecodeStep; the selection lists and flag of fx / sel_* are then outputs.
-template <int D, int G, bool BUF, int STEP_KPT = 0>
+template <int D, int G, bool BUF, int STEP_KPT = 0, bool STEP_W47 = true>
 __global__ void __launch_bounds__(kAttendThreads)
     k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
                          const int32_t *__restrict__ sel_units,
@@ -1272,6 +1328,14 @@ __global__ void __launch_bounds__(kAttendThreads)
   // (query head col < G, else zero) and the same head-dimension entries as
   // the K fragments, so one K load instruction reads a contiguous 64-byte
   // span of each of 16 rows.
+  // kv_decode_step: the boundary test runs on waves 4-7. When a workgroup's
+  // chunk holds at most 128 rows (!STEP_W47) those waves request no rows, so
+  // the test runs while waves 0-3 wait for theirs; otherwise its loads go
+  // first and it waits with everything else.
+  constexpr int BW0 = NW - 4;
+  BoundaryFirst<uint16_t, D> bfirst;
+  if constexpr (DSTEP && STEP_W47)
+    if (st.q_prev != nullptr) boundary_prefetch<uint16_t, D, BW0>(st.q_prev, q, hq, b, bfirst);
   bf16x8a_t qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -1292,37 +1356,61 @@ __global__ void __launch_bounds__(kAttendThreads)
   // each wave requests its first 32 rows now, in the same memory round trip
   // as the flag and the span. A retrieval step (or any other span) discards
   // them and takes the general path.
-  AttendChunk<D> ca;
-  const int spec_chunk = (max(rcap, 1) + nsplit - 1) / nsplit;
-  const int spec_lo = split * spec_chunk;
-  if (!BUF && ws_mode && wave * kAttendChunk < spec_chunk)  // waves with rows in the chunk
-    attend_chunk_load_direct<D>(
-        ca, spec_lo + wave * kAttendChunk, fx.cap - 1,
-        static_cast<const uint16_t *>(fx.k) + (size_t)bg * fx.cap * D,
-        static_cast<const uint16_t *>(fx.v) + (size_t)bg * fx.cap * D, lane);
   // The flag and the working set's one span (read as attend_load_selection
-  // reads a one-entry list) are requested right behind the rows; every value
-  // feeds the test below, so none of the loads is deferred into a branch and
-  // all of them are in flight at once.
+  // reads a one-entry list) are requested with the rows; every value feeds
+  // the test below, so none of the loads is deferred into a branch and all of
+  // them are in flight at once. kv_fetch_attend requests them right behind
+  // the rows (it waits for all of them at once anyway); kv_decode_step right
+  // before them, so that its boundary test runs while the rows are in flight.
   int ws_flag = 0, ws_cnt = 0;
   int2 ws_sp = {0, 0};
   int gen0 = 0;
-  if (ws_mode) {
-    if (!DSTEP) ws_flag = fx.flag[b];
-    if (!BUF) {
-      ws_cnt = fx.count[bg];
-      ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * bg);
+  auto ws_loads = [&]() {
+    if (ws_mode) {
+      if (!DSTEP) ws_flag = fx.flag[b];
+      if (!BUF) {
+        ws_cnt = fx.count[bg];
+        ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * bg);
+      }
     }
+    if constexpr (DSTEP)
+      if (tid == 0) gen0 = __hip_atomic_load(&st.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if constexpr (DSTEP) ws_loads();
+  AttendChunk<D> ca;
+  const int spec_chunk = (max(rcap, 1) + nsplit - 1) / nsplit;
+  const int spec_lo = split * spec_chunk;
+  auto spec_rows = [&]() {
+    if (!BUF && ws_mode && wave * kAttendChunk < spec_chunk)  // waves with rows in the chunk
+      attend_chunk_load_direct<D>(
+          ca, spec_lo + wave * kAttendChunk, fx.cap - 1,
+          static_cast<const uint16_t *>(fx.k) + (size_t)bg * fx.cap * D,
+          static_cast<const uint16_t *>(fx.v) + (size_t)bg * fx.cap * D, lane);
+  };
+  __shared__ float s_part[4];
+  if constexpr (DSTEP && !STEP_W47) {
+    if (wave >= BW0) {
+      if (st.q_prev != nullptr) {
+        boundary_prefetch<uint16_t, D, BW0>(st.q_prev, q, hq, b, bfirst);
+        boundary_partial<uint16_t, D, BW0>(st.q_prev, q, hq, b, s_part, bfirst);
+      }
+    } else {
+      spec_rows();
+    }
+  } else {
+    spec_rows();
   }
+  if constexpr (!DSTEP) ws_loads();
   if constexpr (DSTEP) {
     // the step's retrieval decision, taken here by every workgroup of the
     // sequence with the same function as k_boundary (so the same bits)
-    if (tid == 0) gen0 = __hip_atomic_load(&st.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __shared__ float s_part[4];
     float rv = __builtin_nanf("");
     ws_flag = 1;
     if (st.q_prev != nullptr) {
-      rv = boundary_r<uint16_t, D>(st.q_prev, q, hq, b, s_part);
+      if constexpr (!STEP_W47)
+        rv = boundary_combine(s_part, hq);
+      else
+        rv = boundary_r_pre<uint16_t, D, BW0>(st.q_prev, q, hq, b, s_part, bfirst);
       ws_flag = rv < st.tau ? 1 : 0;
     }
     if (split == 0 && g == 0 && tid == 0) {
@@ -1877,17 +1965,18 @@ static kv_status decode_step_dispatch(const kv_pool *pool, const void *q, int hq
                                       const DecodeStep &st, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
-  const bool small = pool->unit_cap <= kAttendThreads * 4;
-#define KVC_STEP(GG, KPT)                                                                     \
-  k_gather_attend_mfma<D, GG, false, KPT><<<grid, kAttendThreads, 0, s>>>(                   \
+  // do waves 4-7 get rows of the first pass (a chunk of more than 4 x 32 rows)?
+  const bool w47 = (std::max(rcap, 1) + nsplit - 1) / nsplit > (kAttendWaves - 4) * kAttendChunk;
+#define KVC_STEP(GG, W47)                                                                     \
+  k_gather_attend_mfma<D, GG, false, 16, W47><<<grid, kAttendThreads, 0, s>>>(               \
       *pool, (const uint16_t *)q, hq, scale_log2, nullptr, nullptr, 1, nullptr, rcap, out,    \
       partials, counters, fx, st)
 #define KVC_STEP2(GG)       \
   do {                      \
-    if (small)              \
-      KVC_STEP(GG, 4);      \
+    if (w47)                \
+      KVC_STEP(GG, true);   \
     else                    \
-      KVC_STEP(GG, 16);     \
+      KVC_STEP(GG, false);  \
   } while (0)
   switch (G) {
     case 1: KVC_STEP2(1); break;
