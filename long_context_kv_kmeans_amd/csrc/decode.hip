@@ -37,6 +37,23 @@ __device__ __forceinline__ void coherent_store(float *p, float v) {
 __device__ __forceinline__ float coherent_load(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void coherent_store_i(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t coherent_load_i(const int32_t *p) {
+  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store_i2(int32_t *p, int2 v) {
+  const unsigned long long u = (unsigned long long)(uint32_t)v.x | ((unsigned long long)(uint32_t)v.y << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), u, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int2 coherent_load_i2(const int32_t *p) {
+  const unsigned long long u = __hip_atomic_load(
+      reinterpret_cast<unsigned long long *>(const_cast<int32_t *>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return int2{(int)(uint32_t)u, (int)(uint32_t)(u >> 32)};
+}
 __device__ __forceinline__ bool last_block_arrives(int32_t *counter, int nblocks, int *s_last) {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's coherent stores are acknowledged
   __syncthreads();
@@ -501,7 +518,7 @@ __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U,
 // the first unit that no longer fits the budget; every unit ranked before it
 // is written, in ascending id, to sel_units (and its row span to sel_spans),
 // with sel_n and sel_rows. Ends with a barrier.
-template <int NT, int KPT>
+template <int NT, int KPT, bool COH = false>
 __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, const float *sc,
                                     const int (&sz)[KPT], int32_t *__restrict__ sel_units,
                                     int sel_cap, int32_t *__restrict__ sel_n,
@@ -622,7 +639,12 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
       if (pos < sel_cap) {
         const int u = tid * KPT + j;
         out[pos] = u;
-        if (spans) *reinterpret_cast<int2 *>(spans + 2 * pos) = int2{ust[u], sz[j]};
+        if (spans) {
+          if constexpr (COH)
+            coherent_store_i2(spans + 2 * pos, int2{ust[u], sz[j]});
+          else
+            *reinterpret_cast<int2 *>(spans + 2 * pos) = int2{ust[u], sz[j]};
+        }
       }
       ++pos;
     }
@@ -632,7 +654,10 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
                          __HIP_MEMORY_SCOPE_AGENT);
       total = sel_cap;
     }
-    sel_n[bg] = total;
+    if constexpr (COH)
+      coherent_store_i(&sel_n[bg], total);
+    else
+      sel_n[bg] = total;
     sel_rows[bg] = total_rows;
   }
   __syncthreads();
@@ -775,7 +800,7 @@ __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
 // not used), so the ids, the length and the unit table cost two dependent
 // memory round trips whatever the length. Sets *n_out to the list length
 // (clamped to [0, sel_cap]) and returns the selection's row count.
-template <int NT>
+template <int NT, bool COH = false>
 __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t *su,
                                      const int32_t *spans, const int32_t *sel_n, int sel_cap,
                                      int *n_out, int *s_psum, int *s_start, int *s_wsum) {
@@ -791,11 +816,13 @@ __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t 
 #pragma unroll
     for (int j = 0; j < PER_MAX; ++j) {
       int2 v = {0, 0};
-      if (j < per && i0 + j < sel_cap) v = *reinterpret_cast<const int2 *>(spans + 2 * (i0 + j));
+      if (j < per && i0 + j < sel_cap)
+        v = COH ? coherent_load_i2(spans + 2 * (i0 + j))
+                : *reinterpret_cast<const int2 *>(spans + 2 * (i0 + j));
       st[j] = v.x;
       sz[j] = v.y;
     }
-    n = min(max(sel_n[bg], 0), sel_cap);
+    n = min(max(COH ? coherent_load_i(&sel_n[bg]) : sel_n[bg], 0), sel_cap);
 #pragma unroll
     for (int j = 0; j < PER_MAX; ++j) {
       const bool valid = j < per && i0 + j < n;
@@ -1076,6 +1103,35 @@ __device__ __forceinline__ void attend_chunk_load_direct(AttendChunk<D> &c, int 
   }
 }
 
+// A chunk's valid rows (positions it .. it + 31 below plen of the piece that
+// starts at position p0) stored from the registers they were loaded into to
+// rows p0 + position of a working set (wk, wv: its K and V of (b, g)): the
+// inverse of attend_chunk_load's lane layout, so each row is written whole,
+// once.
+template <int D>
+__device__ __forceinline__ void attend_chunk_store(const AttendChunk<D> &c, int it, int plen,
+                                                   int p0, uint16_t *wk, uint16_t *wv, int lane) {
+  using C = AttendChunk<D>;
+  const int col = lane & 15, quad = lane >> 4;
+  const int vpart = lane % C::LPR, sub = (lane & 15) / C::LPR;
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk) {
+    const int li = it + tk * 16 + col;
+    if (li < plen) {
+      uint16_t *kr = wk + (size_t)(p0 + li) * D;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s)
+        *reinterpret_cast<uint4 *>(kr + 32 * s + 8 * quad) = __builtin_bit_cast(uint4, c.kf[tk][s]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::VU; ++i) {
+    const int k = i * C::RPL + sub;
+    const int li = it + 16 * (k >> 2) + 4 * quad + (k & 3);
+    if (li < plen) *reinterpret_cast<uint4 *>(wv + (size_t)(p0 + li) * D + 8 * vpart) = c.vv[i];
+  }
+}
+
 // Working-set mode of the attention (fetch fused in): flag null = off.
 struct AttendFetch {
   const uint8_t *flag;  // [batch]: 1 = retrieval step (fetch), 0 = read the working set
@@ -1116,11 +1172,13 @@ constexpr int kStepSpinLimit = 1 << 22;
 // Retrieval step of kv_decode_step, run by all nsplit workgroups of (b, g):
 // each scores its share of the units, the last one to finish selects (the
 // same functions and arithmetic as k_select, so the same scores and the same
-// set bit for bit), publishes the selection with an agent-scope release and
-// bumps gen[bg]; the others wait for gen[bg] to move past the value they read
-// at launch (gen0, thread 0 only) and acquire. The selecting workgroup is
-// already running when the others wait, and it waits for nobody, so the wait
-// always ends. hw / hc: LDS for the radix histograms.
+// set bit for bit), publishes the spans and the count with device-coherent
+// stores, waits for their acknowledgements and bumps gen[bg] (the completion
+// protocol of last_block_arrives); the others wait for gen[bg] to move past
+// the value they read at launch (gen0, thread 0 only) and then read the
+// selection with device-coherent loads. The selecting workgroup is already
+// running when the others wait, and it waits for nobody, so the wait always
+// ends. hw / hc: LDS for the radix histograms.
 template <int NT, int D, int KPT>
 __device__ void step_select(const kv_pool &pool, const DecodeStep &st,
                             const uint16_t *__restrict__ q, int hq, int b, int g, int bg,
@@ -1142,9 +1200,9 @@ __device__ void step_select(const kv_pool &pool, const DecodeStep &st,
   int sz[KPT];
   select_sizes<KPT>(pool, bg, U, sz);
   if (last_block_arrives(&st.sel_counters[bg], nsplit, s_last)) {
-    select_prefix_block<NT, KPT>(pool, bg, st.budget, sc, sz, st.sel_units, st.sel_cap,
-                                 st.sel_n, st.sel_rows, st.sel_spans, hw, hc);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // every wave's selection stores
+    select_prefix_block<NT, KPT, true>(pool, bg, st.budget, sc, sz, st.sel_units, st.sel_cap,
+                                       st.sel_n, st.sel_rows, st.sel_spans, hw, hc);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's coherent stores are acknowledged
     __syncthreads();
     if (tid == 0) {
       __hip_atomic_store(&st.sel_counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1161,7 +1219,6 @@ __device__ void step_select(const kv_pool &pool, const DecodeStep &st,
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the selection as published
 }
 
 // Rows [r_lo, r_hi) of the concatenated selection (n units, r_sel rows, in
@@ -1447,7 +1504,7 @@ __global__ void __launch_bounds__(kAttendThreads)
     const int scap = from_ws ? 1 : (DSTEP ? st.sel_cap : sel_cap);
     const int32_t *su = (from_ws || DSTEP) ? nullptr : sel_units;
     const int32_t *sp = from_ws ? fx.spans : (DSTEP ? st.sel_spans : sel_spans);
-    r_sel = attend_load_selection<NT>(
+    r_sel = attend_load_selection<NT, DSTEP>(
         pool, bg, su ? su + (size_t)bg * scap : nullptr, sp ? sp + (size_t)bg * scap * 2 : nullptr,
         from_ws ? fx.count : (DSTEP ? st.sel_n : sel_n), scap, &n, s_psum, s_start, s_wsum);
   }
@@ -1462,13 +1519,15 @@ __global__ void __launch_bounds__(kAttendThreads)
   const int chunk = (max(R, rcap) + nsplit - 1) / nsplit;
   const int r_lo = min(R, split * chunk), r_hi = min(R, r_lo + chunk);
 
+  // Retrieval step of working-set mode: the rows this workgroup attends,
+  // [r_lo, r_hi) of the selection, also go to the same positions of the
+  // working set. Without a local buffer each chunk is stored from the
+  // registers the attention loads it into (every row crosses the host link,
+  // for a pool in host memory, once); with one, a copy pass runs first and
+  // the attention reads the pool rows it has brought into L2 (device memory)
+  // or the working set (host memory).
+  const bool store_ws = !BUF && fetching;  // uniform
   if (fetching) {
-    // Retrieval step of working-set mode: this workgroup copies the rows it
-    // is about to attend, [r_lo, r_hi) of the selection, from the pool into
-    // the working set, then attends over them: for a pool in device memory
-    // over the same pool rows, which the copy has just brought into L2 (the
-    // stores need not land first); for a pool in host memory over the
-    // working set, so that no row crosses the host link twice.
     if (split == 0 && tid == 0) {
       fx.spans[2 * bg] = 0;
       fx.spans[2 * bg + 1] = r_sel;
@@ -1477,9 +1536,10 @@ __global__ void __launch_bounds__(kAttendThreads)
         __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    attend_copy_rows<NT, D>(pool, bg, fx, min(r_lo, r_sel), min(r_hi, r_sel), n, r_sel, s_psum,
-                            s_start, s_rowtab);
-    if (fx.reread) {
+    if (!store_ws)
+      attend_copy_rows<NT, D>(pool, bg, fx, min(r_lo, r_sel), min(r_hi, r_sel), n, r_sel, s_psum,
+                              s_start, s_rowtab);
+    if (!store_ws && fx.reread) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the copies are written
       __syncthreads();
       if (tid == 0) {  // the selection is now the working set's one span
@@ -1490,8 +1550,13 @@ __global__ void __launch_bounds__(kAttendThreads)
       __syncthreads();
     }
   }
-  const bool read_ws = ws_mode && (!fetching || fx.reread);
+  const bool read_ws = ws_mode && (!fetching || (!store_ws && fx.reread));
   const int row_cap = read_ws ? fx.cap : pool.row_cap;
+  uint16_t *wsk = nullptr, *wsv = nullptr;
+  if (store_ws) {
+    wsk = static_cast<uint16_t *>(fx.k) + (size_t)bg * fx.cap * D;
+    wsv = static_cast<uint16_t *>(fx.v) + (size_t)bg * fx.cap * D;
+  }
 
   // Online softmax state. m_run / l_run: per query head `col`, identical in
   // the four lanes col, col+16, col+32, col+48. acc: p.v partial sums of this
@@ -1538,10 +1603,12 @@ __global__ void __launch_bounds__(kAttendThreads)
       if (it < plen && !preloaded) load(ca, it);
       while (it < plen) {
         if (it + STEP < plen) load(cb, it + STEP);
+        if (store_ws) attend_chunk_store<D>(ca, it, plen, p0, wsk, wsv, lane);
         attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
         if (it >= plen) break;
         if (it + STEP < plen) load(ca, it + STEP);
+        if (store_ws) attend_chunk_store<D>(cb, it, plen, p0, wsk, wsv, lane);
         attend_chunk_fold<D, G>(cb, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
         it += STEP;
       }
@@ -1549,6 +1616,7 @@ __global__ void __launch_bounds__(kAttendThreads)
       for (; it < plen; it += STEP) {
         if (!preloaded) load(ca, it);
         preloaded = false;
+        if (store_ws) attend_chunk_store<D>(ca, it, plen, p0, wsk, wsv, lane);
         attend_chunk_fold<D, G>(ca, qf, it, plen, scale_log2, m_run, l_run, acc, lane);
       }
     }
@@ -1967,16 +2035,20 @@ static kv_status decode_step_dispatch(const kv_pool *pool, const void *q, int hq
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
   // do waves 4-7 get rows of the first pass (a chunk of more than 4 x 32 rows)?
   const bool w47 = (std::max(rcap, 1) + nsplit - 1) / nsplit > (kAttendWaves - 4) * kAttendChunk;
-#define KVC_STEP(GG, W47)                                                                     \
-  k_gather_attend_mfma<D, GG, false, 16, W47><<<grid, kAttendThreads, 0, s>>>(               \
+  const bool small = pool->unit_cap <= kAttendThreads * 4;  // 4 selection keys per thread
+#define KVC_STEP(GG, KPT, W47)                                                                \
+  k_gather_attend_mfma<D, GG, false, KPT, W47><<<grid, kAttendThreads, 0, s>>>(              \
       *pool, (const uint16_t *)q, hq, scale_log2, nullptr, nullptr, 1, nullptr, rcap, out,    \
       partials, counters, fx, st)
-#define KVC_STEP2(GG)       \
-  do {                      \
-    if (w47)                \
-      KVC_STEP(GG, true);   \
-    else                    \
-      KVC_STEP(GG, false);  \
+#define KVC_STEP2(GG)                                  \
+  do {                                                 \
+    if (small) {                                       \
+      if (w47) KVC_STEP(GG, 4, true);                  \
+      else KVC_STEP(GG, 4, false);                     \
+    } else {                                           \
+      if (w47) KVC_STEP(GG, 16, true);                 \
+      else KVC_STEP(GG, 16, false);                    \
+    }                                                  \
   } while (0)
   switch (G) {
     case 1: KVC_STEP2(1); break;
