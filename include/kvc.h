@@ -367,14 +367,14 @@ kv_status kv_fetch_selected(const kv_pool *pool, const uint8_t *flag, const int3
  *   kv_gather_attend(dst, q, n_q_heads, scale, NULL, dst_spans, 1, dst_n,
  *                    max_rows, out, ws, ws_bytes);
  * with the same working set, spans, status and output bit for bit. On a
- * retrieval step (flag[b] != 0) each attention workgroup copies the rows it
- * is about to attend from the pool into the working set and attends over
- * them (over the pool rows it has just read when the pool is in device
- * memory, over the working set when it is in host memory, so that no row
- * crosses the host link twice); on other steps it reads the working set
- * only, requesting its first rows together with the flag and the span, so
- * a step without retrieval costs one launch and one memory round trip
- * before the rows arrive. fp32 pools run the two launches.
+ * retrieval step (flag[b] != 0) each attention workgroup stores the rows it
+ * attends, as it loads them from the pool, into the working set (from the
+ * same registers, so each row is read once, also over the host link); with
+ * a local buffer it copies them in a pass of its own first. On other steps
+ * it reads the working set only, requesting its first rows together with
+ * the flag and the span, so a step without retrieval costs one launch and
+ * one memory round trip before the rows arrive. fp32 pools run the two
+ * launches.
  * A pool with decode segments (buf_cap > 0; bf16, with buf_k / buf_v set)
  * is supported too: the attended rows are then the working set followed by
  * the local buffer, read from the pool's HBM copy, i.e. exactly the rows
@@ -403,11 +403,12 @@ kv_status kv_fetch_attend(const kv_pool *pool, const void *q, int32_t n_q_heads,
  * of its sequence itself; on a step without retrieval it goes straight to
  * the working set; on a retrieval step the workgroups of (b, g) first score
  * the units (each its share), the last to finish selects and publishes the
- * selection (release), the others wait for it (acquire; the selecting
- * workgroup is already running and waits for nothing, so the wait ends),
- * and all of them then copy and attend as kv_fetch_attend does. A wait that
- * does not end after about 2^22 sleeps would set *pool->status to
- * KV_ERR_HIP. bf16 pools without a local buffer (buf_cap 0), in device or
+ * selection (device-coherent stores, acknowledged before a generation
+ * counter moves), the others wait for the counter (the selecting workgroup
+ * is already running and waits for nothing, so the wait ends) and read it
+ * with device-coherent loads, and all of them then fetch and attend as
+ * kv_fetch_attend does. A wait that does not end after about 2^22 sleeps
+ * would set *pool->status to KV_ERR_HIP. bf16 pools without a local buffer (buf_cap 0), in device or
  * host memory; unit_cap <= 8192; sel_cap >= min(budget, unit_cap), <= 4096.
  * sel_units and sel_spans are outputs ([BH][sel_cap] and [BH][sel_cap][2]
  * int32), written on retrieval steps only, like sel_n and sel_rows ([BH]).
