@@ -430,8 +430,12 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
 //                 label's counts in the earlier parts, added in part order)
 //                 and the chunk's label histogram;
 //  k_colscan   -- per label, exclusive prefix of the histograms over chunks
-//                 and the label's total;
-//  k_startscan -- exclusive scan of totals over labels (cluster starts);
+//                 and the label's total; per block of 256 labels, each
+//                 label's exclusive prefix of totals within the block and
+//                 the block's total (cluster start = the sum of the earlier
+//                 blocks' totals + the in-block prefix: at most 32 blocks up
+//                 to 8192 labels, so every consumer adds them up itself and
+//                 no separate scan over labels is launched);
 //  k_scatter   -- perm[start[a] + chunk_prefix[a] + rank] = key.
 // A label outside [0, c) takes no part: its key gets no rank, no histogram
 // count and no place in the permutation (reported through *status when given).
@@ -500,37 +504,51 @@ __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict
   }
 }
 
-__global__ void k_colscan(int32_t *__restrict__ hist, int32_t *__restrict__ tot, int c,
-                          int nchunk) {
-  const int bh = blockIdx.y, k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= c) return;
-  int32_t run = 0;
-  int32_t *col = hist + (size_t)bh * nchunk * c + k;
-  int ch = 0;
-  for (; ch + 8 <= nchunk; ch += 8) {
-    int32_t h[8];
+constexpr int kLabelBlock = 256;  // labels per k_colscan workgroup
+
+// Sum over the wave of an int (every lane gets it).
+__device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = col[(size_t)(ch + i) * c];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      col[(size_t)(ch + i) * c] = run;
-      run += h[i];
-    }
-  }
-  for (; ch < nchunk; ++ch) {
-    const int32_t h = col[(size_t)ch * c];
-    col[(size_t)ch * c] = run;
-    run += h;
-  }
-  tot[(size_t)bh * c + k] = run;
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
-// Block-wide exclusive scan of one int per thread (1024 threads); returns the
-// exclusive prefix and writes the block total to *total.
-__device__ int block_exclusive_scan_1024(int v, int *total) {
-  __shared__ int wsum[16];
+// Start of label blocks: the sum of the totals of blocks 0 .. blk - 1 of
+// head bh (one wave; blk <= 64).
+__device__ __forceinline__ int label_block_base(const int32_t *__restrict__ agg, int nblk,
+                                                int bh, int blk) {
+  const int lane = threadIdx.x & 63;
+  return wave_sum_i(lane < blk ? agg[(size_t)bh * nblk + lane] : 0);
+}
+
+__global__ void __launch_bounds__(kLabelBlock)
+    k_colscan(int32_t *__restrict__ hist, int32_t *__restrict__ tot, int32_t *__restrict__ ipre,
+              int32_t *__restrict__ agg, int32_t *__restrict__ counts, int c, int nchunk) {
+  __shared__ int wsum[kLabelBlock / 64];
+  const int bh = blockIdx.y, k = blockIdx.x * kLabelBlock + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+  int32_t run = 0;
+  if (k < c) {
+    int32_t *col = hist + (size_t)bh * nchunk * c + k;
+    int ch = 0;
+    for (; ch + 8 <= nchunk; ch += 8) {
+      int32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = col[(size_t)(ch + i) * c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        col[(size_t)(ch + i) * c] = run;
+        run += h[i];
+      }
+    }
+    for (; ch < nchunk; ++ch) {
+      const int32_t h = col[(size_t)ch * c];
+      col[(size_t)ch * c] = run;
+      run += h;
+    }
+  }
+  // exclusive prefix of the totals within the block of 256 labels
+  int incl = run;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o);
@@ -539,44 +557,44 @@ __device__ int block_exclusive_scan_1024(int v, int *total) {
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int off = 0, all = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+#pragma unroll
+  for (int w = 0; w < kLabelBlock / 64; ++w) {
     if (w < wave) off += wsum[w];
     all += wsum[w];
   }
-  __syncthreads();
-  *total = all;
-  return off + incl - v;
-}
-
-__global__ void __launch_bounds__(1024) k_startscan(const int32_t *__restrict__ tot,
-                                                    int32_t *__restrict__ start,
-                                                    int32_t *__restrict__ counts, int c) {
-  const int bh = blockIdx.x;
-  const int per = (c + 1023) / 1024;
-  const int lo = threadIdx.x * per;
-  const int hi = lo + per < c ? lo + per : c;
-  const int32_t *t = tot + (size_t)bh * c;
-  int local = 0;
-  for (int k = lo; k < hi; ++k) local += t[k];
-  int total;
-  int run = block_exclusive_scan_1024(local, &total);
-  for (int k = lo; k < hi; ++k) {
-    start[(size_t)bh * c + k] = run;
-    if (counts) counts[(size_t)bh * c + k] = t[k];
-    run += t[k];
+  if (k < c) {
+    tot[(size_t)bh * c + k] = run;
+    ipre[(size_t)bh * c + k] = off + incl - run;
+    if (counts) counts[(size_t)bh * c + k] = run;
   }
+  if (threadIdx.x == 0) agg[(size_t)bh * gridDim.x + blockIdx.x] = all;
 }
 
-__global__ void k_scatter(const int32_t *__restrict__ labels, const int32_t *__restrict__ rank,
-                          const int32_t *__restrict__ hist, const int32_t *__restrict__ start,
-                          int32_t *__restrict__ perm, int n, int c, int nchunk) {
+__global__ void __launch_bounds__(256)
+    k_scatter(const int32_t *__restrict__ labels, const int32_t *__restrict__ rank,
+              const int32_t *__restrict__ hist, const int32_t *__restrict__ ipre,
+              const int32_t *__restrict__ agg, int32_t *__restrict__ perm, int n, int c,
+              int nchunk) {
+  __shared__ int s_base[64];  // start of each block of 256 labels
   const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int a = labels[(size_t)bh * n + i];
-  if (a < 0 || a >= c) return;  // left out by k_rank_hist too
+  const int nblk = (c + kLabelBlock - 1) / kLabelBlock;
+  const int a = i < n ? labels[(size_t)bh * n + i] : -1;
+  if (threadIdx.x < 64) {  // wave 0: exclusive scan of the block totals
+    const int lane = threadIdx.x;
+    const int v = lane < nblk ? agg[(size_t)bh * nblk + lane] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    s_base[lane] = incl - v;
+  }
+  __syncthreads();
+  if (i >= n || a < 0 || a >= c) return;  // labels out of range: left out by k_rank_hist too
   const int ch = i / kRankChunk;
-  const int dest = start[(size_t)bh * c + a] + hist[((size_t)bh * nchunk + ch) * c + a] +
-                   rank[(size_t)bh * n + i];
+  const int dest = s_base[a / kLabelBlock] + ipre[(size_t)bh * c + a] +
+                   hist[((size_t)bh * nchunk + ch) * c + a] + rank[(size_t)bh * n + i];
   perm[(size_t)bh * n + dest] = i;
 }
 
@@ -587,10 +605,13 @@ __global__ void k_scatter(const int32_t *__restrict__ labels, const int32_t *__r
 // reproducible bit for bit). The mean replaces the centroid (an empty
 // cluster keeps its value). For bf16 keys the same pass writes the next
 // round's MFMA tiles (fragments and norm block), so no separate prep is needed.
+// start: the in-block label prefixes of k_colscan on entry; each wave adds
+// its block's base and writes the cluster's start back (the pack reads it).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
                                                 const int32_t *__restrict__ perm,
-                                                const int32_t *__restrict__ start,
+                                                int32_t *__restrict__ start,
+                                                const int32_t *__restrict__ agg,
                                                 const int32_t *__restrict__ tot,
                                                 const float *cent_in, float *cent_out,
                                                 uint16_t *__restrict__ frags, int n, int c,
@@ -605,7 +626,9 @@ __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
   const int part = lane % LPR, slot = lane / LPR;
   if (k >= c) return;
   const int cnt = tot[(size_t)bh * c + k];
-  const int st = start[(size_t)bh * c + k];
+  const int st = label_block_base(agg, (c + kLabelBlock - 1) / kLabelBlock, bh, k / kLabelBlock) +
+                 start[(size_t)bh * c + k];
+  if (lane == 0) start[(size_t)bh * c + k] = st;
   const int32_t *p = perm + (size_t)bh * n + st;
   const T *kb = keys + (size_t)bh * n * D + part * EPL;
   float acc[EPL];
@@ -679,6 +702,7 @@ size_t update_ws_bytes(int bh, int n, int c) {
   b += align_up((size_t)bh * c * 4, 256);           // tot
   b += align_up((size_t)bh * c * 4, 256);           // start
   b += align_up((size_t)bh * n * 4, 256);           // perm
+  b += align_up((size_t)bh * ((c + kLabelBlock - 1) / kLabelBlock) * 4, 256);  // block totals
   return b;
 }
 
@@ -698,6 +722,9 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   int32_t *start = reinterpret_cast<int32_t *>(w);
   w += align_up((size_t)bh * c * 4, 256);
   int32_t *perm = reinterpret_cast<int32_t *>(w);
+  w += align_up((size_t)bh * n * 4, 256);
+  int32_t *agg = reinterpret_cast<int32_t *>(w);
+  const int nblk = (c + kLabelBlock - 1) / kLabelBlock;
 
   // a chunk's label counts ([waves][c] int32) stay within 64 KB of LDS: 4 waves
   // per chunk up to 4096 labels, 2 up to kMaxClusters = 8192
@@ -708,26 +735,25 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   else
     k_rank_hist<2><<<dim3(nchunk, bh), 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
                                                                     ceil_log2(c), nchunk, status);
-  k_colscan<<<dim3((c + 255) / 256, bh), 256, 0, s>>>(hist, tot, c, nchunk);
-  k_startscan<<<bh, 1024, 0, s>>>(tot, start, counts, c);
-  k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, perm, n, c,
+  k_colscan<<<dim3(nblk, bh), kLabelBlock, 0, s>>>(hist, tot, start, agg, counts, c, nchunk);
+  k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, agg, perm, n, c,
                                                       nchunk);
   const dim3 g((c + 3) / 4, bh);
   uint16_t *fr = static_cast<uint16_t *>(frags_out);
   const int ntile = (c + 31) / 32;
   if (dt == KV_BF16) {
     if (d == 128)
-      k_segsum<uint16_t, 128><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, tot, cent_in,
+      k_segsum<uint16_t, 128><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, agg, tot, cent_in,
                                                 cent_out, fr, n, c, ntile);
     else
-      k_segsum<uint16_t, 64><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, tot, cent_in,
+      k_segsum<uint16_t, 64><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, agg, tot, cent_in,
                                                cent_out, fr, n, c, ntile);
   } else {
     if (d == 128)
-      k_segsum<float, 128><<<g, 256, 0, s>>>((const float *)keys, perm, start, tot, cent_in,
+      k_segsum<float, 128><<<g, 256, 0, s>>>((const float *)keys, perm, start, agg, tot, cent_in,
                                              cent_out, nullptr, n, c, ntile);
     else
-      k_segsum<float, 64><<<g, 256, 0, s>>>((const float *)keys, perm, start, tot, cent_in,
+      k_segsum<float, 64><<<g, 256, 0, s>>>((const float *)keys, perm, start, agg, tot, cent_in,
                                             cent_out, nullptr, n, c, ntile);
   }
   if (perm_out) *perm_out = perm;
