@@ -309,7 +309,7 @@ def main():
     # the whole layer-step in one launch where the path is boundary test -> select ->
     # fused fetch + attention
     one = (fetch and args.fetch == "fused" and not seg and sched is None
-           and args.launches == "one" and args.pool != "host-direct")
+           and args.launches == "one" and args.pool != "host-direct" and cfg.dtype == "bf16")
     if seg and (sched is not None or page is not None or (fetch and args.fetch == "separate")):
         raise SystemExit("with decode segments (--config 2) only --pool host|host-direct "
                          "(fused fetch) applies")
