@@ -131,7 +131,7 @@ def cpu_baseline(cfg, inp, q, lloyd_iters, dk=None, dv=None):
     t0 = time.perf_counter()
     pack = okm.pack(keys0, vals0, o["labels"], o["centroids"], cfg.dtype)
     t_pack = time.perf_counter() - t0
-    dec_steps = 16
+    dec_steps = min(64, cfg.steps)
     t0 = time.perf_counter()
     seg = {} if dk is None else dict(buf_cap=cfg.buf_cap, dec_k=dk[:dec_steps, 0, :1],
                                      dec_v=dv[:dec_steps, 0, :1])
@@ -235,8 +235,7 @@ def main():
                          "that fits one GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-lloyd-iters", type=int, default=None,
-                    help="Lloyd rounds the CPU oracle is timed on (default: 1 when a round "
-                         "takes more than ~2^28 key-cluster pairs, else 3)")
+                    help="Lloyd rounds the CPU oracle is timed on (default 3)")
     ap.add_argument("--gen-threads", type=int, default=None,
                     help="host threads drawing the synthetic inputs (default: min(16, cores))")
     ap.add_argument("--decode-steps", type=int, default=None,
@@ -729,7 +728,7 @@ def main():
         res["cpu_baseline"] = None  # the oracle's sample covers the standard path only
     elif not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        iters = args.cpu_lloyd_iters or (1 if N * C > (1 << 28) else 3)
+        iters = args.cpu_lloyd_iters or 3
         res["cpu_baseline"] = cpu_baseline(cfg, inp, q_np, iters, dk0, dv0)
     else:
         res["cpu_baseline"] = None
