@@ -22,6 +22,16 @@
 
 namespace kvc {
 
+// Zero in a register the compiler cannot prove uniform across the wave: a load
+// indexed by it stays a vector memory load. Scalar loads of the same data
+// would return out of order with the kernel-argument loads, so a later wait
+// for any argument would also wait for them.
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
 // Completion protocol for the last-block steps. Results that another
 // workgroup will read are written with device-coherent stores (relaxed
 // agent-scope atomic stores: `sc1` on gfx950, so they do not sit in this
@@ -173,7 +183,7 @@ __device__ float boundary_r_pre(const T *__restrict__ q_prev, const T *__restric
 }
 
 template <typename T, int D>
-__device__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
+__device__ __forceinline__ float boundary_r(const T *__restrict__ q_prev, const T *__restrict__ q_cur, int hq,
                             int b, float *part) {
   BoundaryFirst<T, D> f;
   boundary_prefetch<T, D>(q_prev, q_cur, hq, b, f);
@@ -922,7 +932,7 @@ __device__ __forceinline__ void merge_load_batch(float (&v)[EPT][kMergeBatch], c
 }
 
 template <int NT, int G, int D>
-__device__ void attend_finish(int bg, int b, int g, int hq, int nsplit, int split,
+__device__ __forceinline__ void attend_finish(int bg, int b, int g, int hq, int nsplit, int split,
                               const float (*s_m)[G], const float (*s_l)[G],
                               const float (*s_acc)[G][D], float *out, float *partials,
                               int32_t *counters, int *s_last) {
@@ -1040,6 +1050,20 @@ template <int D> struct AttendChunk {
   static constexpr int VU = 8 / RPL;    // V loads per lane
   bf16x8a_t kf[2][KS];
   uint4 vv[VU];
+};
+
+// A wave's p.v sums, relative to m_run.
+// D = 128 (kMfma): the products run on MFMA. For D = 128 a lane's V loads are
+// eight rows (the k-slots of its 16-lane row q = l/16, in load order) times
+// elements 8 (l%16) .. +7, which is the A operand of 16x16x32 tile j (M = the
+// elements 8 m + j, K = the 32 rows) once transposed in registers; the
+// probabilities of the same rows for head l%16 are already the B operand.
+// t[j] then holds, in lane l, element 8 (4 q + r) + j (entry r) for head l%16.
+// Other D: VALU sums a[h][e] of this lane's eight V elements per head h.
+template <int D, int G> struct AttendAcc {
+  static constexpr bool kMfma = D == 128;
+  f32x4_t t[kMfma ? 8 : 1];
+  float a[kMfma ? 1 : G][8];
 };
 
 // A row-table entry r >= 0 is row r of kbase / vbase; with BUF (the pool keeps
@@ -1268,14 +1292,16 @@ __device__ void attend_copy_rows(const kv_pool &pool, int bg, const AttendFetch 
 }
 
 // Fold one chunk into the wave's online-softmax state (m_run, l_run per
-// query head `col`, identical in the four lanes col + 16 q; acc per head for
-// this lane's V elements, relative to m_run). Probabilities and the rescale
-// factor move to the V lanes by row broadcasts: no LDS round trip.
+// query head `col`, identical in the four lanes col + 16 q; acc as described
+// at AttendAcc). VALU path: probabilities and the rescale factor move to the V
+// lanes by row broadcasts, no LDS round trip. MFMA path: each probability is
+// split into two bf16 parts (hi = RNE(p), lo = RNE(p - hi)), so the products
+// carry about 16 significant bits of p, and both parts go through the tile.
 template <int D, int G>
 __device__ __forceinline__ void attend_chunk_fold(AttendChunk<D> &c, const bf16x8a_t *qf,
                                                   int it, int plen, float scale_log2,
-                                                  float &m_run, float &l_run, float (*acc)[8],
-                                                  int lane) {
+                                                  float &m_run, float &l_run,
+                                                  AttendAcc<D, G> &acc, int lane) {
   using C = AttendChunk<D>;
   const int quad = lane >> 4, sub = (lane & 15) / C::LPR;
   if (it + kAttendChunk > plen) {
@@ -1319,28 +1345,62 @@ __device__ __forceinline__ void attend_chunk_fold(AttendChunk<D> &c, const bf16x
   ps = sum_xor32(sum_xor16(ps));
   l_run = l_run * alpha + ps;
   m_run = m_new;
-  static_for<G>([&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-    const float al = row_bcast<h>(alpha);
+  if constexpr (AttendAcc<D, G>::kMfma) {
+    // this lane's head is col = l%16, so alpha needs no broadcast
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-  });
+    for (int j = 0; j < 8; ++j) acc.t[j] *= alpha;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    u32x4_t ph, pl;
 #pragma unroll
-  for (int i = 0; i < C::VU; ++i) {
-    float vf[8];
-    unpack16<uint16_t>(c.vv[i], vf);
+    for (int k = 0; k < 4; ++k) {
+      const f32x2_t pp = {p[2 * k], p[2 * k + 1]};
+      const bf16x2_t h = __builtin_convertvector(pp, bf16x2_t);
+      const bf16x2_t l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+      ph[k] = __builtin_bit_cast(uint32_t, h);
+      pl[k] = __builtin_bit_cast(uint32_t, l);
+    }
+    const bf16x8a_t bh = __builtin_bit_cast(bf16x8a_t, ph), bl = __builtin_bit_cast(bf16x8a_t, pl);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // A of tile j: element j of each of the eight rows, rows in k-slot order
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      u32x4_t a;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint4 lo = c.vv[2 * w], hi = c.vv[2 * w + 1];
+        const uint32_t dl = (j >> 1) == 0 ? lo.x : (j >> 1) == 1 ? lo.y : (j >> 1) == 2 ? lo.z : lo.w;
+        const uint32_t dh = (j >> 1) == 0 ? hi.x : (j >> 1) == 1 ? hi.y : (j >> 1) == 2 ? hi.z : hi.w;
+        a[w] = __builtin_amdgcn_perm(dh, dl, sel);
+      }
+      const bf16x8a_t av = __builtin_bit_cast(bf16x8a_t, a);
+      acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc.t[j], 0, 0, 0);
+      acc.t[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc.t[j], 0, 0, 0);
+    }
+  } else {
     static_for<G>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
-      float pu;
-      if constexpr (C::RPL == 1) {
-        pu = row_bcast<h>(p[i]);
-      } else {
-        const float b0 = row_bcast<h>(p[i * C::RPL]), b1 = row_bcast<h>(p[i * C::RPL + 1]);
-        pu = sub ? b1 : b0;
-      }
+      const float al = row_bcast<h>(alpha);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pu, vf[e], acc[h][e]);
+      for (int e = 0; e < 8; ++e) acc.a[h][e] *= al;
     });
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i) {
+      float vf[8];
+      unpack16<uint16_t>(c.vv[i], vf);
+      static_for<G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        float pu;
+        if constexpr (C::RPL == 1) {
+          pu = row_bcast<h>(p[i]);
+        } else {
+          const float b0 = row_bcast<h>(p[i * C::RPL]), b1 = row_bcast<h>(p[i * C::RPL + 1]);
+          pu = sub ? b1 : b0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc.a[h][e] = fmaf(pu, vf[e], acc.a[h][e]);
+      });
+    }
   }
 }
 
@@ -1361,6 +1421,8 @@ __global__ void __launch_bounds__(kAttendThreads)
                          DecodeStep st = DecodeStep{}) {
   static_assert(G <= 16, "query columns of one MFMA tile");
   constexpr bool DSTEP = STEP_KPT > 0;
+  // kv_decode_step: its arguments (408 bytes) in one round trip, before anything
+  if constexpr (DSTEP) kernarg_warm<408>();
   static_assert(!(DSTEP && BUF), "a decode step in one launch has no local buffer");
   constexpr int NT = kAttendThreads, NW = kAttendWaves;
   constexpr int KS = D / 32;
@@ -1371,7 +1433,7 @@ __global__ void __launch_bounds__(kAttendThreads)
   __shared__ int s_rowtab[kAttendMfmaPiece];
   __shared__ int s_wsum[NW];
   __shared__ float s_m[NW][G], s_l[NW][G];
-  __shared__ float s_acc[NW][G][D];
+  __shared__ __align__(16) float s_acc[NW][G][D];
   __shared__ int s_last;
 
   const int H = pool.n_kv_heads;
@@ -1406,7 +1468,9 @@ __global__ void __launch_bounds__(kAttendThreads)
   // without retrieval) from the working set's one span; on a retrieval step
   // of working-set mode they come from the pool and are stored to the
   // working set as they are loaded.
-  const bool ws_mode = fx.flag != nullptr;
+  // (always for kv_decode_step: a compile-time true keeps its span loads out of
+  // a branch, whose merge would make the wave wait for them on the spot)
+  const bool ws_mode = DSTEP || fx.flag != nullptr;
   // Working-set mode without a local buffer: the working set's rows are
   // contiguous from row 0 and this workgroup's chunk starts at
   // split * ceil(rcap / nsplit) whenever the span holds at most rcap rows, so
@@ -1426,8 +1490,11 @@ __global__ void __launch_bounds__(kAttendThreads)
     if (ws_mode) {
       if (!DSTEP) ws_flag = fx.flag[b];
       if (!BUF) {
-        ws_cnt = fx.count[bg];
-        ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * bg);
+        // kv_decode_step: vector loads (see opaque_zero), so that the waits for
+        // kernel arguments before the test and the rows do not wait for these
+        const int z = DSTEP ? opaque_zero() : 0;
+        ws_cnt = fx.count[bg + z];
+        ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * (bg + z));
       }
     }
     if constexpr (DSTEP)
@@ -1562,11 +1629,16 @@ __global__ void __launch_bounds__(kAttendThreads)
   // the four lanes col, col+16, col+32, col+48. acc: p.v partial sums of this
   // lane's V rows, elements 8 vpart .. 8 vpart + 7, relative to m_run.
   float m_run = -INFINITY, l_run = 0.f;
-  float acc[G][8];
+  AttendAcc<D, G> acc;
+  if constexpr (AttendAcc<D, G>::kMfma) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int j = 0; j < 8; ++j) acc.t[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc.a[h][e] = 0.f;
+  }
 
   const uint16_t *kbase =
       static_cast<const uint16_t *>(read_ws ? fx.k : pool.k) + (size_t)bg * row_cap * D;
@@ -1624,16 +1696,29 @@ __global__ void __launch_bounds__(kAttendThreads)
     __syncthreads();
   }
 
-  // rows of one wave share m_run: lane groups combine by plain sums
+  if constexpr (AttendAcc<D, G>::kMfma) {
+    // the tiles already summed over the wave's rows
+    if (col < G) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = sum_stride<LPR>(acc[h][e]);
-  if (lane < LPR) {
+      for (int r = 0; r < 4; ++r) {
+        float *dst = &s_acc[wave][col][8 * (4 * quad + r)];
+        *reinterpret_cast<float4 *>(dst) = float4{acc.t[0][r], acc.t[1][r], acc.t[2][r], acc.t[3][r]};
+        *reinterpret_cast<float4 *>(dst + 4) =
+            float4{acc.t[4][r], acc.t[5][r], acc.t[6][r], acc.t[7][r]};
+      }
+    }
+  } else {
+    // rows of one wave share m_run: lane groups combine by plain sums
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vpart + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) acc.a[h][e] = sum_stride<LPR>(acc.a[h][e]);
+    if (lane < LPR) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * vpart + e] = acc.a[h][e];
+    }
   }
   if (lane < G) {
     s_m[wave][lane] = m_run;

@@ -146,6 +146,26 @@ template <int L> __device__ __forceinline__ float sum_stride(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// Requests every 64-byte line of the first BYTES of the kernel's argument
+// segment at once and waits for them. Left to itself the compiler loads an
+// argument where it is first needed, so each new line is a scalar-cache miss
+// and a wait of its own, one after another, before the first memory request
+// that depends on them. BYTES must lie inside the segment (the explicit
+// arguments, followed by at least 256 bytes of hidden ones).
+template <int BYTES> __device__ __forceinline__ void kernarg_warm() {
+  typedef const uint32_t __attribute__((address_space(4))) karg_u32;
+  karg_u32 *ka = (karg_u32 *)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int N = (BYTES + 63) / 64;
+  uint32_t w[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = ka[16 * i];
+  __builtin_amdgcn_sched_barrier(0);  // every request before the one wait
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) x ^= w[i];
+  asm volatile("" ::"s"(x));
+}
+
 // Map a hardware workgroup id to a logical one so that each XCD (which
 // receives ids x, x+8, x+16, ...) processes one contiguous range of logical
 // work; neighbouring logical blocks then share that XCD's L2.
