@@ -261,8 +261,8 @@ kv_status kv_boundary_segment_append(const kv_pool *pool, const void *q_prev, co
  * q: [batch][n_q_heads][head_dim] (dtype). sel_units: [BH][sel_cap] with
  * sel_cap >= min(budget, unit_cap). scores_out: NULL or [BH][unit_cap] fp32
  * (entries u >= n_cand[b] untouched). pool->unit_cap <= 8192
- * (KV_ERR_UNSUPPORTED above: each of the 1024 threads of a (b, g)'s last
- * workgroup holds at most 8 candidates' sort keys in registers).
+ * (KV_ERR_UNSUPPORTED above: each of the 512 threads of a (b, g)'s last
+ * workgroup holds at most 16 candidates' sort keys in registers).
  */
 size_t kv_select_workspace(const kv_pool *pool, int32_t n_q_heads);
 kv_status kv_select(const kv_pool *pool, const void *q, int32_t n_q_heads, int32_t budget,

@@ -292,7 +292,7 @@ kv_status select_common(const kv_pool *pool, const void *q, int32_t n_q_heads, i
   const int G = n_q_heads / pool->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
   if (sel_cap < (budget < pool->unit_cap ? budget : pool->unit_cap)) return KV_ERR_CAPACITY;
-  if (pool->unit_cap > 1024 * kSelectMaxKeysPerThread) return KV_ERR_UNSUPPORTED;
+  if (pool->unit_cap > kSelectBlockThreads * kSelectMaxKeysPerThread) return KV_ERR_UNSUPPORTED;
   const size_t need = kv_select_workspace(pool, n_q_heads);
   if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
   const size_t bh = (size_t)pool->batch * pool->n_kv_heads;
@@ -498,7 +498,7 @@ kv_status kv_decode_step(const kv_pool *pool, const void *q_prev, const void *q_
   if (pool->dtype != KV_BF16 || pool->buf_cap > 0) return KV_ERR_UNSUPPORTED;
   const int G = n_q_heads / pool->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
-  if (pool->unit_cap > 1024 * kSelectMaxKeysPerThread) return KV_ERR_UNSUPPORTED;
+  if (pool->unit_cap > kSelectBlockThreads * kSelectMaxKeysPerThread) return KV_ERR_UNSUPPORTED;
   if (sel_cap > kMaxSel) return KV_ERR_UNSUPPORTED;
   if (sel_cap < (budget < pool->unit_cap ? budget : pool->unit_cap)) return KV_ERR_CAPACITY;
   if (dst->batch != pool->batch || dst->n_kv_heads != pool->n_kv_heads ||

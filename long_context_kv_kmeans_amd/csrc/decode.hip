@@ -382,32 +382,31 @@ kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void
 }
 
 // ---------------------------------------------------------------- select
-// Scoring: 1024-thread workgroups each score up to 1024 units; a unit's index
+// Scoring: 512-thread workgroups each score up to 512 units; a unit's index
 // vector is read as 16-byte pieces, so one wave instruction covers 64 / LPU
 // units. Selection: the last workgroup of (b, g) holds every candidate as a
 // 64-bit key (orderable score << 32 | ~id) in registers, KPT consecutive
 // units per thread, and finds the first unit that no longer fits the budget
-// with an MSB-first weighted radix select (per-wave LDS histograms, one
-// digit of 8 bits per pass, early exit once the crossing bucket holds a
-// single unit). Every unit ranked before it is selected.
-constexpr int kSelectThreads = 1024;
+// with an MSB-first weighted radix select (per-wave LDS histograms, digits of
+// 8 bits starting at the highest bit in which the keys differ, early exit
+// once the crossing bucket holds a single unit). Every unit ranked before it
+// is selected.
+constexpr int kSelectThreads = kSelectBlockThreads;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int kScoreUnitsPerBlock = kSelectThreads;
 
-// Wave 0 helper: given per-digit weights w[0..255] (LDS), the weight already
-// above the range and the budget, find the highest digit whose inclusion
-// makes the running total (taken from the top digit down) exceed the budget.
-// Returns -1 if even all digits fit. *above_out = weight of digits above it.
-__device__ int find_crossing_digit(const int *w, long above, long budget, long *above_out) {
+// Wave 0 helper: lane l holds the weights wd[i] of digits 255 - 4 l - i
+// (i = 0..3, descending). Given the weight already above the range and the
+// budget, finds the highest digit whose inclusion makes the running total
+// (taken from the top digit down) exceed the budget: returns it, or -1 if
+// every digit fits, with *above_out = the weight of the digits above it and
+// *lane_out = the lane that owns it.
+__device__ int find_crossing_digit(const long (&wd)[4], long above, long budget, long *above_out,
+                                   int *lane_out) {
   const int lane = threadIdx.x & 63;
-  // lane l owns digits 255 - 4l .. 252 - 4l (descending)
   long local = 0;
-  int dg[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dg[i] = w[255 - 4 * lane - i];
-    local += dg[i];
-  }
+  for (int i = 0; i < 4; ++i) local += wd[i];
   long incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -421,18 +420,35 @@ __device__ int find_crossing_digit(const int *w, long above, long budget, long *
   if (run <= budget && above + incl > budget) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (found < 0 && run + dg[i] > budget) {
+      if (found < 0 && run + wd[i] > budget) {
         found = 255 - 4 * lane - i;
         found_above = run;
       }
-      run += dg[i];
+      run += wd[i];
     }
   }
   const uint64_t who = __ballot(found >= 0);
   if (who == 0) return -1;
   const int src = __ffsll((unsigned long long)who) - 1;
   *above_out = __shfl(found_above, src);
+  *lane_out = src;
   return __shfl(found, src);
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_or64(unsigned long long v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v |= __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_and64(unsigned long long v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v &= __shfl_xor(v, o);
+  return v;
 }
 
 __device__ __forceinline__ unsigned long long unit_key(float score, int u) {
@@ -483,7 +499,8 @@ __device__ __forceinline__ void score_units64(const T *__restrict__ idx, float *
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per 16-byte lane load
   constexpr int LPU = D / EPL;               // lanes per index vector
   constexpr int UPW = 64 / LPU;              // units per wave instruction
-  constexpr int UNR = 4;
+  // every load of the wave's 64 units in flight at once (one round trip)
+  constexpr int UNR = 64 / UPW < 16 ? 64 / UPW : 16;
   const int part = lane % LPU, slot = lane / LPU;
 #pragma unroll
   for (int j0 = 0; j0 < 64; j0 += UPW * UNR) {
@@ -512,11 +529,16 @@ __device__ __forceinline__ void score_units64(const T *__restrict__ idx, float *
 template <int KPT>
 __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U, int (&sz)[KPT]) {
   const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
+  // Every load is issued, at a clamped index, and masked afterwards: a load
+  // under a per-lane condition whose result is reshaped inside the branch
+  // makes the compiler wait for it there, one round trip per load.
+  int raw[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) raw[j] = usz[min((int)threadIdx.x * KPT + j, pool.unit_cap - 1)];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int u = threadIdx.x * KPT + j;
-    const int s = u < U ? usz[u] : 0;
-    sz[j] = s > 0 ? s : 0;
+    sz[j] = (u < U && raw[j] > 0) ? raw[j] : 0;
   }
 }
 
@@ -524,8 +546,10 @@ __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U,
 // of (b, g)'s scores: every candidate becomes a 64-bit key (orderable score
 // << 32 | ~id), KPT consecutive units per thread; an MSB-first weighted radix
 // select (per-wave LDS histograms hw / hc [NT / 64][256], one 8-bit digit
-// per pass, early exit once the crossing bucket holds a single unit) finds
-// the first unit that no longer fits the budget; every unit ranked before it
+// per pass from the highest bit in which the keys differ, a thread's run of
+// equal digits counted once and a wave whose keys share one digit counted
+// with one update, early exit once the crossing bucket holds a single unit)
+// finds the first unit that no longer fits the budget; every unit ranked before it
 // is written, in ascending id, to sel_units (and its row span to sel_spans),
 // with sel_n and sel_rows. Ends with a barrier.
 template <int NT, int KPT, bool COH = false>
@@ -538,63 +562,132 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned long long key[KPT];
+  unsigned long long kor = 0ull, kand = ~0ull;
+  float scv[KPT];  // all requested at once (clamped index), masked below
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) scv[j] = coherent_load(&sc[min(tid * KPT + j, pool.unit_cap - 1)]);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int u = tid * KPT + j;
-    key[j] = sz[j] > 0 ? unit_key(coherent_load(&sc[u]), u) : 0ull;
+    key[j] = sz[j] > 0 ? unit_key(scv[j], u) : 0ull;
+    if (sz[j] > 0) {
+      kor |= key[j];
+      kand &= key[j];
+    }
   }
 
-  __shared__ int tw[256];
-  __shared__ int tc[256];
   __shared__ unsigned long long hk[256];
+  __shared__ unsigned long long s_or[NW], s_and[NW];
   __shared__ long s_above;
   __shared__ int s_done, s_none;
   __shared__ unsigned long long s_prefix, s_kstar;
+  // The bits in which the candidates' keys differ: the passes start at the
+  // highest of them (the bits above are common to every key).
+  kor = wave_or64(kor);
+  kand = wave_and64(kand);
+  if (lane == 0) {
+    s_or[wave] = kor;
+    s_and[wave] = kand;
+  }
   if (tid == 0) {
     s_above = 0;
-    s_prefix = 0ull;
     s_done = 0;
     s_none = 0;
   }
-  for (int sh = 56; sh >= 0; sh -= 8) {
-    for (int i = tid; i < NW * 256; i += NT) {
-      (&hw[0][0])[i] = 0;
-      (&hc[0][0])[i] = 0;
+  __syncthreads();
+  kor = 0ull;
+  kand = ~0ull;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    kor |= s_or[v];
+    kand &= s_and[v];
+  }
+  const unsigned long long diff = kor ^ kand;
+  const int hibit = diff ? 63 - __clzll((long long)diff) : 0;
+  // pass: bits [sh, sh + width) of keys that agree with the prefix above them
+  int sh = max(hibit - 7, 0), width = 8;
+  unsigned long long prefix = (sh + width >= 64) ? 0ull : (kand >> (sh + width)) << (sh + width);
+  for (;;) {
+    // each wave counts into its own histogram row: cleared and filled in
+    // program order, so no barrier between
+    for (int i = lane; i < 256; i += 64) {
+      hw[wave][i] = 0;
+      hc[wave][i] = 0;
     }
-    __syncthreads();
-    const unsigned long long prefix = s_prefix;
+    const int top = sh + width;
+    const unsigned long long dmask = (1ull << width) - 1ull;
+    // runs of equal digits among this thread's consecutive units count once
+    int rd = -1, rw = 0, rc = 0;
+    unsigned long long rk = 0ull;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      if (sz[j] == 0) continue;
-      if (sh < 56 && (key[j] >> (sh + 8)) != (prefix >> (sh + 8))) continue;
-      const int dgt = (int)((key[j] >> sh) & 255ull);
-      atomicAdd(&hw[wave][dgt], sz[j]);
-      atomicAdd(&hc[wave][dgt], 1);
-      hk[dgt] = key[j];  // any member; read only when the bucket holds one unit
-    }
-    __syncthreads();
-    if (tid < 256) {
-      int w = 0, c = 0;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) {
-        w += hw[v][tid];
-        c += hc[v][tid];
+      const bool in = sz[j] > 0 && (top >= 64 || (key[j] >> top) == (prefix >> top));
+      if (!in) continue;
+      const int dgt = (int)((key[j] >> sh) & dmask);
+      if (dgt != rd) {
+        if (rc > 0) {
+          atomicAdd(&hw[wave][rd], rw);
+          atomicAdd(&hc[wave][rd], rc);
+          hk[rd] = rk;  // any member; read only when the bucket holds one unit
+        }
+        rd = dgt;
+        rw = 0;
+        rc = 0;
       }
-      tw[tid] = w;
-      tc[tid] = c;
+      rw += sz[j];
+      rc += 1;
+      rk = key[j];
+    }
+    const uint64_t act = __ballot(rc > 0);
+    if (act != 0) {
+      const int src = __ffsll((unsigned long long)act) - 1;
+      const int d0 = __shfl(rd, src);
+      if (__ballot(rc > 0 && rd != d0) == 0) {
+        // one digit for the whole wave (keys concentrated in a bucket): one
+        // update instead of 64 conflicting ones
+        const int w = wave_sum_int(rc > 0 ? rw : 0), c = wave_sum_int(rc);
+        if (lane == src) {
+          hw[wave][d0] += w;
+          hc[wave][d0] += c;
+          hk[d0] = rk;
+        }
+      } else if (rc > 0) {
+        atomicAdd(&hw[wave][rd], rw);
+        atomicAdd(&hc[wave][rd], rc);
+        hk[rd] = rk;
+      }
     }
     __syncthreads();
     if (wave == 0) {
+      // lane l: digits 255 - 4 l .. 252 - 4 l, summed over the waves' rows
+      long wd[4];
+      int cd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 255 - 4 * lane - i;
+        int w = 0, c = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          w += hw[v][d];
+          c += hc[v][d];
+        }
+        wd[i] = w;
+        cd[i] = c;
+      }
       long above_out = 0;
-      const int dgt = find_crossing_digit(tw, s_above, budget, &above_out);
+      int owner = 0;
+      const int dgt = find_crossing_digit(wd, s_above, budget, &above_out, &owner);
+      const int i_own = dgt >= 0 ? (255 - dgt) & 3 : 0;
+      const int cnt = __shfl(i_own == 0 ? cd[0] : i_own == 1 ? cd[1] : i_own == 2 ? cd[2] : cd[3],
+                             owner);
       if (lane == 0) {
         if (dgt < 0) {
-          s_none = 1;  // everything in range fits (only possible at the top level)
+          s_none = 1;  // everything in range fits (only possible in the first pass)
           s_done = 1;
         } else {
           s_above = above_out;
           s_prefix = prefix | ((unsigned long long)dgt << sh);
-          if (tc[dgt] == 1) {
+          if (cnt == 1) {
             s_kstar = hk[dgt];
             s_done = 1;
           } else if (sh == 0) {
@@ -606,6 +699,13 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
     }
     __syncthreads();
     if (s_done) break;
+    prefix = s_prefix;
+    if (sh >= 8) {
+      sh -= 8;
+    } else {
+      width = sh;
+      sh = 0;
+    }
   }
   const bool take_all = s_none != 0;
   const unsigned long long kstar = s_kstar;
@@ -643,6 +743,11 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   int32_t *out = sel_units + (size_t)bg * sel_cap;
   int32_t *spans = sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr;
   const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
+  int ustv[KPT];  // first rows, requested together (clamped index) rather than one wait per unit
+  if (spans) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) ustv[j] = ust[min(tid * KPT + j, pool.unit_cap - 1)];
+  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (sz[j] > 0 && (take_all || key[j] > kstar)) {
@@ -651,9 +756,9 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
         out[pos] = u;
         if (spans) {
           if constexpr (COH)
-            coherent_store_i2(spans + 2 * pos, int2{ust[u], sz[j]});
+            coherent_store_i2(spans + 2 * pos, int2{ustv[j], sz[j]});
           else
-            *reinterpret_cast<int2 *>(spans + 2 * pos) = int2{ust[u], sz[j]};
+            *reinterpret_cast<int2 *>(spans + 2 * pos) = int2{ustv[j], sz[j]};
         }
       }
       ++pos;
@@ -755,9 +860,9 @@ static kv_status select_dispatch(const kv_pool *pool, const void *q, int hq, int
     else                    \
       KVC_SEL(K, false);    \
   } while (0)
-  static_assert(kSelectMaxKeysPerThread == 8, "one instantiation per key count");
-  if (per <= 2) KVC_SEL2(2);
-  else if (per <= 8) KVC_SEL2(8);
+  static_assert(kSelectMaxKeysPerThread == 16, "one instantiation per key count");
+  if (per <= 4) KVC_SEL2(4);
+  else if (per <= 16) KVC_SEL2(16);
   else return KV_ERR_UNSUPPORTED;
 #undef KVC_SEL2
 #undef KVC_SEL
@@ -821,14 +926,16 @@ __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t 
   const int i0 = tid * per;
   int sz[PER_MAX], st[PER_MAX];
   int n;
+  // Loads are issued for every slot at a clamped index (sel_cap >= 1) and
+  // masked afterwards, so that all of them are in flight together: a load
+  // under a per-lane condition makes the compiler wait for it in its branch.
   if (spans != nullptr) {
     // row spans given: ids are not needed, one round trip
 #pragma unroll
     for (int j = 0; j < PER_MAX; ++j) {
-      int2 v = {0, 0};
-      if (j < per && i0 + j < sel_cap)
-        v = COH ? coherent_load_i2(spans + 2 * (i0 + j))
-                : *reinterpret_cast<const int2 *>(spans + 2 * (i0 + j));
+      const int i = min(i0 + j, sel_cap - 1);
+      const int2 v = COH ? coherent_load_i2(spans + 2 * i)
+                         : *reinterpret_cast<const int2 *>(spans + 2 * i);
       st[j] = v.x;
       sz[j] = v.y;
     }
@@ -842,17 +949,24 @@ __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t 
   } else {
     int uid[PER_MAX];
 #pragma unroll
-    for (int j = 0; j < PER_MAX; ++j) uid[j] = (j < per && i0 + j < sel_cap) ? su[i0 + j] : -1;
+    for (int j = 0; j < PER_MAX; ++j) uid[j] = su[min(i0 + j, sel_cap - 1)];
     n = min(max(sel_n[bg], 0), sel_cap);
     const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
     const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
+    int rs[PER_MAX], rz[PER_MAX];
+#pragma unroll
+    for (int j = 0; j < PER_MAX; ++j) {
+      // foreign ids count as empty units (their loads read unit 0)
+      const int u = (uid[j] >= 0 && uid[j] < pool.unit_cap) ? uid[j] : 0;
+      rz[j] = usz[u];
+      rs[j] = ust[u];
+    }
 #pragma unroll
     for (int j = 0; j < PER_MAX; ++j) {
       const int u = uid[j];
-      // foreign ids count as empty units
       const bool valid = j < per && i0 + j < n && u >= 0 && u < pool.unit_cap;
-      sz[j] = valid ? max(usz[u], 0) : 0;
-      st[j] = valid ? ust[u] : 0;
+      sz[j] = valid ? max(rz[j], 0) : 0;
+      st[j] = valid ? rs[j] : 0;
     }
   }
   int run = 0;

@@ -641,7 +641,9 @@ __global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
     for (int u = 0; u < UNR; ++u) {
       const int j = j0 + u * RPI + slot;
       ok[u] = j < cnt;
-      const int row = ok[u] ? p[j] : 0;
+      // clamped (cnt >= 1 here) rather than conditional: the member indices
+      // of the step are requested together instead of one wait each
+      const int row = p[min(j, cnt - 1)];
       v[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)row * D);
     }
 #pragma unroll

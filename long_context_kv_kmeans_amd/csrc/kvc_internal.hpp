@@ -12,7 +12,8 @@ namespace kvc {
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int kMaxSel = 4096; // selected units staged in LDS by the attend kernel
-constexpr int kSelectMaxKeysPerThread = 8;  // selection keys held per thread (x1024 threads)
+constexpr int kSelectBlockThreads = 512;     // threads of a selection workgroup
+constexpr int kSelectMaxKeysPerThread = 16;  // selection keys held per thread
 constexpr int kMaxClusters = 8192;  // one counting-sort chunk's label counts fit 64 KB of LDS
 
 // bf16 is carried as raw uint16_t bits.
