@@ -440,16 +440,6 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ unsigned long long wave_or64(unsigned long long v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v |= __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ unsigned long long wave_and64(unsigned long long v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v &= __shfl_xor(v, o);
-  return v;
-}
 
 __device__ __forceinline__ unsigned long long unit_key(float score, int u) {
   return ((unsigned long long)float_order_key(score) << 32) | (uint32_t)(0xffffffffu - (uint32_t)u);
@@ -583,8 +573,8 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   __shared__ unsigned long long s_prefix, s_kstar;
   // The bits in which the candidates' keys differ: the passes start at the
   // highest of them (the bits above are common to every key).
-  kor = wave_or64(kor);
-  kand = wave_and64(kand);
+  kor = wave_bits64<true>(kor);
+  kand = wave_bits64<false>(kand);
   if (lane == 0) {
     s_or[wave] = kor;
     s_and[wave] = kand;

@@ -451,16 +451,21 @@ __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t *lab = labels + (size_t)bh * n;
   const int base = ch * kRankChunk + wave * KPW;
+  // all label loads in flight at once (clamped index, masked below; n >= 1)
   int a[SUB];
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) a[sub] = lab[min(base + sub * 64 + lane, n - 1)];
+  bool bad = false;
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub) {
     const int i = base + sub * 64 + lane;
-    const int v = i < n ? lab[i] : -1;
+    const int v = i < n ? a[sub] : -1;
     a[sub] = (v >= 0 && v < c) ? v : -1;
-    if (status && i < n && a[sub] < 0)
-      __hip_atomic_store(status, (int)KV_ERR_INVALID_ARG, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    bad |= i < n && a[sub] < 0;
   }
+  if (status && bad)
+    __hip_atomic_store(status, (int)KV_ERR_INVALID_ARG, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   for (int k = threadIdx.x; k < NW * c; k += 64 * NW) cnt[k] = 0;
   __syncthreads();
   // rank within the wave's part: earlier keys of the part with the same label
@@ -529,22 +534,19 @@ __global__ void __launch_bounds__(kLabelBlock)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t run = 0;
   if (k < c) {
+    // 32 chunks per memory round trip (clamped loads, masked stores)
     int32_t *col = hist + (size_t)bh * nchunk * c + k;
-    int ch = 0;
-    for (; ch + 8 <= nchunk; ch += 8) {
-      int32_t h[8];
+    for (int ch = 0; ch < nchunk; ch += 32) {
+      int32_t h[32];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = col[(size_t)(ch + i) * c];
+      for (int i = 0; i < 32; ++i) h[i] = col[(size_t)min(ch + i, nchunk - 1) * c];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        col[(size_t)(ch + i) * c] = run;
-        run += h[i];
+      for (int i = 0; i < 32; ++i) {
+        if (ch + i < nchunk) {
+          col[(size_t)(ch + i) * c] = run;
+          run += h[i];
+        }
       }
-    }
-    for (; ch < nchunk; ++ch) {
-      const int32_t h = col[(size_t)ch * c];
-      col[(size_t)ch * c] = run;
-      run += h;
     }
   }
   // exclusive prefix of the totals within the block of 256 labels
@@ -578,7 +580,10 @@ __global__ void __launch_bounds__(256)
   __shared__ int s_base[64];  // start of each block of 256 labels
   const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
   const int nblk = (c + kLabelBlock - 1) / kLabelBlock;
-  const int a = i < n ? labels[(size_t)bh * n + i] : -1;
+  // the key's label and rank in one round trip (clamped index; n >= 1)
+  const int ic = min(i, n - 1);
+  const int lab_i = labels[(size_t)bh * n + ic], rank_i = rank[(size_t)bh * n + ic];
+  const int a = i < n ? lab_i : -1;
   if (threadIdx.x < 64) {  // wave 0: exclusive scan of the block totals
     const int lane = threadIdx.x;
     const int v = lane < nblk ? agg[(size_t)bh * nblk + lane] : 0;
@@ -594,7 +599,7 @@ __global__ void __launch_bounds__(256)
   if (i >= n || a < 0 || a >= c) return;  // labels out of range: left out by k_rank_hist too
   const int ch = i / kRankChunk;
   const int dest = s_base[a / kLabelBlock] + ipre[(size_t)bh * c + a] +
-                   hist[((size_t)bh * nchunk + ch) * c + a] + rank[(size_t)bh * n + i];
+                   hist[((size_t)bh * nchunk + ch) * c + a] + rank_i;
   perm[(size_t)bh * n + dest] = i;
 }
 

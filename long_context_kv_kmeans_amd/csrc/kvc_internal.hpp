@@ -125,6 +125,24 @@ template <int N> __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Bitwise OR / AND over the whole wave, in every lane (row exchanges, then the
+// 16- and 32-lane swaps; no LDS permute).
+template <bool OR> __device__ __forceinline__ uint32_t wave_bits32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return OR ? (a | b) : (a & b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowMirror, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowHalfMirror, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap2, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap1, 0xf, 0xf, false));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+template <bool OR> __device__ __forceinline__ unsigned long long wave_bits64(unsigned long long v) {
+  return (unsigned long long)wave_bits32<OR>((uint32_t)v) |
+         ((unsigned long long)wave_bits32<OR>((uint32_t)(v >> 32)) << 32);
+}
+
 // Maximum over the whole wave, in every lane (same pairing as group_sum).
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
