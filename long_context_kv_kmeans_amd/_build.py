@@ -35,9 +35,17 @@ def hipcc() -> str:
     return exe
 
 
+# Per-source flags. decode.hip: the first 16 dwords of each kernel's arguments
+# arrive preloaded in SGPRs when the wave starts (gfx950 kernel-argument
+# preloading), so the first memory requests of a decode step do not wait for a
+# scalar load of the argument segment; the attention kernel lists the pointers
+# those requests need first.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _compile(src: str, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -1513,20 +1513,30 @@ __device__ __forceinline__ void attend_chunk_fold(AttendChunk<D> &c, const bf16x
 // spilling, so they fold one chunk at a time.
 template <int G> constexpr bool kAttendPipelined = G == 2 || G == 4;
 
+// Bytes of k_gather_attend_mfma's explicit arguments.
+constexpr int kAttendArgBytes = 456;
+
 // STEP_KPT > 0 (working-set mode, no local buffer): the whole decode step, see
 // DecodeStep; the selection lists and flag of fx / sel_* are then outputs.
 template <int D, int G, bool BUF, int STEP_KPT = 0, bool STEP_W47 = true>
 __global__ void __launch_bounds__(kAttendThreads)
-    k_gather_attend_mfma(kv_pool pool, const uint16_t *__restrict__ q, int hq, float scale_log2,
+    k_gather_attend_mfma(const uint16_t *__restrict__ ws_k, const uint16_t *__restrict__ ws_v,
+                         const uint16_t *__restrict__ q, const uint16_t *__restrict__ q_prev,
+                         int geo, int rcap, int ws_cap, int hq,
+                         const int32_t *__restrict__ ws_spans, const int32_t *__restrict__ ws_count,
+                         kv_pool pool, float scale_log2,
                          const int32_t *__restrict__ sel_units,
                          const int32_t *__restrict__ sel_spans, int sel_cap,
-                         const int32_t *__restrict__ sel_n, int rcap, float *__restrict__ out,
+                         const int32_t *__restrict__ sel_n, float *__restrict__ out,
                          float *__restrict__ partials, int32_t *counters, AttendFetch fx,
                          DecodeStep st = DecodeStep{}) {
   static_assert(G <= 16, "query columns of one MFMA tile");
   constexpr bool DSTEP = STEP_KPT > 0;
-  // kv_decode_step: its arguments (408 bytes) in one round trip, before anything
-  if constexpr (DSTEP) kernarg_warm<408>();
+  // kv_decode_step: the rest of its arguments in one round trip, requested
+  // now and waited for once the rows and the boundary test's loads are out
+  KernargLines<kAttendArgBytes> kargs;
+  if constexpr (DSTEP) kargs.issue();
+
   static_assert(!(DSTEP && BUF), "a decode step in one launch has no local buffer");
   constexpr int NT = kAttendThreads, NW = kAttendWaves;
   constexpr int KS = D / 32;
@@ -1540,10 +1550,10 @@ __global__ void __launch_bounds__(kAttendThreads)
   __shared__ __align__(16) float s_acc[NW][G][D];
   __shared__ int s_last;
 
-  const int H = pool.n_kv_heads;
+  const int H = geo & 0xffff;  // pool.n_kv_heads
   const int bg = blockIdx.y, b = bg / H, g = bg % H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nsplit = gridDim.x, split = blockIdx.x;
+  const int nsplit = geo >> 16, split = blockIdx.x;  // nsplit == gridDim.x
   const int col = lane & 15, quad = lane >> 4;  // MFMA: column (query head) and k group
   const int vpart = lane % LPR;                   // V elements 8 vpart .. 8 vpart + 7
 
@@ -1558,7 +1568,7 @@ __global__ void __launch_bounds__(kAttendThreads)
   constexpr int BW0 = NW - 4;
   BoundaryFirst<uint16_t, D> bfirst;
   if constexpr (DSTEP && STEP_W47)
-    if (st.q_prev != nullptr) boundary_prefetch<uint16_t, D, BW0>(st.q_prev, q, hq, b, bfirst);
+    if (q_prev != nullptr) boundary_prefetch<uint16_t, D, BW0>(q_prev, q, hq, b, bfirst);
   bf16x8a_t qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -1582,11 +1592,11 @@ __global__ void __launch_bounds__(kAttendThreads)
   // as the flag and the span. A retrieval step (or any other span) discards
   // them and takes the general path.
   // The flag and the working set's one span (read as attend_load_selection
-  // reads a one-entry list) are requested with the rows; every value feeds
-  // the test below, so none of the loads is deferred into a branch and all of
-  // them are in flight at once. kv_fetch_attend requests them right behind
-  // the rows (it waits for all of them at once anyway); kv_decode_step right
-  // before them, so that its boundary test runs while the rows are in flight.
+  // reads a one-entry list) are requested right behind the rows (and, in
+  // kv_decode_step, the boundary test's loads); every value feeds the test
+  // below, so none of the loads is deferred into a branch and all of them are
+  // in flight at once. The rows and the test use only the leading, preloaded
+  // kernel arguments, so they go out as the waves start.
   int ws_flag = 0, ws_cnt = 0;
   int2 ws_sp = {0, 0};
   int gen0 = 0;
@@ -1597,30 +1607,28 @@ __global__ void __launch_bounds__(kAttendThreads)
         // kv_decode_step: vector loads (see opaque_zero), so that the waits for
         // kernel arguments before the test and the rows do not wait for these
         const int z = DSTEP ? opaque_zero() : 0;
-        ws_cnt = fx.count[bg + z];
-        ws_sp = *reinterpret_cast<const int2 *>(fx.spans + 2 * (bg + z));
+        ws_cnt = ws_count[bg + z];
+        ws_sp = *reinterpret_cast<const int2 *>(ws_spans + 2 * (bg + z));
       }
     }
     if constexpr (DSTEP)
       if (tid == 0) gen0 = __hip_atomic_load(&st.gen[bg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  if constexpr (DSTEP) ws_loads();
   AttendChunk<D> ca;
   const int spec_chunk = (max(rcap, 1) + nsplit - 1) / nsplit;
   const int spec_lo = split * spec_chunk;
   auto spec_rows = [&]() {
     if (!BUF && ws_mode && wave * kAttendChunk < spec_chunk)  // waves with rows in the chunk
       attend_chunk_load_direct<D>(
-          ca, spec_lo + wave * kAttendChunk, fx.cap - 1,
-          static_cast<const uint16_t *>(fx.k) + (size_t)bg * fx.cap * D,
-          static_cast<const uint16_t *>(fx.v) + (size_t)bg * fx.cap * D, lane);
+          ca, spec_lo + wave * kAttendChunk, ws_cap - 1, ws_k + (size_t)bg * ws_cap * D,
+          ws_v + (size_t)bg * ws_cap * D, lane);
   };
   __shared__ float s_part[4];
   if constexpr (DSTEP && !STEP_W47) {
     if (wave >= BW0) {
-      if (st.q_prev != nullptr) {
-        boundary_prefetch<uint16_t, D, BW0>(st.q_prev, q, hq, b, bfirst);
-        boundary_partial<uint16_t, D, BW0>(st.q_prev, q, hq, b, s_part, bfirst);
+      if (q_prev != nullptr) {
+        boundary_prefetch<uint16_t, D, BW0>(q_prev, q, hq, b, bfirst);
+        boundary_partial<uint16_t, D, BW0>(q_prev, q, hq, b, s_part, bfirst);
       }
     } else {
       spec_rows();
@@ -1628,17 +1636,20 @@ __global__ void __launch_bounds__(kAttendThreads)
   } else {
     spec_rows();
   }
-  if constexpr (!DSTEP) ws_loads();
+  // the span and count need kernel arguments that are not preloaded: requested
+  // after the rows and the boundary test's loads, which need only preloaded ones
+  if constexpr (DSTEP) kargs.consume();
+  ws_loads();
   if constexpr (DSTEP) {
     // the step's retrieval decision, taken here by every workgroup of the
     // sequence with the same function as k_boundary (so the same bits)
     float rv = __builtin_nanf("");
     ws_flag = 1;
-    if (st.q_prev != nullptr) {
+    if (q_prev != nullptr) {
       if constexpr (!STEP_W47)
         rv = boundary_combine(s_part, hq);
       else
-        rv = boundary_r_pre<uint16_t, D, BW0>(st.q_prev, q, hq, b, s_part, bfirst);
+        rv = boundary_r_pre<uint16_t, D, BW0>(q_prev, q, hq, b, s_part, bfirst);
       ws_flag = rv < st.tau ? 1 : 0;
     }
     if (split == 0 && g == 0 && tid == 0) {
@@ -2015,6 +2026,11 @@ int attend_num_splits(const kv_pool *pool, int max_rows) {
   return (int)ns;
 }
 
+// Kernel argument `geo` of k_gather_attend_mfma: n_kv_heads | nsplit << 16.
+static int attend_geo(const kv_pool *pool, int nsplit) {
+  return (pool->n_kv_heads & 0xffff) | (nsplit << 16);
+}
+
 template <typename T, int D>
 static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, float scale_log2,
                                  const int32_t *sel_units, const int32_t *sel_spans,
@@ -2023,18 +2039,21 @@ static kv_status attend_dispatch(const kv_pool *pool, const void *q, int hq, flo
                                  const AttendFetch &fx, hipStream_t s) {
   const int G = hq / pool->n_kv_heads;
   const dim3 grid(nsplit, pool->batch * pool->n_kv_heads);
+  const int geo = attend_geo(pool, nsplit);
   if (sizeof(T) != 2 && fx.flag != nullptr) return KV_ERR_UNSUPPORTED;
 #define KVC_ATT(GG)                                                                           \
   do {                                                                                        \
     if constexpr (sizeof(T) == 2)                                                             \
       if (pool->buf_k != nullptr)                                                             \
         k_gather_attend_mfma<D, GG, true><<<grid, kAttendThreads, 0, s>>>(                    \
-            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, \
-            rcap, out, partials, counters, fx);                                               \
+            (const uint16_t *)fx.k, (const uint16_t *)fx.v, (const uint16_t *)q, nullptr, geo,  \
+            rcap, fx.cap, hq, fx.spans, fx.count, *pool, scale_log2, sel_units, sel_spans,      \
+            sel_cap, sel_n, out, partials, counters, fx);                                     \
       else                                                                                    \
         k_gather_attend_mfma<D, GG, false><<<grid, kAttendThreads, 0, s>>>(                   \
-            *pool, (const uint16_t *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, \
-            rcap, out, partials, counters, fx);                                               \
+            (const uint16_t *)fx.k, (const uint16_t *)fx.v, (const uint16_t *)q, nullptr, geo,  \
+            rcap, fx.cap, hq, fx.spans, fx.count, *pool, scale_log2, sel_units, sel_spans,      \
+            sel_cap, sel_n, out, partials, counters, fx);                                     \
     else                                                                                      \
       k_gather_attend_valu<T, D, GG><<<grid, kAttendValuThreads, 0, s>>>(                     \
           *pool, (const T *)q, hq, scale_log2, sel_units, sel_spans, sel_cap, sel_n, rcap,    \
@@ -2225,10 +2244,12 @@ static kv_status decode_step_dispatch(const kv_pool *pool, const void *q, int hq
   // do waves 4-7 get rows of the first pass (a chunk of more than 4 x 32 rows)?
   const bool w47 = (std::max(rcap, 1) + nsplit - 1) / nsplit > (kAttendWaves - 4) * kAttendChunk;
   const bool small = pool->unit_cap <= kAttendThreads * 4;  // 4 selection keys per thread
+  const int geo = attend_geo(pool, nsplit);
 #define KVC_STEP(GG, KPT, W47)                                                                \
   k_gather_attend_mfma<D, GG, false, KPT, W47><<<grid, kAttendThreads, 0, s>>>(              \
-      *pool, (const uint16_t *)q, hq, scale_log2, nullptr, nullptr, 1, nullptr, rcap, out,    \
-      partials, counters, fx, st)
+      (const uint16_t *)fx.k, (const uint16_t *)fx.v, (const uint16_t *)q,                     \
+      (const uint16_t *)st.q_prev, geo, rcap, fx.cap, hq, fx.spans, fx.count, *pool, scale_log2, \
+      nullptr, nullptr, 1, nullptr, out, partials, counters, fx, st)
 #define KVC_STEP2(GG)                                  \
   do {                                                 \
     if (small) {                                       \

@@ -165,25 +165,29 @@ template <int L> __device__ __forceinline__ float sum_stride(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
-// Requests every 64-byte line of the first BYTES of the kernel's argument
-// segment at once and waits for them. Left to itself the compiler loads an
-// argument where it is first needed, so each new line is a scalar-cache miss
-// and a wait of its own, one after another, before the first memory request
-// that depends on them. BYTES must lie inside the segment (the explicit
-// arguments, followed by at least 256 bytes of hidden ones).
-template <int BYTES> __device__ __forceinline__ void kernarg_warm() {
-  typedef const uint32_t __attribute__((address_space(4))) karg_u32;
-  karg_u32 *ka = (karg_u32 *)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int N = (BYTES + 63) / 64;
+// Every 64-byte line of the first BYTES of the kernel's argument segment,
+// requested at once by issue() and waited for by consume(). Left to itself
+// the compiler loads an argument where it is first needed, so each new line
+// is a scalar-cache miss and a wait of its own, one after another. Only the
+// first dword of each line below BYTES is read, so BYTES up to the size of
+// the explicit arguments keeps every load inside the segment.
+template <int BYTES> struct KernargLines {
+  static constexpr int N = (BYTES + 63) / 64;
   uint32_t w[N];
+  __device__ __forceinline__ void issue() {
+    typedef const uint32_t __attribute__((address_space(4))) karg_u32;
+    karg_u32 *ka = (karg_u32 *)__builtin_amdgcn_kernarg_segment_ptr();
 #pragma unroll
-  for (int i = 0; i < N; ++i) w[i] = ka[16 * i];
-  __builtin_amdgcn_sched_barrier(0);  // every request before the one wait
-  uint32_t x = 0;
+    for (int i = 0; i < N; ++i) w[i] = ka[16 * i];
+    __builtin_amdgcn_sched_barrier(0);  // every request goes out here
+  }
+  __device__ __forceinline__ void consume() const {
+    uint32_t x = 0;
 #pragma unroll
-  for (int i = 0; i < N; ++i) x ^= w[i];
-  asm volatile("" ::"s"(x));
-}
+    for (int i = 0; i < N; ++i) x ^= w[i];
+    asm volatile("" ::"s"(x));
+  }
+};
 
 // Map a hardware workgroup id to a logical one so that each XCD (which
 // receives ids x, x+8, x+16, ...) processes one contiguous range of logical
