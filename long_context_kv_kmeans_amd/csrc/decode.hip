@@ -888,10 +888,12 @@ kv_status launch_select(const kv_pool *pool, const void *q, int hq, int budget,
 // last workgroup merges the shares in order.
 //
 // bf16 keys: q.k for 16 rows x 16 query columns (G used) is one
-// v_mfma_f32_16x16x32_bf16 chain over the head dimension; the probabilities
-// reach the lanes holding the V rows by row broadcasts, and those lanes
-// accumulate p.v on the VALU. fp32 keys take an all-VALU variant.
-constexpr int kAttendMinRowsPerSplit = 128;
+// v_mfma_f32_16x16x32_bf16 chain over the head dimension; p.v runs on the
+// same tiles for head dimension 128 (the V rows transposed in registers,
+// see AttendAcc) and on the VALU for 64, where the probabilities reach the
+// lanes holding the V rows by row broadcasts. fp32 keys take an all-VALU
+// variant.
+constexpr int kAttendMinRowsPerSplit = 64;
 constexpr int kAttendTargetBlocks = 256;  // one 8-wave workgroup per CU
 
 __device__ __forceinline__ float safe_scale(float m_old, float m_new) {
@@ -2022,7 +2024,9 @@ int attend_num_splits(const kv_pool *pool, int max_rows) {
   long by_grid = (kAttendTargetBlocks + bh - 1) / bh;
   long ns = by_rows < by_grid ? by_rows : by_grid;
   if (ns < 1) ns = 1;
-  if (ns > kMaxSplits) ns = kMaxSplits;
+  // at most one batch of shares for the merging workgroup (a second batch is
+  // one more dependent round trip, which costs more than the split saves)
+  if (ns > kMergeBatch) ns = kMergeBatch;
   return (int)ns;
 }
 
