@@ -35,12 +35,12 @@ def hipcc() -> str:
     return exe
 
 
-# Per-source flags. decode.hip: the first 16 dwords of each kernel's arguments
-# arrive preloaded in SGPRs when the wave starts (gfx950 kernel-argument
-# preloading), so the first memory requests of a decode step do not wait for a
-# scalar load of the argument segment; the attention kernel lists the pointers
-# those requests need first.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+# Per-source flags: the leading dwords of each kernel's arguments arrive
+# preloaded in SGPRs when the wave starts (gfx950 kernel-argument preloading),
+# so a kernel's first memory requests do not wait for a scalar load of the
+# argument segment; the kernels list the arguments those requests need first.
+PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+EXTRA = {"decode.hip": PRELOAD, "kmeans.hip": PRELOAD}
 
 
 def _compile(src: str, obj_dir: str) -> str:

@@ -613,14 +613,14 @@ __global__ void __launch_bounds__(256)
 // start: the in-block label prefixes of k_colscan on entry; each wave adds
 // its block's base and writes the cluster's start back (the pack reads it).
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_segsum(const T *__restrict__ keys,
-                                                const int32_t *__restrict__ perm,
+__global__ void __launch_bounds__(256) k_segsum(int n, int c, int ntile,
+                                                const int32_t *__restrict__ tot,
                                                 int32_t *__restrict__ start,
                                                 const int32_t *__restrict__ agg,
-                                                const int32_t *__restrict__ tot,
+                                                const int32_t *__restrict__ perm,
+                                                const T *__restrict__ keys,
                                                 const float *cent_in, float *cent_out,
-                                                uint16_t *__restrict__ frags, int n, int c,
-                                                int ntile) {
+                                                uint16_t *__restrict__ frags) {
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane
   constexpr int LPR = D / EPL;               // lanes per row
   constexpr int RPI = 64 / LPR;              // member rows per wave instruction
@@ -750,18 +750,18 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   const int ntile = (c + 31) / 32;
   if (dt == KV_BF16) {
     if (d == 128)
-      k_segsum<uint16_t, 128><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, agg, tot, cent_in,
-                                                cent_out, fr, n, c, ntile);
+      k_segsum<uint16_t, 128><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const uint16_t *)keys,
+                                                cent_in, cent_out, fr);
     else
-      k_segsum<uint16_t, 64><<<g, 256, 0, s>>>((const uint16_t *)keys, perm, start, agg, tot, cent_in,
-                                               cent_out, fr, n, c, ntile);
+      k_segsum<uint16_t, 64><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const uint16_t *)keys,
+                                               cent_in, cent_out, fr);
   } else {
     if (d == 128)
-      k_segsum<float, 128><<<g, 256, 0, s>>>((const float *)keys, perm, start, agg, tot, cent_in,
-                                             cent_out, nullptr, n, c, ntile);
+      k_segsum<float, 128><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const float *)keys,
+                                             cent_in, cent_out, nullptr);
     else
-      k_segsum<float, 64><<<g, 256, 0, s>>>((const float *)keys, perm, start, agg, tot, cent_in,
-                                            cent_out, nullptr, n, c, ntile);
+      k_segsum<float, 64><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const float *)keys,
+                                            cent_in, cent_out, nullptr);
   }
   if (perm_out) *perm_out = perm;
   if (start_out) *start_out = start;
