@@ -516,17 +516,26 @@ def main():
     def launch_ms(fn, reps):
         """Mean GPU time per launch of fn: `reps` back-to-back launches on
         `stream` between two HIP events, all queued behind a GPU sleep so that
-        the host's enqueue rate does not stretch the interval."""
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            fn()
-            torch.cuda._sleep(20_000_000)
-            a.record(stream)
-            for _ in range(reps):
+        the host's enqueue rate does not stretch the interval. If the first
+        event has already completed when the last launch is queued, the GPU
+        may have waited for the host: the sleep is lengthened and the
+        measurement taken again."""
+        cycles = 20_000_000
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
                 fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+                torch.cuda._sleep(cycles)
+                a.record(stream)
+                for _ in range(reps):
+                    fn()
+                starved = a.query()
+                b.record(stream)
+            torch.cuda.synchronize()
+            if not starved:
+                return a.elapsed_time(b) / reps
+            cycles *= 4
+        raise SystemExit("launch timing: the host could not queue the launches ahead of the GPU")
 
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
