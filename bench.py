@@ -1,37 +1,41 @@
 #!/usr/bin/env python3
 """Benchmark of the centroid-indexed KV retrieval hot path on one MI355X.
 
-One step = one pass of the whole path over one Qwen3-8B-shaped layer
-(8 KV heads, 32 query heads, head dim 128, bf16, batch 1, 32768 prefill keys
-per head, C = 2048, 10 Lloyd rounds):
-  prefill : kv_cluster_build (K-means assign/update x10, CSR pack of K/V);
-  decode  : 256 steps of kv_boundary_select (boundary test + selection in one
-            launch, writing the selected units' row spans) -> kv_fetch_attend
-            over an HBM working set (on a retrieval step the attention launch
-            first copies the selected rows there; on the other steps it reads
-            the working set's contiguous rows, whose addresses are known at
-            launch) on the seeded query walk, replayed from one captured HIP
-            graph. ``--attend pool`` attends the pool's rows directly
-            (kv_gather_attend reading the selection's row spans).
-Inputs are synthetic (seeded Gaussian-mixture keys, random values and query
-walks) and resident in HBM before timing starts.
+One step = one pass of the whole path over one batch of synthetic input. The
+default workload (``--config 3``, long-in-long-out-128k-x36) is 36 layers of a
+Qwen3-8B-shaped model (8 KV heads, 32 query heads, head dim 128, bf16, batch 1)
+with 131072 prefill keys per KV head, C = 8192 clusters, 10 Lloyd rounds,
+budget 2048 rows and 1024 decode steps:
+  prefill : per layer, kv_cluster_build (K-means assign/update x10, then the
+            pack of K/V into cluster-contiguous rows);
+  decode  : 1024 steps x 36 layers of kv_decode_step, one launch per
+            layer-step: the boundary test on the query pair; on a retrieval
+            step, scoring of the centroids, the budgeted top-k selection and
+            the copy of the selected rows into an HBM working set; then
+            attention over the working set. The loop is replayed from captured
+            HIP graphs on the seeded query walks.
+Every layer draws its own prefill keys/values and query walk and clusters
+into a pool of its own, so each layer-step reads its KV from HBM as in a real
+model. Inputs are synthetic (seeded Gaussian-mixture keys, random values and
+query walks) and resident in HBM before timing starts.
 
 ``--config`` selects another workload of the same family: 0 (tiny, fp32),
+1 (one layer of 32768 keys, C = 2048, budget 512, 256 decode steps),
 2 (long output: 2048 prefill keys, 16384 decode steps with temporal segments
 and a 1024-token local buffer; the decode step is kv_boundary_segment_append
-(boundary test + append in one launch) -> kv_select -> kv_gather_attend), 3 (36 layers of 131072
-keys, C = 8192, 1024 decode steps per layer; every layer clusters into a pool
-of its own and has its own query walk, so each layer-step reads its KV from
-HBM as in a real model; the layers share one layer's synthetic prefill
-keys/values), 4 (16 sequences of 32768 keys). Long decode loops are captured
-as several graphs.
+(boundary test + append in one launch) -> kv_select -> kv_gather_attend),
+4 (16 sequences of 32768 keys, C = 2048, budget 1024, 512 decode steps).
+``--launches two`` splits the layer-step into kv_boundary_select and
+kv_fetch_attend; ``--attend pool`` attends the pool's rows directly
+(kv_gather_attend reading the selection's row spans).
 
 Printed JSON (one line): value = prefill keys clustered per second of whole
 steps (the decode loop included); the split into prefill time and decode
 microseconds per layer-step, the decode bytes moved per layer-step and the
 fraction of HBM peak are extra fields. ``roofline`` covers the dominant
-kernel by total time per step, the decode gather-attend (HBM bound);
-``roofline_assign`` covers the MFMA K-means assignment. Both kernels are
+kernel by total time per step: the MFMA K-means assignment at the default
+workload, the decode step's attention kernel (HBM bound) where that
+dominates; ``roofline_assign`` and ``roofline_attend`` carry both. Both kernels are
 timed with HIP events on the stream they run on around back-to-back
 launches queued behind a GPU sleep, so that host enqueue gaps do not enter
 the interval. ``cpu_baseline`` times the CPU oracle on a bounded sample of the
