@@ -21,7 +21,6 @@ constexpr int kAssignColBlocks = 2;                      // 32-key MFMA column b
 constexpr int kAssignMinWaves = 4;                       // waves per SIMD the register budget targets
 constexpr int kTilesPerStage = 2;                        // 64 centroids per LDS stage
 constexpr int kAssignWaves = 8;                          // waves per workgroup
-constexpr int kRankChunk = 1024;                         // keys per counting-sort chunk
 
 // ---------------------------------------------------------------- init
 // An index outside [0, n) is clamped into it (so no read leaves the head's
@@ -423,7 +422,7 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
 
 // ---------------------------------------------------------------- update
 // Stable counting sort of keys by label, in three passes:
-//  k_rank_hist -- one workgroup per chunk of 1024 keys, its NW waves taking
+//  k_rank_hist -- one workgroup per chunk of CHUNK keys, its NW waves taking
 //                 consecutive parts: the rank of each key among earlier keys
 //                 of the chunk with the same label (within a part, label
 //                 equality found with one ballot per label bit; then the
@@ -439,18 +438,18 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
 //  k_scatter   -- perm[start[a] + chunk_prefix[a] + rank] = key.
 // A label outside [0, c) takes no part: its key gets no rank, no histogram
 // count and no place in the permutation (reported through *status when given).
-template <int NW>
+template <int NW, int CHUNK>
 __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict__ labels,
                                                        int32_t *__restrict__ rank,
                                                        int32_t *__restrict__ hist, int n, int c,
                                                        int nbits, int nchunk, int32_t *status) {
-  constexpr int KPW = kRankChunk / NW;  // keys per wave: wave w takes the w-th part of the chunk
+  constexpr int KPW = CHUNK / NW;  // keys per wave: wave w takes the w-th part of the chunk
   constexpr int SUB = KPW / 64;
   extern __shared__ int32_t cnt[];      // [NW][c]: label counts of each wave's part
   const int bh = blockIdx.y, ch = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t *lab = labels + (size_t)bh * n;
-  const int base = ch * kRankChunk + wave * KPW;
+  const int base = ch * CHUNK + wave * KPW;
   // all label loads in flight at once (clamped index, masked below; n >= 1)
   int a[SUB];
 #pragma unroll
@@ -576,7 +575,7 @@ __global__ void __launch_bounds__(256)
     k_scatter(const int32_t *__restrict__ labels, const int32_t *__restrict__ rank,
               const int32_t *__restrict__ hist, const int32_t *__restrict__ ipre,
               const int32_t *__restrict__ agg, int32_t *__restrict__ perm, int n, int c,
-              int nchunk) {
+              int nchunk, int chunk_shift) {
   __shared__ int s_base[64];  // start of each block of 256 labels
   const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
   const int nblk = (c + kLabelBlock - 1) / kLabelBlock;
@@ -597,7 +596,7 @@ __global__ void __launch_bounds__(256)
   }
   __syncthreads();
   if (i >= n || a < 0 || a >= c) return;  // labels out of range: left out by k_rank_hist too
-  const int ch = i / kRankChunk;
+  const int ch = i >> chunk_shift;
   const int dest = s_base[a / kLabelBlock] + ipre[(size_t)bh * c + a] +
                    hist[((size_t)bh * nchunk + ch) * c + a] + rank_i;
   perm[(size_t)bh * n + dest] = i;
@@ -701,8 +700,17 @@ static int ceil_log2(int c) {
   return b;
 }
 
+// Keys per counting-sort chunk. A chunk's waves rank their parts one 64-key
+// step after another, so longer chunks rank more slowly per key; they pay
+// only where the chunk histograms (chunks x labels counts per head) dominate
+// the traffic and there are enough keys for >= 1024 workgroups of 4096:
+// 4096 keys for 1024 < c <= 4096 (4 waves), else 1024.
+static int rank_chunk(int bh, int n, int c) {
+  return (c > 1024 && c <= 4096 && (long)bh * n >= 4096L * 1024) ? 4096 : 1024;
+}
+
 size_t update_ws_bytes(int bh, int n, int c) {
-  const size_t nchunk = (size_t)(n + kRankChunk - 1) / kRankChunk;
+  const size_t nchunk = (size_t)(n + 1023) / 1024;  // the smallest chunk: an upper bound
   size_t b = 0;
   b += align_up((size_t)bh * n * 4, 256);           // rank
   b += align_up((size_t)bh * nchunk * c * 4, 256);  // hist
@@ -718,12 +726,12 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
                         kv_dtype dt, void *ws, hipStream_t s, const int32_t **perm_out,
                         const int32_t **start_out, const int32_t **tot_out, void *frags_out,
                         int32_t *status) {
-  const int nchunk = (n + kRankChunk - 1) / kRankChunk;
+  const int chunk = rank_chunk(bh, n, c), nchunk = (n + chunk - 1) / chunk;
   char *w = static_cast<char *>(ws);
   int32_t *rank = reinterpret_cast<int32_t *>(w);
   w += align_up((size_t)bh * n * 4, 256);
   int32_t *hist = reinterpret_cast<int32_t *>(w);
-  w += align_up((size_t)bh * nchunk * c * 4, 256);
+  w += align_up((size_t)bh * ((n + 1023) / 1024) * c * 4, 256);
   int32_t *tot = reinterpret_cast<int32_t *>(w);
   w += align_up((size_t)bh * c * 4, 256);
   int32_t *start = reinterpret_cast<int32_t *>(w);
@@ -736,15 +744,19 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   // a chunk's label counts ([waves][c] int32) stay within 64 KB of LDS: 4 waves
   // per chunk up to 4096 labels, 2 up to kMaxClusters = 8192
   if (c > kMaxClusters) return KV_ERR_UNSUPPORTED;
-  if (c <= 4096)
-    k_rank_hist<4><<<dim3(nchunk, bh), 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                                    ceil_log2(c), nchunk, status);
+  const dim3 rg(nchunk, bh);
+  if (chunk == 1024 && c <= 4096)
+    k_rank_hist<4, 1024><<<rg, 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
+                                                            ceil_log2(c), nchunk, status);
+  else if (c <= 4096)
+    k_rank_hist<4, 4096><<<rg, 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
+                                                            ceil_log2(c), nchunk, status);
   else
-    k_rank_hist<2><<<dim3(nchunk, bh), 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                                    ceil_log2(c), nchunk, status);
+    k_rank_hist<2, 1024><<<rg, 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
+                                                            ceil_log2(c), nchunk, status);
   k_colscan<<<dim3(nblk, bh), kLabelBlock, 0, s>>>(hist, tot, start, agg, counts, c, nchunk);
   k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, agg, perm, n, c,
-                                                      nchunk);
+                                                      nchunk, ceil_log2(chunk));
   const dim3 g((c + 3) / 4, bh);
   uint16_t *fr = static_cast<uint16_t *>(frags_out);
   const int ntile = (c + 31) / 32;

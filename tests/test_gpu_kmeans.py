@@ -158,7 +158,15 @@ def _cluster_build(cfg, heads, iters, seqs=(0,)):
     return inp, pool, lab.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg_idx,over,heads", CASES[:3])
+# several chunks of the counting sort with a ragged last one, for
+# 1024 < C <= 4096 and for C > 4096 (two ranking waves per chunk)
+BIG_C = [
+    (1, dict(n_keys=9000, n_clusters=1500, n_components=64), [0]),
+    (1, dict(n_keys=17001, n_clusters=5000, n_components=128), [1]),
+]
+
+
+@pytest.mark.parametrize("cfg_idx,over,heads", CASES[:3] + BIG_C)
 def test_cluster_build_invariants_and_pack(cfg_idx, over, heads):
     cfg = wl.get_config(cfg_idx, **over)
     inp, pool, lab = _cluster_build(cfg, heads, cfg.iters)
@@ -330,6 +338,31 @@ def test_full_size_sampled(cfg_idx, heads, sample):
                 assert np.linalg.norm(gc[h][k] - ref) <= 1e-5 * max(np.linalg.norm(ref), 1e-30)
             assert cnt[h].sum() == N
         c = gc
+
+
+def test_update_many_heads_long_chunks():
+    """128 heads x 32773 keys, C = 2048: enough keys (>= 4096 x 1024) for the
+    counting sort's 4096-key chunks, with a ragged last chunk. Counts are exact
+    for every head; centroids of sampled heads match the oracle's update."""
+    BH, N, d, C = 128, 32773, 128, 2048
+    g = torch.Generator(device="cuda").manual_seed(11)
+    keys_d = torch.randn(BH, N, d, generator=g, device="cuda").to(torch.bfloat16)
+    lab_d = torch.randint(0, C, (BH, N), generator=g, device="cuda", dtype=torch.int32)
+    idx = torch.randint(0, N, (BH, C), generator=g, device="cuda")
+    cin = torch.gather(keys_d.float(), 1, idx[..., None].expand(BH, C, d)).contiguous()
+    cout = torch.empty_like(cin)
+    counts = torch.zeros(BH, C, dtype=torch.int32, device="cuda")
+    kvc.kv_kmeans_update(keys_d, lab_d, cin, cout, counts)
+    torch.cuda.synchronize()
+    lab = lab_d.cpu().numpy()
+    cnt = counts.cpu().numpy()
+    for h in range(BH):
+        np.testing.assert_array_equal(cnt[h], np.bincount(lab[h], minlength=C))
+    for h in (0, 77, 127):
+        kh = keys_d[h].float().cpu().numpy()
+        ref, rc = okm.update(kh, lab[h], cin[h].cpu().numpy().astype(np.float64))
+        np.testing.assert_array_equal(cnt[h], rc)
+        assert _rel_err(cout[h].cpu().numpy().astype(np.float64), ref) <= 1e-5
 
 
 def test_out_of_range_labels_and_init_indices_are_ignored_and_reported():
