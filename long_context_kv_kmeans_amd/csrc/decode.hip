@@ -407,12 +407,7 @@ __device__ int find_crossing_digit(const long (&wd)[4], long above, long budget,
   long local = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) local += wd[i];
-  long incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const long y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const long incl = wave_incl_scan_i64(local);
   const long excl = incl - local;
   int found = -1;
   long found_above = 0;
@@ -430,15 +425,9 @@ __device__ int find_crossing_digit(const long (&wd)[4], long above, long budget,
   const uint64_t who = __ballot(found >= 0);
   if (who == 0) return -1;
   const int src = __ffsll((unsigned long long)who) - 1;
-  *above_out = __shfl(found_above, src);
+  *above_out = lane_value_i64(found_above, src);
   *lane_out = src;
-  return __shfl(found, src);
-}
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+  return lane_value(found, src);
 }
 
 __device__ __forceinline__ unsigned long long unit_key(float score, int u) {
@@ -631,11 +620,11 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
     const uint64_t act = __ballot(rc > 0);
     if (act != 0) {
       const int src = __ffsll((unsigned long long)act) - 1;
-      const int d0 = __shfl(rd, src);
+      const int d0 = lane_value(rd, src);
       if (__ballot(rc > 0 && rd != d0) == 0) {
         // one digit for the whole wave (keys concentrated in a bucket): one
         // update instead of 64 conflicting ones
-        const int w = wave_sum_int(rc > 0 ? rw : 0), c = wave_sum_int(rc);
+        const int w = wave_sum_i32(rc > 0 ? rw : 0), c = wave_sum_i32(rc);
         if (lane == src) {
           hw[wave][d0] += w;
           hc[wave][d0] += c;
@@ -668,8 +657,8 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
       int owner = 0;
       const int dgt = find_crossing_digit(wd, s_above, budget, &above_out, &owner);
       const int i_own = dgt >= 0 ? (255 - dgt) & 3 : 0;
-      const int cnt = __shfl(i_own == 0 ? cd[0] : i_own == 1 ? cd[1] : i_own == 2 ? cd[2] : cd[3],
-                             owner);
+      const int cnt =
+          lane_value(i_own == 0 ? cd[0] : i_own == 1 ? cd[1] : i_own == 2 ? cd[2] : cd[3], owner);
       if (lane == 0) {
         if (dgt < 0) {
           s_none = 1;  // everything in range fits (only possible in the first pass)
@@ -709,15 +698,7 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
       rows += sz[j];
     }
   __shared__ int wsum[NW], wrows[NW];
-  int incl = cnt, rincl = rows;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o), z = __shfl_up(rincl, o);
-    if (lane >= o) {
-      incl += y;
-      rincl += z;
-    }
-  }
+  const int incl = wave_incl_scan_i32(cnt), rincl = wave_incl_scan_i32(rows);
   if (lane == 63) {
     wsum[wave] = incl;
     wrows[wave] = rincl;
@@ -964,12 +945,7 @@ __device__ int attend_load_selection(const kv_pool &pool, int bg, const int32_t 
   int run = 0;
 #pragma unroll
   for (int j = 0; j < PER_MAX; ++j) run += sz[j];
-  int incl = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan_i32(run);
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
   int off = incl - run, tot = 0;

@@ -510,19 +510,12 @@ __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict
 
 constexpr int kLabelBlock = 256;  // labels per k_colscan workgroup
 
-// Sum over the wave of an int (every lane gets it).
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 // Start of label blocks: the sum of the totals of blocks 0 .. blk - 1 of
 // head bh (one wave; blk <= 64).
 __device__ __forceinline__ int label_block_base(const int32_t *__restrict__ agg, int nblk,
                                                 int bh, int blk) {
   const int lane = threadIdx.x & 63;
-  return wave_sum_i(lane < blk ? agg[(size_t)bh * nblk + lane] : 0);
+  return wave_sum_i32(lane < blk ? agg[(size_t)bh * nblk + lane] : 0);
 }
 
 __global__ void __launch_bounds__(kLabelBlock)
@@ -549,12 +542,7 @@ __global__ void __launch_bounds__(kLabelBlock)
     }
   }
   // exclusive prefix of the totals within the block of 256 labels
-  int incl = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan_i32(run);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int off = 0, all = 0;
@@ -586,13 +574,7 @@ __global__ void __launch_bounds__(256)
   if (threadIdx.x < 64) {  // wave 0: exclusive scan of the block totals
     const int lane = threadIdx.x;
     const int v = lane < nblk ? agg[(size_t)bh * nblk + lane] : 0;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    s_base[lane] = incl - v;
+    s_base[lane] = wave_incl_scan_i32(v) - v;
   }
   __syncthreads();
   if (i >= n || a < 0 || a >= c) return;  // labels out of range: left out by k_rank_hist too

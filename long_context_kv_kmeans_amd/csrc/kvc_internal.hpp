@@ -143,6 +143,69 @@ template <bool OR> __device__ __forceinline__ unsigned long long wave_bits64(uns
          ((unsigned long long)wave_bits32<OR>((uint32_t)(v >> 32)) << 32);
 }
 
+// Integer sum over the whole wave, in every lane (same pairing as group_sum;
+// exact, so the pairing does not matter).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowMirror, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowHalfMirror, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppQuadSwap2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppQuadSwap1, 0xf, 0xf, false);
+  const auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int)r16[0] + (int)r16[1];
+  const auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)r32[0] + (int)r32[1];
+}
+
+// Inclusive prefix sums over the wave in lane order, by DPP lane moves only:
+// shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in from
+// outside the row read 0), then the last lane of row 0 and of row 2 added to
+// rows 1 and 3, and the last lane of row 1 added to rows 2 and 3.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false);
+  return v;
+}
+
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ long long dpp_mov_i64(long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, BOUND);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((unsigned long long)v >> 32), CTRL,
+                                             ROWS, 0xf, BOUND);
+  return (long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ long long wave_incl_scan_i64(long long v) {
+  v += dpp_mov_i64<kDppRowShr1, 0xf, true>(v);
+  v += dpp_mov_i64<kDppRowShr2, 0xf, true>(v);
+  v += dpp_mov_i64<kDppRowShr4, 0xf, true>(v);
+  v += dpp_mov_i64<kDppRowShr8, 0xf, true>(v);
+  v += dpp_mov_i64<kDppRowBcast15, 0xa, false>(v);
+  v += dpp_mov_i64<kDppRowBcast31, 0xc, false>(v);
+  return v;
+}
+
+// The value of lane `src` (the same in every lane) in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+__device__ __forceinline__ long long lane_value_i64(long long v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((unsigned long long)v >> 32), src);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // Maximum over the whole wave, in every lane (same pairing as group_sum).
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
