@@ -504,7 +504,16 @@ __device__ __forceinline__ void score_units64(const T *__restrict__ idx, float *
   }
 }
 
-// Unit sizes of this thread's KPT consecutive units (tid KPT ..), 0 past U.
+// The selection's units: slot j (< KPT) of wave w, lane l holds unit
+// (w KPT + j) 64 + l, so that each wave instruction that reads or writes a
+// per-unit value touches 64 consecutive units (the scores, written by other
+// workgroups, are read past the L2s: 256 contiguous bytes per instruction
+// rather than one dword from each of 64 lines).
+template <int KPT> __device__ __forceinline__ int select_unit(int j) {
+  return (((int)threadIdx.x >> 6) * KPT + j) * 64 + ((int)threadIdx.x & 63);
+}
+
+// Unit sizes of this thread's KPT units, 0 past U.
 template <int KPT>
 __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U, int (&sz)[KPT]) {
   const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
@@ -513,17 +522,17 @@ __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U,
   // makes the compiler wait for it there, one round trip per load.
   int raw[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) raw[j] = usz[min((int)threadIdx.x * KPT + j, pool.unit_cap - 1)];
+  for (int j = 0; j < KPT; ++j) raw[j] = usz[min(select_unit<KPT>(j), pool.unit_cap - 1)];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int u = threadIdx.x * KPT + j;
+    const int u = select_unit<KPT>(j);
     sz[j] = (u < U && raw[j] > 0) ? raw[j] : 0;
   }
 }
 
 // The selection proper, run by the one workgroup of NT threads that holds all
 // of (b, g)'s scores: every candidate becomes a 64-bit key (orderable score
-// << 32 | ~id), KPT consecutive units per thread; an MSB-first weighted radix
+// << 32 | ~id), KPT units per thread (select_unit); an MSB-first weighted radix
 // select (per-wave LDS histograms hw / hc [NT / 64][256], one 8-bit digit
 // per pass from the highest bit in which the keys differ, a thread's run of
 // equal digits counted once and a wave whose keys share one digit counted
@@ -544,10 +553,10 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   unsigned long long kor = 0ull, kand = ~0ull;
   float scv[KPT];  // all requested at once (clamped index), masked below
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) scv[j] = coherent_load(&sc[min(tid * KPT + j, pool.unit_cap - 1)]);
+  for (int j = 0; j < KPT; ++j) scv[j] = coherent_load(&sc[min(select_unit<KPT>(j), pool.unit_cap - 1)]);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int u = tid * KPT + j;
+    const int u = select_unit<KPT>(j);
     key[j] = sz[j] > 0 ? unit_key(scv[j], u) : 0ull;
     if (sz[j] > 0) {
       kor |= key[j];
@@ -689,51 +698,54 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   const bool take_all = s_none != 0;
   const unsigned long long kstar = s_kstar;
 
-  // ---- compaction in ascending unit id (thread t owns units t*KPT .. t*KPT+KPT-1)
-  int cnt = 0, rows = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (sz[j] > 0 && (take_all || key[j] > kstar)) {
-      ++cnt;
-      rows += sz[j];
-    }
-  __shared__ int wsum[NW], wrows[NW];
-  const int incl = wave_incl_scan_i32(cnt), rincl = wave_incl_scan_i32(rows);
-  if (lane == 63) {
-    wsum[wave] = incl;
-    wrows[wave] = rincl;
-  }
-  __syncthreads();
-  int off = 0, total = 0, total_rows = 0;
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) off += wsum[w];
-    total += wsum[w];
-    total_rows += wrows[w];
-  }
-  int pos = off + incl - cnt;
+  // ---- compaction in ascending unit id: units go in (wave, slot, lane)
+  // order, so a unit's position is the selected count of the earlier waves,
+  // of this wave's earlier slots and of the slot's lower lanes (ballots)
   int32_t *out = sel_units + (size_t)bg * sel_cap;
   int32_t *spans = sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr;
   const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
   int ustv[KPT];  // first rows, requested together (clamped index) rather than one wait per unit
   if (spans) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) ustv[j] = ust[min(tid * KPT + j, pool.unit_cap - 1)];
+    for (int j = 0; j < KPT; ++j) ustv[j] = ust[min(select_unit<KPT>(j), pool.unit_cap - 1)];
   }
+  uint64_t bsel[KPT];
+  int cnt = 0, rows = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (sz[j] > 0 && (take_all || key[j] > kstar)) {
-      if (pos < sel_cap) {
-        const int u = tid * KPT + j;
-        out[pos] = u;
-        if (spans) {
-          if constexpr (COH)
-            coherent_store_i2(spans + 2 * pos, int2{ustv[j], sz[j]});
-          else
-            *reinterpret_cast<int2 *>(spans + 2 * pos) = int2{ustv[j], sz[j]};
-        }
+  for (int j = 0; j < KPT; ++j) {
+    const bool sj = sz[j] > 0 && (take_all || key[j] > kstar);
+    bsel[j] = __ballot(sj);
+    cnt += __popcll(bsel[j]);
+    rows += sj ? sz[j] : 0;
+  }
+  rows = wave_sum_i32(rows);
+  __shared__ int wsum[NW], wrows[NW];
+  if (lane == 0) {
+    wsum[wave] = cnt;
+    wrows[wave] = rows;
+  }
+  __syncthreads();
+  int pos = 0, total = 0, total_rows = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) pos += wsum[w];
+    total += wsum[w];
+    total_rows += wrows[w];
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int p = pos + __popcll(bsel[j] & below);
+    if (((bsel[j] >> lane) & 1ull) && p < sel_cap) {
+      out[p] = select_unit<KPT>(j);
+      if (spans) {
+        if constexpr (COH)
+          coherent_store_i2(spans + 2 * p, int2{ustv[j], sz[j]});
+        else
+          *reinterpret_cast<int2 *>(spans + 2 * p) = int2{ustv[j], sz[j]};
       }
-      ++pos;
     }
+    pos += __popcll(bsel[j]);
+  }
   if (tid == 0) {
     if (total > sel_cap) {
       __hip_atomic_store(pool.status, (int)KV_ERR_CAPACITY, __ATOMIC_RELAXED,
