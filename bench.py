@@ -310,9 +310,12 @@ def main():
         raise SystemExit(f"unknown --units {args.units!r}")
     variant = host or sched is not None or page is not None
     # the whole layer-step in one launch where the path is boundary test -> select ->
-    # fused fetch + attention
-    one = (fetch and args.fetch == "fused" and not seg and sched is None
+    # fused fetch + attention; per-token retrieval is that launch with a boundary
+    # threshold no cosine reaches (every step retrieves)
+    every = sched is not None and bool(sched.all())
+    one = (fetch and args.fetch == "fused" and not seg and (sched is None or every)
            and args.launches == "one" and args.pool != "host-direct" and cfg.dtype == "bf16")
+    tau_step = float("inf") if every else cfg.tau
     if seg and (sched is not None or page is not None or (fetch and args.fetch == "separate")):
         raise SystemExit("with decode segments (--config 2) only --pool host|host-direct "
                          "(fused fetch) applies")
@@ -409,7 +412,7 @@ def main():
         q_prev = y.q[t - 1] if t else None
         flag = y.flags[t]
         if one:
-            kvc.kv_decode_step(y.pool, q_prev, y.q[t], cfg.tau, cfg.scale, cfg.budget, flag,
+            kvc.kv_decode_step(y.pool, q_prev, y.q[t], tau_step, cfg.scale, cfg.budget, flag,
                                y.sel, y.sel_spans, y.sel_n, y.sel_rows, y.wset, y.wspans, y.wn,
                                y.out, ws=y.ws_step)
             return
@@ -548,7 +551,17 @@ def main():
     if one:
         # the whole layer-step on a step without retrieval for every sequence (the
         # boundary test, then the working set): two adjacent queries of a drift step
-        t_nr = int(np.nonzero(~fl.any(1))[0][-1])
+        if sched is None:
+            drift = ~fl.any(1)
+        else:  # the schedule retrieved every step: where would the boundary test not?
+            fb = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
+            for t in range(1, T):
+                kvc.kv_boundary(y0.q[t - 1], y0.q[t], cfg.tau, fb[t])
+            drift = ~fb.cpu().numpy().astype(bool).any(1)
+            drift[0] = False
+        if not drift.any():
+            raise SystemExit("no decode step without retrieval to time the plain layer-step on")
+        t_nr = int(np.nonzero(drift)[0][-1])
         flag_tmp = torch.zeros(B, dtype=torch.uint8, device="cuda")
 
         def att_fn(wset=None):
@@ -626,6 +639,33 @@ def main():
                      "h2d_copy_gbs": (64 << 20) / (h2d_ms * 1e-3) / 1e9,
                      "fetch_attend_retrieval_ms": fa_ms,
                      "fetch_attend_gbs": f_bytes / (fa_ms * 1e-3) / 1e9}
+
+    # Phases of a retrieval step, every sequence retrieving: the selection alone
+    # (kv_select: scoring + budgeted selection, one launch) and, on the
+    # one-launch path, the whole retrieval layer-step (kv_decode_step with a
+    # threshold no cosine reaches: boundary test, scoring, selection, working-set
+    # fetch, attention) beside the plain layer-step timed above. Last, since both
+    # rewrite the selection and the working set.
+    retrieval = None
+    if fetch and not seg and cfg.dtype == "bf16" and args.pool != "host-direct":
+        ws_sel0 = y0.ws_sel
+        sel_ms = launch_ms(lambda: kvc.kv_select(pool, y0.q[T - 1], cfg.budget, None, sel, sel_n,
+                                                 sel_rows, ws=ws_sel0, sel_spans=sel_spans),
+                           args.attend_reps)
+        retrieval = {"select_us": sel_ms * 1e3, "units_scored": B * H * C}
+        if one:
+            flag_r = torch.zeros(B, dtype=torch.uint8, device="cuda")
+            ret_ms = launch_ms(lambda: kvc.kv_decode_step(
+                pool, y0.q[T - 2], y0.q[T - 1], float("inf"), cfg.scale, cfg.budget, flag_r, sel,
+                sel_spans, sel_n, sel_rows, y0.wset, y0.wspans, y0.wn, y0.out, ws=y0.ws_step),
+                args.attend_reps)
+            retrieval.update({"step_us": ret_ms * 1e3, "plain_step_us": att_ms * 1e3})
+        retrieval["how"] = ("HIP events around back-to-back launches on the final step's "
+                            "queries, every sequence retrieving; select_us: kv_select (scoring + "
+                            "selection)" + ("; step_us: kv_decode_step retrieving (boundary, "
+                                            "scoring, selection, working-set fetch, attention); "
+                                            "plain_step_us: the same launch on a step without "
+                                            "retrieval" if one else ""))
 
     # MFMA K-means assignment against prepared centroids (the kernel the
     # prefill runs once per Lloyd round)
@@ -712,6 +752,7 @@ def main():
                    "prefill_keys_shared_across_layers": False,
                    "decode_steps_overridden": args.decode_steps is not None},
         "retrieval_steps": int(fl.sum()),
+        "retrieval": retrieval,
         "prefill_ms": pre_ms,
         "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),
         "decode_us_per_layer_step": dec_us,
