@@ -551,6 +551,7 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned long long key[KPT];
   unsigned long long kor = 0ull, kand = ~0ull;
+  uint32_t vmax = 0u, vmin = 0xffffffffu;  // score parts of the keys
   float scv[KPT];  // all requested at once (clamped index), masked below
 #pragma unroll
   for (int j = 0; j < KPT; ++j) scv[j] = coherent_load(&sc[min(select_unit<KPT>(j), pool.unit_cap - 1)]);
@@ -561,26 +562,37 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
     if (sz[j] > 0) {
       kor |= key[j];
       kand &= key[j];
+      vmax = max(vmax, (uint32_t)(key[j] >> 32));
+      vmin = min(vmin, (uint32_t)(key[j] >> 32));
     }
   }
 
   __shared__ unsigned long long hk[256];
   __shared__ unsigned long long s_or[NW], s_and[NW];
+  __shared__ uint32_t s_vmax[NW], s_vmin[NW];
   __shared__ long s_above;
-  __shared__ int s_done, s_none;
+  __shared__ int s_done, s_none, s_cnt, s_cn;
   __shared__ unsigned long long s_prefix, s_kstar;
-  // The bits in which the candidates' keys differ: the passes start at the
-  // highest of them (the bits above are common to every key).
+  __shared__ unsigned long long s_ck[64];
+  __shared__ int s_cs[64];
+  // The bits in which the candidates' keys differ (the bit passes start at the
+  // highest of them: the bits above are common to every key) and the range of
+  // their scores.
   kor = wave_bits64<true>(kor);
   kand = wave_bits64<false>(kand);
+  vmax = wave_max_u32(vmax);
+  vmin = wave_min_u32(vmin);
   if (lane == 0) {
     s_or[wave] = kor;
     s_and[wave] = kand;
+    s_vmax[wave] = vmax;
+    s_vmin[wave] = vmin;
   }
   if (tid == 0) {
     s_above = 0;
     s_done = 0;
     s_none = 0;
+    s_cn = 0;
   }
   __syncthreads();
   kor = 0ull;
@@ -589,29 +601,29 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   for (int v = 0; v < NW; ++v) {
     kor |= s_or[v];
     kand &= s_and[v];
+    vmax = max(vmax, s_vmax[v]);
+    vmin = min(vmin, s_vmin[v]);
   }
-  const unsigned long long diff = kor ^ kand;
-  const int hibit = diff ? 63 - __clzll((long long)diff) : 0;
-  // pass: bits [sh, sh + width) of keys that agree with the prefix above them
-  int sh = max(hibit - 7, 0), width = 8;
-  unsigned long long prefix = (sh + width >= 64) ? 0ull : (kand >> (sh + width)) << (sh + width);
-  for (;;) {
+
+  // One counting pass: every candidate with in(j) adds its weight and count to
+  // the bucket dig(j) (0..255) of its wave's histogram row; wave 0 then finds
+  // the crossing bucket over the rows (digits from 255 down, after the weight
+  // s_above already above them). Sets s_prefix's digit field through `mark`,
+  // s_above, s_cnt (the crossing bucket's units), or s_none / s_done.
+  auto count_pass = [&](auto in, auto dig, auto mark) {
     // each wave counts into its own histogram row: cleared and filled in
     // program order, so no barrier between
     for (int i = lane; i < 256; i += 64) {
       hw[wave][i] = 0;
       hc[wave][i] = 0;
     }
-    const int top = sh + width;
-    const unsigned long long dmask = (1ull << width) - 1ull;
-    // runs of equal digits among this thread's consecutive units count once
+    // runs of equal digits among this thread's units count once
     int rd = -1, rw = 0, rc = 0;
     unsigned long long rk = 0ull;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool in = sz[j] > 0 && (top >= 64 || (key[j] >> top) == (prefix >> top));
-      if (!in) continue;
-      const int dgt = (int)((key[j] >> sh) & dmask);
+      if (!in(j)) continue;
+      const int dgt = dig(j);
       if (dgt != rd) {
         if (rc > 0) {
           atomicAdd(&hw[wave][rd], rw);
@@ -674,25 +686,93 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
           s_done = 1;
         } else {
           s_above = above_out;
-          s_prefix = prefix | ((unsigned long long)dgt << sh);
+          s_cnt = cnt;
+          mark(dgt);
           if (cnt == 1) {
             s_kstar = hk[dgt];
-            s_done = 1;
-          } else if (sh == 0) {
-            s_kstar = s_prefix;
             s_done = 1;
           }
         }
       }
     }
     __syncthreads();
-    if (s_done) break;
-    prefix = s_prefix;
-    if (sh >= 8) {
-      sh -= 8;
-    } else {
-      width = sh;
-      sh = 0;
+  };
+
+  // First pass over score values: 256 equal-width buckets between the lowest
+  // and the highest score (monotone in the score, so in key order), which
+  // spread the candidates where the top bits of their keys do not. Skipped
+  // when a score is not finite or all are equal.
+  const float smax = order_key_float(vmax), smin = order_key_float(vmin);
+  const float vrange = smax - smin, vscale = 256.0f / vrange;
+  const bool vpass = vmax > vmin && isfinite(smax) && isfinite(smin) && vrange > 0.f &&
+                     isfinite(vscale);
+  auto vdigit = [&](int j) {
+    const float sj = order_key_float((uint32_t)(key[j] >> 32));
+    return min(255, (int)((sj - smin) * vscale));
+  };
+  int vstar = -1;  // the crossing value bucket
+  if (vpass) {
+    count_pass([&](int j) { return sz[j] > 0; }, vdigit, [&](int d) { s_prefix = (unsigned long long)d; });
+    vstar = (int)s_prefix;
+    if (!s_done && s_cnt <= 64) {
+      // few units in the crossing bucket: wave 0 ranks them directly (the
+      // weight of the bucket's units above each, added to the weight above
+      // the bucket) and the unit whose own weight crosses the budget ends it
+      for (int j = 0; j < KPT; ++j)
+        if (sz[j] > 0 && vdigit(j) == vstar) {
+          const int p = atomicAdd(&s_cn, 1);
+          s_ck[p] = key[j];
+          s_cs[p] = sz[j];
+        }
+      __syncthreads();
+      if (wave == 0) {
+        const int n = s_cn;
+        const unsigned long long mine = lane < n ? s_ck[lane] : 0ull;
+        const long base = s_above;
+        long ab = base;
+        for (int k = 0; k < n; ++k)
+          if (s_ck[k] > mine) ab += s_cs[k];
+        const bool cross = lane < n && ab <= budget && ab + (lane < n ? s_cs[lane] : 0) > budget;
+        const uint64_t who = __ballot(cross);
+        if (lane == 0) {
+          s_kstar = who ? s_ck[__ffsll((unsigned long long)who) - 1] : s_ck[0];
+          s_done = 1;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!s_done) {
+    // MSB-first bit passes: bits [sh, sh + width) of the keys that agree with
+    // the prefix above them (and lie in the crossing value bucket)
+    const unsigned long long diff = kor ^ kand;
+    const int hibit = diff ? 63 - __clzll((long long)diff) : 0;
+    int sh = max(hibit - 7, 0), width = 8;
+    unsigned long long prefix = (sh + width >= 64) ? 0ull : (kand >> (sh + width)) << (sh + width);
+    for (;;) {
+      const int top = sh + width;
+      const unsigned long long dmask = (1ull << width) - 1ull;
+      count_pass(
+          [&](int j) {
+            return sz[j] > 0 && (top >= 64 || (key[j] >> top) == (prefix >> top)) &&
+                   (vstar < 0 || vdigit(j) == vstar);
+          },
+          [&](int j) { return (int)((key[j] >> sh) & dmask); },
+          [&](int d) {
+            s_prefix = prefix | ((unsigned long long)d << sh);
+            if (sh == 0) {
+              s_kstar = s_prefix;
+              s_done = 1;
+            }
+          });
+      if (s_done) break;
+      prefix = s_prefix;
+      if (sh >= 8) {
+        sh -= 8;
+      } else {
+        width = sh;
+        sh = 0;
+      }
     }
   }
   const bool take_all = s_none != 0;

@@ -138,6 +138,21 @@ template <bool OR> __device__ __forceinline__ uint32_t wave_bits32(uint32_t v) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return op(r32[0], r32[1]);
 }
+// Unsigned maximum / minimum over the whole wave, in every lane (same pairing).
+template <bool MAX> __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowMirror, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowHalfMirror, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap2, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap1, 0xf, 0xf, false));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_ext_u32<true>(v); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_ext_u32<false>(v); }
+
 template <bool OR> __device__ __forceinline__ unsigned long long wave_bits64(unsigned long long v) {
   return (unsigned long long)wave_bits32<OR>((uint32_t)v) |
          ((unsigned long long)wave_bits32<OR>((uint32_t)(v >> 32)) << 32);
@@ -266,6 +281,11 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The float whose float_order_key is k (-0 comes back as +0).
+__device__ __forceinline__ float order_key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

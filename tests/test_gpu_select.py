@@ -149,6 +149,41 @@ def test_select_ties_large_and_empty_units():
     assert got.tolist() == np.nonzero(sizes)[0].tolist()
 
 
+@pytest.mark.parametrize("case", ["outlier", "infinite", "all_equal", "two_values", "eps_range",
+                                  "tiny_range"])
+def test_select_score_distributions(case):
+    """Score layouts for the selection's first pass (equal-width buckets between
+    the lowest and highest score) and its fallbacks: a far outlier that puts
+    hundreds of units in the crossing bucket, infinite scores (no value pass),
+    all scores equal, two distinct values, and a range so narrow that the
+    bucket width is not representable. Bit-exact against the oracle's rule."""
+    rng = np.random.default_rng(17)
+    U = 3000
+    if case == "outlier":
+        scores = rng.standard_normal(U).astype(np.float32)
+        scores[5] = 1.0e6
+    elif case == "infinite":
+        scores = rng.standard_normal(U).astype(np.float32)
+        scores[7], scores[11] = np.inf, -np.inf
+    elif case == "all_equal":
+        scores = np.full(U, 0.5, np.float32)
+    elif case == "two_values":
+        scores = np.where(rng.random(U) < 0.5, 1.0, 2.0).astype(np.float32)
+    elif case == "eps_range":
+        scores = (1.0 + rng.integers(0, 4, U) * np.finfo(np.float32).eps).astype(np.float32)
+    else:  # normal floats whose range is too small for 256 / range to be finite
+        scores = (1e-37 * (1.0 + 0.1 * rng.integers(0, 4, U))).astype(np.float32)
+    sizes = rng.integers(1, 9, U)
+    pool, q = _hand_pool(scores, sizes)
+    for budget in [1, 9, 100, 1000, 7000, int(sizes.sum()) - 1]:
+        cap = max(1, min(budget, U))
+        (su, sn, sr), _ = _run_select(pool, q, budget, cap)
+        got = su[0, 0, :int(sn[0, 0])].cpu().numpy()
+        ref = osel.select_prefix(scores.astype(np.float64), sizes, budget)
+        np.testing.assert_array_equal(got, ref, err_msg=f"{case} budget {budget}")
+        assert int(sr[0, 0]) == int(sizes[ref].sum())
+
+
 def test_select_negative_zero_and_negative_scores():
     scores = np.array([-0.0, 0.0, -1.5, -1.5, 2.0], np.float32)
     sizes = [1, 1, 1, 1, 1]
