@@ -481,15 +481,16 @@ __device__ __forceinline__ void score_units64(const T *__restrict__ idx, float *
   // every load of the wave's 64 units in flight at once (one round trip)
   constexpr int UNR = 64 / UPW < 16 ? 64 / UPW : 16;
   const int part = lane % LPU, slot = lane / LPU;
+  const int ulast = max(U - 1, 0);  // loads at clamped units (in the pool), masked at the store
 #pragma unroll
   for (int j0 = 0; j0 < 64; j0 += UPW * UNR) {
     uint4 v[UNR];
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
-      const int u = u0 + j0 + i * UPW + slot;
-      v[i] = u < U ? *reinterpret_cast<const uint4 *>(idx + (size_t)u * D + part * EPL)
-                   : uint4{0u, 0u, 0u, 0u};
+      const int u = min(u0 + j0 + i * UPW + slot, ulast);
+      v[i] = *reinterpret_cast<const uint4 *>(idx + (size_t)u * D + part * EPL);
     }
+    float dots[UNR];
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       float f[EPL];
@@ -497,9 +498,24 @@ __device__ __forceinline__ void score_units64(const T *__restrict__ idx, float *
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dot = fmaf(qs[e], f[e], dot);
-      dot = group_sum<LPU>(dot);
-      const int u = u0 + j0 + i * UPW + slot;
-      if (part == 0 && u < U) coherent_store(&sc[u], dot);
+      dots[i] = group_sum<LPU>(dot);
+    }
+    if constexpr (UNR * UPW == 64) {
+      // one store instruction for the 64 units: lane s offers the dot of its
+      // group's unit i = s % LPU, and lane l takes unit l's from lane
+      // (l % UPW) LPU + l / UPW
+      float w = dots[0];
+#pragma unroll
+      for (int i = 1; i < UNR; ++i) w = (part == i) ? dots[i] : w;
+      const int src = (lane % UPW) * LPU + lane / UPW;
+      const float mine = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(w)));
+      if (u0 + lane < U) coherent_store(&sc[u0 + lane], mine);
+    } else {
+#pragma unroll
+      for (int i = 0; i < UNR; ++i) {
+        const int u = u0 + j0 + i * UPW + slot;
+        if (part == 0 && u < U) coherent_store(&sc[u], dots[i]);
+      }
     }
   }
 }
@@ -513,16 +529,21 @@ template <int KPT> __device__ __forceinline__ int select_unit(int j) {
   return (((int)threadIdx.x >> 6) * KPT + j) * 64 + ((int)threadIdx.x & 63);
 }
 
-// Unit sizes of this thread's KPT units, 0 past U.
+// Unit sizes (0 past U) and first rows of this thread's KPT units.
 template <int KPT>
-__device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U, int (&sz)[KPT]) {
+__device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U, int (&sz)[KPT],
+                                             int (&ust)[KPT]) {
   const int32_t *usz = pool.unit_size + (size_t)bg * pool.unit_cap;
+  const int32_t *ustp = pool.unit_start + (size_t)bg * pool.unit_cap;
   // Every load is issued, at a clamped index, and masked afterwards: a load
   // under a per-lane condition whose result is reshaped inside the branch
   // makes the compiler wait for it there, one round trip per load.
   int raw[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) raw[j] = usz[min(select_unit<KPT>(j), pool.unit_cap - 1)];
+  for (int j = 0; j < KPT; ++j) {
+    raw[j] = usz[min(select_unit<KPT>(j), pool.unit_cap - 1)];
+    ust[j] = ustp[min(select_unit<KPT>(j), pool.unit_cap - 1)];
+  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int u = select_unit<KPT>(j);
@@ -542,7 +563,8 @@ __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U,
 // with sel_n and sel_rows. Ends with a barrier.
 template <int NT, int KPT, bool COH = false>
 __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, const float *sc,
-                                    const int (&sz)[KPT], int32_t *__restrict__ sel_units,
+                                    const int (&sz)[KPT], const int (&ustv)[KPT],
+                                    int32_t *__restrict__ sel_units,
                                     int sel_cap, int32_t *__restrict__ sel_n,
                                     int32_t *__restrict__ sel_rows,
                                     int32_t *__restrict__ sel_spans, int (*hw)[256],
@@ -783,12 +805,6 @@ __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, con
   // of this wave's earlier slots and of the slot's lower lanes (ballots)
   int32_t *out = sel_units + (size_t)bg * sel_cap;
   int32_t *spans = sel_spans ? sel_spans + (size_t)bg * sel_cap * 2 : nullptr;
-  const int32_t *ust = pool.unit_start + (size_t)bg * pool.unit_cap;
-  int ustv[KPT];  // first rows, requested together (clamped index) rather than one wait per unit
-  if (spans) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) ustv[j] = ust[min(select_unit<KPT>(j), pool.unit_cap - 1)];
-  }
   uint64_t bsel[KPT];
   int cnt = 0, rows = 0;
 #pragma unroll
@@ -887,13 +903,13 @@ __global__ void __launch_bounds__(kSelectThreads)
 
   // ---- completion: the last block of (b, g) selects. Unit sizes are
   // requested before the arrival so that they land with the store acks.
-  int sz[KPT];
-  select_sizes<KPT>(pool, bg, U, sz);
+  int sz[KPT], ust[KPT];
+  select_sizes<KPT>(pool, bg, U, sz, ust);
   __shared__ int s_last;
   if (!last_block_arrives(&counters[bg], (int)gridDim.x, &s_last)) return;
   __shared__ int hw[kSelectWaves][256];
   __shared__ int hc[kSelectWaves][256];
-  select_prefix_block<kSelectThreads, KPT>(pool, bg, budget, sc, sz, sel_units, sel_cap, sel_n,
+  select_prefix_block<kSelectThreads, KPT>(pool, bg, budget, sc, sz, ust, sel_units, sel_cap, sel_n,
                                            sel_rows, sel_spans, hw, hc);
   if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1395,10 +1411,10 @@ __device__ void step_select(const kv_pool &pool, const DecodeStep &st,
   const int u_hi = min(U, (split + 1) * ups);
   for (int u0 = split * ups + wave * 64; u0 < u_hi; u0 += NW * 64)
     score_units64<uint16_t, D>(idx, sc, qs, u0, u_hi, lane);
-  int sz[KPT];
-  select_sizes<KPT>(pool, bg, U, sz);
+  int sz[KPT], ust[KPT];
+  select_sizes<KPT>(pool, bg, U, sz, ust);
   if (last_block_arrives(&st.sel_counters[bg], nsplit, s_last)) {
-    select_prefix_block<NT, KPT, true>(pool, bg, st.budget, sc, sz, st.sel_units, st.sel_cap,
+    select_prefix_block<NT, KPT, true>(pool, bg, st.budget, sc, sz, ust, st.sel_units, st.sel_cap,
                                        st.sel_n, st.sel_rows, st.sel_spans, hw, hc);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's coherent stores are acknowledged
     __syncthreads();
