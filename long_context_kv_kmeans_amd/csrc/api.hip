@@ -229,8 +229,12 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
       st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream, fused);
       if (st != KV_OK) return st;
       void *next_frags = (fused && it + 1 < iters) ? asg_ws : nullptr;
-      st = launch_update(keys, labels, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt, upd_ws,
-                         stream, &perm, &start, &tot, next_frags);
+      if (it + 1 < iters && update_local_ok(bh, n_keys, n_clusters))  // the pack reads the last only
+        st = launch_update_local(keys, labels, cent, cent, bh, n_keys, d, n_clusters, dt, upd_ws,
+                                 stream, next_frags);
+      else
+        st = launch_update(keys, labels, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt,
+                           upd_ws, stream, &perm, &start, &tot, next_frags);
       if (st != KV_OK) return st;
     }
   }

@@ -584,6 +584,54 @@ __global__ void __launch_bounds__(256)
   perm[(size_t)bh * n + dest] = i;
 }
 
+// The cluster's member sums (this lane's part of the row, summed over its
+// row slot) -> the mean, which replaces the centroid (an empty cluster keeps
+// its value), and for bf16 keys the next round's MFMA tiles (fragments and
+// norm block).
+template <typename T, int D>
+__device__ __forceinline__ void segsum_finish(float (&acc)[16 / Elem<T>::kBytes], int cnt, int bh,
+                                              int c, int k, int ntile, const float *cent_in,
+                                              float *cent_out, uint16_t *__restrict__ frags) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;
+  constexpr int LPR = D / EPL;
+  const int lane = threadIdx.x & 63;
+  const int part = lane % LPR, slot = lane / LPR;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = sum_stride<LPR>(acc[e]);
+  float mean[EPL];
+  const float *in = cent_in + ((size_t)bh * c + k) * D + part * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) mean[e] = cnt > 0 ? acc[e] / (float)cnt : in[e];
+  if (slot == 0) {
+    float *out = cent_out + ((size_t)bh * c + k) * D + part * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = mean[e];
+  }
+  if (frags != nullptr && EPL == 8) {
+    // element e0 = 8 part lives in k-step e0 / 16, lane half (e0 % 16) / 8
+    uint16_t b[8];
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = f32_to_bf16_rne(mean[e % EPL]);
+      const float r = bf16_bits_to_f32(b[e]);
+      sq = fmaf(r, r, sq);
+    }
+    sq = group_sum<LPR>(sq);
+    const int t = k / 32, m = k % 32, e0 = part * 8;
+    uint4 *tile = reinterpret_cast<uint4 *>(frags) + ((size_t)bh * ntile + t) * AssignTile<D>::U4;
+    if (slot == 0) {
+      uint4 pk;
+      pk.x = b[0] | ((uint32_t)b[1] << 16);
+      pk.y = b[2] | ((uint32_t)b[3] << 16);
+      pk.z = b[4] | ((uint32_t)b[5] << 16);
+      pk.w = b[6] | ((uint32_t)b[7] << 16);
+      tile[(e0 / 16) * 64 + m + 32 * ((e0 % 16) / 8)] = pk;
+    }
+    if (lane == 0) write_centroid_norm(tile, AssignTile<D>::KS, m, -0.5f * sq);
+  }
+}
+
 // One wave per cluster. Lanes split a key row into 16-byte pieces, so one
 // wave instruction reads RPI member rows; members are dealt round-robin to
 // the RPI row slots, each slot sums its members in key order, and the slots
@@ -640,40 +688,194 @@ __global__ void __launch_bounds__(256) k_segsum(int n, int c, int ntile,
       for (int e = 0; e < EPL; ++e) acc[e] += ok[u] ? f[e] : 0.f;
     }
   }
+  segsum_finish<T, D>(acc, cnt, bh, c, k, ntile, cent_in, cent_out, frags);
+}
+
+// ---- two-launch update for the rounds whose permutation nobody reads
+// (every Lloyd round but the last of kv_cluster_build): no global scan.
+//  k_rank_local   -- per chunk of 1024 keys, the ranks of k_rank_hist, then
+//                    the chunk's own exclusive prefix of its label counts and
+//                    a stable local sort: local[chunk base + prefix[a] + rank]
+//                    = key; per (chunk, label) the entry prefix << 16 | count;
+//  k_segsum_local -- per cluster, the chunks' entries in chunk order give its
+//                    members in key order (the order the global sort gives),
+//                    64 at a time into LDS; then the sums of k_segsum, in the
+//                    same order and grouping, so the centroids and tiles are
+//                    the same bits.
+constexpr int kLocalChunk = 1024;
+// A cluster's entries are read one per chunk (a line each) and its members
+// found by a search, so the two launches do not move less data than the four;
+// they save two launches, which is what counts when the launches are short:
+// at most 64 chunks per head, 4096 labels and 1024 chunks in all (measured:
+// 31 against 35 us per round at 8 heads x 32768 keys x 2048 clusters; 352
+// against 357 us at 128 heads of that size; 169 against 131 us at 8 heads x
+// 131072 keys x 8192 clusters).
+constexpr int kLocalMaxChunks = 64;  // n <= 65536 keys per head
+constexpr int kSegWindow = 64;        // members placed in LDS at a time
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) k_rank_local(const int32_t *__restrict__ labels,
+                                                        int32_t *__restrict__ local,
+                                                        int32_t *__restrict__ ltab, int n, int c,
+                                                        int nbits, int nchunk) {
+  constexpr int KPW = kLocalChunk / NW;
+  constexpr int SUB = KPW / 64;
+  extern __shared__ int32_t cnt[];  // [NW][c]: label counts of each wave's part
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t *lab = labels + (size_t)bh * n;
+  const int base = ch * kLocalChunk + wave * KPW;
+  int a[SUB];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = sum_stride<LPR>(acc[e]);
-  float mean[EPL];
-  const float *in = cent_in + ((size_t)bh * c + k) * D + part * EPL;
+  for (int sub = 0; sub < SUB; ++sub) a[sub] = lab[min(base + sub * 64 + lane, n - 1)];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) mean[e] = cnt > 0 ? acc[e] / (float)cnt : in[e];
-  if (slot == 0) {
-    float *out = cent_out + ((size_t)bh * c + k) * D + part * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) out[e] = mean[e];
+  for (int sub = 0; sub < SUB; ++sub) {
+    const int i = base + sub * 64 + lane;
+    const int v = i < n ? a[sub] : -1;
+    a[sub] = (v >= 0 && v < c) ? v : -1;
   }
-  if (frags != nullptr && EPL == 8) {
-    // element e0 = 8 part lives in k-step e0 / 16, lane half (e0 % 16) / 8
-    uint16_t b[8];
-    float sq = 0.f;
+  for (int k = threadIdx.x; k < NW * c; k += 64 * NW) cnt[k] = 0;
+  __syncthreads();
+  int32_t *mine = cnt + wave * c;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int r[SUB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      b[e] = f32_to_bf16_rne(mean[e % EPL]);
-      const float r = bf16_bits_to_f32(b[e]);
-      sq = fmaf(r, r, sq);
+  for (int sub = 0; sub < SUB; ++sub) {
+    const bool valid = a[sub] >= 0;
+    const int v = valid ? a[sub] : 0;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (v >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      mask &= bit ? m : ~m;
     }
-    sq = group_sum<LPR>(sq);
-    const int t = k / 32, m = k % 32, e0 = part * 8;
-    uint4 *tile = reinterpret_cast<uint4 *>(frags) + ((size_t)bh * ntile + t) * AssignTile<D>::U4;
-    if (slot == 0) {
-      uint4 pk;
-      pk.x = b[0] | ((uint32_t)b[1] << 16);
-      pk.y = b[2] | ((uint32_t)b[3] << 16);
-      pk.z = b[4] | ((uint32_t)b[5] << 16);
-      pk.w = b[6] | ((uint32_t)b[7] << 16);
-      tile[(e0 / 16) * 64 + m + 32 * ((e0 % 16) / 8)] = pk;
+    r[sub] = 0;
+    if (valid) {
+      r[sub] = mine[v] + __popcll(mask & below);
+      if ((mask >> lane) == 1ull) mine[v] += __popcll(mask);
     }
-    if (lane == 0) write_centroid_norm(tile, AssignTile<D>::KS, m, -0.5f * sq);
+    __builtin_amdgcn_wave_barrier();
   }
+  __syncthreads();
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+    if (a[sub] >= 0)
+      for (int w = 0; w < wave; ++w) r[sub] += cnt[w * c + a[sub]];
+  __syncthreads();  // every rank read before row 0 is overwritten
+  // exclusive prefix of the chunk's label counts: wave w takes the labels
+  // [w span, (w + 1) span) in tiles of 64 and leaves prefix-within-its-span
+  // << 16 | count in row 0; the spans' offsets are added on the way out
+  const int span = ((c + NW - 1) / NW + 63) / 64 * 64;
+  int carry = 0;
+  for (int k0 = wave * span; k0 < min((wave + 1) * span, c); k0 += 64) {
+    const int k = k0 + lane;
+    int t = 0;
+    if (k < c)
+      for (int w = 0; w < NW; ++w) t += cnt[w * c + k];
+    const int incl = wave_incl_scan_i32(t);
+    if (k < c) cnt[k] = ((carry + incl - t) << 16) | t;
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  __syncthreads();
+  // a span's total is its last label's prefix + count
+  auto span_off = [&](int k) {
+    const int ws = k / span;
+    int o = 0;
+    for (int w = 0; w < NW - 1; ++w) {
+      const int last = min((w + 1) * span, c) - 1;
+      if (w < ws && last >= w * span) o += (cnt[last] >> 16) + (cnt[last] & 0xffff);
+    }
+    return o;
+  };
+  int32_t *trow = ltab + ((size_t)bh * nchunk + ch) * c;
+  for (int k = threadIdx.x; k < c; k += 64 * NW) trow[k] = cnt[k] + (span_off(k) << 16);
+  int32_t *lrow = local + (size_t)bh * n + (size_t)ch * kLocalChunk;
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+    if (a[sub] >= 0)
+      lrow[(cnt[a[sub]] >> 16) + span_off(a[sub]) + r[sub]] = base + sub * 64 + lane;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_segsum_local(int n, int c, int ntile, int nchunk,
+                                                      const int32_t *__restrict__ ltab,
+                                                      const int32_t *__restrict__ local,
+                                                      const T *__restrict__ keys,
+                                                      const float *cent_in, float *cent_out,
+                                                      uint16_t *__restrict__ frags) {
+  constexpr int EPL = 16 / Elem<T>::kBytes;
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = 64 / LPR;
+  constexpr int UNR = 4;
+  static_assert(kSegWindow % (RPI * UNR) == 0, "window holds whole steps");
+  constexpr int NG = kLocalMaxChunks / 64;
+  __shared__ int s_pre[4][kLocalMaxChunks];  // members of earlier chunks
+  __shared__ int s_at[4][kLocalMaxChunks];   // the chunk's first member in `local`
+  __shared__ int s_mem[4][kSegWindow];
+  const int bh = blockIdx.y, wave = threadIdx.x >> 6;
+  const int k = blockIdx.x * 4 + wave;
+  const int lane = threadIdx.x & 63;
+  const int part = lane % LPR, slot = lane / LPR;
+  if (k >= c) return;
+  // the chunks' (prefix, count) entries of label k, requested together
+  int e[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int chn = min(g * 64 + lane, nchunk - 1);
+    e[g] = ltab[((size_t)bh * nchunk + chn) * c + k];
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g * 64 >= nchunk) break;
+    const int chn = g * 64 + lane;
+    const int m = chn < nchunk ? (e[g] & 0xffff) : 0;
+    const int incl = wave_incl_scan_i32(m);
+    if (chn < nchunk) {
+      s_pre[wave][chn] = cnt + incl - m;
+      s_at[wave][chn] = chn * kLocalChunk + (e[g] >> 16);
+    }
+    cnt += __builtin_amdgcn_readlane(incl, 63);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int32_t *lrow = local + (size_t)bh * n;
+  const T *kb = keys + (size_t)bh * n * D + part * EPL;
+  float acc[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
+  for (int w0 = 0; w0 < cnt; w0 += kSegWindow) {
+    // member w0 + lane: the last chunk whose first member is at or before it
+    const int t = min(w0 + lane, cnt - 1);
+    int lo = 0, hi = nchunk - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[wave][mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int id = lrow[s_at[wave][lo] + (t - s_pre[wave][lo])];
+    __builtin_amdgcn_wave_barrier();
+    s_mem[wave][lane] = id;
+    __builtin_amdgcn_wave_barrier();
+    const int wend = min(w0 + kSegWindow, cnt);
+    for (int j0 = w0; j0 < wend; j0 += RPI * UNR) {
+      uint4 v[UNR];
+      bool ok[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int j = j0 + u * RPI + slot;
+        ok[u] = j < cnt;
+        const int row = s_mem[wave][min(j, cnt - 1) - w0];
+        v[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)row * D);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        float f[EPL];
+        unpack16<T>(v[u], f);
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) acc[q] += ok[u] ? f[q] : 0.f;
+      }
+    }
+  }
+  segsum_finish<T, D>(acc, cnt, bh, c, k, ntile, cent_in, cent_out, frags);
 }
 
 static int ceil_log2(int c) {
@@ -760,6 +962,46 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   if (perm_out) *perm_out = perm;
   if (start_out) *start_out = start;
   if (tot_out) *tot_out = tot;
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+bool update_local_ok(int bh, int n, int c) {
+  const long nchunk = (n + kLocalChunk - 1) / kLocalChunk;
+  return nchunk <= kLocalMaxChunks && c <= 4096 && (long)bh * nchunk <= 1024;
+}
+
+kv_status launch_update_local(const void *keys, const int32_t *labels, const float *cent_in,
+                              float *cent_out, int bh, int n, int d, int c, kv_dtype dt,
+                              void *ws, hipStream_t s, void *frags_out) {
+  if (!update_local_ok(bh, n, c)) return KV_ERR_UNSUPPORTED;
+  const int nchunk = (n + kLocalChunk - 1) / kLocalChunk;
+  // the update workspace's rank and histogram regions hold the local order
+  // and the (prefix, count) table
+  char *w = static_cast<char *>(ws);
+  int32_t *local = reinterpret_cast<int32_t *>(w);
+  w += align_up((size_t)bh * n * 4, 256);
+  int32_t *ltab = reinterpret_cast<int32_t *>(w);
+  const dim3 rg(nchunk, bh);
+  k_rank_local<4><<<rg, 256, (size_t)4 * c * 4, s>>>(labels, local, ltab, n, c, ceil_log2(c),
+                                                      nchunk);
+  const dim3 g((c + 3) / 4, bh);
+  uint16_t *fr = static_cast<uint16_t *>(frags_out);
+  const int ntile = (c + 31) / 32;
+  if (dt == KV_BF16) {
+    if (d == 128)
+      k_segsum_local<uint16_t, 128><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
+                                                      (const uint16_t *)keys, cent_in, cent_out, fr);
+    else
+      k_segsum_local<uint16_t, 64><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
+                                                     (const uint16_t *)keys, cent_in, cent_out, fr);
+  } else {
+    if (d == 128)
+      k_segsum_local<float, 128><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
+                                                    (const float *)keys, cent_in, cent_out, nullptr);
+    else
+      k_segsum_local<float, 64><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
+                                                   (const float *)keys, cent_in, cent_out, nullptr);
+  }
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

@@ -314,6 +314,13 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
                         const int32_t **perm_out, const int32_t **start_out,
                         const int32_t **tot_out, void *frags_out = nullptr,
                         int32_t *status = nullptr);
+// The update of a round whose permutation, starts and counts nobody reads
+// (centroids and next tiles only; the same bits as launch_update), in two
+// launches, where that is the faster way (update_local_ok).
+bool update_local_ok(int bh, int n, int c);
+kv_status launch_update_local(const void *keys, const int32_t *labels, const float *cent_in,
+                              float *cent_out, int bh, int n, int d, int c, kv_dtype dt,
+                              void *ws, hipStream_t s, void *frags_out);
 kv_status launch_pack(const kv_pool *pool, const void *keys, const void *values,
                       const float *cent, const int32_t *perm, const int32_t *start,
                       const int32_t *tot, int n, int c, hipStream_t s);

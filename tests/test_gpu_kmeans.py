@@ -196,6 +196,31 @@ def test_cluster_build_invariants_and_pack(cfg_idx, over, heads):
     assert pool.n_units.cpu().tolist() == [C] and pool.n_cand.cpu().tolist() == [C]
 
 
+@pytest.mark.parametrize("cfg_idx,over,heads", [CASES[0], CASES[2]] + BIG_C)
+def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads):
+    """kv_cluster_build's rounds (the two-launch update of every round but the
+    last) give the same labels and centroids, bit for bit, as running
+    kv_kmeans_assign and kv_kmeans_update round by round from the same start."""
+    cfg = wl.get_config(cfg_idx, **over)
+    iters = 4
+    inp, pool, lab = _cluster_build(cfg, heads, iters)
+    B, H, N, d = inp["keys"].shape
+    keys_d = to_dev(inp["keys"], cfg.dtype).reshape(B * H, N, d)
+    idx = torch.from_numpy(inp["init_idx"]).cuda().reshape(B * H, -1).long()
+    cent = torch.gather(keys_d.float(), 1, idx[..., None].expand(-1, -1, d)).contiguous()
+    labels = torch.zeros(B * H, N, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B * H, cfg.n_clusters, dtype=torch.int32, device="cuda")
+    for _ in range(iters):
+        kvc.kv_kmeans_assign(keys_d, cent, labels)
+        nxt = torch.empty_like(cent)
+        kvc.kv_kmeans_update(keys_d, labels, cent, nxt, counts)
+        cent = nxt
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lab.reshape(B * H, N), labels.cpu().numpy())
+    um = pool.unit_mean[:, :, :cfg.n_clusters].reshape(B * H, cfg.n_clusters, d)
+    assert torch.equal(um, cent)
+
+
 def test_cluster_build_free_running_cfg0():
     cfg = wl.get_config(0)
     inp, pool, lab = _cluster_build(cfg, [0, 1], cfg.iters)
