@@ -777,14 +777,20 @@ __global__ void __launch_bounds__(64 * NW) k_rank_local(const int32_t *__restric
     carry += __builtin_amdgcn_readlane(incl, 63);
   }
   __syncthreads();
-  // a span's total is its last label's prefix + count
+  // where each span starts in the chunk's order: the earlier spans' totals
+  // (a span's total is its last label's prefix + count)
+  int soff[NW];
+  soff[0] = 0;
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    const int last = min(w * span, c) - 1;
+    const int e = last >= (w - 1) * span ? cnt[last] : 0;
+    soff[w] = soff[w - 1] + (e >> 16) + (e & 0xffff);
+  }
   auto span_off = [&](int k) {
-    const int ws = k / span;
     int o = 0;
-    for (int w = 0; w < NW - 1; ++w) {
-      const int last = min((w + 1) * span, c) - 1;
-      if (w < ws && last >= w * span) o += (cnt[last] >> 16) + (cnt[last] & 0xffff);
-    }
+#pragma unroll
+    for (int w = 1; w < NW; ++w) o = k >= w * span ? soff[w] : o;
     return o;
   };
   int32_t *trow = ltab + ((size_t)bh * nchunk + ch) * c;
@@ -808,50 +814,34 @@ __global__ void __launch_bounds__(256) k_segsum_local(int n, int c, int ntile, i
   constexpr int RPI = 64 / LPR;
   constexpr int UNR = 4;
   static_assert(kSegWindow % (RPI * UNR) == 0, "window holds whole steps");
-  constexpr int NG = kLocalMaxChunks / 64;
-  __shared__ int s_pre[4][kLocalMaxChunks];  // members of earlier chunks
-  __shared__ int s_at[4][kLocalMaxChunks];   // the chunk's first member in `local`
-  __shared__ int s_mem[4][kSegWindow];
+  static_assert(kLocalMaxChunks <= 64, "one chunk per lane");
+  __shared__ int s_at[4][kSegWindow];   // positions in `local` of the window's members
+  __shared__ int s_mem[4][kSegWindow];  // the window's members
   const int bh = blockIdx.y, wave = threadIdx.x >> 6;
   const int k = blockIdx.x * 4 + wave;
   const int lane = threadIdx.x & 63;
   const int part = lane % LPR, slot = lane / LPR;
   if (k >= c) return;
-  // the chunks' (prefix, count) entries of label k, requested together
-  int e[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int chn = min(g * 64 + lane, nchunk - 1);
-    e[g] = ltab[((size_t)bh * nchunk + chn) * c + k];
-  }
-  int cnt = 0;
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if (g * 64 >= nchunk) break;
-    const int chn = g * 64 + lane;
-    const int m = chn < nchunk ? (e[g] & 0xffff) : 0;
-    const int incl = wave_incl_scan_i32(m);
-    if (chn < nchunk) {
-      s_pre[wave][chn] = cnt + incl - m;
-      s_at[wave][chn] = chn * kLocalChunk + (e[g] >> 16);
-    }
-    cnt += __builtin_amdgcn_readlane(incl, 63);
-  }
-  __builtin_amdgcn_wave_barrier();
+  // lane = chunk: label k's (prefix, count) entry there; the members of the
+  // earlier chunks; where its members start in `local`
+  const int chn = min(lane, nchunk - 1);
+  const int e = ltab[((size_t)bh * nchunk + chn) * c + k];
+  const int m = lane < nchunk ? (e & 0xffff) : 0;
+  const int incl = wave_incl_scan_i32(m);
+  const int pre = incl - m, at = chn * kLocalChunk + (e >> 16);
+  const int cnt = __builtin_amdgcn_readlane(incl, 63);
   const int32_t *lrow = local + (size_t)bh * n;
   const T *kb = keys + (size_t)bh * n * D + part * EPL;
   float acc[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) acc[q] = 0.f;
   for (int w0 = 0; w0 < cnt; w0 += kSegWindow) {
-    // member w0 + lane: the last chunk whose first member is at or before it
-    const int t = min(w0 + lane, cnt - 1);
-    int lo = 0, hi = nchunk - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[wave][mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int id = lrow[s_at[wave][lo] + (t - s_pre[wave][lo])];
+    // each chunk places the positions of its members that fall in the window
+    // (LDS only), then every lane loads one member
+    const int i1 = min(pre + m, w0 + kSegWindow);
+    for (int i = max(pre, w0); i < i1; ++i) s_at[wave][i - w0] = at + (i - pre);
+    __builtin_amdgcn_wave_barrier();
+    const int id = lrow[s_at[wave][min(w0 + lane, cnt - 1) - w0]];
     __builtin_amdgcn_wave_barrier();
     s_mem[wave][lane] = id;
     __builtin_amdgcn_wave_barrier();
