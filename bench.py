@@ -520,7 +520,7 @@ def main():
         if st != 0:
             raise SystemExit(f"pool status {st} ({kvc.lib().kv_status_string(st).decode()})")
 
-    def launch_ms(fn, reps):
+    def launch_ms(fn, reps, name="launch"):
         """Mean GPU time per launch of fn: `reps` back-to-back launches on
         `stream` between two HIP events, all queued behind a GPU sleep so that
         the host's enqueue rate does not stretch the interval. If the first
@@ -528,21 +528,25 @@ def main():
         may have waited for the host: the sleep is lengthened and the
         measurement taken again."""
         cycles = 20_000_000
+        t_host = 0.0
         for _ in range(5):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 fn()
                 torch.cuda._sleep(cycles)
                 a.record(stream)
+                t0_host = time.perf_counter()
                 for _ in range(reps):
                     fn()
+                t_host = time.perf_counter() - t0_host
                 starved = a.query()
                 b.record(stream)
             torch.cuda.synchronize()
             if not starved:
                 return a.elapsed_time(b) / reps
             cycles *= 4
-        raise SystemExit("launch timing: the host could not queue the launches ahead of the GPU")
+        raise SystemExit(f"{name} timing: the host could not queue {reps} launches ahead of the "
+                         f"GPU ({t_host * 1e3:.1f} ms to queue them)")
 
     # gather-attend on the final step's selection (the state the graph left)
     sel_units_n = int(sel_n.sum().item())
@@ -583,13 +587,15 @@ def main():
             kvc.kv_gather_attend(pool, y0.q[T - 1], cfg.scale, None, sel_n, cfg.budget, y0.out,
                                  ws=y0.ws_att, sel_spans=sel_spans)
         att_spans = sel_units_n
-    att_ms = launch_ms(att_fn, args.attend_reps)
+    att_ms = launch_ms(att_fn, args.attend_reps, "attention")
     # Cold: the same launch over copies of the rows it reads, more than
     # --cold-mib of them, taken in turn back to back, so that every launch
     # finds its rows in neither the L2s nor the Infinity Cache (256 MB).
     att_cold_ms, n_copies = None, 0
-    if fetch:
-        per_copy = 2 * B * H * cfg.budget * d * e
+    per_copy = 2 * B * H * cfg.budget * d * e
+    # (working sets under 1 MiB would need thousands of copies, more launches
+    # than the host queues ahead of the GPU: no cold figure for those)
+    if fetch and per_copy >= (1 << 20):
         n_copies = max(2, -(-(args.cold_mib << 20) // per_copy))
         copies = []
         for _ in range(n_copies):
@@ -603,7 +609,7 @@ def main():
             c = copies[it[0] % n_copies]
             it[0] += 1
             att_fn(c)
-        att_cold_ms = launch_ms(cold_fn, max(args.attend_reps, 2 * n_copies))
+        att_cold_ms = launch_ms(cold_fn, max(args.attend_reps, 2 * n_copies), "cold attention")
         del copies
     att_buf = int((pool.n_rows - pool.buf_begin).sum().item()) * H if seg else 0
     att_bytes = ((att_rows + att_buf) * 2 * d * e  # selected (and local-buffer) K and V rows
