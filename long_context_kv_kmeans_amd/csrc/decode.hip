@@ -384,13 +384,12 @@ kv_status launch_segment_append(const kv_pool *pool, const void *k_t, const void
 // ---------------------------------------------------------------- select
 // Scoring: 512-thread workgroups each score up to 512 units; a unit's index
 // vector is read as 16-byte pieces, so one wave instruction covers 64 / LPU
-// units. Selection: the last workgroup of (b, g) holds every candidate as a
-// 64-bit key (orderable score << 32 | ~id) in registers, KPT consecutive
-// units per thread, and finds the first unit that no longer fits the budget
-// with an MSB-first weighted radix select (per-wave LDS histograms, digits of
-// 8 bits starting at the highest bit in which the keys differ, early exit
-// once the crossing bucket holds a single unit). Every unit ranked before it
-// is selected.
+// units, and a wave's 64 scores leave in one store. Selection: the last
+// workgroup of (b, g) holds every candidate as a 64-bit key (orderable score
+// << 32 | ~id) in registers, KPT units per thread, and finds the first unit
+// that no longer fits the budget (select_prefix_block: a pass over score
+// buckets, then a direct ranking or radix passes within the crossing bucket).
+// Every unit ranked before it is selected.
 constexpr int kSelectThreads = kSelectBlockThreads;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int kScoreUnitsPerBlock = kSelectThreads;
@@ -553,14 +552,18 @@ __device__ __forceinline__ void select_sizes(const kv_pool &pool, int bg, int U,
 
 // The selection proper, run by the one workgroup of NT threads that holds all
 // of (b, g)'s scores: every candidate becomes a 64-bit key (orderable score
-// << 32 | ~id), KPT units per thread (select_unit); an MSB-first weighted radix
-// select (per-wave LDS histograms hw / hc [NT / 64][256], one 8-bit digit
-// per pass from the highest bit in which the keys differ, a thread's run of
-// equal digits counted once and a wave whose keys share one digit counted
-// with one update, early exit once the crossing bucket holds a single unit)
-// finds the first unit that no longer fits the budget; every unit ranked before it
-// is written, in ascending id, to sel_units (and its row span to sel_spans),
-// with sel_n and sel_rows. Ends with a barrier.
+// << 32 | ~id), KPT units per thread (select_unit). The first unit that no
+// longer fits the budget (the crossing unit) is found by counting passes into
+// per-wave LDS histograms hw / hc [NT / 64][256] (weight, count; a thread's
+// run of equal digits counted once, a wave whose keys share one digit counted
+// with one update): first over 256 equal-width buckets of the score between
+// the lowest and highest score (when all scores are finite and differ); a
+// crossing bucket of <= 64 units is then ranked directly by wave 0; otherwise
+// MSB-first 8-bit digits of the keys in that bucket, from the highest bit in
+// which the keys differ, until the crossing digit holds a single unit. Every
+// unit ranked before the crossing unit is written, in ascending id, to
+// sel_units (and its row span to sel_spans), with sel_n and sel_rows. Ends
+// with a barrier.
 template <int NT, int KPT, bool COH = false>
 __device__ void select_prefix_block(const kv_pool &pool, int bg, int budget, const float *sc,
                                     const int (&sz)[KPT], const int (&ustv)[KPT],

@@ -703,13 +703,13 @@ __global__ void __launch_bounds__(256) k_segsum(int n, int c, int ntile,
 //                    same order and grouping, so the centroids and tiles are
 //                    the same bits.
 constexpr int kLocalChunk = 1024;
-// A cluster's entries are read one per chunk (a line each) and its members
-// found by a search, so the two launches do not move less data than the four;
-// they save two launches, which is what counts when the launches are short:
-// at most 64 chunks per head, 4096 labels and 1024 chunks in all (measured:
-// 31 against 35 us per round at 8 heads x 32768 keys x 2048 clusters; 352
-// against 357 us at 128 heads of that size; 169 against 131 us at 8 heads x
-// 131072 keys x 8192 clusters).
+// A cluster's entries are read one per chunk (a line each), so the two
+// launches do not move less data than the four; they save two launches,
+// which is what counts when the launches are short: at most 64 chunks per
+// head, 4096 labels and 1024 chunks in all (measured: 29 against 35 us per
+// round at 8 heads x 32768 keys x 2048 clusters; 352 against 357 us at 128
+// heads of that size; 169 against 131 us at 8 heads x 131072 keys x 8192
+// clusters).
 constexpr int kLocalMaxChunks = 64;  // n <= 65536 keys per head
 constexpr int kSegWindow = 64;        // members placed in LDS at a time
 
