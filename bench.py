@@ -7,7 +7,9 @@ Qwen3-8B-shaped model (8 KV heads, 32 query heads, head dim 128, bf16, batch 1)
 with 131072 prefill keys per KV head, C = 8192 clusters, 10 Lloyd rounds,
 budget 2048 rows and 1024 decode steps:
   prefill : per layer, kv_cluster_build (K-means assign/update x10, then the
-            pack of K/V into cluster-contiguous rows);
+            pack of K/V into cluster-contiguous rows; a head whose assignment
+            changes no label has reached a fixed point and skips the rounds
+            left, with the result of all ten);
   decode  : 1024 steps x 36 layers of kv_decode_step, one launch per
             layer-step: the boundary test on the query pair; on a retrieval
             step, scoring of the centroids, the budgeted top-k selection and
@@ -372,6 +374,7 @@ def main():
             y.init = torch.from_numpy(np.broadcast_to(
                 (np.arange(C) * page).astype(np.int32), (B, H, C)).copy()).cuda()
         y.labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
+        y.rounds = torch.zeros(B, H, dtype=torch.int32, device="cuda")  # Lloyd rounds run per head
         y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
         y.sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
         y.sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
@@ -406,7 +409,7 @@ def main():
             kvc.kv_cluster_build(y.pool, y.keys, y.vals, C, cfg.iters, y.init,
                                  assign_in=y.assign_in,
                                  assign_out=None if y.assign_in is not None else y.labels,
-                                 ws=y.ws_build)
+                                 ws=y.ws_build, rounds_out=y.rounds)
 
     def decode_step(y, t):
         q_prev = y.q[t - 1] if t else None
@@ -685,8 +688,11 @@ def main():
     asg_ms = launch_ms(asg_fn, args.assign_reps)
     flops = 2.0 * B * H * N * C * d
     achieved = flops / (asg_ms * 1e-3) / 1e12
+    # assignment launches' worth of work per step: a head at a fixed point of
+    # Lloyd's iteration skips its later rounds (rounds_out of each build)
+    rounds_run = [float(y.rounds.float().mean().item()) for y in layers]
     share = {"k_gather_attend": T * L * att_ms / ms_step,
-             "k_assign_mfma": (0 if page is not None else cfg.iters) * L * asg_ms / ms_step}
+             "k_assign_mfma": (0 if page is not None else sum(rounds_run)) * asg_ms / ms_step}
 
     # What this machine reaches on plain work: a 1 GiB device copy (bytes read +
     # written) and a large bf16 GEMM through torch (hipBLASLt).
@@ -758,6 +764,7 @@ def main():
                    "prefill_keys_shared_across_layers": False,
                    "decode_steps_overridden": args.decode_steps is not None},
         "retrieval_steps": int(fl.sum()),
+        "lloyd_rounds_per_head": sum(rounds_run) / L,
         "retrieval": retrieval,
         "prefill_ms": pre_ms,
         "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),

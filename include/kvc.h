@@ -140,6 +140,14 @@ const char *kv_status_string(kv_status s);
  *               outside [0, n_clusters) is left out of every unit (its row is
  *               not packed) and *pool->status is set to KV_ERR_INVALID_ARG.
  * assign_out:   NULL, or [BH][n_keys]: the final labels.
+ * rounds_out:   NULL, or [BH] int32: the rounds whose assignment ran for
+ *               each head. A head whose assignment changes no label has
+ *               reached a fixed point of the iteration (the update then
+ *               reproduces its centroids bit for bit, and so on), so for
+ *               KV_BF16 keys its later rounds are skipped: the labels,
+ *               centroids and pool are those of exactly `iters` rounds. It
+ *               is iters where no such round came before the last (always
+ *               for KV_F32), 0 with assign_in.
  * iters >= 1 unless assign_in is given. n_clusters <= n_keys,
  * n_keys <= pool->row_cap, n_clusters <= pool->unit_cap.
  */
@@ -148,8 +156,8 @@ size_t kv_cluster_build_workspace(int32_t batch, int32_t n_kv_heads, int32_t n_k
 kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *values,
                            int32_t n_keys, int32_t n_clusters, int32_t iters,
                            const int32_t *init_idx, const int32_t *assign_in,
-                           int32_t *assign_out, void *ws, size_t ws_bytes,
-                           hipStream_t stream);
+                           int32_t *assign_out, int32_t *rounds_out, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* One Lloyd assignment step (the same kernel kv_cluster_build runs).
  * keys [n_heads][n_keys][head_dim] (dtype); centroids [n_heads][n_clusters]

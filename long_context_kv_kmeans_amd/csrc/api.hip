@@ -29,7 +29,8 @@ kv_status check_pool(const kv_pool *p) {
 }
 
 size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_cent,
-                         size_t *off_labels, size_t *off_assign, size_t *off_update) {
+                         size_t *off_labels, size_t *off_assign, size_t *off_update,
+                         size_t *off_skip = nullptr) {
   size_t o = 0;
   *off_cent = o;
   o += align_up((size_t)bh * c * d * sizeof(float), 256);
@@ -39,6 +40,8 @@ size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_c
   o += assign_ws_bytes(bh, c, d, dt);
   *off_update = o;
   o += update_ws_bytes(bh, n, c);
+  if (off_skip) *off_skip = o;  // fixed-point flags: conv[bh], chg[bh]
+  o += align_up((size_t)2 * bh * sizeof(int32_t), 256);
   return o;
 }
 
@@ -185,7 +188,7 @@ size_t kv_cluster_build_workspace(int32_t batch, int32_t n_kv_heads, int32_t n_k
 kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *values,
                            int32_t n_keys, int32_t n_clusters, int32_t iters,
                            const int32_t *init_idx, const int32_t *assign_in, int32_t *assign_out,
-                           void *ws, size_t ws_bytes, hipStream_t stream) {
+                           int32_t *rounds_out, void *ws, size_t ws_bytes, hipStream_t stream) {
   kv_status st = check_pool(pool);
   if (st != KV_OK) return st;
   if (!keys || !values || !init_idx) return KV_ERR_INVALID_ARG;
@@ -195,18 +198,27 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
   if (n_keys > pool->row_cap || n_clusters > pool->unit_cap) return KV_ERR_CAPACITY;
   const int bh = pool->batch * pool->n_kv_heads, d = pool->head_dim;
   const kv_dtype dt = (kv_dtype)pool->dtype;
-  size_t o_cent, o_lab, o_asg, o_upd;
+  size_t o_cent, o_lab, o_asg, o_upd, o_skip;
   const size_t need = cluster_ws_layout(bh, n_keys, d, n_clusters, dt, &o_cent, &o_lab, &o_asg,
-                                        &o_upd);
+                                        &o_upd, &o_skip);
   if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
   char *w = static_cast<char *>(ws);
   float *cent = reinterpret_cast<float *>(w + o_cent);
   int32_t *labels = assign_out ? assign_out : reinterpret_cast<int32_t *>(w + o_lab);
   void *asg_ws = w + o_asg;
   void *upd_ws = w + o_upd;
+  // Heads that reach a fixed point of Lloyd's iteration (an assignment that
+  // changes no label) skip the rest of their rounds: the later rounds would
+  // give the same labels and centroids bit for bit (bf16 keys; the flags are
+  // zeroed with the initial centroids).
+  LloydSkip skip;
+  if (dt == KV_BF16 && !assign_in) {
+    skip.conv = reinterpret_cast<int32_t *>(w + o_skip);
+    skip.chg = skip.conv + bh;
+  }
 
   st = launch_init_centroids(keys, init_idx, cent, bh, n_keys, n_clusters, d, dt, pool->status,
-                             stream);
+                             stream, skip.conv, skip.conv ? 2 * bh : 0);
   if (st != KV_OK) return st;
   const int32_t *perm = nullptr, *start = nullptr, *tot = nullptr;
   if (assign_in) {
@@ -226,17 +238,28 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
       if (st != KV_OK) return st;
     }
     for (int it = 0; it < iters; ++it) {
-      st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream, fused);
+      // from the second round on, compare with the previous round's labels
+      LloydSkip round_skip = it > 0 ? skip : LloydSkip{};
+      round_skip.round = it + 1;
+      st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream, fused,
+                         round_skip);
       if (st != KV_OK) return st;
       void *next_frags = (fused && it + 1 < iters) ? asg_ws : nullptr;
       if (it + 1 < iters && update_local_ok(bh, n_keys, n_clusters))  // the pack reads the last only
         st = launch_update_local(keys, labels, cent, cent, bh, n_keys, d, n_clusters, dt, upd_ws,
-                                 stream, next_frags);
-      else
+                                 stream, next_frags, round_skip);
+      else if (it + 1 < iters)
+        st = launch_update(keys, labels, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt,
+                           upd_ws, stream, &perm, &start, &tot, next_frags, nullptr, round_skip);
+      else  // the last round runs whole: the pack reads its order, starts and counts
         st = launch_update(keys, labels, cent, cent, nullptr, bh, n_keys, d, n_clusters, dt,
                            upd_ws, stream, &perm, &start, &tot, next_frags);
       if (st != KV_OK) return st;
     }
+  }
+  if (rounds_out) {
+    st = launch_rounds_out(skip.conv, rounds_out, bh, assign_in ? 0 : iters, stream);
+    if (st != KV_OK) return st;
   }
   return launch_pack(pool, keys, values, cent, perm, start, tot, n_keys, n_clusters, stream);
 }

@@ -28,9 +28,10 @@ constexpr int kAssignWaves = 8;                          // waves per workgroup
 template <typename T>
 __global__ void k_init_centroids(const T *__restrict__ keys, const int32_t *__restrict__ init_idx,
                                  float *__restrict__ cent, int n, int c, int d, long total,
-                                 int32_t *status) {
+                                 int32_t *status, int32_t *__restrict__ zero, int nzero) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
        i += (long)gridDim.x * blockDim.x) {
+    if (i < nzero) zero[i] = 0;  // (total >= nzero: every entry is reached)
     const long bh = i / ((long)c * d);
     const int k = (int)((i / d) % c), e = (int)(i % d);
     int src = init_idx[bh * c + k];
@@ -45,15 +46,17 @@ __global__ void k_init_centroids(const T *__restrict__ keys, const int32_t *__re
 }
 
 kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
-                                int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s) {
+                                int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s,
+                                int32_t *zero, int nzero) {
   const long total = (long)bh * c * d;
+  if (nzero > total) return KV_ERR_INVALID_ARG;
   const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   if (dt == KV_BF16)
     k_init_centroids<uint16_t><<<blocks, 256, 0, s>>>((const uint16_t *)keys, init_idx, cent, n,
-                                                      c, d, total, status);
+                                                      c, d, total, status, zero, nzero);
   else
     k_init_centroids<float><<<blocks, 256, 0, s>>>((const float *)keys, init_idx, cent, n, c, d,
-                                                   total, status);
+                                                   total, status, zero, nzero);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -141,7 +144,7 @@ template <int D, int NCB, int MINW>
 __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
     k_assign_mfma(const uint16_t *__restrict__ keys, const uint16_t *__restrict__ frags,
                   int32_t *__restrict__ labels, int n, int c, int ntile, int blocks_per_head,
-                  int total_blocks) {
+                  int total_blocks, const int32_t *__restrict__ conv, int32_t *__restrict__ chg) {
   using TL = AssignTile<D>;
   constexpr int KS = TL::KS;
   constexpr int TILE_U4 = TL::U4;
@@ -152,6 +155,7 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
 
   const int bid = xcd_remap(blockIdx.x, total_blocks);
   const int bh = bid / blocks_per_head;
+  if (conv != nullptr && conv[bh] != 0) return;  // the head's labels are final
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int KPW = 32 * NCB;  // keys per wave
   const int key0 = (bid % blocks_per_head) * (kAssignWaves * KPW) + wave * KPW;
@@ -295,6 +299,7 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
   }
   argmin_all(true);
 
+  bool diff = false;  // a label of this wave differs from the previous round's
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const uint32_t r = bestp[cb] & 15u;
@@ -304,8 +309,13 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
     const int oi = __shfl_xor(idx, 32);
     if (ok < key_t || (ok == key_t && oi < idx)) idx = oi;
     const int key = key0 + cb * 32 + (lane & 31);
-    if (half == 0 && key < n) labels[(size_t)bh * n + key] = idx;
+    if (half == 0 && key < n) {
+      int32_t *lp = labels + (size_t)bh * n + key;
+      if (chg != nullptr) diff |= *lp != idx;
+      *lp = idx;
+    }
   }
+  if (chg != nullptr && __ballot(diff) != 0ull && lane == 0) chg[bh] = 1;
 }
 
 // ---------------------------------------------------------------- fp32 assign
@@ -386,7 +396,8 @@ kv_status launch_assign_prepare(const float *cent, int bh, int d, int c, kv_dtyp
 }
 
 kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, int n, int d, int c,
-                                 kv_dtype dt, int32_t *labels, const void *ws, hipStream_t s) {
+                                 kv_dtype dt, int32_t *labels, const void *ws, hipStream_t s,
+                                 LloydSkip skip) {
   if (dt == KV_BF16) {
     const int ntile = (c + 31) / 32;
     const uint16_t *frags = static_cast<const uint16_t *>(ws);
@@ -396,10 +407,10 @@ kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, in
     const int total = bph * bh;
     if (d == 128)
       k_assign_mfma<128, NCB, kAssignMinWaves><<<total, 64 * kAssignWaves, 0, s>>>(
-          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
+          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg);
     else
       k_assign_mfma<64, NCB, kAssignMinWaves><<<total, 64 * kAssignWaves, 0, s>>>(
-          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total);
+          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg);
   } else {
     const float *hn = static_cast<const float *>(ws);
     const dim3 grid((n + 255) / 256, bh);
@@ -412,12 +423,13 @@ kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, in
 }
 
 kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
-                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s, bool frags_ready) {
+                        kv_dtype dt, int32_t *labels, void *ws, hipStream_t s, bool frags_ready,
+                        LloydSkip skip) {
   if (!(frags_ready && dt == KV_BF16)) {
     const kv_status st = launch_assign_prepare(cent, bh, d, c, dt, ws, s);
     if (st != KV_OK) return st;
   }
-  return launch_assign_prepared(keys, cent, bh, n, d, c, dt, labels, ws, s);
+  return launch_assign_prepared(keys, cent, bh, n, d, c, dt, labels, ws, s, skip);
 }
 
 // ---------------------------------------------------------------- update
@@ -438,15 +450,43 @@ kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int 
 //  k_scatter   -- perm[start[a] + chunk_prefix[a] + rank] = key.
 // A label outside [0, c) takes no part: its key gets no rank, no histogram
 // count and no place in the permutation (reported through *status when given).
+// First kernel of an update round under the fixed-point skip: true when the
+// workgroup has nothing to do because head bh has reached its fixed point
+// (conv set earlier, or no label changed in this round's assignment, which
+// then records the round in conv).
+__device__ __forceinline__ bool update_head_done(const int32_t *chg, int32_t *conv, int bh,
+                                                 int round) {
+  if (chg == nullptr) return false;
+  if (conv[bh] != 0) return true;
+  if (chg[bh] != 0) return false;
+  if (blockIdx.x == 0 && threadIdx.x == 0) conv[bh] = round;
+  return true;
+}
+
+__global__ void k_rounds_out(const int32_t *__restrict__ conv, int32_t *__restrict__ rounds,
+                             int bh, int iters) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < bh) rounds[i] = (conv != nullptr && conv[i] != 0) ? conv[i] : iters;
+}
+
+kv_status launch_rounds_out(const int32_t *conv, int32_t *rounds, int bh, int iters,
+                            hipStream_t s) {
+  k_rounds_out<<<(bh + 255) / 256, 256, 0, s>>>(conv, rounds, bh, iters);
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
 template <int NW, int CHUNK>
 __global__ void __launch_bounds__(64 * NW) k_rank_hist(const int32_t *__restrict__ labels,
                                                        int32_t *__restrict__ rank,
                                                        int32_t *__restrict__ hist, int n, int c,
-                                                       int nbits, int nchunk, int32_t *status) {
+                                                       int nbits, int nchunk, int32_t *status,
+                                                       const int32_t *chg, int32_t *conv,
+                                                       int round) {
   constexpr int KPW = CHUNK / NW;  // keys per wave: wave w takes the w-th part of the chunk
   constexpr int SUB = KPW / 64;
   extern __shared__ int32_t cnt[];      // [NW][c]: label counts of each wave's part
   const int bh = blockIdx.y, ch = blockIdx.x;
+  if (update_head_done(chg, conv, bh, round)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t *lab = labels + (size_t)bh * n;
   const int base = ch * CHUNK + wave * KPW;
@@ -520,9 +560,11 @@ __device__ __forceinline__ int label_block_base(const int32_t *__restrict__ agg,
 
 __global__ void __launch_bounds__(kLabelBlock)
     k_colscan(int32_t *__restrict__ hist, int32_t *__restrict__ tot, int32_t *__restrict__ ipre,
-              int32_t *__restrict__ agg, int32_t *__restrict__ counts, int c, int nchunk) {
+              int32_t *__restrict__ agg, int32_t *__restrict__ counts, int c, int nchunk,
+              const int32_t *conv) {
   __shared__ int wsum[kLabelBlock / 64];
   const int bh = blockIdx.y, k = blockIdx.x * kLabelBlock + threadIdx.x;
+  if (conv != nullptr && conv[bh] != 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t run = 0;
   if (k < c) {
@@ -563,9 +605,10 @@ __global__ void __launch_bounds__(256)
     k_scatter(const int32_t *__restrict__ labels, const int32_t *__restrict__ rank,
               const int32_t *__restrict__ hist, const int32_t *__restrict__ ipre,
               const int32_t *__restrict__ agg, int32_t *__restrict__ perm, int n, int c,
-              int nchunk, int chunk_shift) {
+              int nchunk, int chunk_shift, const int32_t *conv) {
   __shared__ int s_base[64];  // start of each block of 256 labels
   const int bh = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (conv != nullptr && conv[bh] != 0) return;
   const int nblk = (c + kLabelBlock - 1) / kLabelBlock;
   // the key's label and rank in one round trip (clamped index; n >= 1)
   const int ic = min(i, n - 1);
@@ -649,12 +692,15 @@ __global__ void __launch_bounds__(256) k_segsum(int n, int c, int ntile,
                                                 const int32_t *__restrict__ perm,
                                                 const T *__restrict__ keys,
                                                 const float *cent_in, float *cent_out,
-                                                uint16_t *__restrict__ frags) {
+                                                uint16_t *__restrict__ frags,
+                                                const int32_t *conv, int32_t *chg) {
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane
   constexpr int LPR = D / EPL;               // lanes per row
   constexpr int RPI = 64 / LPR;              // member rows per wave instruction
   constexpr int UNR = 4;
   const int bh = blockIdx.y;
+  if (chg != nullptr && blockIdx.x == 0 && threadIdx.x == 0) chg[bh] = 0;  // for the next round
+  if (conv != nullptr && conv[bh] != 0) return;
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int part = lane % LPR, slot = lane / LPR;
@@ -717,11 +763,13 @@ template <int NW>
 __global__ void __launch_bounds__(64 * NW) k_rank_local(const int32_t *__restrict__ labels,
                                                         int32_t *__restrict__ local,
                                                         int32_t *__restrict__ ltab, int n, int c,
-                                                        int nbits, int nchunk) {
+                                                        int nbits, int nchunk, const int32_t *chg,
+                                                        int32_t *conv, int round) {
   constexpr int KPW = kLocalChunk / NW;
   constexpr int SUB = KPW / 64;
   extern __shared__ int32_t cnt[];  // [NW][c]: label counts of each wave's part
   const int bh = blockIdx.y, ch = blockIdx.x;
+  if (update_head_done(chg, conv, bh, round)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t *lab = labels + (size_t)bh * n;
   const int base = ch * kLocalChunk + wave * KPW;
@@ -808,12 +856,15 @@ __global__ void __launch_bounds__(256) k_segsum_local(int n, int c, int ntile, i
                                                       const int32_t *__restrict__ local,
                                                       const T *__restrict__ keys,
                                                       const float *cent_in, float *cent_out,
-                                                      uint16_t *__restrict__ frags) {
+                                                      uint16_t *__restrict__ frags,
+                                                      const int32_t *conv, int32_t *chg) {
   constexpr int EPL = 16 / Elem<T>::kBytes;
   constexpr int LPR = D / EPL;
   constexpr int RPI = 64 / LPR;
   constexpr int UNR = 4;
   static_assert(kSegWindow % (RPI * UNR) == 0, "window holds whole steps");
+  if (chg != nullptr && blockIdx.x == 0 && threadIdx.x == 0) chg[blockIdx.y] = 0;  // next round
+  if (conv != nullptr && conv[blockIdx.y] != 0) return;
   static_assert(kLocalMaxChunks <= 64, "one chunk per lane");
   __shared__ int s_at[4][kSegWindow];   // positions in `local` of the window's members
   __shared__ int s_mem[4][kSegWindow];  // the window's members
@@ -899,7 +950,7 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
                         float *cent_out, int32_t *counts, int bh, int n, int d, int c,
                         kv_dtype dt, void *ws, hipStream_t s, const int32_t **perm_out,
                         const int32_t **start_out, const int32_t **tot_out, void *frags_out,
-                        int32_t *status) {
+                        int32_t *status, LloydSkip skip) {
   const int chunk = rank_chunk(bh, n, c), nchunk = (n + chunk - 1) / chunk;
   char *w = static_cast<char *>(ws);
   int32_t *rank = reinterpret_cast<int32_t *>(w);
@@ -921,33 +972,37 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   const dim3 rg(nchunk, bh);
   if (chunk == 1024 && c <= 4096)
     k_rank_hist<4, 1024><<<rg, 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                            ceil_log2(c), nchunk, status);
+                                                            ceil_log2(c), nchunk, status, skip.chg,
+                                                            skip.conv, skip.round);
   else if (c <= 4096)
     k_rank_hist<4, 4096><<<rg, 256, (size_t)4 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                            ceil_log2(c), nchunk, status);
+                                                            ceil_log2(c), nchunk, status, skip.chg,
+                                                            skip.conv, skip.round);
   else
     k_rank_hist<2, 1024><<<rg, 128, (size_t)2 * c * 4, s>>>(labels, rank, hist, n, c,
-                                                            ceil_log2(c), nchunk, status);
-  k_colscan<<<dim3(nblk, bh), kLabelBlock, 0, s>>>(hist, tot, start, agg, counts, c, nchunk);
+                                                            ceil_log2(c), nchunk, status, skip.chg,
+                                                            skip.conv, skip.round);
+  k_colscan<<<dim3(nblk, bh), kLabelBlock, 0, s>>>(hist, tot, start, agg, counts, c, nchunk,
+                                                    skip.conv);
   k_scatter<<<dim3((n + 255) / 256, bh), 256, 0, s>>>(labels, rank, hist, start, agg, perm, n, c,
-                                                      nchunk, ceil_log2(chunk));
+                                                      nchunk, ceil_log2(chunk), skip.conv);
   const dim3 g((c + 3) / 4, bh);
   uint16_t *fr = static_cast<uint16_t *>(frags_out);
   const int ntile = (c + 31) / 32;
   if (dt == KV_BF16) {
     if (d == 128)
       k_segsum<uint16_t, 128><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const uint16_t *)keys,
-                                                cent_in, cent_out, fr);
+                                                cent_in, cent_out, fr, skip.conv, skip.chg);
     else
       k_segsum<uint16_t, 64><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const uint16_t *)keys,
-                                               cent_in, cent_out, fr);
+                                               cent_in, cent_out, fr, skip.conv, skip.chg);
   } else {
     if (d == 128)
       k_segsum<float, 128><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const float *)keys,
-                                             cent_in, cent_out, nullptr);
+                                             cent_in, cent_out, nullptr, skip.conv, skip.chg);
     else
       k_segsum<float, 64><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const float *)keys,
-                                            cent_in, cent_out, nullptr);
+                                            cent_in, cent_out, nullptr, skip.conv, skip.chg);
   }
   if (perm_out) *perm_out = perm;
   if (start_out) *start_out = start;
@@ -962,7 +1017,7 @@ bool update_local_ok(int bh, int n, int c) {
 
 kv_status launch_update_local(const void *keys, const int32_t *labels, const float *cent_in,
                               float *cent_out, int bh, int n, int d, int c, kv_dtype dt,
-                              void *ws, hipStream_t s, void *frags_out) {
+                              void *ws, hipStream_t s, void *frags_out, LloydSkip skip) {
   if (!update_local_ok(bh, n, c)) return KV_ERR_UNSUPPORTED;
   const int nchunk = (n + kLocalChunk - 1) / kLocalChunk;
   // the update workspace's rank and histogram regions hold the local order
@@ -973,24 +1028,24 @@ kv_status launch_update_local(const void *keys, const int32_t *labels, const flo
   int32_t *ltab = reinterpret_cast<int32_t *>(w);
   const dim3 rg(nchunk, bh);
   k_rank_local<4><<<rg, 256, (size_t)4 * c * 4, s>>>(labels, local, ltab, n, c, ceil_log2(c),
-                                                      nchunk);
+                                                      nchunk, skip.chg, skip.conv, skip.round);
   const dim3 g((c + 3) / 4, bh);
   uint16_t *fr = static_cast<uint16_t *>(frags_out);
   const int ntile = (c + 31) / 32;
   if (dt == KV_BF16) {
     if (d == 128)
       k_segsum_local<uint16_t, 128><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                      (const uint16_t *)keys, cent_in, cent_out, fr);
+                                                      (const uint16_t *)keys, cent_in, cent_out, fr, skip.conv, skip.chg);
     else
       k_segsum_local<uint16_t, 64><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                     (const uint16_t *)keys, cent_in, cent_out, fr);
+                                                     (const uint16_t *)keys, cent_in, cent_out, fr, skip.conv, skip.chg);
   } else {
     if (d == 128)
       k_segsum_local<float, 128><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                    (const float *)keys, cent_in, cent_out, nullptr);
+                                                    (const float *)keys, cent_in, cent_out, nullptr, skip.conv, skip.chg);
     else
       k_segsum_local<float, 64><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                   (const float *)keys, cent_in, cent_out, nullptr);
+                                                   (const float *)keys, cent_in, cent_out, nullptr, skip.conv, skip.chg);
   }
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }

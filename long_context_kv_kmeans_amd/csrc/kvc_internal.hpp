@@ -296,31 +296,54 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 namespace kvc {
 
 // K-means
+// A head whose assignment in some round gives back the previous round's
+// labels has reached a fixed point of Lloyd's iteration: the update then
+// reproduces the centroids bit for bit, so every later round gives the same
+// labels and centroids. kv_cluster_build tracks this per head and lets the
+// kernels of the later rounds return at once for such heads:
+//   conv[bh]: once the head has reached its fixed point, the number of
+//             rounds whose assignment ran (the last of them changed nothing);
+//   chg[bh]:  1 when this round's assignment changed a label of the head.
+// Both are zeroed with the initial centroids. A null pointer disables it.
+struct LloydSkip {
+  int32_t *conv = nullptr;
+  int32_t *chg = nullptr;
+  int round = 0;  // 1-based number of the round the launch belongs to
+};
+// rounds[i] = conv[i] if set, else iters (conv null: iters for every head).
+kv_status launch_rounds_out(const int32_t *conv, int32_t *rounds, int bh, int iters,
+                            hipStream_t s);
 kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
-                                int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s);
+                                int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s,
+                                int32_t *zero = nullptr, int nzero = 0);
 size_t assign_ws_bytes(int bh, int c, int d, kv_dtype dt);
 kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, hipStream_t s);
 kv_status launch_assign_prepare(const float *cent, int bh, int d, int c, kv_dtype dt, void *ws,
                                 hipStream_t s);
+// skip (bf16 only): heads with conv set return at once; the others compare
+// their new labels with the ones in `labels` and set chg when one differs.
 kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, int n, int d, int c,
-                                 kv_dtype dt, int32_t *labels, const void *ws, hipStream_t s);
+                                 kv_dtype dt, int32_t *labels, const void *ws, hipStream_t s,
+                                 LloydSkip skip = {});
 kv_status launch_assign(const void *keys, const float *cent, int bh, int n, int d, int c,
                         kv_dtype dt, int32_t *labels, void *ws, hipStream_t s,
-                        bool frags_ready = false);
+                        bool frags_ready = false, LloydSkip skip = {});
 size_t update_ws_bytes(int bh, int n, int c);
 kv_status launch_update(const void *keys, const int32_t *labels, const float *cent_in,
                         float *cent_out, int32_t *counts, int bh, int n, int d, int c,
                         kv_dtype dt, void *ws, hipStream_t s,
                         const int32_t **perm_out, const int32_t **start_out,
                         const int32_t **tot_out, void *frags_out = nullptr,
-                        int32_t *status = nullptr);
+                        int32_t *status = nullptr, LloydSkip skip = {});
 // The update of a round whose permutation, starts and counts nobody reads
 // (centroids and next tiles only; the same bits as launch_update), in two
 // launches, where that is the faster way (update_local_ok).
 bool update_local_ok(int bh, int n, int c);
+// skip: the first kernel marks conv for heads whose chg is 0 (and every
+// kernel returns at once for heads with conv set); the last clears chg.
 kv_status launch_update_local(const void *keys, const int32_t *labels, const float *cent_in,
                               float *cent_out, int bh, int n, int d, int c, kv_dtype dt,
-                              void *ws, hipStream_t s, void *frags_out);
+                              void *ws, hipStream_t s, void *frags_out, LloydSkip skip = {});
 kv_status launch_pack(const kv_pool *pool, const void *keys, const void *values,
                       const float *cent, const int32_t *perm, const int32_t *start,
                       const int32_t *tot, int n, int c, hipStream_t s);

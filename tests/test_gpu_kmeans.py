@@ -145,7 +145,7 @@ def test_update_empty_cluster_keeps_centroid(tiny):
     assert cnt[0].tolist() == case["expect_counts"]
 
 
-def _cluster_build(cfg, heads, iters, seqs=(0,)):
+def _cluster_build(cfg, heads, iters, seqs=(0,), rounds=None):
     inp = wl.layer_inputs(cfg, 0, heads=heads, seqs=seqs)
     B, H, N, d = inp["keys"].shape
     pool = make_pool(B, H, d, cfg.dtype, N, cfg.n_clusters)
@@ -153,7 +153,8 @@ def _cluster_build(cfg, heads, iters, seqs=(0,)):
     vals = to_dev(inp["values"], cfg.dtype)
     init = torch.from_numpy(inp["init_idx"]).cuda()
     lab = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
-    kvc.kv_cluster_build(pool, keys, vals, cfg.n_clusters, iters, init, assign_out=lab)
+    kvc.kv_cluster_build(pool, keys, vals, cfg.n_clusters, iters, init, assign_out=lab,
+                         rounds_out=rounds)
     torch.cuda.synchronize()
     return inp, pool, lab.cpu().numpy()
 
@@ -196,14 +197,25 @@ def test_cluster_build_invariants_and_pack(cfg_idx, over, heads):
     assert pool.n_units.cpu().tolist() == [C] and pool.n_cand.cpu().tolist() == [C]
 
 
+@pytest.mark.parametrize("iters", [4, 14])
 @pytest.mark.parametrize("cfg_idx,over,heads", [CASES[0], CASES[2]] + BIG_C)
-def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads):
+def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, iters):
     """kv_cluster_build's rounds (the two-launch update of every round but the
-    last) give the same labels and centroids, bit for bit, as running
-    kv_kmeans_assign and kv_kmeans_update round by round from the same start."""
+    last; heads that reach a fixed point skip their later rounds) give the
+    same labels and centroids, bit for bit, as running kv_kmeans_assign and
+    kv_kmeans_update round by round from the same start. 14 rounds take these
+    heads past their fixed points."""
     cfg = wl.get_config(cfg_idx, **over)
-    iters = 4
-    inp, pool, lab = _cluster_build(cfg, heads, iters)
+    rounds = torch.full((1, len(heads)), -1, dtype=torch.int32, device="cuda")
+    inp, pool, lab = _cluster_build(cfg, heads, iters, rounds=rounds)
+    rounds = rounds.cpu().numpy()
+    # assignments run per head: iters, or (bf16) fewer for a head whose
+    # assignment in some round 2.. changed no label
+    if cfg.dtype == "fp32":
+        assert (rounds == iters).all()
+    else:
+        assert ((rounds >= 2) & (rounds <= iters)).all(), rounds
+    print(f"rounds run per head: {rounds.tolist()} of {iters}")
     B, H, N, d = inp["keys"].shape
     keys_d = to_dev(inp["keys"], cfg.dtype).reshape(B * H, N, d)
     idx = torch.from_numpy(inp["init_idx"]).cuda().reshape(B * H, -1).long()
@@ -418,11 +430,14 @@ def test_out_of_range_labels_and_init_indices_are_ignored_and_reported():
     B, H = 1, BH
     pool = make_pool(B, H, d, cfg.dtype, N, C)
     vals_d = to_dev(inp["values"], cfg.dtype)
+    rounds = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     kvc.kv_cluster_build(pool, keys_d.reshape(B, H, N, d), vals_d, C, 1,
                          torch.from_numpy(init.reshape(B, H, C)).cuda(),
-                         assign_in=torch.from_numpy(lab_bad.astype(np.int32).reshape(B, H, N)).cuda())
+                         assign_in=torch.from_numpy(lab_bad.astype(np.int32).reshape(B, H, N)).cuda(),
+                         rounds_out=rounds)
     torch.cuda.synchronize()
     assert int(pool.status.item()) == kvc.KV_ERR_INVALID_ARG
+    assert (rounds.cpu().numpy() == 0).all()  # a given clustering runs no round
     sizes = pool.unit_size[0].cpu().numpy()
     starts = pool.unit_start[0].cpu().numpy()
     pk = to_np(pool.k[0])
