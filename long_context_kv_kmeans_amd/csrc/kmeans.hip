@@ -113,6 +113,40 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
   if (e0 == 0) write_centroid_norm(tile, TL::KS, m, real ? -0.5f * sq : kPadNorm);
 }
 
+// Work of the heads that have not reached a fixed point, spread over the whole
+// grid: with A such heads, blocks i < A * bph take work item w = xcd_remap(i,
+// A * bph) (so every XCD still gets a contiguous range), i.e. key block w % bph
+// of the (w / bph)-th head in index order whose conv flag is 0; the other
+// blocks have nothing to do. Without this a converged head's blocks would
+// leave its XCD idle while the others' XCDs still work through theirs.
+// Returns that head (wave-uniform, the same in every wave) or -1.
+__device__ __forceinline__ int active_head_block(const int32_t *__restrict__ conv, int nbh, int bph,
+                                                 int *bid) {
+  const int lane = threadIdx.x & 63;
+  int na = 0;
+  for (int b0 = 0; b0 < nbh; b0 += 64) {
+    const int i = b0 + lane;
+    na += __popcll(__ballot(i < nbh && conv[i] == 0));
+  }
+  const int work = na * bph;
+  if ((int)blockIdx.x >= work) return -1;
+  *bid = xcd_remap(blockIdx.x, work);
+  int r = *bid / bph;
+  for (int b0 = 0; b0 < nbh; b0 += 64) {
+    const int i = b0 + lane;
+    const bool act = i < nbh && conv[i] == 0;
+    const uint64_t m = __ballot(act);
+    const int cnt = __popcll(m);
+    if (r < cnt) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      return b0 + __builtin_ctzll(__ballot(act && below == r));
+    }
+    r -= cnt;
+  }
+  return -1;
+}
+
 // One workgroup = 8 waves x 64 keys. Keys are the B operand (column n = key),
 // resident in VGPRs for the whole centroid sweep. Centroid tiles stream into
 // two LDS stage buffers with direct global->LDS loads (each wave instruction
@@ -153,9 +187,12 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
   __shared__ uint4 lds0[STAGE_BLOCKS * 64];
   __shared__ uint4 lds1[STAGE_BLOCKS * 64];
 
-  const int bid = xcd_remap(blockIdx.x, total_blocks);
-  const int bh = bid / blocks_per_head;
-  if (conv != nullptr && conv[bh] != 0) return;  // the head's labels are final
+  int bid = xcd_remap(blockIdx.x, total_blocks);
+  int bh = bid / blocks_per_head;
+  if (conv != nullptr) {  // only heads still iterating get blocks
+    bh = active_head_block(conv, total_blocks / blocks_per_head, blocks_per_head, &bid);
+    if (bh < 0) return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int KPW = 32 * NCB;  // keys per wave
   const int key0 = (bid % blocks_per_head) * (kAssignWaves * KPW) + wave * KPW;
