@@ -30,7 +30,7 @@ kv_status check_pool(const kv_pool *p) {
 
 size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_cent,
                          size_t *off_labels, size_t *off_assign, size_t *off_update,
-                         size_t *off_skip = nullptr) {
+                         size_t *off_skip = nullptr, size_t *off_inc = nullptr) {
   size_t o = 0;
   *off_cent = o;
   o += align_up((size_t)bh * c * d * sizeof(float), 256);
@@ -42,6 +42,8 @@ size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_c
   o += update_ws_bytes(bh, n, c);
   if (off_skip) *off_skip = o;  // fixed-point flags: conv[bh], chg[bh]
   o += align_up((size_t)2 * bh * sizeof(int32_t), 256);
+  if (off_inc) *off_inc = o;  // incremental assignment (bf16)
+  if (dt == KV_BF16) o += assign_inc_ws_bytes(bh, n, c, d);
   return o;
 }
 
@@ -198,9 +200,9 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
   if (n_keys > pool->row_cap || n_clusters > pool->unit_cap) return KV_ERR_CAPACITY;
   const int bh = pool->batch * pool->n_kv_heads, d = pool->head_dim;
   const kv_dtype dt = (kv_dtype)pool->dtype;
-  size_t o_cent, o_lab, o_asg, o_upd, o_skip;
+  size_t o_cent, o_lab, o_asg, o_upd, o_skip, o_inc;
   const size_t need = cluster_ws_layout(bh, n_keys, d, n_clusters, dt, &o_cent, &o_lab, &o_asg,
-                                        &o_upd, &o_skip);
+                                        &o_upd, &o_skip, &o_inc);
   if (!ws || !aligned256(ws) || ws_bytes < need) return KV_ERR_WORKSPACE;
   char *w = static_cast<char *>(ws);
   float *cent = reinterpret_cast<float *>(w + o_cent);
@@ -212,9 +214,14 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
   // give the same labels and centroids bit for bit (bf16 keys; the flags are
   // zeroed with the initial centroids).
   LloydSkip skip;
+  AssignIncWs inc{};
   if (dt == KV_BF16 && !assign_in) {
     skip.conv = reinterpret_cast<int32_t *>(w + o_skip);
     skip.chg = skip.conv + bh;
+    // Centroids that did not move score every key exactly as before, so
+    // later rounds sweep only the moved ones (and every centroid for the keys
+    // whose own centroid moved): the labels of a whole sweep, bit for bit.
+    assign_inc_ws_carve(w + o_inc, bh, n_keys, n_clusters, d, &inc);
   }
 
   st = launch_init_centroids(keys, init_idx, cent, bh, n_keys, n_clusters, d, dt, pool->status,
@@ -241,8 +248,12 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
       // from the second round on, compare with the previous round's labels
       LloydSkip round_skip = it > 0 ? skip : LloydSkip{};
       round_skip.round = it + 1;
-      st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream, fused,
-                         round_skip);
+      if (skip.conv != nullptr)
+        st = launch_assign_round(keys, bh, n_keys, d, n_clusters, labels, asg_ws, inc, it + 1,
+                                 round_skip, stream);
+      else
+        st = launch_assign(keys, cent, bh, n_keys, d, n_clusters, dt, labels, asg_ws, stream,
+                           fused, round_skip);
       if (st != KV_OK) return st;
       void *next_frags = (fused && it + 1 < iters) ? asg_ws : nullptr;
       if (it + 1 < iters && update_local_ok(bh, n_keys, n_clusters))  // the pack reads the last only

@@ -113,20 +113,27 @@ __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ ce
   if (e0 == 0) write_centroid_norm(tile, TL::KS, m, real ? -0.5f * sq : kPadNorm);
 }
 
-// Work of the heads that have not reached a fixed point, spread over the whole
-// grid: with A such heads, blocks i < A * bph take work item w = xcd_remap(i,
-// A * bph) (so every XCD still gets a contiguous range), i.e. key block w % bph
-// of the (w / bph)-th head in index order whose conv flag is 0; the other
-// blocks have nothing to do. Without this a converged head's blocks would
-// leave its XCD idle while the others' XCDs still work through theirs.
-// Returns that head (wave-uniform, the same in every wave) or -1.
-__device__ __forceinline__ int active_head_block(const int32_t *__restrict__ conv, int nbh, int bph,
-                                                 int *bid) {
+// Heads whose blocks a launch serves, spread over the whole grid: with A such
+// heads, blocks i < A * bph take work item w = xcd_remap(i, A * bph) (so every
+// XCD still gets a contiguous range), i.e. key block w % bph of the
+// (w / bph)-th served head in index order; the other blocks have nothing to
+// do. Without this a converged head's blocks would leave its XCD idle while
+// the others' XCDs still work through theirs. A head is served when its conv
+// flag is 0 and, with a state table, its sweep mode is `want`. Returns that
+// head (wave-uniform, the same in every wave) or -1.
+__device__ __forceinline__ bool head_served(const int32_t *__restrict__ conv,
+                                            const int32_t *__restrict__ hstate, int want, int i) {
+  return conv[i] == 0 && (hstate == nullptr || hstate[4 * i + 1] == want);
+}
+
+__device__ __forceinline__ int active_head_block(const int32_t *__restrict__ conv,
+                                                 const int32_t *__restrict__ hstate, int want,
+                                                 int nbh, int bph, int *bid) {
   const int lane = threadIdx.x & 63;
   int na = 0;
   for (int b0 = 0; b0 < nbh; b0 += 64) {
     const int i = b0 + lane;
-    na += __popcll(__ballot(i < nbh && conv[i] == 0));
+    na += __popcll(__ballot(i < nbh && head_served(conv, hstate, want, i)));
   }
   const int work = na * bph;
   if ((int)blockIdx.x >= work) return -1;
@@ -134,7 +141,7 @@ __device__ __forceinline__ int active_head_block(const int32_t *__restrict__ con
   int r = *bid / bph;
   for (int b0 = 0; b0 < nbh; b0 += 64) {
     const int i = b0 + lane;
-    const bool act = i < nbh && conv[i] == 0;
+    const bool act = i < nbh && head_served(conv, hstate, want, i);
     const uint64_t m = __ballot(act);
     const int cnt = __popcll(m);
     if (r < cnt) {
@@ -145,6 +152,32 @@ __device__ __forceinline__ int active_head_block(const int32_t *__restrict__ con
     r -= cnt;
   }
   return -1;
+}
+
+// Key groups of the full sweep over gathered keys (kAssignGather): head i
+// holds ceil(gathered_i / keys per workgroup) of them when it is served in
+// incremental mode. Sets *total to their sum over the heads; for group g <
+// total also the head (return value) and the group's index within the head.
+__device__ __forceinline__ int gathered_groups(const int32_t *__restrict__ conv,
+                                               const int32_t *__restrict__ hstate, int nbh,
+                                               int kpb, int g, int *total, int *gin) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0, head = -1;
+  for (int b0 = 0; b0 < nbh; b0 += 64) {
+    const int i = b0 + lane;
+    const int gi = (i < nbh && head_served(conv, hstate, 0, i)) ? (hstate[4 * i + 2] + kpb - 1) / kpb
+                                                                : 0;
+    const int incl = wave_incl_scan_i32(gi);
+    const int tot = lane_value(incl, 63);
+    if (head < 0 && g >= sum && g < sum + tot) {
+      const int l = __builtin_ctzll(__ballot(sum + incl > g));
+      head = b0 + l;
+      *gin = g - (sum + lane_value(incl, l) - lane_value(gi, l));
+    }
+    sum += tot;
+  }
+  *total = sum;
+  return head;
 }
 
 // One workgroup = 8 waves x 64 keys. Keys are the B operand (column n = key),
@@ -174,11 +207,34 @@ __device__ __forceinline__ int active_head_block(const int32_t *__restrict__ con
 // so earlier (lower-index) tiles win ties. Comparing 28 of 32 bits moves a
 // decision only where two scores agree to about 2^-19 relative, the size of
 // the fp32 accumulation error of the 128-term dot product.
-template <int D, int NCB, int MINW>
+// The label is therefore the minimum of (upper 28 score bits, index) in
+// lexicographic order over the centroids swept, whatever their order: a
+// sweep may be split over centroid ranges or restricted to a subset and
+// still give the same label as the whole sweep. Each (key, centroid) score
+// depends only on the key, K_w of the key's 64-key wave and the centroid's
+// tile row, which the incremental modes below rely on.
+//
+// MODE (the incremental assignment of kv_cluster_build, exact: the labels of
+// a whole sweep):
+//   kAssignFull    -- every centroid for the keys of the served heads; with
+//                     `inc` also records each key's winning score bits, each
+//                     wave's K_w and the clusters its label changes touch;
+//   kAssignMoved   -- only the moved centroids (compact tiles): a key whose
+//                     own cluster did not move keeps the lexicographic
+//                     minimum of its recorded score and the moved ones; a key
+//                     whose own cluster moved is queued for kAssignGather;
+//   kAssignGather  -- every centroid for the queued keys, the centroid range
+//                     split over workgroups (a loop over work items); the
+//                     splits meet in a 64-bit atomic minimum of
+//                     (score bits << 32 | label) per queued key.
+constexpr int kAssignFull = 0, kAssignMoved = 1, kAssignGather = 2;
+
+template <int D, int NCB, int MINW, int MODE>
 __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
     k_assign_mfma(const uint16_t *__restrict__ keys, const uint16_t *__restrict__ frags,
                   int32_t *__restrict__ labels, int n, int c, int ntile, int blocks_per_head,
-                  int total_blocks, const int32_t *__restrict__ conv, int32_t *__restrict__ chg) {
+                  int total_blocks, const int32_t *__restrict__ conv, int32_t *__restrict__ chg,
+                  AssignInc inc) {
   using TL = AssignTile<D>;
   constexpr int KS = TL::KS;
   constexpr int TILE_U4 = TL::U4;
@@ -187,172 +243,406 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
   __shared__ uint4 lds0[STAGE_BLOCKS * 64];
   __shared__ uint4 lds1[STAGE_BLOCKS * 64];
 
-  int bid = xcd_remap(blockIdx.x, total_blocks);
-  int bh = bid / blocks_per_head;
-  if (conv != nullptr) {  // only heads still iterating get blocks
-    bh = active_head_block(conv, total_blocks / blocks_per_head, blocks_per_head, &bid);
-    if (bh < 0) return;
-  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int KPW = 32 * NCB;  // keys per wave
-  const int key0 = (bid % blocks_per_head) * (kAssignWaves * KPW) + wave * KPW;
+  constexpr int KPB = kAssignWaves * KPW;
   const int half = lane >> 5;
+  const int nbh = total_blocks / blocks_per_head;
+  const int nw = (n + KPW - 1) / KPW;  // 64-key waves per head
+  const int nstage_all = (ntile + kTilesPerStage - 1) / kTilesPerStage;
 
-  // Key fragments (B operand): lane holds key n = lane % 32, k = 16 s + 8 half + j.
-  bf16x8_t bfrag[NCB][KS];
-  float kmax = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int key = key0 + cb * 32 + (lane & 31);
-    const uint16_t *krow = keys + ((size_t)bh * n + (key < n ? key : 0)) * D;
-    float sq = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (key < n) v = *reinterpret_cast<const uint4 *>(krow + 16 * s + 8 * half);
-      bfrag[cb][s] = __builtin_bit_cast(bf16x8_t, v);
-      float f[8];
-      unpack16<uint16_t>(v, f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sq = fmaf(f[j], f[j], sq);
-    }
-    kmax = fmaxf(kmax, sum_xor32(sq));
+  // kAssignGather: work items (key group, centroid split), S splits per group
+  int item = blockIdx.x, nitems = 1, nsplit = 1;
+  if constexpr (MODE == kAssignGather) {
+    int total = 0, gin = 0;
+    (void)gathered_groups(conv, inc.hstate, nbh, KPB, -1, &total, &gin);
+    nsplit = total >= (int)gridDim.x ? 1 : min(nstage_all, (int)gridDim.x / max(total, 1));
+    nitems = total * nsplit;
+    if (item >= nitems) return;
   }
-  // The empty asm makes the product opaque, so the compiler cannot fuse it
-  // into the per-tile subtractions below in some tiles and not in others:
-  // every tile's accumulator start must be the same function of its norms
-  // bit for bit (identical centroids must score identically in every tile
-  // for the lowest-index tie rule).
-  float koff = 0.5f * wave_max(kmax) * 1.001f;
-  asm volatile("" : "+v"(koff));
-
-  uint32_t bestp[NCB];
-  int btile[NCB];
+  for (;;) {
+    int bh = 0, key0 = 0, t0 = 0, ntl = ntile, cl = c, gcount = 0, gpos0 = 0;
+    const uint16_t *src = frags;
+    bool work = true;
+    if constexpr (MODE == kAssignGather) {
+      int total = 0, gin = 0;
+      bh = gathered_groups(conv, inc.hstate, nbh, KPB, item / nsplit, &total, &gin);
+      const int sps = (nstage_all + nsplit - 1) / nsplit;  // stages per split
+      const int st0 = (item % nsplit) * sps, st1 = min(st0 + sps, nstage_all);
+      work = bh >= 0 && st0 < st1;
+      t0 = st0 * kTilesPerStage;
+      ntl = min(st1 * kTilesPerStage, ntile) - t0;
+      cl = c - t0 * 32;
+      gcount = bh >= 0 ? inc.hstate[4 * bh + 2] : 0;
+      gpos0 = gin * KPB + wave * KPW;
+    } else {
+      int bid = xcd_remap(blockIdx.x, total_blocks);
+      bh = bid / blocks_per_head;
+      if (conv != nullptr) {  // only heads still iterating (in this mode) get blocks
+        bh = active_head_block(conv, inc.hstate, MODE == kAssignMoved ? 0 : 1, nbh,
+                               blocks_per_head, &bid);
+        if (bh < 0) return;
+      }
+      key0 = (bid % blocks_per_head) * KPB + wave * KPW;
+      if constexpr (MODE == kAssignMoved) {
+        src = inc.cfrags;
+        cl = inc.hstate[4 * bh + 0];
+        ntl = (cl + 31) / 32;
+        if (ntl == 0) return;  // nothing moved: every label stands
+      }
+    }
+    if (work) {
+      // Key fragments (B operand): lane holds key n = lane % 32, k = 16 s + 8 half + j.
+      bf16x8_t bfrag[NCB][KS];
+      float kmax = 0.f;
+      int gkey[NCB];   // kAssignGather: the lane's key (valid when < n)
+      float kofs[NCB];  // kAssignGather: K_w of that key's wave
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    bestp[cb] = 0xffffffffu;
-    btile[cb] = 0;
+      for (int cb = 0; cb < NCB; ++cb) {
+        int key = key0 + cb * 32 + (lane & 31);
+        if constexpr (MODE == kAssignGather) {
+          const int p = gpos0 + cb * 32 + (lane & 31);
+          key = p < gcount ? inc.glist[(size_t)bh * n + p] : n;
+          gkey[cb] = key;
+          kofs[cb] = key < n ? inc.koff[(size_t)bh * nw + key / KPW] : 0.f;
+        }
+        const uint16_t *krow = keys + ((size_t)bh * n + (key < n ? key : 0)) * D;
+        float sq = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          uint4 v = {0u, 0u, 0u, 0u};
+          if (key < n) v = *reinterpret_cast<const uint4 *>(krow + 16 * s + 8 * half);
+          bfrag[cb][s] = __builtin_bit_cast(bf16x8_t, v);
+          if constexpr (MODE != kAssignGather) {
+            float f[8];
+            unpack16<uint16_t>(v, f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sq = fmaf(f[j], f[j], sq);
+          }
+        }
+        if constexpr (MODE != kAssignGather) kmax = fmaxf(kmax, sum_xor32(sq));
+      }
+      // The empty asm makes the product opaque, so the compiler cannot fuse it
+      // into the per-tile subtractions below in some tiles and not in others:
+      // every tile's accumulator start must be the same function of its norms
+      // bit for bit (identical centroids must score identically in every tile
+      // for the lowest-index tie rule).
+      float koff = 0.5f * wave_max(kmax) * 1.001f;
+      asm volatile("" : "+v"(koff));
+      if (MODE != kAssignGather && inc.koff != nullptr && lane == 0 && key0 < n)
+        inc.koff[(size_t)bh * nw + key0 / KPW] = koff;
+
+      uint32_t bestp[NCB];
+      int btile[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        bestp[cb] = 0xffffffffu;
+        btile[cb] = 0;
+      }
+
+      const uint4 *gfr = reinterpret_cast<const uint4 *>(src) + ((size_t)bh * ntile + t0) * TILE_U4;
+      const int nstage = (ntl + kTilesPerStage - 1) / kTilesPerStage;
+
+      // Stage st -> LDS as one flat copy of its tiles: wave w moves 1 KB blocks
+      // w, w + 8, ...; units past the range's last tile are not loaded (and never read).
+      auto dma_stage = [&](int st, uint4 *dst) {
+        const int lim = min(ntl - st * kTilesPerStage, kTilesPerStage) * TILE_U4;
+#pragma unroll
+        for (int i = wave; i < STAGE_BLOCKS; i += kAssignWaves) {
+          if (i * 64 + lane < lim)
+            __builtin_amdgcn_global_load_lds(gfr + (size_t)st * STAGE_U4 + i * 64 + lane,
+                                             dst + i * 64, 16, 0, 0);
+        }
+      };
+      // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4,
+      // whose norms are entries 8 j + 4 half .. + 3 (unit 2 j + half) of the norm block.
+      // The next k-step's A fragment is requested before this k-step's MFMAs issue.
+      // kAssignGather: the columns' keys come from different waves, so each
+      // column block starts from its own K_w (per lane).
+      auto mfma_tile = [&](const uint4 *buf, int tt, f32x16_t *o) {
+        const uint4 *tb = buf + tt * TILE_U4;
+        bf16x8_t a[2];
+        a[0] = __builtin_bit_cast(bf16x8_t, tb[lane]);
+        f32x16_t ci;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 u = tb[KS * 64 + 2 * j + half];
+          ci[4 * j + 0] = __uint_as_float(u.x);
+          ci[4 * j + 1] = __uint_as_float(u.y);
+          ci[4 * j + 2] = __uint_as_float(u.z);
+          ci[4 * j + 3] = __uint_as_float(u.w);
+        }
+        if constexpr (MODE == kAssignGather) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[cb][r] = ci[r] - kofs[cb];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ci[r] -= koff;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          if (s + 1 < KS) a[(s + 1) & 1] = __builtin_bit_cast(bf16x8_t, tb[(s + 1) * 64 + lane]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            if constexpr (MODE == kAssignGather)
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1], bfrag[cb][s], o[cb], 0, 0, 0);
+            else
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1], bfrag[cb][s],
+                                                              s == 0 ? ci : o[cb], 0, 0, 0);
+          }
+        }
+      };
+      auto argmin_tile = [&](const f32x16_t &acc, int cb, int t, bool last) {
+        uint32_t p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[r] = (__float_as_uint(acc[r]) & 0xfffffff0u) | (uint32_t)r;
+        if (last && t * 32 + 32 > cl) {  // ragged last tile: padding rows never take part
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= cl) p[r] = 0xffffffffu;
+        }
+        const uint32_t m0 = min(min(p[0], p[1]), p[2]);
+        const uint32_t m1 = min(min(p[3], p[4]), p[5]);
+        const uint32_t m2 = min(min(p[6], p[7]), p[8]);
+        const uint32_t m3 = min(min(p[9], p[10]), p[11]);
+        const uint32_t m4 = min(min(p[12], p[13]), p[14]);
+        const uint32_t q0 = min(min(m0, m1), m2);
+        const uint32_t q1 = min(min(m3, m4), p[15]);
+        const uint32_t m = min(q0, q1);
+        if ((m | 15u) < (bestp[cb] & 0xfffffff0u)) {
+          bestp[cb] = m;
+          btile[cb] = t;
+        }
+      };
+
+      f32x16_t acc[NCB];
+      int t = 0;  // tile whose scores sit in acc
+      auto argmin_all = [&](bool last) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) argmin_tile(acc[cb], cb, t, last);
+      };
+      auto advance = [&](const uint4 *buf, int tt, int nt) {
+        argmin_all(false);
+        mfma_tile(buf, tt, acc);
+        t = nt;
+      };
+      // Tiles [st * TPS + 1, (st + 1) * TPS) of stage st (in `cur`), then the first
+      // tile of stage st + 1 (in `nxt`) once that stage has landed.
+      auto run_stage = [&](int st, const uint4 *cur, uint4 *cur_w, const uint4 *nxt) {
+#pragma unroll
+        for (int tt = 1; tt < kTilesPerStage; ++tt) {
+          const int nt = st * kTilesPerStage + tt;
+          if (nt >= ntl) return;
+          advance(cur, tt, nt);
+        }
+        const int nt = (st + 1) * kTilesPerStage;
+        if (nt >= ntl) return;
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): stage st + 1 has landed
+        __syncthreads();                     // ... for every wave; `cur` is free again
+        if (st + 2 < nstage) dma_stage(st + 2, cur_w);
+        advance(nxt, 0, nt);
+      };
+
+      dma_stage(0, lds0);
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+      if (nstage > 1) dma_stage(1, lds1);
+      mfma_tile(lds0, 0, acc);
+      for (int st = 0; st < nstage; st += 2) {
+        run_stage(st, lds0, lds0, lds1);
+        if (st + 1 < nstage) run_stage(st + 1, lds1, lds1, lds0);
+      }
+      argmin_all(true);
+
+      bool diff = false;  // a label of this wave differs from the previous round's
+      bool queue[NCB];    // kAssignMoved: the key's own cluster moved
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        queue[cb] = false;
+        const uint32_t r = bestp[cb] & 15u;
+        uint32_t kt = bestp[cb] & 0xfffffff0u;
+        int idx = btile[cb] * 32 + 8 * (int)(r >> 2) + (int)(r & 3u) + 4 * half;
+        const uint32_t ok = __shfl_xor(kt, 32);
+        const int oi = __shfl_xor(idx, 32);
+        if (ok < kt || (ok == kt && oi < idx)) {
+          idx = oi;
+          kt = ok;
+        }
+        if constexpr (MODE == kAssignGather) {
+          const int p = gpos0 + cb * 32 + (lane & 31);
+          if (half == 0 && gkey[cb] < n)
+            atomicMin(inc.gbest + (size_t)bh * n + p,
+                      ((unsigned long long)kt << 32) | (uint32_t)(t0 * 32 + idx));
+          continue;
+        }
+        const int key = key0 + cb * 32 + (lane & 31);
+        if (half != 0 || key >= n) continue;
+        int32_t *lp = labels + (size_t)bh * n + key;
+        if constexpr (MODE == kAssignMoved) {
+          const int old = *lp;
+          if (inc.fprev[(size_t)bh * c + old] != 0) {
+            queue[cb] = true;
+            continue;
+          }
+          const int j = inc.mlist[(size_t)bh * c + min(idx, cl - 1)];
+          const uint32_t own = (uint32_t)inc.own[(size_t)bh * n + key];
+          if (kt < own || (kt == own && j < old)) {
+            *lp = j;
+            inc.own[(size_t)bh * n + key] = (int32_t)kt;
+            inc.fcur[(size_t)bh * c + old] = 1;
+            inc.fcur[(size_t)bh * c + j] = 1;
+            diff = true;
+          }
+        } else {
+          if (chg != nullptr) {
+            const int old = *lp;
+            if (old != idx) {
+              diff = true;
+              if (inc.fcur != nullptr) {
+                inc.fcur[(size_t)bh * c + old] = 1;
+                inc.fcur[(size_t)bh * c + idx] = 1;
+              }
+            }
+          }
+          *lp = idx;
+          if (inc.own != nullptr) inc.own[(size_t)bh * n + key] = (int32_t)kt;
+        }
+      }
+      if constexpr (MODE == kAssignMoved) {
+        // queue the keys whose own cluster moved (a slot per key, one atomic per wave)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const uint64_t m = __ballot(queue[cb]);
+          if (m == 0ull) continue;
+          int base = 0;
+          if (lane == 0) base = atomicAdd(inc.hstate + 4 * bh + 2, __popcll(m));
+          base = __shfl(base, 0);
+          if (queue[cb]) {
+            const int p = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            inc.glist[(size_t)bh * n + p] = key0 + cb * 32 + (lane & 31);
+            inc.gbest[(size_t)bh * n + p] = ~0ull;
+          }
+        }
+      }
+      if (MODE != kAssignGather && chg != nullptr && __ballot(diff) != 0ull && lane == 0)
+        chg[bh] = 1;
+    }
+    if constexpr (MODE != kAssignGather) break;
+    item += gridDim.x;
+    if (item >= nitems) break;
+    __syncthreads();  // the stage buffers are filled again for the next item
   }
+}
 
-  const uint4 *gfr = reinterpret_cast<const uint4 *>(frags) + (size_t)bh * ntile * TILE_U4;
-  const int nstage = (ntile + kTilesPerStage - 1) / kTilesPerStage;
+// After kAssignGather: the queued keys take the labels the splits agreed on.
+__global__ void __launch_bounds__(256) k_assign_gathered_finish(int32_t *__restrict__ labels,
+                                                                int n, int c,
+                                                                const int32_t *__restrict__ conv,
+                                                                int32_t *__restrict__ chg,
+                                                                AssignInc inc) {
+  const int bh = blockIdx.y;
+  if (!head_served(conv, inc.hstate, 0, bh)) return;
+  const int g = inc.hstate[4 * bh + 2];
+  bool diff = false;
+  for (int p = blockIdx.x * 256 + threadIdx.x; p < g; p += gridDim.x * 256) {
+    const int key = inc.glist[(size_t)bh * n + p];
+    const unsigned long long b = inc.gbest[(size_t)bh * n + p];
+    const int j = (int)(uint32_t)b;
+    if (key < 0 || key >= n || j < 0 || j >= c) continue;  // every split wrote a label
+    int32_t *lp = labels + (size_t)bh * n + key;
+    const int old = *lp;
+    inc.own[(size_t)bh * n + key] = (int32_t)(uint32_t)(b >> 32);
+    if (j != old) {
+      *lp = j;
+      inc.fcur[(size_t)bh * c + old] = 1;
+      inc.fcur[(size_t)bh * c + j] = 1;
+      diff = true;
+    }
+  }
+  if (__ballot(diff) != 0ull && (threadIdx.x & 63) == 0) chg[bh] = 1;
+}
 
-  // Stage st -> LDS as one flat copy of its tiles: wave w moves 1 KB blocks
-  // w, w + 8, ...; units past the head's last tile are not loaded (and never read).
-  auto dma_stage = [&](int st, uint4 *dst) {
-    const int lim = min(ntile - st * kTilesPerStage, kTilesPerStage) * TILE_U4;
-#pragma unroll
-    for (int i = wave; i < STAGE_BLOCKS; i += kAssignWaves) {
-      if (i * 64 + lane < lim)
-        __builtin_amdgcn_global_load_lds(gfr + (size_t)st * STAGE_U4 + i * 64 + lane, dst + i * 64,
-                                         16, 0, 0);
+// Before a round's assignment: the clusters the previous round's label
+// changes touched (fprev) are the only ones whose centroid can have moved.
+// Lists them in index order with their tiles copied into compact tiles, and
+// sets the head's state: [0] moved count, [1] mode (1: sweep every centroid,
+// when more than a third moved or on force_full; 0: incremental; 2: head
+// converged), [2] queued keys = 0. Clears fcur for this round's assignment.
+template <int D>
+__global__ void __launch_bounds__(256) k_moved_list(const uint16_t *__restrict__ frags, int c,
+                                                    int ntile, const int32_t *__restrict__ conv,
+                                                    int force_full, AssignInc inc) {
+  using TL = AssignTile<D>;
+  __shared__ int s_w[2][4];
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = blockIdx.x * 256 + tid;
+  int32_t *hs = inc.hstate + 4 * bh;
+  if (conv[bh] != 0) {
+    if (blockIdx.x == 0 && tid == 0) {
+      hs[0] = 0;
+      hs[1] = 2;
+      hs[2] = 0;
     }
-  };
-  // D layout: lane holds column n = lane % 32 and rows 8 (r / 4) + 4 half + r % 4,
-  // whose norms are entries 8 j + 4 half .. + 3 (unit 2 j + half) of the norm block.
-  // The next k-step's A fragment is requested before this k-step's MFMAs issue.
-  auto mfma_tile = [&](const uint4 *buf, int tt, f32x16_t *o) {
-    const uint4 *tb = buf + tt * TILE_U4;
-    bf16x8_t a[2];
-    a[0] = __builtin_bit_cast(bf16x8_t, tb[lane]);
-    f32x16_t ci;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 u = tb[KS * 64 + 2 * j + half];
-      ci[4 * j + 0] = __uint_as_float(u.x) - koff;
-      ci[4 * j + 1] = __uint_as_float(u.y) - koff;
-      ci[4 * j + 2] = __uint_as_float(u.z) - koff;
-      ci[4 * j + 3] = __uint_as_float(u.w) - koff;
+    return;
+  }
+  if (k < c) inc.fcur[(size_t)bh * c + k] = 0;
+  if (force_full) {
+    if (blockIdx.x == 0 && tid == 0) {
+      hs[0] = c;
+      hs[1] = 1;
+      hs[2] = 0;
     }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) a[(s + 1) & 1] = __builtin_bit_cast(bf16x8_t, tb[(s + 1) * 64 + lane]);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1], bfrag[cb][s],
-                                                        s == 0 ? ci : o[cb], 0, 0, 0);
-    }
-  };
-  auto argmin_tile = [&](const f32x16_t &acc, int cb, int t, bool last) {
-    uint32_t p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      p[r] = (__float_as_uint(acc[r]) & 0xfffffff0u) | (uint32_t)r;
-    if (last && t * 32 + 32 > c) {  // ragged last tile: padding rows never take part
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (t * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= c) p[r] = 0xffffffffu;
-    }
-    const uint32_t m0 = min(min(p[0], p[1]), p[2]);
-    const uint32_t m1 = min(min(p[3], p[4]), p[5]);
-    const uint32_t m2 = min(min(p[6], p[7]), p[8]);
-    const uint32_t m3 = min(min(p[9], p[10]), p[11]);
-    const uint32_t m4 = min(min(p[12], p[13]), p[14]);
-    const uint32_t q0 = min(min(m0, m1), m2);
-    const uint32_t q1 = min(min(m3, m4), p[15]);
-    const uint32_t m = min(q0, q1);
-    if ((m | 15u) < (bestp[cb] & 0xfffffff0u)) {
-      bestp[cb] = m;
-      btile[cb] = t;
-    }
-  };
-
-  f32x16_t acc[NCB];
-  int t = 0;  // tile whose scores sit in acc
-  auto argmin_all = [&](bool last) {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) argmin_tile(acc[cb], cb, t, last);
-  };
-  auto advance = [&](const uint4 *buf, int tt, int nt) {
-    argmin_all(false);
-    mfma_tile(buf, tt, acc);
-    t = nt;
-  };
-  // Tiles [st * TPS + 1, (st + 1) * TPS) of stage st (in `cur`), then the first
-  // tile of stage st + 1 (in `nxt`) once that stage has landed.
-  auto run_stage = [&](int st, const uint4 *cur, uint4 *cur_w, const uint4 *nxt) {
-#pragma unroll
-    for (int tt = 1; tt < kTilesPerStage; ++tt) {
-      const int nt = st * kTilesPerStage + tt;
-      if (nt >= ntile) return;
-      advance(cur, tt, nt);
-    }
-    const int nt = (st + 1) * kTilesPerStage;
-    if (nt >= ntile) return;
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): stage st + 1 has landed
-    __syncthreads();                     // ... for every wave; `cur` is free again
-    if (st + 2 < nstage) dma_stage(st + 2, cur_w);
-    advance(nxt, 0, nt);
-  };
-
-  dma_stage(0, lds0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+    return;
+  }
+  const int32_t *fp = inc.fprev + (size_t)bh * c;
+  const int lo = blockIdx.x * 256;
+  int before = 0, tot = 0;
+  for (int i = tid; i < c; i += 256) {
+    const int f = fp[i] != 0;
+    tot += f;
+    before += (i < lo) ? f : 0;
+  }
+  before = wave_sum_i32(before);
+  tot = wave_sum_i32(tot);
+  if (lane == 0) {
+    s_w[0][wave] = before;
+    s_w[1][wave] = tot;
+  }
   __syncthreads();
-  if (nstage > 1) dma_stage(1, lds1);
-  mfma_tile(lds0, 0, acc);
-  for (int st = 0; st < nstage; st += 2) {
-    run_stage(st, lds0, lds0, lds1);
-    if (st + 1 < nstage) run_stage(st + 1, lds1, lds1, lds0);
+  before = s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
+  tot = s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
+  const int mode = 3 * tot > c ? 1 : 0;
+  if (blockIdx.x == 0 && tid == 0) {
+    hs[0] = tot;
+    hs[1] = mode;
+    hs[2] = 0;
   }
-  argmin_all(true);
-
-  bool diff = false;  // a label of this wave differs from the previous round's
+  if (mode != 0) return;
+  __syncthreads();  // s_w is reused
+  const int f = (k < c && fp[k] != 0) ? 1 : 0;
+  const int incl = wave_incl_scan_i32(f);
+  if (lane == 63) s_w[0][wave] = incl;
+  __syncthreads();
+  int q = before + incl - f;
+  for (int w = 0; w < wave; ++w) q += s_w[0][w];
+  if (f) {
+    inc.mlist[(size_t)bh * c + q] = k;
+    const uint4 *st = reinterpret_cast<const uint4 *>(frags) + ((size_t)bh * ntile + k / 32) * TL::U4;
+    uint4 *dt = reinterpret_cast<uint4 *>(inc.cfrags) +
+                ((size_t)bh * ntile + q / 32) * TL::U4;
+    const int ms = k % 32, md = q % 32;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const uint32_t r = bestp[cb] & 15u;
-    const uint32_t key_t = bestp[cb] & 0xfffffff0u;
-    int idx = btile[cb] * 32 + 8 * (int)(r >> 2) + (int)(r & 3u) + 4 * half;
-    const uint32_t ok = __shfl_xor(key_t, 32);
-    const int oi = __shfl_xor(idx, 32);
-    if (ok < key_t || (ok == key_t && oi < idx)) idx = oi;
-    const int key = key0 + cb * 32 + (lane & 31);
-    if (half == 0 && key < n) {
-      int32_t *lp = labels + (size_t)bh * n + key;
-      if (chg != nullptr) diff |= *lp != idx;
-      *lp = idx;
+    for (int s = 0; s < TL::KS; ++s) {
+      dt[s * 64 + md] = st[s * 64 + ms];
+      dt[s * 64 + md + 32] = st[s * 64 + ms + 32];
     }
+    reinterpret_cast<float *>(dt + TL::KS * 64)[md] =
+        reinterpret_cast<const float *>(st + TL::KS * 64)[ms];
   }
-  if (chg != nullptr && __ballot(diff) != 0ull && lane == 0) chg[bh] = 1;
 }
 
 // ---------------------------------------------------------------- fp32 assign
@@ -443,11 +733,13 @@ kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, in
     const int bph = (n + KPB - 1) / KPB;
     const int total = bph * bh;
     if (d == 128)
-      k_assign_mfma<128, NCB, kAssignMinWaves><<<total, 64 * kAssignWaves, 0, s>>>(
-          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg);
+      k_assign_mfma<128, NCB, kAssignMinWaves, kAssignFull><<<total, 64 * kAssignWaves, 0, s>>>(
+          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg,
+          AssignInc{});
     else
-      k_assign_mfma<64, NCB, kAssignMinWaves><<<total, 64 * kAssignWaves, 0, s>>>(
-          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg);
+      k_assign_mfma<64, NCB, kAssignMinWaves, kAssignFull><<<total, 64 * kAssignWaves, 0, s>>>(
+          (const uint16_t *)keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg,
+          AssignInc{});
   } else {
     const float *hn = static_cast<const float *>(ws);
     const dim3 grid((n + 255) / 256, bh);
@@ -456,6 +748,95 @@ kv_status launch_assign_prepared(const void *keys, const float *cent, int bh, in
     else
       k_assign_f32<64><<<grid, 256, 0, s>>>((const float *)keys, cent, hn, labels, n, c);
   }
+  return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+size_t assign_inc_ws_bytes(int bh, int n, int c, int d) {
+  const size_t ntile = (size_t)(c + 31) / 32, nw = (size_t)(n + 63) / 64;
+  size_t b = 0;
+  b += align_up((size_t)bh * n * 4, 256);                                        // own
+  b += align_up((size_t)bh * nw * 4, 256);                                       // koff
+  b += 2 * align_up((size_t)bh * c * 4, 256);                                    // flags
+  b += align_up((size_t)bh * c * 4, 256);                                        // mlist
+  b += align_up((size_t)bh * 4 * 4, 256);                                        // hstate
+  b += align_up((size_t)bh * ntile * ((size_t)(d / 16) * 64 + kNormU4) * 16, 256);  // cfrags
+  b += align_up((size_t)bh * n * 4, 256);                                        // glist
+  b += align_up((size_t)bh * n * 8, 256);                                        // gbest
+  return b;
+}
+
+void assign_inc_ws_carve(void *base, int bh, int n, int c, int d, AssignIncWs *w) {
+  const size_t ntile = (size_t)(c + 31) / 32, nw = (size_t)(n + 63) / 64;
+  char *p = static_cast<char *>(base);
+  auto take = [&](size_t bytes) {
+    char *q = p;
+    p += align_up(bytes, 256);
+    return q;
+  };
+  w->own = reinterpret_cast<int32_t *>(take((size_t)bh * n * 4));
+  w->koff = reinterpret_cast<float *>(take((size_t)bh * nw * 4));
+  w->flags[0] = reinterpret_cast<int32_t *>(take((size_t)bh * c * 4));
+  w->flags[1] = reinterpret_cast<int32_t *>(take((size_t)bh * c * 4));
+  w->mlist = reinterpret_cast<int32_t *>(take((size_t)bh * c * 4));
+  w->hstate = reinterpret_cast<int32_t *>(take((size_t)bh * 4 * 4));
+  w->cfrags = reinterpret_cast<uint16_t *>(
+      take((size_t)bh * ntile * ((size_t)(d / 16) * 64 + kNormU4) * 16));
+  w->glist = reinterpret_cast<int32_t *>(take((size_t)bh * n * 4));
+  w->gbest = reinterpret_cast<unsigned long long *>(take((size_t)bh * n * 8));
+}
+
+// Workgroups of the gathered sweep: one full residency of the chip (one
+// 8-wave workgroup per CU: the per-column offsets need more than 128
+// registers), looping over the (key group, split) items.
+constexpr int kGatherGrid = 256;
+constexpr int kGatherMinWaves = 2;
+
+template <int D>
+static void assign_round_kernels(const uint16_t *keys, int bh, int n, int c, int32_t *labels,
+                                 const uint16_t *frags, const AssignInc &ia, int round,
+                                 LloydSkip skip, hipStream_t s) {
+  constexpr int NCB = kAssignColBlocks;
+  constexpr int KPB = kAssignWaves * 32 * NCB;
+  const int ntile = (c + 31) / 32, bph = (n + KPB - 1) / KPB, total = bph * bh;
+  if (round >= 2)
+    k_moved_list<D><<<dim3((c + 255) / 256, bh), 256, 0, s>>>(frags, c, ntile, skip.conv,
+                                                               round == 2 ? 1 : 0, ia);
+  k_assign_mfma<D, NCB, kAssignMinWaves, kAssignFull><<<total, 64 * kAssignWaves, 0, s>>>(
+      keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg, ia);
+  if (round >= 3) {
+    k_assign_mfma<D, NCB, kAssignMinWaves, kAssignMoved><<<total, 64 * kAssignWaves, 0, s>>>(
+        keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg, ia);
+    k_assign_mfma<D, NCB, kGatherMinWaves, kAssignGather>
+        <<<kGatherGrid, 64 * kAssignWaves, 0, s>>>(keys, frags, labels, n, c, ntile, bph, total,
+                                                    skip.conv, skip.chg, ia);
+    k_assign_gathered_finish<<<dim3(16, bh), 256, 0, s>>>(labels, n, c, skip.conv, skip.chg, ia);
+  }
+}
+
+kv_status launch_assign_round(const void *keys, int bh, int n, int d, int c, int32_t *labels,
+                              const void *frags, const AssignIncWs &w, int round, LloydSkip skip,
+                              hipStream_t s) {
+  if (round >= 2 && (skip.conv == nullptr || skip.chg == nullptr)) return KV_ERR_INVALID_ARG;
+  AssignInc ia;
+  ia.own = w.own;
+  ia.koff = w.koff;
+  if (round >= 2) {
+    ia.fprev = w.flags[(round - 1) & 1];
+    ia.fcur = w.flags[round & 1];
+    ia.mlist = w.mlist;
+    ia.hstate = w.hstate;
+    ia.cfrags = w.cfrags;
+    ia.glist = w.glist;
+    ia.gbest = w.gbest;
+  }
+  const uint16_t *k = static_cast<const uint16_t *>(keys);
+  const uint16_t *f = static_cast<const uint16_t *>(frags);
+  if (d == 128)
+    assign_round_kernels<128>(k, bh, n, c, labels, f, ia, round, skip, s);
+  else if (d == 64)
+    assign_round_kernels<64>(k, bh, n, c, labels, f, ia, round, skip, s);
+  else
+    return KV_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

@@ -310,6 +310,39 @@ struct LloydSkip {
   int32_t *chg = nullptr;
   int round = 0;  // 1-based number of the round the launch belongs to
 };
+// Incremental assignment of kv_cluster_build (bf16): a round sweeps every
+// centroid only for the keys whose own cluster moved in the last update; the
+// other keys compare their recorded score with the moved centroids alone.
+// Kernel-side view (per head; null members disable the part that uses them):
+struct AssignInc {
+  int32_t *own = nullptr;                // [bh][n]  winning score bits (upper 28) of each key
+  float *koff = nullptr;                 // [bh][ceil(n/64)]  K_w of each 64-key wave
+  const int32_t *fprev = nullptr;        // [bh][c]  clusters the last round's changes touched
+  int32_t *fcur = nullptr;               // [bh][c]  ... this round's
+  int32_t *mlist = nullptr;              // [bh][c]  moved clusters, ascending
+  int32_t *hstate = nullptr;             // [bh][4]  moved count, mode, queued keys, -
+  uint16_t *cfrags = nullptr;            // the moved clusters' tiles, in mlist order
+  int32_t *glist = nullptr;              // [bh][n]  queued keys
+  unsigned long long *gbest = nullptr;   // [bh][n]  (score bits << 32 | label) per queued key
+};
+// Its workspace (carved from kv_cluster_build's).
+struct AssignIncWs {
+  int32_t *own, *flags[2], *mlist, *hstate, *glist;
+  float *koff;
+  uint16_t *cfrags;
+  unsigned long long *gbest;
+};
+size_t assign_inc_ws_bytes(int bh, int n, int c, int d);
+void assign_inc_ws_carve(void *base, int bh, int n, int c, int d, AssignIncWs *w);
+// One assignment round (1-based `round`) of kv_cluster_build, bf16, with the
+// fixed-point skip active from round 2 on: round 1 sweeps every centroid and
+// records the scores; round 2 as well (every centroid moved in round 1's
+// update); from round 3 on, heads where at most a third of the centroids
+// moved run incrementally. The labels equal those of a whole sweep bit for
+// bit. `frags` holds the current centroids' tiles.
+kv_status launch_assign_round(const void *keys, int bh, int n, int d, int c, int32_t *labels,
+                              const void *frags, const AssignIncWs &w, int round, LloydSkip skip,
+                              hipStream_t s);
 // rounds[i] = conv[i] if set, else iters (conv null: iters for every head).
 kv_status launch_rounds_out(const int32_t *conv, int32_t *rounds, int bh, int iters,
                             hipStream_t s);

@@ -145,8 +145,11 @@ def test_update_empty_cluster_keeps_centroid(tiny):
     assert cnt[0].tolist() == case["expect_counts"]
 
 
-def _cluster_build(cfg, heads, iters, seqs=(0,), rounds=None):
+def _cluster_build(cfg, heads, iters, seqs=(0,), rounds=None, dup=0):
     inp = wl.layer_inputs(cfg, 0, heads=heads, seqs=seqs)
+    if dup:  # exact copies: key i repeats key i - i % dup (ties between keys and centroids)
+        src = np.arange(inp["keys"].shape[2])
+        inp["keys"] = inp["keys"][:, :, src - src % dup].copy()
     B, H, N, d = inp["keys"].shape
     pool = make_pool(B, H, d, cfg.dtype, N, cfg.n_clusters)
     keys = to_dev(inp["keys"], cfg.dtype)
@@ -197,17 +200,29 @@ def test_cluster_build_invariants_and_pack(cfg_idx, over, heads):
     assert pool.n_units.cpu().tolist() == [C] and pool.n_cand.cpu().tolist() == [C]
 
 
+# many heads converging at different rounds (a mix of whole and incremental
+# sweeps in one launch, queued keys of several heads); head_dim 64; copied keys
+EQ_EXTRA = [
+    (1, dict(n_keys=16384, n_clusters=1024, n_components=128), list(range(8)), 0),
+    (CASES[3][0], CASES[3][1], CASES[3][2], 0),
+    (1, dict(n_keys=8192, n_clusters=700, n_components=96), [0, 1, 2], 3),
+]
+
+
 @pytest.mark.parametrize("iters", [4, 14])
-@pytest.mark.parametrize("cfg_idx,over,heads", [CASES[0], CASES[2]] + BIG_C)
-def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, iters):
+@pytest.mark.parametrize("cfg_idx,over,heads,dup",
+                         [c + (0,) for c in [CASES[0], CASES[2]] + BIG_C] + EQ_EXTRA)
+def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, dup, iters):
     """kv_cluster_build's rounds (the two-launch update of every round but the
-    last; heads that reach a fixed point skip their later rounds) give the
-    same labels and centroids, bit for bit, as running kv_kmeans_assign and
-    kv_kmeans_update round by round from the same start. 14 rounds take these
-    heads past their fixed points."""
+    last; heads that reach a fixed point skip their later rounds; from the
+    third round on, the sweep covers only the centroids that moved, plus every
+    centroid for the keys whose own centroid moved) give the same labels and
+    centroids, bit for bit, as running kv_kmeans_assign and kv_kmeans_update
+    round by round from the same start. 14 rounds take these heads past their
+    fixed points."""
     cfg = wl.get_config(cfg_idx, **over)
     rounds = torch.full((1, len(heads)), -1, dtype=torch.int32, device="cuda")
-    inp, pool, lab = _cluster_build(cfg, heads, iters, rounds=rounds)
+    inp, pool, lab = _cluster_build(cfg, heads, iters, rounds=rounds, dup=dup)
     rounds = rounds.cpu().numpy()
     # assignments run per head: iters, or (bf16) fewer for a head whose
     # assignment in some round 2.. changed no label
