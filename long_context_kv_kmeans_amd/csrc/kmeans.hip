@@ -297,6 +297,13 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
       float kmax = 0.f;
       int gkey[NCB];   // kAssignGather: the lane's key (valid when < n)
       float kofs[NCB];  // kAssignGather: K_w of that key's wave
+      // kAssignMoved: the key's label (requested now, used after the sweep)
+      int oldl[NCB];
+      if constexpr (MODE == kAssignMoved) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          oldl[cb] = labels[(size_t)bh * n + min(key0 + cb * 32 + (lane & 31), n - 1)];
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         int key = key0 + cb * 32 + (lane & 31);
@@ -482,7 +489,7 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
         if (half != 0 || key >= n) continue;
         int32_t *lp = labels + (size_t)bh * n + key;
         if constexpr (MODE == kAssignMoved) {
-          const int old = *lp;
+          const int old = oldl[cb];
           if (inc.fprev[(size_t)bh * c + old] != 0) {
             queue[cb] = true;
             continue;
@@ -512,23 +519,41 @@ __global__ void __launch_bounds__(64 * kAssignWaves, MINW)
         }
       }
       if constexpr (MODE == kAssignMoved) {
-        // queue the keys whose own cluster moved (a slot per key, one atomic per wave)
+        // queue the keys whose own cluster moved: a slot per key, one atomic
+        // per workgroup (the head's counter is shared by all its workgroups)
+        __shared__ int s_q[kAssignWaves + 1];
+        uint64_t qm[NCB];
+        int wq = 0;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const uint64_t m = __ballot(queue[cb]);
-          if (m == 0ull) continue;
-          int base = 0;
-          if (lane == 0) base = atomicAdd(inc.hstate + 4 * bh + 2, __popcll(m));
-          base = __shfl(base, 0);
+          qm[cb] = __ballot(queue[cb]);
+          wq += __popcll(qm[cb]);
+        }
+        if (lane == 0) s_q[wave] = wq;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int tq = 0;
+          for (int w = 0; w < kAssignWaves; ++w) tq += s_q[w];
+          s_q[kAssignWaves] = tq > 0 ? atomicAdd(inc.hstate + 4 * bh + 2, tq) : 0;
+        }
+        __syncthreads();
+        int base = s_q[kAssignWaves];
+        for (int w = 0; w < wave; ++w) base += s_q[w];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
           if (queue[cb]) {
-            const int p = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            const int p = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(qm[cb] >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)qm[cb], 0u));
             inc.glist[(size_t)bh * n + p] = key0 + cb * 32 + (lane & 31);
             inc.gbest[(size_t)bh * n + p] = ~0ull;
           }
+          base += __popcll(qm[cb]);
         }
       }
-      if (MODE != kAssignGather && chg != nullptr && __ballot(diff) != 0ull && lane == 0)
+      // the head's change flag: stored by the first waves that see it clear
+      // (every wave storing to one line would queue thousands of writes there)
+      if (MODE != kAssignGather && chg != nullptr && __ballot(diff) != 0ull && lane == 0 &&
+          chg[bh] == 0)
         chg[bh] = 1;
     }
     if constexpr (MODE != kAssignGather) break;
@@ -563,7 +588,7 @@ __global__ void __launch_bounds__(256) k_assign_gathered_finish(int32_t *__restr
       diff = true;
     }
   }
-  if (__ballot(diff) != 0ull && (threadIdx.x & 63) == 0) chg[bh] = 1;
+  if (__ballot(diff) != 0ull && (threadIdx.x & 63) == 0 && chg[bh] == 0) chg[bh] = 1;
 }
 
 // Before a round's assignment: the clusters the previous round's label
