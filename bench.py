@@ -375,6 +375,7 @@ def main():
                 (np.arange(C) * page).astype(np.int32), (B, H, C)).copy()).cuda()
         y.labels = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
         y.rounds = torch.zeros(B, H, dtype=torch.int32, device="cuda")  # Lloyd rounds run per head
+        y.sweeps = torch.zeros(B, H, dtype=torch.float32, device="cuda")  # assignment work
         y.flags = torch.zeros(T, B, dtype=torch.uint8, device="cuda")
         y.sel = torch.zeros(B, H, sel_cap, dtype=torch.int32, device="cuda")
         y.sel_n = torch.zeros(B, H, dtype=torch.int32, device="cuda")
@@ -409,7 +410,7 @@ def main():
             kvc.kv_cluster_build(y.pool, y.keys, y.vals, C, cfg.iters, y.init,
                                  assign_in=y.assign_in,
                                  assign_out=None if y.assign_in is not None else y.labels,
-                                 ws=y.ws_build, rounds_out=y.rounds)
+                                 ws=y.ws_build, rounds_out=y.rounds, sweeps_out=y.sweeps)
 
     def decode_step(y, t):
         q_prev = y.q[t - 1] if t else None
@@ -688,11 +689,13 @@ def main():
     asg_ms = launch_ms(asg_fn, args.assign_reps)
     flops = 2.0 * B * H * N * C * d
     achieved = flops / (asg_ms * 1e-3) / 1e12
-    # assignment launches' worth of work per step: a head at a fixed point of
-    # Lloyd's iteration skips its later rounds (rounds_out of each build)
+    # assignment work per step in whole sweeps (sweeps_out of each build): a
+    # head at a fixed point of Lloyd's iteration skips its later rounds, and
+    # rounds after the second score only the centroids that moved
     rounds_run = [float(y.rounds.float().mean().item()) for y in layers]
+    sweeps_run = [float(y.sweeps.mean().item()) for y in layers]
     share = {"k_gather_attend": T * L * att_ms / ms_step,
-             "k_assign_mfma": (0 if page is not None else sum(rounds_run)) * asg_ms / ms_step}
+             "k_assign_mfma": (0 if page is not None else sum(sweeps_run)) * asg_ms / ms_step}
 
     # What this machine reaches on plain work: a 1 GiB device copy (bytes read +
     # written) and a large bf16 GEMM through torch (hipBLASLt).
@@ -765,6 +768,7 @@ def main():
                    "decode_steps_overridden": args.decode_steps is not None},
         "retrieval_steps": int(fl.sum()),
         "lloyd_rounds_per_head": sum(rounds_run) / L,
+        "assign_sweeps_per_head": sum(sweeps_run) / L,
         "retrieval": retrieval,
         "prefill_ms": pre_ms,
         "prefill_keys_per_s": keys_per_step / (pre_ms * 1e-3),

@@ -148,6 +148,13 @@ const char *kv_status_string(kv_status s);
  *               centroids and pool are those of exactly `iters` rounds. It
  *               is iters where no such round came before the last (always
  *               for KV_F32), 0 with assign_in.
+ * sweeps_out:   NULL, or [BH] float: the assignment work each head took, in
+ *               whole sweeps of n_keys x n_clusters distance evaluations. For
+ *               KV_BF16 keys a round after the second scores only the
+ *               centroids that moved in the last update (every one of them
+ *               for the keys whose own centroid moved), which gives the
+ *               labels of a whole sweep bit for bit at a fraction of its
+ *               work; otherwise it equals rounds_out.
  * iters >= 1 unless assign_in is given. n_clusters <= n_keys,
  * n_keys <= pool->row_cap, n_clusters <= pool->unit_cap.
  */
@@ -156,8 +163,8 @@ size_t kv_cluster_build_workspace(int32_t batch, int32_t n_kv_heads, int32_t n_k
 kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *values,
                            int32_t n_keys, int32_t n_clusters, int32_t iters,
                            const int32_t *init_idx, const int32_t *assign_in,
-                           int32_t *assign_out, int32_t *rounds_out, void *ws,
-                           size_t ws_bytes, hipStream_t stream);
+                           int32_t *assign_out, int32_t *rounds_out, float *sweeps_out,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* One Lloyd assignment step (the same kernel kv_cluster_build runs).
  * keys [n_heads][n_keys][head_dim] (dtype); centroids [n_heads][n_clusters]

@@ -90,7 +90,7 @@ def lib() -> ctypes.CDLL:
         "kv_status_string": (ctypes.c_char_p, [c_int]),
         "kv_cluster_build_workspace": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
         "kv_cluster_build": (c_int, [pool_p, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp,
-                                     c_size, vp]),
+                                     vp, c_size, vp]),
         "kv_kmeans_assign_workspace": (c_size, [c_int, c_int, c_int, c_int]),
         "kv_kmeans_assign": (c_int, [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp, c_size, vp]),
         "kv_kmeans_prepare": (c_int, [vp, c_int, c_int, c_int, c_int, vp, c_size, vp]),
@@ -287,10 +287,12 @@ def kv_cluster_build_workspace(batch, n_kv_heads, n_keys, head_dim, n_clusters, 
 
 def kv_cluster_build(pool: Pool, keys, values, n_clusters: int, iters: int, init_idx,
                      assign_in=None, assign_out=None, ws=None, stream=None,
-                     rounds_out=None) -> None:
+                     rounds_out=None, sweeps_out=None) -> None:
     """rounds_out (optional) [B, H] int32 receives the rounds whose assignment
     ran for each head (a head at a fixed point of Lloyd's iteration skips the
-    rest, with the same result)."""
+    rest, with the same result); sweeps_out (optional) [B, H] float32 the
+    assignment work in whole sweeps of keys x clusters (later rounds score
+    only the centroids that moved, with the same result)."""
     B, H, D = pool.batch, pool.n_kv_heads, pool.head_dim
     _expect("keys", keys, (B, H, None, D), pool.dtype)
     N = keys.shape[2]
@@ -299,11 +301,13 @@ def kv_cluster_build(pool: Pool, keys, values, n_clusters: int, iters: int, init
     _expect("assign_in", assign_in, (B, H, N), torch.int32, optional=True)
     _expect("assign_out", assign_out, (B, H, N), torch.int32, optional=True)
     _expect("rounds_out", rounds_out, (B, H), torch.int32, optional=True)
+    _expect("sweeps_out", sweeps_out, (B, H), torch.float32, optional=True)
     if ws is None:
         ws = _call_workspace(kv_cluster_build_workspace(B, H, N, D, n_clusters, keys.dtype), stream)
     _check("kv_cluster_build", lib().kv_cluster_build(
         pool.ref(), _ptr(keys), _ptr(values), N, n_clusters, iters, _ptr(init_idx),
-        _ptr(assign_in), _ptr(assign_out), _ptr(rounds_out), _ptr(ws), _nbytes(ws),
+        _ptr(assign_in), _ptr(assign_out), _ptr(rounds_out), _ptr(sweeps_out), _ptr(ws),
+        _nbytes(ws),
         _stream(stream)))
 
 

@@ -40,8 +40,8 @@ size_t cluster_ws_layout(int bh, int n, int d, int c, kv_dtype dt, size_t *off_c
   o += assign_ws_bytes(bh, c, d, dt);
   *off_update = o;
   o += update_ws_bytes(bh, n, c);
-  if (off_skip) *off_skip = o;  // fixed-point flags: conv[bh], chg[bh]
-  o += align_up((size_t)2 * bh * sizeof(int32_t), 256);
+  if (off_skip) *off_skip = o;  // fixed-point flags conv[bh], chg[bh]; work counters [bh] (u64)
+  o += align_up((size_t)4 * bh * sizeof(int32_t), 256);
   if (off_inc) *off_inc = o;  // incremental assignment (bf16)
   if (dt == KV_BF16) o += assign_inc_ws_bytes(bh, n, c, d);
   return o;
@@ -190,7 +190,8 @@ size_t kv_cluster_build_workspace(int32_t batch, int32_t n_kv_heads, int32_t n_k
 kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *values,
                            int32_t n_keys, int32_t n_clusters, int32_t iters,
                            const int32_t *init_idx, const int32_t *assign_in, int32_t *assign_out,
-                           int32_t *rounds_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+                           int32_t *rounds_out, float *sweeps_out, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
   kv_status st = check_pool(pool);
   if (st != KV_OK) return st;
   if (!keys || !values || !init_idx) return KV_ERR_INVALID_ARG;
@@ -222,10 +223,11 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
     // later rounds sweep only the moved ones (and every centroid for the keys
     // whose own centroid moved): the labels of a whole sweep, bit for bit.
     assign_inc_ws_carve(w + o_inc, bh, n_keys, n_clusters, d, &inc);
+    inc.work = reinterpret_cast<unsigned long long *>(skip.conv + 2 * bh);
   }
 
   st = launch_init_centroids(keys, init_idx, cent, bh, n_keys, n_clusters, d, dt, pool->status,
-                             stream, skip.conv, skip.conv ? 2 * bh : 0);
+                             stream, skip.conv, skip.conv ? 4 * bh : 0);
   if (st != KV_OK) return st;
   const int32_t *perm = nullptr, *start = nullptr, *tot = nullptr;
   if (assign_in) {
@@ -268,8 +270,9 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
       if (st != KV_OK) return st;
     }
   }
-  if (rounds_out) {
-    st = launch_rounds_out(skip.conv, rounds_out, bh, assign_in ? 0 : iters, stream);
+  if (rounds_out || sweeps_out) {
+    st = launch_rounds_out(skip.conv, skip.conv ? inc.work : nullptr, rounds_out, sweeps_out, bh,
+                           assign_in ? 0 : iters, n_keys, n_clusters, stream);
     if (st != KV_OK) return st;
   }
   return launch_pack(pool, keys, values, cent, perm, start, tot, n_keys, n_clusters, stream);

@@ -572,6 +572,8 @@ __global__ void __launch_bounds__(256) k_assign_gathered_finish(int32_t *__restr
   const int bh = blockIdx.y;
   if (!head_served(conv, inc.hstate, 0, bh)) return;
   const int g = inc.hstate[4 * bh + 2];
+  if (inc.work != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+    inc.work[bh] += (unsigned long long)g * c;
   bool diff = false;
   for (int p = blockIdx.x * 256 + threadIdx.x; p < g; p += gridDim.x * 256) {
     const int key = inc.glist[(size_t)bh * n + p];
@@ -598,8 +600,9 @@ __global__ void __launch_bounds__(256) k_assign_gathered_finish(int32_t *__restr
 // when more than a third moved or on force_full; 0: incremental; 2: head
 // converged), [2] queued keys = 0. Clears fcur for this round's assignment.
 template <int D>
-__global__ void __launch_bounds__(256) k_moved_list(const uint16_t *__restrict__ frags, int c,
-                                                    int ntile, const int32_t *__restrict__ conv,
+__global__ void __launch_bounds__(256) k_moved_list(const uint16_t *__restrict__ frags, int n,
+                                                    int c, int ntile,
+                                                    const int32_t *__restrict__ conv,
                                                     int force_full, AssignInc inc) {
   using TL = AssignTile<D>;
   __shared__ int s_w[2][4];
@@ -620,6 +623,7 @@ __global__ void __launch_bounds__(256) k_moved_list(const uint16_t *__restrict__
       hs[0] = c;
       hs[1] = 1;
       hs[2] = 0;
+      if (inc.work != nullptr) inc.work[bh] += (unsigned long long)n * c;
     }
     return;
   }
@@ -645,6 +649,7 @@ __global__ void __launch_bounds__(256) k_moved_list(const uint16_t *__restrict__
     hs[0] = tot;
     hs[1] = mode;
     hs[2] = 0;
+    if (inc.work != nullptr) inc.work[bh] += (unsigned long long)n * (mode != 0 ? c : tot);
   }
   if (mode != 0) return;
   __syncthreads();  // s_w is reused
@@ -824,7 +829,7 @@ static void assign_round_kernels(const uint16_t *keys, int bh, int n, int c, int
   constexpr int KPB = kAssignWaves * 32 * NCB;
   const int ntile = (c + 31) / 32, bph = (n + KPB - 1) / KPB, total = bph * bh;
   if (round >= 2)
-    k_moved_list<D><<<dim3((c + 255) / 256, bh), 256, 0, s>>>(frags, c, ntile, skip.conv,
+    k_moved_list<D><<<dim3((c + 255) / 256, bh), 256, 0, s>>>(frags, n, c, ntile, skip.conv,
                                                                round == 2 ? 1 : 0, ia);
   k_assign_mfma<D, NCB, kAssignMinWaves, kAssignFull><<<total, 64 * kAssignWaves, 0, s>>>(
       keys, frags, labels, n, c, ntile, bph, total, skip.conv, skip.chg, ia);
@@ -845,6 +850,7 @@ kv_status launch_assign_round(const void *keys, int bh, int n, int d, int c, int
   AssignInc ia;
   ia.own = w.own;
   ia.koff = w.koff;
+  ia.work = w.work;
   if (round >= 2) {
     ia.fprev = w.flags[(round - 1) & 1];
     ia.fcur = w.flags[round & 1];
@@ -906,15 +912,23 @@ __device__ __forceinline__ bool update_head_done(const int32_t *chg, int32_t *co
   return true;
 }
 
-__global__ void k_rounds_out(const int32_t *__restrict__ conv, int32_t *__restrict__ rounds,
-                             int bh, int iters) {
+__global__ void k_rounds_out(const int32_t *__restrict__ conv,
+                             const unsigned long long *__restrict__ work,
+                             int32_t *__restrict__ rounds, float *__restrict__ sweeps, int bh,
+                             int iters, int n, int c) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < bh) rounds[i] = (conv != nullptr && conv[i] != 0) ? conv[i] : iters;
+  if (i >= bh) return;
+  const int r = (conv != nullptr && conv[i] != 0) ? conv[i] : iters;
+  if (rounds != nullptr) rounds[i] = r;
+  if (sweeps != nullptr)
+    sweeps[i] = (work != nullptr && iters > 0)
+                    ? (float)(1.0 + (double)work[i] / ((double)n * (double)c))
+                    : (float)r;
 }
 
-kv_status launch_rounds_out(const int32_t *conv, int32_t *rounds, int bh, int iters,
-                            hipStream_t s) {
-  k_rounds_out<<<(bh + 255) / 256, 256, 0, s>>>(conv, rounds, bh, iters);
+kv_status launch_rounds_out(const int32_t *conv, const unsigned long long *work, int32_t *rounds,
+                            float *sweeps, int bh, int iters, int n, int c, hipStream_t s) {
+  k_rounds_out<<<(bh + 255) / 256, 256, 0, s>>>(conv, work, rounds, sweeps, bh, iters, n, c);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

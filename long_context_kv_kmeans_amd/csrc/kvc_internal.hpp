@@ -324,6 +324,7 @@ struct AssignInc {
   uint16_t *cfrags = nullptr;            // the moved clusters' tiles, in mlist order
   int32_t *glist = nullptr;              // [bh][n]  queued keys
   unsigned long long *gbest = nullptr;   // [bh][n]  (score bits << 32 | label) per queued key
+  unsigned long long *work = nullptr;    // [bh]     (key, centroid) pairs scored after round 1
 };
 // Its workspace (carved from kv_cluster_build's).
 struct AssignIncWs {
@@ -331,6 +332,7 @@ struct AssignIncWs {
   float *koff;
   uint16_t *cfrags;
   unsigned long long *gbest;
+  unsigned long long *work;  // zeroed with the fixed-point flags
 };
 size_t assign_inc_ws_bytes(int bh, int n, int c, int d);
 void assign_inc_ws_carve(void *base, int bh, int n, int c, int d, AssignIncWs *w);
@@ -343,9 +345,12 @@ void assign_inc_ws_carve(void *base, int bh, int n, int c, int d, AssignIncWs *w
 kv_status launch_assign_round(const void *keys, int bh, int n, int d, int c, int32_t *labels,
                               const void *frags, const AssignIncWs &w, int round, LloydSkip skip,
                               hipStream_t s);
-// rounds[i] = conv[i] if set, else iters (conv null: iters for every head).
-kv_status launch_rounds_out(const int32_t *conv, int32_t *rounds, int bh, int iters,
-                            hipStream_t s);
+// rounds[i] = conv[i] if set, else iters (conv null: iters for every head);
+// sweeps[i] (when given) = the assignment work in whole sweeps of n x c
+// pairs: 1 + work[i] / (n c) with the incremental work counter, else the
+// rounds.
+kv_status launch_rounds_out(const int32_t *conv, const unsigned long long *work, int32_t *rounds,
+                            float *sweeps, int bh, int iters, int n, int c, hipStream_t s);
 kv_status launch_init_centroids(const void *keys, const int32_t *init_idx, float *cent, int bh,
                                 int n, int c, int d, kv_dtype dt, int32_t *status, hipStream_t s,
                                 int32_t *zero = nullptr, int nzero = 0);

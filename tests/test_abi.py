@@ -159,17 +159,17 @@ def test_cluster_build_validation():
     p = _fake_pool(row_cap=1000, unit_cap=64)
     ws_need = L.kv_cluster_build_workspace(1, 8, 1000, 128, 64, kvc.KV_BF16)
     assert ws_need > 0
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 65, 10, a, None, None, None, a, ws_need,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 65, 10, a, None, None, None, None, a, ws_need,
                               None) == kvc.KV_ERR_CAPACITY  # clusters > unit_cap
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1001, 64, 10, a, None, None, None, a, ws_need,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1001, 64, 10, a, None, None, None, None, a, ws_need,
                               None) == kvc.KV_ERR_CAPACITY  # keys > row_cap
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 50, 64, 10, a, None, None, None, a, ws_need,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 50, 64, 10, a, None, None, None, None, a, ws_need,
                               None) == kvc.KV_ERR_INVALID_ARG  # clusters > keys
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 0, a, None, None, None, a, ws_need,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 0, a, None, None, None, None, a, ws_need,
                               None) == kvc.KV_ERR_INVALID_ARG  # no iterations, no labels
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 10, None, None, None, None, a, ws_need,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 10, None, None, None, None, None, a, ws_need,
                               None) == kvc.KV_ERR_INVALID_ARG
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 10, a, None, None, None, a, ws_need - 1,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 1000, 64, 10, a, None, None, None, None, a, ws_need - 1,
                               None) == kvc.KV_ERR_WORKSPACE
     assert L.kv_kmeans_assign(a, a, 8, 1000, 128, 40000, kvc.KV_BF16, a, a, 1 << 30,
                               None) == kvc.KV_ERR_UNSUPPORTED  # too many clusters
@@ -311,11 +311,11 @@ def test_ranges_beyond_the_kernels_limits_are_refused():
     assert L.kv_kmeans_update(a, a, a, a, None, 8, 20000, 128, 8193, kvc.KV_BF16, a, big,
                               None) == kvc.KV_ERR_UNSUPPORTED
     p = _fake_pool(row_cap=20000, unit_cap=9000)
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 20000, 8193, 10, a, None, None, None, a, big,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 20000, 8193, 10, a, None, None, None, None, a, big,
                               None) == kvc.KV_ERR_UNSUPPORTED
     # 8192 clusters and 8192 units are inside the limits (only the workspace is short here)
     p = _fake_pool(row_cap=20000, unit_cap=8192)
-    assert L.kv_cluster_build(ctypes.byref(p), a, a, 20000, 8192, 10, a, None, None, None, a, 256,
+    assert L.kv_cluster_build(ctypes.byref(p), a, a, 20000, 8192, 10, a, None, None, None, None, a, 256,
                               None) == kvc.KV_ERR_WORKSPACE
     assert L.kv_select(ctypes.byref(p), a, 32, 512, None, a, 512, a, a, None, None, a, 16,
                        None) == kvc.KV_ERR_WORKSPACE

@@ -145,7 +145,7 @@ def test_update_empty_cluster_keeps_centroid(tiny):
     assert cnt[0].tolist() == case["expect_counts"]
 
 
-def _cluster_build(cfg, heads, iters, seqs=(0,), rounds=None, dup=0):
+def _cluster_build(cfg, heads, iters, seqs=(0,), rounds=None, dup=0, sweeps=None):
     inp = wl.layer_inputs(cfg, 0, heads=heads, seqs=seqs)
     if dup:  # exact copies: key i repeats key i - i % dup (ties between keys and centroids)
         src = np.arange(inp["keys"].shape[2])
@@ -157,7 +157,7 @@ def _cluster_build(cfg, heads, iters, seqs=(0,), rounds=None, dup=0):
     init = torch.from_numpy(inp["init_idx"]).cuda()
     lab = torch.zeros(B, H, N, dtype=torch.int32, device="cuda")
     kvc.kv_cluster_build(pool, keys, vals, cfg.n_clusters, iters, init, assign_out=lab,
-                         rounds_out=rounds)
+                         rounds_out=rounds, sweeps_out=sweeps)
     torch.cuda.synchronize()
     return inp, pool, lab.cpu().numpy()
 
@@ -222,15 +222,19 @@ def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, dup, it
     fixed points."""
     cfg = wl.get_config(cfg_idx, **over)
     rounds = torch.full((1, len(heads)), -1, dtype=torch.int32, device="cuda")
-    inp, pool, lab = _cluster_build(cfg, heads, iters, rounds=rounds, dup=dup)
-    rounds = rounds.cpu().numpy()
+    sweeps = torch.full((1, len(heads)), -1.0, dtype=torch.float32, device="cuda")
+    inp, pool, lab = _cluster_build(cfg, heads, iters, rounds=rounds, dup=dup, sweeps=sweeps)
+    rounds, sweeps = rounds.cpu().numpy(), sweeps.cpu().numpy()
     # assignments run per head: iters, or (bf16) fewer for a head whose
-    # assignment in some round 2.. changed no label
+    # assignment in some round 2.. changed no label; their work in whole
+    # sweeps: rounds 1 and 2 sweep everything, later rounds at most a third of
+    # the centroids for every key plus all of them for the queued keys
     if cfg.dtype == "fp32":
-        assert (rounds == iters).all()
+        assert (rounds == iters).all() and (sweeps == iters).all()
     else:
         assert ((rounds >= 2) & (rounds <= iters)).all(), rounds
-    print(f"rounds run per head: {rounds.tolist()} of {iters}")
+        assert ((sweeps >= 2 - 1e-6) & (sweeps <= 2 + (rounds - 2) * 4 / 3 + 1e-3)).all(), sweeps
+    print(f"rounds run per head: {rounds.tolist()} of {iters}; sweeps {sweeps.round(3).tolist()}")
     B, H, N, d = inp["keys"].shape
     keys_d = to_dev(inp["keys"], cfg.dtype).reshape(B * H, N, d)
     idx = torch.from_numpy(inp["init_idx"]).cuda().reshape(B * H, -1).long()
