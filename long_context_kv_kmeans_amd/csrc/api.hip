@@ -250,6 +250,10 @@ kv_status kv_cluster_build(const kv_pool *pool, const void *keys, const void *va
       // from the second round on, compare with the previous round's labels
       LloydSkip round_skip = it > 0 ? skip : LloydSkip{};
       round_skip.round = it + 1;
+      // from the second round on the assignment marks the clusters its label
+      // changes touch; the member sums of the others stand (not in the last
+      // round, whose update also lays out the pack)
+      if (it > 0 && it + 1 < iters && skip.conv != nullptr) round_skip.touched = inc.flags[(it + 1) & 1];
       if (skip.conv != nullptr)
         st = launch_assign_round(keys, bh, n_keys, d, n_clusters, labels, asg_ws, inc, it + 1,
                                  round_skip, stream);

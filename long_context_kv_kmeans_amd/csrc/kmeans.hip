@@ -1150,7 +1150,8 @@ __global__ void __launch_bounds__(256) k_segsum(int n, int c, int ntile,
                                                 const T *__restrict__ keys,
                                                 const float *cent_in, float *cent_out,
                                                 uint16_t *__restrict__ frags,
-                                                const int32_t *conv, int32_t *chg) {
+                                                const int32_t *conv, int32_t *chg,
+                                                const int32_t *__restrict__ touched) {
   constexpr int EPL = 16 / Elem<T>::kBytes;  // elements per lane
   constexpr int LPR = D / EPL;               // lanes per row
   constexpr int RPI = 64 / LPR;              // member rows per wave instruction
@@ -1162,6 +1163,7 @@ __global__ void __launch_bounds__(256) k_segsum(int n, int c, int ntile,
   const int lane = threadIdx.x & 63;
   const int part = lane % LPR, slot = lane / LPR;
   if (k >= c) return;
+  if (touched != nullptr && touched[(size_t)bh * c + k] == 0) return;  // same members as before
   const int cnt = tot[(size_t)bh * c + k];
   const int st = label_block_base(agg, (c + kLabelBlock - 1) / kLabelBlock, bh, k / kLabelBlock) +
                  start[(size_t)bh * c + k];
@@ -1314,7 +1316,8 @@ __global__ void __launch_bounds__(256) k_segsum_local(int n, int c, int ntile, i
                                                       const T *__restrict__ keys,
                                                       const float *cent_in, float *cent_out,
                                                       uint16_t *__restrict__ frags,
-                                                      const int32_t *conv, int32_t *chg) {
+                                                      const int32_t *conv, int32_t *chg,
+                                                      const int32_t *__restrict__ touched) {
   constexpr int EPL = 16 / Elem<T>::kBytes;
   constexpr int LPR = D / EPL;
   constexpr int RPI = 64 / LPR;
@@ -1330,6 +1333,7 @@ __global__ void __launch_bounds__(256) k_segsum_local(int n, int c, int ntile, i
   const int lane = threadIdx.x & 63;
   const int part = lane % LPR, slot = lane / LPR;
   if (k >= c) return;
+  if (touched != nullptr && touched[(size_t)bh * c + k] == 0) return;  // same members as before
   // lane = chunk: label k's (prefix, count) entry there; the members of the
   // earlier chunks; where its members start in `local`
   const int chn = min(lane, nchunk - 1);
@@ -1449,17 +1453,17 @@ kv_status launch_update(const void *keys, const int32_t *labels, const float *ce
   if (dt == KV_BF16) {
     if (d == 128)
       k_segsum<uint16_t, 128><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const uint16_t *)keys,
-                                                cent_in, cent_out, fr, skip.conv, skip.chg);
+                                                cent_in, cent_out, fr, skip.conv, skip.chg, skip.touched);
     else
       k_segsum<uint16_t, 64><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const uint16_t *)keys,
-                                               cent_in, cent_out, fr, skip.conv, skip.chg);
+                                               cent_in, cent_out, fr, skip.conv, skip.chg, skip.touched);
   } else {
     if (d == 128)
       k_segsum<float, 128><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const float *)keys,
-                                             cent_in, cent_out, nullptr, skip.conv, skip.chg);
+                                             cent_in, cent_out, nullptr, skip.conv, skip.chg, skip.touched);
     else
       k_segsum<float, 64><<<g, 256, 0, s>>>(n, c, ntile, tot, start, agg, perm, (const float *)keys,
-                                            cent_in, cent_out, nullptr, skip.conv, skip.chg);
+                                            cent_in, cent_out, nullptr, skip.conv, skip.chg, skip.touched);
   }
   if (perm_out) *perm_out = perm;
   if (start_out) *start_out = start;
@@ -1492,17 +1496,17 @@ kv_status launch_update_local(const void *keys, const int32_t *labels, const flo
   if (dt == KV_BF16) {
     if (d == 128)
       k_segsum_local<uint16_t, 128><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                      (const uint16_t *)keys, cent_in, cent_out, fr, skip.conv, skip.chg);
+                                                      (const uint16_t *)keys, cent_in, cent_out, fr, skip.conv, skip.chg, skip.touched);
     else
       k_segsum_local<uint16_t, 64><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                     (const uint16_t *)keys, cent_in, cent_out, fr, skip.conv, skip.chg);
+                                                     (const uint16_t *)keys, cent_in, cent_out, fr, skip.conv, skip.chg, skip.touched);
   } else {
     if (d == 128)
       k_segsum_local<float, 128><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                    (const float *)keys, cent_in, cent_out, nullptr, skip.conv, skip.chg);
+                                                    (const float *)keys, cent_in, cent_out, nullptr, skip.conv, skip.chg, skip.touched);
     else
       k_segsum_local<float, 64><<<g, 256, 0, s>>>(n, c, ntile, nchunk, ltab, local,
-                                                   (const float *)keys, cent_in, cent_out, nullptr, skip.conv, skip.chg);
+                                                   (const float *)keys, cent_in, cent_out, nullptr, skip.conv, skip.chg, skip.touched);
   }
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }

@@ -309,6 +309,10 @@ struct LloydSkip {
   int32_t *conv = nullptr;
   int32_t *chg = nullptr;
   int round = 0;  // 1-based number of the round the launch belongs to
+  // [bh][c] or null: the clusters this round's label changes touched; the
+  // member sums of an untouched cluster are those of the last round, so its
+  // centroid and tile stay as they are
+  const int32_t *touched = nullptr;
 };
 // Incremental assignment of kv_cluster_build (bf16): a round sweeps every
 // centroid only for the keys whose own cluster moved in the last update; the
