@@ -9,7 +9,8 @@ budget 2048 rows and 1024 decode steps:
   prefill : per layer, kv_cluster_build (K-means assign/update x10, then the
             pack of K/V into cluster-contiguous rows; a head whose assignment
             changes no label has reached a fixed point and skips the rounds
-            left, with the result of all ten);
+            left, and from the third round on only the centroids that moved
+            are rescored, all with the result of ten whole rounds);
   decode  : 1024 steps x 36 layers of kv_decode_step, one launch per
             layer-step: the boundary test on the query pair; on a retrieval
             step, scoring of the centroids, the budgeted top-k selection and
