@@ -82,34 +82,44 @@ __device__ __forceinline__ void write_centroid_norm(uint4 *tile, int ks, int m, 
   reinterpret_cast<float *>(tile + ks * 64)[m] = neg_halfsq;
 }
 
-// fp32 centroids -> tiles; D/4 threads per centroid row, 4 elements each.
+// fp32 centroids -> tiles; D/8 lanes per centroid row, 8 consecutive
+// elements each: the lane layout, the in-lane order of the squared-norm sum
+// and the pairing across lanes of segsum_finish, which writes the tiles of
+// the later rounds, so both give the same tile bits for the same centroid.
 template <int D>
 __global__ void __launch_bounds__(256) k_prep_frags(const float *__restrict__ cent,
                                                     uint16_t *__restrict__ frags, int c, int ntile) {
   using TL = AssignTile<D>;
-  constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
   const int bh = blockIdx.y;
-  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int e0 = (threadIdx.x % TPR) * 4;
-  if (row >= ntile * 32) return;  // uniform per row group (TPR divides 64)
+  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int e0 = (threadIdx.x % LPR) * 8;
+  if (row >= ntile * 32) return;  // uniform per row group (LPR divides 64)
   const bool real = row < c;
-  float4 v = {0.f, 0.f, 0.f, 0.f};
-  if (real) v = *reinterpret_cast<const float4 *>(cent + ((size_t)bh * c + row) * D + e0);
-  const uint16_t b0 = f32_to_bf16_rne(v.x), b1 = f32_to_bf16_rne(v.y);
-  const uint16_t b2 = f32_to_bf16_rne(v.z), b3 = f32_to_bf16_rne(v.w);
+  float v[8];
+  const float4 *src = reinterpret_cast<const float4 *>(cent + ((size_t)bh * c + (real ? row : 0)) * D + e0);
+  const float4 lo = real ? src[0] : float4{0.f, 0.f, 0.f, 0.f};
+  const float4 hi = real ? src[1] : float4{0.f, 0.f, 0.f, 0.f};
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  uint16_t b[8];
   float sq = 0.f;
-  sq = fmaf(bf16_bits_to_f32(b0), bf16_bits_to_f32(b0), sq);
-  sq = fmaf(bf16_bits_to_f32(b1), bf16_bits_to_f32(b1), sq);
-  sq = fmaf(bf16_bits_to_f32(b2), bf16_bits_to_f32(b2), sq);
-  sq = fmaf(bf16_bits_to_f32(b3), bf16_bits_to_f32(b3), sq);
-  sq = group_sum<TPR>(sq);
-  const int t = row / 32, m = row % 32, s = e0 / 16, hf = (e0 % 16) / 8, j0 = e0 % 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    b[e] = f32_to_bf16_rne(v[e]);
+    const float r = bf16_bits_to_f32(b[e]);
+    sq = fmaf(r, r, sq);
+  }
+  sq = group_sum<LPR>(sq);
+  const int t = row / 32, m = row % 32;
   uint4 *tile = reinterpret_cast<uint4 *>(frags) + ((size_t)bh * ntile + t) * TL::U4;
-  uint2 pk;
-  pk.x = b0 | ((uint32_t)b1 << 16);
-  pk.y = b2 | ((uint32_t)b3 << 16);
-  *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(tile + s * 64 + m + 32 * hf) + j0) = pk;
+  uint4 pk;
+  pk.x = b[0] | ((uint32_t)b[1] << 16);
+  pk.y = b[2] | ((uint32_t)b[3] << 16);
+  pk.z = b[4] | ((uint32_t)b[5] << 16);
+  pk.w = b[6] | ((uint32_t)b[7] << 16);
+  tile[(e0 / 16) * 64 + m + 32 * ((e0 % 16) / 8)] = pk;
   if (e0 == 0) write_centroid_norm(tile, TL::KS, m, real ? -0.5f * sq : kPadNorm);
 }
 
@@ -734,9 +744,9 @@ kv_status launch_prep_frags(const float *cent, int bh, int d, int c, void *ws, h
   const int ntile = (c + 31) / 32;
   uint16_t *frags = static_cast<uint16_t *>(ws);
   if (d == 128)
-    k_prep_frags<128><<<dim3((ntile * 32 + 7) / 8, bh), 256, 0, s>>>(cent, frags, c, ntile);
+    k_prep_frags<128><<<dim3((ntile * 32 + 15) / 16, bh), 256, 0, s>>>(cent, frags, c, ntile);
   else
-    k_prep_frags<64><<<dim3((ntile * 32 + 15) / 16, bh), 256, 0, s>>>(cent, frags, c, ntile);
+    k_prep_frags<64><<<dim3((ntile * 32 + 31) / 32, bh), 256, 0, s>>>(cent, frags, c, ntile);
   return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

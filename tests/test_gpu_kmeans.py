@@ -209,21 +209,11 @@ EQ_EXTRA = [
 ]
 
 
-@pytest.mark.parametrize("iters", [4, 14])
-@pytest.mark.parametrize("cfg_idx,over,heads,dup",
-                         [c + (0,) for c in [CASES[0], CASES[2]] + BIG_C] + EQ_EXTRA)
-def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, dup, iters):
-    """kv_cluster_build's rounds (the two-launch update of every round but the
-    last; heads that reach a fixed point skip their later rounds; from the
-    third round on, the sweep covers only the centroids that moved, plus every
-    centroid for the keys whose own centroid moved) give the same labels and
-    centroids, bit for bit, as running kv_kmeans_assign and kv_kmeans_update
-    round by round from the same start. 14 rounds take these heads past their
-    fixed points."""
-    cfg = wl.get_config(cfg_idx, **over)
-    rounds = torch.full((1, len(heads)), -1, dtype=torch.int32, device="cuda")
-    sweeps = torch.full((1, len(heads)), -1.0, dtype=torch.float32, device="cuda")
-    inp, pool, lab = _cluster_build(cfg, heads, iters, rounds=rounds, dup=dup, sweeps=sweeps)
+def _check_build_equals_rounds(cfg, heads, iters, dup=0, seqs=(0,)):
+    rounds = torch.full((len(seqs), len(heads)), -1, dtype=torch.int32, device="cuda")
+    sweeps = torch.full((len(seqs), len(heads)), -1.0, dtype=torch.float32, device="cuda")
+    inp, pool, lab = _cluster_build(cfg, heads, iters, seqs=seqs, rounds=rounds, dup=dup,
+                                    sweeps=sweeps)
     rounds, sweeps = rounds.cpu().numpy(), sweeps.cpu().numpy()
     # assignments run per head: iters, or (bf16) fewer for a head whose
     # assignment in some round 2.. changed no label; their work in whole
@@ -250,6 +240,37 @@ def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, dup, it
     np.testing.assert_array_equal(lab.reshape(B * H, N), labels.cpu().numpy())
     um = pool.unit_mean[:, :, :cfg.n_clusters].reshape(B * H, cfg.n_clusters, d)
     assert torch.equal(um, cent)
+
+
+@pytest.mark.parametrize("iters", [4, 14])
+@pytest.mark.parametrize("cfg_idx,over,heads,dup",
+                         [c + (0,) for c in [CASES[0], CASES[2]] + BIG_C] + EQ_EXTRA)
+def test_cluster_build_equals_assign_update_rounds(cfg_idx, over, heads, dup, iters):
+    """kv_cluster_build's rounds (the two-launch update of every round but the
+    last; heads that reach a fixed point skip their later rounds; from the
+    third round on, the sweep covers only the centroids that moved, plus every
+    centroid for the keys whose own centroid moved; intermediate updates skip
+    the member sums of untouched clusters) give the same labels and
+    centroids, bit for bit, as running kv_kmeans_assign and kv_kmeans_update
+    round by round from the same start. 14 rounds take these heads past their
+    fixed points."""
+    _check_build_equals_rounds(wl.get_config(cfg_idx, **over), heads, iters, dup=dup)
+
+
+def test_cluster_build_equals_rounds_128_heads():
+    """16 sequences x 8 KV heads in one build: the served-head lists and the
+    queued-key groups span two 64-head chunks."""
+    cfg = wl.get_config(4, n_keys=4096, n_clusters=256, n_components=64)
+    _check_build_equals_rounds(cfg, list(range(8)), cfg.iters, seqs=tuple(range(16)))
+
+
+@pytest.mark.parametrize("cfg_idx", [3, 1])
+def test_cluster_build_equals_rounds_full_size(cfg_idx):
+    """One layer at the full sizes of the 36-layer and the single-layer
+    workloads (8 heads x 131072 keys, C = 8192; 8 x 32768, C = 2048), the
+    rounds the bench runs."""
+    cfg = wl.get_config(cfg_idx)
+    _check_build_equals_rounds(cfg, list(range(cfg.n_kv_heads)), cfg.iters)
 
 
 def test_cluster_build_free_running_cfg0():
