@@ -156,7 +156,7 @@ def test_decode_loop_parity(cfg_idx, over, steps, seqs):
 
 
 @pytest.mark.parametrize("attend", ["step", "wset", "pool"])
-def test_decode_full_size_cfg1_benchmark_path(attend):
+def test_decode_full_size_qwen3_layer_32k_benchmark_path(attend):
     # the Qwen3-8B-shaped layer at full size (8 KV heads x 32768 keys, C = 2048, 256 steps)
     # through the calls the benchmark times: kv_boundary_select with row spans, then
     # kv_fetch_attend over an HBM working set (the default) or kv_gather_attend on the
@@ -170,7 +170,7 @@ def test_decode_full_size_cfg1_benchmark_path(attend):
 
 
 @pytest.mark.parametrize("attend", ["step", "wset", "pool"])
-def test_decode_full_size_cfg4_batch16_benchmark_path(attend):
+def test_decode_full_size_batch16_32k_benchmark_path(attend):
     # batched decode at full size: 16 sequences x 8 KV heads x 32768 keys in one launch,
     # budget 1024; sequences 0 and 9 carry the oracle's clustering and are checked
     cfg = wl.get_config(4, iters=2)
@@ -181,7 +181,7 @@ def test_decode_full_size_cfg4_batch16_benchmark_path(attend):
 
 
 @pytest.mark.parametrize("attend", ["step", "wset", "pool"])
-def test_decode_full_size_cfg3_layer_shape(attend):
+def test_decode_full_size_128k_layer_shape(attend):
     # one layer of the long-input long-output workload at full size: 8 KV heads x 131072
     # keys, 8192 units, budget 2048, 1024 steps, through the benchmark's calls.
     # Both sides get the same fixed clustering (key i in unit i mod 8192, indexed by the
@@ -309,7 +309,7 @@ def test_segment_append_capacity_errors_are_reported():
     assert int(pool2.n_rows.item()) == 12 and int(pool2.n_units.item()) == 2
 
 
-def test_decode_cfg3_two_layers_through_captured_graphs():
+def test_decode_128k_two_layers_through_captured_graphs():
     """Two layers of the 36-layer long-input long-output workload (131072 keys per KV
     head, 8192 units, budget 2048), each with its own keys, pool, working set and
     query walk, through the benchmark's launch configuration: every decode step

@@ -228,7 +228,7 @@ def test_fetch_attend_equals_fetch_then_attend(dtype, d, hq, cap, max_rows):
             assert torch.equal(w0.v[bi, h, :r], w1.v[bi, h, :r])
 
 
-def test_host_pool_working_set_decode_parity_cfg1_full_size():
+def test_host_pool_working_set_decode_parity_qwen3_layer_32k_full_size():
     # the Qwen3-8B-shaped layer at full size with its K/V in host memory: fetch on
     # retrieval steps, attention over the working set, checked against the oracle
     cfg = wl.get_config(1, iters=2)

@@ -273,7 +273,7 @@ def test_cluster_build_equals_rounds_full_size(cfg_idx):
     _check_build_equals_rounds(cfg, list(range(cfg.n_kv_heads)), cfg.iters)
 
 
-def test_cluster_build_free_running_cfg0():
+def test_cluster_build_free_running_tiny_fp32():
     cfg = wl.get_config(0)
     inp, pool, lab = _cluster_build(cfg, [0, 1], cfg.iters)
     for g in range(2):
@@ -285,7 +285,7 @@ def test_cluster_build_free_running_cfg0():
         assert J_gpu <= J_ora * (1 + 1e-3)
 
 
-def test_cluster_build_free_running_report_cfg1_small():
+def test_cluster_build_free_running_report_qwen3_layer_small():
     cfg = wl.get_config(1, n_keys=4096, n_clusters=256, n_components=64)
     inp, pool, lab = _cluster_build(cfg, [0], cfg.iters)
     o = okm.lloyd(inp["keys"][0, 0], inp["init_idx"][0, 0], cfg.iters, mode="parity", dtype="bf16")

@@ -208,8 +208,8 @@ def test_select_flag_zero_keeps_previous():
     assert sel[0][0, 0, :int(sel[1][0, 0])].cpu().tolist() == [0, 1]
 
 
-def test_select_full_size_cfg3_head():
-    """Full cfg3 cluster count on one head (8192 units, budget 2048), oracle scores."""
+def test_select_full_size_8192_unit_head():
+    """The 36-layer 128K workload's cluster count on one head (8192 units, budget 2048), oracle scores."""
     cfg = wl.get_config(3)
     rng = np.random.default_rng(11)
     C, d = cfg.n_clusters, cfg.head_dim
