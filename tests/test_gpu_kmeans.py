@@ -206,6 +206,11 @@ EQ_EXTRA = [
     (1, dict(n_keys=16384, n_clusters=1024, n_components=128), list(range(8)), 0),
     (CASES[3][0], CASES[3][1], CASES[3][2], 0),
     (1, dict(n_keys=8192, n_clusters=700, n_components=96), [0, 1, 2], 3),
+    # more shapes: few components (clusters split one mixture component),
+    # C above a third of a small key set, head_dim 64 with many heads
+    (1, dict(n_keys=6000, n_clusters=333, n_components=12), [0, 1, 2, 3], 0),
+    (1, dict(n_keys=12000, n_clusters=3000, n_components=200), [4, 5], 0),
+    (4, dict(n_keys=2500, n_clusters=100, n_components=30, head_dim=64), list(range(8)), 2),
 ]
 
 
